@@ -1,0 +1,141 @@
+"""fp64 reference definition of grouped local causal attention (AAH-v3 execution).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: "Asymmetric Attention Heads: Structured Head-Wise Context Allocation for
+Transformer Attention" (AAH).
+  * Section 4 (Background: Standard Multi-Head Attention): O_h = softmax(Q_h K_h^T
+    / sqrt(d_h) + M) V_h; the softmax scale is passed in explicitly here.
+  * Section 5.8 (Head mapping and execution): for a head with window W, key t_k is
+    allowed for query t_q iff t_q - W + 1 <= t_k <= t_q; A = softmax(Q K^T/sqrt(d_h)
+    + M_W), Y = A V; W is clamped to at most T, and W = T is standard causal
+    attention.  Heads are bucketed by W and scattered back to head order, which
+    has no numerical effect: head h's output depends only on (Q_h, K_h, V_h, W_h).
+  * Section 7.7 (Backend-realized local attention): the same predicate written as
+    k <= q and k >= q - (W - 1).
+  * Section 5.10 (Measuring Attention Coverage and Hardware FLOPs): the exact
+    allowed-pair count of a window W over length T is the sum over t = 1..T of
+    min(t, W); ACR is the rectangular proxy sum_h T * T_k / (H T^2).
+  * Table 6 caption: inference ACR reconstructed as sum_W f_W * W / T.
+
+Readings where the pages are silent (each listed in the design notes):
+  * the additive mask value is -inf, so masked weights are exactly zero;
+  * the log-sum-exp is the natural log of sum_j exp(scaled score) over the
+    window, one value per query row;
+  * the backward pass is plain matrix calculus of the forward definition.
+
+Everything is computed in float64 from whatever inputs are passed (the tests
+pass the same bf16-rounded values the device sees, promoted exactly).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def window_allowed(T: int, w: int) -> np.ndarray:
+    """Boolean [T, T] matrix; entry (i, j) is True when key j is in query i's window.
+
+    AAH section 5.8: t_q - W + 1 <= t_k <= t_q, with W clamped to T."""
+    if w < 1:
+        raise ValueError("window must be >= 1")
+    w = min(int(w), T)
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (j <= i) & (j >= i - w + 1)
+
+
+def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None):
+    """Scores, mask and softmax of one head (AAH section 5.8).
+
+    Returns (P, m, l) where P[r, j] is the attention weight of query row r on
+    key j, m the row max of the scaled masked scores and l the row sum of
+    exp(score - m)."""
+    T = k.shape[0]
+    allowed = window_allowed(T, w)
+    if rows is not None:
+        allowed = allowed[rows]
+        q = q[rows]
+    S = scale * (q @ k.T)                      # explicit scores
+    S = np.where(allowed, S, -np.inf)          # additive -inf mask M_W
+    m = S.max(axis=1, keepdims=True)           # the diagonal is always allowed: finite
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return E / l, m[:, 0], l[:, 0]
+
+
+def attn_fwd_ref(q, k, v, windows, scale):
+    """Forward pass for Q/K/V laid out [B, H, T, d] with one window per head.
+
+    Returns (O [B,H,T,d], LSE [B,H,T]) in float64.  AAH section 5.8."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, T, d = q.shape
+    O = np.empty((B, H, T, v.shape[-1]), dtype=np.float64)
+    LSE = np.empty((B, H, T), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            P, m, l = _head_probs(q[b, h], k[b, h], int(windows[h]), scale)
+            O[b, h] = P @ v[b, h]
+            LSE[b, h] = m + np.log(l)
+    return O, LSE
+
+
+def attn_fwd_rows_ref(q_h, k_h, v_h, w, scale, rows):
+    """Forward pass of selected query rows of ONE head (arrays [T, d]).
+
+    Same definition as attn_fwd_ref restricted to the given rows, so that large
+    inputs can be spot-checked row by row.  Returns (O [len(rows), d], LSE)."""
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    P, m, l = _head_probs(q_h, k_h, int(w), scale, rows=np.asarray(rows))
+    return P @ v_h, m + np.log(l)
+
+
+def attn_bwd_ref(q, k, v, windows, scale, do):
+    """Gradients (dQ, dK, dV) of sum(O * dO) by matrix calculus of section 5.8.
+
+    With P the masked row softmax of S = scale Q K^T and O = P V:
+      dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+      dS = P * (dP - D 1^T)  (zero where masked, since P is),
+      dQ = scale dS K,  dK = scale dS^T Q."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    B, H, T, d = q.shape
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale)
+            dv[b, h] = P.T @ do[b, h]
+            dP = do[b, h] @ v[b, h].T
+            D = (P * dP).sum(axis=1, keepdims=True)
+            dS = P * (dP - D)
+            dq[b, h] = scale * (dS @ k[b, h])
+            dk[b, h] = scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
+def pair_count_ref(T: int, w: int) -> int:
+    """Exact allowed query-key pairs of one head: sum_{t=1}^{T} min(t, W).
+
+    AAH section 5.10 (with W clamped to T, section 5.8)."""
+    W = min(int(w), T)
+    return int(sum(min(t, W) for t in range(1, T + 1)))
+
+
+def acr_ref(windows, T: int) -> float:
+    """Attention Coverage Ratio of one layer, decoder-only (T_q = T, T_k = W_h).
+
+    AAH section 5.10: sum_h T * T_k / (H * T^2)."""
+    windows = [min(int(w), T) for w in windows]
+    return float(sum(T * w for w in windows)) / (len(windows) * T * T)
+
+
+def acr_from_fractions_ref(fractions, windows, T: int) -> float:
+    """Inference ACR from window-bucket fractions: sum_W f_W * W / T (AAH Table 6 caption)."""
+    return float(sum(f * w for f, w in zip(fractions, windows))) / T

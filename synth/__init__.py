@@ -1,0 +1,167 @@
+"""Seeded synthetic inputs for per-head causal local-window attention.
+
+This module is shared by the fp64 oracle's tests and by the HIP path's tests
+and benchmark.  It draws random numbers and assembles window vectors; it holds
+none of the attention arithmetic (no scores, masks, softmax or products).
+
+Workloads follow the pages' 4096-token bf16 setting (Asymmetric Attention
+Heads, Table 2: precision bf16, batch size 1, context 4096, candidate windows
+[512, 1024, 2048, 4096]).  The pages train on an unnamed dataset with trained
+weights; N(0, 1) activations stand in for the projected Q/K/V.
+
+Recipe (fixed, so every consumer sees identical bits):
+  * ``numpy.random.default_rng(seed)``; fp32 standard normals drawn in the
+    order Q, K, V, dO (dO is drawn for every bf16 workload so the window draw
+    that follows is the same with or without a backward pass), then windows.
+  * bf16 workloads round each fp32 draw once to bf16, round-to-nearest-even.
+    The returned float32 arrays hold exactly the bf16 values; ``*_bits`` hold
+    the raw uint16 patterns handed to the device.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, List, Optional
+
+import numpy as np
+
+CANDIDATE_WINDOWS = (512, 1024, 2048, 4096)
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (round-to-nearest-even) and return uint16 bit patterns.
+
+    Inputs here are finite normals; NaN/inf handling is not needed."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclasses.dataclass
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    d: int
+    dtype: str                      # "bf16" or "f32"
+    windows: np.ndarray             # int32 [H]
+    scale: float
+    q: np.ndarray                   # float32 [B,H,T,d] (bf16-exact when dtype == "bf16")
+    k: np.ndarray
+    v: np.ndarray
+    do: Optional[np.ndarray] = None
+    bits: Dict[str, np.ndarray] = dataclasses.field(default_factory=dict)  # uint16 for bf16
+    backward: bool = False
+    meta: Dict[str, object] = dataclasses.field(default_factory=dict)
+
+
+def _draw(rng: np.random.Generator, shape, dtype: str):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if dtype == "bf16":
+        b = bf16_bits(x)
+        return bf16_to_f32(b), b
+    return x, None
+
+
+def random_workload(B: int, H: int, T: int, d: int, windows, dtype: str = "bf16",
+                    seed: int = 0, backward: bool = True, name: str = "random",
+                    value_scale: float = 1.0) -> Workload:
+    """Q, K, V (and dO) ~ N(0, 1) * value_scale for an arbitrary shape and window vector."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, T, d)
+    out = {}
+    bits = {}
+    for key in ("q", "k", "v", "do"):
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        if value_scale != 1.0:
+            x = (x * np.float32(value_scale)).astype(np.float32)
+        if dtype == "bf16":
+            b = bf16_bits(x)
+            bits[key] = b
+            x = bf16_to_f32(b)
+        out[key] = x
+    return Workload(name=name, B=B, H=H, T=T, d=d, dtype=dtype,
+                    windows=np.asarray(windows, dtype=np.int32), scale=1.0 / np.sqrt(d),
+                    q=out["q"], k=out["k"], v=out["v"], do=out["do"] if backward else None,
+                    bits=bits, backward=backward)
+
+
+def _hierarchy_from_groups(group_windows: np.ndarray) -> List[List[int]]:
+    """Binary hierarchy over level-0 groups whose parent window is the larger of
+    its two children, so every child window is <= its parent's (the pages'
+    parent constraint, Asymmetric Attention Heads section 5.7)."""
+    levels = [list(int(x) for x in group_windows)]
+    while len(levels[-1]) > 1:
+        cur = levels[-1]
+        levels.append([max(cur[2 * i], cur[2 * i + 1]) for i in range(len(cur) // 2)])
+    return levels
+
+
+# Workload catalogue.  Index 0 is the small fp32 case the oracle finishes at once;
+# 1 and 2 are the single-layer and 1B-scale forward workloads; 3 is workload 2 with
+# a backward pass; "4a"/"4b"/"4c" are the coverage controls.
+DESCRIPTIONS = {
+    0: "tiny fp32 check: B=1 H=4 T=256 d=32, windows [16,32,64,256]",
+    1: "single layer fwd: B=1 H=16 T=4096 d=64 bf16, windows uniform over {512..4096}",
+    2: "1B-scale layer fwd: B=4 H=32 T=4096 d=64 bf16, 8 groups x 4 heads, P=(.5,.25,.125,.125)",
+    3: "1B-scale layer fwd+bwd: workload 2 shapes and windows with dO",
+    "4a": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, all windows 4096",
+    "4b": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, all windows 512",
+    "4c": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, even heads 512, odd heads 4096",
+}
+
+
+def make_workload(idx, seed: int = 0) -> Workload:
+    """Build one catalogued workload (see DESCRIPTIONS)."""
+    if idx == 0:
+        rng = np.random.default_rng(seed)
+        shape = (1, 4, 256, 32)
+        q = rng.standard_normal(size=shape, dtype=np.float32)
+        k = rng.standard_normal(size=shape, dtype=np.float32)
+        v = rng.standard_normal(size=shape, dtype=np.float32)
+        return Workload(name="tiny-fp32", B=1, H=4, T=256, d=32, dtype="f32",
+                        windows=np.array([16, 32, 64, 256], dtype=np.int32),
+                        scale=1.0 / np.sqrt(32), q=q, k=k, v=v, backward=False)
+
+    if idx in (1, 2, 3, "4a", "4b", "4c"):
+        if idx == 1:
+            B, H = 1, 16
+        else:
+            B, H = 4, 32
+        T, d = 4096, 64
+        rng = np.random.default_rng(seed)
+        shape = (B, H, T, d)
+        arrs, bits = {}, {}
+        for key in ("q", "k", "v", "do"):
+            arrs[key], bits[key] = _draw(rng, shape, "bf16")
+        meta: Dict[str, object] = {}
+        if idx == 1:
+            windows = rng.choice(np.array(CANDIDATE_WINDOWS), size=H).astype(np.int32)
+            name = "single-layer-B1-H16-T4096-d64"
+        elif idx in (2, 3):
+            groups = rng.choice(np.array(CANDIDATE_WINDOWS), size=8,
+                                p=[0.5, 0.25, 0.125, 0.125]).astype(np.int32)
+            meta["group_windows"] = groups.tolist()
+            meta["hierarchy"] = _hierarchy_from_groups(groups)
+            windows = np.repeat(groups, H // 8).astype(np.int32)   # head h -> group h // 4
+            name = "1b-layer-B4-H32-T4096-d64" + ("-fwdbwd" if idx == 3 else "")
+        elif idx == "4a":
+            windows = np.full(H, 4096, dtype=np.int32)
+            name = "control-all4096"
+        elif idx == "4b":
+            windows = np.full(H, 512, dtype=np.int32)
+            name = "control-all512"
+        else:
+            windows = np.where(np.arange(H) % 2 == 0, 512, 4096).astype(np.int32)
+            name = "control-interleaved-512-4096"
+        backward = idx != 1 and idx != 2
+        return Workload(name=name, B=B, H=H, T=T, d=d, dtype="bf16", windows=windows,
+                        scale=1.0 / np.sqrt(d), q=arrs["q"], k=arrs["k"], v=arrs["v"],
+                        do=arrs["do"] if backward else None, bits=bits, backward=backward,
+                        meta=meta)
+    raise KeyError(f"unknown workload {idx!r}")
