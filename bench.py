@@ -1,0 +1,194 @@
+#!/usr/bin/env python3
+"""Benchmark of per-head causal local-window attention on one MI355X.
+
+One step = one pass of the whole path over one batch: window intake and work
+lists (cached after the first call), the forward kernel, the backward
+preprocess and the backward kernels, on the 1B-scale layer workload
+(B=4, H=32, T=4096, d=64, bf16; 8 groups of 4 heads whose windows are drawn
+from {512, 1024, 2048, 4096} with P = (.5, .25, .125, .125); seed 0).
+
+Effective FLOPs count in-window query/key pairs only: 4*d per pair forward
+(Q K^T and P V) and 10*d per pair backward (recomputed Q K^T, dO V^T, P^T dO,
+dS K, dS^T Q).  Pairs per head = sum_{t=1}^{T} min(t, W_h).
+
+Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_FP32_VALU_TFLOPS = 157.3  # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="3", help="catalogued workload id (default 3: fwd+bwd 1B-scale layer)")
+    ap.add_argument("--cpu-heads", type=int, default=48, help="heads of the oracle CPU-baseline sample (0 = skip)")
+    ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
+    return ap.parse_args()
+
+
+def to_dev(wl, key):
+    import torch
+    return torch.from_numpy(wl.bits[key].view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def cpu_baseline(wl, n_heads, with_bwd):
+    """Time the fp64 oracle (as it stands) on a bounded sample of the same workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count() or 1
+    # Sample: the first n_heads (b, h) pairs of batch entry 0, cycling over distinct windows first.
+    order = []
+    seen = set()
+    for h in range(wl.H):
+        if int(wl.windows[h]) not in seen:
+            seen.add(int(wl.windows[h]))
+            order.append(h)
+    order += [h for h in range(wl.H) if h not in order]
+    heads = order[:n_heads]
+    import head_causal_local_amd as aah
+    pairs, _ = aah.window_stats(wl.windows[heads], wl.T)
+    t0 = time.perf_counter()
+    for h in heads:
+        sl = (slice(0, 1), slice(h, h + 1))
+        oracle.attn_fwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale)
+        if with_bwd:
+            oracle.attn_bwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, wl.do[sl])
+    dt = time.perf_counter() - t0
+    flops = (4 + (10 if with_bwd else 0)) * wl.d * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"fp64 oracle {'fwd+bwd' if with_bwd else 'fwd'} of {len(heads)} full heads (b=0, "
+                      f"h={heads}) of the same workload, {pairs} in-window pairs, effective FLOPs as on the GPU"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library runs every head of a layer on a single MI355X "
+              "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import head_causal_local_amd as aah
+    import synth
+
+    if not torch.cuda.is_available():
+        print("no HIP device visible", file=sys.stderr)
+        sys.exit(1)
+
+    wid = int(args.workload) if args.workload.isdigit() else args.workload
+    wl = synth.make_workload(wid)
+    if wl.dtype != "bf16":
+        print("bench.py times bf16 workloads", file=sys.stderr)
+        sys.exit(2)
+    with_bwd = (wl.do is not None) and not args.fwd_only
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    q, k, v = to_dev(wl, "q"), to_dev(wl, "k"), to_dev(wl, "v")
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
+    if with_bwd:
+        do = to_dev(wl, "do")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        ws = torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if with_bwd:
+            aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
+                         stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in events]) if with_bwd else np.zeros(1)
+    ms_per_step = wall * 1e3 / args.steps
+
+    pairs_b, acr = aah.window_stats(wl.windows, T)
+    pairs = B * pairs_b
+    f_fwd = 4 * d * pairs
+    f_bwd = 10 * d * pairs if with_bwd else 0
+    value = (f_fwd + f_bwd) / (ms_per_step * 1e-3) / 1e12
+    fwd_tf = f_fwd / (fwd_ms.mean() * 1e-3) / 1e12
+    bwd_tf = f_bwd / (bwd_ms.mean() * 1e-3) / 1e12 if with_bwd else None
+
+    # Roofline of the kernel that dominates the step.
+    if (not with_bwd) or fwd_ms.mean() >= bwd_ms.mean():
+        roof = {"kernel": "fwd_bf16_kernel<64>", "bound": "mfma", "achieved": round(fwd_tf, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+                "traffic": None, "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2),
+                "algorithmic_flops_per_launch": f_fwd}
+    else:
+        roof = {"kernel": "aah_attn_bwd (preprocess + scalar dQ + scalar dK/dV kernels)", "bound": "alu",
+                "achieved": round(bwd_tf, 2), "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(bwd_tf / PEAK_FP32_VALU_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(float(bwd_ms.mean()) * 1e3, 2), "algorithmic_flops_per_launch": f_bwd}
+
+    out = {
+        "metric": "effective TFLOP/s (in-window pairs only) fwd/bwd, % of bf16 MFMA peak",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (N(0,1) bf16 Q/K/V/dO, seed 0)",
+        "config": {
+            "workload": wl.name + (" fwd+bwd" if with_bwd else " fwd"),
+            "B": B, "H": H, "T": T, "d": d,
+            "windows": [int(x) for x in wl.windows],
+            "in_window_pairs": int(pairs),
+            "acr": round(acr, 4),
+            "fwd_ms": round(float(fwd_ms.mean()), 4),
+            "bwd_ms": round(float(bwd_ms.mean()), 4) if with_bwd else None,
+            "fwd_tflops": round(fwd_tf, 2),
+            "bwd_tflops": round(bwd_tf, 2) if with_bwd else None,
+            "fwd_pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+            "bwd_pct_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2) if with_bwd else None,
+            "step_pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        },
+        "roofline": roof,
+    }
+    if args.cpu_heads > 0:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_heads, with_bwd)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,166 @@
+"""Per-head causal local-window attention for AMD MI355X (gfx950).
+
+The execution branch of Asymmetric Attention Heads (AAH-v3): every head h
+attends only to keys j with i - w_h < j <= i of its own causal local window
+("Asymmetric Attention Heads", section 5.8).  All arithmetic runs in the HIP
+kernels of libaah_attn.so behind the C ABI of include/aah_attn.h; this module
+only marshals arguments.  PyTorch provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+from ._lib import (AAH_BF16, AAH_F32, AahError, EXPORTS, LIB_PATH, WorkItem, check, lib)  # noqa: F401
+
+__all__ = ["attn_fwd", "attn_bwd", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
+           "cache_clear", "AahError", "LIB_PATH"]
+
+
+def _windows_arg(windows) -> np.ndarray:
+    w = np.ascontiguousarray(np.asarray(windows, dtype=np.int64))
+    if w.ndim != 1:
+        raise ValueError("windows must be a 1-D sequence with one entry per head")
+    if np.any(w > np.iinfo(np.int32).max) or np.any(w < np.iinfo(np.int32).min):
+        raise ValueError("window out of int32 range")
+    return np.ascontiguousarray(w.astype(np.int32))
+
+
+def _wptr(w: np.ndarray):
+    return w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return AAH_BF16
+    if t.dtype == torch.float32:
+        return AAH_F32
+    raise AahError(2, "AAH_ERR_UNSUPPORTED", f"dtype {t.dtype} has no kernel (bfloat16 or float32)")
+
+
+def _stream_ptr(t, stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return s.cuda_stream
+
+
+def _check_operand(name, t, ref):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, T, d]")
+
+
+def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None):
+    """O, LSE = local-window attention of q, k, v ([B, H, T, d] device tensors).
+
+    windows: one int per head (>= 1; values above T act as T).  scale defaults
+    to 1/sqrt(d).  Returns (O with q's dtype, LSE float32 [B, H, T])."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_operand(name, t, q)
+    B, H, T, d = q.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_operand("out", out, q)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), B, H, T, d, _dtype_code(q),
+                            float(scale), out.data_ptr(), lse.data_ptr(), None, 0, _stream_ptr(q, stream))
+    check(st)
+    return out, lse
+
+
+def workspace_size(B: int, H: int, T: int, d: int, dtype: str = "bf16", is_bwd: bool = True) -> int:
+    code = AAH_BF16 if dtype in ("bf16", "bfloat16") else AAH_F32
+    return int(lib().aah_attn_workspace_size(B, H, T, d, code, 1 if is_bwd else 0))
+
+
+def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=None, dk=None, dv=None,
+             workspace=None, stream=None):
+    """dQ, dK, dV of sum(O * do) for local-window attention (see attn_fwd)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check_operand(name, t, q)
+    B, H, T, d = q.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_operand(name, t, q)
+    code = _dtype_code(q)
+    need = int(lib().aah_attn_workspace_size(B, H, T, d, code, 1))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib().aah_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+                            _wptr(w), B, H, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                            _stream_ptr(q, stream))
+    check(st)
+    return dq, dk, dv
+
+
+def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:
+    """(row tile, column tile) the kernels use for this dtype / head dim / pass."""
+    code = AAH_BF16 if dtype in ("bf16", "bfloat16") else AAH_F32
+    r, c = ctypes.c_int(), ctypes.c_int()
+    check(lib().aah_tile_shape(code, d, 1 if is_bwd else 0, ctypes.byref(r), ctypes.byref(c)))
+    return r.value, c.value
+
+
+def _plan(fn, windows, B, H, T, q_tile, kv_tile, n_queues) -> np.ndarray:
+    w = _windows_arg(windows)
+    n = ctypes.c_int64()
+    st = fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, None, 0, ctypes.byref(n))
+    if st not in (0, 1):
+        check(st)
+    buf = (WorkItem * max(n.value, 1))()
+    check(fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, buf, n.value, ctypes.byref(n)))
+    arr = np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[: n.value].copy()
+    return arr
+
+
+def plan_fwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8):
+    """Forward work list as an int32 array [n, 4] of (bh, q_tile_index, kv_lo, kv_hi)."""
+    return _plan(lib().aah_plan_fwd, windows, B, H, T, q_tile, kv_tile, n_queues)
+
+
+def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8):
+    """Backward work list as an int32 array [n, 4] of (bh, kv_tile_index, q_lo, q_hi)."""
+    return _plan(lib().aah_plan_bwd, windows, B, H, T, q_tile, kv_tile, n_queues)
+
+
+def window_stats(windows: Sequence[int], T: int) -> Tuple[int, float]:
+    """(exact in-window pairs per batch entry, ACR) of a window vector."""
+    w = _windows_arg(windows)
+    pairs = ctypes.c_int64()
+    acr = ctypes.c_double()
+    check(lib().aah_window_stats(_wptr(w), w.shape[0], T, ctypes.byref(pairs), ctypes.byref(acr)))
+    return pairs.value, acr.value
+
+
+def cache_clear() -> None:
+    lib().aah_cache_clear()

@@ -1,0 +1,322 @@
+// C ABI of the per-head causal local-window attention library: argument
+// validation (always before the first HIP call), the device work-list cache,
+// and kernel dispatch.  Contracts are documented in include/aah_attn.h.
+#include "aah_attn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels.hpp"
+#include "workplan.hpp"
+
+namespace {
+
+using aah::WorkItem;
+
+thread_local std::string g_detail;
+
+aah_status fail(aah_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+aah_status fail(aah_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return st;
+}
+
+aah_status hip_fail(hipError_t e, const char* what) {
+  return fail(AAH_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shape checks shared by every entry point.
+aah_status check_shape(const int32_t* windows, int B, int H, int T, int d, aah_dtype dt) {
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
+  if (static_cast<int64_t>(B) * H > INT32_MAX / 2)
+    return fail(AAH_ERR_INVALID_ARG, "B * H = %lld is too large", static_cast<long long>(B) * H);
+  if (T > (1 << 28)) return fail(AAH_ERR_INVALID_ARG, "T = %d is too large", T);
+  if (d < 1) return fail(AAH_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
+  if (dt != AAH_BF16 && dt != AAH_F32) return fail(AAH_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
+  if (!supported_d(d)) return fail(AAH_ERR_UNSUPPORTED, "head dim %d has no kernel (supported: 32, 64, 128)", d);
+  for (int h = 0; h < H; ++h)
+    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  return AAH_OK;
+}
+
+aah_status check_tensor(const void* p, const char* name, size_t align) {
+  if (p == nullptr) return fail(AAH_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(AAH_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return AAH_OK;
+}
+
+#define AAH_TRY(expr)                 \
+  do {                                \
+    const aah_status st_ = (expr);    \
+    if (st_ != AAH_OK) return st_;    \
+  } while (0)
+
+// ------------------------------------------------------------------ plan cache
+
+struct DevicePlan {
+  WorkItem* items = nullptr;
+  int n_items = 0;
+  int32_t* win = nullptr;  // effective windows, int32[H]
+};
+
+enum PlanKind : int64_t { kPlanFwd = 0, kPlanBwd = 1 };
+
+std::mutex g_mu;
+std::map<std::vector<int64_t>, DevicePlan> g_cache;
+
+constexpr int kQueues = 8;  // MI355X has eight XCDs; workgroups are placed round-robin over them
+
+aah_status get_plan(PlanKind kind, const int32_t* windows, int B, int H, int T, int row_tile, int col_tile,
+                    DevicePlan* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::vector<int64_t> key = {kind, dev, B, H, T, row_tile, col_tile, kQueues};
+  key.reserve(key.size() + H);
+  for (int h = 0; h < H; ++h) key.push_back(aah::effective_window(windows[h], T));
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto found = g_cache.find(key);
+  if (found != g_cache.end()) {
+    *out = found->second;
+    return AAH_OK;
+  }
+  // Forward: row tile = query rows per item, col tile = keys per step.
+  // Backward: row tile = keys per item, col tile = query rows per step.
+  const std::vector<WorkItem> items =
+      kind == kPlanFwd ? aah::plan_forward(windows, B, H, T, row_tile, col_tile, kQueues)
+                       : aah::plan_backward(windows, B, H, T, col_tile, row_tile, kQueues);
+  std::vector<int32_t> win(H);
+  for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
+
+  DevicePlan p;
+  p.n_items = static_cast<int>(items.size());
+  e = hipMalloc(&p.items, items.size() * sizeof(WorkItem));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
+  e = hipMalloc(&p.win, win.size() * sizeof(int32_t));
+  if (e != hipSuccess) {
+    (void)hipFree(p.items);
+    return hip_fail(e, "hipMalloc(windows)");
+  }
+  e = hipMemcpy(p.items, items.data(), items.size() * sizeof(WorkItem), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p.win, win.data(), win.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(p.items);
+    (void)hipFree(p.win);
+    return hip_fail(e, "hipMemcpy(work list)");
+  }
+  g_cache.emplace(std::move(key), p);
+  *out = p;
+  return AAH_OK;
+}
+
+void fwd_tiles(aah_dtype dt, int* row, int* col) {
+  if (dt == AAH_BF16) {
+    *row = aah::kFwdBf16RowTile;
+    *col = aah::kFwdBf16ColTile;
+  } else {
+    *row = aah::kSimpleRowTile;
+    *col = aah::kSimpleColTile;
+  }
+}
+
+void bwd_tiles(aah_dtype /*dt*/, int* row, int* col) {
+  *row = aah::kSimpleRowTile;
+  *col = aah::kSimpleColTile;
+}
+
+// Workspace layout of the backward: D (fp32 [B,H,T]) at offset 0, then the fp32
+// dQ accumulator [B,H,T,d] (bf16 only) at a 256-byte boundary.
+size_t bwd_d_bytes(int B, int H, int T) {
+  return round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256);
+}
+
+size_t bwd_workspace(int B, int H, int T, int d, aah_dtype dt) {
+  size_t bytes = bwd_d_bytes(B, H, T);
+  if (dt == AAH_BF16) bytes += round_up(static_cast<size_t>(B) * H * T * d * sizeof(float), 256);
+  return bytes;
+}
+
+aah_status plan_to_host(PlanKind kind, const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile,
+                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
+  if (n_items == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items is NULL");
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
+  if (q_tile < 1 || kv_tile < 1 || n_queues < 1) return fail(AAH_ERR_INVALID_ARG, "tiles and n_queues must be >= 1");
+  for (int h = 0; h < H; ++h)
+    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  const std::vector<WorkItem> v = kind == kPlanFwd
+                                      ? aah::plan_forward(windows, B, H, T, q_tile, kv_tile, n_queues)
+                                      : aah::plan_backward(windows, B, H, T, q_tile, kv_tile, n_queues);
+  *n_items = static_cast<int64_t>(v.size());
+  if (capacity < static_cast<int64_t>(v.size()))
+    return fail(AAH_ERR_INVALID_ARG, "capacity %lld < %zu items", static_cast<long long>(capacity), v.size());
+  if (items == nullptr) return fail(AAH_ERR_INVALID_ARG, "items is NULL");
+  static_assert(sizeof(aah_work_item) == sizeof(WorkItem), "ABI work item layout");
+  std::memcpy(items, v.data(), v.size() * sizeof(WorkItem));
+  return AAH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int aah_abi_version(void) { return AAH_ABI_VERSION; }
+
+const char* aah_status_string(aah_status status) {
+  switch (status) {
+    case AAH_OK: return "AAH_OK";
+    case AAH_ERR_INVALID_ARG: return "AAH_ERR_INVALID_ARG";
+    case AAH_ERR_UNSUPPORTED: return "AAH_ERR_UNSUPPORTED";
+    case AAH_ERR_WORKSPACE: return "AAH_ERR_WORKSPACE";
+    case AAH_ERR_HIP: return "AAH_ERR_HIP";
+  }
+  return "AAH_ERR_UNKNOWN";
+}
+
+const char* aah_last_error_detail(void) { return g_detail.c_str(); }
+
+size_t aah_attn_workspace_size(int B, int H, int T, int d, aah_dtype dt, int is_bwd) {
+  if (B < 1 || H < 1 || T < 1 || !supported_d(d) || (dt != AAH_BF16 && dt != AAH_F32)) return 0;
+  return is_bwd ? bwd_workspace(B, H, T, d, dt) : 0;
+}
+
+aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* col_tile) {
+  if (row_tile == nullptr || col_tile == nullptr) return fail(AAH_ERR_INVALID_ARG, "NULL output pointer");
+  if (dt != AAH_BF16 && dt != AAH_F32) return fail(AAH_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
+  if (!supported_d(d)) return fail(AAH_ERR_UNSUPPORTED, "head dim %d has no kernel", d);
+  if (is_bwd)
+    bwd_tiles(dt, row_tile, col_tile);
+  else
+    fwd_tiles(dt, row_tile, col_tile);
+  return AAH_OK;
+}
+
+aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, int B, int H, int T,
+                        int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, aah_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_detail.clear();
+  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(o, "o", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+
+  int row = 0, col = 0;
+  fwd_tiles(dt, &row, &col);
+  DevicePlan plan;
+  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
+  const aah::AttnShape s{B, H, T, d, scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dt == AAH_BF16)
+    e = aah::launch_fwd_bf16(q, k, v, o, lse, plan.items, plan.n_items, plan.win, s, st);
+  else
+    e = aah::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                            static_cast<const float*>(v), static_cast<float*>(o), lse, plan.items, plan.n_items,
+                            plan.win, s, st);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return AAH_OK;
+}
+
+aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
+                        float scale, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                        aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(o, "o", 16));
+  AAH_TRY(check_tensor(dout, "dout", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  AAH_TRY(check_tensor(dq, "dq", 16));
+  AAH_TRY(check_tensor(dk, "dk", 16));
+  AAH_TRY(check_tensor(dv, "dv", 16));
+  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  const size_t need = bwd_workspace(B, H, T, d, dt);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
+                need);
+  if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+
+  float* Dbuf = static_cast<float*>(workspace);
+  const aah::AttnShape s{B, H, T, d, scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool is_bf16 = dt == AAH_BF16;
+
+  DevicePlan fplan, bplan;
+  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &fplan));
+  AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &bplan));
+  hipError_t e = aah::launch_bwd_preprocess(o, dout, is_bf16, Dbuf, nullptr, s, st);
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  e = aah::launch_bwd_simple(q, k, v, dout, lse, Dbuf, is_bf16, dq, dk, dv, fplan.items, fplan.n_items, bplan.items,
+                             bplan.n_items, fplan.win, s, st);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return AAH_OK;
+}
+
+aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                        aah_work_item* items, int64_t capacity, int64_t* n_items) {
+  g_detail.clear();
+  return plan_to_host(kPlanFwd, windows, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+}
+
+aah_status aah_plan_bwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                        aah_work_item* items, int64_t capacity, int64_t* n_items) {
+  g_detail.clear();
+  return plan_to_host(kPlanBwd, windows, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+}
+
+aah_status aah_window_stats(const int32_t* windows, int H, int T, int64_t* pairs_per_batch, double* acr) {
+  g_detail.clear();
+  if (windows == nullptr || pairs_per_batch == nullptr || acr == nullptr)
+    return fail(AAH_ERR_INVALID_ARG, "NULL pointer argument");
+  if (H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "H and T must be >= 1");
+  int64_t pairs = 0;
+  double cover = 0.0;
+  for (int h = 0; h < H; ++h) {
+    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+    pairs += aah::pair_count(T, windows[h]);
+    cover += static_cast<double>(aah::effective_window(windows[h], T)) / T;
+  }
+  *pairs_per_batch = pairs;
+  *acr = cover / H;
+  return AAH_OK;
+}
+
+void aah_cache_clear(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  for (auto& kv : g_cache) {
+    (void)hipFree(kv.second.items);
+    (void)hipFree(kv.second.win);
+  }
+  g_cache.clear();
+}
+
+}  // extern "C"

@@ -1,0 +1,49 @@
+// Launch wrappers of the HIP kernels (defined in the .hip files).  Every
+// wrapper only enqueues on `stream` and returns the launch status; argument
+// checking has already happened in the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "workplan.hpp"
+
+namespace aah {
+
+// Tile shapes (rows of the stationary operand per item, rows of the streamed
+// operand per step).  The planner is called with exactly these.
+constexpr int kFwdBf16RowTile = 128;  // 4 waves x 32 query rows
+constexpr int kFwdBf16ColTile = 64;   // keys per LDS stage
+constexpr int kSimpleRowTile = 64;    // one wave, one row per lane
+constexpr int kSimpleColTile = 64;
+
+struct AttnShape {
+  int B, H, T, d;
+  float scale;          // softmax scale applied to q . k
+};
+
+// bf16 forward on MFMA (d in {32, 64, 128}).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const WorkItem* items, int n_items, const int32_t* win_eff,
+                           const AttnShape& s, hipStream_t stream);
+
+// Scalar forward for fp32 (d in {32, 64, 128}).
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const AttnShape& s, hipStream_t stream);
+
+// D_i = sum_c dO_ic * O_ic in fp32; when dq_acc != nullptr also zeroes the
+// fp32 dQ accumulator rows.  is_bf16 selects the element type of o / dout.
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D,
+                                 float* dq_acc, const AttnShape& s, hipStream_t stream);
+
+// Scalar backward (reference-grade, any supported dtype): dQ per query row
+// over the forward work list, dK/dV per key row over the backward work list.
+hipError_t launch_bwd_simple(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const float* D, bool is_bf16,
+                             void* dq, void* dk, void* dv,
+                             const WorkItem* fwd_items, int n_fwd, const WorkItem* bwd_items, int n_bwd,
+                             const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+
+}  // namespace aah

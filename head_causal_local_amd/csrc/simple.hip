@@ -1,0 +1,339 @@
+// Scalar (VALU) kernels of per-head causal local-window attention:
+//   * the fp32 forward (exact fp32 arithmetic, one query row per lane);
+//   * the backward preprocess D_i = sum_c dO_ic O_ic;
+//   * a straightforward backward (one row per lane) for fp32 and bf16.
+//
+// Operation: "Asymmetric Attention Heads" section 5.8 -- key j is visible to
+// query i iff i - W < j <= i; A = softmax(scale Q K^T + M_W), Y = A V.  The
+// backward gradients are those of sum(Y * dO):
+//   P_ij = exp(scale q_i.k_j - lse_i),  dP_ij = dO_i.v_j,  D_i = sum_j P_ij dP_ij,
+//   dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale sum_j dS_ij k_j,
+//   dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+// D_i is computed as dO_i . O_i, which equals sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace aah {
+namespace {
+
+typedef __bf16 bf16;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kRows = kSimpleRowTile;  // rows per item = lanes per workgroup
+constexpr int kCols = kSimpleColTile;  // streamed rows per LDS stage
+constexpr int kChunk = 16;             // keys scored per inner pass
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(bf16 x) { return static_cast<float>(x); }
+template <typename E> __device__ inline E from_f32(float x);
+template <> __device__ inline float from_f32<float>(float x) { return x; }
+template <> __device__ inline bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// Copy rows [r0, r0 + kCols) of a [T, D] tensor into an fp32 LDS tile; rows past T are zero.
+template <typename E, int D>
+__device__ inline void stage_rows(float* dst, const E* src, int r0, int T) {
+  for (int e = threadIdx.x; e < kCols * D; e += blockDim.x) {
+    const int row = r0 + e / D;
+    dst[e] = row < T ? to_f32(src[static_cast<size_t>(row) * D + e % D]) : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- fp32 forward
+
+template <int D>
+__global__ __launch_bounds__(kRows) void fwd_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    float* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
+    const int32_t* __restrict__ win_eff, int H, int T, float c) {
+  __shared__ float ks[kCols * D];
+  __shared__ float vs[kCols * D];
+  const WorkItem it = items[blockIdx.x];
+  if (it.bh < 0) return;
+  const int W = win_eff[it.bh % H];
+  const size_t base = static_cast<size_t>(it.bh) * T * D;
+  const int qi = it.tile * kRows + threadIdx.x;
+  const bool row_ok = qi < T;
+
+  float qr[D], acc[D];
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+    qr[x] = row_ok ? Q[base + static_cast<size_t>(qi) * D + x] : 0.f;
+    acc[x] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;  // log2-domain running max and running sum
+
+  for (int kt = it.lo; kt < it.hi; ++kt) {
+    const int k0 = kt * kCols;
+    __syncthreads();
+    stage_rows<float, D>(ks, K + base, k0, T);
+    stage_rows<float, D>(vs, V + base, k0, T);
+    __syncthreads();
+    for (int j0 = 0; j0 < kCols; j0 += kChunk) {
+      float s[kChunk];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const int key = k0 + j0 + j;
+        float dot = 0.f;
+#pragma unroll
+        for (int x = 0; x < D; ++x) dot = fmaf(qr[x], ks[(j0 + j) * D + x], dot);
+        const bool ok = key <= qi && key > qi - W && key < T;
+        s[j] = ok ? dot * c : -INFINITY;
+        mx = fmaxf(mx, s[j]);
+      }
+      const float m_new = fmaxf(m, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = exp2f(m - m_use);
+      l *= alpha;
+#pragma unroll
+      for (int x = 0; x < D; ++x) acc[x] *= alpha;
+#pragma unroll
+      for (int j = 0; j < kChunk; ++j) {
+        const float p = exp2f(s[j] - m_use);
+        l += p;
+#pragma unroll
+        for (int x = 0; x < D; ++x) acc[x] = fmaf(p, vs[(j0 + j) * D + x], acc[x]);
+      }
+      m = m_new;
+    }
+  }
+  if (!row_ok) return;
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int x = 0; x < D; ++x) O[base + static_cast<size_t>(qi) * D + x] = acc[x] * inv;
+  LSE[static_cast<size_t>(it.bh) * T + qi] = (m + log2f(l)) * kLn2;
+}
+
+// ---------------------------------------------------------------- backward preprocess
+
+// Each thread reduces one 16-byte chunk of a row; the D/E lanes of a row then
+// combine with xor-shuffles (E = elements per chunk).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO,
+                                                      float* __restrict__ Dout, float* __restrict__ dq_acc,
+                                                      int64_t rows) {
+  constexpr int kPer = 16 / sizeof(E);
+  constexpr int kLanesPerRow = D / kPer;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t row = t / kLanesPerRow;
+  const int part = static_cast<int>(t % kLanesPerRow);
+  float sum = 0.f;
+  if (row < rows) {
+    const u32x4 ov = *reinterpret_cast<const u32x4*>(O + row * D + part * kPer);
+    const u32x4 gv = *reinterpret_cast<const u32x4*>(dO + row * D + part * kPer);
+    const E* oe = reinterpret_cast<const E*>(&ov);
+    const E* ge = reinterpret_cast<const E*>(&gv);
+#pragma unroll
+    for (int x = 0; x < kPer; ++x) sum = fmaf(to_f32(oe[x]), to_f32(ge[x]), sum);
+    if (dq_acc != nullptr) {
+#pragma unroll
+      for (int x = 0; x < kPer; x += 4)
+        *reinterpret_cast<u32x4*>(dq_acc + row * D + part * kPer + x) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  if (row < rows && part == 0) Dout[row] = sum;
+}
+
+// ---------------------------------------------------------------- simple backward
+
+// dQ: one query row per lane, over the forward work list (query tile, key tiles).
+template <typename E, int D>
+__global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    E* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
+    int H, int T, float scale) {
+  __shared__ float ks[kCols * D];
+  __shared__ float vs[kCols * D];
+  const WorkItem it = items[blockIdx.x];
+  if (it.bh < 0) return;
+  const int W = win_eff[it.bh % H];
+  const size_t base = static_cast<size_t>(it.bh) * T * D;
+  const int qi = it.tile * kRows + threadIdx.x;
+  const bool row_ok = qi < T;
+  const float c = scale * kLog2e;
+
+  float qr[D], gr[D], dq[D];
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+    qr[x] = row_ok ? to_f32(Q[base + static_cast<size_t>(qi) * D + x]) : 0.f;
+    gr[x] = row_ok ? to_f32(dO[base + static_cast<size_t>(qi) * D + x]) : 0.f;
+    dq[x] = 0.f;
+  }
+  const float lse2 = row_ok ? LSE[static_cast<size_t>(it.bh) * T + qi] * kLog2e : 0.f;
+  const float Di = row_ok ? Dv[static_cast<size_t>(it.bh) * T + qi] : 0.f;
+
+  for (int kt = it.lo; kt < it.hi; ++kt) {
+    const int k0 = kt * kCols;
+    __syncthreads();
+    stage_rows<E, D>(ks, K + base, k0, T);
+    stage_rows<E, D>(vs, V + base, k0, T);
+    __syncthreads();
+    for (int j = 0; j < kCols; ++j) {
+      const int key = k0 + j;
+      if (!(key <= qi && key > qi - W && key < T)) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int x = 0; x < D; ++x) {
+        s = fmaf(qr[x], ks[j * D + x], s);
+        dp = fmaf(gr[x], vs[j * D + x], dp);
+      }
+      const float p = exp2f(fmaf(s, c, -lse2));
+      const float ds = p * (dp - Di);
+#pragma unroll
+      for (int x = 0; x < D; ++x) dq[x] = fmaf(ds, ks[j * D + x], dq[x]);
+    }
+  }
+  if (!row_ok) return;
+#pragma unroll
+  for (int x = 0; x < D; ++x) dQ[base + static_cast<size_t>(qi) * D + x] = from_f32<E>(dq[x] * scale);
+}
+
+// dK, dV: one key row per lane, over the backward work list (key tile, query tiles).
+template <typename E, int D>
+__global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
+    const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
+    const E* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
+    E* __restrict__ dK, E* __restrict__ dV, const WorkItem* __restrict__ items,
+    const int32_t* __restrict__ win_eff, int H, int T, float scale) {
+  __shared__ float qs[kCols * D];
+  __shared__ float gs[kCols * D];
+  __shared__ float ls[kCols];
+  __shared__ float ds_[kCols];
+  const WorkItem it = items[blockIdx.x];
+  if (it.bh < 0) return;
+  const int W = win_eff[it.bh % H];
+  const size_t base = static_cast<size_t>(it.bh) * T * D;
+  const size_t rbase = static_cast<size_t>(it.bh) * T;
+  const int kj = it.tile * kRows + threadIdx.x;
+  const bool row_ok = kj < T;
+  const float c = scale * kLog2e;
+
+  float kr[D], vr[D], dk[D], dv[D];
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+    kr[x] = row_ok ? to_f32(K[base + static_cast<size_t>(kj) * D + x]) : 0.f;
+    vr[x] = row_ok ? to_f32(V[base + static_cast<size_t>(kj) * D + x]) : 0.f;
+    dk[x] = 0.f;
+    dv[x] = 0.f;
+  }
+  for (int qt = it.lo; qt < it.hi; ++qt) {
+    const int q0 = qt * kCols;
+    __syncthreads();
+    stage_rows<E, D>(qs, Q + base, q0, T);
+    stage_rows<E, D>(gs, dO + base, q0, T);
+    for (int e = threadIdx.x; e < kCols; e += blockDim.x) {
+      const int row = q0 + e;
+      ls[e] = row < T ? LSE[rbase + row] * kLog2e : 0.f;
+      ds_[e] = row < T ? Dv[rbase + row] : 0.f;
+    }
+    __syncthreads();
+    for (int i = 0; i < kCols; ++i) {
+      const int qrow = q0 + i;
+      if (!(kj <= qrow && kj > qrow - W && qrow < T && row_ok)) continue;
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int x = 0; x < D; ++x) {
+        s = fmaf(qs[i * D + x], kr[x], s);
+        dp = fmaf(gs[i * D + x], vr[x], dp);
+      }
+      const float p = exp2f(fmaf(s, c, -ls[i]));
+      const float dsv = p * (dp - ds_[i]);
+#pragma unroll
+      for (int x = 0; x < D; ++x) {
+        dv[x] = fmaf(p, gs[i * D + x], dv[x]);
+        dk[x] = fmaf(dsv, qs[i * D + x], dk[x]);
+      }
+    }
+  }
+  if (!row_ok) return;
+#pragma unroll
+  for (int x = 0; x < D; ++x) {
+    dK[base + static_cast<size_t>(kj) * D + x] = from_f32<E>(dk[x] * scale);
+    dV[base + static_cast<size_t>(kj) * D + x] = from_f32<E>(dv[x]);
+  }
+}
+
+template <int D>
+hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, float* lse,
+                     const WorkItem* items, int n_items, const int32_t* win_eff,
+                     const AttnShape& s, hipStream_t stream) {
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(n_items), dim3(kRows), 0, stream, q, k, v, o, lse, items,
+                     win_eff, s.H, s.T, s.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t pre_d(const void* o, const void* dout, float* Dout, float* dq_acc, const AttnShape& s,
+                 hipStream_t stream) {
+  constexpr int kLanesPerRow = D / (16 / sizeof(E));
+  const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.T;
+  const int64_t threads = rows * kLanesPerRow;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
+                     static_cast<const E*>(o), static_cast<const E*>(dout), Dout, dq_acc, rows);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t bwd_simple_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                        const float* D_, void* dq, void* dk, void* dv, const WorkItem* fwd_items, int n_fwd,
+                        const WorkItem* bwd_items, int n_bwd, const int32_t* win_eff, const AttnShape& s,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_simple_kernel<E, D>), dim3(n_fwd), dim3(kRows), 0, stream,
+                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+                     static_cast<const E*>(dout), lse, D_, static_cast<E*>(dq), fwd_items, win_eff, s.H, s.T,
+                     s.scale);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkdv_simple_kernel<E, D>), dim3(n_bwd), dim3(kRows), 0, stream,
+                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
+                     static_cast<const E*>(dout), lse, D_, static_cast<E*>(dk), static_cast<E*>(dv), bwd_items,
+                     win_eff, s.H, s.T, s.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                          const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const AttnShape& s, hipStream_t stream) {
+  switch (s.d) {
+    case 32: return fwd_f32_d<32>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
+    case 64: return fwd_f32_d<64>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
+    case 128: return fwd_f32_d<128>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D, float* dq_acc,
+                                 const AttnShape& s, hipStream_t stream) {
+  switch (s.d) {
+    case 32: return is_bf16 ? pre_d<bf16, 32>(o, dout, D, dq_acc, s, stream) : pre_d<float, 32>(o, dout, D, dq_acc, s, stream);
+    case 64: return is_bf16 ? pre_d<bf16, 64>(o, dout, D, dq_acc, s, stream) : pre_d<float, 64>(o, dout, D, dq_acc, s, stream);
+    case 128: return is_bf16 ? pre_d<bf16, 128>(o, dout, D, dq_acc, s, stream) : pre_d<float, 128>(o, dout, D, dq_acc, s, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_simple(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                             const float* D, bool is_bf16, void* dq, void* dk, void* dv,
+                             const WorkItem* fwd_items, int n_fwd, const WorkItem* bwd_items, int n_bwd,
+                             const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
+#define AAH_SIMPLE(E, DD) \
+  bwd_simple_d<E, DD>(q, k, v, dout, lse, D, dq, dk, dv, fwd_items, n_fwd, bwd_items, n_bwd, win_eff, s, stream)
+  switch (s.d) {
+    case 32: return is_bf16 ? AAH_SIMPLE(bf16, 32) : AAH_SIMPLE(float, 32);
+    case 64: return is_bf16 ? AAH_SIMPLE(bf16, 64) : AAH_SIMPLE(float, 64);
+    case 128: return is_bf16 ? AAH_SIMPLE(bf16, 128) : AAH_SIMPLE(float, 128);
+    default: return hipErrorInvalidValue;
+  }
+#undef AAH_SIMPLE
+}
+
+}  // namespace aah

@@ -1,0 +1,172 @@
+/*
+ * aah_attn.h -- C ABI of the per-head causal local-window attention library
+ * (the execution branch of Asymmetric Attention Heads, AAH-v3) for AMD MI355X
+ * (gfx950).
+ *
+ * Operation.  "Asymmetric Attention Heads: Structured Head-Wise Context
+ * Allocation for Transformer Attention", section 5.8 (Head mapping and
+ * execution): every head h has its own causal local window W_h; key t_k is
+ * visible to query t_q iff t_q - W_h + 1 <= t_k <= t_q, and
+ *     A = softmax(Q K^T * scale + M_W),   Y = A V
+ * with the softmax scale 1/sqrt(d_h) of section 4.  W_h >= T is standard
+ * causal attention (sections 5.2 and 5.8).  The pages bucket heads by window,
+ * run each bucket and scatter the results back to head order (Figure 1); here
+ * one launch runs every head and each work item writes its own (b, h) slice,
+ * so head order is preserved without gather or scatter copies.  A bucket is
+ * never silently run by another backend (section 7.7): unsupported inputs
+ * return AAH_ERR_UNSUPPORTED.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, T, d] tensors
+ *     (d fastest), all of one dtype `dt`, device pointers aligned to 16 bytes.
+ *     LSE and the backward's D are fp32 [B, H, T].
+ *   - `windows` is a HOST pointer to int32[H], one window per head, shared by
+ *     every batch entry (section 5.8 maps one decision per head).  Each entry
+ *     must be >= 1; entries above T act as T.  No lower clamp is applied: the
+ *     pages' W_min = 512 belongs to the window controller, not to execution.
+ *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
+ *     stream).  Calls only enqueue work on it and return; they never
+ *     synchronise the device, except that the first call for a new
+ *     (B, H, T, dtype, d, windows) combination builds its work list on the
+ *     host and uploads it once (hipMalloc + hipMemcpy), to be reused by every
+ *     later call with the same combination.
+ *   - The caller allocates and owns every tensor, the workspace and the
+ *     stream.  The library owns only its cached work lists, released by
+ *     aah_cache_clear().
+ *   - Every argument check runs before any HIP call; on an error nothing is
+ *     written to any output and the call returns a status other than AAH_OK.
+ *     aah_last_error_detail() then describes the failure (thread-local).
+ *   - Supported: dt = AAH_BF16 with d in {32, 64, 128}; dt = AAH_F32 with d in
+ *     {32, 64, 128}; any T >= 1 (ragged tails are masked).
+ */
+#ifndef AAH_ATTN_H
+#define AAH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AAH_ABI_VERSION 1
+
+typedef enum {
+  AAH_OK = 0,
+  AAH_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, window < 1, misalignment, non-finite scale */
+  AAH_ERR_UNSUPPORTED = 2,  /* dtype / head dim combination without a kernel */
+  AAH_ERR_WORKSPACE = 3,    /* workspace smaller than aah_attn_workspace_size() */
+  AAH_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} aah_status;
+
+typedef enum { AAH_BF16 = 0, AAH_F32 = 1 } aah_dtype;
+
+typedef void* aah_stream_t;
+
+/* One unit of work: a (batch*H + head) index, a row tile of the stationary
+ * operand and the half-open range [lo, hi) of tiles of the streamed operand
+ * it must visit.  Forward items: tile = query tile, [lo, hi) = key/value
+ * tiles.  Backward items: tile = key/value tile, [lo, hi) = query tiles.
+ * bh = -1 marks a padding slot that does nothing. */
+typedef struct {
+  int32_t bh;
+  int32_t tile;
+  int32_t lo;
+  int32_t hi;
+} aah_work_item;
+
+/* ABI version of the loaded library (AAH_ABI_VERSION). */
+int aah_abi_version(void);
+
+/* Static name of a status code; never NULL. */
+const char* aah_status_string(aah_status status);
+
+/* Thread-local description of the last failed call on this thread ("" if none). */
+const char* aah_last_error_detail(void);
+
+/*
+ * Forward pass (section 5.8).  Reads q, k, v [B,H,T,d] of dtype dt; writes
+ * o [B,H,T,d] (dtype dt) and lse [B,H,T] (fp32): lse[b,h,i] is the natural log
+ * of sum_j exp(scale * q_i . k_j) over the window of row i.  Accumulation and
+ * softmax run in fp32 whatever dt is; bf16 outputs are rounded to nearest even.
+ * The forward needs no workspace: pass workspace = NULL, workspace_bytes = 0
+ * (a non-NULL workspace is accepted and ignored).
+ */
+aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
+                        const int32_t* windows, int B, int H, int T, int d,
+                        aah_dtype dt, float scale, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes,
+                        aah_stream_t stream);
+
+/*
+ * Backward pass: gradients of sum(O * dout) with respect to q, k and v, given
+ * the forward's o and lse (the log-sum-exp saved by aah_attn_fwd with the same
+ * scale and windows).  Writes dq, dk, dv [B,H,T,d] of dtype dt (fully
+ * overwritten).  Needs a device workspace of at least
+ * aah_attn_workspace_size(B, H, T, d, dt, 1) bytes, 256-byte aligned; its
+ * contents on entry do not matter and are clobbered.  With dt = AAH_BF16 the
+ * dq accumulation uses fp32 atomics, so dq may differ in the last bits
+ * between runs; dk and dv are deterministic.
+ */
+aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
+                        const void* o, const void* dout, const float* lse,
+                        const int32_t* windows, int B, int H, int T, int d,
+                        aah_dtype dt, float scale, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes,
+                        aah_stream_t stream);
+
+/* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
+ * 0 for invalid arguments. */
+size_t aah_attn_workspace_size(int B, int H, int T, int d, aah_dtype dt, int is_bwd);
+
+/* Tile shape used by the kernels for (dt, d, is_bwd): rows of the stationary
+ * operand per item and rows of the streamed operand per inner step. */
+aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* col_tile);
+
+/*
+ * Host-only work-list builders (no HIP call; usable without a GPU).
+ *
+ * Forward: for each (b, h, query tile qt) with rows [qt*q_tile, min(T, (qt+1)*q_tile)),
+ * the keys needed are [max(0, q0 - W + 1), q1 - 1], i.e. key tiles
+ * [floor(max(0, q0 - W + 1) / kv_tile), floor((q1 - 1) / kv_tile) + 1).
+ * Backward: for each (b, h, key tile kt) with keys [k0, k1), the queries that
+ * see them are [k0, min(T, k1 + W - 1)), i.e. query tiles
+ * [floor(k0 / q_tile), floor((min(T, k1 + W - 1) - 1) / q_tile) + 1).
+ * W = min(windows[h], T).  Tiles wholly outside every row's window are never
+ * listed.  Items are grouped into `n_queues` queues (heads are dealt to
+ * queues longest-total-first, each to the least-loaded queue); each queue is
+ * sorted by item cost (hi - lo) descending, ties by (bh, tile) ascending; the
+ * output interleaves the queues so that slot s belongs to queue s % n_queues,
+ * padding short queues with bh = -1 slots.  With n_queues = 8 this matches
+ * the round-robin placement of workgroups on MI355X's eight XCDs, so the
+ * items of one head share an L2.
+ *
+ * Writes up to `capacity` items to `items` (may be NULL when capacity = 0)
+ * and always stores the full slot count in *n_items; returns
+ * AAH_ERR_INVALID_ARG if capacity is too small (after setting *n_items).
+ */
+aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T,
+                        int q_tile, int kv_tile, int n_queues,
+                        aah_work_item* items, int64_t capacity, int64_t* n_items);
+
+aah_status aah_plan_bwd(const int32_t* windows, int B, int H, int T,
+                        int q_tile, int kv_tile, int n_queues,
+                        aah_work_item* items, int64_t capacity, int64_t* n_items);
+
+/*
+ * Coverage of a window vector (section 5.10): the exact in-window query/key
+ * pair count of one batch entry, sum_h sum_{t=1}^{T} min(t, W_h), and the
+ * Attention Coverage Ratio sum_h T * W_h / (H * T^2), both with W_h = min(W_h, T).
+ */
+aah_status aah_window_stats(const int32_t* windows, int H, int T,
+                            int64_t* pairs_per_batch, double* acr);
+
+/* Free every cached device work list.  Not thread-safe against concurrent
+ * aah_attn_* calls that may be using them. */
+void aah_cache_clear(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AAH_ATTN_H */

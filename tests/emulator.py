@@ -1,0 +1,78 @@
+"""fp64 tile-loop emulator of the device work lists (a test tool, not the oracle).
+
+It executes the C++ planner's forward work list the way the kernels do --
+online softmax over the listed key tiles, mask evaluated per element -- and
+the backward work list key-tile by key-tile, so that a tile-range bug in the
+planner shows up as a difference from the oracle on the CPU.  It shares no
+code with the oracle and does not import it.
+"""
+import numpy as np
+
+
+def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile):
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, T, d = q.shape
+    O = np.full((B, H, T, d), np.nan)
+    L = np.full((B, H, T), np.nan)
+    for bh, qt, lo, hi in items:
+        if bh < 0:
+            continue
+        b, h = divmod(int(bh), H)
+        W = min(int(windows[h]), T)
+        rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        acc = np.zeros((len(rows), d))
+        for kt in range(lo, hi):
+            keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
+            s = scale * q[b, h, rows] @ k[b, h, keys].T
+            ok = (keys[None, :] <= rows[:, None]) & (keys[None, :] > rows[:, None] - W)
+            s = np.where(ok, s, -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            m_use = np.where(np.isneginf(m_new), 0.0, m_new)
+            alpha = np.exp(m - m_use)
+            p = np.exp(s - m_use[:, None])
+            l = l * alpha + p.sum(axis=1)
+            acc = acc * alpha[:, None] + p @ v[b, h, keys]
+            m = m_new
+        O[b, h, rows] = acc / l[:, None]
+        L[b, h, rows] = m + np.log(l)
+    return O, L
+
+
+def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile):
+    """KV-stationary backward over the backward work list: dK, dV per key tile,
+    dQ accumulated from every key tile (as the device's atomic dQ does)."""
+    q, k, v, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, lse))
+    B, H, T, d = q.shape
+    dq = np.zeros_like(q)
+    dk = np.full_like(k, np.nan)
+    dv = np.full_like(v, np.nan)
+    # D_i = dO_i . O_i, with O recomputed from lse over the full window (as the preprocess does from O).
+    for bh, kt, lo, hi in items:
+        if bh < 0:
+            continue
+        b, h = divmod(int(bh), H)
+        W = min(int(windows[h]), T)
+        keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
+        dk_t = np.zeros((len(keys), d))
+        dv_t = np.zeros((len(keys), d))
+        for qt in range(lo, hi):
+            rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
+            s = scale * q[b, h, rows] @ k[b, h, keys].T
+            ok = (keys[None, :] <= rows[:, None]) & (keys[None, :] > rows[:, None] - W)
+            p = np.where(ok, np.exp(s - lse[b, h, rows][:, None]), 0.0)
+            # D for these rows: sum over the row's whole window of P * dP
+            Drow = np.empty(len(rows))
+            for n, i in enumerate(rows):
+                kk = np.arange(max(0, i - W + 1), i + 1)
+                pi = np.exp(scale * k[b, h, kk] @ q[b, h, i] - lse[b, h, i])
+                Drow[n] = pi @ (v[b, h, kk] @ do[b, h, i])
+            dp = do[b, h, rows] @ v[b, h, keys].T
+            ds = p * (dp - Drow[:, None])
+            dv_t += p.T @ do[b, h, rows]
+            dk_t += scale * ds.T @ q[b, h, rows]
+            dq[b, h, rows] += scale * ds @ k[b, h, keys]
+        dk[b, h, keys] = dk_t
+        dv[b, h, keys] = dv_t
+    return dq, dk, dv

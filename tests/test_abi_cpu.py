@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: every declared symbol is exported, argument
+validation returns the documented status before any HIP call, and the
+coverage helpers agree with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import head_causal_local_amd as aah
+import oracle
+from head_causal_local_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "aah_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aah_\w+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = _lib.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_abi_version_and_status_strings():
+    lib = _lib.lib()
+    assert lib.aah_abi_version() == 1
+    for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
+                       (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
+        assert lib.aah_status_string(code) == name
+    assert lib.aah_status_string(99) == b"AAH_ERR_UNKNOWN"
+
+
+FAKE = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
+
+
+def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, scale=0.125):
+    w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
+    H = len(w) if H is None else H
+    wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(w) else None
+    return _lib.lib().aah_attn_fwd(q, k, v, wp, B, H, T, d, dt, scale, o, lse, None, 0, None)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(windows=[4, 0]), 1),                    # window < 1
+    (dict(windows=[4, -3]), 1),
+    (dict(windows=[4], B=0), 1),                  # B < 1
+    (dict(windows=[4], T=0), 1),
+    (dict(windows=[4], d=48), 2),                 # unsupported head dim
+    (dict(windows=[4], d=256), 2),
+    (dict(windows=[4], dt=7), 2),                 # unknown dtype
+    (dict(windows=[4], q=0), 1),                  # NULL tensor
+    (dict(windows=[4], lse=0), 1),
+    (dict(windows=[4], v=FAKE + 8), 1),           # misaligned
+    (dict(windows=[4], lse=FAKE + 2), 1),
+    (dict(windows=[4], scale=float("nan")), 1),
+    (dict(windows=[4], scale=float("inf")), 1),
+])
+def test_fwd_validation(kwargs, status):
+    st = _fwd(**kwargs)
+    assert st == status
+    assert _lib.lib().aah_last_error_detail().decode() != ""
+
+
+def test_fwd_null_windows():
+    st = _lib.lib().aah_attn_fwd(FAKE, FAKE, FAKE, None, 1, 1, 8, 64, 0, 0.1, FAKE, FAKE, None, 0, None)
+    assert st == 1
+
+
+def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE):
+    w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
+    H = len(w)
+    need = aah.workspace_size(B, H, T, d, "bf16" if dt == 0 else "f32")
+    ws_bytes = need if ws_bytes is None else ws_bytes
+    return _lib.lib().aah_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), B, H, T, d, dt, 0.125,
+                                   dq, FAKE, FAKE, ws, ws_bytes, None)
+
+
+def test_bwd_validation():
+    assert _bwd([4, 0]) == 1
+    assert _bwd([4], ws=None) == 3
+    assert _bwd([4], ws_bytes=10) == 3
+    assert _bwd([4], dq=0) == 1
+    assert _bwd([4], ws=FAKE + 16) == 1       # workspace must be 256-byte aligned
+    assert _bwd([4], d=40) == 2
+
+
+def test_workspace_sizes():
+    B, H, T, d = 4, 32, 4096, 64
+    rows = B * H * T
+    assert aah.workspace_size(B, H, T, d, "bf16", is_bwd=False) == 0
+    assert aah.workspace_size(B, H, T, d, "bf16") == rows * 4 + rows * d * 4
+    assert aah.workspace_size(B, H, T, d, "f32") == rows * 4
+    assert aah.workspace_size(1, 1, 3, 32, "f32") == 256           # rounded to 256 bytes
+    assert _lib.lib().aah_attn_workspace_size(0, 1, 1, 64, 0, 1) == 0
+    assert _lib.lib().aah_attn_workspace_size(1, 1, 1, 48, 0, 1) == 0
+
+
+def test_tile_shape():
+    assert aah.tile_shape("bf16", 64, False) == (128, 64)
+    r, c = aah.tile_shape("f32", 32, False)
+    assert r >= 1 and c >= 1
+    with pytest.raises(aah.AahError):
+        aah.tile_shape("bf16", 48, False)
+
+
+@pytest.mark.parametrize("T,windows", [(4096, [512, 1024, 2048, 4096]), (257, [1, 2, 256, 257, 300]),
+                                       (1, [1, 5])])
+def test_window_stats_match_oracle(T, windows):
+    pairs, acr = aah.window_stats(windows, T)
+    assert pairs == sum(oracle.pair_count_ref(T, w) for w in windows)
+    assert abs(acr - oracle.acr_ref(windows, T)) < 1e-15
+
+
+def test_window_stats_rejects_bad_window():
+    with pytest.raises(aah.AahError) as e:
+        aah.window_stats([3, 0], 16)
+    assert e.value.status == 1
+
+
+def test_plan_capacity_reporting():
+    lib = _lib.lib()
+    w = np.array([5, 9], dtype=np.int32)
+    n = ctypes.c_int64()
+    st = lib.aah_plan_fwd(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 2, 100, 16, 16, 8, None, 0,
+                          ctypes.byref(n))
+    assert st == 1 and n.value >= 2 * 2 * 7

@@ -1,0 +1,229 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Tolerances: fp32 workloads max-abs 1e-5; bf16 outputs max-abs 1e-2 (per
+element max(1e-2, 2^-8 |reference|): above |O| = 2.56 a bf16 output cannot be
+held to 1e-2 by rounding alone, since its spacing there is 2^-7 |O| or more);
+gradients 3e-2 x max |gradient|.  The log-sum-exp is computed in fp32 from exactly
+represented inputs; its bound (1e-3 absolute for bf16 inputs, 1e-5 for fp32)
+follows from fp32 accumulation over at most 4096 terms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_causal_local_amd as aah
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+O_TOL_BF16 = 1e-2
+LSE_TOL_BF16 = 1e-3
+TOL_F32 = 1e-5
+GRAD_REL = 3e-2
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a HIP device")
+
+
+def dev(wl, key):
+    """Device copy of a workload tensor with exactly the generator's bits."""
+    if wl.dtype == "bf16":
+        return torch.from_numpy(wl.bits[key].view(np.int16)).view(torch.bfloat16).to("cuda")
+    return torch.from_numpy(getattr(wl, key)).to("cuda")
+
+
+def assert_bf16_close(got, ref):
+    bound = np.maximum(O_TOL_BF16, np.abs(ref) * 2.0 ** -8)
+    excess = np.abs(got - ref) - bound
+    assert excess.max() <= 0, f"max |err| {np.abs(got - ref).max():.3e}, worst excess {excess.max():.3e}"
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+_CACHE = {}
+
+
+def workload(idx):
+    if idx not in _CACHE:
+        _CACHE[idx] = synth.make_workload(idx)
+    return _CACHE[idx]
+
+
+def run_fwd(wl):
+    q, k, v = dev(wl, "q"), dev(wl, "k"), dev(wl, "v")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+# ---------------------------------------------------------------- forward
+
+def test_tiny_fp32_workload():
+    """The tiny fp32 workload (B=1 H=4 T=256 d=32, windows 16/32/64/256) at max-abs 1e-5."""
+    _require_gpu()
+    wl = workload(0)
+    o, lse = run_fwd(wl)
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale)
+    assert np.abs(host(o) - O).max() < TOL_F32
+    assert np.abs(host(lse) - L).max() < TOL_F32
+
+
+BF16_SHAPES = [
+    # B, H, T, d, windows        (several tiles, ragged tails, windows below/at/above T)
+    (2, 5, 333, 64, [1, 7, 64, 200, 1000]),
+    (1, 3, 200, 32, [5, 100, 200]),
+    (1, 2, 300, 128, [3, 300]),
+    (1, 4, 1, 64, [1, 2, 3, 4]),
+    (1, 3, 129, 64, [129, 128, 64]),
+    (2, 2, 640, 64, [512, 65]),
+]
+
+
+@pytest.mark.parametrize("B,H,T,d,windows", BF16_SHAPES)
+def test_bf16_forward_small(B, H, T, d, windows):
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=B * 1000 + T, backward=False)
+    o, lse = run_fwd(wl)
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale)
+    assert_bf16_close(host(o), O)
+    assert np.abs(host(lse) - L).max() < LSE_TOL_BF16
+
+
+@pytest.mark.parametrize("B,H,T,d,windows", [(1, 3, 200, 32, [5, 100, 200]), (2, 2, 130, 64, [1, 64]),
+                                             (1, 2, 70, 128, [3, 70])])
+def test_fp32_forward_small(B, H, T, d, windows):
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="f32", seed=7, backward=False)
+    o, lse = run_fwd(wl)
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale)
+    assert np.abs(host(o) - O).max() < TOL_F32
+    assert np.abs(host(lse) - L).max() < TOL_F32
+
+
+def test_window_one_returns_v_exactly():
+    _require_gpu()
+    wl = synth.random_workload(2, 3, 150, 64, [1, 1, 1], dtype="bf16", seed=5, backward=False)
+    o, _ = run_fwd(wl)
+    assert torch.equal(o, dev(wl, "v"))
+
+
+def test_forward_deterministic_and_head_permutation():
+    """Two runs are bitwise equal; permuting heads permutes outputs bitwise (bucket/scatter commutes)."""
+    _require_gpu()
+    wl = synth.random_workload(2, 6, 700, 64, [512, 1, 4096, 64, 700, 128], dtype="bf16", seed=9, backward=False)
+    q, k, v = dev(wl, "q"), dev(wl, "k"), dev(wl, "v")
+    o1, l1 = aah.attn_fwd(q, k, v, wl.windows)
+    o2, l2 = aah.attn_fwd(q, k, v, wl.windows)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    perm = [4, 2, 0, 5, 1, 3]
+    op, lp = aah.attn_fwd(q[:, perm].contiguous(), k[:, perm].contiguous(), v[:, perm].contiguous(),
+                          wl.windows[perm])
+    torch.cuda.synchronize()
+    assert torch.equal(op, o1[:, perm]) and torch.equal(lp, l1[:, perm])
+
+
+SAMPLE_ROWS = [0, 1, 31, 32, 63, 64, 127, 128, 511, 512, 513, 1000, 1023, 1024, 2047, 2048, 3000, 4095]
+
+
+def _check_sampled_rows(wl, o, lse, heads):
+    on, ln = host(o), host(lse)
+    worst = 0.0
+    for b, h in heads:
+        Or, Lr = oracle.attn_fwd_rows_ref(wl.q[b, h], wl.k[b, h], wl.v[b, h], int(wl.windows[h]), wl.scale,
+                                          SAMPLE_ROWS)
+        assert_bf16_close(on[b, h, SAMPLE_ROWS], Or)
+        assert np.abs(ln[b, h, SAMPLE_ROWS] - Lr).max() < LSE_TOL_BF16, (b, h)
+        worst = max(worst, float(np.abs(on[b, h, SAMPLE_ROWS] - Or).max()))
+    return worst
+
+
+def test_single_layer_workload_sampled():
+    """B=1 H=16 T=4096 d=64 bf16, windows drawn from {512,...,4096}: every head, sampled rows."""
+    _require_gpu()
+    wl = workload(1)
+    o, lse = run_fwd(wl)
+    _check_sampled_rows(wl, o, lse, [(0, h) for h in range(wl.H)])
+    assert torch.isfinite(o.float()).all()
+
+
+def test_1b_layer_workload_sampled():
+    """B=4 H=32 T=4096 d=64 bf16 with the grouped window hierarchy: sampled heads and rows."""
+    _require_gpu()
+    wl = workload(3)
+    o, lse = run_fwd(wl)
+    heads = [(b, h) for b in (0, 3) for h in (0, 5, 12, 17, 28, 31)]
+    _check_sampled_rows(wl, o, lse, heads)
+    assert torch.isfinite(o.float()).all()
+
+
+@pytest.mark.parametrize("idx", ["4a", "4b", "4c"])
+def test_coverage_controls_sampled(idx):
+    _require_gpu()
+    wl = synth.make_workload(idx)
+    o, lse = run_fwd(wl)
+    _check_sampled_rows(wl, o, lse, [(1, 0), (2, 1), (3, 30), (0, 31)])
+
+
+# ---------------------------------------------------------------- backward
+
+def _grad_check(got, ref, rel=GRAD_REL, name=""):
+    scale = max(np.abs(ref).max(), 1e-12)
+    err = np.abs(got - ref).max()
+    assert err <= rel * scale, f"{name}: max err {err:.3e} vs bound {rel * scale:.3e}"
+
+
+@pytest.mark.parametrize("B,H,T,d,windows", [(1, 3, 200, 64, [1, 17, 200]), (2, 2, 333, 64, [64, 500]),
+                                             (1, 2, 150, 32, [3, 150]), (1, 2, 140, 128, [9, 140])])
+def test_bf16_backward_small(B, H, T, d, windows):
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=11 + T, backward=True)
+    q, k, v, do = dev(wl, "q"), dev(wl, "k"), dev(wl, "v"), dev(wl, "do")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows)
+    dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, wl.do)
+    _grad_check(host(dq), rq, name="dq")
+    _grad_check(host(dk), rk, name="dk")
+    _grad_check(host(dv), rv, name="dv")
+
+
+@pytest.mark.parametrize("B,H,T,d,windows", [(1, 3, 200, 32, [1, 17, 200]), (1, 2, 130, 64, [64, 500])])
+def test_fp32_backward_small(B, H, T, d, windows):
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="f32", seed=3 + T, backward=True)
+    q, k, v, do = dev(wl, "q"), dev(wl, "k"), dev(wl, "v"), dev(wl, "do")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows)
+    dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
+    torch.cuda.synchronize()
+    rq, rk, rv = oracle.attn_bwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, wl.do)
+    _grad_check(host(dq), rq, rel=1e-4, name="dq")
+    _grad_check(host(dk), rk, rel=1e-4, name="dk")
+    _grad_check(host(dv), rv, rel=1e-4, name="dv")
+
+
+def test_1b_layer_backward_sampled_heads():
+    """Full-size B=4 H=32 T=4096 d=64 backward; heads of every window class checked in full."""
+    _require_gpu()
+    wl = workload(3)
+    q, k, v, do = dev(wl, "q"), dev(wl, "k"), dev(wl, "v"), dev(wl, "do")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows)
+    dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
+    torch.cuda.synchronize()
+    distinct = {}
+    for h, w in enumerate(wl.windows):
+        distinct.setdefault(int(w), h)
+    heads = [(b, h) for b, h in zip((0, 1, 2, 3), sorted(distinct.values()))]
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rq, rk, rv = oracle.attn_bwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, wl.do[sl])
+        _grad_check(host(dq[sl]), rq, name=f"dq b{b} h{h}")
+        _grad_check(host(dk[sl]), rk, name=f"dk b{b} h{h}")
+        _grad_check(host(dv[sl]), rv, name=f"dv b{b} h{h}")
+    for t in (dq, dk, dv):
+        assert torch.isfinite(t.float()).all()
