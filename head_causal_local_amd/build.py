@@ -25,7 +25,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 HOST_ONLY = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]
 
-SOURCES = ["workplan.cpp", "aah_api.cpp", "fwd_bf16.hip", "simple.hip"]
+SOURCES = ["workplan.cpp", "aah_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "simple.hip"]
 
 
 def _compile(src: str) -> str:

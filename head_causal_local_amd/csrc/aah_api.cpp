@@ -140,9 +140,14 @@ void fwd_tiles(aah_dtype dt, int* row, int* col) {
   }
 }
 
-void bwd_tiles(aah_dtype /*dt*/, int* row, int* col) {
-  *row = aah::kSimpleRowTile;
-  *col = aah::kSimpleColTile;
+void bwd_tiles(aah_dtype dt, int* row, int* col) {
+  if (dt == AAH_BF16) {
+    *row = aah::kBwdBf16RowTile;
+    *col = aah::kBwdBf16ColTile;
+  } else {
+    *row = aah::kSimpleRowTile;
+    *col = aah::kSimpleColTile;
+  }
 }
 
 // Workspace layout of the backward: D (fp32 [B,H,T]) at offset 0, then the fp32
@@ -268,14 +273,26 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   float* Dbuf = static_cast<float*>(workspace);
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool is_bf16 = dt == AAH_BF16;
+
+  if (dt == AAH_BF16) {
+    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_d_bytes(B, H, T));
+    DevicePlan bplan;
+    AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, aah::kBwdBf16RowTile, aah::kBwdBf16ColTile, &bplan));
+    hipError_t e = aah::launch_bwd_preprocess(o, dout, true, Dbuf, dq_acc, s, st);
+    if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+    e = aah::launch_bwd_bf16(q, k, v, dout, lse, Dbuf, dk, dv, dq_acc, bplan.items, bplan.n_items, bplan.win, s, st);
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
+    e = aah::launch_dq_convert(dq_acc, dq, s, st);
+    if (e != hipSuccess) return hip_fail(e, "dq convert launch");
+    return AAH_OK;
+  }
 
   DevicePlan fplan, bplan;
   AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &fplan));
   AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &bplan));
-  hipError_t e = aah::launch_bwd_preprocess(o, dout, is_bf16, Dbuf, nullptr, s, st);
+  hipError_t e = aah::launch_bwd_preprocess(o, dout, false, Dbuf, nullptr, s, st);
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  e = aah::launch_bwd_simple(q, k, v, dout, lse, Dbuf, is_bf16, dq, dk, dv, fplan.items, fplan.n_items, bplan.items,
+  e = aah::launch_bwd_simple(q, k, v, dout, lse, Dbuf, false, dq, dk, dv, fplan.items, fplan.n_items, bplan.items,
                              bplan.n_items, fplan.win, s, st);
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return AAH_OK;

@@ -15,6 +15,8 @@ namespace aah {
 // operand per step).  The planner is called with exactly these.
 constexpr int kFwdBf16RowTile = 128;  // 4 waves x 32 query rows
 constexpr int kFwdBf16ColTile = 64;   // keys per LDS stage
+constexpr int kBwdBf16RowTile = 128;  // 4 waves x 32 keys per item
+constexpr int kBwdBf16ColTile = 64;   // queries per step
 constexpr int kSimpleRowTile = 64;    // one wave, one row per lane
 constexpr int kSimpleColTile = 64;
 
@@ -37,6 +39,16 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
 // fp32 dQ accumulator rows.  is_bf16 selects the element type of o / dout.
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D,
                                  float* dq_acc, const AttnShape& s, hipStream_t stream);
+
+// bf16 backward on MFMA: dK, dV written directly, dQ accumulated into the
+// zeroed fp32 dq_acc with atomics (items from the backward planner with
+// kBwdBf16RowTile keys per item and kBwdBf16ColTile queries per step).
+hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const float* D, void* dk, void* dv, float* dq_acc, const WorkItem* items, int n_items,
+                           const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+
+// dq = bf16(dq_acc), elementwise over B*H*T*d.
+hipError_t launch_dq_convert(const float* dq_acc, void* dq, const AttnShape& s, hipStream_t stream);
 
 // Scalar backward (reference-grade, any supported dtype): dQ per query row
 // over the forward work list, dK/dV per key row over the backward work list.
