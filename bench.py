@@ -8,8 +8,9 @@ preprocess and the backward kernels, on the 1B-scale layer workload
 from {512, 1024, 2048, 4096} with P = (.5, .25, .125, .125); seed 0).
 
 Effective FLOPs count in-window query/key pairs only: 4*d per pair forward
-(Q K^T and P V) and 10*d per pair backward (recomputed Q K^T, dO V^T, P^T dO,
-dS K, dS^T Q).  Pairs per head = sum_{t=1}^{T} min(t, W_h).
+(Q K^T and P V) and 10*d per pair backward (Q K^T, dO V^T, P^T dO, dS K,
+dS^T Q); the backward kernels recompute Q K^T and dO V^T once more for dQ, which
+is not counted.  Pairs per head = sum_{t=1}^{T} min(t, W_h).
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -36,7 +37,47 @@ def parse():
     ap.add_argument("--workload", default="3", help="catalogued workload id (default 3: fwd+bwd 1B-scale layer)")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a device-to-device copy of a known size (to scale HBM byte counters)")
     return ap.parse_args()
+
+
+COPY_BYTES = 512 * 1024 * 1024
+
+
+def calibrate_copy(steps):
+    """A plain copy of COPY_BYTES: counter readings on it convert FETCH_SIZE/WRITE_SIZE to bytes."""
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                      "launches": steps}), flush=True)
+
+
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel<64>": "head_causal_local_amd/csrc/fwd_bf16.hip",
+    "bwd_dkdv_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "bwd_dq_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from profiles/hbm_traffic.txt, if taken on the current kernel source."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "hbm_traffic.txt")
+    src = KERNEL_SOURCES.get(kernel)
+    if src is None or not os.path.exists(path):
+        return None
+    sha = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()[:16]
+    for line in open(path):
+        parts = line.split()
+        if len(parts) == 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == sha:
+            return int(parts[2]) + int(parts[3])
+    return None
 
 
 def to_dev(wl, key):
@@ -91,6 +132,9 @@ def main():
     if not torch.cuda.is_available():
         print("no HIP device visible", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate_copy:
+        calibrate_copy(max(args.steps, 1))
+        return
 
     wid = int(args.workload) if args.workload.isdigit() else args.workload
     wl = synth.make_workload(wid)
@@ -107,24 +151,28 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    n_ev = 5 if with_bwd else 2
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
         aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        mark(1)
         if with_bwd:
-            aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, dq=dq, dk=dk, dv=dv, workspace=ws,
-                         stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+            aah.attn_bwd_preprocess(o, do, ws, stream=stream)
+            mark(2)
+            aah.attn_bwd_dkdv(q, k, v, do, lse, wl.windows, dk, dv, ws, wl.scale, stream=stream)
+            mark(3)
+            aah.attn_bwd_dq(q, k, v, do, lse, wl.windows, dq, ws, wl.scale, stream=stream)
+            mark(4)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -132,8 +180,14 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in events])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in events]) if with_bwd else np.zeros(1)
+    def span(a, b):
+        return np.array([e[a].elapsed_time(e[b]) for e in events])
+
+    fwd_ms = span(0, 1)
+    pre_ms = span(1, 2) if with_bwd else np.zeros(1)
+    dkdv_ms = span(2, 3) if with_bwd else np.zeros(1)
+    dq_ms = span(3, 4) if with_bwd else np.zeros(1)
+    bwd_ms = span(1, 4) if with_bwd else np.zeros(1)
     ms_per_step = wall * 1e3 / args.steps
 
     pairs_b, acr = aah.window_stats(wl.windows, T)
@@ -144,17 +198,18 @@ def main():
     fwd_tf = f_fwd / (fwd_ms.mean() * 1e-3) / 1e12
     bwd_tf = f_bwd / (bwd_ms.mean() * 1e-3) / 1e12 if with_bwd else None
 
-    # Roofline of the kernel that dominates the step.
-    if (not with_bwd) or fwd_ms.mean() >= bwd_ms.mean():
-        roof = {"kernel": "fwd_bf16_kernel<64>", "bound": "mfma", "achieved": round(fwd_tf, 2),
-                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
-                "traffic": None, "avg_launch_us": round(float(fwd_ms.mean()) * 1e3, 2),
-                "algorithmic_flops_per_launch": f_fwd}
-    else:
-        roof = {"kernel": "aah_attn_bwd (preprocess + scalar dQ + scalar dK/dV kernels)", "bound": "alu",
-                "achieved": round(bwd_tf, 2), "peak": PEAK_FP32_VALU_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(bwd_tf / PEAK_FP32_VALU_TFLOPS, 4), "traffic": None,
-                "avg_launch_us": round(float(bwd_ms.mean()) * 1e3, 2), "algorithmic_flops_per_launch": f_bwd}
+    # Roofline of the kernel that dominates the step (each step is one launch on `stream`).
+    # Algorithmic FLOPs per in-window pair: forward 4 d (Q K^T, P V); dK/dV kernel 8 d
+    # (Q K^T, dO V^T, dO^T P, Q^T dS); dQ kernel 6 d (K Q^T, V dO^T, K^T dS^T).
+    kernels = [("fwd_bf16_kernel<64>", float(fwd_ms.mean()), f_fwd)]
+    if with_bwd:
+        kernels += [("bwd_dkdv_kernel<64>", float(dkdv_ms.mean()), 8 * d * pairs),
+                    ("bwd_dq_kernel<64>", float(dq_ms.mean()), 6 * d * pairs)]
+    kname, kms, kflops = max(kernels, key=lambda x: x[1])
+    achieved = kflops / (kms * 1e-3) / 1e12
+    roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),
+            "avg_launch_us": round(kms * 1e3, 2), "algorithmic_flops_per_launch": int(kflops)}
 
     out = {
         "metric": "effective TFLOP/s (in-window pairs only) fwd/bwd, % of bf16 MFMA peak",
@@ -177,6 +232,9 @@ def main():
             "acr": round(acr, 4),
             "fwd_ms": round(float(fwd_ms.mean()), 4),
             "bwd_ms": round(float(bwd_ms.mean()), 4) if with_bwd else None,
+            "bwd_preprocess_ms": round(float(pre_ms.mean()), 4) if with_bwd else None,
+            "bwd_dkdv_ms": round(float(dkdv_ms.mean()), 4) if with_bwd else None,
+            "bwd_dq_ms": round(float(dq_ms.mean()), 4) if with_bwd else None,
             "fwd_tflops": round(fwd_tf, 2),
             "bwd_tflops": round(bwd_tf, 2) if with_bwd else None,
             "fwd_pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),

@@ -24,7 +24,7 @@ ABI_VERSION = 1
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
     "aah_attn_workspace_size", "aah_tile_shape", "aah_plan_fwd", "aah_plan_bwd", "aah_window_stats",
-    "aah_cache_clear",
+    "aah_cache_clear", "aah_attn_bwd_preprocess", "aah_attn_bwd_dkdv", "aah_attn_bwd_dq",
 )
 
 
@@ -66,6 +66,16 @@ def _declare(lib):
     lib.aah_attn_bwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int,
                                  c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                  c_void_p]
+    lib.aah_attn_bwd_preprocess.restype = c_int
+    lib.aah_attn_bwd_preprocess.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                            c_size_t, c_void_p]
+    lib.aah_attn_bwd_dkdv.restype = c_int
+    lib.aah_attn_bwd_dkdv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int,
+                                      c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                      c_void_p]
+    lib.aah_attn_bwd_dq.restype = c_int
+    lib.aah_attn_bwd_dq.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int, c_int,
+                                    c_int, c_int, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_workspace_size.restype = c_size_t
     lib.aah_attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_tile_shape.restype = c_int

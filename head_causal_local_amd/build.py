@@ -22,7 +22,9 @@ ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 # Device code: no packed-fp32 instructions (v_pk_fma_f32 and friends).
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # keep MFMA accumulators in ordinary VGPRs (no v_accvgpr copies around every VALU touch)
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HOST_ONLY = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]
 
 SOURCES = ["workplan.cpp", "aah_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "simple.hip"]

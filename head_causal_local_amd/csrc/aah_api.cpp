@@ -40,13 +40,28 @@ aah_status hip_fail(hipError_t e, const char* what) {
 
 bool supported_d(int d) { return d == 32 || d == 64 || d == 128; }
 
+#define AAH_TRY_INNER(expr)           \
+  do {                                \
+    const aah_status st_ = (expr);    \
+    if (st_ != AAH_OK) return st_;    \
+  } while (0)
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Shape checks shared by every entry point.
+aah_status check_dims(int B, int H, int T, int d, aah_dtype dt);
+
+// Shape checks shared by every entry point that takes windows.
 aah_status check_shape(const int32_t* windows, int B, int H, int T, int d, aah_dtype dt) {
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  AAH_TRY_INNER(check_dims(B, H, T, d, dt));
+  for (int h = 0; h < H; ++h)
+    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  return AAH_OK;
+}
+
+aah_status check_dims(int B, int H, int T, int d, aah_dtype dt) {
   if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
   if (static_cast<int64_t>(B) * H > INT32_MAX / 2)
     return fail(AAH_ERR_INVALID_ARG, "B * H = %lld is too large", static_cast<long long>(B) * H);
@@ -54,8 +69,9 @@ aah_status check_shape(const int32_t* windows, int B, int H, int T, int d, aah_d
   if (d < 1) return fail(AAH_ERR_INVALID_ARG, "d must be >= 1 (got %d)", d);
   if (dt != AAH_BF16 && dt != AAH_F32) return fail(AAH_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
   if (!supported_d(d)) return fail(AAH_ERR_UNSUPPORTED, "head dim %d has no kernel (supported: 32, 64, 128)", d);
-  for (int h = 0; h < H; ++h)
-    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  // Kernels address one head's [T, d] slice with 32-bit buffer offsets.
+  if (static_cast<int64_t>(T) * d * 4 >= (int64_t{1} << 31))
+    return fail(AAH_ERR_UNSUPPORTED, "T * d = %lld is too large for one head slice", static_cast<long long>(T) * d);
   return AAH_OK;
 }
 
@@ -150,16 +166,18 @@ void bwd_tiles(aah_dtype dt, int* row, int* col) {
   }
 }
 
-// Workspace layout of the backward: D (fp32 [B,H,T]) at offset 0, then the fp32
-// dQ accumulator [B,H,T,d] (bf16 only) at a 256-byte boundary.
-size_t bwd_d_bytes(int B, int H, int T) {
+// Workspace of the backward: D (fp32 [B,H,T]), rounded up to 256 bytes.
+size_t bwd_workspace(int B, int H, int T, int /*d*/, aah_dtype /*dt*/) {
   return round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256);
 }
 
-size_t bwd_workspace(int B, int H, int T, int d, aah_dtype dt) {
-  size_t bytes = bwd_d_bytes(B, H, T);
-  if (dt == AAH_BF16) bytes += round_up(static_cast<size_t>(B) * H * T * d * sizeof(float), 256);
-  return bytes;
+aah_status check_workspace(const void* workspace, size_t workspace_bytes, int B, int H, int T, int d, aah_dtype dt) {
+  const size_t need = bwd_workspace(B, H, T, d, dt);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
+                need);
+  if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return AAH_OK;
 }
 
 aah_status plan_to_host(PlanKind kind, const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile,
@@ -248,11 +266,90 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
   return AAH_OK;
 }
 
+aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, int B, int H, int T, int d, aah_dtype dt,
+                                   void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_dims(B, H, T, d, dt));
+  AAH_TRY(check_tensor(o, "o", 16));
+  AAH_TRY(check_tensor(dout, "dout", 16));
+  AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
+  const aah::AttnShape s{B, H, T, d, 1.0f};
+  const hipError_t e = aah::launch_bwd_preprocess(o, dout, dt == AAH_BF16, static_cast<float*>(workspace), s,
+                                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
+  return AAH_OK;
+}
+
+aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                             const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale, void* dk,
+                             void* dv, const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(dout, "dout", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  AAH_TRY(check_tensor(dk, "dk", 16));
+  AAH_TRY(check_tensor(dv, "dv", 16));
+  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
+  const aah::AttnShape s{B, H, T, d, scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float* Dbuf = static_cast<const float*>(workspace);
+  int row = 0, col = 0;
+  bwd_tiles(dt, &row, &col);
+  DevicePlan plan;
+  AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, row, col, &plan));
+  hipError_t e;
+  if (dt == AAH_BF16)
+    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, lse, Dbuf, dk, dv, plan.items, plan.n_items, plan.win, s, st);
+  else
+    e = aah::launch_bwd_dkdv_simple(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<const float*>(dout), lse, Dbuf,
+                                    static_cast<float*>(dk), static_cast<float*>(dv), plan.items, plan.n_items,
+                                    plan.win, s, st);
+  if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
+  return AAH_OK;
+}
+
+aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                           const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale, void* dq,
+                           const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(dout, "dout", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  AAH_TRY(check_tensor(dq, "dq", 16));
+  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
+  const aah::AttnShape s{B, H, T, d, scale};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float* Dbuf = static_cast<const float*>(workspace);
+  int row = 0, col = 0;
+  fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
+  DevicePlan plan;
+  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
+  hipError_t e;
+  if (dt == AAH_BF16)
+    e = aah::launch_bwd_dq_bf16(q, k, v, dout, lse, Dbuf, dq, plan.items, plan.n_items, plan.win, s, st);
+  else
+    e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
+                                  static_cast<const float*>(v), static_cast<const float*>(dout), lse, Dbuf,
+                                  static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
+  if (e != hipSuccess) return hip_fail(e, "dQ launch");
+  return AAH_OK;
+}
+
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                         const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
                         float scale, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                         aah_stream_t stream) {
   g_detail.clear();
+  // Validate everything up front so that no step runs unless all of them can.
   AAH_TRY(check_shape(windows, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
@@ -264,38 +361,11 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dk, "dk", 16));
   AAH_TRY(check_tensor(dv, "dv", 16));
   if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
-  const size_t need = bwd_workspace(B, H, T, d, dt);
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
-                need);
-  if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-
-  float* Dbuf = static_cast<float*>(workspace);
-  const aah::AttnShape s{B, H, T, d, scale};
-  hipStream_t st = static_cast<hipStream_t>(stream);
-
-  if (dt == AAH_BF16) {
-    float* dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_d_bytes(B, H, T));
-    DevicePlan bplan;
-    AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, aah::kBwdBf16RowTile, aah::kBwdBf16ColTile, &bplan));
-    hipError_t e = aah::launch_bwd_preprocess(o, dout, true, Dbuf, dq_acc, s, st);
-    if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-    e = aah::launch_bwd_bf16(q, k, v, dout, lse, Dbuf, dk, dv, dq_acc, bplan.items, bplan.n_items, bplan.win, s, st);
-    if (e != hipSuccess) return hip_fail(e, "backward launch");
-    e = aah::launch_dq_convert(dq_acc, dq, s, st);
-    if (e != hipSuccess) return hip_fail(e, "dq convert launch");
-    return AAH_OK;
-  }
-
-  DevicePlan fplan, bplan;
-  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &fplan));
-  AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, aah::kSimpleRowTile, aah::kSimpleColTile, &bplan));
-  hipError_t e = aah::launch_bwd_preprocess(o, dout, false, Dbuf, nullptr, s, st);
-  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  e = aah::launch_bwd_simple(q, k, v, dout, lse, Dbuf, false, dq, dk, dv, fplan.items, fplan.n_items, bplan.items,
-                             bplan.n_items, fplan.win, s, st);
-  if (e != hipSuccess) return hip_fail(e, "backward launch");
-  return AAH_OK;
+  AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
+  AAH_TRY(aah_attn_bwd_preprocess(o, dout, B, H, T, d, dt, workspace, workspace_bytes, stream));
+  AAH_TRY(aah_attn_bwd_dkdv(q, k, v, dout, lse, windows, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
+                            stream));
+  return aah_attn_bwd_dq(q, k, v, dout, lse, windows, B, H, T, d, dt, scale, dq, workspace, workspace_bytes, stream);
 }
 
 aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,

@@ -1,0 +1,81 @@
+// Device-side helpers shared by the bf16 MFMA kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace aah {
+namespace dev {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+#define AAH_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+constexpr int kBufferFlags = 0x00020000;  // raw buffer, 32-bit words, bounds-checked
+
+// v_mfma_f32_32x32x16_bf16 lane layouts (lane l, half h = l / 32):
+//   A (32 x 16): lane holds A[l % 32][8 h .. 8 h + 7]
+//   B (16 x 32): lane holds B[8 h .. 8 h + 7][l % 32]
+//   C (32 x 32): register r holds C[8 (r / 4) + 4 h + r % 4][l % 32]
+__device__ inline f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Lanes l and l ^ 32 hold the same MFMA column; combine their values.
+__device__ inline float half_swap_max(float x) {
+  // permlane32_swap(x, x): lanes < 32 get (own, partner) and lanes >= 32 get (partner, own).
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Buffer resource covering `bytes` bytes from `p`; loads past the end return zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), kBufferFlags);
+}
+
+__device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
+}
+
+__device__ inline float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
+}
+
+// ds_read_b64_tr_b16 works on 16-lane groups: if source lane s of a group
+// addresses row R0 + s / 4, columns C0 + 4 (s % 4) .. + 3 of a row-major bf16
+// tile, destination lane i of the group receives column C0 + i, rows R0 .. R0 + 3.
+// Two reads, the second `gap` elements further, give eight rows of one column:
+// an MFMA A or B operand whose k index runs down the tile.
+__device__ inline bf16x8 read_tr(const bf16* p, int gap) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p + gap));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Store 4 consecutive fp32 values as bf16 (round to nearest even) with one 8-byte store.
+__device__ inline void store_bf16x4(bf16* dst, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = static_cast<bf16>(a);
+  v[1] = static_cast<bf16>(b);
+  v[2] = static_cast<bf16>(c);
+  v[3] = static_cast<bf16>(d);
+  *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v);
+}
+
+}  // namespace dev
+}  // namespace aah

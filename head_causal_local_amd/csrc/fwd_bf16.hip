@@ -25,28 +25,28 @@
 //     lane four consecutive rows of one column.
 //   * The online softmax runs in the log2 domain: exp2(s * scale * log2 e - m).
 // Only tiles that touch a window edge, the diagonal or the end of the
-// sequence evaluate the mask.
+// sequence evaluate the mask.  The running max is updated lazily: the O
+// accumulators are rescaled only when some row's tile max exceeds its running
+// max by more than kLazyTau (log2 units), so P never exceeds 2^kLazyTau and
+// most tiles skip the rescale.  Row sums accumulate the fp32 P before its
+// rounding to bf16, so the log-sum-exp carries no bf16 quantization.
+// Global loads go through buffer resources whose range is the head's [T, d]
+// slice, so rows past T read as zero without branches.
 #include <cmath>
 
+#include "device_common.hpp"
 #include "kernels.hpp"
 
 namespace aah {
 namespace {
 
-typedef __bf16 bf16;
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-#define AAH_LDS __attribute__((address_space(3)))
+using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // query rows per item
 constexpr int kKeys = 64;           // keys per LDS stage
 constexpr int kThreads = 64 * kWaves;
+constexpr float kLazyTau = 8.0f;    // rescale threshold in log2 units (P <= 256)
 static_assert(kRows == kFwdBf16RowTile && kKeys == kFwdBf16ColTile, "planner tile mismatch");
 
 template <int D>
@@ -60,25 +60,6 @@ struct Cfg {
   static constexpr size_t kSmemBytes = 2u * 2u * kTileElems * sizeof(bf16);
   static_assert(kChunksPerThread >= 1, "tile too small for the thread count");
 };
-
-__device__ inline float half_swap_max(float x) {
-  // permlane32_swap(x, x): lanes < 32 get (own, partner) and lanes >= 32 get (partner, own).
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ inline float half_swap_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ inline bf16x8 read_vt(const bf16* p, int stride) {
-  // Two transposing reads: rows [r, r+4) and [r+8, r+12) of one 4-wide column chunk group.
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p + 8 * stride));
-  const auto both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, both);
-}
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
@@ -107,14 +88,14 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
   const int wave_key_hi = min(q0w + 31, T - 1); // last key any row of the wave sees
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds q[qi][16 s + 8 hl + 0..7].
+  const uint32_t slice_bytes = static_cast<uint32_t>(T) * D * sizeof(bf16);
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, slice_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, slice_bytes);
   bf16x8 qf[C::kSteps];
 #pragma unroll
-  for (int s = 0; s < C::kSteps; ++s) {
-    if (row_ok)
-      qf[s] = *reinterpret_cast<const bf16x8*>(Qh + static_cast<size_t>(qi) * D + 16 * s + 8 * hl);
-    else
-      qf[s] = bf16x8{};
-  }
+  for (int s = 0; s < C::kSteps; ++s)
+    qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (static_cast<uint32_t>(qi) * D + 16 * s + 8 * hl) * sizeof(bf16)));
 
   f32x16 acc[C::kBlocks];
 #pragma unroll
@@ -131,14 +112,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
       const int cidx = tid + kThreads * i;
       const int row = cidx / C::kChunkPerRow;
       const int col = (cidx % C::kChunkPerRow) * 8;
-      const int key = k0 + row;
-      if (key < T) {
-        stk[i] = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(key) * D + col);
-        stv[i] = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(key) * D + col);
-      } else {
-        stk[i] = u32x4{0u, 0u, 0u, 0u};  // keys past T: zero K and V (masked, and 0 * 0 in P V)
-        stv[i] = u32x4{0u, 0u, 0u, 0u};
-      }
+      // Keys past T read as zero (masked in S, and 0 * 0 in P V).
+      const uint32_t off = (static_cast<uint32_t>(k0 + row) * D + col) * sizeof(bf16);
+      stk[i] = load16(rk, off);
+      stv[i] = load16(rv, off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -182,20 +159,22 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
 #pragma unroll
         for (int st = 0; st < C::kSteps; ++st) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (32 * mb + ln) * C::kStride + 16 * st + 8 * hl);
-          s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[mb], 0, 0, 0);
+          s[mb] = mfma(a, qf[st], s[mb]);
         }
       }
 
-      // Mask only when some (row, key) pair of the wave x tile lies outside a window.
+      // Mask only when some (row, key) pair of the wave x tile lies outside a
+      // window.  Key j is visible to row qi iff 0 <= qi - j < W; keys past T
+      // fail qi - j >= 0 for every stored row, and rows past T are never stored.
       const bool interior = (k0 + kKeys - 1 <= q0w) && (k0 >= q0w + 31 - W + 1);
       if (!interior) {
+        const int rel = qi - k0 - 4 * hl;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-            const bool ok = key <= qi && key > qi - W && key < T;
-            if (!ok) s[mb][r] = -INFINITY;
+            const int dist = rel - (32 * mb + 8 * (r >> 2) + (r & 3));
+            if (static_cast<unsigned>(dist) >= static_cast<unsigned>(W)) s[mb][r] = -INFINITY;
           }
       }
 
@@ -204,35 +183,40 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      mx = half_swap_max(mx);
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // row with nothing visible yet
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      const float m_tile = half_swap_max(mx) * c;
+      // Lazy rescale: only when some row's max grew by more than kLazyTau.
+      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kLazyTau) != 0) {
+        const float m_new = fmaxf(m_run, m_tile);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with nothing visible yet
 
       // P^T fragments for the four 16-key MFMA steps.  Step st takes registers
       // 8*(st&1) .. 8*(st&1)+7 of block st>>1, i.e. keys 16 st + 8 (e/4) + 4 hl + e%4.
       bf16x8 pf[4];
-      float lsum = 0.f;
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m_use));
-          lsum += p;
-          pf[st][e] = static_cast<bf16>(p);
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c, -m_use));
+          l_run += p0;
+          l_run += p1;
+          pf[st][e] = static_cast<bf16>(p0);
+          pf[st][e + 1] = static_cast<bf16>(p1);
         }
-      l_run = l_run * alpha + lsum;
-      m_run = m_new;
-#pragma unroll
-      for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
 
       // O^T += V^T P^T.
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int b = 0; b < C::kBlocks; ++b) {
-          const bf16x8 a = read_vt(vb + (16 * st + vt_row) * C::kStride + 32 * b + vt_col, C::kStride);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[st], acc[b], 0, 0, 0);
+          const bf16x8 a = read_tr(vb + (16 * st + vt_row) * C::kStride + 32 * b + vt_col, 8 * C::kStride);
+          acc[b] = mfma(a, pf[st], acc[b]);
         }
     }
 
@@ -249,13 +233,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
 #pragma unroll
   for (int b = 0; b < C::kBlocks; ++b)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x4 o4;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) o4[j] = static_cast<bf16>(acc[b][4 * i + j] * inv);
-      *reinterpret_cast<u32x2*>(Orow + 32 * b + 8 * i + 4 * hl) = __builtin_bit_cast(u32x2, o4);
-    }
-  if (hl == 0) LSE[static_cast<size_t>(it.bh) * T + qi] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+    for (int i = 0; i < 4; ++i)
+      store_bf16x4(Orow + 32 * b + 8 * i + 4 * hl, acc[b][4 * i] * inv, acc[b][4 * i + 1] * inv,
+                   acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
+  if (hl == 0) LSE[static_cast<size_t>(it.bh) * T + qi] = (m_run + log2f(l_tot)) * kLn2;
 }
 
 template <int D>

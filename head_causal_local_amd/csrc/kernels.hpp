@@ -35,27 +35,29 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           const WorkItem* items, int n_items, const int32_t* win_eff,
                           const AttnShape& s, hipStream_t stream);
 
-// D_i = sum_c dO_ic * O_ic in fp32; when dq_acc != nullptr also zeroes the
-// fp32 dQ accumulator rows.  is_bf16 selects the element type of o / dout.
+// D_i = sum_c dO_ic * O_ic in fp32.  is_bf16 selects the element type of o / dout.
 hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D,
-                                 float* dq_acc, const AttnShape& s, hipStream_t stream);
+                                 const AttnShape& s, hipStream_t stream);
 
-// bf16 backward on MFMA: dK, dV written directly, dQ accumulated into the
-// zeroed fp32 dq_acc with atomics (items from the backward planner with
-// kBwdBf16RowTile keys per item and kBwdBf16ColTile queries per step).
-hipError_t launch_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                           const float* D, void* dk, void* dv, float* dq_acc, const WorkItem* items, int n_items,
-                           const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+// bf16 backward on MFMA, no atomics.  dK, dV: items from the backward
+// planner (kBwdBf16RowTile keys per item, kBwdBf16ColTile queries per step).
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                                const float* D, void* dk, void* dv, const WorkItem* items, int n_items,
+                                const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
 
-// dq = bf16(dq_acc), elementwise over B*H*T*d.
-hipError_t launch_dq_convert(const float* dq_acc, void* dq, const AttnShape& s, hipStream_t stream);
+// dQ: items from the forward planner (kFwdBf16RowTile queries, kFwdBf16ColTile keys per step).
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              const float* D, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+                              const AttnShape& s, hipStream_t stream);
 
-// Scalar backward (reference-grade, any supported dtype): dQ per query row
-// over the forward work list, dK/dV per key row over the backward work list.
-hipError_t launch_bwd_simple(const void* q, const void* k, const void* v, const void* dout,
-                             const float* lse, const float* D, bool is_bf16,
-                             void* dq, void* dk, void* dv,
-                             const WorkItem* fwd_items, int n_fwd, const WorkItem* bwd_items, int n_bwd,
-                             const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+// Scalar backward for fp32: dQ one query row per lane over the forward work
+// list; dK/dV one key row per lane over the backward work list.
+hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout,
+                                const float* lse, const float* D, float* dq, const WorkItem* items,
+                                int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
+                                  const float* lse, const float* D, float* dk, float* dv,
+                                  const WorkItem* items, int n_items, const int32_t* win_eff,
+                                  const AttnShape& s, hipStream_t stream);
 
 }  // namespace aah

@@ -1,7 +1,7 @@
 // Scalar (VALU) kernels of per-head causal local-window attention:
 //   * the fp32 forward (exact fp32 arithmetic, one query row per lane);
 //   * the backward preprocess D_i = sum_c dO_ic O_ic;
-//   * a straightforward backward (one row per lane) for fp32 and bf16.
+//   * the fp32 backward: dQ one query row per lane, dK/dV one key row per lane.
 //
 // Operation: "Asymmetric Attention Heads" section 5.8 -- key j is visible to
 // query i iff i - W < j <= i; A = softmax(scale Q K^T + M_W), Y = A V.  The
@@ -30,7 +30,6 @@ __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(bf16 x) { return static_cast<float>(x); }
 template <typename E> __device__ inline E from_f32(float x);
 template <> __device__ inline float from_f32<float>(float x) { return x; }
-template <> __device__ inline bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
 
 // Copy rows [r0, r0 + kCols) of a [T, D] tensor into an fp32 LDS tile; rows past T are zero.
 template <typename E, int D>
@@ -113,8 +112,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
 // combine with xor-shuffles (E = elements per chunk).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO,
-                                                      float* __restrict__ Dout, float* __restrict__ dq_acc,
-                                                      int64_t rows) {
+                                                      float* __restrict__ Dout, int64_t rows) {
   constexpr int kPer = 16 / sizeof(E);
   constexpr int kLanesPerRow = D / kPer;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -128,11 +126,6 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, c
     const E* ge = reinterpret_cast<const E*>(&gv);
 #pragma unroll
     for (int x = 0; x < kPer; ++x) sum = fmaf(to_f32(oe[x]), to_f32(ge[x]), sum);
-    if (dq_acc != nullptr) {
-#pragma unroll
-      for (int x = 0; x < kPer; x += 4)
-        *reinterpret_cast<u32x4*>(dq_acc + row * D + part * kPer + x) = u32x4{0u, 0u, 0u, 0u};
-    }
   }
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
@@ -269,32 +262,13 @@ hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, f
 }
 
 template <typename E, int D>
-hipError_t pre_d(const void* o, const void* dout, float* Dout, float* dq_acc, const AttnShape& s,
-                 hipStream_t stream) {
+hipError_t pre_d(const void* o, const void* dout, float* Dout, const AttnShape& s, hipStream_t stream) {
   constexpr int kLanesPerRow = D / (16 / sizeof(E));
   const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.T;
   const int64_t threads = rows * kLanesPerRow;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     static_cast<const E*>(o), static_cast<const E*>(dout), Dout, dq_acc, rows);
-  return hipGetLastError();
-}
-
-template <typename E, int D>
-hipError_t bwd_simple_d(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                        const float* D_, void* dq, void* dk, void* dv, const WorkItem* fwd_items, int n_fwd,
-                        const WorkItem* bwd_items, int n_bwd, const int32_t* win_eff, const AttnShape& s,
-                        hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dq_simple_kernel<E, D>), dim3(n_fwd), dim3(kRows), 0, stream,
-                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
-                     static_cast<const E*>(dout), lse, D_, static_cast<E*>(dq), fwd_items, win_eff, s.H, s.T,
-                     s.scale);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkdv_simple_kernel<E, D>), dim3(n_bwd), dim3(kRows), 0, stream,
-                     static_cast<const E*>(q), static_cast<const E*>(k), static_cast<const E*>(v),
-                     static_cast<const E*>(dout), lse, D_, static_cast<E*>(dk), static_cast<E*>(dv), bwd_items,
-                     win_eff, s.H, s.T, s.scale);
+                     static_cast<const E*>(o), static_cast<const E*>(dout), Dout, rows);
   return hipGetLastError();
 }
 
@@ -311,29 +285,46 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   }
 }
 
-hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D, float* dq_acc,
-                                 const AttnShape& s, hipStream_t stream) {
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, bool is_bf16, float* D, const AttnShape& s,
+                                 hipStream_t stream) {
   switch (s.d) {
-    case 32: return is_bf16 ? pre_d<bf16, 32>(o, dout, D, dq_acc, s, stream) : pre_d<float, 32>(o, dout, D, dq_acc, s, stream);
-    case 64: return is_bf16 ? pre_d<bf16, 64>(o, dout, D, dq_acc, s, stream) : pre_d<float, 64>(o, dout, D, dq_acc, s, stream);
-    case 128: return is_bf16 ? pre_d<bf16, 128>(o, dout, D, dq_acc, s, stream) : pre_d<float, 128>(o, dout, D, dq_acc, s, stream);
+    case 32: return is_bf16 ? pre_d<bf16, 32>(o, dout, D, s, stream) : pre_d<float, 32>(o, dout, D, s, stream);
+    case 64: return is_bf16 ? pre_d<bf16, 64>(o, dout, D, s, stream) : pre_d<float, 64>(o, dout, D, s, stream);
+    case 128: return is_bf16 ? pre_d<bf16, 128>(o, dout, D, s, stream) : pre_d<float, 128>(o, dout, D, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_simple(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                             const float* D, bool is_bf16, void* dq, void* dk, void* dv,
-                             const WorkItem* fwd_items, int n_fwd, const WorkItem* bwd_items, int n_bwd,
-                             const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
-#define AAH_SIMPLE(E, DD) \
-  bwd_simple_d<E, DD>(q, k, v, dout, lse, D, dq, dk, dv, fwd_items, n_fwd, bwd_items, n_bwd, win_eff, s, stream)
+hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout, const float* lse,
+                                const float* D, float* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+                                const AttnShape& s, hipStream_t stream) {
+#define AAH_DQ(DD)                                                                                                \
+  hipLaunchKernelGGL((bwd_dq_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, lse, \
+                     D, dq, items, win_eff, s.H, s.T, s.scale)
   switch (s.d) {
-    case 32: return is_bf16 ? AAH_SIMPLE(bf16, 32) : AAH_SIMPLE(float, 32);
-    case 64: return is_bf16 ? AAH_SIMPLE(bf16, 64) : AAH_SIMPLE(float, 64);
-    case 128: return is_bf16 ? AAH_SIMPLE(bf16, 128) : AAH_SIMPLE(float, 128);
+    case 32: AAH_DQ(32); break;
+    case 64: AAH_DQ(64); break;
+    case 128: AAH_DQ(128); break;
     default: return hipErrorInvalidValue;
   }
-#undef AAH_SIMPLE
+#undef AAH_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
+                                  const float* lse, const float* D, float* dk, float* dv, const WorkItem* items,
+                                  int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
+#define AAH_DKDV(DD)                                                                                            \
+  hipLaunchKernelGGL((bwd_dkdv_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, \
+                     lse, D, dk, dv, items, win_eff, s.H, s.T, s.scale)
+  switch (s.d) {
+    case 32: AAH_DKDV(32); break;
+    case 64: AAH_DKDV(64); break;
+    case 128: AAH_DKDV(128); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef AAH_DKDV
+  return hipGetLastError();
 }
 
 }  // namespace aah

@@ -37,7 +37,8 @@
  *     written to any output and the call returns a status other than AAH_OK.
  *     aah_last_error_detail() then describes the failure (thread-local).
  *   - Supported: dt = AAH_BF16 with d in {32, 64, 128}; dt = AAH_F32 with d in
- *     {32, 64, 128}; any T >= 1 (ragged tails are masked).
+ *     {32, 64, 128}; any T >= 1 (ragged tails are masked) with T * d * 4 < 2^31
+ *     (one head's slice is addressed with 32-bit offsets).
  */
 #ifndef AAH_ATTN_H
 #define AAH_ATTN_H
@@ -101,12 +102,12 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Backward pass: gradients of sum(O * dout) with respect to q, k and v, given
  * the forward's o and lse (the log-sum-exp saved by aah_attn_fwd with the same
- * scale and windows).  Writes dq, dk, dv [B,H,T,d] of dtype dt (fully
- * overwritten).  Needs a device workspace of at least
- * aah_attn_workspace_size(B, H, T, d, dt, 1) bytes, 256-byte aligned; its
- * contents on entry do not matter and are clobbered.  With dt = AAH_BF16 the
- * dq accumulation uses fp32 atomics, so dq may differ in the last bits
- * between runs; dk and dv are deterministic.
+ * scale and windows).  Writes dq, dk, dv [B,H,T,d] of dtype dt (each element
+ * exactly once: no atomics, results are bitwise reproducible).  Needs a device
+ * workspace of at least aah_attn_workspace_size(B, H, T, d, dt, 1) bytes,
+ * 256-byte aligned; its contents on entry do not matter and are clobbered.
+ * Runs aah_attn_bwd_preprocess, aah_attn_bwd_dkdv and aah_attn_bwd_dq, in
+ * that order, on `stream`.
  */
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse,
@@ -114,6 +115,31 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         aah_dtype dt, float scale, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
+
+/*
+ * The backward's steps as separate calls, for callers that schedule or time
+ * them.  Arguments mean what they mean for aah_attn_bwd and the same checks
+ * apply; the workspace carries D from the first step to the other two.
+ *   aah_attn_bwd_preprocess: D_i = dout_i . o_i (fp32 [B,H,T], into the
+ *     workspace).  Must complete before either of the others starts.
+ *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel).
+ *   aah_attn_bwd_dq:   writes dq (query-stationary kernel).
+ * dkdv and dq only read the workspace and may run in either order or
+ * concurrently on different streams once the preprocess has completed.
+ */
+aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, int B, int H, int T, int d,
+                                   aah_dtype dt, void* workspace, size_t workspace_bytes,
+                                   aah_stream_t stream);
+
+aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                             const float* lse, const int32_t* windows, int B, int H, int T, int d,
+                             aah_dtype dt, float scale, void* dk, void* dv,
+                             const void* workspace, size_t workspace_bytes, aah_stream_t stream);
+
+aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                           const float* lse, const int32_t* windows, int B, int H, int T, int d,
+                           aah_dtype dt, float scale, void* dq,
+                           const void* workspace, size_t workspace_bytes, aah_stream_t stream);
 
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */

@@ -227,3 +227,23 @@ def test_1b_layer_backward_sampled_heads():
         _grad_check(host(dv[sl]), rv, name=f"dv b{b} h{h}")
     for t in (dq, dk, dv):
         assert torch.isfinite(t.float()).all()
+
+
+def test_backward_deterministic_and_steps():
+    """The backward writes every gradient once (no atomics): two runs are bitwise equal, and the
+    three separate steps reproduce the combined call bitwise."""
+    _require_gpu()
+    wl = synth.random_workload(2, 3, 700, 64, [64, 700, 300], dtype="bf16", seed=17, backward=True)
+    q, k, v, do = dev(wl, "q"), dev(wl, "k"), dev(wl, "v"), dev(wl, "do")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows)
+    g1 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
+    g2 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
+    ws = torch.empty(aah.workspace_size(2, 3, 700, 64, "bf16"), dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    aah.attn_bwd_preprocess(o, do, ws)
+    aah.attn_bwd_dq(q, k, v, do, lse, wl.windows, dq, ws)     # either order after the preprocess
+    aah.attn_bwd_dkdv(q, k, v, do, lse, wl.windows, dk, dv, ws)
+    torch.cuda.synchronize()
+    for a, b, c in zip(g1, g2, (dq, dk, dv)):
+        assert torch.equal(a, b)
+        assert torch.equal(a, c)
