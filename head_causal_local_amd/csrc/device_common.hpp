@@ -11,6 +11,7 @@ namespace dev {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -50,6 +51,51 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes
 
 __device__ inline u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
+}
+
+// Raw buffer resource words (base, stride 0, range in bytes, flags) for the
+// LDS-copy instruction below, which takes them as a scalar quad.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ inline i32x4 rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 r;
+  r[0] = static_cast<int>(static_cast<uint32_t>(a));
+  r[1] = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
+  r[2] = static_cast<int>(bytes);
+  r[3] = kBufferFlags;
+  return r;
+}
+
+// Asynchronous copy of 16 bytes per lane from a buffer straight into LDS
+// (buffer_load_dwordx4 ... lds): lane i's bytes land at lds_base + 16 i, where
+// lds_base must be uniform across the wave.  Loads past the resource's range
+// deliver zeros.  Completion is counted by vmcnt and is the caller's to wait
+// for (wait_vm_barrier).  Issued as inline assembly so that the compiler's own
+// wait-count bookkeeping does not serialise later LDS reads of other buffers
+// behind these copies.
+__device__ inline void dma16(const i32x4& rsrc, const void* lds_base, uint32_t byte_off) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(lds_base)));
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(rsrc)
+                   : "memory", "m0");
+}
+
+// Workgroup barrier after waiting until at most n of this wave's vector-memory
+// operations (loads, LDS copies) are outstanding; n is a literal 0..15.  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+#define wait_vm_barrier(n) __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(n) : "memory")
+
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile whose rows hold
+// NC chunks (NC = d / 8): logical chunk c of row r is stored at chunk
+// c ^ swz<NC>(r).  Chosen so that (a) eight consecutive rows read at one
+// logical chunk (an MFMA operand read with ds_read_b128) and (b) four
+// consecutive rows read at two adjacent chunks 2j, 2j + 1 (one 16-lane group of
+// ds_read_b64_tr_b16) each touch all 32 four-byte banks once.
+template <int NC>
+__device__ constexpr int swz(int r) {
+  return NC >= 8 ? (((2 * r) & 6) | ((r >> 2) & 1)) : ((((r >> 1) & 1) << 1) | ((r >> 2) & 1));
 }
 
 __device__ inline float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {

@@ -7,31 +7,39 @@
 //
 // One workgroup = one work item = 128 query rows of one head (4 waves x 32
 // rows) and the contiguous range of 64-key tiles the planner listed for them;
-// tiles wholly outside the window are never visited, and inside a workgroup
-// each wave also skips the tiles that none of its own 32 rows can see.
+// tiles wholly outside the window are never visited.  Each wave walks the
+// tile in two 32-key blocks and classifies each block against its own 32
+// rows: blocks no row sees are skipped (no MFMA, no exp), blocks every row
+// sees in full run without a mask, and only the (at most two) partial blocks
+// per wave -- the diagonal and the window's trailing edge -- apply a
+// one-sided mask.
 //
 // Data flow per 64-key tile:
-//   * K and V tiles are copied row-major from HBM to LDS with 16-byte loads
-//     (double-buffered: the next tile's loads are in flight while the current
-//     one is used).
+//   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, no
+//     register staging), double-buffered: the next tile's copies are in flight
+//     while the current tile is used.  Tiles are row-major with an XOR swizzle
+//     of their 16-byte chunks so that both read patterns below are free of
+//     bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = d).
 //     The output layout gives lane l the query (l mod 32) and 16 keys per
-//     32-key block, so the row max / row sum of the online softmax are
-//     in-lane reductions plus one permlane32 swap between the half-waves.
+//     32-key block, so all softmax bookkeeping is in-lane, plus one
+//     permlane32 swap between the half-waves when a row max is needed.
 //   * P^T (bf16) stays in registers and is the B operand of O^T += V^T P^T
 //     (M = d, N = queries, K = keys).  The MFMA k-slots are mapped to keys in
 //     the order the S^T output already holds them, and the V^T operand is
 //     read from the row-major V tile with ds_read_b64_tr_b16, which hands each
 //     lane four consecutive rows of one column.
-//   * The online softmax runs in the log2 domain: exp2(s * scale * log2 e - m).
-// Only tiles that touch a window edge, the diagonal or the end of the
-// sequence evaluate the mask.  The running max is updated lazily: the O
-// accumulators are rescaled only when some row's tile max exceeds its running
-// max by more than kLazyTau (log2 units), so P never exceeds 2^kLazyTau and
-// most tiles skip the rescale.  Row sums accumulate the fp32 P before its
-// rounding to bf16, so the log-sum-exp carries no bf16 quantization.
-// Global loads go through buffer resources whose range is the head's [T, d]
-// slice, so rows past T read as zero without branches.
+//
+// Softmax (log2 domain, p = exp2(s * scale * log2 e - m)).  The reference m of
+// a row is refreshed lazily: each lane takes the max of its 16 scores of the
+// block (v_max3), and only when some lane's max exceeds its row's reference by
+// more than kTau (or a row has no reference yet) does the wave exchange the
+// half-row maxima, rescale O and the row sum, and move the reference.  So
+// every p is <= 2^kTau and the row's true max is >= its reference.  P is
+// packed to bf16 and the row sum adds exactly those bf16 weights with v_dot2,
+// so the normalisation matches the weights used in P V.
+// Global loads go through buffer resources whose range ends at the head's
+// last row, so rows past T read as zero without branches.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -46,28 +54,39 @@ constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // query rows per item
 constexpr int kKeys = 64;           // keys per LDS stage
 constexpr int kThreads = 64 * kWaves;
-constexpr float kLazyTau = 8.0f;    // rescale threshold in log2 units (P <= 256)
+constexpr float kTau = 8.0f;       // lazy-rescale bound: p <= 2^kTau
 static_assert(kRows == kFwdBf16RowTile && kKeys == kFwdBf16ColTile, "planner tile mismatch");
 
 template <int D>
 struct Cfg {
-  static constexpr int kStride = D + 8;               // LDS row stride (elements): 16-byte pad
-  static constexpr int kTileElems = kKeys * kStride;  // one K or V stage
-  static constexpr int kChunkPerRow = D / 8;          // 16-byte chunks per row
-  static constexpr int kChunksPerThread = kKeys * kChunkPerRow / kThreads;
-  static constexpr int kSteps = D / 16;               // MFMA k-steps over d for S^T
-  static constexpr int kBlocks = D / 32;              // 32-row blocks of O^T
-  static constexpr size_t kSmemBytes = 2u * 2u * kTileElems * sizeof(bf16);
-  static_assert(kChunksPerThread >= 1, "tile too small for the thread count");
+  static constexpr int kNC = D / 8;                 // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kKeys * kRowBytes;  // one K or V stage
+  static constexpr int kDmaPerWave = kNC / kWaves;  // 1 KiB DMA instructions per wave per tensor per tile
+  static constexpr int kSteps = D / 16;             // MFMA k-steps over d for S^T
+  static constexpr int kBlocks = D / 32;            // 32-row blocks of O^T
+  // Resident waves per SIMD the register allocation is sized for.
+  static constexpr int kWavesPerSimd = D <= 64 ? 4 : 2;
+  static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
 };
 
+// Key offset (within its 32-key block, before the 4 hl lane offset) held by S^T register r.
+__device__ constexpr int reg_key(int r) { return 8 * (r >> 2) + (r & 3); }
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    bf16* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, int H, int T, float c) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd)))
+void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                     bf16* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
+                     const int32_t* __restrict__ win_eff, int H, int T, float c) {
   using C = Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  constexpr int NC = C::kNC;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[C::kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[C::kTileBytes];
+  constexpr int kDmaInstr = 2 * C::kDmaPerWave;  // copies one wave issues per tile
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
@@ -78,7 +97,10 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
   const bf16* Vh = V + base;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int lane = tid & 63;
+  // The wave index is uniform across the wave: keep it (and everything derived
+  // from it) in scalar registers so block decisions compile to scalar branches.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
   const int q0w = it.tile * kRows + wave * 32;  // first query row of this wave
   const int qi = q0w + ln;                      // this lane's query row
@@ -88,140 +110,181 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
   const int wave_key_hi = min(q0w + 31, T - 1); // last key any row of the wave sees
 
   // Q^T fragments (B operand of S^T = K Q^T): lane holds q[qi][16 s + 8 hl + 0..7].
-  const uint32_t slice_bytes = static_cast<uint32_t>(T) * D * sizeof(bf16);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh, slice_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh, slice_bytes);
+  const uint32_t slice_bytes = static_cast<uint32_t>(T) * C::kRowBytes;
   bf16x8 qf[C::kSteps];
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, slice_bytes);
 #pragma unroll
-  for (int s = 0; s < C::kSteps; ++s)
-    qf[s] = __builtin_bit_cast(bf16x8, load16(rq, (static_cast<uint32_t>(qi) * D + 16 * s + 8 * hl) * sizeof(bf16)));
+    for (int s = 0; s < C::kSteps; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, load16(rq, static_cast<uint32_t>(qi) * C::kRowBytes + (16 * s + 8 * hl) * 2));
+    // Consume the fragments here, so that the compiler waits for these loads now
+    // rather than at their first use inside the loop, where its wait would also
+    // cover the LDS copies in flight.
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) __asm__ volatile("" ::"v"(qf[s]));
+  }
 
   f32x16 acc[C::kBlocks];
 #pragma unroll
   for (int b = 0; b < C::kBlocks; ++b) acc[b] = f32x16{};
-  float m_run = -INFINITY;  // running max of scaled scores (log2 domain)
-  float l_run = 0.f;        // this half-wave's running sum of exp2(. - m_run)
+  float m_run = -INFINITY;  // reference max of this lane's row (log2 domain)
+  float m_use = 0.f;        // m_run, or 0 while the row has seen no visible key (then every p is 0)
+  float l_run = 0.f;        // this half-wave's running sum of the bf16 weights
 
-  // Staging registers for one K and one V tile.
-  u32x4 stk[C::kChunksPerThread], stv[C::kChunksPerThread];
-  auto load_tile = [&](int kt) {
+  // DMA sources: instruction j of this wave fills tile chunks P = (wave * kDmaPerWave + j) * 64 + lane,
+  // i.e. row P / NC at stored chunk P % NC, which holds logical chunk (P % NC) ^ swz(row).
+  uint32_t dma_off[C::kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < C::kDmaPerWave; ++j) {
+    const int P = (wave * C::kDmaPerWave + j) * 64 + lane;
+    const int row = P / NC;
+    dma_off[j] = static_cast<uint32_t>(row * C::kRowBytes + (((P % NC) ^ swz<NC>(row)) * 16));
+  }
+  auto issue_tile = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
     const int k0 = kt * kKeys;
+    // Resources start at the tile's first row and end at row T: keys past T read as zero.
+    const uint32_t left = static_cast<uint32_t>(T - k0) * C::kRowBytes;
+    const i32x4 rk = rsrc_words(Kh + static_cast<size_t>(k0) * D, left);
+    const i32x4 rv = rsrc_words(Vh + static_cast<size_t>(k0) * D, left);
 #pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int row = cidx / C::kChunkPerRow;
-      const int col = (cidx % C::kChunkPerRow) * 8;
-      // Keys past T read as zero (masked in S, and 0 * 0 in P V).
-      const uint32_t off = (static_cast<uint32_t>(k0 + row) * D + col) * sizeof(bf16);
-      stk[i] = load16(rk, off);
-      stv[i] = load16(rv, off);
-    }
-  };
-  auto store_tile = [&](int buf) {
-    bf16* kb = smem + buf * 2 * C::kTileElems;
-    bf16* vb = kb + C::kTileElems;
-#pragma unroll
-    for (int i = 0; i < C::kChunksPerThread; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int row = cidx / C::kChunkPerRow;
-      const int col = (cidx % C::kChunkPerRow) * 8;
-      *reinterpret_cast<u32x4*>(kb + row * C::kStride + col) = stk[i];
-      *reinterpret_cast<u32x4*>(vb + row * C::kStride + col) = stv[i];
+    for (int j = 0; j < C::kDmaPerWave; ++j) {
+      const int off = (wave * C::kDmaPerWave + j) * 1024;
+      dma16(rk, kdst + off, dma_off[j]);
+      dma16(rv, vdst + off, dma_off[j]);
     }
   };
 
-  // Lane-constant parts of the LDS addresses.
+  // Lane-constant LDS read offsets.  K (A operand of S^T): row 32 mb + ln, logical chunk 2 st + hl.
+  uint32_t k_off[C::kSteps];
+#pragma unroll
+  for (int st = 0; st < C::kSteps; ++st)
+    k_off[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
+  // V^T (A operand of O^T += V^T P^T) by ds_read_b64_tr_b16: lane (g, s16) addresses
+  // row 16 st + 4 hl + s16 / 4 (+ 8 for the second read), columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3.
   const int g = lane >> 4, s16 = lane & 15;
-  const int vt_row = 4 * hl + (s16 >> 2);       // + 16 * step
-  const int vt_col = 16 * (g & 1) + 4 * (s16 & 3);  // + 32 * block
-
-  load_tile(it.lo);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = it.lo; kt < it.hi; ++kt) {
-    const int buf = (kt - it.lo) & 1;
-    const bool has_next = kt + 1 < it.hi;
-    if (has_next) load_tile(kt + 1);
-
-    const int k0 = kt * kKeys;
-    const bool needed = wave_active && k0 <= wave_key_hi && k0 + kKeys - 1 >= wave_key_lo;
-    if (needed) {
-      const bf16* kb = smem + buf * 2 * C::kTileElems;
-      const bf16* vb = kb + C::kTileElems;
-
-      // S^T for the 64 keys of the tile (two 32-key blocks) and this wave's 32 queries.
-      f32x16 s[2];
+  const int vrow = 4 * hl + (s16 >> 2);  // row mod 16; its swizzle does not depend on st or the +8
+  uint32_t v_off[C::kBlocks];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
+  for (int b = 0; b < C::kBlocks; ++b) {
+    const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
+    v_off[b] = static_cast<uint32_t>(vrow * C::kRowBytes + (((col >> 3) ^ swz<NC>(vrow)) * 16) + (col & 7) * 2);
+  }
+  const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
+
+  // One 32-key block [kb, kb + 32) of the tile held in (kt_lds, vt_lds), for this wave.
+  auto do_block = [&](const char* kt_lds, const char* vt_lds, int kb, int mb) __attribute__((always_inline)) {
+    if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;  // no row sees it
+    const bool mh = kb + 31 > q0w;       // some key may be after some row (diagonal)
+    const bool ml = kb < q0w + 32 - W;   // some key may precede some row's window (trailing edge)
+    const int lim = qi - kb - 4 * hl;    // register r's key is visible iff lim - W < reg_key(r) <= lim
+
+    auto compute_s = [&]() __attribute__((always_inline)) {
+      f32x16 s = f32x16{};
 #pragma unroll
-        for (int st = 0; st < C::kSteps; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + (32 * mb + ln) * C::kStride + 16 * st + 8 * hl);
-          s[mb] = mfma(a, qf[st], s[mb]);
-        }
+      for (int st = 0; st < C::kSteps; ++st) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + 32 * mb * C::kRowBytes + k_off[st]);
+        s = mfma(a, qf[st], s);
       }
-
-      // Mask only when some (row, key) pair of the wave x tile lies outside a
-      // window.  Key j is visible to row qi iff 0 <= qi - j < W; keys past T
-      // fail qi - j >= 0 for every stored row, and rows past T are never stored.
-      const bool interior = (k0 + kKeys - 1 <= q0w) && (k0 >= q0w + 31 - W + 1);
-      if (!interior) {
-        const int rel = qi - k0 - 4 * hl;
+      if (mh) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int dist = rel - (32 * mb + 8 * (r >> 2) + (r & 3));
-            if (static_cast<unsigned>(dist) >= static_cast<unsigned>(W)) s[mb][r] = -INFINITY;
-          }
+        for (int r = 0; r < 16; ++r)
+          if (reg_key(r) > lim) s[r] = -INFINITY;
       }
+      if (ml) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (reg_key(r) <= lim - W) s[r] = -INFINITY;
+      }
+      return s;
+    };
 
-      float mx = -INFINITY;
+    const f32x16 s = compute_s();
+    // Lazy reference max: refresh only when some key of this lane would give
+    // p > 2^kTau against the current reference (or the row has no reference yet).
+    float mx = s[0];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      const float m_tile = half_swap_max(mx) * c;
-      // Lazy rescale: only when some row's max grew by more than kLazyTau.
-      if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kLazyTau) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kTau) != 0) {
+      const float m_new = fmaxf(m_run, half_swap_max(mx) * c);
+      if (m_new > m_run) {
+        // m_run = -inf (nothing seen yet): alpha = 0 clears the still-empty state.
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
         m_run = m_new;
+        m_use = m_new;
       }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;  // row with nothing visible yet
-
-      // P^T fragments for the four 16-key MFMA steps.  Step st takes registers
-      // 8*(st&1) .. 8*(st&1)+7 of block st>>1, i.e. keys 16 st + 8 (e/4) + 4 hl + e%4.
-      bf16x8 pf[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c, -m_use));
-          l_run += p0;
-          l_run += p1;
-          pf[st][e] = static_cast<bf16>(p0);
-          pf[st][e + 1] = static_cast<bf16>(p1);
-        }
-
-      // O^T += V^T P^T.
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int b = 0; b < C::kBlocks; ++b) {
-          const bf16x8 a = read_tr(vb + (16 * st + vt_row) * C::kStride + 32 * b + vt_col, 8 * C::kStride);
-          acc[b] = mfma(a, pf[st], acc[b]);
-        }
     }
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+    // P^T fragments of the block's two 16-key MFMA steps: step h takes registers
+    // 8 h .. 8 h + 7, i.e. keys kb + 16 h + 8 (e / 4) + 4 hl + e % 4 for e = 0 .. 7.
+    // The row sum adds exactly the bf16 weights that enter P V.
+    bf16x8 pf[2];
+    float pa = 0.f, pb = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2 pp;
+        pp[0] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e], c, -m_use)));
+        pp[1] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e + 1], c, -m_use)));
+        if (e & 2)
+          pb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pb, false);
+        else
+          pa = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pa, false);
+        pf[h][e] = pp[0];
+        pf[h][e + 1] = pp[1];
+      }
+    l_run += pa + pb;
+
+    // O^T += V^T P^T over the block's two 16-key steps.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row0 = 32 * mb + 16 * h;
+#pragma unroll
+      for (int b = 0; b < C::kBlocks; ++b) {
+        const char* p = vt_lds + row0 * C::kRowBytes + v_off[b];
+        acc[b] = mfma(read_tr(reinterpret_cast<const bf16*>(p), 8 * D), pf[h], acc[b]);  // second read 8 rows down
+      }
+    }
+  };
+
+  auto do_tile = [&](const char* kt_lds, const char* vt_lds, int kt) __attribute__((always_inline)) {
+    const int k0 = kt * kKeys;
+    do_block(kt_lds, vt_lds, k0, 0);
+    do_block(kt_lds, vt_lds, k0 + 32, 1);
+  };
+
+  // One step of the ring: compute tile kt from (kc, vc), fill (kn, vn) with
+  // tile kt + 2, then wait for tile kt + 1 and barrier.  Returns true after the
+  // last tile.
+  auto step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
+    const bool fill = kt + 2 < it.hi;
+    if (fill) issue_tile(kt + 2, kn, vn);
+    do_tile(kc, vc, kt);
+    if (kt + 1 >= it.hi) return true;  // nothing left to wait for; the workgroup is done with LDS
+    if (fill)
+      wait_vm_barrier(kDmaInstr);
+    else
+      wait_vm_barrier(0);
+    return false;
+  };
+
+  // Three-stage ring: tile kt lives in stage kt % 3 and its copy is issued two
+  // steps ahead.  Before the barrier that ends a step, each wave waits only for
+  // its copies of the next tile (the ones issued a step earlier); the copies
+  // issued in this step stay in flight.
+  issue_tile(it.lo, k_lds0, v_lds0);
+  if (it.lo + 1 < it.hi) issue_tile(it.lo + 1, k_lds1, v_lds1);
+  if (it.lo + 1 < it.hi)
+    wait_vm_barrier(kDmaInstr);
+  else
+    wait_vm_barrier(0);
+  for (int kt = it.lo;; kt += 3) {
+    if (step(kt, k_lds0, v_lds0, k_lds2, v_lds2)) break;
+    if (step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
+    if (step(kt + 2, k_lds2, v_lds2, k_lds1, v_lds1)) break;
   }
 
   if (!wave_active) return;
@@ -243,14 +306,8 @@ template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse,
                     const WorkItem* items, int n_items, const int32_t* win_eff,
                     const AttnShape& s, hipStream_t stream) {
-  const size_t smem = Cfg<D>::kSmemBytes;
-  if (smem > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
-    if (e != hipSuccess) return e;
-  }
   const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n_items), dim3(kThreads), smem, stream,
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<bf16*>(o), lse, items, win_eff, s.H, s.T, c);
   return hipGetLastError();
