@@ -31,13 +31,15 @@
 //     lane four consecutive rows of one column.
 //
 // Softmax (log2 domain, p = exp2(s * scale * log2 e - m)).  The reference m of
-// a row is refreshed lazily: each lane takes the max of its 16 scores of the
-// block (v_max3), and only when some lane's max exceeds its row's reference by
-// more than kTau (or a row has no reference yet) does the wave exchange the
-// half-row maxima, rescale O and the row sum, and move the reference.  So
-// every p is <= 2^kTau and the row's true max is >= its reference.  P is
-// packed to bf16 and the row sum adds exactly those bf16 weights with v_dot2,
-// so the normalisation matches the weights used in P V.
+// a row is the exact running max at its last refresh.  A block's weights are
+// first formed against the current reference, packed to bf16 and summed with
+// v_dot2 (so the row sum adds exactly the weights used in P V).  A lane's
+// partial sum bounds each of its weights, so only if some partial sum exceeds
+// 2^10 (or some row of the wave has no reference yet) is the block redone:
+// the wave exchanges the half-row maxima, rescales O and the row sum, moves
+// the reference and forms the weights again.  Hence every p is <= 2^10 and
+// some p of every row was >= 1 when its reference was set, so row sums never
+// underflow.
 // Global loads go through buffer resources whose range ends at the head's
 // last row, so rows past T read as zero without branches.
 #include <cmath>
@@ -54,7 +56,7 @@ constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // query rows per item
 constexpr int kKeys = 64;           // keys per LDS stage
 constexpr int kThreads = 64 * kWaves;
-constexpr float kTau = 8.0f;       // lazy-rescale bound: p <= 2^kTau
+constexpr float kThresh = 1024.0f;  // lazy-rescale bound on every weight p (2^10)
 static_assert(kRows == kFwdBf16RowTile && kKeys == kFwdBf16ColTile, "planner tile mismatch");
 
 template <int D>
@@ -130,6 +132,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   float m_run = -INFINITY;  // reference max of this lane's row (log2 domain)
   float m_use = 0.f;        // m_run, or 0 while the row has seen no visible key (then every p is 0)
   float l_run = 0.f;        // this half-wave's running sum of the bf16 weights
+  bool ready = false;       // every row of the wave has a reference
 
   // DMA sources: instruction j of this wave fills tile chunks P = (wave * kDmaPerWave + j) * 64 + lane,
   // i.e. row P / NC at stored chunk P % NC, which holds logical chunk (P % NC) ^ swz(row).
@@ -199,12 +202,44 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     };
 
     const f32x16 s = compute_s();
-    // Lazy reference max: refresh only when some key of this lane would give
-    // p > 2^kTau against the current reference (or the row has no reference yet).
-    float mx = s[0];
+
+    // P^T fragments of the block's two 16-key MFMA steps: step h takes registers
+    // 8 h .. 8 h + 7, i.e. keys kb + 16 h + 8 (e / 4) + 4 hl + e % 4 for e = 0 .. 7.
+    // part = this lane's sum of exactly the bf16 weights that enter P V.
+    bf16x8 pf[2];
+    float part;
+    auto make_p = [&]() __attribute__((always_inline)) {
+      float pa = 0.f, pb = 0.f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    if (__builtin_amdgcn_ballot_w64(mx * c > m_run + kTau) != 0) {
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          bf16x2 pp;
+          pp[0] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e], c, -m_use)));
+          pp[1] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e + 1], c, -m_use)));
+          if (e & 2)
+            pb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pb, false);
+          else
+            pa = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pa, false);
+          pf[h][e] = pp[0];
+          pf[h][e + 1] = pp[1];
+        }
+      part = pa + pb;
+    };
+
+    // Lazy reference: the weights are formed against the current reference
+    // first; since a lane's partial sum bounds each of its weights, the block is
+    // redone against a refreshed reference only if some partial sum exceeds
+    // 2^kTau (or some row of the wave has no reference yet).
+    bool refresh = !ready;
+    if (ready) {
+      make_p();
+      refresh = __builtin_amdgcn_ballot_w64(part > kThresh) != 0;
+    }
+    if (refresh) {
+      float mx = s[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
       const float m_new = fmaxf(m_run, half_swap_max(mx) * c);
       if (m_new > m_run) {
         // m_run = -inf (nothing seen yet): alpha = 0 clears the still-empty state.
@@ -215,28 +250,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
         m_run = m_new;
         m_use = m_new;
       }
+      ready = __builtin_amdgcn_ballot_w64(m_run == -INFINITY) == 0;
+      make_p();
     }
-
-    // P^T fragments of the block's two 16-key MFMA steps: step h takes registers
-    // 8 h .. 8 h + 7, i.e. keys kb + 16 h + 8 (e / 4) + 4 hl + e % 4 for e = 0 .. 7.
-    // The row sum adds exactly the bf16 weights that enter P V.
-    bf16x8 pf[2];
-    float pa = 0.f, pb = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        bf16x2 pp;
-        pp[0] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e], c, -m_use)));
-        pp[1] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e + 1], c, -m_use)));
-        if (e & 2)
-          pb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pb, false);
-        else
-          pa = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pa, false);
-        pf[h][e] = pp[0];
-        pf[h][e + 1] = pp[1];
-      }
-    l_run += pa + pb;
+    l_run += part;
 
     // O^T += V^T P^T over the block's two 16-key steps.
 #pragma unroll
