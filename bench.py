@@ -161,11 +161,11 @@ def main():
         aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream)
         mark(1)
         if with_bwd:
-            aah.attn_bwd_preprocess(o, do, ws, stream=stream)
+            aah.attn_bwd_preprocess(o, do, lse, ws, wl.scale, stream=stream)
             mark(2)
-            aah.attn_bwd_dkdv(q, k, v, do, lse, wl.windows, dk, dv, ws, wl.scale, stream=stream)
+            aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws, wl.scale, stream=stream)
             mark(3)
-            aah.attn_bwd_dq(q, k, v, do, lse, wl.windows, dq, ws, wl.scale, stream=stream)
+            aah.attn_bwd_dq(q, k, v, do, wl.windows, dq, ws, wl.scale, stream=stream)
             mark(4)
 
     for _ in range(args.warmup):

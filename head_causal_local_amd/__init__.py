@@ -127,45 +127,46 @@ def _ws(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def attn_bwd_preprocess(o, do, workspace, stream=None):
-    """Backward step 1: D = rowsum(do * o) into the workspace."""
+def attn_bwd_preprocess(o, do, lse, workspace, scale: Optional[float] = None, stream=None):
+    """Backward step 1: lse2 = lse * log2(e) and sD = scale * rowsum(do * o) into the workspace."""
     _check_operand("do", do, o)
     B, H, T, d = o.shape
+    if lse.shape != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), B, H, T, d, _dtype_code(o), ptr, nbytes,
-                                        _stream_ptr(o, stream)))
+    check(lib().aah_attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, T, d, _dtype_code(o),
+                                        scale, ptr, nbytes, _stream_ptr(o, stream)))
 
 
-def _bwd_args(q, k, v, do, lse, windows, scale):
+def _bwd_args(q, k, v, do, windows, scale):
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_operand(name, t, q)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
         raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
-    if lse.shape != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     return B, H, T, d, w, float(scale)
 
 
-def attn_bwd_dkdv(q, k, v, do, lse, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 2: dK and dV (needs D from attn_bwd_preprocess in the workspace)."""
-    B, H, T, d, w, scale = _bwd_args(q, k, v, do, lse, windows, scale)
+def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None):
+    """Backward step 2: dK and dV (needs attn_bwd_preprocess's workspace, same scale)."""
+    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
     _check_operand("dk", dk, q)
     _check_operand("dv", dv, q)
     ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), _wptr(w),
+    check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
                                   B, H, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
 
 
-def attn_bwd_dq(q, k, v, do, lse, windows, dq, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 3: dQ (needs D from attn_bwd_preprocess in the workspace)."""
-    B, H, T, d, w, scale = _bwd_args(q, k, v, do, lse, windows, scale)
+def attn_bwd_dq(q, k, v, do, windows, dq, workspace, scale: Optional[float] = None, stream=None):
+    """Backward step 3: dQ (needs attn_bwd_preprocess's workspace, same scale)."""
+    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
     _check_operand("dq", dq, q)
     ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), lse.data_ptr(), _wptr(w),
+    check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
                                 B, H, T, d, _dtype_code(q), scale, dq.data_ptr(), ptr, nbytes,
                                 _stream_ptr(q, stream)))
 

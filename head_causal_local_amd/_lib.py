@@ -67,15 +67,14 @@ def _declare(lib):
                                  c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
                                  c_void_p]
     lib.aah_attn_bwd_preprocess.restype = c_int
-    lib.aah_attn_bwd_preprocess.argtypes = [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_void_p,
-                                            c_size_t, c_void_p]
+    lib.aah_attn_bwd_preprocess.argtypes = [c_void_p, c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                            c_float, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_bwd_dkdv.restype = c_int
-    lib.aah_attn_bwd_dkdv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int,
-                                      c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
-                                      c_void_p]
+    lib.aah_attn_bwd_dkdv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int, c_int, c_int,
+                                      c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_bwd_dq.restype = c_int
-    lib.aah_attn_bwd_dq.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int, c_int,
-                                    c_int, c_int, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.aah_attn_bwd_dq.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int, c_int, c_int,
+                                    c_int, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_workspace_size.restype = c_size_t
     lib.aah_attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_tile_shape.restype = c_int

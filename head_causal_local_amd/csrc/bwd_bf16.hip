@@ -5,21 +5,25 @@
 // i - W < j <= i), given the forward's per-row log-sum-exp:
 //   P = exp(scale Q K^T - lse),  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+// The preprocess step leaves lse2 = lse * log2(e) and sD = scale * D per row in
+// the workspace, so a weight is exp2(fma(s, scale log2 e, -lse2)) and the
+// scaled dS is p * fma(dp, scale, -sD).
 //
 // Two kernels, no atomics, every output written exactly once:
 //
 // bwd_dkdv_kernel -- one item = 128 keys of one head (4 waves x 32 keys) and
 //   the 64-query steps that can see them.  K and V rows stay in registers, dK
-//   and dV accumulate in registers.  Per step (Q, dO, lse, D double-buffered
-//   in LDS): S = Q K^T and dP = dO V^T with M = queries, N = the wave's keys,
-//   so P and dS come out with one key per lane and are directly the B operand
-//   of dV^T += dO^T P and dK^T += Q^T dS (M = d, N = keys, K = queries); the
-//   A operands are read transposed from the row-major Q / dO tiles.
+//   and dV accumulate in registers.  Per step the Q and dO tiles and the
+//   step's lse2 / sD rows are copied HBM -> LDS (three-stage ring).  For each
+//   32-query block S = Q K^T and dP = dO V^T with M = queries, so P and dS come
+//   out with one key per lane and are directly the B operand of
+//   dV^T += dO^T P and dK^T += Q^T dS (M = d, N = keys, K = queries); the A
+//   operands are read transposed from the row-major Q / dO tiles.
 //
 // bwd_dq_kernel -- one item = 128 queries of one head (4 waves x 32 queries)
 //   and the 64-key tiles of their windows (the forward's work list).  Q and dO
-//   rows stay in registers; K and V tiles are double-buffered in LDS.  Per
-//   tile: S^T = K Q^T and dP^T = V dO^T with M = keys, N = the wave's queries,
+//   rows stay in registers; K and V tiles come through the same kind of LDS
+//   ring.  For each 32-key block S^T = K Q^T and dP^T = V dO^T with M = keys,
 //   so P^T and dS^T come out with one query per lane and are directly the B
 //   operand of dQ^T += K^T dS^T, whose A operand is read transposed from the
 //   row-major K tile.
@@ -29,10 +33,10 @@
 // accumulator in HBM and no atomics (which this device resolves in memory,
 // not in L2), and every gradient is deterministic.
 //
-// In both kernels a wave skips the MFMAs of a step none of its rows/keys can
-// see, and only steps that touch a window edge or the diagonal evaluate the
-// mask.  Rows and keys past T read as zero through bounds-checked buffer
-// loads and are never stored.
+// Both kernels skip 32-row blocks that no row of the wave sees and mask only
+// blocks that cross the diagonal or the window's trailing edge.  Tiles are
+// row-major with the XOR chunk swizzle of the forward kernel.  Rows past T
+// read as zero (bounded buffer resources) and contribute nothing.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -52,27 +56,76 @@ static_assert(kStat == kFwdBf16RowTile && kStep == kFwdBf16ColTile, "planner til
 
 template <int D>
 struct Cfg {
-  static constexpr int kStride = D + 8;              // LDS row stride (elements): 16-byte pad
-  static constexpr int kTile = kStep * kStride;      // one streamed tile
-  static constexpr int kSteps = D / 16;              // MFMA k-steps over d
-  static constexpr int kBlocks = D / 32;             // 32-wide blocks over d
-  static constexpr int kChunkPerRow = D / 8;         // 16-byte chunks per row
-  static constexpr int kChunks = kStep * kChunkPerRow / kThreads;  // per thread per tile
-  static constexpr size_t kBytes = 2u * 2u * kTile * sizeof(bf16) + 2u * 2u * kStep * sizeof(float);
-  static_assert(kChunks >= 1, "tile too small for the thread count");
+  static constexpr int kNC = D / 8;                     // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kTileBytes = kStep * kRowBytes;  // one streamed tile
+  static constexpr int kDmaPerWave = kNC / kWaves;      // 1 KiB copies per wave per tensor per step
+  static constexpr int kSteps = D / 16;                 // MFMA k-steps over d
+  static constexpr int kBlocks = D / 32;                // 32-wide blocks over d
+  static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
 };
+
+// Row offset (within a 32-row block, before the 4 hl lane offset) held by MFMA output register r.
+__device__ constexpr int reg_row(int r) { return 8 * (r >> 2) + (r & 3); }
+
+// Lane-constant LDS offsets shared by both kernels, for a row-major swizzled tile:
+//   rd[st]: MFMA A operand read with ds_read_b128 -- row ln, logical chunk 2 st + hl;
+//   tr[b]:  ds_read_b64_tr_b16 of row 4 hl + s16 / 4 (+ 16 step, + 8 for the second
+//           read), columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3;
+//   dma[j]: source offset of this lane's chunk in the wave's j-th 1 KiB copy.
+template <int D>
+struct Offsets {
+  uint32_t rd[Cfg<D>::kSteps];
+  uint32_t tr[Cfg<D>::kBlocks];
+  uint32_t dma[Cfg<D>::kDmaPerWave];
+  __device__ Offsets(int wave, int lane) {
+    using C = Cfg<D>;
+    constexpr int NC = C::kNC;
+    const int hl = lane >> 5, ln = lane & 31, g = lane >> 4, s16 = lane & 15;
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st)
+      rd[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
+    const int trow = 4 * hl + (s16 >> 2);
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b) {
+      const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
+      tr[b] = static_cast<uint32_t>(trow * C::kRowBytes + (((col >> 3) ^ swz<NC>(trow)) * 16) + (col & 7) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < C::kDmaPerWave; ++j) {
+      const int P = (wave * C::kDmaPerWave + j) * 64 + lane;
+      const int row = P / NC;
+      dma[j] = static_cast<uint32_t>(row * C::kRowBytes + (((P % NC) ^ swz<NC>(row)) * 16));
+    }
+  }
+};
+
+// Copy rows [r0, r0 + 64) of one head's [T, D] tensor into a swizzled LDS tile
+// (this wave's share); rows past T arrive as zeros.
+template <int D>
+__device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char* dst, int wave,
+                                          const Offsets<D>& o) {
+  using C = Cfg<D>;
+  const i32x4 r = rsrc_words(head + static_cast<size_t>(r0) * D, static_cast<uint32_t>(T - r0) * C::kRowBytes);
+#pragma unroll
+  for (int j = 0; j < C::kDmaPerWave; ++j) dma16(r, dst + (wave * C::kDmaPerWave + j) * 1024, o.dma[j]);
+}
 
 // ---------------------------------------------------------------- dK, dV
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, int H, int T, float scale) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ SD,
+                     bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
+                     const int32_t* __restrict__ win_eff, int H, int T, float scale) {
   using C = Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  float* const rowf = reinterpret_cast<float*>(smem + 2 * 2 * C::kTile);  // [buf][lse2 | scale*D][kStep]
+  // Three-stage ring; stage = {Q tile, dO tile, lse2 row, sD row}.
+  constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
+  __shared__ __attribute__((aligned(1024))) char ring0[kStage];
+  __shared__ __attribute__((aligned(1024))) char ring1[kStage];
+  __shared__ __attribute__((aligned(1024))) char ring2[kStage];
+  constexpr int kG = C::kTileBytes, kL = 2 * C::kTileBytes, kDd = kL + kStep * 4;  // offsets in a stage
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
@@ -80,63 +133,53 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const float c = scale * kLog2e;
-  const uint32_t slice = static_cast<uint32_t>(T) * D * sizeof(bf16);
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, slice);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + base, slice);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(LSE + rbase, static_cast<uint32_t>(T) * sizeof(float));
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(Dv + rbase, static_cast<uint32_t>(T) * sizeof(float));
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
-  const int g = lane >> 4, s16 = lane & 15;
   const int k0w = it.tile * kStat + 32 * wave;  // first key of this wave
   const int key = k0w + ln;                      // this lane's key (column of S)
+  const bool wave_active = k0w < T;
+  const Offsets<D> off(wave, lane);
 
   // K and V rows (B operands of S = Q K^T and dP = dO V^T): lane holds dims 16 st + 8 hl + 0..7.
   bf16x8 kf[C::kSteps], vf[C::kSteps];
   {
+    const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slice);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slice);
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
-      const uint32_t off = (static_cast<uint32_t>(key) * D + 16 * st + 8 * hl) * sizeof(bf16);
-      kf[st] = __builtin_bit_cast(bf16x8, load16(rk, off));
-      vf[st] = __builtin_bit_cast(bf16x8, load16(rv, off));
+      const uint32_t o = static_cast<uint32_t>(key) * C::kRowBytes + (16 * st + 8 * hl) * 2;
+      kf[st] = __builtin_bit_cast(bf16x8, load16(rk, o));
+      vf[st] = __builtin_bit_cast(bf16x8, load16(rv, o));
     }
+    // Wait for these loads here rather than inside the loop, where the wait
+    // would also cover LDS copies in flight.
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
   }
 
-  u32x4 stq[C::kChunks], stg[C::kChunks];
-  float st_l = 0.f, st_d = 0.f;
-  auto load_step = [&](int qt) {
+  // Stage fill: Q and dO tiles (every wave its share), lse2 row (wave 0), sD row (wave 1).
+  auto fill = [&](int qt, char* st) __attribute__((always_inline)) {
     const int q0 = qt * kStep;
-#pragma unroll
-    for (int i = 0; i < C::kChunks; ++i) {
-      const int cidx = tid + kThreads * i;
-      const uint32_t off = (static_cast<uint32_t>(q0 + cidx / C::kChunkPerRow) * D + (cidx % C::kChunkPerRow) * 8) *
-                           sizeof(bf16);
-      stq[i] = load16(rq, off);
-      stg[i] = load16(rg, off);
-    }
-    if (tid < kStep) {
-      // Rows past T read lse = D = 0; their Q and dO are zero, so they add nothing.
-      st_l = load_f32(rl, static_cast<uint32_t>(q0 + tid) * sizeof(float)) * kLog2e;
-      st_d = load_f32(rd, static_cast<uint32_t>(q0 + tid) * sizeof(float)) * scale;
+    copy_tile<D>(Q + base, q0, T, st, wave, off);
+    copy_tile<D>(dO + base, q0, T, st + kG, wave, off);
+    if (wave < 2) {
+      const float* src = (wave == 0 ? LSE2 : SD) + rbase + q0;
+      dma4(rsrc_words(src, static_cast<uint32_t>(T - q0) * 4), st + (wave == 0 ? kL : kDd),
+           static_cast<uint32_t>(lane) * 4);
     }
   };
-  auto store_step = [&](int buf) {
-    bf16* qs = smem + buf * 2 * C::kTile;
-    bf16* gs = qs + C::kTile;
-#pragma unroll
-    for (int i = 0; i < C::kChunks; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int off = (cidx / C::kChunkPerRow) * C::kStride + (cidx % C::kChunkPerRow) * 8;
-      *reinterpret_cast<u32x4*>(qs + off) = stq[i];
-      *reinterpret_cast<u32x4*>(gs + off) = stg[i];
-    }
-    if (tid < kStep) {
-      rowf[buf * 2 * kStep + tid] = st_l;
-      rowf[buf * 2 * kStep + kStep + tid] = st_d;
+  constexpr int kFill = 2 * C::kDmaPerWave;  // copies per wave per fill, plus one for waves 0 and 1
+  auto wait_barrier = [&](bool keep_next) __attribute__((always_inline)) {
+    if (keep_next) {
+      if (wave < 2)
+        wait_vm_barrier(kFill + 1);
+      else
+        wait_vm_barrier(kFill);
+    } else {
+      wait_vm_barrier(0);
     }
   };
 
@@ -146,73 +189,77 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
     dk[b] = f32x16{};
     dv[b] = f32x16{};
   }
-  // Transposed reads in the slot order of the P / dS registers (second read 8 rows down).
-  const int tr_off = (4 * hl + (s16 >> 2)) * C::kStride + 16 * (g & 1) + 4 * (s16 & 3);
 
-  load_step(it.lo);
-  store_step(0);
-  __syncthreads();
-
-  for (int qt = it.lo; qt < it.hi; ++qt) {
-    const int buf = (qt - it.lo) & 1;
-    const bool has_next = qt + 1 < it.hi;
-    if (has_next) load_step(qt + 1);
-    const int q0 = qt * kStep;
-
-    // Can any query of this step see any key of this wave?
-    if (k0w <= q0 + kStep - 1 && k0w + 31 > q0 - W && k0w < T) {
-      const bf16* qs = smem + buf * 2 * C::kTile;
-      const bf16* gs = qs + C::kTile;
-      const float* lse2 = rowf + buf * 2 * kStep;
-      const float* sD = lse2 + kStep;
-      f32x16 s[2], dp[2];
+  // One 32-query block [qb, qb + 32) of the stage in st (mb = block within the step).
+  auto do_block = [&](const char* st, int qb, int mb) __attribute__((always_inline)) {
+    // Query i sees key j iff 0 <= i - j < W; the wave's keys are [k0w, k0w + 32).
+    if (!(wave_active && qb < T && qb + 31 >= k0w && qb <= k0w + 30 + W)) return;
+    const char* qs = st;
+    const char* gs = st + kG;
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-        dp[mb] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < C::kSteps; ++st) {
-          const int off = (32 * mb + ln) * C::kStride + 16 * st + 8 * hl;
-          s[mb] = mfma(*reinterpret_cast<const bf16x8*>(qs + off), kf[st], s[mb]);
-          dp[mb] = mfma(*reinterpret_cast<const bf16x8*>(gs + off), vf[st], dp[mb]);
-        }
-      }
-      // Register r of block mb holds query q0 + 32 mb + 8 (r/4) + 4 hl + r%4.
-      const bool interior = (k0w + 31 <= q0) && (k0w > q0 + kStep - 1 - W);
-      bf16x8 pf[4], df[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r0 = 32 * mb + 8 * i + 4 * hl;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + r0);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + r0);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int r = 4 * i + j;
-            float sv = s[mb][r];
-            if (!interior && static_cast<unsigned>(q0 + r0 + j - key) >= static_cast<unsigned>(W)) sv = -INFINITY;
-            const float p = __builtin_amdgcn_exp2f(fmaf(sv, c, -l4[j]));
-            const float ds = p * fmaf(dp[mb][r], scale, -d4[j]);
-            const int st = 2 * mb + (i >> 1);
-            const int e = 4 * (i & 1) + j;
-            pf[st][e] = static_cast<bf16>(p);
-            df[st][e] = static_cast<bf16>(ds);
-          }
-        }
-      // dV^T += dO^T P,  dK^T += Q^T dS   (K = the step's 64 queries in 4 MFMA steps).
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int b = 0; b < C::kBlocks; ++b) {
-          const int off = 16 * st * C::kStride + 32 * b + tr_off;
-          dv[b] = mfma(read_tr(gs + off, 8 * C::kStride), pf[st], dv[b]);
-          dk[b] = mfma(read_tr(qs + off, 8 * C::kStride), df[st], dk[b]);
-        }
+    for (int k = 0; k < C::kSteps; ++k) {
+      s = mfma(*reinterpret_cast<const bf16x8*>(qs + 32 * mb * C::kRowBytes + off.rd[k]), kf[k], s);
+      dp = mfma(*reinterpret_cast<const bf16x8*>(gs + 32 * mb * C::kRowBytes + off.rd[k]), vf[k], dp);
     }
+    // Register r holds query qb + 4 hl + reg_row(r); i - j = reg_row(r) - lim.
+    const int lim = key - qb - 4 * hl;
+    if (qb < k0w + 31) {  // some query precedes some key
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) < lim ? -INFINITY : s[r];
+    }
+    if (qb + 31 >= k0w + W) {  // some query is W or more past some key
+      const int hi = lim + W;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) >= hi ? -INFINITY : s[r];
+    }
+    // Registers 4 i .. 4 i + 3 hold queries qb + 8 i + 4 hl + 0..3: one 16-byte read each of lse2 and sD.
+    const float* l2 = reinterpret_cast<const float*>(st + kL) + 32 * mb + 4 * hl;
+    const float* sd = reinterpret_cast<const float*>(st + kDd) + 32 * mb + 4 * hl;
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2 + 8 * i);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * i + j;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[j]));
+        const float ds = p * fmaf(dp[r], scale, -d4[j]);
+        pf[r >> 3][r & 7] = static_cast<bf16>(p);
+        df[r >> 3][r & 7] = static_cast<bf16>(ds);
+      }
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS over the block's two 16-query steps.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
+#pragma unroll
+      for (int b = 0; b < C::kBlocks; ++b) {
+        dv[b] = mfma(read_tr(reinterpret_cast<const bf16*>(gs + row0 + off.tr[b]), 8 * D), pf[h], dv[b]);
+        dk[b] = mfma(read_tr(reinterpret_cast<const bf16*>(qs + row0 + off.tr[b]), 8 * D), df[h], dk[b]);
+      }
+    }
+  };
 
-    if (has_next) store_step(buf ^ 1);
-    __syncthreads();
+  // Ring: step qt uses stage (qt - lo) % 3 and fills the stage of step qt + 2.
+  auto step = [&](int qt, const char* cur, char* nxt2) __attribute__((always_inline)) {
+    const bool more = qt + 2 < it.hi;
+    if (more) fill(qt + 2, nxt2);
+    const int q0 = qt * kStep;
+    do_block(cur, q0, 0);
+    do_block(cur, q0 + 32, 1);
+    if (qt + 1 >= it.hi) return true;
+    wait_barrier(more);
+    return false;
+  };
+  fill(it.lo, ring0);
+  if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+  wait_barrier(it.lo + 1 < it.hi);
+  for (int qt = it.lo;; qt += 3) {
+    if (step(qt, ring0, ring2)) break;
+    if (step(qt + 1, ring1, ring0)) break;
+    if (step(qt + 2, ring2, ring1)) break;
   }
 
   if (key >= T) return;
@@ -232,13 +279,16 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
 // ---------------------------------------------------------------- dQ
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    const bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    bf16* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff, int H,
-    int T, float scale) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2)))
+void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+                   const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ SD,
+                   bf16* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
+                   int H, int T, float scale) {
   using C = Cfg<D>;
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
+  __shared__ __attribute__((aligned(1024))) char ring0[kStage];
+  __shared__ __attribute__((aligned(1024))) char ring1[kStage];
+  __shared__ __attribute__((aligned(1024))) char ring2[kStage];
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
@@ -246,119 +296,114 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const float c = scale * kLog2e;
-  const uint32_t slice = static_cast<uint32_t>(T) * D * sizeof(bf16);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slice);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slice);
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
-  const int g = lane >> 4, s16 = lane & 15;
   const int q0w = it.tile * kStat + 32 * wave;   // first query of this wave
   const int qi = q0w + ln;                        // this lane's query (column of S^T)
   const bool wave_active = q0w < T;
   const int wave_key_lo = q0w - W + 1;
   const int wave_key_hi = min(q0w + 31, T - 1);
+  const Offsets<D> off(wave, lane);
 
   // Q and dO rows of this lane's query (B operands of S^T = K Q^T and dP^T = V dO^T).
   bf16x8 qf[C::kSteps], gf[C::kSteps];
+  float lse2 = 0.f, sD = 0.f;
   {
+    const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, slice);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + base, slice);
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
-      const uint32_t off = (static_cast<uint32_t>(qi) * D + 16 * st + 8 * hl) * sizeof(bf16);
-      qf[st] = __builtin_bit_cast(bf16x8, load16(rq, off));
-      gf[st] = __builtin_bit_cast(bf16x8, load16(rg, off));
+      const uint32_t o = static_cast<uint32_t>(qi) * C::kRowBytes + (16 * st + 8 * hl) * 2;
+      qf[st] = __builtin_bit_cast(bf16x8, load16(rq, o));
+      gf[st] = __builtin_bit_cast(bf16x8, load16(rg, o));
     }
+    const uint32_t rows = static_cast<uint32_t>(T) * 4;
+    lse2 = load_f32(make_rsrc(LSE2 + rbase, rows), static_cast<uint32_t>(qi) * 4);
+    sD = load_f32(make_rsrc(SD + rbase, rows), static_cast<uint32_t>(qi) * 4);
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(qf[st]), "v"(gf[st]));
+    __asm__ volatile("" ::"v"(lse2), "v"(sD));
   }
-  const bool row_ok = qi < T;
-  const float lse2 = row_ok ? LSE[rbase + qi] * kLog2e : 0.f;
-  const float sD = row_ok ? Dv[rbase + qi] * scale : 0.f;
 
-  u32x4 stk[C::kChunks], stv[C::kChunks];
-  auto load_tile = [&](int kt) {
+  auto fill = [&](int kt, char* st) __attribute__((always_inline)) {
     const int k0 = kt * kStep;
-#pragma unroll
-    for (int i = 0; i < C::kChunks; ++i) {
-      const int cidx = tid + kThreads * i;
-      const uint32_t off = (static_cast<uint32_t>(k0 + cidx / C::kChunkPerRow) * D + (cidx % C::kChunkPerRow) * 8) *
-                           sizeof(bf16);
-      stk[i] = load16(rk, off);
-      stv[i] = load16(rv, off);
-    }
+    copy_tile<D>(K + base, k0, T, st, wave, off);
+    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, off);
   };
-  auto store_tile = [&](int buf) {
-    bf16* ks = smem + buf * 2 * C::kTile;
-    bf16* vs = ks + C::kTile;
-#pragma unroll
-    for (int i = 0; i < C::kChunks; ++i) {
-      const int cidx = tid + kThreads * i;
-      const int off = (cidx / C::kChunkPerRow) * C::kStride + (cidx % C::kChunkPerRow) * 8;
-      *reinterpret_cast<u32x4*>(ks + off) = stk[i];
-      *reinterpret_cast<u32x4*>(vs + off) = stv[i];
-    }
-  };
+  constexpr int kFill = 2 * C::kDmaPerWave;
 
   f32x16 acc[C::kBlocks];
 #pragma unroll
   for (int b = 0; b < C::kBlocks; ++b) acc[b] = f32x16{};
-  const int tr_off = (4 * hl + (s16 >> 2)) * C::kStride + 16 * (g & 1) + 4 * (s16 & 3);
 
-  load_tile(it.lo);
-  store_tile(0);
-  __syncthreads();
-
-  for (int kt = it.lo; kt < it.hi; ++kt) {
-    const int buf = (kt - it.lo) & 1;
-    const bool has_next = kt + 1 < it.hi;
-    if (has_next) load_tile(kt + 1);
-    const int k0 = kt * kStep;
-
-    if (wave_active && k0 <= wave_key_hi && k0 + kStep - 1 >= wave_key_lo) {
-      const bf16* ks = smem + buf * 2 * C::kTile;
-      const bf16* vs = ks + C::kTile;
-      f32x16 s[2], dp[2];
+  // One 32-key block [kb, kb + 32) of the stage in st.
+  auto do_block = [&](const char* st, int kb, int mb) __attribute__((always_inline)) {
+    if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;
+    const char* ks = st;
+    const char* vs = st + C::kTileBytes;
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        s[mb] = f32x16{};
-        dp[mb] = f32x16{};
-#pragma unroll
-        for (int st = 0; st < C::kSteps; ++st) {
-          const int off = (32 * mb + ln) * C::kStride + 16 * st + 8 * hl;
-          s[mb] = mfma(*reinterpret_cast<const bf16x8*>(ks + off), qf[st], s[mb]);
-          dp[mb] = mfma(*reinterpret_cast<const bf16x8*>(vs + off), gf[st], dp[mb]);
-        }
-      }
-      // Register r of block mb holds key k0 + 32 mb + 8 (r/4) + 4 hl + r%4.  Keys past T
-      // fail qi - key >= 0 for every stored row.
-      const bool interior = (k0 + kStep - 1 <= q0w) && (k0 >= q0w + 31 - W + 1);
-      const int rel = qi - k0 - 4 * hl;
-      bf16x8 df[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int mb = st >> 1, r = 8 * (st & 1) + e;
-          float sv = s[mb][r];
-          if (!interior && static_cast<unsigned>(rel - (32 * mb + 8 * (r >> 2) + (r & 3))) >= static_cast<unsigned>(W))
-            sv = -INFINITY;
-          const float p = __builtin_amdgcn_exp2f(fmaf(sv, c, -lse2));
-          df[st][e] = static_cast<bf16>(p * fmaf(dp[mb][r], scale, -sD));
-        }
-      // dQ^T += K^T dS^T  (K = the tile's 64 keys in 4 MFMA steps, slot order of the dS registers).
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int b = 0; b < C::kBlocks; ++b)
-          acc[b] = mfma(read_tr(ks + 16 * st * C::kStride + 32 * b + tr_off, 8 * C::kStride), df[st], acc[b]);
+    for (int k = 0; k < C::kSteps; ++k) {
+      s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd[k]), qf[k], s);
+      dp = mfma(*reinterpret_cast<const bf16x8*>(vs + 32 * mb * C::kRowBytes + off.rd[k]), gf[k], dp);
     }
+    // Register r holds key kb + 4 hl + reg_row(r), visible iff lim - W < reg_row(r) <= lim.
+    const int lim = qi - kb - 4 * hl;
+    if (kb + 31 > q0w) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) > lim ? -INFINITY : s[r];
+    }
+    if (kb < q0w + 32 - W) {
+      const int lo = lim - W;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) <= lo ? -INFINITY : s[r];
+    }
+    bf16x8 df[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
+      df[r >> 3][r & 7] = static_cast<bf16>(p * fmaf(dp[r], scale, -sD));
+    }
+    // dQ^T += K^T dS^T over the block's two 16-key steps (slot order of the dS registers).
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
+#pragma unroll
+      for (int b = 0; b < C::kBlocks; ++b)
+        acc[b] = mfma(read_tr(reinterpret_cast<const bf16*>(ks + row0 + off.tr[b]), 8 * D), df[h], acc[b]);
+    }
+  };
 
-    if (has_next) store_tile(buf ^ 1);
-    __syncthreads();
+  auto step = [&](int kt, const char* cur, char* nxt2) __attribute__((always_inline)) {
+    const bool more = kt + 2 < it.hi;
+    if (more) fill(kt + 2, nxt2);
+    const int k0 = kt * kStep;
+    do_block(cur, k0, 0);
+    do_block(cur, k0 + 32, 1);
+    if (kt + 1 >= it.hi) return true;
+    if (more)
+      wait_vm_barrier(kFill);
+    else
+      wait_vm_barrier(0);
+    return false;
+  };
+  fill(it.lo, ring0);
+  if (it.lo + 1 < it.hi) {
+    fill(it.lo + 1, ring1);
+    wait_vm_barrier(kFill);
+  } else {
+    wait_vm_barrier(0);
+  }
+  for (int kt = it.lo;; kt += 3) {
+    if (step(kt, ring0, ring2)) break;
+    if (step(kt + 1, ring1, ring0)) break;
+    if (step(kt + 2, ring2, ring1)) break;
   }
 
-  if (!row_ok) return;
+  if (qi >= T) return;
   bf16* dqrow = dQ + base + static_cast<size_t>(qi) * D;
   // dQ^T block b, register r: dim 32 b + 8 (r/4) + 4 hl + r%4 of this lane's query.
 #pragma unroll
@@ -369,59 +414,46 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(
                    acc[b][4 * i + 3]);
 }
 
-template <typename Kernel>
-hipError_t allow_smem(Kernel* k, size_t bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             static_cast<int>(bytes));
-}
-
 template <int D>
-hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse, const float* Dv,
+hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* sd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
                   const AttnShape& s, hipStream_t stream) {
-  const size_t smem = Cfg<D>::kBytes;
-  hipError_t e = allow_smem(&bwd_dkdv_kernel<D>, smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_items), dim3(kThreads), smem, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, Dv,
-                     static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
+  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse2,
+                     sd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* lse, const float* Dv,
+hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* sd,
                 void* dq, const WorkItem* items, int n_items, const int32_t* win_eff, const AttnShape& s,
                 hipStream_t stream) {
-  const size_t smem = Cfg<D>::kBytes;
-  hipError_t e = allow_smem(&bwd_dq_kernel<D>, smem);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), smem, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, Dv,
-                     static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
+  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse2,
+                     sd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                                const float* D, void* dk, void* dv, const WorkItem* items, int n_items,
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                                const float* sd, void* dk, void* dv, const WorkItem* items, int n_items,
                                 const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dkdv_d<32>(q, k, v, dout, lse, D, dk, dv, items, n_items, win_eff, s, stream);
-    case 64: return dkdv_d<64>(q, k, v, dout, lse, D, dk, dv, items, n_items, win_eff, s, stream);
-    case 128: return dkdv_d<128>(q, k, v, dout, lse, D, dk, dv, items, n_items, win_eff, s, stream);
+    case 32: return dkdv_d<32>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
+    case 64: return dkdv_d<64>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
+    case 128: return dkdv_d<128>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                              const float* D, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
+                              const float* sd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
                               const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_d<32>(q, k, v, dout, lse, D, dq, items, n_items, win_eff, s, stream);
-    case 64: return dq_d<64>(q, k, v, dout, lse, D, dq, items, n_items, win_eff, s, stream);
-    case 128: return dq_d<128>(q, k, v, dout, lse, D, dq, items, n_items, win_eff, s, stream);
+    case 32: return dq_d<32>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
+    case 64: return dq_d<64>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
+    case 128: return dq_d<128>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -82,6 +82,17 @@ __device__ inline void dma16(const i32x4& rsrc, const void* lds_base, uint32_t b
                    : "memory", "m0");
 }
 
+// As dma16 with 4 bytes per lane (buffer_load_dword ... lds): lane i's word
+// lands at lds_base + 4 i.
+__device__ inline void dma4(const i32x4& rsrc, const void* lds_base, uint32_t byte_off) {
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (const __attribute__((address_space(3))) char*)(lds_base)));
+  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(rsrc)
+                   : "memory", "m0");
+}
+
 // Workgroup barrier after waiting until at most n of this wave's vector-memory
 // operations (loads, LDS copies) are outstanding; n is a literal 0..15.  The
 // memory clobber keeps the compiler from moving memory accesses across it.

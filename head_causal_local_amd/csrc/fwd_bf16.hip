@@ -68,7 +68,7 @@ struct Cfg {
   static constexpr int kSteps = D / 16;             // MFMA k-steps over d for S^T
   static constexpr int kBlocks = D / 32;            // 32-row blocks of O^T
   // Resident waves per SIMD the register allocation is sized for.
-  static constexpr int kWavesPerSimd = D <= 64 ? 4 : 2;
+  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 3 : 1;
   static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
 };
 

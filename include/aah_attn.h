@@ -119,27 +119,29 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
 /*
  * The backward's steps as separate calls, for callers that schedule or time
  * them.  Arguments mean what they mean for aah_attn_bwd and the same checks
- * apply; the workspace carries D from the first step to the other two.
- *   aah_attn_bwd_preprocess: D_i = dout_i . o_i (fp32 [B,H,T], into the
- *     workspace).  Must complete before either of the others starts.
+ * apply; the workspace carries two fp32 [B,H,T] arrays from the first step to
+ * the other two (lse2 = lse * log2(e) at byte 0, then sD = scale * D at the
+ * next 256-byte boundary after B*H*T floats).
+ *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes lse2 and sD into the
+ *     workspace.  Must complete before either of the others starts.
  *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel).
  *   aah_attn_bwd_dq:   writes dq (query-stationary kernel).
  * dkdv and dq only read the workspace and may run in either order or
- * concurrently on different streams once the preprocess has completed.
+ * concurrently on different streams once the preprocess has completed; they
+ * must use the scale the preprocess was given.
  */
-aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, int B, int H, int T, int d,
-                                   aah_dtype dt, void* workspace, size_t workspace_bytes,
+aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int T, int d,
+                                   aah_dtype dt, float scale, void* workspace, size_t workspace_bytes,
                                    aah_stream_t stream);
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                             const float* lse, const int32_t* windows, int B, int H, int T, int d,
-                             aah_dtype dt, float scale, void* dk, void* dv,
-                             const void* workspace, size_t workspace_bytes, aah_stream_t stream);
+                             const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
+                             void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                             aah_stream_t stream);
 
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                           const float* lse, const int32_t* windows, int B, int H, int T, int d,
-                           aah_dtype dt, float scale, void* dq,
-                           const void* workspace, size_t workspace_bytes, aah_stream_t stream);
+                           const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
+                           void* dq, const void* workspace, size_t workspace_bytes, aah_stream_t stream);
 
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */

@@ -243,9 +243,9 @@ def test_backward_deterministic_and_steps():
     g2 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
     ws = torch.empty(aah.workspace_size(2, 3, 700, 64, "bf16"), dtype=torch.uint8, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    aah.attn_bwd_preprocess(o, do, ws)
-    aah.attn_bwd_dq(q, k, v, do, lse, wl.windows, dq, ws)     # either order after the preprocess
-    aah.attn_bwd_dkdv(q, k, v, do, lse, wl.windows, dk, dv, ws)
+    aah.attn_bwd_preprocess(o, do, lse, ws)
+    aah.attn_bwd_dq(q, k, v, do, wl.windows, dq, ws)     # either order after the preprocess
+    aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws)
     torch.cuda.synchronize()
     for a, b, c in zip(g1, g2, (dq, dk, dv)):
         assert torch.equal(a, b)
