@@ -166,12 +166,12 @@ void bwd_tiles(aah_dtype dt, int* row, int* col) {
   }
 }
 
-// Workspace of the backward: lse2 = lse * log2(e) and sD = scale * D, fp32
-// [B,H,T] each, every array starting on a 256-byte boundary.
+// Workspace of the backward: nls = -lse / scale and nD = -D, fp32 [B,H,T]
+// each, every array starting on a 256-byte boundary.
 size_t bwd_array_bytes(int B, int H, int T) { return round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256); }
 size_t bwd_workspace(int B, int H, int T, int /*d*/, aah_dtype /*dt*/) { return 2 * bwd_array_bytes(B, H, T); }
-const float* ws_lse2(const void* ws) { return static_cast<const float*>(ws); }
-const float* ws_sd(const void* ws, int B, int H, int T) {
+const float* ws_nls(const void* ws) { return static_cast<const float*>(ws); }
+const float* ws_nd(const void* ws, int B, int H, int T) {
   return reinterpret_cast<const float*>(static_cast<const char*>(ws) + bwd_array_bytes(B, H, T));
 }
 
@@ -251,7 +251,7 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
@@ -278,11 +278,11 @@ aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float*
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(dout, "dout", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
-  const hipError_t e = aah::launch_bwd_preprocess(o, dout, lse, dt == AAH_BF16, const_cast<float*>(ws_lse2(workspace)),
-                                                  const_cast<float*>(ws_sd(workspace, B, H, T)), s,
+  const hipError_t e = aah::launch_bwd_preprocess(o, dout, lse, dt == AAH_BF16, const_cast<float*>(ws_nls(workspace)),
+                                                  const_cast<float*>(ws_nd(workspace, B, H, T)), s,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
   return AAH_OK;
@@ -299,22 +299,22 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   AAH_TRY(check_tensor(dout, "dout", 16));
   AAH_TRY(check_tensor(dk, "dk", 16));
   AAH_TRY(check_tensor(dv, "dv", 16));
-  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* lse2 = ws_lse2(workspace);
-  const float* sd = ws_sd(workspace, B, H, T);
+  const float* nls = ws_nls(workspace);
+  const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
   DevicePlan plan;
   AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, lse2, sd, dk, dv, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nls, nd, dk, dv, plan.items, plan.n_items, plan.win, s, st);
   else
     e = aah::launch_bwd_dkdv_simple(static_cast<const float*>(q), static_cast<const float*>(k),
-                                    static_cast<const float*>(v), static_cast<const float*>(dout), lse2, sd,
+                                    static_cast<const float*>(v), static_cast<const float*>(dout), nls, nd,
                                     static_cast<float*>(dk), static_cast<float*>(dv), plan.items, plan.n_items,
                                     plan.win, s, st);
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
@@ -331,22 +331,22 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(dout, "dout", 16));
   AAH_TRY(check_tensor(dq, "dq", 16));
-  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* lse2 = ws_lse2(workspace);
-  const float* sd = ws_sd(workspace, B, H, T);
+  const float* nls = ws_nls(workspace);
+  const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
   DevicePlan plan;
   AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_bwd_dq_bf16(q, k, v, dout, lse2, sd, dq, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dq_bf16(q, k, v, dout, nls, nd, dq, plan.items, plan.n_items, plan.win, s, st);
   else
     e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
-                                  static_cast<const float*>(v), static_cast<const float*>(dout), lse2, sd,
+                                  static_cast<const float*>(v), static_cast<const float*>(dout), nls, nd,
                                   static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
   if (e != hipSuccess) return hip_fail(e, "dQ launch");
   return AAH_OK;
@@ -368,7 +368,7 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dq, "dq", 16));
   AAH_TRY(check_tensor(dk, "dk", 16));
   AAH_TRY(check_tensor(dv, "dv", 16));
-  if (!std::isfinite(scale)) return fail(AAH_ERR_INVALID_ARG, "scale is not finite");
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   AAH_TRY(aah_attn_bwd_preprocess(o, dout, lse, B, H, T, d, dt, scale, workspace, workspace_bytes, stream));
   AAH_TRY(aah_attn_bwd_dkdv(q, k, v, dout, windows, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,

@@ -5,16 +5,19 @@
 // i - W < j <= i), given the forward's per-row log-sum-exp:
 //   P = exp(scale Q K^T - lse),  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
-// The preprocess step leaves lse2 = lse * log2(e) and sD = scale * D per row in
-// the workspace, so a weight is exp2(fma(s, scale log2 e, -lse2)) and the
-// scaled dS is p * fma(dp, scale, -sD).
+// The preprocess step leaves nls = -lse / scale and nD = -D per row in the
+// workspace.  In the key-stationary kernel the S and dP MFMA chains start from
+// those rows instead of zero, so s - lse / scale and dP - D come straight out of
+// the matrix cores: a weight is exp2(scale log2(e) * acc) and dS = p * (dP - D)
+// is one multiply.  The softmax scale of dK and dQ is applied once, when they
+// are stored.
 //
 // Two kernels, no atomics, every output written exactly once:
 //
 // bwd_dkdv_kernel -- one item = 128 keys of one head (4 waves x 32 keys) and
 //   the 64-query steps that can see them.  K and V rows stay in registers, dK
 //   and dV accumulate in registers.  Per step the Q and dO tiles and the
-//   step's lse2 / sD rows are copied HBM -> LDS (three-stage ring).  For each
+//   step's nls / nD rows are copied HBM -> LDS (three-stage ring).  For each
 //   32-query block S = Q K^T and dP = dO V^T with M = queries, so P and dS come
 //   out with one key per lane and are directly the B operand of
 //   dV^T += dO^T P and dK^T += Q^T dS (M = d, N = keys, K = queries); the A
@@ -70,57 +73,67 @@ __device__ constexpr int reg_row(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // Lane-constant LDS offsets shared by both kernels, for a row-major swizzled tile:
 //   rd[st]: MFMA A operand read with ds_read_b128 -- row ln, logical chunk 2 st + hl;
-//   tr[b]:  ds_read_b64_tr_b16 of row 4 hl + s16 / 4 (+ 16 step, + 8 for the second
-//           read), columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3;
-//   dma[j]: source offset of this lane's chunk in the wave's j-th 1 KiB copy.
+//   tr[half][b]: ds_read_b64_tr_b16 of row 4 hl + s16 / 4 + 8 half (+ 16 step),
+//           columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3 (the swizzle depends on
+//           the row modulo 16, so each half has its own offset);
+// (The copy offsets, dma_off below, are recomputed per copy: cheap, and they
+// would otherwise hold registers through the whole loop.)
 template <int D>
 struct Offsets {
   uint32_t rd[Cfg<D>::kSteps];
-  uint32_t tr[Cfg<D>::kBlocks];
-  uint32_t dma[Cfg<D>::kDmaPerWave];
-  __device__ Offsets(int wave, int lane) {
+  uint32_t tr[2][Cfg<D>::kBlocks];
+  __device__ Offsets(int /*wave*/, int lane) {
     using C = Cfg<D>;
     constexpr int NC = C::kNC;
     const int hl = lane >> 5, ln = lane & 31, g = lane >> 4, s16 = lane & 15;
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st)
       rd[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
-    const int trow = 4 * hl + (s16 >> 2);
 #pragma unroll
-    for (int b = 0; b < C::kBlocks; ++b) {
-      const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
-      tr[b] = static_cast<uint32_t>(trow * C::kRowBytes + (((col >> 3) ^ swz<NC>(trow)) * 16) + (col & 7) * 2);
-    }
+    for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int j = 0; j < C::kDmaPerWave; ++j) {
-      const int P = (wave * C::kDmaPerWave + j) * 64 + lane;
-      const int row = P / NC;
-      dma[j] = static_cast<uint32_t>(row * C::kRowBytes + (((P % NC) ^ swz<NC>(row)) * 16));
-    }
+      for (int b = 0; b < C::kBlocks; ++b) {
+        const int trow = 4 * hl + (s16 >> 2) + 8 * half;
+        const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
+        tr[half][b] =
+            static_cast<uint32_t>(trow * C::kRowBytes + (((col >> 3) ^ swz<NC>(trow)) * 16) + (col & 7) * 2);
+      }
   }
 };
+
+// Source offset of this lane's chunk in the wave's j-th 1 KiB copy of a tile:
+// tile chunk P = (wave * kDmaPerWave + j) * 64 + lane is row P / NC at stored
+// chunk P % NC, which holds logical chunk (P % NC) ^ swz(row).
+template <int D>
+__device__ __forceinline__ uint32_t dma_off(int wave, int lane, int j) {
+  using C = Cfg<D>;
+  constexpr int NC = C::kNC;
+  const int P = (wave * C::kDmaPerWave + j) * 64 + lane;
+  const int row = P / NC;
+  return static_cast<uint32_t>(row * C::kRowBytes + (((P % NC) ^ swz<NC>(row)) * 16));
+}
 
 // Copy rows [r0, r0 + 64) of one head's [T, D] tensor into a swizzled LDS tile
 // (this wave's share); rows past T arrive as zeros.
 template <int D>
-__device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char* dst, int wave,
-                                          const Offsets<D>& o) {
+__device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char* dst, int wave, int lane) {
   using C = Cfg<D>;
   const i32x4 r = rsrc_words(head + static_cast<size_t>(r0) * D, static_cast<uint32_t>(T - r0) * C::kRowBytes);
 #pragma unroll
-  for (int j = 0; j < C::kDmaPerWave; ++j) dma16(r, dst + (wave * C::kDmaPerWave + j) * 1024, o.dma[j]);
+  for (int j = 0; j < C::kDmaPerWave; ++j)
+    dma16(r, dst + (wave * C::kDmaPerWave + j) * 1024, dma_off<D>(wave, lane, j));
 }
 
 // ---------------------------------------------------------------- dK, dV
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                     const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ SD,
+                     const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, int H, int T, float scale) {
   using C = Cfg<D>;
-  // Three-stage ring; stage = {Q tile, dO tile, lse2 row, sD row}.
+  // Three-stage ring; stage = {Q tile, dO tile, nls row, nD row}.
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
   __shared__ __attribute__((aligned(1024))) char ring0[kStage];
   __shared__ __attribute__((aligned(1024))) char ring1[kStage];
@@ -160,13 +173,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
   }
 
-  // Stage fill: Q and dO tiles (every wave its share), lse2 row (wave 0), sD row (wave 1).
+  // Stage fill: Q and dO tiles (every wave its share), nls row (wave 0), nD row (wave 1).
   auto fill = [&](int qt, char* st) __attribute__((always_inline)) {
     const int q0 = qt * kStep;
-    copy_tile<D>(Q + base, q0, T, st, wave, off);
-    copy_tile<D>(dO + base, q0, T, st + kG, wave, off);
+    copy_tile<D>(Q + base, q0, T, st, wave, lane);
+    copy_tile<D>(dO + base, q0, T, st + kG, wave, lane);
     if (wave < 2) {
-      const float* src = (wave == 0 ? LSE2 : SD) + rbase + q0;
+      const float* src = (wave == 0 ? NLS : ND) + rbase + q0;
       dma4(rsrc_words(src, static_cast<uint32_t>(T - q0) * 4), st + (wave == 0 ? kL : kDd),
            static_cast<uint32_t>(lane) * 4);
     }
@@ -190,55 +203,78 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     dv[b] = f32x16{};
   }
 
-  // One 32-query block [qb, qb + 32) of the stage in st (mb = block within the step).
-  auto do_block = [&](const char* st, int qb, int mb) __attribute__((always_inline)) {
-    // Query i sees key j iff 0 <= i - j < W; the wave's keys are [k0w, k0w + 32).
-    if (!(wave_active && qb < T && qb + 31 >= k0w && qb <= k0w + 30 + W)) return;
+  // s - lse / scale and dP - D of 32-query block mb of the stage in st: the chains
+  // start from the step's nls and nD rows.
+  auto scores = [&](const char* st, int mb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const char* qs = st;
     const char* gs = st + kG;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // Registers 4 i .. 4 i + 3 hold queries 32 mb + 8 i + 4 hl + 0..3 of the step.
+    const float* nl = reinterpret_cast<const float*>(st + kL) + 32 * mb + 4 * hl;
+    const float* nd = reinterpret_cast<const float*>(st + kDd) + 32 * mb + 4 * hl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(nl + 8 * i);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(nd + 8 * i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[4 * i + j] = l4[j];
+        dp[4 * i + j] = d4[j];
+      }
+    }
 #pragma unroll
     for (int k = 0; k < C::kSteps; ++k) {
       s = mfma(*reinterpret_cast<const bf16x8*>(qs + 32 * mb * C::kRowBytes + off.rd[k]), kf[k], s);
       dp = mfma(*reinterpret_cast<const bf16x8*>(gs + 32 * mb * C::kRowBytes + off.rd[k]), vf[k], dp);
     }
-    // Register r holds query qb + 4 hl + reg_row(r); i - j = reg_row(r) - lim.
-    const int lim = key - qb - 4 * hl;
-    if (qb < k0w + 31) {  // some query precedes some key
+  };
+  // P and dS (bf16 B operands; step h takes registers 8 h .. 8 h + 7).
+  auto weights = [&](const f32x16& s, const f32x16& dp, bf16x8* pf, bf16x8* df) __attribute__((always_inline)) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) < lim ? -INFINITY : s[r];
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(s[r] * c);
+      pf[r >> 3][r & 7] = static_cast<bf16>(p);
+      df[r >> 3][r & 7] = static_cast<bf16>(p * dp[r]);
     }
-    if (qb + 31 >= k0w + W) {  // some query is W or more past some key
-      const int hi = lim + W;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) >= hi ? -INFINITY : s[r];
-    }
-    // Registers 4 i .. 4 i + 3 hold queries qb + 8 i + 4 hl + 0..3: one 16-byte read each of lse2 and sD.
-    const float* l2 = reinterpret_cast<const float*>(st + kL) + 32 * mb + 4 * hl;
-    const float* sd = reinterpret_cast<const float*>(st + kDd) + 32 * mb + 4 * hl;
-    bf16x8 pf[2], df[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(l2 + 8 * i);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(sd + 8 * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * i + j;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -l4[j]));
-        const float ds = p * fmaf(dp[r], scale, -d4[j]);
-        pf[r >> 3][r & 7] = static_cast<bf16>(p);
-        df[r >> 3][r & 7] = static_cast<bf16>(ds);
-      }
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS over the block's two 16-query steps.
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dS over block mb's two 16-query steps.
+  auto accumulate = [&](const char* st, int mb, const bf16x8* pf, const bf16x8* df) __attribute__((always_inline)) {
+    const char* qs = st;
+    const char* gs = st + kG;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
 #pragma unroll
       for (int b = 0; b < C::kBlocks; ++b) {
-        dv[b] = mfma(read_tr(reinterpret_cast<const bf16*>(gs + row0 + off.tr[b]), 8 * D), pf[h], dv[b]);
-        dk[b] = mfma(read_tr(reinterpret_cast<const bf16*>(qs + row0 + off.tr[b]), 8 * D), df[h], dk[b]);
+        dv[b] = mfma(read_tr(gs + row0 + off.tr[0][b], gs + row0 + off.tr[1][b]), pf[h], dv[b]);
+        dk[b] = mfma(read_tr(qs + row0 + off.tr[0][b], qs + row0 + off.tr[1][b]), df[h], dk[b]);
       }
+    }
+  };
+
+  // One 64-query step, block by block.  Query i sees key j iff 0 <= i - j < W;
+  // the wave's keys are [k0w, k0w + 32).  Blocks no key sees are skipped; only
+  // blocks crossing the diagonal or the window's trailing edge are masked.
+  auto do_step = [&](const char* st, int q0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int qb = q0 + 32 * mb;
+      if (!(wave_active && qb < T && qb + 31 >= k0w && qb <= k0w + 30 + W)) continue;
+      f32x16 s, dp;
+      scores(st, mb, s, dp);
+      // Register r holds query qb + 4 hl + reg_row(r); i - j = reg_row(r) - lim.
+      const int lim = key - qb - 4 * hl;
+      if (qb < k0w + 31) {  // some query precedes some key
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = reg_row(r) < lim ? -INFINITY : s[r];
+      }
+      if (qb + 31 >= k0w + W) {  // some query is W or more past some key
+        const int hi = lim + W;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = reg_row(r) >= hi ? -INFINITY : s[r];
+      }
+      bf16x8 pf[2], df[2];
+      weights(s, dp, pf, df);
+      accumulate(st, mb, pf, df);
     }
   };
 
@@ -246,9 +282,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   auto step = [&](int qt, const char* cur, char* nxt2) __attribute__((always_inline)) {
     const bool more = qt + 2 < it.hi;
     if (more) fill(qt + 2, nxt2);
-    const int q0 = qt * kStep;
-    do_block(cur, q0, 0);
-    do_block(cur, q0 + 32, 1);
+    do_step(cur, qt * kStep);
     if (qt + 1 >= it.hi) return true;
     wait_barrier(more);
     return false;
@@ -271,7 +305,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int col = 32 * b + 8 * i + 4 * hl;
-      store_bf16x4(dkrow + col, dk[b][4 * i], dk[b][4 * i + 1], dk[b][4 * i + 2], dk[b][4 * i + 3]);
+      store_bf16x4(dkrow + col, dk[b][4 * i] * scale, dk[b][4 * i + 1] * scale, dk[b][4 * i + 2] * scale,
+                   dk[b][4 * i + 3] * scale);
       store_bf16x4(dvrow + col, dv[b][4 * i], dv[b][4 * i + 1], dv[b][4 * i + 2], dv[b][4 * i + 3]);
     }
 }
@@ -279,9 +314,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 // ---------------------------------------------------------------- dQ
 
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                   const bf16* __restrict__ dO, const float* __restrict__ LSE2, const float* __restrict__ SD,
+                   const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
                    bf16* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
                    int H, int T, float scale) {
   using C = Cfg<D>;
@@ -309,7 +344,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
   // Q and dO rows of this lane's query (B operands of S^T = K Q^T and dP^T = V dO^T).
   bf16x8 qf[C::kSteps], gf[C::kSteps];
-  float lse2 = 0.f, sD = 0.f;
+  float cl = 0.f, nD = 0.f;  // -lse * log2(e) and -D of this lane's query
   {
     const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, slice);
@@ -321,17 +356,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       gf[st] = __builtin_bit_cast(bf16x8, load16(rg, o));
     }
     const uint32_t rows = static_cast<uint32_t>(T) * 4;
-    lse2 = load_f32(make_rsrc(LSE2 + rbase, rows), static_cast<uint32_t>(qi) * 4);
-    sD = load_f32(make_rsrc(SD + rbase, rows), static_cast<uint32_t>(qi) * 4);
+    cl = load_f32(make_rsrc(NLS + rbase, rows), static_cast<uint32_t>(qi) * 4);
+    nD = load_f32(make_rsrc(ND + rbase, rows), static_cast<uint32_t>(qi) * 4);
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(qf[st]), "v"(gf[st]));
-    __asm__ volatile("" ::"v"(lse2), "v"(sD));
+    __asm__ volatile("" ::"v"(cl), "v"(nD));
+    cl *= c;
   }
+  // -D of this lane's query in every register: the start value of each dP^T chain.
+  f32x16 nd16;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd16[r] = nD;
 
   auto fill = [&](int kt, char* st) __attribute__((always_inline)) {
     const int k0 = kt * kStep;
-    copy_tile<D>(K + base, k0, T, st, wave, off);
-    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, off);
+    copy_tile<D>(K + base, k0, T, st, wave, lane);
+    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, lane);
   };
   constexpr int kFill = 2 * C::kDmaPerWave;
 
@@ -344,7 +384,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;
     const char* ks = st;
     const char* vs = st + C::kTileBytes;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    f32x16 s = f32x16{}, dp = nd16;
 #pragma unroll
     for (int k = 0; k < C::kSteps; ++k) {
       s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd[k]), qf[k], s);
@@ -364,8 +404,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     bf16x8 df[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, -lse2));
-      df[r >> 3][r & 7] = static_cast<bf16>(p * fmaf(dp[r], scale, -sD));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, cl));
+      df[r >> 3][r & 7] = static_cast<bf16>(p * dp[r]);
     }
     // dQ^T += K^T dS^T over the block's two 16-key steps (slot order of the dS registers).
 #pragma unroll
@@ -373,7 +413,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
 #pragma unroll
       for (int b = 0; b < C::kBlocks; ++b)
-        acc[b] = mfma(read_tr(reinterpret_cast<const bf16*>(ks + row0 + off.tr[b]), 8 * D), df[h], acc[b]);
+        acc[b] = mfma(read_tr(ks + row0 + off.tr[0][b], ks + row0 + off.tr[1][b]), df[h], acc[b]);
     }
   };
 
@@ -410,50 +450,50 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   for (int b = 0; b < C::kBlocks; ++b)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      store_bf16x4(dqrow + 32 * b + 8 * i + 4 * hl, acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2],
-                   acc[b][4 * i + 3]);
+      store_bf16x4(dqrow + 32 * b + 8 * i + 4 * hl, acc[b][4 * i] * scale, acc[b][4 * i + 1] * scale,
+                   acc[b][4 * i + 2] * scale, acc[b][4 * i + 3] * scale);
 }
 
 template <int D>
-hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* sd,
+hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nls, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
                   const AttnShape& s, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse2,
-                     sd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nls,
+                     nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* lse2, const float* sd,
+hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* nls, const float* nd,
                 void* dq, const WorkItem* items, int n_items, const int32_t* win_eff, const AttnShape& s,
                 hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse2,
-                     sd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nls,
+                     nd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
-                                const float* sd, void* dk, void* dv, const WorkItem* items, int n_items,
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+                                const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
                                 const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dkdv_d<32>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
-    case 64: return dkdv_d<64>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
-    case 128: return dkdv_d<128>(q, k, v, dout, lse2, sd, dk, dv, items, n_items, win_eff, s, stream);
+    case 32: return dkdv_d<32>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 64: return dkdv_d<64>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 128: return dkdv_d<128>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse2,
-                              const float* sd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+                              const float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
                               const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_d<32>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
-    case 64: return dq_d<64>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
-    case 128: return dq_d<128>(q, k, v, dout, lse2, sd, dq, items, n_items, win_eff, s, stream);
+    case 32: return dq_d<32>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
+    case 64: return dq_d<64>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
+    case 128: return dq_d<128>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

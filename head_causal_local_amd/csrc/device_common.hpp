@@ -100,13 +100,20 @@ __device__ inline void dma4(const i32x4& rsrc, const void* lds_base, uint32_t by
 
 // XOR swizzle of the 16-byte chunks of a row-major bf16 tile whose rows hold
 // NC chunks (NC = d / 8): logical chunk c of row r is stored at chunk
-// c ^ swz<NC>(r).  Chosen so that (a) eight consecutive rows read at one
-// logical chunk (an MFMA operand read with ds_read_b128) and (b) four
-// consecutive rows read at two adjacent chunks 2j, 2j + 1 (one 16-lane group of
-// ds_read_b64_tr_b16) each touch all 32 four-byte banks once.
+// c ^ swz<NC>(r).  gfx950's LDS serves 256 bytes per cycle from 64 four-byte
+// banks, i.e. sixteen 16-byte bank groups.  The swizzle makes both read
+// patterns of the kernels touch every bank group once per cycle:
+//   * ds_read_b128 of one logical chunk by 16 consecutive rows (one MFMA
+//     operand; 16 lanes per cycle), and
+//   * ds_read_b64_tr_b16 of four consecutive rows 4k .. 4k + 3 at four chunks
+//     (32 lanes per cycle).
+// (A tile probe measured 3.8 conflict cycles per ds_read_b128 without a
+// swizzle adapted to 64 banks and none with this one.)
 template <int NC>
 __device__ constexpr int swz(int r) {
-  return NC >= 8 ? (((2 * r) & 6) | ((r >> 2) & 1)) : ((((r >> 1) & 1) << 1) | ((r >> 2) & 1));
+  return NC >= 16 ? (((r & 3) << 2) | ((r >> 2) & 3))
+       : NC == 8  ? ((((r >> 1) & 1) << 2) | ((r >> 2) & 3))
+                  : ((r >> 2) & 3);
 }
 
 __device__ inline float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
@@ -116,12 +123,13 @@ __device__ inline float load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
 // ds_read_b64_tr_b16 works on 16-lane groups: if source lane s of a group
 // addresses row R0 + s / 4, columns C0 + 4 (s % 4) .. + 3 of a row-major bf16
 // tile, destination lane i of the group receives column C0 + i, rows R0 .. R0 + 3.
-// Two reads, the second `gap` elements further, give eight rows of one column:
-// an MFMA A or B operand whose k index runs down the tile.
-__device__ inline bf16x8 read_tr(const bf16* p, int gap) {
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(p + gap));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+// Two reads, the second of rows R0 + 8 .. R0 + 11 (at its own, swizzled,
+// address), give eight rows of one column: an MFMA A or B operand whose k index
+// runs down the tile.
+__device__ inline bf16x8 read_tr(const void* lo, const void* hi) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(lo));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((AAH_LDS s16x4*)(hi));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Store 4 consecutive fp32 values as bf16 (round to nearest even) with one 8-byte store.

@@ -163,15 +163,19 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   for (int st = 0; st < C::kSteps; ++st)
     k_off[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
   // V^T (A operand of O^T += V^T P^T) by ds_read_b64_tr_b16: lane (g, s16) addresses
-  // row 16 st + 4 hl + s16 / 4 (+ 8 for the second read), columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3.
+  // row 16 st + 4 hl + s16 / 4 and that row + 8, columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3.
+  // The swizzle depends on the row modulo 16, so the +16 st offset is common to both reads.
   const int g = lane >> 4, s16 = lane & 15;
-  const int vrow = 4 * hl + (s16 >> 2);  // row mod 16; its swizzle does not depend on st or the +8
-  uint32_t v_off[C::kBlocks];
+  uint32_t v_off[2][C::kBlocks];
 #pragma unroll
-  for (int b = 0; b < C::kBlocks; ++b) {
-    const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
-    v_off[b] = static_cast<uint32_t>(vrow * C::kRowBytes + (((col >> 3) ^ swz<NC>(vrow)) * 16) + (col & 7) * 2);
-  }
+  for (int half = 0; half < 2; ++half)
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b) {
+      const int vrow = 4 * hl + (s16 >> 2) + 8 * half;
+      const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
+      v_off[half][b] =
+          static_cast<uint32_t>(vrow * C::kRowBytes + (((col >> 3) ^ swz<NC>(vrow)) * 16) + (col & 7) * 2);
+    }
   const bf16x2 ones = {static_cast<bf16>(1.f), static_cast<bf16>(1.f)};
 
   // One 32-key block [kb, kb + 32) of the tile held in (kt_lds, vt_lds), for this wave.
@@ -261,8 +265,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       const int row0 = 32 * mb + 16 * h;
 #pragma unroll
       for (int b = 0; b < C::kBlocks; ++b) {
-        const char* p = vt_lds + row0 * C::kRowBytes + v_off[b];
-        acc[b] = mfma(read_tr(reinterpret_cast<const bf16*>(p), 8 * D), pf[h], acc[b]);  // second read 8 rows down
+        const char* p = vt_lds + row0 * C::kRowBytes;
+        acc[b] = mfma(read_tr(p + v_off[0][b], p + v_off[1][b]), pf[h], acc[b]);
       }
     }
   };

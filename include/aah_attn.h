@@ -120,15 +120,15 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
  * The backward's steps as separate calls, for callers that schedule or time
  * them.  Arguments mean what they mean for aah_attn_bwd and the same checks
  * apply; the workspace carries two fp32 [B,H,T] arrays from the first step to
- * the other two (lse2 = lse * log2(e) at byte 0, then sD = scale * D at the
- * next 256-byte boundary after B*H*T floats).
- *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes lse2 and sD into the
- *     workspace.  Must complete before either of the others starts.
+ * the other two (nls = -lse / scale at byte 0, then nD = -D at the next
+ * 256-byte boundary after B*H*T floats).
+ *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes nls and nD into the
+ *     workspace.  Must complete before either of the others starts, and the
+ *     other two must be given the same scale.
  *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel).
  *   aah_attn_bwd_dq:   writes dq (query-stationary kernel).
  * dkdv and dq only read the workspace and may run in either order or
- * concurrently on different streams once the preprocess has completed; they
- * must use the scale the preprocess was given.
+ * concurrently on different streams once the preprocess has completed.
  */
 aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int T, int d,
                                    aah_dtype dt, float scale, void* workspace, size_t workspace_bytes,

@@ -98,7 +98,7 @@ def test_workspace_sizes():
     B, H, T, d = 4, 32, 4096, 64
     rows = B * H * T
     assert aah.workspace_size(B, H, T, d, "bf16", is_bwd=False) == 0
-    assert aah.workspace_size(B, H, T, d, "bf16") == 2 * rows * 4     # lse2 and sD
+    assert aah.workspace_size(B, H, T, d, "bf16") == 2 * rows * 4     # lse2 and nD
     assert aah.workspace_size(B, H, T, d, "f32") == 2 * rows * 4
     assert aah.workspace_size(1, 1, 3, 32, "f32") == 512           # each array rounded to 256 bytes
     assert _lib.lib().aah_attn_workspace_size(0, 1, 1, 64, 0, 1) == 0
@@ -117,7 +117,9 @@ def test_bwd_step_validation():
     assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8, None) == 3
     assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 48, 0, 0.1, FAKE, need, None) == 2
     assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, 0, 1, 2, 64, 64, 0, 0.1, FAKE, need, None) == 1   # NULL lse
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, float("nan"), FAKE, need, None) == 1
+    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, 0.1, FAKE, 8, None) == 3   # small ws
+    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, 0.0, FAKE, need, None) == 1  # scale 0
+    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, float("inf"), FAKE, need, None) == 1
 
 
 def test_slice_limit():
