@@ -68,7 +68,8 @@ struct Cfg {
   static constexpr int kSteps = D / 16;             // MFMA k-steps over d for S^T
   static constexpr int kBlocks = D / 32;            // 32-row blocks of O^T
   // Resident waves per SIMD the register allocation is sized for.
-  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 3 : 1;
+  // (d = 64: 94 registers and 32 KiB of LDS per workgroup allow five.)
+  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 5 : 1;
   static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
 };
 
@@ -86,9 +87,6 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   __shared__ __attribute__((aligned(1024))) char k_lds1[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes];
   __shared__ __attribute__((aligned(1024))) char v_lds1[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds2[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds2[C::kTileBytes];
-  constexpr int kDmaInstr = 2 * C::kDmaPerWave;  // copies one wave issues per tile
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
@@ -277,35 +275,27 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     do_block(kt_lds, vt_lds, k0 + 32, 1);
   };
 
-  // One step of the ring: compute tile kt from (kc, vc), fill (kn, vn) with
-  // tile kt + 2, then wait for tile kt + 1 and barrier.  Returns true after the
-  // last tile.
+  // Two-stage ring: tile kt lives in stage (kt - lo) % 2.  A step issues the
+  // copies of the next tile into the other stage (which every wave finished
+  // reading before the barrier that ended the previous step), computes the
+  // current tile, then waits for its own copies and meets the other waves at
+  // the barrier.  Returns true after the last tile.  Two stages instead of
+  // three leave room for five workgroups per CU at d = 64; the copies still
+  // have a whole step to land.
   auto step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
-    const bool fill = kt + 2 < it.hi;
-    if (fill) issue_tile(kt + 2, kn, vn);
+    const bool fill = kt + 1 < it.hi;
+    if (fill) issue_tile(kt + 1, kn, vn);
     do_tile(kc, vc, kt);
-    if (kt + 1 >= it.hi) return true;  // nothing left to wait for; the workgroup is done with LDS
-    if (fill)
-      wait_vm_barrier(kDmaInstr);
-    else
-      wait_vm_barrier(0);
+    if (!fill) return true;  // nothing left to wait for; the workgroup is done with LDS
+    wait_vm_barrier(0);
     return false;
   };
 
-  // Three-stage ring: tile kt lives in stage kt % 3 and its copy is issued two
-  // steps ahead.  Before the barrier that ends a step, each wave waits only for
-  // its copies of the next tile (the ones issued a step earlier); the copies
-  // issued in this step stay in flight.
   issue_tile(it.lo, k_lds0, v_lds0);
-  if (it.lo + 1 < it.hi) issue_tile(it.lo + 1, k_lds1, v_lds1);
-  if (it.lo + 1 < it.hi)
-    wait_vm_barrier(kDmaInstr);
-  else
-    wait_vm_barrier(0);
-  for (int kt = it.lo;; kt += 3) {
-    if (step(kt, k_lds0, v_lds0, k_lds2, v_lds2)) break;
+  wait_vm_barrier(0);
+  for (int kt = it.lo;; kt += 2) {
+    if (step(kt, k_lds0, v_lds0, k_lds1, v_lds1)) break;
     if (step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
-    if (step(kt + 2, k_lds2, v_lds2, k_lds1, v_lds1)) break;
   }
 
   if (!wave_active) return;
