@@ -128,7 +128,7 @@ def _ws(workspace):
 
 
 def attn_bwd_preprocess(o, do, lse, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 1: -lse / scale and -rowsum(do * o) into the workspace."""
+    """Backward step 1: -lse * log2(e) and -rowsum(do * o) into the workspace."""
     _check_operand("do", do, o)
     B, H, T, d = o.shape
     if lse.shape != (B, H, T) or not lse.is_contiguous():

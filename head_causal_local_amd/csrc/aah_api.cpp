@@ -166,11 +166,11 @@ void bwd_tiles(aah_dtype dt, int* row, int* col) {
   }
 }
 
-// Workspace of the backward: nls = -lse / scale and nD = -D, fp32 [B,H,T]
+// Workspace of the backward: nl2 = -lse log2(e) and nD = -D, fp32 [B,H,T]
 // each, every array starting on a 256-byte boundary.
 size_t bwd_array_bytes(int B, int H, int T) { return round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256); }
 size_t bwd_workspace(int B, int H, int T, int /*d*/, aah_dtype /*dt*/) { return 2 * bwd_array_bytes(B, H, T); }
-const float* ws_nls(const void* ws) { return static_cast<const float*>(ws); }
+const float* ws_nl2(const void* ws) { return static_cast<const float*>(ws); }
 const float* ws_nd(const void* ws, int B, int H, int T) {
   return reinterpret_cast<const float*>(static_cast<const char*>(ws) + bwd_array_bytes(B, H, T));
 }
@@ -281,7 +281,7 @@ aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float*
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
-  const hipError_t e = aah::launch_bwd_preprocess(o, dout, lse, dt == AAH_BF16, const_cast<float*>(ws_nls(workspace)),
+  const hipError_t e = aah::launch_bwd_preprocess(o, dout, lse, dt == AAH_BF16, const_cast<float*>(ws_nl2(workspace)),
                                                   const_cast<float*>(ws_nd(workspace, B, H, T)), s,
                                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
@@ -303,7 +303,7 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* nls = ws_nls(workspace);
+  const float* nl2 = ws_nl2(workspace);
   const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
@@ -311,10 +311,10 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nls, nd, dk, dv, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nl2, nd, dk, dv, plan.items, plan.n_items, plan.win, s, st);
   else
     e = aah::launch_bwd_dkdv_simple(static_cast<const float*>(q), static_cast<const float*>(k),
-                                    static_cast<const float*>(v), static_cast<const float*>(dout), nls, nd,
+                                    static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
                                     static_cast<float*>(dk), static_cast<float*>(dv), plan.items, plan.n_items,
                                     plan.win, s, st);
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
@@ -335,7 +335,7 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* nls = ws_nls(workspace);
+  const float* nl2 = ws_nl2(workspace);
   const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
@@ -343,10 +343,10 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_bwd_dq_bf16(q, k, v, dout, nls, nd, dq, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dq_bf16(q, k, v, dout, nl2, nd, dq, plan.items, plan.n_items, plan.win, s, st);
   else
     e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
-                                  static_cast<const float*>(v), static_cast<const float*>(dout), nls, nd,
+                                  static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
                                   static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
   if (e != hipSuccess) return hip_fail(e, "dQ launch");
   return AAH_OK;

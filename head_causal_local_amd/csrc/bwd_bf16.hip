@@ -5,19 +5,24 @@
 // i - W < j <= i), given the forward's per-row log-sum-exp:
 //   P = exp(scale Q K^T - lse),  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
-// The preprocess step leaves nls = -lse / scale and nD = -D per row in the
-// workspace.  In the key-stationary kernel the S and dP MFMA chains start from
-// those rows instead of zero, so s - lse / scale and dP - D come straight out of
-// the matrix cores: a weight is exp2(scale log2(e) * acc) and dS = p * (dP - D)
-// is one multiply.  The softmax scale of dK and dQ is applied once, when they
-// are stored.
+// The preprocess step leaves nl2 = -lse log2(e) and nD = -D per row in the
+// workspace.  Each kernel keeps its stationary operand of S (K rows in the
+// key-stationary kernel, Q rows in the query-stationary one) in registers
+// premultiplied by c = scale log2(e) and rounded to bf16, and starts the S and
+// dP MFMA chains from nl2 and nD instead of zero.  So c s - lse log2(e) and
+// dP - D come straight out of the matrix cores: a weight is exp2(acc) and
+// dS = p * (dP - D) is one multiply.  The rounding of the premultiplied operand
+// moves each exponent by at most 2^-9 sum_i |c q_i k_i|, a relative change of
+// the weight of the same order as its own rounding to bf16 for the dV / dK /
+// dQ products.  The softmax scale of dK and dQ is applied once, when they are
+// stored.
 //
 // Two kernels, no atomics, every output written exactly once:
 //
 // bwd_dkdv_kernel -- one item = 128 keys of one head (4 waves x 32 keys) and
 //   the 64-query steps that can see them.  K and V rows stay in registers, dK
 //   and dV accumulate in registers.  Per step the Q and dO tiles and the
-//   step's nls / nD rows are copied HBM -> LDS (three-stage ring).  For each
+//   step's nl2 / nD rows are copied HBM -> LDS (three-stage ring).  For each
 //   32-query block S = Q K^T and dP = dO V^T with M = queries, so P and dS come
 //   out with one key per lane and are directly the B operand of
 //   dV^T += dO^T P and dK^T += Q^T dS (M = d, N = keys, K = queries); the A
@@ -129,11 +134,11 @@ __device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char*
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                     const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
+                     const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, int H, int T, float scale) {
   using C = Cfg<D>;
-  // Three-stage ring; stage = {Q tile, dO tile, nls row, nD row}.
+  // Three-stage ring; stage = {Q tile, dO tile, nl2 row, nD row}.
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
   __shared__ __attribute__((aligned(1024))) char ring0[kStage];
   __shared__ __attribute__((aligned(1024))) char ring1[kStage];
@@ -155,31 +160,15 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const bool wave_active = k0w < T;
   const Offsets<D> off(wave, lane);
 
-  // K and V rows (B operands of S = Q K^T and dP = dO V^T): lane holds dims 16 st + 8 hl + 0..7.
   bf16x8 kf[C::kSteps], vf[C::kSteps];
-  {
-    const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slice);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slice);
-#pragma unroll
-    for (int st = 0; st < C::kSteps; ++st) {
-      const uint32_t o = static_cast<uint32_t>(key) * C::kRowBytes + (16 * st + 8 * hl) * 2;
-      kf[st] = __builtin_bit_cast(bf16x8, load16(rk, o));
-      vf[st] = __builtin_bit_cast(bf16x8, load16(rv, o));
-    }
-    // Wait for these loads here rather than inside the loop, where the wait
-    // would also cover LDS copies in flight.
-#pragma unroll
-    for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
-  }
 
-  // Stage fill: Q and dO tiles (every wave its share), nls row (wave 0), nD row (wave 1).
+  // Stage fill: Q and dO tiles (every wave its share), nl2 row (wave 0), nD row (wave 1).
   auto fill = [&](int qt, char* st) __attribute__((always_inline)) {
     const int q0 = qt * kStep;
     copy_tile<D>(Q + base, q0, T, st, wave, lane);
     copy_tile<D>(dO + base, q0, T, st + kG, wave, lane);
     if (wave < 2) {
-      const float* src = (wave == 0 ? NLS : ND) + rbase + q0;
+      const float* src = (wave == 0 ? NL2 : ND) + rbase + q0;
       dma4(rsrc_words(src, static_cast<uint32_t>(T - q0) * 4), st + (wave == 0 ? kL : kDd),
            static_cast<uint32_t>(lane) * 4);
     }
@@ -203,8 +192,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     dv[b] = f32x16{};
   }
 
-  // s - lse / scale and dP - D of 32-query block mb of the stage in st: the chains
-  // start from the step's nls and nD rows.
+  // c s - lse log2(e) and dP - D of 32-query block mb of the stage in st: the
+  // chains start from the step's nl2 and nD rows.
   auto scores = [&](const char* st, int mb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
     const char* qs = st;
     const char* gs = st + kG;
@@ -231,7 +220,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   auto weights = [&](const f32x16& s, const f32x16& dp, bf16x8* pf, bf16x8* df) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(s[r] * c);
+      const float p = __builtin_amdgcn_exp2f(s[r]);
       pf[r >> 3][r & 7] = static_cast<bf16>(p);
       df[r >> 3][r & 7] = static_cast<bf16>(p * dp[r]);
     }
@@ -287,9 +276,30 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     wait_barrier(more);
     return false;
   };
+  // Prologue: the first two stages' copies and the K / V row loads all go out
+  // before the first wait, so their latencies overlap.
   fill(it.lo, ring0);
   if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
-  wait_barrier(it.lo + 1 < it.hi);
+  // K and V rows (B operands of S = Q K^T and dP = dO V^T): lane holds dims
+  // 16 st + 8 hl + 0..7; K premultiplied by c.
+  {
+    const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(K + base, slice);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(V + base, slice);
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) {
+      const uint32_t o = static_cast<uint32_t>(key) * C::kRowBytes + (16 * st + 8 * hl) * 2;
+      kf[st] = __builtin_bit_cast(bf16x8, load16(rk, o));
+      vf[st] = __builtin_bit_cast(bf16x8, load16(rv, o));
+    }
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) kf[st] = scale_bf16x8(kf[st], c);
+    // Consume the rows here: the compiler's wait for them (which also covers
+    // the copies above) then sits before the loop, not inside it.
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
+  }
+  wait_vm_barrier(0);
   for (int qt = it.lo;; qt += 3) {
     if (step(qt, ring0, ring2)) break;
     if (step(qt + 1, ring1, ring0)) break;
@@ -316,7 +326,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                   const bf16* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
+                   const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                    bf16* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
                    int H, int T, float scale) {
   using C = Cfg<D>;
@@ -342,9 +352,22 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const int wave_key_hi = min(q0w + 31, T - 1);
   const Offsets<D> off(wave, lane);
 
-  // Q and dO rows of this lane's query (B operands of S^T = K Q^T and dP^T = V dO^T).
+  auto fill = [&](int kt, char* st) __attribute__((always_inline)) {
+    const int k0 = kt * kStep;
+    copy_tile<D>(K + base, k0, T, st, wave, lane);
+    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, lane);
+  };
+  constexpr int kFill = 2 * C::kDmaPerWave;
+
+  // Prologue: the first two stages' copies go out before the row loads below,
+  // so that their latencies overlap.
+  fill(it.lo, ring0);
+  if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+
+  // Q (premultiplied by c) and dO rows of this lane's query: the B operands of
+  // S^T = K Q^T and dP^T = V dO^T.
   bf16x8 qf[C::kSteps], gf[C::kSteps];
-  float cl = 0.f, nD = 0.f;  // -lse * log2(e) and -D of this lane's query
+  float cl = 0.f, nD = 0.f;  // -lse log2(e) and -D of this lane's query
   {
     const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, slice);
@@ -356,24 +379,24 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       gf[st] = __builtin_bit_cast(bf16x8, load16(rg, o));
     }
     const uint32_t rows = static_cast<uint32_t>(T) * 4;
-    cl = load_f32(make_rsrc(NLS + rbase, rows), static_cast<uint32_t>(qi) * 4);
+    cl = load_f32(make_rsrc(NL2 + rbase, rows), static_cast<uint32_t>(qi) * 4);
     nD = load_f32(make_rsrc(ND + rbase, rows), static_cast<uint32_t>(qi) * 4);
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st) qf[st] = scale_bf16x8(qf[st], c);
+    // Consume the rows here: the compiler's wait for them (which also covers
+    // the copies above) then sits before the loop, not inside it.
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(qf[st]), "v"(gf[st]));
     __asm__ volatile("" ::"v"(cl), "v"(nD));
-    cl *= c;
   }
-  // -D of this lane's query in every register: the start value of each dP^T chain.
-  f32x16 nd16;
+  // The start values of the S^T and dP^T chains: -lse log2(e) and -D of this
+  // lane's query in every register.
+  f32x16 cl16, nd16;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) nd16[r] = nD;
-
-  auto fill = [&](int kt, char* st) __attribute__((always_inline)) {
-    const int k0 = kt * kStep;
-    copy_tile<D>(K + base, k0, T, st, wave, lane);
-    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, lane);
-  };
-  constexpr int kFill = 2 * C::kDmaPerWave;
+  for (int r = 0; r < 16; ++r) {
+    cl16[r] = cl;
+    nd16[r] = nD;
+  }
 
   f32x16 acc[C::kBlocks];
 #pragma unroll
@@ -384,7 +407,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;
     const char* ks = st;
     const char* vs = st + C::kTileBytes;
-    f32x16 s = f32x16{}, dp = nd16;
+    f32x16 s = cl16, dp = nd16;
 #pragma unroll
     for (int k = 0; k < C::kSteps; ++k) {
       s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd[k]), qf[k], s);
@@ -404,7 +427,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     bf16x8 df[2];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[r], c, cl));
+      const float p = __builtin_amdgcn_exp2f(s[r]);
       df[r >> 3][r & 7] = static_cast<bf16>(p * dp[r]);
     }
     // dQ^T += K^T dS^T over the block's two 16-key steps (slot order of the dS registers).
@@ -430,13 +453,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       wait_vm_barrier(0);
     return false;
   };
-  fill(it.lo, ring0);
-  if (it.lo + 1 < it.hi) {
-    fill(it.lo + 1, ring1);
-    wait_vm_barrier(kFill);
-  } else {
-    wait_vm_barrier(0);
-  }
+  wait_vm_barrier(0);
   for (int kt = it.lo;; kt += 3) {
     if (step(kt, ring0, ring2)) break;
     if (step(kt + 1, ring1, ring0)) break;
@@ -455,45 +472,45 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 }
 
 template <int D>
-hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nls, const float* nd,
+hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
                   const AttnShape& s, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nls,
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nl2,
                      nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* nls, const float* nd,
+hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                 void* dq, const WorkItem* items, int n_items, const int32_t* win_eff, const AttnShape& s,
                 hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nls,
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nl2,
                      nd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
                                 const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dkdv_d<32>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
-    case 64: return dkdv_d<64>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
-    case 128: return dkdv_d<128>(q, k, v, dout, nls, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 32: return dkdv_d<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 64: return dkdv_d<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 128: return dkdv_d<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                               const float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
                               const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_d<32>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
-    case 64: return dq_d<64>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
-    case 128: return dq_d<128>(q, k, v, dout, nls, nd, dq, items, n_items, win_eff, s, stream);
+    case 32: return dq_d<32>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 64: return dq_d<64>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 128: return dq_d<128>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

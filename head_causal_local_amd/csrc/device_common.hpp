@@ -142,5 +142,13 @@ __device__ inline void store_bf16x4(bf16* dst, float a, float b, float c, float 
   *reinterpret_cast<u32x2*>(dst) = __builtin_bit_cast(u32x2, v);
 }
 
+// Eight bf16 values times c, each rounded back to bf16 (nearest even).
+__device__ inline bf16x8 scale_bf16x8(const bf16x8& x, float c) {
+  bf16x8 y;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = static_cast<bf16>(static_cast<float>(x[i]) * c);
+  return y;
+}
+
 }  // namespace dev
 }  // namespace aah

@@ -35,29 +35,29 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
                           const WorkItem* items, int n_items, const int32_t* win_eff,
                           const AttnShape& s, hipStream_t stream);
 
-// Per row: nd = -(dO . O) and nls = -lse / scale, in fp32.  is_bf16 selects the
+// Per row: nd = -(dO . O) and nl2 = -lse log2(e), in fp32.  is_bf16 selects the
 // element type of o / dout.
-hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, bool is_bf16, float* nls,
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, bool is_bf16, float* nl2,
                                  float* nd, const AttnShape& s, hipStream_t stream);
 
 // bf16 backward on MFMA, no atomics.  dK, dV: items from the backward
 // planner (kBwdBf16RowTile keys per item, kBwdBf16ColTile queries per step).
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
                                 const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
 
 // dQ: items from the forward planner (kFwdBf16RowTile queries, kFwdBf16ColTile keys per step).
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nls,
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                               const float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
                               const AttnShape& s, hipStream_t stream);
 
 // Scalar backward for fp32: dQ one query row per lane over the forward work
 // list; dK/dV one key row per lane over the backward work list.
 hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout,
-                                const float* nls, const float* nd, float* dq, const WorkItem* items,
+                                const float* nl2, const float* nd, float* dq, const WorkItem* items,
                                 int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
-                                  const float* nls, const float* nd, float* dk, float* dv,
+                                  const float* nl2, const float* nd, float* dk, float* dv,
                                   const WorkItem* items, int n_items, const int32_t* win_eff,
                                   const AttnShape& s, hipStream_t stream);
 

@@ -111,12 +111,12 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
 
 // Each thread reduces one 16-byte chunk of a row; the D/E lanes of a row then
 // combine with xor-shuffles (E = elements per chunk).  Writes, per row,
-// nls = -lse / scale and nD = -(dO . O): a weight is exp2(scale log2(e) (s + nls))
+// nl2 = -lse log2(e) and nD = -(dO . O): a weight is exp2(scale log2(e) s + nl2)
 // and dS = p * (dp + nD), where s = q . k and dp = dO . v are unscaled.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, const E* __restrict__ dO,
-                                                      const float* __restrict__ LSE, float* __restrict__ NLS,
-                                                      float* __restrict__ ND, int64_t rows, float inv_scale) {
+                                                      const float* __restrict__ LSE, float* __restrict__ NL2,
+                                                      float* __restrict__ ND, int64_t rows) {
   constexpr int kPer = 16 / sizeof(E);
   constexpr int kLanesPerRow = D / kPer;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, c
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
   if (row < rows && part == 0) {
     ND[row] = -sum;
-    NLS[row] = -LSE[row] * inv_scale;
+    NL2[row] = -LSE[row] * kLog2e;
   }
 }
 
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const E* __restrict__ O, c
 template <typename E, int D>
 __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
-    const E* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
+    const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
     int H, int T, float scale) {
   __shared__ float ks[kCols * D];
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
     gr[x] = row_ok ? to_f32(dO[base + static_cast<size_t>(qi) * D + x]) : 0.f;
     dq[x] = 0.f;
   }
-  const float cl = row_ok ? NLS[static_cast<size_t>(it.bh) * T + qi] * c : 0.f;  // -lse * log2(e)
+  const float cl = row_ok ? NL2[static_cast<size_t>(it.bh) * T + qi] : 0.f;  // -lse * log2(e)
   const float nD = row_ok ? ND[static_cast<size_t>(it.bh) * T + qi] : 0.f;
 
   for (int kt = it.lo; kt < it.hi; ++kt) {
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
 template <typename E, int D>
 __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
-    const E* __restrict__ dO, const float* __restrict__ NLS, const float* __restrict__ ND,
+    const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dK, E* __restrict__ dV, const WorkItem* __restrict__ items,
     const int32_t* __restrict__ win_eff, int H, int T, float scale) {
   __shared__ float qs[kCols * D];
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     stage_rows<E, D>(gs, dO + base, q0, T);
     for (int e = threadIdx.x; e < kCols; e += blockDim.x) {
       const int row = q0 + e;
-      ls[e] = row < T ? NLS[rbase + row] * c : 0.f;  // -lse * log2(e)
+      ls[e] = row < T ? NL2[rbase + row] : 0.f;  // -lse * log2(e)
       ds_[e] = row < T ? ND[rbase + row] : 0.f;
     }
     __syncthreads();
@@ -269,14 +269,14 @@ hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, f
 }
 
 template <typename E, int D>
-hipError_t pre_d(const void* o, const void* dout, const float* lse, float* nls, float* nd, const AttnShape& s,
+hipError_t pre_d(const void* o, const void* dout, const float* lse, float* nl2, float* nd, const AttnShape& s,
                  hipStream_t stream) {
   constexpr int kLanesPerRow = D / (16 / sizeof(E));
   const int64_t rows = static_cast<int64_t>(s.B) * s.H * s.T;
   const int64_t threads = rows * kLanesPerRow;
   const int64_t blocks = (threads + 255) / 256;
   hipLaunchKernelGGL((bwd_pre_kernel<E, D>), dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream,
-                     static_cast<const E*>(o), static_cast<const E*>(dout), lse, nls, nd, rows, 1.0f / s.scale);
+                     static_cast<const E*>(o), static_cast<const E*>(dout), lse, nl2, nd, rows);
   return hipGetLastError();
 }
 
@@ -293,24 +293,24 @@ hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float*
   }
 }
 
-hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, bool is_bf16, float* nls,
+hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* lse, bool is_bf16, float* nl2,
                                  float* nd, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return is_bf16 ? pre_d<bf16, 32>(o, dout, lse, nls, nd, s, stream)
-                            : pre_d<float, 32>(o, dout, lse, nls, nd, s, stream);
-    case 64: return is_bf16 ? pre_d<bf16, 64>(o, dout, lse, nls, nd, s, stream)
-                            : pre_d<float, 64>(o, dout, lse, nls, nd, s, stream);
-    case 128: return is_bf16 ? pre_d<bf16, 128>(o, dout, lse, nls, nd, s, stream)
-                             : pre_d<float, 128>(o, dout, lse, nls, nd, s, stream);
+    case 32: return is_bf16 ? pre_d<bf16, 32>(o, dout, lse, nl2, nd, s, stream)
+                            : pre_d<float, 32>(o, dout, lse, nl2, nd, s, stream);
+    case 64: return is_bf16 ? pre_d<bf16, 64>(o, dout, lse, nl2, nd, s, stream)
+                            : pre_d<float, 64>(o, dout, lse, nl2, nd, s, stream);
+    case 128: return is_bf16 ? pre_d<bf16, 128>(o, dout, lse, nl2, nd, s, stream)
+                             : pre_d<float, 128>(o, dout, lse, nl2, nd, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout, const float* nls,
+hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout, const float* nl2,
                                 const float* nd, float* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
                                 const AttnShape& s, hipStream_t stream) {
 #define AAH_DQ(DD)                                                                                                \
-  hipLaunchKernelGGL((bwd_dq_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, nls, \
+  hipLaunchKernelGGL((bwd_dq_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, nl2, \
                      nd, dq, items, win_eff, s.H, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DQ(32); break;
@@ -323,11 +323,11 @@ hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, 
 }
 
 hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
-                                  const float* nls, const float* nd, float* dk, float* dv, const WorkItem* items,
+                                  const float* nl2, const float* nd, float* dk, float* dv, const WorkItem* items,
                                   int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
 #define AAH_DKDV(DD)                                                                                            \
   hipLaunchKernelGGL((bwd_dkdv_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, \
-                     nls, nd, dk, dv, items, win_eff, s.H, s.T, s.scale)
+                     nl2, nd, dk, dv, items, win_eff, s.H, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DKDV(32); break;
     case 64: AAH_DKDV(64); break;

@@ -120,11 +120,10 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
  * The backward's steps as separate calls, for callers that schedule or time
  * them.  Arguments mean what they mean for aah_attn_bwd and the same checks
  * apply; the workspace carries two fp32 [B,H,T] arrays from the first step to
- * the other two (nls = -lse / scale at byte 0, then nD = -D at the next
+ * the other two (nl2 = -lse log2(e) at byte 0, then nD = -D at the next
  * 256-byte boundary after B*H*T floats).
- *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes nls and nD into the
- *     workspace.  Must complete before either of the others starts, and the
- *     other two must be given the same scale.
+ *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes nl2 and nD into the
+ *     workspace.  Must complete before either of the others starts.
  *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel).
  *   aah_attn_bwd_dq:   writes dq (query-stationary kernel).
  * dkdv and dq only read the workspace and may run in either order or
