@@ -2,8 +2,9 @@
 """Benchmark of per-head causal local-window attention on one MI355X.
 
 One step = one pass of the whole path over one batch: window intake and work
-lists (cached after the first call), the forward kernel, the backward
-preprocess and the backward kernels, on the 1B-scale layer workload
+lists (cached after the first call), the forward kernel and the two backward
+kernels (dQ, which also forms the per-row D = dO . O, then dK/dV), on the
+1B-scale layer workload
 (B=4, H=32, T=4096, d=64, bf16; 8 groups of 4 heads whose windows are drawn
 from {512, 1024, 2048, 4096} with P = (.5, .25, .125, .125); seed 0).
 
@@ -151,7 +152,7 @@ def main():
         dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
         ws = torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-    n_ev = 5 if with_bwd else 2
+    n_ev = 4 if with_bwd else 2
 
     def step(ev=None):
         def mark(i):
@@ -161,12 +162,10 @@ def main():
         aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream)
         mark(1)
         if with_bwd:
-            aah.attn_bwd_preprocess(o, do, lse, ws, wl.scale, stream=stream)
+            aah.attn_bwd_dq(q, k, v, o, do, lse, wl.windows, dq, ws, wl.scale, stream=stream)
             mark(2)
             aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws, wl.scale, stream=stream)
             mark(3)
-            aah.attn_bwd_dq(q, k, v, do, wl.windows, dq, ws, wl.scale, stream=stream)
-            mark(4)
 
     for _ in range(args.warmup):
         step()
@@ -184,10 +183,9 @@ def main():
         return np.array([e[a].elapsed_time(e[b]) for e in events])
 
     fwd_ms = span(0, 1)
-    pre_ms = span(1, 2) if with_bwd else np.zeros(1)
+    dq_ms = span(1, 2) if with_bwd else np.zeros(1)
     dkdv_ms = span(2, 3) if with_bwd else np.zeros(1)
-    dq_ms = span(3, 4) if with_bwd else np.zeros(1)
-    bwd_ms = span(1, 4) if with_bwd else np.zeros(1)
+    bwd_ms = span(1, 3) if with_bwd else np.zeros(1)
     ms_per_step = wall * 1e3 / args.steps
 
     pairs_b, acr = aah.window_stats(wl.windows, T)
@@ -232,7 +230,6 @@ def main():
             "acr": round(acr, 4),
             "fwd_ms": round(float(fwd_ms.mean()), 4),
             "bwd_ms": round(float(bwd_ms.mean()), 4) if with_bwd else None,
-            "bwd_preprocess_ms": round(float(pre_ms.mean()), 4) if with_bwd else None,
             "bwd_dkdv_ms": round(float(dkdv_ms.mean()), 4) if with_bwd else None,
             "bwd_dq_ms": round(float(dq_ms.mean()), 4) if with_bwd else None,
             "fwd_tflops": round(fwd_tf, 2),

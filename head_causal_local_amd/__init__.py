@@ -16,7 +16,7 @@ import numpy as np
 
 from ._lib import (AAH_BF16, AAH_F32, AahError, EXPORTS, LIB_PATH, WorkItem, check, lib)  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
            "cache_clear", "AahError", "LIB_PATH"]
 
 
@@ -127,18 +127,6 @@ def _ws(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
-def attn_bwd_preprocess(o, do, lse, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 1: -lse * log2(e) and -rowsum(do * o) into the workspace."""
-    _check_operand("do", do, o)
-    B, H, T, d = o.shape
-    if lse.shape != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_preprocess(o.data_ptr(), do.data_ptr(), lse.data_ptr(), B, H, T, d, _dtype_code(o),
-                                        scale, ptr, nbytes, _stream_ptr(o, stream)))
-
-
 def _bwd_args(q, k, v, do, windows, scale):
     for name, t in (("k", k), ("v", v), ("do", do)):
         _check_operand(name, t, q)
@@ -150,8 +138,22 @@ def _bwd_args(q, k, v, do, windows, scale):
     return B, H, T, d, w, float(scale)
 
 
+def attn_bwd_dq(q, k, v, o, do, lse, windows, dq, workspace, scale: Optional[float] = None, stream=None):
+    """Backward step 1: dQ, and the per-row -lse * log2(e) and -rowsum(do * o) into the workspace."""
+    import torch
+    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
+    _check_operand("o", o, q)
+    _check_operand("dq", dq, q)
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    ptr, nbytes = _ws(workspace)
+    check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+                                lse.data_ptr(), _wptr(w), B, H, T, d, _dtype_code(q), scale, dq.data_ptr(), ptr,
+                                nbytes, _stream_ptr(q, stream)))
+
+
 def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 2: dK and dV (needs attn_bwd_preprocess's workspace, same scale)."""
+    """Backward step 2: dK and dV (reads the workspace rows attn_bwd_dq wrote; run it after that step)."""
     B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
     _check_operand("dk", dk, q)
     _check_operand("dv", dv, q)
@@ -159,16 +161,6 @@ def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float
     check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
                                   B, H, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
-
-
-def attn_bwd_dq(q, k, v, do, windows, dq, workspace, scale: Optional[float] = None, stream=None):
-    """Backward step 3: dQ (needs attn_bwd_preprocess's workspace, same scale)."""
-    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
-    _check_operand("dq", dq, q)
-    ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
-                                B, H, T, d, _dtype_code(q), scale, dq.data_ptr(), ptr, nbytes,
-                                _stream_ptr(q, stream)))
 
 
 def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:

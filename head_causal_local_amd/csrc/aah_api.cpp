@@ -270,24 +270,6 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
   return AAH_OK;
 }
 
-aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int T, int d,
-                                   aah_dtype dt, float scale, void* workspace, size_t workspace_bytes,
-                                   aah_stream_t stream) {
-  g_detail.clear();
-  AAH_TRY(check_dims(B, H, T, d, dt));
-  AAH_TRY(check_tensor(o, "o", 16));
-  AAH_TRY(check_tensor(dout, "dout", 16));
-  AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
-  AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  const aah::AttnShape s{B, H, T, d, scale};
-  const hipError_t e = aah::launch_bwd_preprocess(o, dout, lse, dt == AAH_BF16, const_cast<float*>(ws_nl2(workspace)),
-                                                  const_cast<float*>(ws_nd(workspace, B, H, T)), s,
-                                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return hip_fail(e, "backward preprocess launch");
-  return AAH_OK;
-}
-
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const int32_t* windows,
                              int B, int H, int T, int d, aah_dtype dt, float scale, void* dk, void* dv,
                              const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
@@ -321,33 +303,39 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   return AAH_OK;
 }
 
-aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout, const int32_t* windows,
-                           int B, int H, int T, int d, aah_dtype dt, float scale, void* dq, const void* workspace,
-                           size_t workspace_bytes, aah_stream_t stream) {
+aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
+                           float scale, void* dq, void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_shape(windows, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(dout, "dout", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
   AAH_TRY(check_tensor(dq, "dq", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const float* nl2 = ws_nl2(workspace);
-  const float* nd = ws_nd(workspace, B, H, T);
+  float* nl2 = const_cast<float*>(ws_nl2(workspace));
+  float* nd = const_cast<float*>(ws_nd(workspace, B, H, T));
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
   DevicePlan plan;
   AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
   hipError_t e;
-  if (dt == AAH_BF16)
-    e = aah::launch_bwd_dq_bf16(q, k, v, dout, nl2, nd, dq, plan.items, plan.n_items, plan.win, s, st);
-  else
-    e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
-                                  static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
-                                  static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
+  if (dt == AAH_BF16) {
+    // One kernel: D and the workspace rows come out of the dQ kernel's prologue.
+    e = aah::launch_bwd_dq_bf16(q, k, v, o, dout, lse, nl2, nd, dq, plan.items, plan.n_items, plan.win, s, st);
+  } else {
+    e = aah::launch_bwd_preprocess(o, dout, lse, false, nl2, nd, s, st);
+    if (e == hipSuccess)
+      e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
+                                    static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
+                                    static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "dQ launch");
   return AAH_OK;
 }
@@ -370,10 +358,10 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dv, "dv", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  AAH_TRY(aah_attn_bwd_preprocess(o, dout, lse, B, H, T, d, dt, scale, workspace, workspace_bytes, stream));
-  AAH_TRY(aah_attn_bwd_dkdv(q, k, v, dout, windows, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
-                            stream));
-  return aah_attn_bwd_dq(q, k, v, dout, windows, B, H, T, d, dt, scale, dq, workspace, workspace_bytes, stream);
+  AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, B, H, T, d, dt, scale, dq, workspace, workspace_bytes,
+                          stream));
+  return aah_attn_bwd_dkdv(q, k, v, dout, windows, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
+                           stream);
 }
 
 aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,

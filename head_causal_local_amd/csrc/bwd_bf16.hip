@@ -5,8 +5,9 @@
 // i - W < j <= i), given the forward's per-row log-sum-exp:
 //   P = exp(scale Q K^T - lse),  dP = dO V^T,  dS = P * (dP - D),  D_i = dO_i . O_i,
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
-// The preprocess step leaves nl2 = -lse log2(e) and nD = -D per row in the
-// workspace.  Each kernel keeps its stationary operand of S (K rows in the
+// The query-stationary kernel runs first: from each of its query rows it forms
+// D = dO . O and leaves nl2 = -lse log2(e) and nD = -D in the workspace, which
+// the key-stationary kernel then reads.  Each kernel keeps its stationary operand of S (K rows in the
 // key-stationary kernel, Q rows in the query-stationary one) in registers
 // premultiplied by c = scale log2(e) and rounded to bf16, and starts the S and
 // dP MFMA chains from nl2 and nD instead of zero.  So c s - lse log2(e) and
@@ -30,8 +31,8 @@
 //
 // bwd_dq_kernel -- one item = 128 queries of one head (4 waves x 32 queries)
 //   and the 64-key tiles of their windows (the forward's work list).  Q and dO
-//   rows stay in registers; K and V tiles come through the same kind of LDS
-//   ring.  For each 32-key block S^T = K Q^T and dP^T = V dO^T with M = keys,
+//   rows stay in registers (the O rows are read once, for D); K and V tiles
+//   come through the same kind of LDS ring.  For each 32-key block S^T = K Q^T and dP^T = V dO^T with M = keys,
 //   so P^T and dS^T come out with one query per lane and are directly the B
 //   operand of dQ^T += K^T dS^T, whose A operand is read transposed from the
 //   row-major K tile.
@@ -326,9 +327,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 template <int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                   const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
-                   bf16* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
-                   int H, int T, float scale) {
+                   const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
+                   float* __restrict__ NL2, float* __restrict__ ND, bf16* __restrict__ dQ,
+                   const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff, int H, int T,
+                   float scale) {
   using C = Cfg<D>;
   constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
   __shared__ __attribute__((aligned(1024))) char ring0[kStage];
@@ -365,22 +367,36 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
 
   // Q (premultiplied by c) and dO rows of this lane's query: the B operands of
-  // S^T = K Q^T and dP^T = V dO^T.
+  // S^T = K Q^T and dP^T = V dO^T.  Lanes ln and ln + 32 hold the two halves
+  // of the row (dims 16 st + 8 hl + 0..7).
   bf16x8 qf[C::kSteps], gf[C::kSteps];
   float cl = 0.f, nD = 0.f;  // -lse log2(e) and -D of this lane's query
   {
     const uint32_t slice = static_cast<uint32_t>(T) * C::kRowBytes;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + base, slice);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(dO + base, slice);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(O + base, slice);
+    bf16x8 of[C::kSteps];
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) {
       const uint32_t o = static_cast<uint32_t>(qi) * C::kRowBytes + (16 * st + 8 * hl) * 2;
       qf[st] = __builtin_bit_cast(bf16x8, load16(rq, o));
       gf[st] = __builtin_bit_cast(bf16x8, load16(rg, o));
+      of[st] = __builtin_bit_cast(bf16x8, load16(ro, o));
     }
-    const uint32_t rows = static_cast<uint32_t>(T) * 4;
-    cl = load_f32(make_rsrc(NL2 + rbase, rows), static_cast<uint32_t>(qi) * 4);
-    nD = load_f32(make_rsrc(ND + rbase, rows), static_cast<uint32_t>(qi) * 4);
+    const float lse = load_f32(make_rsrc(LSE + rbase, static_cast<uint32_t>(T) * 4), static_cast<uint32_t>(qi) * 4);
+    // D = dO . O over this lane's half row, then over both halves.
+    float dh = 0.f;
+#pragma unroll
+    for (int st = 0; st < C::kSteps; ++st)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const bf16x2 a = {gf[st][e], gf[st][e + 1]};
+        const bf16x2 b = {of[st][e], of[st][e + 1]};
+        dh = __builtin_amdgcn_fdot2_f32_bf16(a, b, dh, false);
+      }
+    nD = -half_swap_sum(dh);
+    cl = -lse * kLog2e;
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) qf[st] = scale_bf16x8(qf[st], c);
     // Consume the rows here: the compiler's wait for them (which also covers
@@ -461,6 +477,13 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   }
 
   if (qi >= T) return;
+  // The rows the key-stationary kernel starts its chains from (stored here,
+  // after the loop, so that no store is outstanding while the loop counts its
+  // copies).
+  if (hl == 0) {
+    NL2[rbase + qi] = cl;
+    ND[rbase + qi] = nD;
+  }
   bf16* dqrow = dQ + base + static_cast<size_t>(qi) * D;
   // dQ^T block b, register r: dim 32 b + 8 (r/4) + 4 hl + r%4 of this lane's query.
 #pragma unroll
@@ -482,12 +505,13 @@ hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout,
 }
 
 template <int D>
-hipError_t dq_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
-                void* dq, const WorkItem* items, int n_items, const int32_t* win_eff, const AttnShape& s,
-                hipStream_t stream) {
+hipError_t dq_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+                const AttnShape& s, hipStream_t stream) {
   hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nl2,
-                     nd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T, s.scale);
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(o),
+                     static_cast<const bf16*>(dout), lse, nl2, nd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T,
+                     s.scale);
   return hipGetLastError();
 }
 
@@ -504,13 +528,13 @@ hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, con
   }
 }
 
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
-                              const float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                              const AttnShape& s, hipStream_t stream) {
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items, int n_items,
+                              const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_d<32>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
-    case 64: return dq_d<64>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
-    case 128: return dq_d<128>(q, k, v, dout, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 32: return dq_d<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 64: return dq_d<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 128: return dq_d<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

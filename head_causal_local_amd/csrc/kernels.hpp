@@ -47,9 +47,11 @@ hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, con
                                 const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
 
 // dQ: items from the forward planner (kFwdBf16RowTile queries, kFwdBf16ColTile keys per step).
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
-                              const float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                              const AttnShape& s, hipStream_t stream);
+// Also writes, for every row, nl2 = -lse log2(e) and nd = -(dO . O), which
+// launch_bwd_dkdv_bf16 reads: it must run first.
+hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                              const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items, int n_items,
+                              const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
 
 // Scalar backward for fp32: dQ one query row per lane over the forward work
 // list; dK/dV one key row per lane over the backward work list.

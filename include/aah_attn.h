@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 1
+#define AAH_ABI_VERSION 2
 
 typedef enum {
   AAH_OK = 0,
@@ -106,8 +106,7 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
  * exactly once: no atomics, results are bitwise reproducible).  Needs a device
  * workspace of at least aah_attn_workspace_size(B, H, T, d, dt, 1) bytes,
  * 256-byte aligned; its contents on entry do not matter and are clobbered.
- * Runs aah_attn_bwd_preprocess, aah_attn_bwd_dkdv and aah_attn_bwd_dq, in
- * that order, on `stream`.
+ * Runs aah_attn_bwd_dq and then aah_attn_bwd_dkdv on `stream`.
  */
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse,
@@ -117,30 +116,25 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         aah_stream_t stream);
 
 /*
- * The backward's steps as separate calls, for callers that schedule or time
- * them.  Arguments mean what they mean for aah_attn_bwd and the same checks
- * apply; the workspace carries two fp32 [B,H,T] arrays from the first step to
- * the other two (nl2 = -lse log2(e) at byte 0, then nD = -D at the next
- * 256-byte boundary after B*H*T floats).
- *   aah_attn_bwd_preprocess: D_i = dout_i . o_i; writes nl2 and nD into the
- *     workspace.  Must complete before either of the others starts.
- *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel).
- *   aah_attn_bwd_dq:   writes dq (query-stationary kernel).
- * dkdv and dq only read the workspace and may run in either order or
- * concurrently on different streams once the preprocess has completed.
+ * The backward's two steps as separate calls, for callers that schedule or
+ * time them.  Arguments mean what they mean for aah_attn_bwd and the same
+ * checks apply.  The workspace carries two fp32 [B,H,T] arrays from the first
+ * step to the second: nl2 = -lse log2(e) at byte 0, then nD = -D, with
+ * D_i = dout_i . o_i, at the next 256-byte boundary after B*H*T floats.
+ *   aah_attn_bwd_dq:   writes dq (query-stationary kernel) and, for every
+ *     row, nl2 and nD into the workspace.
+ *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel) from q, k,
+ *     v, dout and the workspace rows; it must not start before
+ *     aah_attn_bwd_dq has completed on the same workspace.
  */
-aah_status aah_attn_bwd_preprocess(const void* o, const void* dout, const float* lse, int B, int H, int T, int d,
-                                   aah_dtype dt, float scale, void* workspace, size_t workspace_bytes,
-                                   aah_stream_t stream);
+aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                           const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
+                           float scale, void* dq, void* workspace, size_t workspace_bytes, aah_stream_t stream);
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                              const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
                              void* dk, void* dv, const void* workspace, size_t workspace_bytes,
                              aah_stream_t stream);
-
-aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                           const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
-                           void* dq, const void* workspace, size_t workspace_bytes, aah_stream_t stream);
 
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == 1
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 2
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -113,13 +113,21 @@ def test_bwd_step_validation():
     assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need,
                                  None) == 1
     w[1] = 3
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, 0, FAKE, need, None) == 1
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8, None) == 3
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 48, 0, 0.1, FAKE, need, None) == 2
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, 0, 1, 2, 64, 64, 0, 0.1, FAKE, need, None) == 1   # NULL lse
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, 0.1, FAKE, 8, None) == 3   # small ws
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, 0.0, FAKE, need, None) == 1  # scale 0
-    assert lib.aah_attn_bwd_preprocess(FAKE, FAKE, FAKE, 1, 2, 64, 64, 0, float("inf"), FAKE, need, None) == 1
+    # aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, B, H, T, d, dt, scale, dq, workspace, bytes, stream)
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, 0, FAKE, need,
+                               None) == 1                                                      # NULL dq
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8,
+                               None) == 3                                                      # small ws
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, need,
+                               None) == 2                                                      # d = 48
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 0, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+                               None) == 1                                                      # NULL lse
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, 0, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+                               None) == 1                                                      # NULL o
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.0, FAKE, FAKE, need,
+                               None) == 1                                                      # scale 0
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
+                               need, None) == 1                                                # scale inf
 
 
 def test_slice_limit():

@@ -234,7 +234,7 @@ def test_1b_layer_backward_sampled_heads():
 
 def test_backward_deterministic_and_steps():
     """The backward writes every gradient once (no atomics): two runs are bitwise equal, and the
-    three separate steps reproduce the combined call bitwise."""
+    two separate steps (dQ, then dK/dV) reproduce the combined call bitwise."""
     _require_gpu()
     wl = synth.random_workload(2, 3, 700, 64, [64, 700, 300], dtype="bf16", seed=17, backward=True)
     q, k, v, do = dev(wl, "q"), dev(wl, "k"), dev(wl, "v"), dev(wl, "do")
@@ -243,8 +243,7 @@ def test_backward_deterministic_and_steps():
     g2 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows)
     ws = torch.empty(aah.workspace_size(2, 3, 700, 64, "bf16"), dtype=torch.uint8, device="cuda")
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    aah.attn_bwd_preprocess(o, do, lse, ws)
-    aah.attn_bwd_dq(q, k, v, do, wl.windows, dq, ws)     # either order after the preprocess
+    aah.attn_bwd_dq(q, k, v, o, do, lse, wl.windows, dq, ws)   # also writes the workspace rows
     aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws)
     torch.cuda.synchronize()
     for a, b, c in zip(g1, g2, (dq, dk, dv)):
