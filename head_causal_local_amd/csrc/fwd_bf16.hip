@@ -67,9 +67,10 @@ struct Cfg {
   static constexpr int kDmaPerWave = kNC / kWaves;  // 1 KiB DMA instructions per wave per tensor per tile
   static constexpr int kSteps = D / 16;             // MFMA k-steps over d for S^T
   static constexpr int kBlocks = D / 32;            // 32-row blocks of O^T
-  // Resident waves per SIMD the register allocation is sized for.
-  // (d = 64: 94 registers and 32 KiB of LDS per workgroup allow five.)
-  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 5 : 1;
+  // Resident waves per SIMD the register allocation is sized for.  At d = 64
+  // LDS is the tighter bound: a CU holds four workgroups of 32 KiB (five only
+  // at 32000 bytes or less), so registers up to 128 would cost nothing.
+  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 4 : 1;
   static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
 };
 
@@ -280,8 +281,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // reading before the barrier that ended the previous step), computes the
   // current tile, then waits for its own copies and meets the other waves at
   // the barrier.  Returns true after the last tile.  Two stages instead of
-  // three leave room for five workgroups per CU at d = 64; the copies still
-  // have a whole step to land.
+  // three leave room for four workgroups per CU at d = 64 instead of three;
+  // the copies still have a whole step to land.
   auto step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
     const bool fill = kt + 1 < it.hi;
     if (fill) issue_tile(kt + 1, kn, vn);
