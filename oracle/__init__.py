@@ -19,3 +19,9 @@ from .attention import (  # noqa: F401
     acr_ref,
     acr_from_fractions_ref,
 )
+from .decode import (  # noqa: F401
+    cache_rows_ref,
+    decode_positions,
+    decode_ref,
+    cache_content_ref,
+)
