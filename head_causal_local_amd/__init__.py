@@ -16,7 +16,8 @@ import numpy as np
 
 from ._lib import (AAH_BF16, AAH_F32, AahError, EXPORTS, LIB_PATH, WorkItem, check, lib)  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
+__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "kv_cache_fill", "kv_cache_rows",
+           "decode_workspace_size", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
            "cache_clear", "AahError", "LIB_PATH"]
 
 
@@ -161,6 +162,75 @@ def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float
     check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
                                   B, H, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
+
+
+def kv_cache_rows(windows, T_max: int) -> int:
+    """Rows per batch entry of the trimmed decode caches: sum over heads of min(W_h, T_max)."""
+    w = _windows_arg(windows)
+    r = int(lib().aah_kv_cache_rows(_wptr(w), w.shape[0], int(T_max)))
+    if r < 0:
+        raise ValueError("invalid windows or T_max")
+    return r
+
+
+def decode_workspace_size(windows, B: int, T_max: int, d: int) -> int:
+    """Workspace bytes of one decoding step (bf16)."""
+    w = _windows_arg(windows)
+    return int(lib().aah_attn_decode_workspace_size(_wptr(w), B, w.shape[0], int(T_max), d, AAH_BF16))
+
+
+def kv_cache_fill(k, v, windows, T_max: int, kcache=None, vcache=None, stream=None):
+    """Store a prefill's K/V [B, H, T, d] (positions 0..T-1) into trimmed caches [B, R, d]."""
+    import torch
+    _check_operand("v", v, k)
+    B, H, T, d = k.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    R = kv_cache_rows(w, T_max)
+    if kcache is None:
+        kcache = torch.zeros((B, R, d), dtype=k.dtype, device=k.device)
+    if vcache is None:
+        vcache = torch.zeros((B, R, d), dtype=k.dtype, device=k.device)
+    for name, t in (("kcache", kcache), ("vcache", vcache)):
+        if t.shape != (B, R, d) or t.dtype != k.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{B}, {R}, {d}] tensor of k's dtype")
+    check(lib().aah_kv_cache_fill(k.data_ptr(), v.data_ptr(), _wptr(w), B, H, T, int(T_max), d, _dtype_code(k),
+                                  kcache.data_ptr(), vcache.data_ptr(), _stream_ptr(k, stream)))
+    return kcache, vcache
+
+
+def attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, scale: Optional[float] = None,
+                out=None, lse=None, workspace=None, stream=None):
+    """One decoding step: q, k_new, v_new [B, H, d] at positions pos (int32 device tensor [B]).
+
+    Stores k_new / v_new into the caches and returns (o [B, H, d], lse [B, H])."""
+    import torch
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _check_operand(name, t, q)
+    B, H, d = q.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    R = kv_cache_rows(w, T_max)
+    for name, t in (("kcache", kcache), ("vcache", vcache)):
+        if t.shape != (B, R, d) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{B}, {R}, {d}] tensor of q's dtype")
+    if pos.shape != (B,) or pos.dtype != torch.int32 or not pos.is_contiguous() or pos.device != q.device:
+        raise ValueError("pos must be a contiguous int32 [B] tensor on q's device")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_operand("out", out, q)
+    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(decode_workspace_size(w, B, T_max, d), 1), dtype=torch.uint8, device=q.device)
+    ptr, nbytes = _ws(workspace)
+    check(lib().aah_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(),
+                                vcache.data_ptr(), pos.data_ptr(), _wptr(w), B, H, int(T_max), d, _dtype_code(q),
+                                scale, out.data_ptr(), lse.data_ptr(), ptr, nbytes, _stream_ptr(q, stream)))
+    return out, lse
 
 
 def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:

@@ -19,12 +19,13 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
     "aah_attn_workspace_size", "aah_tile_shape", "aah_plan_fwd", "aah_plan_bwd", "aah_window_stats",
-    "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv",
+    "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
+    "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode",
 )
 
 
@@ -84,6 +85,16 @@ def _declare(lib):
     lib.aah_window_stats.argtypes = [P_i32, c_int, c_int, P_i64, P_double]
     lib.aah_cache_clear.restype = None
     lib.aah_cache_clear.argtypes = []
+    lib.aah_kv_cache_rows.restype = c_int64
+    lib.aah_kv_cache_rows.argtypes = [P_i32, c_int, c_int]
+    lib.aah_attn_decode_workspace_size.restype = c_size_t
+    lib.aah_attn_decode_workspace_size.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int]
+    lib.aah_kv_cache_fill.restype = c_int
+    lib.aah_kv_cache_fill.argtypes = [c_void_p, c_void_p, P_i32, c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_void_p, c_void_p, c_void_p]
+    lib.aah_attn_decode.restype = c_int
+    lib.aah_attn_decode.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int,
+                                    c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
 
 
 def lib():

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -181,6 +182,99 @@ aah_status check_workspace(const void* workspace, size_t workspace_bytes, int B,
     return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
                 need);
   if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  return AAH_OK;
+}
+
+// ------------------------------------------------------------------ decode plans
+
+struct DecodePlan {
+  aah::DecodeChunk* chunks = nullptr;
+  int32_t* tables = nullptr;  // head_off[H], head_cap[H], head_first[H + 1]
+  std::vector<int32_t> host_cap;
+  int n_chunks = 0;
+  int rows = 0;
+  int H = 0;
+  aah::DecodePlanView view() const {
+    return aah::DecodePlanView{chunks, n_chunks, tables, tables + H, tables + 2 * H, rows, host_cap.data()};
+  }
+};
+
+std::map<std::vector<int64_t>, DecodePlan> g_decode_cache;
+
+// Rows R = sum_h min(W_h, T_max) of one batch entry's cache; -1 if it does not fit in int32.
+int64_t decode_rows(const int32_t* windows, int H, int T_max) {
+  int64_t r = 0;
+  for (int h = 0; h < H; ++h) r += std::min<int64_t>(windows[h], T_max);
+  return r > INT32_MAX ? -1 : r;
+}
+
+int decode_chunks(const int32_t* windows, int H, int T_max) {
+  int64_t n = 0;
+  for (int h = 0; h < H; ++h) n += (std::min<int64_t>(windows[h], T_max) + aah::kDecodeRows - 1) / aah::kDecodeRows;
+  return static_cast<int>(n);
+}
+
+aah_status get_decode_plan(const int32_t* windows, int H, int T_max, const DecodePlan** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::vector<int64_t> key = {dev, H, T_max};
+  for (int h = 0; h < H; ++h) key.push_back(std::min(windows[h], T_max));
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto found = g_decode_cache.find(key);
+  if (found != g_decode_cache.end()) {
+    *out = &found->second;
+    return AAH_OK;
+  }
+  DecodePlan p;
+  p.H = H;
+  std::vector<int32_t> tables(3 * H + 1);
+  std::vector<aah::DecodeChunk> chunks;
+  int32_t off = 0;
+  for (int h = 0; h < H; ++h) {
+    const int32_t cap = std::min(windows[h], T_max);
+    tables[h] = off;
+    tables[H + h] = cap;
+    tables[2 * H + h] = static_cast<int32_t>(chunks.size());
+    for (int32_t s0 = 0; s0 < cap; s0 += aah::kDecodeRows) chunks.push_back(aah::DecodeChunk{h, s0});
+    off += cap;
+  }
+  tables[3 * H] = static_cast<int32_t>(chunks.size());
+  p.rows = off;
+  p.n_chunks = static_cast<int>(chunks.size());
+  p.host_cap.assign(tables.begin() + H, tables.begin() + 2 * H);
+  e = hipMalloc(&p.chunks, chunks.size() * sizeof(aah::DecodeChunk));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(decode chunks)");
+  e = hipMalloc(&p.tables, tables.size() * sizeof(int32_t));
+  if (e != hipSuccess) {
+    (void)hipFree(p.chunks);
+    return hip_fail(e, "hipMalloc(decode tables)");
+  }
+  e = hipMemcpy(p.chunks, chunks.data(), chunks.size() * sizeof(aah::DecodeChunk), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemcpy(p.tables, tables.data(), tables.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(p.chunks);
+    (void)hipFree(p.tables);
+    return hip_fail(e, "hipMemcpy(decode tables)");
+  }
+  auto it = g_decode_cache.emplace(std::move(key), std::move(p)).first;
+  *out = &it->second;
+  return AAH_OK;
+}
+
+size_t decode_workspace(const int32_t* windows, int B, int H, int T_max, int d) {
+  return round_up(static_cast<size_t>(B) * decode_chunks(windows, H, T_max) * (2 + d) * sizeof(float), 256);
+}
+
+// Checks shared by the decode entry points (bf16 only; T_max plays the role of T).
+aah_status check_decode(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt) {
+  AAH_TRY_INNER(check_shape(windows, B, H, T_max, d, dt));
+  if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
+  if (decode_rows(windows, H, T_max) < 0) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
+  // The decode and cache-fill launches put B (and B * H) on the second grid dimension.
+  if (static_cast<int64_t>(B) * H > 65535) return fail(AAH_ERR_UNSUPPORTED, "B * H = %lld exceeds 65535", static_cast<long long>(B) * H);
+  if (static_cast<int64_t>(B) * decode_rows(windows, H, T_max) * d >= (int64_t{1} << 40))
+    return fail(AAH_ERR_UNSUPPORTED, "cache too large");
   return AAH_OK;
 }
 
@@ -364,6 +458,67 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
                            stream);
 }
 
+int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max) {
+  g_detail.clear();
+  if (windows == nullptr || H < 1 || T_max < 1) return -1;
+  for (int h = 0; h < H; ++h)
+    if (windows[h] < 1) return -1;
+  return decode_rows(windows, H, T_max);
+}
+
+size_t aah_attn_decode_workspace_size(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt) {
+  if (windows == nullptr || B < 1 || H < 1 || T_max < 1 || !supported_d(d) || dt != AAH_BF16) return 0;
+  for (int h = 0; h < H; ++h)
+    if (windows[h] < 1) return 0;
+  return decode_workspace(windows, B, H, T_max, d);
+}
+
+aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, int B, int H, int T, int T_max,
+                             int d, aah_dtype dt, void* kcache, void* vcache, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_decode(windows, B, H, T_max, d, dt));
+  if (T < 1 || T > T_max) return fail(AAH_ERR_INVALID_ARG, "prefill length T = %d must be in [1, T_max = %d]", T, T_max);
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  AAH_TRY(check_tensor(kcache, "kcache", 16));
+  AAH_TRY(check_tensor(vcache, "vcache", 16));
+  const DecodePlan* plan = nullptr;
+  AAH_TRY(get_decode_plan(windows, H, T_max, &plan));
+  const hipError_t e = aah::launch_cache_fill_bf16(k, v, kcache, vcache, plan->view(), B, H, T, d,
+                                                   static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache fill launch");
+  return AAH_OK;
+}
+
+aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                           const int32_t* pos, const int32_t* windows, int B, int H, int T_max, int d,
+                           aah_dtype dt, float scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                           aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_decode(windows, B, H, T_max, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k_new, "k_new", 16));
+  AAH_TRY(check_tensor(v_new, "v_new", 16));
+  AAH_TRY(check_tensor(kcache, "kcache", 16));
+  AAH_TRY(check_tensor(vcache, "vcache", 16));
+  AAH_TRY(check_tensor(pos, "pos", 4));
+  AAH_TRY(check_tensor(o, "o", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  const size_t need = decode_workspace(windows, B, H, T_max, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
+                need);
+  if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  const DecodePlan* plan = nullptr;
+  AAH_TRY(get_decode_plan(windows, H, T_max, &plan));
+  const hipError_t e = aah::launch_decode_bf16(q, k_new, v_new, kcache, vcache, pos, plan->view(), B, H, T_max, d,
+                                               scale, o, lse, static_cast<float*>(workspace),
+                                               static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return AAH_OK;
+}
+
 aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();
@@ -400,6 +555,11 @@ void aah_cache_clear(void) {
     (void)hipFree(kv.second.win);
   }
   g_cache.clear();
+  for (auto& kv : g_decode_cache) {
+    (void)hipFree(kv.second.chunks);
+    (void)hipFree(kv.second.tables);
+  }
+  g_decode_cache.clear();
 }
 
 }  // extern "C"

@@ -63,4 +63,38 @@ hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v
                                   const WorkItem* items, int n_items, const int32_t* win_eff,
                                   const AttnShape& s, hipStream_t stream);
 
+// ---- decoding over per-head trimmed K/V caches (bf16)
+constexpr int kDecodeRows = 256;  // ring rows per decode workgroup
+
+// One decode workgroup's share: ring rows [slot0, slot0 + kDecodeRows) of one head.
+struct DecodeChunk {
+  int32_t head;
+  int32_t slot0;
+};
+static_assert(sizeof(DecodeChunk) == 8, "DecodeChunk layout");
+
+// Device tables of one (H, T_max, windows) combination: head h's ring has
+// head_cap[h] = min(W_h, T_max) rows starting at row head_off[h]; its chunks
+// are [head_first[h], head_first[h + 1]).
+struct DecodePlanView {
+  const DecodeChunk* chunks;
+  int n_chunks;
+  const int32_t* head_off;
+  const int32_t* head_cap;
+  const int32_t* head_first;
+  int rows;                  // R = sum of head_cap
+  const int32_t* host_cap;   // host copy of head_cap
+};
+
+// Writes k_new / v_new [B,H,d] into the ring row of position pos[b] (device
+// int32[B], clamped to [0, T_max)) and o [B,H,d] / lse [B,H] of that token;
+// partials: B * n_chunks * (2 + d) floats.
+hipError_t launch_decode_bf16(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
+                              const int32_t* pos, const DecodePlanView& plan, int B, int H, int T_max, int d,
+                              float scale, void* o, float* lse, float* partials, hipStream_t stream);
+
+// Copies the positions each ring keeps (the last min(C_h, T)) of a prefill k, v [B,H,T,d].
+hipError_t launch_cache_fill_bf16(const void* k, const void* v, void* kcache, void* vcache,
+                                  const DecodePlanView& plan, int B, int H, int T, int d, hipStream_t stream);
+
 }  // namespace aah

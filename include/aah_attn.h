@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 2
+#define AAH_ABI_VERSION 3
 
 typedef enum {
   AAH_OK = 0,
@@ -135,6 +135,54 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
                              const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
                              void* dk, void* dv, const void* workspace, size_t workspace_bytes,
                              aah_stream_t stream);
+
+/*
+ * Decoding over per-head trimmed K/V caches (bf16).
+ *
+ * One decoding step is section 5.8 for the newest position only: the token at
+ * position p of head h (window W_h) attends to positions max(0, p - C_h + 1)
+ * .. p, where C_h = min(W_h, T_max) and T_max is the maximum context the
+ * caches are built for.  Table 6 runs inference with per-head windows, and
+ * "Autonomy-of-Heads" section 5 bounds a streaming head's decode-time cache
+ * by its window: here head h keeps exactly C_h rows of K and of V.
+ *
+ * Cache layout: kcache and vcache are device tensors [B, R, d] of dtype dt
+ * with R = aah_kv_cache_rows(windows, H, T_max) = sum_h C_h.  Head h owns rows
+ * off_h .. off_h + C_h - 1 (off_h = sum of C over the heads before h), and
+ * position t of head h lives in row off_h + (t mod C_h).  Rows not yet written
+ * are never read.  Only dt = AAH_BF16 is supported (AAH_ERR_UNSUPPORTED
+ * otherwise); d in {32, 64, 128}; windows and stream as for the other calls.
+ */
+
+/* R = sum_h min(windows[h], T_max) rows per batch entry; -1 for invalid arguments. */
+int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max);
+
+/* Workspace bytes aah_attn_decode needs (B * chunks * (2 + d) floats, chunks =
+ * sum_h ceil(C_h / 256)); 0 for invalid arguments. */
+size_t aah_attn_decode_workspace_size(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt);
+
+/*
+ * Prefill into the caches: k, v [B,H,T,d] hold positions 0 .. T - 1
+ * (1 <= T <= T_max); writes the positions each head keeps, the last
+ * min(C_h, T) of them, into their rows.  Other rows are left as they are.
+ */
+aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, int B, int H, int T, int T_max,
+                             int d, aah_dtype dt, void* kcache, void* vcache, aah_stream_t stream);
+
+/*
+ * One decoding step.  q, k_new, v_new [B,H,d]: the new token of every
+ * sequence; pos: DEVICE pointer to int32[B], the new token's position in each
+ * sequence, 0 <= pos[b] < T_max (values outside are clamped into that range),
+ * with positions max(0, pos[b] - C_h + 1) .. pos[b] - 1 already in the cache.
+ * Writes k_new / v_new into the row of position pos[b] and o [B,H,d] (dtype
+ * dt), lse [B,H] (fp32, natural log of sum_j exp(scale q . k_j) over the
+ * attended positions).  Workspace: at least aah_attn_decode_workspace_size
+ * bytes, 256-byte aligned; contents on entry do not matter.
+ */
+aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                           const int32_t* pos, const int32_t* windows, int B, int H, int T_max, int d,
+                           aah_dtype dt, float scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                           aah_stream_t stream);
 
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */

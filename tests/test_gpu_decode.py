@@ -1,0 +1,125 @@
+"""GPU parity of decoding over per-head trimmed K/V caches, through the C ABI.
+
+The expected values come from oracle.decode_ref / oracle.cache_content_ref on the same
+bf16-rounded histories the device sees.  Outputs: bf16 o within 1e-2 max-abs (widened to
+2^-8 |ref| above 2.56, as for the forward), fp32 lse within 1e-3 (the step sums fp32
+weights, so only exp2 and accumulation rounding remain); cache rows bit-exact.
+"""
+import numpy as np
+import pytest
+import torch
+
+import head_causal_local_amd as aah
+import oracle
+from synth import bf16_bits, bf16_to_f32
+
+pytestmark = pytest.mark.gpu
+
+O_TOL = 1e-2
+LSE_TOL = 1e-3
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a HIP device")
+
+
+def _history(B, H, L, d, seed):
+    """bf16-exact fp32 histories q, k, v [B, H, L, d] and their device copies."""
+    rng = np.random.default_rng(seed)
+    host, devs = [], []
+    for _ in range(3):
+        bits = bf16_bits(rng.standard_normal((B, H, L, d), dtype=np.float32))
+        host.append(bf16_to_f32(bits).astype(np.float64))
+        devs.append(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda"))
+    return host, devs
+
+
+def _check_o(got, ref):
+    got = got.float().cpu().numpy().astype(np.float64)
+    bound = np.maximum(O_TOL, np.abs(ref) * 2.0 ** -8)
+    assert (np.abs(got - ref) - bound).max() <= 0, f"max |err| {np.abs(got - ref).max():.3e}"
+
+
+def _check_cache(kc, vc, kh, vh, windows, n_written, T_max):
+    for cache, hist in ((kc, kh), (vc, vh)):
+        rows, valid = oracle.cache_content_ref(hist, windows, n_written, T_max)
+        got = cache.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(got[valid], rows[valid])
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("windows,T_max,T0", [
+    ([1, 5, 256, 300], 300, 200),        # W = 1, a window filling the cache, one wider than T_max
+    ([40, 513, 1000, 700], 1024, 700),   # rings of 40, 513 (3 chunks), 1000; ragged chunk tails
+])
+def test_prefill_then_decode_steps(d, windows, T_max, T0):
+    """Prefill T0 positions, then 40 decoding steps; each step against the oracle, and the
+    caches bit-exact against the storage rule at the end (several rings wrap around)."""
+    _require_gpu()
+    B, H, steps = 2, len(windows), 40
+    L = T0 + steps
+    (qh, kh, vh), (q, k, v) = _history(B, H, L, d, seed=d)
+    scale = 1.0 / np.sqrt(d)
+    kc, vc = aah.kv_cache_fill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), windows, T_max)
+    _check_cache(kc, vc, kh, vh, windows, [T0, T0], T_max)
+    ws = torch.empty(aah.decode_workspace_size(windows, B, T_max, d), dtype=torch.uint8, device="cuda")
+    # Sequence 1 repeats position T0 for its first 7 steps (a repeated step writes the same row and
+    # gives the same output), so the two sequences sit at different positions afterwards.
+    for i in range(steps):
+        p = np.array([T0 + i, T0 + max(0, i - 7)])
+        pos = torch.tensor(p, dtype=torch.int32, device="cuda")
+        bi = np.arange(B)
+        qt = q[bi, :, p].contiguous()
+        kt = k[bi, :, p].contiguous()
+        vt = v[bi, :, p].contiguous()
+        o, lse = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, scale=scale, workspace=ws)
+        ref_o, ref_l = oracle.decode_ref(qh[bi, :, p], kh, vh, windows, p, T_max, scale)
+        _check_o(o, ref_o)
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL, i
+    torch.cuda.synchronize()
+    _check_cache(kc, vc, kh, vh, windows, [T0 + steps, T0 + steps - 7], T_max)
+
+
+def test_decode_from_empty_and_first_positions():
+    """Positions 0, 1, 2 with nothing prefilled: the ring is filled by the steps themselves."""
+    _require_gpu()
+    B, H, d, T_max = 1, 3, 64, 64
+    windows = [1, 2, 64]
+    (qh, kh, vh), (q, k, v) = _history(B, H, 3, d, seed=11)
+    R = aah.kv_cache_rows(windows, T_max)
+    kc = torch.zeros((B, R, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for t in range(3):
+        pos = torch.tensor([t], dtype=torch.int32, device="cuda")
+        o, lse = aah.attn_decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                                 kc, vc, pos, windows, T_max, scale=0.125)
+        ref_o, ref_l = oracle.decode_ref(qh[:, :, t], kh, vh, windows, np.array([t]), T_max, 0.125)
+        _check_o(o, ref_o)
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL
+    # window 1: the output is the new token's value, bit for bit
+    assert torch.equal(o[:, 0], v[:, 0, 2])
+
+
+def test_decode_1b_layer_shape_sampled():
+    """The 1B-scale layer's shape (B=4, H=32, d=64, T_max=4096, grouped windows) at position 4095
+    after a full prefill; a sample of heads against the oracle, all heads finite."""
+    _require_gpu()
+    import synth
+    wl = synth.make_workload(2)
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    k = torch.from_numpy(wl.bits["k"].view(np.int16)).view(torch.bfloat16).to("cuda")
+    v = torch.from_numpy(wl.bits["v"].view(np.int16)).view(torch.bfloat16).to("cuda")
+    q = torch.from_numpy(wl.bits["q"].view(np.int16)).view(torch.bfloat16).to("cuda")
+    kc, vc = aah.kv_cache_fill(k[:, :, :T - 1].contiguous(), v[:, :, :T - 1].contiguous(), wl.windows, T)
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    o, lse = aah.attn_decode(q[:, :, T - 1].contiguous(), k[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous(),
+                             kc, vc, pos, wl.windows, T, scale=wl.scale)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    for b, h in ((0, 0), (1, 12), (2, 28), (3, 31)):
+        js = oracle.decode_positions(T - 1, int(wl.windows[h]), T)
+        ref_o, ref_l = oracle.decode_ref(wl.q[b:b + 1, h:h + 1, T - 1], wl.k[b:b + 1, h:h + 1], wl.v[b:b + 1, h:h + 1],
+                                         wl.windows[h:h + 1], np.array([T - 1]), T, wl.scale)
+        _check_o(o[b:b + 1, h:h + 1], ref_o)
+        assert abs(lse[b, h].item() - ref_l[0, 0]) < LSE_TOL
+        assert len(js) == min(int(wl.windows[h]), T)
