@@ -40,7 +40,95 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device-to-device copy of a known size (to scale HBM byte counters)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time one decoding step over the trimmed per-head caches of the workload's layer "
+                         "(a separate measurement; prints its own JSON line)")
     return ap.parse_args()
+
+
+def bench_decode(args, wl):
+    """Decoding over per-head trimmed K/V caches: the layer's caches hold positions 0..T-2 (a prefill), and
+    every timed step decodes the token at position T-1 (every ring full; repeating the step rewrites the same
+    row and reads the same bytes).  Bound: HBM.  Algorithmic bytes per step = the K and V rows attended
+    (2 * 2 d bytes each) + q, k_new, v_new read + o written + the new K/V rows written + lse."""
+    import torch
+    import head_causal_local_amd as aah
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    k, v, q = to_dev(wl, "k"), to_dev(wl, "v"), to_dev(wl, "q")
+    kc, vc = aah.kv_cache_fill(k[:, :, :T - 1].contiguous(), v[:, :, :T - 1].contiguous(), wl.windows, T)
+    qt, kt, vt = (x[:, :, T - 1].contiguous() for x in (q, k, v))
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    ws = torch.zeros(aah.decode_workspace_size(wl.windows, B, T, d), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(qt)
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        aah.attn_decode(qt, kt, vt, kc, vc, pos, wl.windows, T, scale=wl.scale, out=o, lse=lse, workspace=ws,
+                        stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Eager: one library call per step from Python (includes the host's per-call cost).
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eager_us = e0.elapsed_time(e1) * 1e3 / args.steps
+    # Graph: the same steps captured once and replayed, as a serving loop would run them; this is
+    # the device's time per step.
+    g = torch.cuda.CUDAGraph()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        with torch.cuda.graph(g, stream=gs):
+            for _ in range(10):
+                aah.attn_decode(qt, kt, vt, kc, vc, pos, wl.windows, T, scale=wl.scale, out=o, lse=lse,
+                                workspace=ws, stream=gs)
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 10)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
+    rows = int(sum(min(int(w), T) for w in wl.windows))            # attended rows per batch entry (every ring full)
+    alg = B * (rows * 2 * 2 * d + 3 * H * 2 * d + H * 2 * d + 2 * H * 2 * d + H * 4)
+    gbs = alg / (us * 1e-6) / 1e9
+    out = {
+        "metric": "decode step: algorithmic HBM bytes per step / device time per step (graph replay; "
+                  "per-head trimmed K/V caches)",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (N(0,1) bf16 Q/K/V, seed 0)",
+        "config": {"workload": wl.name + " decode at position T-1", "B": B, "H": H, "T_max": T, "d": d,
+                   "windows": [int(x) for x in wl.windows], "cache_rows_per_batch_entry": rows,
+                   "step_us": round(us, 3), "eager_step_us": round(eager_us, 3),
+                   "tokens_per_s": round(B / (us * 1e-6), 1),
+                   "algorithmic_bytes_per_step": int(alg)},
+        "roofline": {"kernel": "decode_partial_kernel<64> + decode_combine_kernel<64>", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "avg_launch_us": round(us, 3),
+                     "algorithmic_bytes_per_launch": int(alg)},
+    }
+    print(json.dumps(out))
 
 
 COPY_BYTES = 512 * 1024 * 1024
@@ -142,6 +230,9 @@ def main():
     if wl.dtype != "bf16":
         print("bench.py times bf16 workloads", file=sys.stderr)
         sys.exit(2)
+    if args.decode:
+        bench_decode(args, wl)
+        return
     with_bwd = (wl.do is not None) and not args.fwd_only
     B, H, T, d = wl.B, wl.H, wl.T, wl.d
     q, k, v = to_dev(wl, "q"), to_dev(wl, "k"), to_dev(wl, "v")

@@ -224,8 +224,8 @@ def attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, scale
     _check_operand("out", out, q)
     if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
-    if workspace is None:
-        workspace = torch.empty(max(decode_workspace_size(w, B, T_max, d), 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:   # zeroed: its first B*H int32 are the kernels' merge counters
+        workspace = torch.zeros(max(decode_workspace_size(w, B, T_max, d), 1), dtype=torch.uint8, device=q.device)
     ptr, nbytes = _ws(workspace)
     check(lib().aah_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(),
                                 vcache.data_ptr(), pos.data_ptr(), _wptr(w), B, H, int(T_max), d, _dtype_code(q),

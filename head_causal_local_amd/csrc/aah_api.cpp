@@ -262,8 +262,11 @@ aah_status get_decode_plan(const int32_t* windows, int H, int T_max, const Decod
   return AAH_OK;
 }
 
+// Decode workspace: B*H int32 merge counters (256-byte rounded), then the partials.
+size_t decode_counter_bytes(int B, int H) { return round_up(static_cast<size_t>(B) * H * sizeof(int32_t), 256); }
 size_t decode_workspace(const int32_t* windows, int B, int H, int T_max, int d) {
-  return round_up(static_cast<size_t>(B) * decode_chunks(windows, H, T_max) * (2 + d) * sizeof(float), 256);
+  return decode_counter_bytes(B, H) +
+         round_up(static_cast<size_t>(B) * decode_chunks(windows, H, T_max) * (2 + d) * sizeof(float), 256);
 }
 
 // Checks shared by the decode entry points (bf16 only; T_max plays the role of T).
@@ -512,9 +515,11 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   const DecodePlan* plan = nullptr;
   AAH_TRY(get_decode_plan(windows, H, T_max, &plan));
-  const hipError_t e = aah::launch_decode_bf16(q, k_new, v_new, kcache, vcache, pos, plan->view(), B, H, T_max, d,
-                                               scale, o, lse, static_cast<float*>(workspace),
-                                               static_cast<hipStream_t>(stream));
+  const hipError_t e = aah::launch_decode_bf16(
+      q, k_new, v_new, kcache, vcache, pos, plan->view(), B, H, T_max, d, scale, o, lse,
+      static_cast<int32_t*>(workspace),
+      reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, H)),
+      static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return AAH_OK;
 }

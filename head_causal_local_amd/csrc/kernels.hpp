@@ -87,11 +87,13 @@ struct DecodePlanView {
 };
 
 // Writes k_new / v_new [B,H,d] into the ring row of position pos[b] (device
-// int32[B], clamped to [0, T_max)) and o [B,H,d] / lse [B,H] of that token;
-// partials: B * n_chunks * (2 + d) floats.
+// int32[B], clamped to [0, T_max)) and o [B,H,d] / lse [B,H] of that token.
+// counters: int32[B*H], zero on entry and left zero; partials: B * n_chunks *
+// (2 + d) floats.
 hipError_t launch_decode_bf16(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
                               const int32_t* pos, const DecodePlanView& plan, int B, int H, int T_max, int d,
-                              float scale, void* o, float* lse, float* partials, hipStream_t stream);
+                              float scale, void* o, float* lse, int32_t* counters, float* partials,
+                              hipStream_t stream);
 
 // Copies the positions each ring keeps (the last min(C_h, T)) of a prefill k, v [B,H,T,d].
 hipError_t launch_cache_fill_bf16(const void* k, const void* v, void* kcache, void* vcache,

@@ -157,8 +157,9 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
 /* R = sum_h min(windows[h], T_max) rows per batch entry; -1 for invalid arguments. */
 int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max);
 
-/* Workspace bytes aah_attn_decode needs (B * chunks * (2 + d) floats, chunks =
- * sum_h ceil(C_h / 256)); 0 for invalid arguments. */
+/* Workspace bytes aah_attn_decode needs: B*H int32 merge counters (rounded up
+ * to 256 bytes), then B * chunks * (2 + d) floats of partial results, chunks =
+ * sum_h ceil(C_h / 256); 0 for invalid arguments. */
 size_t aah_attn_decode_workspace_size(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt);
 
 /*
@@ -177,7 +178,10 @@ aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* window
  * Writes k_new / v_new into the row of position pos[b] and o [B,H,d] (dtype
  * dt), lse [B,H] (fp32, natural log of sum_j exp(scale q . k_j) over the
  * attended positions).  Workspace: at least aah_attn_decode_workspace_size
- * bytes, 256-byte aligned; contents on entry do not matter.
+ * bytes, 256-byte aligned.  Its first B*H int32 (the merge counters) must be
+ * zero before the first call that uses it; every call leaves them zero again,
+ * the rest of it carries nothing between calls.  Calls that share a
+ * workspace must not run concurrently.
  */
 aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
                            const int32_t* pos, const int32_t* windows, int B, int H, int T_max, int d,

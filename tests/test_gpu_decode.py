@@ -63,7 +63,7 @@ def test_prefill_then_decode_steps(d, windows, T_max, T0):
     scale = 1.0 / np.sqrt(d)
     kc, vc = aah.kv_cache_fill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), windows, T_max)
     _check_cache(kc, vc, kh, vh, windows, [T0, T0], T_max)
-    ws = torch.empty(aah.decode_workspace_size(windows, B, T_max, d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d), dtype=torch.uint8, device="cuda")
     # Sequence 1 repeats position T0 for its first 7 steps (a repeated step writes the same row and
     # gives the same output), so the two sequences sit at different positions afterwards.
     for i in range(steps):
@@ -123,3 +123,39 @@ def test_decode_1b_layer_shape_sampled():
         _check_o(o[b:b + 1, h:h + 1], ref_o)
         assert abs(lse[b, h].item() - ref_l[0, 0]) < LSE_TOL
         assert len(js) == min(int(wl.windows[h]), T)
+
+
+def test_decode_graph_replays_match_eager():
+    """The step has no allocation or memset, so it can be captured in a HIP graph: every replay
+    (with eager work and synchronisations in between) gives the eager result bit for bit."""
+    _require_gpu()
+    B, H, d, T_max = 2, 4, 64, 512
+    windows = [16, 300, 512, 1000]
+    (qh, kh, vh), (q, k, v) = _history(B, H, T_max, d, seed=21)
+    p = T_max - 1
+    kc, vc = aah.kv_cache_fill(k[:, :, :p].contiguous(), v[:, :, :p].contiguous(), windows, T_max)
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    qt, kt, vt = (x[:, :, p].contiguous() for x in (q, k, v))
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d), dtype=torch.uint8, device="cuda")
+    o_eager, l_eager = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, workspace=ws)
+    o_eager, l_eager = o_eager.clone(), l_eager.clone()
+    o = torch.empty_like(o_eager)
+    lse = torch.empty_like(l_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, out=o, lse=lse, workspace=ws, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    for r in range(4):
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager) and torch.equal(lse, l_eager), r
+        # eager work on the same workspace between replays
+        aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, workspace=ws)
+    ref_o, ref_l = oracle.decode_ref(qh[:, :, p], kh, vh, windows, np.array([p, p]), T_max, 1.0 / np.sqrt(d))
+    _check_o(o, ref_o)
