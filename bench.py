@@ -123,9 +123,10 @@ def bench_decode(args, wl):
                    "step_us": round(us, 3), "eager_step_us": round(eager_us, 3),
                    "tokens_per_s": round(B / (us * 1e-6), 1),
                    "algorithmic_bytes_per_step": int(alg)},
-        "roofline": {"kernel": "decode_partial_kernel<64> + decode_combine_kernel<64>", "bound": "hbm",
+        "roofline": {"kernel": "decode_kernel<64>", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None, "avg_launch_us": round(us, 3),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_kernel<64>"),
+                     "avg_launch_us": round(us, 3),
                      "algorithmic_bytes_per_launch": int(alg)},
     }
     print(json.dumps(out))
@@ -150,6 +151,7 @@ KERNEL_SOURCES = {
     "fwd_bf16_kernel<64>": "head_causal_local_amd/csrc/fwd_bf16.hip",
     "bwd_dkdv_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
     "bwd_dq_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "decode_kernel<64>": "head_causal_local_amd/csrc/decode.hip",
 }
 
 
