@@ -18,6 +18,12 @@ Transformer Attention" (AAH).
     min(t, W); ACR is the rectangular proxy sum_h T * T_k / (H T^2).
   * Table 6 caption: inference ACR reconstructed as sum_W f_W * W / T.
 
+Sink tokens ("Autonomy-of-Heads: Data-Free Sparse Attention from Frozen Query-Key
+Geometry", section 5, Deploying LLMs With AoH, and section 6.1): a streaming head
+attends to the first s_sink tokens and to its recent window.  With a sink size S
+per head, key t_k is allowed for query t_q iff t_k <= t_q and (t_k >= t_q - W + 1
+or t_k < S); S = 0 is the plain local window.
+
 Readings where the pages are silent (each listed in the design notes):
   * the additive mask value is -inf, so masked weights are exactly zero;
   * the log-sum-exp is the natural log of sum_j exp(scaled score) over the
@@ -32,26 +38,33 @@ from __future__ import annotations
 import numpy as np
 
 
-def window_allowed(T: int, w: int) -> np.ndarray:
+def window_allowed(T: int, w: int, sink: int = 0) -> np.ndarray:
     """Boolean [T, T] matrix; entry (i, j) is True when key j is in query i's window.
 
-    AAH section 5.8: t_q - W + 1 <= t_k <= t_q, with W clamped to T."""
+    AAH section 5.8: t_q - W + 1 <= t_k <= t_q, with W clamped to T; with a sink
+    size S (AoH section 5), keys t_k < S are allowed too (still t_k <= t_q)."""
     if w < 1:
         raise ValueError("window must be >= 1")
+    if sink < 0:
+        raise ValueError("sink must be >= 0")
     w = min(int(w), T)
     i = np.arange(T)[:, None]
     j = np.arange(T)[None, :]
-    return (j <= i) & (j >= i - w + 1)
+    return (j <= i) & ((j >= i - w + 1) | (j < sink))
 
 
-def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None):
+def _sink(sinks, h) -> int:
+    return 0 if sinks is None else int(sinks[h])
+
+
+def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None, sink: int = 0):
     """Scores, mask and softmax of one head (AAH section 5.8).
 
     Returns (P, m, l) where P[r, j] is the attention weight of query row r on
     key j, m the row max of the scaled masked scores and l the row sum of
     exp(score - m)."""
     T = k.shape[0]
-    allowed = window_allowed(T, w)
+    allowed = window_allowed(T, w, sink)
     if rows is not None:
         allowed = allowed[rows]
         q = q[rows]
@@ -63,10 +76,10 @@ def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None):
     return E / l, m[:, 0], l[:, 0]
 
 
-def attn_fwd_ref(q, k, v, windows, scale):
-    """Forward pass for Q/K/V laid out [B, H, T, d] with one window per head.
+def attn_fwd_ref(q, k, v, windows, scale, sinks=None):
+    """Forward pass for Q/K/V laid out [B, H, T, d] with one window (and sink size) per head.
 
-    Returns (O [B,H,T,d], LSE [B,H,T]) in float64.  AAH section 5.8."""
+    Returns (O [B,H,T,d], LSE [B,H,T]) in float64.  AAH section 5.8; AoH section 5 for sinks."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -75,13 +88,13 @@ def attn_fwd_ref(q, k, v, windows, scale):
     LSE = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            P, m, l = _head_probs(q[b, h], k[b, h], int(windows[h]), scale)
+            P, m, l = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
             O[b, h] = P @ v[b, h]
             LSE[b, h] = m + np.log(l)
     return O, LSE
 
 
-def attn_fwd_rows_ref(q_h, k_h, v_h, w, scale, rows):
+def attn_fwd_rows_ref(q_h, k_h, v_h, w, scale, rows, sink: int = 0):
     """Forward pass of selected query rows of ONE head (arrays [T, d]).
 
     Same definition as attn_fwd_ref restricted to the given rows, so that large
@@ -89,11 +102,11 @@ def attn_fwd_rows_ref(q_h, k_h, v_h, w, scale, rows):
     q_h = np.asarray(q_h, dtype=np.float64)
     k_h = np.asarray(k_h, dtype=np.float64)
     v_h = np.asarray(v_h, dtype=np.float64)
-    P, m, l = _head_probs(q_h, k_h, int(w), scale, rows=np.asarray(rows))
+    P, m, l = _head_probs(q_h, k_h, int(w), scale, rows=np.asarray(rows), sink=int(sink))
     return P @ v_h, m + np.log(l)
 
 
-def attn_bwd_ref(q, k, v, windows, scale, do):
+def attn_bwd_ref(q, k, v, windows, scale, do, sinks=None):
     """Gradients (dQ, dK, dV) of sum(O * dO) by matrix calculus of section 5.8.
 
     With P the masked row softmax of S = scale Q K^T and O = P V:
@@ -110,7 +123,7 @@ def attn_bwd_ref(q, k, v, windows, scale, do):
     dv = np.empty_like(v)
     for b in range(B):
         for h in range(H):
-            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale)
+            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
             dv[b, h] = P.T @ do[b, h]
             dP = do[b, h] @ v[b, h].T
             D = (P * dP).sum(axis=1, keepdims=True)
@@ -120,12 +133,14 @@ def attn_bwd_ref(q, k, v, windows, scale, do):
     return dq, dk, dv
 
 
-def pair_count_ref(T: int, w: int) -> int:
-    """Exact allowed query-key pairs of one head: sum_{t=1}^{T} min(t, W).
+def pair_count_ref(T: int, w: int, sink: int = 0) -> int:
+    """Exact allowed query-key pairs of one head: sum_{t=1}^{T} min(t, W), plus the sink
+    keys row t sees before its window (keys 0 .. t - W - 1): sum_t max(0, min(S, t - W)).
 
-    AAH section 5.10 (with W clamped to T, section 5.8)."""
+    AAH section 5.10 (with W clamped to T, section 5.8); AoH section 5 for sinks."""
     W = min(int(w), T)
-    return int(sum(min(t, W) for t in range(1, T + 1)))
+    S = int(sink)
+    return int(sum(min(t, W) + max(0, min(S, t - W)) for t in range(1, T + 1)))
 
 
 def acr_ref(windows, T: int) -> float:
