@@ -6,8 +6,9 @@ held to 1e-2 by rounding alone, since its spacing there is 2^-7 |O| or more);
 gradients 3e-2 x max |gradient|.  The log-sum-exp of the bf16 path is the log
 of the sum of the bf16-rounded weights that also enter P V (round to nearest
 keeps 8 significant bits, so each weight carries a relative error of at most
-2^-9 and so does their sum): |error| <= -ln(1 - 2^-9) = 1.96e-3, plus fp32
-accumulation and exp2 rounding well below 1e-4, hence 2.5e-3.  The fp32 path
+the unit roundoff 2^-8, and so does their sum): |error| <= -ln(1 - 2^-8) =
+3.92e-3, reached only when one or two weights dominate a row, plus fp32
+accumulation and exp2 rounding well below 1e-4, hence 4e-3.  The fp32 path
 sums fp32 weights: 1e-5.
 """
 import numpy as np
@@ -21,7 +22,7 @@ import synth
 pytestmark = pytest.mark.gpu
 
 O_TOL_BF16 = 1e-2
-LSE_TOL_BF16 = 2.5e-3
+LSE_TOL_BF16 = 4e-3
 TOL_F32 = 1e-5
 GRAD_REL = 3e-2
 
