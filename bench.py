@@ -11,7 +11,12 @@ from {512, 1024, 2048, 4096} with P = (.5, .25, .125, .125); seed 0).
 Effective FLOPs count in-window query/key pairs only: 4*d per pair forward
 (Q K^T and P V) and 10*d per pair backward (Q K^T, dO V^T, P^T dO, dS K,
 dS^T Q); the backward kernels recompute Q K^T and dO V^T once more for dQ, which
-is not counted.  Pairs per head = sum_{t=1}^{T} min(t, W_h).
+is not counted.  Pairs per head = sum_{t=1}^{T} min(t, W_h) (plus, for heads
+with sink tokens, the sinks each row sees before its window).
+
+--workload 5 times the same step on the streaming-head layer (heads 0-15 full
+causal, heads 16-31 sink 128 + recent window 256; "Autonomy-of-Heads" section
+5 and 6.1).
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -148,9 +153,12 @@ def calibrate_copy(steps):
 
 
 KERNEL_SOURCES = {
-    "fwd_bf16_kernel<64>": "head_causal_local_amd/csrc/fwd_bf16.hip",
-    "bwd_dkdv_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
-    "bwd_dq_kernel<64>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "fwd_bf16_kernel<64, false>": "head_causal_local_amd/csrc/fwd_bf16.hip",
+    "bwd_dkdv_kernel<64, false>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "bwd_dq_kernel<64, false>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "fwd_bf16_kernel<64, true>": "head_causal_local_amd/csrc/fwd_bf16.hip",
+    "bwd_dkdv_kernel<64, true>": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "bwd_dq_kernel<64, true>": "head_causal_local_amd/csrc/bwd_bf16.hip",
     "decode_kernel<64>": "head_causal_local_amd/csrc/decode.hip",
 }
 
@@ -166,7 +174,11 @@ def measured_traffic(kernel):
     sha = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()[:16]
     for line in open(path):
         parts = line.split()
-        if len(parts) == 4 and not line.startswith("#") and parts[0] == kernel and parts[1] == sha:
+        if line.startswith("#"):
+            continue
+        # <kernel name (may hold spaces)> <source sha16> <fetch bytes> <write bytes>
+        parts = line.rsplit(None, 3)
+        if len(parts) == 4 and parts[0] == kernel and parts[1] == sha:
             return int(parts[2]) + int(parts[3])
     return None
 
@@ -194,13 +206,15 @@ def cpu_baseline(wl, n_heads, with_bwd):
     order += [h for h in range(wl.H) if h not in order]
     heads = order[:n_heads]
     import head_causal_local_amd as aah
-    pairs, _ = aah.window_stats(wl.windows[heads], wl.T)
+    sinks = None if wl.sinks is None else wl.sinks[heads]
+    pairs, _ = aah.window_stats(wl.windows[heads], wl.T, sinks=sinks)
     t0 = time.perf_counter()
     for h in heads:
         sl = (slice(0, 1), slice(h, h + 1))
-        oracle.attn_fwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale)
+        sk = None if wl.sinks is None else wl.sinks[h:h + 1]
+        oracle.attn_fwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, sinks=sk)
         if with_bwd:
-            oracle.attn_bwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, wl.do[sl])
+            oracle.attn_bwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, wl.do[sl], sinks=sk)
     dt = time.perf_counter() - t0
     flops = (4 + (10 if with_bwd else 0)) * wl.d * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
@@ -252,12 +266,12 @@ def main():
             if ev is not None:
                 ev[i].record(stream)
         mark(0)
-        aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream)
+        aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream, sinks=wl.sinks)
         mark(1)
         if with_bwd:
-            aah.attn_bwd_dq(q, k, v, o, do, lse, wl.windows, dq, ws, wl.scale, stream=stream)
+            aah.attn_bwd_dq(q, k, v, o, do, lse, wl.windows, dq, ws, wl.scale, stream=stream, sinks=wl.sinks)
             mark(2)
-            aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws, wl.scale, stream=stream)
+            aah.attn_bwd_dkdv(q, k, v, do, wl.windows, dk, dv, ws, wl.scale, stream=stream, sinks=wl.sinks)
             mark(3)
 
     for _ in range(args.warmup):
@@ -281,7 +295,7 @@ def main():
     bwd_ms = span(1, 3) if with_bwd else np.zeros(1)
     ms_per_step = wall * 1e3 / args.steps
 
-    pairs_b, acr = aah.window_stats(wl.windows, T)
+    pairs_b, acr = aah.window_stats(wl.windows, T, sinks=wl.sinks)
     pairs = B * pairs_b
     f_fwd = 4 * d * pairs
     f_bwd = 10 * d * pairs if with_bwd else 0
@@ -292,10 +306,12 @@ def main():
     # Roofline of the kernel that dominates the step (each step is one launch on `stream`).
     # Algorithmic FLOPs per in-window pair: forward 4 d (Q K^T, P V); dK/dV kernel 8 d
     # (Q K^T, dO V^T, dO^T P, Q^T dS); dQ kernel 6 d (K Q^T, V dO^T, K^T dS^T).
-    kernels = [("fwd_bf16_kernel<64>", float(fwd_ms.mean()), f_fwd)]
+    # Heads with sinks run the kernels' SINK instantiations.
+    tag = f"<{d}, {'true' if wl.sinks is not None and int(np.max(wl.sinks)) > 0 else 'false'}>"
+    kernels = [("fwd_bf16_kernel" + tag, float(fwd_ms.mean()), f_fwd)]
     if with_bwd:
-        kernels += [("bwd_dkdv_kernel<64>", float(dkdv_ms.mean()), 8 * d * pairs),
-                    ("bwd_dq_kernel<64>", float(dq_ms.mean()), 6 * d * pairs)]
+        kernels += [("bwd_dkdv_kernel" + tag, float(dkdv_ms.mean()), 8 * d * pairs),
+                    ("bwd_dq_kernel" + tag, float(dq_ms.mean()), 6 * d * pairs)]
     kname, kms, kflops = max(kernels, key=lambda x: x[1])
     achieved = kflops / (kms * 1e-3) / 1e12
     roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -319,6 +335,7 @@ def main():
             "workload": wl.name + (" fwd+bwd" if with_bwd else " fwd"),
             "B": B, "H": H, "T": T, "d": d,
             "windows": [int(x) for x in wl.windows],
+            **({"sinks": [int(x) for x in wl.sinks]} if wl.sinks is not None else {}),
             "in_window_pairs": int(pairs),
             "acr": round(acr, 4),
             "fwd_ms": round(float(fwd_ms.mean()), 4),

@@ -2,7 +2,9 @@
 
 The execution branch of Asymmetric Attention Heads (AAH-v3): every head h
 attends only to keys j with i - w_h < j <= i of its own causal local window
-("Asymmetric Attention Heads", section 5.8).  All arithmetic runs in the HIP
+("Asymmetric Attention Heads", section 5.8).  Optionally a head also keeps its
+first s_h keys visible to every later query (sink tokens plus a recent window,
+"Autonomy-of-Heads", section 5): pass `sinks`, one int per head.  All arithmetic runs in the HIP
 kernels of libaah_attn.so behind the C ABI of include/aah_attn.h; this module
 only marshals arguments.  PyTorch provides device memory and the stream.
 """
@@ -34,6 +36,20 @@ def _wptr(w: np.ndarray):
     return w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
+def _sinks_arg(sinks, H: int):
+    """int32 array of sink sizes (or None when there are none)."""
+    if sinks is None:
+        return None
+    s = _windows_arg(sinks)
+    if s.shape[0] != H:
+        raise ValueError(f"sinks has {s.shape[0]} entries, expected H = {H}")
+    return s
+
+
+def _sptr(s):
+    return None if s is None else _wptr(s)
+
+
 def _dtype_code(t) -> int:
     import torch
     if t.dtype == torch.bfloat16:
@@ -58,11 +74,13 @@ def _check_operand(name, t, ref):
         raise ValueError(f"{name} must be contiguous [B, H, T, d]")
 
 
-def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None):
+def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None, sinks=None):
     """O, LSE = local-window attention of q, k, v ([B, H, T, d] device tensors).
 
-    windows: one int per head (>= 1; values above T act as T).  scale defaults
-    to 1/sqrt(d).  Returns (O with q's dtype, LSE float32 [B, H, T])."""
+    windows: one int per head (>= 1; values above T act as T).  sinks: None or
+    one int per head (>= 0), the number of leading keys every later query also
+    sees.  scale defaults to 1/sqrt(d).  Returns (O with q's dtype, LSE float32
+    [B, H, T])."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
@@ -82,8 +100,10 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
-    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), B, H, T, d, _dtype_code(q),
-                            float(scale), out.data_ptr(), lse.data_ptr(), None, 0, _stream_ptr(q, stream))
+    sk = _sinks_arg(sinks, H)
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d,
+                            _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(), None, 0,
+                            _stream_ptr(q, stream))
     check(st)
     return out, lse
 
@@ -94,7 +114,7 @@ def workspace_size(B: int, H: int, T: int, d: int, dtype: str = "bf16", is_bwd: 
 
 
 def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=None, dk=None, dv=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, sinks=None):
     """dQ, dK, dV of sum(O * do) for local-window attention (see attn_fwd)."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
@@ -116,8 +136,10 @@ def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=Non
     need = int(lib().aah_attn_workspace_size(B, H, T, d, code, 1))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    sk = _sinks_arg(sinks, H)
     st = lib().aah_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                            _wptr(w), B, H, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            _wptr(w), _sptr(sk), B, H, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(),
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream_ptr(q, stream))
     check(st)
@@ -139,27 +161,31 @@ def _bwd_args(q, k, v, do, windows, scale):
     return B, H, T, d, w, float(scale)
 
 
-def attn_bwd_dq(q, k, v, o, do, lse, windows, dq, workspace, scale: Optional[float] = None, stream=None):
+def attn_bwd_dq(q, k, v, o, do, lse, windows, dq, workspace, scale: Optional[float] = None, stream=None,
+                sinks=None):
     """Backward step 1: dQ, and the per-row -lse * log2(e) and -rowsum(do * o) into the workspace."""
     import torch
     B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
+    sk = _sinks_arg(sinks, H)
     _check_operand("o", o, q)
     _check_operand("dq", dq, q)
     if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     ptr, nbytes = _ws(workspace)
     check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                lse.data_ptr(), _wptr(w), B, H, T, d, _dtype_code(q), scale, dq.data_ptr(), ptr,
-                                nbytes, _stream_ptr(q, stream)))
+                                lse.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d, _dtype_code(q), scale,
+                                dq.data_ptr(), ptr, nbytes, _stream_ptr(q, stream)))
 
 
-def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None):
+def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None,
+                  sinks=None):
     """Backward step 2: dK and dV (reads the workspace rows attn_bwd_dq wrote; run it after that step)."""
     B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
+    sk = _sinks_arg(sinks, H)
     _check_operand("dk", dk, q)
     _check_operand("dv", dv, q)
     ptr, nbytes = _ws(workspace)
-    check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w),
+    check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w), _sptr(sk),
                                   B, H, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
 
@@ -241,34 +267,38 @@ def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:
     return r.value, c.value
 
 
-def _plan(fn, windows, B, H, T, q_tile, kv_tile, n_queues) -> np.ndarray:
+def _plan(fn, windows, sinks, B, H, T, q_tile, kv_tile, n_queues) -> np.ndarray:
     w = _windows_arg(windows)
+    sk = None if sinks is None else _windows_arg(sinks)
     n = ctypes.c_int64()
-    st = fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, None, 0, ctypes.byref(n))
+    st = fn(_wptr(w), _sptr(sk), B, H, T, q_tile, kv_tile, n_queues, None, 0, ctypes.byref(n))
     if st not in (0, 1):
         check(st)
     buf = (WorkItem * max(n.value, 1))()
-    check(fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, buf, n.value, ctypes.byref(n)))
+    check(fn(_wptr(w), _sptr(sk), B, H, T, q_tile, kv_tile, n_queues, buf, n.value, ctypes.byref(n)))
     arr = np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[: n.value].copy()
     return arr
 
 
-def plan_fwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8):
+def plan_fwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8,
+             sinks: Optional[Sequence[int]] = None):
     """Forward work list as an int32 array [n, 4] of (bh, q_tile_index, kv_lo, kv_hi)."""
-    return _plan(lib().aah_plan_fwd, windows, B, H, T, q_tile, kv_tile, n_queues)
+    return _plan(lib().aah_plan_fwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
 
 
-def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8):
+def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8,
+             sinks: Optional[Sequence[int]] = None):
     """Backward work list as an int32 array [n, 4] of (bh, kv_tile_index, q_lo, q_hi)."""
-    return _plan(lib().aah_plan_bwd, windows, B, H, T, q_tile, kv_tile, n_queues)
+    return _plan(lib().aah_plan_bwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
 
 
-def window_stats(windows: Sequence[int], T: int) -> Tuple[int, float]:
-    """(exact in-window pairs per batch entry, ACR) of a window vector."""
+def window_stats(windows: Sequence[int], T: int, sinks: Optional[Sequence[int]] = None) -> Tuple[int, float]:
+    """(exact visible query/key pairs per batch entry, ACR) of a window vector (and sink sizes)."""
     w = _windows_arg(windows)
+    sk = _sinks_arg(sinks, w.shape[0])
     pairs = ctypes.c_int64()
     acr = ctypes.c_double()
-    check(lib().aah_window_stats(_wptr(w), w.shape[0], T, ctypes.byref(pairs), ctypes.byref(acr)))
+    check(lib().aah_window_stats(_wptr(w), _sptr(sk), w.shape[0], T, ctypes.byref(pairs), ctypes.byref(acr)))
     return pairs.value, acr.value
 
 

@@ -53,13 +53,21 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 aah_status check_dims(int B, int H, int T, int d, aah_dtype dt);
 
-// Shape checks shared by every entry point that takes windows.
-aah_status check_shape(const int32_t* windows, int B, int H, int T, int d, aah_dtype dt) {
+aah_status check_windows(const int32_t* windows, const int32_t* sinks, int H) {
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
-  AAH_TRY_INNER(check_dims(B, H, T, d, dt));
   for (int h = 0; h < H; ++h)
     if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  if (sinks != nullptr)
+    for (int h = 0; h < H; ++h)
+      if (sinks[h] < 0) return fail(AAH_ERR_INVALID_ARG, "sinks[%d] = %d; every sink size must be >= 0", h, sinks[h]);
   return AAH_OK;
+}
+
+// Shape checks shared by every entry point that takes windows (and sink sizes, may be NULL).
+aah_status check_shape(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt) {
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  AAH_TRY_INNER(check_dims(B, H, T, d, dt));
+  return check_windows(windows, sinks, H);
 }
 
 aah_status check_dims(int B, int H, int T, int d, aah_dtype dt) {
@@ -93,7 +101,8 @@ aah_status check_tensor(const void* p, const char* name, size_t align) {
 struct DevicePlan {
   WorkItem* items = nullptr;
   int n_items = 0;
-  int32_t* win = nullptr;  // effective windows, int32[H]
+  int32_t* win = nullptr;   // effective windows int32[H], then effective sink sizes int32[H]
+  const int32_t* sink = nullptr;  // win + H if some head has a sink, else NULL (the kernels without sinks)
 };
 
 enum PlanKind : int64_t { kPlanFwd = 0, kPlanBwd = 1 };
@@ -103,14 +112,22 @@ std::map<std::vector<int64_t>, DevicePlan> g_cache;
 
 constexpr int kQueues = 8;  // MI355X has eight XCDs; workgroups are placed round-robin over them
 
-aah_status get_plan(PlanKind kind, const int32_t* windows, int B, int H, int T, int row_tile, int col_tile,
-                    DevicePlan* out) {
+aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int row_tile,
+                    int col_tile, DevicePlan* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::vector<int64_t> key = {kind, dev, B, H, T, row_tile, col_tile, kQueues};
-  key.reserve(key.size() + H);
-  for (int h = 0; h < H; ++h) key.push_back(aah::effective_window(windows[h], T));
+  std::vector<int32_t> win(2 * H);
+  bool any_sink = false;
+  for (int h = 0; h < H; ++h) {
+    win[h] = aah::effective_window(windows[h], T);
+    win[H + h] = sinks == nullptr ? 0 : aah::effective_sink(sinks[h], windows[h], T);
+    any_sink = any_sink || win[H + h] > 0;
+  }
+  // Heads whose sinks change nothing plan (and run) exactly as without sinks.
+  const int32_t* sink_arg = any_sink ? win.data() + H : nullptr;
+  std::vector<int64_t> key = {kind, dev, B, H, T, row_tile, col_tile, kQueues, any_sink ? 1 : 0};
+  key.insert(key.end(), win.begin(), win.end());
 
   std::lock_guard<std::mutex> lock(g_mu);
   auto found = g_cache.find(key);
@@ -121,10 +138,8 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, int B, int H, int T, 
   // Forward: row tile = query rows per item, col tile = keys per step.
   // Backward: row tile = keys per item, col tile = query rows per step.
   const std::vector<WorkItem> items =
-      kind == kPlanFwd ? aah::plan_forward(windows, B, H, T, row_tile, col_tile, kQueues)
-                       : aah::plan_backward(windows, B, H, T, col_tile, row_tile, kQueues);
-  std::vector<int32_t> win(H);
-  for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
+      kind == kPlanFwd ? aah::plan_forward(windows, sink_arg, B, H, T, row_tile, col_tile, kQueues)
+                       : aah::plan_backward(windows, sink_arg, B, H, T, col_tile, row_tile, kQueues);
 
   DevicePlan p;
   p.n_items = static_cast<int>(items.size());
@@ -142,6 +157,7 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, int B, int H, int T, 
     (void)hipFree(p.win);
     return hip_fail(e, "hipMemcpy(work list)");
   }
+  p.sink = any_sink ? p.win + H : nullptr;
   g_cache.emplace(std::move(key), p);
   *out = p;
   return AAH_OK;
@@ -271,7 +287,7 @@ size_t decode_workspace(const int32_t* windows, int B, int H, int T_max, int d) 
 
 // Checks shared by the decode entry points (bf16 only; T_max plays the role of T).
 aah_status check_decode(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt) {
-  AAH_TRY_INNER(check_shape(windows, B, H, T_max, d, dt));
+  AAH_TRY_INNER(check_shape(windows, nullptr, B, H, T_max, d, dt));
   if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
   if (decode_rows(windows, H, T_max) < 0) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
   // The decode and cache-fill launches put B (and B * H) on the second grid dimension.
@@ -281,17 +297,17 @@ aah_status check_decode(const int32_t* windows, int B, int H, int T_max, int d, 
   return AAH_OK;
 }
 
-aah_status plan_to_host(PlanKind kind, const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile,
-                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
+aah_status plan_to_host(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+                        int q_tile, int kv_tile, int n_queues, aah_work_item* items, int64_t capacity,
+                        int64_t* n_items) {
   if (n_items == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items is NULL");
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
   if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
   if (q_tile < 1 || kv_tile < 1 || n_queues < 1) return fail(AAH_ERR_INVALID_ARG, "tiles and n_queues must be >= 1");
-  for (int h = 0; h < H; ++h)
-    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
+  AAH_TRY_INNER(check_windows(windows, sinks, H));
   const std::vector<WorkItem> v = kind == kPlanFwd
-                                      ? aah::plan_forward(windows, B, H, T, q_tile, kv_tile, n_queues)
-                                      : aah::plan_backward(windows, B, H, T, q_tile, kv_tile, n_queues);
+                                      ? aah::plan_forward(windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
+                                      : aah::plan_backward(windows, sinks, B, H, T, q_tile, kv_tile, n_queues);
   *n_items = static_cast<int64_t>(v.size());
   if (capacity < static_cast<int64_t>(v.size()))
     return fail(AAH_ERR_INVALID_ARG, "capacity %lld < %zu items", static_cast<long long>(capacity), v.size());
@@ -336,13 +352,13 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
   return AAH_OK;
 }
 
-aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, int B, int H, int T,
-                        int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
+aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks,
+                        int B, int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
                         size_t workspace_bytes, aah_stream_t stream) {
   (void)workspace;
   (void)workspace_bytes;
   g_detail.clear();
-  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -353,25 +369,25 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, T, row, col, &plan));
   const aah::AttnShape s{B, H, T, d, scale};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_fwd_bf16(q, k, v, o, lse, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_fwd_bf16(q, k, v, o, lse, plan.items, plan.n_items, plan.win, plan.sink, s, st);
   else
     e = aah::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                             static_cast<const float*>(v), static_cast<float*>(o), lse, plan.items, plan.n_items,
-                            plan.win, s, st);
+                            plan.win, plan.sink, s, st);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return AAH_OK;
 }
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const int32_t* windows,
-                             int B, int H, int T, int d, aah_dtype dt, float scale, void* dk, void* dv,
-                             const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* dk,
+                             void* dv, const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -387,24 +403,26 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanBwd, windows, B, H, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nl2, nd, dk, dv, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nl2, nd, dk, dv, plan.items, plan.n_items, plan.win, plan.sink, s,
+                                  st);
   else
     e = aah::launch_bwd_dkdv_simple(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
                                     static_cast<float*>(dk), static_cast<float*>(dv), plan.items, plan.n_items,
-                                    plan.win, s, st);
+                                    plan.win, plan.sink, s, st);
   if (e != hipSuccess) return hip_fail(e, "dK/dV launch");
   return AAH_OK;
 }
 
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
-                           float scale, void* dq, void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
+                           aah_dtype dt, float scale, void* dq, void* workspace, size_t workspace_bytes,
+                           aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -421,29 +439,30 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, B, H, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16) {
     // One kernel: D and the workspace rows come out of the dQ kernel's prologue.
-    e = aah::launch_bwd_dq_bf16(q, k, v, o, dout, lse, nl2, nd, dq, plan.items, plan.n_items, plan.win, s, st);
+    e = aah::launch_bwd_dq_bf16(q, k, v, o, dout, lse, nl2, nd, dq, plan.items, plan.n_items, plan.win, plan.sink,
+                                s, st);
   } else {
     e = aah::launch_bwd_preprocess(o, dout, lse, false, nl2, nd, s, st);
     if (e == hipSuccess)
       e = aah::launch_bwd_dq_simple(static_cast<const float*>(q), static_cast<const float*>(k),
                                     static_cast<const float*>(v), static_cast<const float*>(dout), nl2, nd,
-                                    static_cast<float*>(dq), plan.items, plan.n_items, plan.win, s, st);
+                                    static_cast<float*>(dq), plan.items, plan.n_items, plan.win, plan.sink, s, st);
   }
   if (e != hipSuccess) return hip_fail(e, "dQ launch");
   return AAH_OK;
 }
 
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
-                        float scale, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
-                        aah_stream_t stream) {
+                        const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
+                        aah_dtype dt, float scale, void* dq, void* dk, void* dv, void* workspace,
+                        size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   // Validate everything up front so that no step runs unless all of them can.
-  AAH_TRY(check_shape(windows, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -455,9 +474,9 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dv, "dv", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, B, H, T, d, dt, scale, dq, workspace, workspace_bytes,
-                          stream));
-  return aah_attn_bwd_dkdv(q, k, v, dout, windows, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
+  AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, T, d, dt, scale, dq, workspace,
+                          workspace_bytes, stream));
+  return aah_attn_bwd_dkdv(q, k, v, dout, windows, sinks, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
                            stream);
 }
 
@@ -524,28 +543,29 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   return AAH_OK;
 }
 
-aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                        aah_work_item* items, int64_t capacity, int64_t* n_items) {
+aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int q_tile, int kv_tile,
+                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();
-  return plan_to_host(kPlanFwd, windows, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+  return plan_to_host(kPlanFwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
 }
 
-aah_status aah_plan_bwd(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                        aah_work_item* items, int64_t capacity, int64_t* n_items) {
+aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int q_tile, int kv_tile,
+                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();
-  return plan_to_host(kPlanBwd, windows, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+  return plan_to_host(kPlanBwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
 }
 
-aah_status aah_window_stats(const int32_t* windows, int H, int T, int64_t* pairs_per_batch, double* acr) {
+aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H, int T, int64_t* pairs_per_batch,
+                            double* acr) {
   g_detail.clear();
   if (windows == nullptr || pairs_per_batch == nullptr || acr == nullptr)
     return fail(AAH_ERR_INVALID_ARG, "NULL pointer argument");
   if (H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "H and T must be >= 1");
+  AAH_TRY(check_windows(windows, sinks, H));
   int64_t pairs = 0;
   double cover = 0.0;
   for (int h = 0; h < H; ++h) {
-    if (windows[h] < 1) return fail(AAH_ERR_INVALID_ARG, "windows[%d] = %d; every window must be >= 1", h, windows[h]);
-    pairs += aah::pair_count(T, windows[h]);
+    pairs += aah::pair_count(T, windows[h], sinks == nullptr ? 0 : sinks[h]);
     cover += static_cast<double>(aah::effective_window(windows[h], T)) / T;
   }
   *pairs_per_batch = pairs;

@@ -13,7 +13,7 @@
 // dP MFMA chains from nl2 and nD instead of zero.  So c s - lse log2(e) and
 // dP - D come straight out of the matrix cores: a weight is exp2(acc) and
 // dS = p * (dP - D) is one multiply.  The rounding of the premultiplied operand
-// moves each exponent by at most 2^-9 sum_i |c q_i k_i|, a relative change of
+// moves each exponent by at most 2^-8 sum_i |c q_i k_i|, a relative change of
 // the weight of the same order as its own rounding to bf16 for the dV / dK /
 // dQ products.  The softmax scale of dK and dQ is applied once, when they are
 // stored.
@@ -46,6 +46,13 @@
 // blocks that cross the diagonal or the window's trailing edge.  Tiles are
 // row-major with the XOR chunk swizzle of the forward kernel.  Rows past T
 // read as zero (bounded buffer resources) and contribute nothing.
+//
+// Sink keys ("Autonomy-of-Heads", section 5): with S sinks, key j is visible
+// to query i iff j <= i and (i - W < j or j < S).  The SINK instantiations
+// spare keys below S from the trailing-edge mask and never skip their blocks;
+// the dQ kernel walks the sink tiles before its window tiles (as the forward
+// does), and a dK/dV item holding a sink key runs over every later query tile
+// (its planner range says so).  Without sinks the SINK = false code runs.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -132,12 +139,13 @@ __device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char*
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D>
+template <int D, bool SINK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
-                     const int32_t* __restrict__ win_eff, int H, int T, float scale) {
+                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T,
+                     float scale) {
   using C = Cfg<D>;
   // Three-stage ring; stage = {Q tile, dO tile, nl2 row, nD row}.
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
@@ -149,6 +157,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
+  const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const float c = scale * kLog2e;
@@ -157,6 +166,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
   const int k0w = it.tile * kStat + 32 * wave;  // first key of this wave
+  const bool wave_sink = SINK && k0w < S;         // every later query sees some key of this wave
   const int key = k0w + ln;                      // this lane's key (column of S)
   const bool wave_active = k0w < T;
   const Offsets<D> off(wave, lane);
@@ -241,14 +251,15 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     }
   };
 
-  // One 64-query step, block by block.  Query i sees key j iff 0 <= i - j < W;
-  // the wave's keys are [k0w, k0w + 32).  Blocks no key sees are skipped; only
-  // blocks crossing the diagonal or the window's trailing edge are masked.
+  // One 64-query step, block by block.  Query i sees key j iff 0 <= i - j < W
+  // (or j < S and i >= j); the wave's keys are [k0w, k0w + 32).  Blocks no key
+  // sees are skipped; only blocks crossing the diagonal or the window's
+  // trailing edge are masked.
   auto do_step = [&](const char* st, int q0) __attribute__((always_inline)) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb = q0 + 32 * mb;
-      if (!(wave_active && qb < T && qb + 31 >= k0w && qb <= k0w + 30 + W)) continue;
+      if (!(wave_active && qb < T && qb + 31 >= k0w && (qb <= k0w + 30 + W || wave_sink))) continue;
       f32x16 s, dp;
       scores(st, mb, s, dp);
       // Register r holds query qb + 4 hl + reg_row(r); i - j = reg_row(r) - lim.
@@ -257,8 +268,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = reg_row(r) < lim ? -INFINITY : s[r];
       }
-      if (qb + 31 >= k0w + W) {  // some query is W or more past some key
-        const int hi = lim + W;
+      if (qb + 31 >= k0w + W && (!SINK || k0w + 31 >= S)) {  // some query is W or more past some non-sink key
+        // A sink key (key < S) is never past the edge: reg_row(r) < 32 <= hi.
+        const int hi = SINK && key < S ? 32 : lim + W;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = reg_row(r) >= hi ? -INFINITY : s[r];
       }
@@ -324,13 +336,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
 // ---------------------------------------------------------------- dQ
 
-template <int D>
+template <int D, bool SINK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
                    float* __restrict__ NL2, float* __restrict__ ND, bf16* __restrict__ dQ,
-                   const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff, int H, int T,
-                   float scale) {
+                   const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
+                   const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
   using C = Cfg<D>;
   constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
   __shared__ __attribute__((aligned(1024))) char ring0[kStage];
@@ -340,6 +352,11 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
+  const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
+  // Tiles in visiting order: the sink tiles before the window's first tile, then it.lo .. it.hi - 1.
+  const int ns = SINK ? min((S + kStep - 1) / kStep, it.lo) : 0;
+  const int n_tiles = ns + it.hi - it.lo;
+  auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + it.lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const float c = scale * kLog2e;
@@ -363,8 +380,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
   // Prologue: the first two stages' copies go out before the row loads below,
   // so that their latencies overlap.
-  fill(it.lo, ring0);
-  if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+  fill(tile_at(0), ring0);
+  if (1 < n_tiles) fill(tile_at(1), ring1);
 
   // Q (premultiplied by c) and dO rows of this lane's query: the B operands of
   // S^T = K Q^T and dP^T = V dO^T.  Lanes ln and ln + 32 hold the two halves
@@ -420,7 +437,11 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
 
   // One 32-key block [kb, kb + 32) of the stage in st.
   auto do_block = [&](const char* st, int kb, int mb) __attribute__((always_inline)) {
-    if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;
+    if constexpr (SINK) {
+      if (!(wave_active && kb <= wave_key_hi && (kb + 31 >= wave_key_lo || kb < S))) return;
+    } else {
+      if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;
+    }
     const char* ks = st;
     const char* vs = st + C::kTileBytes;
     f32x16 s = cl16, dp = nd16;
@@ -429,16 +450,18 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd[k]), qf[k], s);
       dp = mfma(*reinterpret_cast<const bf16x8*>(vs + 32 * mb * C::kRowBytes + off.rd[k]), gf[k], dp);
     }
-    // Register r holds key kb + 4 hl + reg_row(r), visible iff lim - W < reg_row(r) <= lim.
+    // Register r holds key kb + 4 hl + reg_row(r), visible iff lim - W < reg_row(r) <= lim
+    // (or reg_row(r) < sl, a sink, with reg_row(r) <= lim).
     const int lim = qi - kb - 4 * hl;
     if (kb + 31 > q0w) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[r] = reg_row(r) > lim ? -INFINITY : s[r];
     }
-    if (kb < q0w + 32 - W) {
+    if (SINK ? kb < q0w + 32 - W && kb + 31 >= S : kb < q0w + 32 - W) {
       const int lo = lim - W;
+      const int sl = S - kb - 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) <= lo ? -INFINITY : s[r];
+      for (int r = 0; r < 16; ++r) s[r] = reg_row(r) <= lo && (!SINK || reg_row(r) >= sl) ? -INFINITY : s[r];
     }
     bf16x8 df[2];
 #pragma unroll
@@ -456,13 +479,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     }
   };
 
-  auto step = [&](int kt, const char* cur, char* nxt2) __attribute__((always_inline)) {
-    const bool more = kt + 2 < it.hi;
-    if (more) fill(kt + 2, nxt2);
-    const int k0 = kt * kStep;
+  // Ring: the v-th tile visited uses stage v % 3 and fills the stage of tile v + 2.
+  auto step = [&](int v, const char* cur, char* nxt2) __attribute__((always_inline)) {
+    const bool more = v + 2 < n_tiles;
+    if (more) fill(tile_at(v + 2), nxt2);
+    const int k0 = tile_at(v) * kStep;
     do_block(cur, k0, 0);
     do_block(cur, k0 + 32, 1);
-    if (kt + 1 >= it.hi) return true;
+    if (v + 1 >= n_tiles) return true;
     if (more)
       wait_vm_barrier(kFill);
     else
@@ -470,10 +494,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     return false;
   };
   wait_vm_barrier(0);
-  for (int kt = it.lo;; kt += 3) {
-    if (step(kt, ring0, ring2)) break;
-    if (step(kt + 1, ring1, ring0)) break;
-    if (step(kt + 2, ring2, ring1)) break;
+  for (int v = 0;; v += 3) {
+    if (step(v, ring0, ring2)) break;
+    if (step(v + 1, ring1, ring0)) break;
+    if (step(v + 2, ring2, ring1)) break;
   }
 
   if (qi >= T) return;
@@ -494,47 +518,68 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    acc[b][4 * i + 2] * scale, acc[b][4 * i + 3] * scale);
 }
 
-template <int D>
+template <int D, bool SINK>
 hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
-                  const AttnShape& s, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_dkdv_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(dout), nl2,
-                     nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items, win_eff, s.H, s.T, s.scale);
+                  const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SINK>), dim3(n_items), dim3(kThreads), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<const bf16*>(dout), nl2, nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items,
+                     win_eff, sink_eff, s.H, s.T, s.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool SINK>
+hipError_t dq_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+                const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_dq_kernel<D, SINK>), dim3(n_items), dim3(kThreads), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, nl2, nd,
+                     static_cast<bf16*>(dq), items, win_eff, sink_eff, s.H, s.T, s.scale);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t dq_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+hipError_t dkdv_s(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
+                  void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
+                  const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+  return sink_eff != nullptr
+             ? dkdv_d<D, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream)
+             : dkdv_d<D, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+}
+
+template <int D>
+hipError_t dq_s(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                const AttnShape& s, hipStream_t stream) {
-  hipLaunchKernelGGL(bwd_dq_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
-                     static_cast<const bf16*>(k), static_cast<const bf16*>(v), static_cast<const bf16*>(o),
-                     static_cast<const bf16*>(dout), lse, nl2, nd, static_cast<bf16*>(dq), items, win_eff, s.H, s.T,
-                     s.scale);
-  return hipGetLastError();
+                const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+  return sink_eff != nullptr
+             ? dq_d<D, true>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream)
+             : dq_d<D, false>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream);
 }
 
 }  // namespace
 
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
-                                const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
+                                const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s,
+                                hipStream_t stream) {
   switch (s.d) {
-    case 32: return dkdv_d<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
-    case 64: return dkdv_d<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
-    case 128: return dkdv_d<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, stream);
+    case 32: return dkdv_s<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return dkdv_s<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return dkdv_s<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items, int n_items,
-                              const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
+                              const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s,
+                              hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_d<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
-    case 64: return dq_d<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
-    case 128: return dq_d<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, stream);
+    case 32: return dq_s<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return dq_s<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return dq_s<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -42,6 +42,14 @@
 // underflow.
 // Global loads go through buffer resources whose range ends at the head's
 // last row, so rows past T read as zero without branches.
+//
+// Sink keys ("Autonomy-of-Heads", section 5: a streaming head keeps its first
+// S tokens besides its recent window).  Key j is then visible to query i iff
+// j <= i and (i - W < j or j < S).  The SINK instantiation walks the sink
+// tiles before the item's first window tile (keys there precede every row's
+// window, so only j < S decides), then the window tiles as usual; its
+// trailing-edge mask spares keys below S, and blocks of sink keys are never
+// skipped.  Without sinks the SINK = false instantiation runs, unchanged.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -77,11 +85,12 @@ struct Cfg {
 // Key offset (within its 32-key block, before the 4 hl lane offset) held by S^T register r.
 __device__ constexpr int reg_key(int r) { return 8 * (r >> 2) + (r & 3); }
 
-template <int D>
+template <int D, bool SINK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      bf16* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
-                     const int32_t* __restrict__ win_eff, int H, int T, float c) {
+                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T,
+                     float c) {
   using C = Cfg<D>;
   constexpr int NC = C::kNC;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes];
@@ -92,6 +101,12 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
   const int W = win_eff[it.bh % H];
+  const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
+  // Tiles in visiting order: sink tiles 0 .. ns - 1 (those before the window's
+  // first tile), then the window tiles it.lo .. it.hi - 1.
+  const int ns = SINK ? min((S + kKeys - 1) / kKeys, it.lo) : 0;
+  const int n_tiles = ns + it.hi - it.lo;
+  auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + it.lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const bf16* Qh = Q + base;
   const bf16* Kh = K + base;
@@ -179,10 +194,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
   // One 32-key block [kb, kb + 32) of the tile held in (kt_lds, vt_lds), for this wave.
   auto do_block = [&](const char* kt_lds, const char* vt_lds, int kb, int mb) __attribute__((always_inline)) {
-    if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;  // no row sees it
+    if constexpr (SINK) {
+      if (!(wave_active && kb <= wave_key_hi && (kb + 31 >= wave_key_lo || kb < S))) return;  // no row sees it
+    } else {
+      if (!(wave_active && kb <= wave_key_hi && kb + 31 >= wave_key_lo)) return;  // no row sees it
+    }
     const bool mh = kb + 31 > q0w;       // some key may be after some row (diagonal)
-    const bool ml = kb < q0w + 32 - W;   // some key may precede some row's window (trailing edge)
+    // Some non-sink key may precede some row's window (trailing edge).
+    const bool ml = SINK ? kb < q0w + 32 - W && kb + 31 >= S : kb < q0w + 32 - W;
     const int lim = qi - kb - 4 * hl;    // register r's key is visible iff lim - W < reg_key(r) <= lim
+    const int sl = S - kb - 4 * hl;      // ... or reg_key(r) < sl (a sink), with reg_key(r) <= lim
 
     auto compute_s = [&]() __attribute__((always_inline)) {
       f32x16 s = f32x16{};
@@ -199,7 +220,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       if (ml) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (reg_key(r) <= lim - W) s[r] = -INFINITY;
+          if (reg_key(r) <= lim - W && (!SINK || reg_key(r) >= sl)) s[r] = -INFINITY;
       }
       return s;
     };
@@ -276,27 +297,27 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     do_block(kt_lds, vt_lds, k0 + 32, 1);
   };
 
-  // Two-stage ring: tile kt lives in stage (kt - lo) % 2.  A step issues the
-  // copies of the next tile into the other stage (which every wave finished
+  // Two-stage ring: the v-th tile visited lives in stage v % 2.  A step issues
+  // the copies of the next tile into the other stage (which every wave finished
   // reading before the barrier that ended the previous step), computes the
   // current tile, then waits for its own copies and meets the other waves at
   // the barrier.  Returns true after the last tile.  Two stages instead of
   // three leave room for four workgroups per CU at d = 64 instead of three;
   // the copies still have a whole step to land.
-  auto step = [&](int kt, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
-    const bool fill = kt + 1 < it.hi;
-    if (fill) issue_tile(kt + 1, kn, vn);
-    do_tile(kc, vc, kt);
+  auto step = [&](int v, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
+    const bool fill = v + 1 < n_tiles;
+    if (fill) issue_tile(tile_at(v + 1), kn, vn);
+    do_tile(kc, vc, tile_at(v));
     if (!fill) return true;  // nothing left to wait for; the workgroup is done with LDS
     wait_vm_barrier(0);
     return false;
   };
 
-  issue_tile(it.lo, k_lds0, v_lds0);
+  issue_tile(tile_at(0), k_lds0, v_lds0);
   wait_vm_barrier(0);
-  for (int kt = it.lo;; kt += 2) {
-    if (step(kt, k_lds0, v_lds0, k_lds1, v_lds1)) break;
-    if (step(kt + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
+  for (int v = 0;; v += 2) {
+    if (step(v, k_lds0, v_lds0, k_lds1, v_lds1)) break;
+    if (step(v + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
   }
 
   if (!wave_active) return;
@@ -316,24 +337,29 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse,
-                    const WorkItem* items, int n_items, const int32_t* win_eff,
+                    const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                     const AttnShape& s, hipStream_t stream) {
   const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n_items), dim3(kThreads), 0, stream,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<bf16*>(o), lse, items, win_eff, s.H, s.T, c);
+  if (sink_eff != nullptr)
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(n_items), dim3(kThreads), 0, stream,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                       static_cast<bf16*>(o), lse, items, win_eff, sink_eff, s.H, s.T, c);
+  else
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(n_items), dim3(kThreads), 0, stream,
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                       static_cast<bf16*>(o), lse, items, win_eff, sink_eff, s.H, s.T, c);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const WorkItem* items, int n_items, const int32_t* win_eff,
+                           const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                            const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return launch_d<32>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
-    case 64: return launch_d<64>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
-    case 128: return launch_d<128>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
+    case 32: return launch_d<32>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return launch_d<64>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return launch_d<128>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

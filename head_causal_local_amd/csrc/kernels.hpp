@@ -20,6 +20,11 @@ constexpr int kBwdBf16ColTile = 64;   // queries per step
 constexpr int kSimpleRowTile = 64;    // one wave, one row per lane
 constexpr int kSimpleColTile = 64;
 
+// win_eff: effective window per head (int32[H], device).  sink_eff: effective
+// sink size per head (int32[H], device; keys 0 .. S - 1 stay visible to every
+// later query), or nullptr when no head has one -- then the kernels without
+// sink handling run.
+
 struct AttnShape {
   int B, H, T, d;
   float scale;          // softmax scale applied to q . k
@@ -27,12 +32,12 @@ struct AttnShape {
 
 // bf16 forward on MFMA (d in {32, 64, 128}).
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const WorkItem* items, int n_items, const int32_t* win_eff,
+                           const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                            const AttnShape& s, hipStream_t stream);
 
 // Scalar forward for fp32 (d in {32, 64, 128}).
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                           const AttnShape& s, hipStream_t stream);
 
 // Per row: nd = -(dO . O) and nl2 = -lse log2(e), in fp32.  is_bf16 selects the
@@ -44,23 +49,23 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 // planner (kBwdBf16RowTile keys per item, kBwdBf16ColTile queries per step).
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
-                                const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+                                const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 
 // dQ: items from the forward planner (kFwdBf16RowTile queries, kFwdBf16ColTile keys per step).
 // Also writes, for every row, nl2 = -lse log2(e) and nd = -(dO . O), which
 // launch_bwd_dkdv_bf16 reads: it must run first.
 hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o, const void* dout,
                               const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items, int n_items,
-                              const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+                              const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 
 // Scalar backward for fp32: dQ one query row per lane over the forward work
 // list; dK/dV one key row per lane over the backward work list.
 hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout,
                                 const float* nl2, const float* nd, float* dq, const WorkItem* items,
-                                int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream);
+                                int n_items, const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
                                   const float* nl2, const float* nd, float* dk, float* dv,
-                                  const WorkItem* items, int n_items, const int32_t* win_eff,
+                                  const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                                   const AttnShape& s, hipStream_t stream);
 
 // ---- decoding over per-head trimmed K/V caches (bf16)

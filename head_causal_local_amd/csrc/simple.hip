@@ -11,6 +11,10 @@
 //   dS_ij = P_ij (dP_ij - D_i),  dQ_i = scale sum_j dS_ij k_j,
 //   dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
 // D_i is computed as dO_i . O_i, which equals sum_j P_ij dP_ij because O_i = sum_j P_ij v_j.
+// With S sink keys per head ("Autonomy-of-Heads", section 5) key j is also
+// visible to every query i >= j when j < S; items then visit the sink tiles
+// before their window tiles (forward and dQ), and dK/dV items of sink keys
+// run to the last query tile (the planner's range).
 #include <cmath>
 
 #include "kernels.hpp"
@@ -29,6 +33,12 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 __device__ inline float to_f32(float x) { return x; }
 __device__ inline float to_f32(bf16 x) { return static_cast<float>(x); }
+
+// Key j visible to query i: causal, and inside the window of W or a sink (j < S).
+__device__ inline bool visible(int i, int j, int W, int S) { return j <= i && (j > i - W || j < S); }
+
+// Sink tiles an item visits before its window tiles [lo, hi).
+__device__ inline int n_sink_tiles(int S, int lo) { return min((S + kCols - 1) / kCols, lo); }
 template <typename E> __device__ inline E from_f32(float x);
 template <> __device__ inline float from_f32<float>(float x) { return x; }
 
@@ -47,12 +57,14 @@ template <int D>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, int H, int T, float c) {
+    const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T, float c) {
   __shared__ float ks[kCols * D];
   __shared__ float vs[kCols * D];
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
+  const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
+  const int ns = n_sink_tiles(S, it.lo);
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const int qi = it.tile * kRows + threadIdx.x;
   const bool row_ok = qi < T;
@@ -65,8 +77,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
   }
   float m = -INFINITY, l = 0.f;  // log2-domain running max and running sum
 
-  for (int kt = it.lo; kt < it.hi; ++kt) {
-    const int k0 = kt * kCols;
+  for (int v = 0; v < ns + it.hi - it.lo; ++v) {
+    const int k0 = (v < ns ? v : v - ns + it.lo) * kCols;
     __syncthreads();
     stage_rows<float, D>(ks, K + base, k0, T);
     stage_rows<float, D>(vs, V + base, k0, T);
@@ -80,7 +92,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
         float dot = 0.f;
 #pragma unroll
         for (int x = 0; x < D; ++x) dot = fmaf(qr[x], ks[(j0 + j) * D + x], dot);
-        const bool ok = key <= qi && key > qi - W && key < T;
+        const bool ok = visible(qi, key, W, S) && key < T;
         s[j] = ok ? dot * c : -INFINITY;
         mx = fmaxf(mx, s[j]);
       }
@@ -147,12 +159,14 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
-    int H, int T, float scale) {
+    const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
   __shared__ float ks[kCols * D];
   __shared__ float vs[kCols * D];
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
+  const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
+  const int ns = n_sink_tiles(S, it.lo);
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const int qi = it.tile * kRows + threadIdx.x;
   const bool row_ok = qi < T;
@@ -168,15 +182,15 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
   const float cl = row_ok ? NL2[static_cast<size_t>(it.bh) * T + qi] : 0.f;  // -lse * log2(e)
   const float nD = row_ok ? ND[static_cast<size_t>(it.bh) * T + qi] : 0.f;
 
-  for (int kt = it.lo; kt < it.hi; ++kt) {
-    const int k0 = kt * kCols;
+  for (int v = 0; v < ns + it.hi - it.lo; ++v) {
+    const int k0 = (v < ns ? v : v - ns + it.lo) * kCols;
     __syncthreads();
     stage_rows<E, D>(ks, K + base, k0, T);
     stage_rows<E, D>(vs, V + base, k0, T);
     __syncthreads();
     for (int j = 0; j < kCols; ++j) {
       const int key = k0 + j;
-      if (!(key <= qi && key > qi - W && key < T)) continue;
+      if (!(visible(qi, key, W, S) && key < T)) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int x = 0; x < D; ++x) {
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dK, E* __restrict__ dV, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, int H, int T, float scale) {
+    const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
   __shared__ float qs[kCols * D];
   __shared__ float gs[kCols * D];
   __shared__ float ls[kCols];
@@ -208,6 +222,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
+  const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const int kj = it.tile * kRows + threadIdx.x;
@@ -235,7 +250,7 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     __syncthreads();
     for (int i = 0; i < kCols; ++i) {
       const int qrow = q0 + i;
-      if (!(kj <= qrow && kj > qrow - W && qrow < T && row_ok)) continue;
+      if (!(visible(qrow, kj, W, S) && qrow < T && row_ok)) continue;
       float s = 0.f, dp = 0.f;
 #pragma unroll
       for (int x = 0; x < D; ++x) {
@@ -261,10 +276,10 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
 
 template <int D>
 hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, float* lse,
-                     const WorkItem* items, int n_items, const int32_t* win_eff,
+                     const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                      const AttnShape& s, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(n_items), dim3(kRows), 0, stream, q, k, v, o, lse, items,
-                     win_eff, s.H, s.T, s.scale * kLog2e);
+                     win_eff, sink_eff, s.H, s.T, s.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -283,12 +298,12 @@ hipError_t pre_d(const void* o, const void* dout, const float* lse, float* nl2, 
 }  // namespace
 
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                           const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return fwd_f32_d<32>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
-    case 64: return fwd_f32_d<64>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
-    case 128: return fwd_f32_d<128>(q, k, v, o, lse, items, n_items, win_eff, s, stream);
+    case 32: return fwd_f32_d<32>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return fwd_f32_d<64>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return fwd_f32_d<128>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -308,10 +323,10 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
 
 hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, const float* dout, const float* nl2,
                                 const float* nd, float* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                                const AttnShape& s, hipStream_t stream) {
+                                const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
 #define AAH_DQ(DD)                                                                                                \
   hipLaunchKernelGGL((bwd_dq_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, nl2, \
-                     nd, dq, items, win_eff, s.H, s.T, s.scale)
+                     nd, dq, items, win_eff, sink_eff, s.H, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DQ(32); break;
     case 64: AAH_DQ(64); break;
@@ -324,10 +339,11 @@ hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, 
 
 hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v, const float* dout,
                                   const float* nl2, const float* nd, float* dk, float* dv, const WorkItem* items,
-                                  int n_items, const int32_t* win_eff, const AttnShape& s, hipStream_t stream) {
+                                  int n_items, const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s,
+                                  hipStream_t stream) {
 #define AAH_DKDV(DD)                                                                                            \
   hipLaunchKernelGGL((bwd_dkdv_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, \
-                     nl2, nd, dk, dv, items, win_eff, s.H, s.T, s.scale)
+                     nl2, nd, dk, dv, items, win_eff, sink_eff, s.H, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DKDV(32); break;
     case 64: AAH_DKDV(64); break;

@@ -19,18 +19,38 @@ static_assert(sizeof(WorkItem) == 16, "WorkItem must stay 16 bytes (one int4 loa
 // Effective window of a head: windows above T act as T.
 inline int effective_window(int32_t w, int T) { return w > T ? T : w; }
 
-// Exact in-window pairs of one head over length T: sum_{t=1}^{T} min(t, W).
-inline int64_t pair_count(int T, int w) {
+// Effective sink size of a head (sink keys 0 .. S - 1 stay visible to every later
+// query): only keys j <= T - 1 - W ever fall out of some row's window, so sinks
+// past T - W change nothing, and a head whose window covers T has none.
+inline int effective_sink(int32_t s, int32_t w, int T) {
+  const int lim = T - effective_window(w, T);
+  return s < 0 ? 0 : (s < lim ? s : lim);
+}
+
+// Sink key tiles a forward item visits before its window tiles [lo, hi): the
+// tiles of keys 0 .. S - 1 that lie before lo.
+inline int sink_tiles(int S, int lo, int kv_tile) {
+  const int n = (S + kv_tile - 1) / kv_tile;
+  return n < lo ? n : lo;
+}
+
+// Exact visible pairs of one head over length T: sum_{t=1}^{T} min(t, W), plus,
+// with S sink keys, the sinks row t sees before its window: sum_t max(0, min(S, t - W)).
+inline int64_t pair_count(int T, int w, int s = 0) {
   const int64_t W = effective_window(w, T);
-  return W * (W + 1) / 2 + (static_cast<int64_t>(T) - W) * W;
+  const int64_t S = effective_sink(s, w, T);
+  const int64_t U = static_cast<int64_t>(T) - W;  // rows with keys before their window
+  const int64_t sinks = U <= S ? U * (U + 1) / 2 : S * (S + 1) / 2 + (U - S) * S;
+  return W * (W + 1) / 2 + U * W + sinks;
 }
 
 // Forward items: one per (b, h, query tile), with the key-tile range it needs.
-std::vector<WorkItem> plan_forward(const int32_t* windows, int B, int H, int T,
+// sinks: int32[H] or nullptr; an item's sink tiles are implied (sink_tiles).
+std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
                                    int q_tile, int kv_tile, int n_queues);
 
 // Backward items: one per (b, h, key tile), with the query-tile range that sees it.
-std::vector<WorkItem> plan_backward(const int32_t* windows, int B, int H, int T,
+std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
                                     int q_tile, int kv_tile, int n_queues);
 
 }  // namespace aah

@@ -24,6 +24,15 @@
  *     every batch entry (section 5.8 maps one decision per head).  Each entry
  *     must be >= 1; entries above T act as T.  No lower clamp is applied: the
  *     pages' W_min = 512 belongs to the window controller, not to execution.
+ *   - `sinks` is NULL or a HOST pointer to int32[H], each >= 0: head h also
+ *     keeps its first sinks[h] keys visible to every later query, i.e. key t_k
+ *     is visible to query t_q iff t_k <= t_q and (t_q - W_h < t_k or
+ *     t_k < sinks[h]).  This is the sink + recent-window attention of a
+ *     streaming head in "Autonomy-of-Heads: Data-Free Sparse Attention from
+ *     Frozen Query-Key Geometry", section 5 (Deploying LLMs With AoH; section
+ *     6.1 uses 128 sinks and a window of 256).  NULL, or all zeros, is the
+ *     plain window.  Sinks past T - min(W_h, T) change nothing and are
+ *     ignored; lse then covers the sink keys too.
  *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *     stream).  Calls only enqueue work on it and return; they never
  *     synchronise the device, except that the first call for a new
@@ -50,7 +59,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 3
+#define AAH_ABI_VERSION 4
 
 typedef enum {
   AAH_OK = 0,
@@ -94,7 +103,7 @@ const char* aah_last_error_detail(void);
  * (a non-NULL workspace is accepted and ignored).
  */
 aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
-                        const int32_t* windows, int B, int H, int T, int d,
+                        const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
                         aah_dtype dt, float scale, void* o, float* lse,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
@@ -102,7 +111,7 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Backward pass: gradients of sum(O * dout) with respect to q, k and v, given
  * the forward's o and lse (the log-sum-exp saved by aah_attn_fwd with the same
- * scale and windows).  Writes dq, dk, dv [B,H,T,d] of dtype dt (each element
+ * scale, windows and sinks).  Writes dq, dk, dv [B,H,T,d] of dtype dt (each element
  * exactly once: no atomics, results are bitwise reproducible).  Needs a device
  * workspace of at least aah_attn_workspace_size(B, H, T, d, dt, 1) bytes,
  * 256-byte aligned; its contents on entry do not matter and are clobbered.
@@ -110,7 +119,7 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
  */
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse,
-                        const int32_t* windows, int B, int H, int T, int d,
+                        const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
                         aah_dtype dt, float scale, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
@@ -128,12 +137,13 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
  *     aah_attn_bwd_dq has completed on the same workspace.
  */
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* windows, int B, int H, int T, int d, aah_dtype dt,
-                           float scale, void* dq, void* workspace, size_t workspace_bytes, aah_stream_t stream);
+                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+                           int d, aah_dtype dt, float scale, void* dq, void* workspace, size_t workspace_bytes,
+                           aah_stream_t stream);
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                             const int32_t* windows, int B, int H, int T, int d, aah_dtype dt, float scale,
-                             void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                             const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt,
+                             float scale, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
                              aah_stream_t stream);
 
 /*
@@ -206,9 +216,14 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
  * see them are [k0, min(T, k1 + W - 1)), i.e. query tiles
  * [floor(k0 / q_tile), floor((min(T, k1 + W - 1) - 1) / q_tile) + 1).
  * W = min(windows[h], T).  Tiles wholly outside every row's window are never
- * listed.  Items are grouped into `n_queues` queues (heads are dealt to
+ * listed.  With sinks (NULL = none), S = min(sinks[h], T - W): a forward
+ * item also visits the sink key tiles [0, min(ceil(S / kv_tile), lo)) before
+ * [lo, hi) (implied, not stored); a backward item whose keys start below S
+ * runs to the last query tile, [floor(k0 / q_tile), ceil(T / q_tile)).
+ * Items are grouped into `n_queues` queues (heads are dealt to
  * queues longest-total-first, each to the least-loaded queue); each queue is
- * sorted by item cost (hi - lo) descending, ties by (bh, tile) ascending; the
+ * sorted by item cost (tiles visited, sink tiles included) descending, ties
+ * by (bh, tile) ascending; the
  * output interleaves the queues so that slot s belongs to queue s % n_queues,
  * padding short queues with bh = -1 slots.  With n_queues = 8 this matches
  * the round-robin placement of workgroups on MI355X's eight XCDs, so the
@@ -218,20 +233,23 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
  * and always stores the full slot count in *n_items; returns
  * AAH_ERR_INVALID_ARG if capacity is too small (after setting *n_items).
  */
-aah_status aah_plan_fwd(const int32_t* windows, int B, int H, int T,
+aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
 
-aah_status aah_plan_bwd(const int32_t* windows, int B, int H, int T,
+aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
 
 /*
- * Coverage of a window vector (section 5.10): the exact in-window query/key
- * pair count of one batch entry, sum_h sum_{t=1}^{T} min(t, W_h), and the
- * Attention Coverage Ratio sum_h T * W_h / (H * T^2), both with W_h = min(W_h, T).
+ * Coverage of a window vector (section 5.10): the exact visible query/key
+ * pair count of one batch entry, sum_h sum_{t=1}^{T} min(t, W_h) (plus, with
+ * sinks, the sink keys each row sees before its window,
+ * sum_t max(0, min(S_h, t - W_h))), and the Attention Coverage Ratio
+ * sum_h T * W_h / (H * T^2) of the windows alone, with W_h = min(W_h, T).
+ * sinks may be NULL.
  */
-aah_status aah_window_stats(const int32_t* windows, int H, int T,
+aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H, int T,
                             int64_t* pairs_per_batch, double* acr);
 
 /* Free every cached device work list.  Not thread-safe against concurrent

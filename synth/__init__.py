@@ -7,7 +7,11 @@ none of the attention arithmetic (no scores, masks, softmax or products).
 Workloads follow the pages' 4096-token bf16 setting (Asymmetric Attention
 Heads, Table 2: precision bf16, batch size 1, context 4096, candidate windows
 [512, 1024, 2048, 4096]).  The pages train on an unnamed dataset with trained
-weights; N(0, 1) activations stand in for the projected Q/K/V.
+weights; N(0, 1) activations stand in for the projected Q/K/V.  The
+streaming-head workload follows "Autonomy-of-Heads" (section 5: retrieval
+heads keep full attention, streaming heads keep sink + recent-window caches;
+section 6.1: 128 sinks and a recent window of 256; section 6.4: sparsity
+around 0.5) on the same 1B-scale layer shape.
 
 Recipe (fixed, so every consumer sees identical bits):
   * ``numpy.random.default_rng(seed)``; fp32 standard normals drawn in the
@@ -58,6 +62,7 @@ class Workload:
     bits: Dict[str, np.ndarray] = dataclasses.field(default_factory=dict)  # uint16 for bf16
     backward: bool = False
     meta: Dict[str, object] = dataclasses.field(default_factory=dict)
+    sinks: Optional[np.ndarray] = None  # int32 [H] sink sizes, or None
 
 
 def _draw(rng: np.random.Generator, shape, dtype: str):
@@ -70,7 +75,7 @@ def _draw(rng: np.random.Generator, shape, dtype: str):
 
 def random_workload(B: int, H: int, T: int, d: int, windows, dtype: str = "bf16",
                     seed: int = 0, backward: bool = True, name: str = "random",
-                    value_scale: float = 1.0) -> Workload:
+                    value_scale: float = 1.0, sinks=None) -> Workload:
     """Q, K, V (and dO) ~ N(0, 1) * value_scale for an arbitrary shape and window vector."""
     rng = np.random.default_rng(seed)
     shape = (B, H, T, d)
@@ -88,7 +93,8 @@ def random_workload(B: int, H: int, T: int, d: int, windows, dtype: str = "bf16"
     return Workload(name=name, B=B, H=H, T=T, d=d, dtype=dtype,
                     windows=np.asarray(windows, dtype=np.int32), scale=1.0 / np.sqrt(d),
                     q=out["q"], k=out["k"], v=out["v"], do=out["do"] if backward else None,
-                    bits=bits, backward=backward)
+                    bits=bits, backward=backward,
+                    sinks=None if sinks is None else np.asarray(sinks, dtype=np.int32))
 
 
 def _hierarchy_from_groups(group_windows: np.ndarray) -> List[List[int]]:
@@ -113,6 +119,8 @@ DESCRIPTIONS = {
     "4a": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, all windows 4096",
     "4b": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, all windows 512",
     "4c": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, even heads 512, odd heads 4096",
+    5: "streaming heads fwd+bwd: B=4 H=32 T=4096 d=64 bf16, heads 0-15 full causal (4096), "
+       "heads 16-31 sink 128 + recent window 256",
 }
 
 
@@ -128,7 +136,7 @@ def make_workload(idx, seed: int = 0) -> Workload:
                         windows=np.array([16, 32, 64, 256], dtype=np.int32),
                         scale=1.0 / np.sqrt(32), q=q, k=k, v=v, backward=False)
 
-    if idx in (1, 2, 3, "4a", "4b", "4c"):
+    if idx in (1, 2, 3, "4a", "4b", "4c", 5):
         if idx == 1:
             B, H = 1, 16
         else:
@@ -156,12 +164,19 @@ def make_workload(idx, seed: int = 0) -> Workload:
         elif idx == "4b":
             windows = np.full(H, 512, dtype=np.int32)
             name = "control-all512"
-        else:
+        elif idx == "4c":
             windows = np.where(np.arange(H) % 2 == 0, 512, 4096).astype(np.int32)
             name = "control-interleaved-512-4096"
+        else:
+            # Retrieval heads first, then streaming heads (the reordered layout of
+            # "Autonomy-of-Heads" section 5), half of each at sparsity 0.5 (section 6.4).
+            windows = np.where(np.arange(H) < H // 2, T, 256).astype(np.int32)
+            meta["sinks"] = np.where(np.arange(H) < H // 2, 0, 128).astype(np.int32)
+            name = "streaming-B4-H32-T4096-d64-sink128-recent256"
         backward = idx != 1 and idx != 2
+        sinks = meta.pop("sinks", None)
         return Workload(name=name, B=B, H=H, T=T, d=d, dtype="bf16", windows=windows,
                         scale=1.0 / np.sqrt(d), q=arrs["q"], k=arrs["k"], v=arrs["v"],
                         do=arrs["do"] if backward else None, bits=bits, backward=backward,
-                        meta=meta)
+                        meta=meta, sinks=sinks)
     raise KeyError(f"unknown workload {idx!r}")

@@ -5,11 +5,23 @@ online softmax over the listed key tiles, mask evaluated per element -- and
 the backward work list key-tile by key-tile, so that a tile-range bug in the
 planner shows up as a difference from the oracle on the CPU.  It shares no
 code with the oracle and does not import it.
+
+With sink sizes, the forward items visit the implied sink tiles
+[0, min(ceil(S / kv_tile), lo)) first, S = min(sinks[h], T - W) (the library's
+effective sink), exactly as the kernels do.
 """
 import numpy as np
 
 
-def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile):
+def _eff_sink(sinks, h, T, W):
+    return 0 if sinks is None else max(0, min(int(sinks[h]), T - W))
+
+
+def _visible(rows, keys, W, S):
+    return (keys[None, :] <= rows[:, None]) & ((keys[None, :] > rows[:, None] - W) | (keys[None, :] < S))
+
+
+def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, T, d = q.shape
     O = np.full((B, H, T, d), np.nan)
@@ -19,14 +31,16 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile):
             continue
         b, h = divmod(int(bh), H)
         W = min(int(windows[h]), T)
+        S = _eff_sink(sinks, h, T, W)
         rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
         m = np.full(len(rows), -np.inf)
         l = np.zeros(len(rows))
         acc = np.zeros((len(rows), d))
-        for kt in range(lo, hi):
+        n_sink = min(-(-S // kv_tile), int(lo))
+        for kt in list(range(n_sink)) + list(range(lo, hi)):
             keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
             s = scale * q[b, h, rows] @ k[b, h, keys].T
-            ok = (keys[None, :] <= rows[:, None]) & (keys[None, :] > rows[:, None] - W)
+            ok = _visible(rows, keys, W, S)
             s = np.where(ok, s, -np.inf)
             m_new = np.maximum(m, s.max(axis=1))
             m_use = np.where(np.isneginf(m_new), 0.0, m_new)
@@ -40,7 +54,7 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile):
     return O, L
 
 
-def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile):
+def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None):
     """KV-stationary backward over the backward work list: dK, dV per key tile,
     dQ accumulated from every key tile (as the device's atomic dQ does)."""
     q, k, v, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, lse))
@@ -54,18 +68,19 @@ def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile):
             continue
         b, h = divmod(int(bh), H)
         W = min(int(windows[h]), T)
+        S = _eff_sink(sinks, h, T, W)
         keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
         dk_t = np.zeros((len(keys), d))
         dv_t = np.zeros((len(keys), d))
         for qt in range(lo, hi):
             rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
             s = scale * q[b, h, rows] @ k[b, h, keys].T
-            ok = (keys[None, :] <= rows[:, None]) & (keys[None, :] > rows[:, None] - W)
+            ok = _visible(rows, keys, W, S)
             p = np.where(ok, np.exp(s - lse[b, h, rows][:, None]), 0.0)
-            # D for these rows: sum over the row's whole window of P * dP
+            # D for these rows: sum over the row's whole key set of P * dP
             Drow = np.empty(len(rows))
             for n, i in enumerate(rows):
-                kk = np.arange(max(0, i - W + 1), i + 1)
+                kk = np.union1d(np.arange(max(0, i - W + 1), i + 1), np.arange(min(S, i + 1)))
                 pi = np.exp(scale * k[b, h, kk] @ q[b, h, i] - lse[b, h, i])
                 Drow[n] = pi @ (v[b, h, kk] @ do[b, h, i])
             dp = do[b, h, rows] @ v[b, h, keys].T

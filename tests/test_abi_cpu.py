@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 4
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -42,11 +42,13 @@ def test_abi_version_and_status_strings():
 FAKE = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
 
 
-def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, scale=0.125):
+def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, scale=0.125, sinks=None):
     w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
     H = len(w) if H is None else H
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(w) else None
-    return _lib.lib().aah_attn_fwd(q, k, v, wp, B, H, T, d, dt, scale, o, lse, None, 0, None)
+    sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.int32))
+    sp = None if sk is None else sk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    return _lib.lib().aah_attn_fwd(q, k, v, wp, sp, B, H, T, d, dt, scale, o, lse, None, 0, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -63,6 +65,8 @@ def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
     (dict(windows=[4], lse=FAKE + 2), 1),
     (dict(windows=[4], scale=float("nan")), 1),
     (dict(windows=[4], scale=float("inf")), 1),
+    (dict(windows=[4, 8], sinks=[0, -1]), 1),     # sink size < 0
+    (dict(windows=[4, 8], sinks=[2, 3], d=48), 2),
 ])
 def test_fwd_validation(kwargs, status):
     st = _fwd(**kwargs)
@@ -71,17 +75,19 @@ def test_fwd_validation(kwargs, status):
 
 
 def test_fwd_null_windows():
-    st = _lib.lib().aah_attn_fwd(FAKE, FAKE, FAKE, None, 1, 1, 8, 64, 0, 0.1, FAKE, FAKE, None, 0, None)
+    st = _lib.lib().aah_attn_fwd(FAKE, FAKE, FAKE, None, None, 1, 1, 8, 64, 0, 0.1, FAKE, FAKE, None, 0, None)
     assert st == 1
 
 
-def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE):
+def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE, sinks=None):
     w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
     H = len(w)
     need = aah.workspace_size(B, H, T, d, "bf16" if dt == 0 else "f32")
     ws_bytes = need if ws_bytes is None else ws_bytes
+    sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.int32))
+    sp = None if sk is None else sk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     return _lib.lib().aah_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                   w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), B, H, T, d, dt, 0.125,
+                                   w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), sp, B, H, T, d, dt, 0.125,
                                    dq, FAKE, FAKE, ws, ws_bytes, None)
 
 
@@ -92,6 +98,7 @@ def test_bwd_validation():
     assert _bwd([4], dq=0) == 1
     assert _bwd([4], ws=FAKE + 16) == 1       # workspace must be 256-byte aligned
     assert _bwd([4], d=40) == 2
+    assert _bwd([4, 2], sinks=[1, -5]) == 1
 
 
 def test_workspace_sizes():
@@ -110,23 +117,26 @@ def test_bwd_step_validation():
     w = np.array([4, 0], dtype=np.int32)
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     need = aah.workspace_size(1, 2, 64, 64, "bf16")
-    assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need,
                                  None) == 1
     w[1] = 3
-    # aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, B, H, T, d, dt, scale, dq, workspace, bytes, stream)
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, 0, FAKE, need,
+    bad = np.array([0, -1], dtype=np.int32)
+    assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need, None) == 1   # sink < 0
+    # aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, T, d, dt, scale, dq, workspace, bytes, stream)
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, 0, FAKE, need,
                                None) == 1                                                      # NULL dq
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8,
                                None) == 3                                                      # small ws
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, need,
                                None) == 2                                                      # d = 48
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 0, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 0, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
                                None) == 1                                                      # NULL lse
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, 0, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, 0, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
                                None) == 1                                                      # NULL o
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, 0.0, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.0, FAKE, FAKE, need,
                                None) == 1                                                      # scale 0
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, 1, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
                                need, None) == 1                                                # scale inf
 
 
@@ -152,9 +162,20 @@ def test_window_stats_match_oracle(T, windows):
     assert abs(acr - oracle.acr_ref(windows, T)) < 1e-15
 
 
+@pytest.mark.parametrize("T,windows,sinks", [(4096, [256, 256, 4096, 1024], [128, 0, 128, 3000]),
+                                             (300, [1, 7, 299, 300], [1, 300, 2, 5]), (5, [1, 2], [9, 1])])
+def test_window_stats_with_sinks_match_oracle(T, windows, sinks):
+    pairs, acr = aah.window_stats(windows, T, sinks=sinks)
+    assert pairs == sum(oracle.pair_count_ref(T, w, s) for w, s in zip(windows, sinks))
+    assert abs(acr - oracle.acr_ref(windows, T)) < 1e-15
+
+
 def test_window_stats_rejects_bad_window():
     with pytest.raises(aah.AahError) as e:
         aah.window_stats([3, 0], 16)
+    assert e.value.status == 1
+    with pytest.raises(aah.AahError) as e:
+        aah.window_stats([3, 4], 16, sinks=[0, -2])
     assert e.value.status == 1
 
 
@@ -162,7 +183,7 @@ def test_plan_capacity_reporting():
     lib = _lib.lib()
     w = np.array([5, 9], dtype=np.int32)
     n = ctypes.c_int64()
-    st = lib.aah_plan_fwd(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 2, 100, 16, 16, 8, None, 0,
+    st = lib.aah_plan_fwd(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 2, 2, 100, 16, 16, 8, None, 0,
                           ctypes.byref(n))
     assert st == 1 and n.value >= 2 * 2 * 7
 

@@ -113,3 +113,86 @@ def test_emulated_backward_equals_oracle(B, H, T, windows, qt_, kt_, nq):
     rq, rk, rv = oracle.attn_bwd_ref(q, k, v, windows, 0.4, do)
     for a, r in ((dq, rq), (dk, rk), (dv, rv)):
         np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
+
+
+SINK_CASES = [
+    # (B, H, T, windows, sinks, q_tile, kv_tile, n_queues)
+    (1, 4, 256, [16, 32, 64, 256], [8, 40, 0, 100], 64, 64, 8),
+    (2, 3, 100, [1, 7, 1000], [1, 30, 5], 16, 8, 8),
+    (1, 5, 37, [1, 2, 5, 36, 37], [36, 3, 9, 1, 2], 8, 16, 3),
+    (1, 2, 300, [20, 128], [128, 17], 32, 64, 8),
+]
+
+
+def _eff_sink(s, w, T):
+    return max(0, min(s, T - min(w, T)))
+
+
+@pytest.mark.parametrize("B,H,T,windows,sinks,qt_,kt_,nq", SINK_CASES)
+def test_forward_plan_with_sinks(B, H, T, windows, sinks, qt_, kt_, nq):
+    """The listed window range plus the implied sink tiles [0, min(ceil(S / kv), lo)) are exactly
+    the key tiles the rows see (brute force over the visibility rule)."""
+    items = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks)
+    real = items[items[:, 0] >= 0]
+    assert len({(int(bh), int(t)) for bh, t, _, _ in real}) == len(real) == B * H * -(-T // qt_)
+    # the window ranges do not depend on the sinks
+    plain = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq)
+    assert {tuple(x) for x in plain[plain[:, 0] >= 0]} == {tuple(x) for x in real}
+    for bh, t, lo, hi in real:
+        h = bh % H
+        W, S = min(windows[h], T), _eff_sink(sinks[h], windows[h], T)
+        needed = set()
+        for i in range(t * qt_, min(T, (t + 1) * qt_)):
+            for j in range(i + 1):
+                if j > i - W or j < sinks[h]:
+                    needed.add(j // kt_)
+        n_sink = min(-(-S // kt_), lo)
+        assert needed == set(range(n_sink)) | set(range(lo, hi))
+    for qi in range(nq):    # queues sorted by visited tiles, sink tiles included
+        costs = [hi - lo + min(-(-_eff_sink(sinks[bh % H], windows[bh % H], T) // kt_), lo)
+                 for bh, _, lo, hi in items[qi::nq] if bh >= 0]
+        assert costs == sorted(costs, reverse=True)
+
+
+@pytest.mark.parametrize("B,H,T,windows,sinks,qt_,kt_,nq", SINK_CASES)
+def test_backward_plan_with_sinks(B, H, T, windows, sinks, qt_, kt_, nq):
+    items = aah.plan_bwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks)
+    real = items[items[:, 0] >= 0]
+    assert len({(int(bh), int(t)) for bh, t, _, _ in real}) == len(real) == B * H * -(-T // kt_)
+    for bh, t, lo, hi in real:
+        h = bh % H
+        W = min(windows[h], T)
+        needed = set()
+        for j in range(t * kt_, min(T, (t + 1) * kt_)):
+            for i in range(j, T):
+                if j > i - W or j < sinks[h]:
+                    needed.add(i // qt_)
+        assert needed == set(range(lo, hi))
+
+
+@pytest.mark.parametrize("B,H,T,windows,sinks,qt_,kt_,nq", SINK_CASES)
+def test_emulated_forward_with_sinks_equals_oracle(B, H, T, windows, sinks, qt_, kt_, nq):
+    rng = np.random.default_rng(23)
+    q, k, v = (rng.standard_normal((B, H, T, 8)) for _ in range(3))
+    items = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks)
+    O, L = emulate_forward(items, q, k, v, windows, 0.4, qt_, kt_, sinks=sinks)
+    Or, Lr = oracle.attn_fwd_ref(q, k, v, windows, 0.4, sinks=sinks)
+    np.testing.assert_allclose(O, Or, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lr, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("B,H,T,windows,sinks,qt_,kt_,nq", SINK_CASES)
+def test_emulated_backward_with_sinks_equals_oracle(B, H, T, windows, sinks, qt_, kt_, nq):
+    rng = np.random.default_rng(24)
+    q, k, v, do = (rng.standard_normal((B, H, T, 8)) for _ in range(4))
+    _, L = oracle.attn_fwd_ref(q, k, v, windows, 0.4, sinks=sinks)
+    items = aah.plan_bwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks)
+    dq, dk, dv = emulate_backward(items, q, k, v, do, L, windows, 0.4, qt_, kt_, sinks=sinks)
+    rq, rk, rv = oracle.attn_bwd_ref(q, k, v, windows, 0.4, do, sinks=sinks)
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
+
+
+def test_plan_rejects_negative_sinks():
+    with pytest.raises(aah.AahError):
+        aah.plan_fwd([3, 4], 1, 2, 16, 8, 8, sinks=[0, -1])
