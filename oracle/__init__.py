@@ -19,6 +19,12 @@ from .attention import (  # noqa: F401
     acr_ref,
     acr_from_fractions_ref,
 )
+from .features import (  # noqa: F401
+    N_FEATURES,
+    attn_row_stats_ref,
+    head_features_ref,
+    features_ema_ref,
+)
 from .decode import (  # noqa: F401
     cache_rows_ref,
     decode_positions,

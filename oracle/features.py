@@ -1,0 +1,82 @@
+"""fp64 reference of the per-head controller features and their EMA.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: "Asymmetric Attention Heads" (AAH), section 5.3 (Head features and EMA
+smoothing).  Each head h gets a base feature
+    x_h = [mu(|q_h|), sigma(q_h), mu(|k_h|), sigma(k_h), mu(|v_h|), sigma(v_h), e_h, n_h, rho_h],
+where the Q/K/V entries are scalar reductions over the batch, sequence and
+per-head feature axes of that head (mu(|.|) is the mean ABSOLUTE activation,
+not the absolute value of the mean), and e_h, n_h, rho_h are the previous
+attention diagnostics: entropy, output norm and usage.  The features are
+smoothed as xbar_t = alpha xbar_{t-1} + (1 - alpha) x_t, with xbar_0 = x_0 at the
+first control update; missing diagnostics are zero.
+
+Readings where the page is silent (each listed in the design notes):
+  * sigma is the population standard deviation (divide by the count N); with
+    N = B T d of the order of 10^6 the unbiased form differs by 1/(2N) relative;
+  * e_h is the mean over batch entries and query rows of the row's attention
+    entropy -sum_j p_ij ln p_ij (natural log) over its visible keys;
+  * n_h is the mean over batch entries and query rows of the Euclidean norm of
+    the head's output row O_i;
+  * rho_h, the usage, is the fraction of the context the head's window covers,
+    min(W_h, T) / T: the head's term of the coverage ratio of section 5.10,
+    matching the pages' window-branch usage (Table 6 caption).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import _head_probs, _sink
+
+N_FEATURES = 9
+
+
+def attn_row_stats_ref(q, k, v, windows, scale, sinks=None):
+    """Per query row of every (b, h): (entropy [B,H,T], output norm [B,H,T]) in float64.
+
+    entropy_i = -sum_j p_ij ln p_ij over the row's visible keys (masked weights
+    are exactly zero and contribute nothing); norm_i = ||sum_j p_ij v_j||_2."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, H, T, _ = q.shape
+    ent = np.empty((B, H, T))
+    nrm = np.empty((B, H, T))
+    for b in range(B):
+        for h in range(H):
+            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
+            with np.errstate(divide="ignore", invalid="ignore"):
+                plogp = np.where(P > 0, P * np.log(P), 0.0)
+            ent[b, h] = -plogp.sum(axis=1)
+            nrm[b, h] = np.linalg.norm(P @ v[b, h], axis=1)
+    return ent, nrm
+
+
+def _mean_abs_std(x_h):
+    x_h = np.asarray(x_h, dtype=np.float64).ravel()
+    mu = x_h.mean()
+    return np.abs(x_h).mean(), np.sqrt(((x_h - mu) ** 2).mean())
+
+
+def head_features_ref(q, k, v, windows, row_entropy=None, row_norm=None):
+    """Base features x [H, 9] (section 5.3) from Q/K/V [B,H,T,d] and, if given, the
+    per-row diagnostics of the most recent forward pass ([B,H,T] each; None = zero)."""
+    q = np.asarray(q, dtype=np.float64)
+    B, H, T, _ = q.shape
+    x = np.zeros((H, N_FEATURES))
+    for h in range(H):
+        for slot, t in enumerate((q, k, v)):
+            x[h, 2 * slot], x[h, 2 * slot + 1] = _mean_abs_std(np.asarray(t)[:, h])
+        x[h, 6] = 0.0 if row_entropy is None else np.asarray(row_entropy, dtype=np.float64)[:, h].mean()
+        x[h, 7] = 0.0 if row_norm is None else np.asarray(row_norm, dtype=np.float64)[:, h].mean()
+        x[h, 8] = min(int(windows[h]), T) / T
+    return x
+
+
+def features_ema_ref(xbar_prev, x, alpha, init):
+    """xbar_t = alpha xbar_{t-1} + (1 - alpha) x_t; the first update (init) takes x_t itself."""
+    x = np.asarray(x, dtype=np.float64)
+    if init:
+        return x.copy()
+    return alpha * np.asarray(xbar_prev, dtype=np.float64) + (1.0 - alpha) * x
