@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a device-to-device copy of a known size (to scale HBM byte counters)")
+    ap.add_argument("--diag", action="store_true",
+                    help="time a control-update forward: the forward with per-row entropy and output norm, "
+                         "then the per-head features and their EMA (prints its own JSON line)")
     ap.add_argument("--decode", action="store_true",
                     help="time one decoding step over the trimmed per-head caches of the workload's layer "
                          "(a separate measurement; prints its own JSON line)")
@@ -135,6 +138,80 @@ def bench_decode(args, wl):
                      "algorithmic_bytes_per_launch": int(alg)},
     }
     print(json.dumps(out))
+
+
+def bench_diag(args, wl):
+    """Controller diagnostics (AAH section 5.3) on a control-update step: the diagnostic forward (same O and
+    LSE as the plain forward, plus per-row entropy and output norm) and the head-features call (Q/K/V
+    statistics, means of the rows, EMA).  The features call is HBM-bound: its algorithmic bytes are Q, K, V
+    read once, the two row arrays read once, and the features / EMA written."""
+    import torch
+    import head_causal_local_amd as aah
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    q, k, v = to_dev(wl, "q"), to_dev(wl, "k"), to_dev(wl, "v")
+    o = torch.empty_like(q)
+    lse, ent, nrm = (torch.empty((B, H, T), dtype=torch.float32, device="cuda") for _ in range(3))
+    feats = torch.empty((H, aah.N_FEATURES), dtype=torch.float32, device="cuda")
+    ema = torch.zeros_like(feats)
+    ws = torch.empty(aah.head_features_workspace_size(B, H, T, d), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        aah.attn_fwd(q, k, v, wl.windows, wl.scale, out=o, lse=lse, stream=stream, sinks=wl.sinks)
+        mark(1)
+        aah.attn_fwd_diag(q, k, v, wl.windows, wl.scale, out=o, lse=lse, row_entropy=ent, row_onorm=nrm,
+                          stream=stream, sinks=wl.sinks)
+        mark(2)
+        aah.head_features(q, k, v, wl.windows, ent, nrm, features_ema=ema, alpha=0.9, out=feats, workspace=ws,
+                          stream=stream)
+        mark(3)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def span(a, b):
+        return float(np.mean([e[a].elapsed_time(e[b]) for e in events]))
+
+    fwd_ms, diag_ms, feat_ms = span(0, 1), span(1, 2), span(2, 3)
+    chunks = -(-(T * d) // 32768)
+    alg = 3 * B * H * T * d * 2 + 2 * B * H * T * 4 + 3 * H * 9 * 4 + 2 * 3 * H * B * chunks * 32
+    gbs = alg / (feat_ms * 1e-3) / 1e9
+    pairs_b, _ = aah.window_stats(wl.windows, T, sinks=wl.sinks)
+    out = {
+        "metric": "control-update diagnostics: head-features call, algorithmic HBM bytes / time",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (N(0,1) bf16 Q/K/V, seed 0)",
+        "config": {"workload": wl.name + " control-update forward + head features", "B": B, "H": H, "T": T, "d": d,
+                   "fwd_ms": round(fwd_ms, 4), "fwd_diag_ms": round(diag_ms, 4),
+                   "diag_overhead_pct": round(100 * (diag_ms / fwd_ms - 1), 2),
+                   "fwd_diag_tflops": round(4 * d * B * pairs_b / (diag_ms * 1e-3) / 1e12, 2),
+                   "features_us": round(feat_ms * 1e3, 2), "algorithmic_bytes_features": int(alg)},
+        "roofline": {"kernel": "head features (qkv_stats_kernel + features_kernel)", "bound": "hbm",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(feat_ms * 1e3, 2), "algorithmic_bytes_per_launch": int(alg)},
+    }
+    print(json.dumps(out), flush=True)
 
 
 COPY_BYTES = 512 * 1024 * 1024
@@ -248,6 +325,9 @@ def main():
         sys.exit(2)
     if args.decode:
         bench_decode(args, wl)
+        return
+    if args.diag:
+        bench_diag(args, wl)
         return
     with_bwd = (wl.do is not None) and not args.fwd_only
     B, H, T, d = wl.B, wl.H, wl.T, wl.d

@@ -18,7 +18,7 @@ import numpy as np
 
 from ._lib import (AAH_BF16, AAH_F32, AahError, EXPORTS, LIB_PATH, WorkItem, check, lib)  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "kv_cache_fill", "kv_cache_rows",
+__all__ = ["attn_fwd", "attn_fwd_diag", "head_features", "head_features_workspace_size", "N_FEATURES", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "kv_cache_fill", "kv_cache_rows",
            "decode_workspace_size", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
            "cache_clear", "AahError", "LIB_PATH"]
 
@@ -106,6 +106,79 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
                             _stream_ptr(q, stream))
     check(st)
     return out, lse
+
+
+def attn_fwd_diag(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, row_entropy=None,
+                  row_onorm=None, stream=None, sinks=None):
+    """attn_fwd plus the per-row attention entropy and output norm (float32 [B, H, T] each).
+
+    Returns (O, LSE, row_entropy, row_onorm)."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_operand(name, t, q)
+    B, H, T, d = q.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = torch.empty_like(q) if out is None else out
+    _check_operand("out", out, q)
+    rows = []
+    for name, t in (("lse", lse), ("row_entropy", row_entropy), ("row_onorm", row_onorm)):
+        if t is None:
+            t = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        elif t.shape != (B, H, T) or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, T] tensor")
+        rows.append(t)
+    lse, row_entropy, row_onorm = rows
+    sk = _sinks_arg(sinks, H)
+    check(lib().aah_attn_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d,
+                                  _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(),
+                                  row_entropy.data_ptr(), row_onorm.data_ptr(), _stream_ptr(q, stream)))
+    return out, lse, row_entropy, row_onorm
+
+
+N_FEATURES = 9
+
+
+def head_features_workspace_size(B: int, H: int, T: int, d: int) -> int:
+    return int(lib().aah_head_features_workspace_size(B, H, T, d))
+
+
+def head_features(q, k, v, windows, row_entropy=None, row_onorm=None, features_ema=None, alpha: float = 0.9,
+                  init: bool = False, out=None, workspace=None, stream=None):
+    """Per-head controller features x [H, 9] (float32) of q, k, v [B, H, T, d] and the diagnostic rows of
+    attn_fwd_diag (None: entropy and norm features are 0); if features_ema ([H, 9] float32) is given it is
+    updated in place: init ? x : alpha * ema + (1 - alpha) * x.  Returns x."""
+    import torch
+    for name, t in (("k", k), ("v", v)):
+        _check_operand(name, t, q)
+    B, H, T, d = q.shape
+    w = _windows_arg(windows)
+    if w.shape[0] != H:
+        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
+    if (row_entropy is None) != (row_onorm is None):
+        raise ValueError("give both row_entropy and row_onorm, or neither")
+    for name, t in (("row_entropy", row_entropy), ("row_onorm", row_onorm)):
+        if t is not None and (t.shape != (B, H, T) or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [B, H, T] tensor")
+    out = torch.empty((H, N_FEATURES), dtype=torch.float32, device=q.device) if out is None else out
+    for name, t in (("out", out), ("features_ema", features_ema)):
+        if t is not None and (t.shape != (H, N_FEATURES) or t.dtype != torch.float32 or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous float32 [H, {N_FEATURES}] tensor")
+    if workspace is None:
+        workspace = torch.empty(max(head_features_workspace_size(B, H, T, d), 1), dtype=torch.uint8,
+                                device=q.device)
+    ptr, nbytes = _ws(workspace)
+    check(lib().aah_head_features(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  None if row_entropy is None else row_entropy.data_ptr(),
+                                  None if row_onorm is None else row_onorm.data_ptr(), _wptr(w), B, H, T, d,
+                                  _dtype_code(q), float(alpha), 1 if init else 0, out.data_ptr(),
+                                  None if features_ema is None else features_ema.data_ptr(), ptr, nbytes,
+                                  _stream_ptr(q, stream)))
+    return out
 
 
 def workspace_size(B: int, H: int, T: int, d: int, dtype: str = "bf16", is_bwd: bool = True) -> int:

@@ -352,12 +352,14 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
   return AAH_OK;
 }
 
-aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks,
-                        int B, int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
-                        size_t workspace_bytes, aah_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
-  g_detail.clear();
+}  // extern "C"
+
+namespace {
+
+// Forward, with the per-row diagnostics when ent / onorm are set (both or neither).
+aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks, int B,
+                    int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, float* ent, float* onorm,
+                    aah_stream_t stream) {
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
@@ -374,12 +376,82 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dt == AAH_BF16)
-    e = aah::launch_fwd_bf16(q, k, v, o, lse, plan.items, plan.n_items, plan.win, plan.sink, s, st);
+    e = aah::launch_fwd_bf16(q, k, v, o, lse, ent, onorm, plan.items, plan.n_items, plan.win, plan.sink, s, st);
   else
     e = aah::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
-                            static_cast<const float*>(v), static_cast<float*>(o), lse, plan.items, plan.n_items,
-                            plan.win, plan.sink, s, st);
+                            static_cast<const float*>(v), static_cast<float*>(o), lse, ent, onorm, plan.items,
+                            plan.n_items, plan.win, plan.sink, s, st);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return AAH_OK;
+}
+
+size_t features_workspace(int B, int H, int T, int d) {
+  return round_up(static_cast<size_t>(3) * H * B * aah::feature_chunks(T, d) * 4 * sizeof(double), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks,
+                        int B, int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, aah_stream_t stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  g_detail.clear();
+  return fwd_impl(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, nullptr, nullptr, stream);
+}
+
+aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
+                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* o,
+                             float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
+  AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
+  return fwd_impl(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream);
+}
+
+size_t aah_head_features_workspace_size(int B, int H, int T, int d) {
+  if (B < 1 || H < 1 || T < 1 || !supported_d(d)) return 0;
+  return features_workspace(B, H, T, d);
+}
+
+aah_status aah_head_features(const void* q, const void* k, const void* v, const float* row_entropy,
+                             const float* row_onorm, const int32_t* windows, int B, int H, int T, int d,
+                             aah_dtype dt, float alpha, int init, float* features, float* features_ema,
+                             void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+  g_detail.clear();
+  AAH_TRY(check_shape(windows, nullptr, B, H, T, d, dt));
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k, "k", 16));
+  AAH_TRY(check_tensor(v, "v", 16));
+  if ((row_entropy == nullptr) != (row_onorm == nullptr))
+    return fail(AAH_ERR_INVALID_ARG, "row_entropy and row_onorm must both be given or both be NULL");
+  if (row_entropy != nullptr) {
+    AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
+    AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
+  }
+  if (features == nullptr && features_ema == nullptr)
+    return fail(AAH_ERR_INVALID_ARG, "features and features_ema are both NULL: nothing to write");
+  if (features != nullptr) AAH_TRY(check_tensor(features, "features", 4));
+  if (features_ema != nullptr) AAH_TRY(check_tensor(features_ema, "features_ema", 4));
+  if (!(alpha >= 0.0f && alpha <= 1.0f)) return fail(AAH_ERR_INVALID_ARG, "alpha must be in [0, 1]");
+  const size_t need = features_workspace(B, H, T, d);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
+                need);
+  if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+  if (static_cast<int64_t>(B) * H * aah::feature_chunks(T, d) > INT32_MAX)
+    return fail(AAH_ERR_UNSUPPORTED, "too many statistics workgroups");
+  // The effective windows (usage = min(W, T) / T) come from the cached forward work list's table.
+  int row = 0, col = 0;
+  fwd_tiles(dt, &row, &col);
+  DevicePlan plan;
+  AAH_TRY(get_plan(kPlanFwd, windows, nullptr, B, H, T, row, col, &plan));
+  const hipError_t e = aah::launch_head_features(q, k, v, dt == AAH_BF16, row_entropy, row_onorm, plan.win, B, H, T,
+                                                 d, alpha, init != 0, features, features_ema,
+                                                 static_cast<double*>(workspace), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "head features launch");
   return AAH_OK;
 }
 

@@ -50,6 +50,17 @@
 // window, so only j < S decides), then the window tiles as usual; its
 // trailing-edge mask spares keys below S, and blocks of sink keys are never
 // skipped.  Without sinks the SINK = false instantiation runs, unchanged.
+//
+// Diagnostics ("Asymmetric Attention Heads" section 5.3: the controller's head
+// features include the attention entropy and the output norm).  The DIAG
+// instantiation also writes, per query row, the entropy -sum_j p_j ln p_j of
+// its attention weights and the Euclidean norm of its output row, from values
+// the kernel already has: with w_j the bf16 weights that enter the row sum l
+// and x_j = s_j c - m their log2 offsets from the reference m, the entropy is
+// ln 2 (log2 l - sum_j w_j x_j / l).  The sum follows the reference like l does
+// (when m moves by -delta, a becomes alpha (a + delta l)).  Using the rounded
+// weights for both sums makes the result the cross entropy of the normalised
+// rounded weights against the exact ones, within 2^-7 H + 2^-8 of the exact H.
 #include <cmath>
 
 #include "device_common.hpp"
@@ -85,10 +96,11 @@ struct Cfg {
 // Key offset (within its 32-key block, before the 4 hl lane offset) held by S^T register r.
 __device__ constexpr int reg_key(int r) { return 8 * (r >> 2) + (r & 3); }
 
-template <int D, bool SINK>
+template <int D, bool SINK, bool DIAG>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D>::kWavesPerSimd)))
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
-                     bf16* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
+                     bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ENT,
+                     float* __restrict__ ONORM, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T,
                      float c) {
   using C = Cfg<D>;
@@ -146,6 +158,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   float m_run = -INFINITY;  // reference max of this lane's row (log2 domain)
   float m_use = 0.f;        // m_run, or 0 while the row has seen no visible key (then every p is 0)
   float l_run = 0.f;        // this half-wave's running sum of the bf16 weights
+  float a_run = 0.f;        // DIAG: this half-wave's sum of those weights times their offsets x = s c - m_run
   bool ready = false;       // every row of the wave has a reference
 
   // DMA sources: instruction j of this wave fills tile chunks P = (wave * kDmaPerWave + j) * 64 + lane,
@@ -232,23 +245,33 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     // part = this lane's sum of exactly the bf16 weights that enter P V.
     bf16x8 pf[2];
     float part;
+    float apart = 0.f;  // DIAG: sum of the lane's weights times their offsets
     auto make_p = [&]() __attribute__((always_inline)) {
-      float pa = 0.f, pb = 0.f;
+      float pa = 0.f, pb = 0.f, ea = 0.f;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           bf16x2 pp;
-          pp[0] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e], c, -m_use)));
-          pp[1] = static_cast<bf16>(__builtin_amdgcn_exp2f(fmaf(s[8 * h + e + 1], c, -m_use)));
+          const float x0 = fmaf(s[8 * h + e], c, -m_use);
+          const float x1 = fmaf(s[8 * h + e + 1], c, -m_use);
+          pp[0] = static_cast<bf16>(__builtin_amdgcn_exp2f(x0));
+          pp[1] = static_cast<bf16>(__builtin_amdgcn_exp2f(x1));
           if (e & 2)
             pb = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pb, false);
           else
             pa = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, pa, false);
+          if constexpr (DIAG) {
+            // A masked score gives x = -inf with weight 0: clamp x (exp2 of anything below -150
+            // is 0 in fp32 anyway) so that the product stays 0.
+            ea = fmaf(static_cast<float>(pp[0]), fmaxf(x0, -256.f), ea);
+            ea = fmaf(static_cast<float>(pp[1]), fmaxf(x1, -256.f), ea);
+          }
           pf[h][e] = pp[0];
           pf[h][e + 1] = pp[1];
         }
       part = pa + pb;
+      if constexpr (DIAG) apart = ea;
     };
 
     // Lazy reference: the weights are formed against the current reference
@@ -268,6 +291,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       if (m_new > m_run) {
         // m_run = -inf (nothing seen yet): alpha = 0 clears the still-empty state.
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        if constexpr (DIAG) a_run = m_run == -INFINITY ? 0.f : alpha * fmaf(m_run - m_new, l_run, a_run);
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
@@ -278,6 +302,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       make_p();
     }
     l_run += part;
+    if constexpr (DIAG) a_run += apart;
 
     // O^T += V^T P^T over the block's two 16-key steps.
 #pragma unroll
@@ -322,6 +347,16 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
   if (!wave_active) return;
   const float l_tot = half_swap_sum(l_run);
+  float a_tot = 0.f, sq_tot = 0.f;
+  if constexpr (DIAG) {
+    a_tot = half_swap_sum(a_run);
+    float sq = 0.f;  // this lane's share of |O row|^2 (before the division by l)
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sq = fmaf(acc[b][r], acc[b][r], sq);
+    sq_tot = half_swap_sum(sq);
+  }
   if (!row_ok) return;
   const float inv = 1.f / l_tot;
   bf16* Orow = O + base + static_cast<size_t>(qi) * D;
@@ -332,34 +367,51 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     for (int i = 0; i < 4; ++i)
       store_bf16x4(Orow + 32 * b + 8 * i + 4 * hl, acc[b][4 * i] * inv, acc[b][4 * i + 1] * inv,
                    acc[b][4 * i + 2] * inv, acc[b][4 * i + 3] * inv);
-  if (hl == 0) LSE[static_cast<size_t>(it.bh) * T + qi] = (m_run + log2f(l_tot)) * kLn2;
+  if (hl == 0) {
+    const size_t row = static_cast<size_t>(it.bh) * T + qi;
+    LSE[row] = (m_run + log2f(l_tot)) * kLn2;
+    if constexpr (DIAG) {
+      ENT[row] = (log2f(l_tot) - a_tot * inv) * kLn2;
+      ONORM[row] = sqrtf(sq_tot) * inv;
+    }
+  }
+}
+
+template <int D, bool SINK, bool DIAG>
+void launch_k(const void* q, const void* k, const void* v, void* o, float* lse, float* ent, float* onorm,
+              const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
+              const AttnShape& s, hipStream_t stream) {
+  const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, SINK, DIAG>), dim3(n_items), dim3(kThreads), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.T, c);
 }
 
 template <int D>
-hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse,
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, float* ent, float* onorm,
                     const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                     const AttnShape& s, hipStream_t stream) {
-  const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
-  if (sink_eff != nullptr)
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), dim3(n_items), dim3(kThreads), 0, stream,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                       static_cast<bf16*>(o), lse, items, win_eff, sink_eff, s.H, s.T, c);
+  const bool sink = sink_eff != nullptr, diag = ent != nullptr;
+  if (sink && diag)
+    launch_k<D, true, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+  else if (sink)
+    launch_k<D, true, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+  else if (diag)
+    launch_k<D, false, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
   else
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), dim3(n_items), dim3(kThreads), 0, stream,
-                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                       static_cast<bf16*>(o), lse, items, win_eff, sink_eff, s.H, s.T, c);
+    launch_k<D, false, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                           const AttnShape& s, hipStream_t stream) {
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ent,
+                           float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
+                           const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return launch_d<32>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
-    case 64: return launch_d<64>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
-    case 128: return launch_d<128>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 32: return launch_d<32>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return launch_d<64>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return launch_d<128>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -30,15 +30,17 @@ struct AttnShape {
   float scale;          // softmax scale applied to q . k
 };
 
-// bf16 forward on MFMA (d in {32, 64, 128}).
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                           const AttnShape& s, hipStream_t stream);
+// bf16 forward on MFMA (d in {32, 64, 128}).  ent / onorm: nullptr, or fp32
+// [B,H,T] outputs of each row's attention entropy and output-row norm (both set
+// or both null).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ent,
+                           float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
+                           const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 
-// Scalar forward for fp32 (d in {32, 64, 128}).
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                          const AttnShape& s, hipStream_t stream);
+// Scalar forward for fp32 (d in {32, 64, 128}); ent / onorm as for bf16.
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, float* ent,
+                          float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 
 // Per row: nd = -(dO . O) and nl2 = -lse log2(e), in fp32.  is_bf16 selects the
 // element type of o / dout.
@@ -67,6 +69,25 @@ hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v
                                   const float* nl2, const float* nd, float* dk, float* dv,
                                   const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
                                   const AttnShape& s, hipStream_t stream);
+
+// ---- per-head controller features
+constexpr int kNumFeatures = 9;      // [mu|q|, sigma q, mu|k|, sigma k, mu|v|, sigma v, entropy, out norm, usage]
+constexpr int kFeatureSpan = 32768;  // elements of one (b, h) slice per statistics workgroup
+
+// Statistics workgroups per (b, h) slice of T * d elements.
+inline int feature_chunks(int T, int d) {
+  const int64_t n = static_cast<int64_t>(T) * d;
+  return static_cast<int>((n + kFeatureSpan - 1) / kFeatureSpan);
+}
+
+// Writes features [H, 9] (if non-null) and updates ema [H, 9] (if non-null;
+// ema = x when init) from q, k, v [B,H,T,d] (bf16 or fp32) and the per-row
+// entropy / output norm [B,H,T] (nullptr: those features are 0).  partials:
+// 3 * H * B * feature_chunks(T, d) * 4 doubles of scratch.
+hipError_t launch_head_features(const void* q, const void* k, const void* v, bool is_bf16, const float* ent,
+                                const float* onorm, const int32_t* win_eff, int B, int H, int T, int d,
+                                float alpha, bool init, float* features, float* ema, double* partials,
+                                hipStream_t stream);
 
 // ---- decoding over per-head trimmed K/V caches (bf16)
 constexpr int kDecodeRows = 256;  // ring rows per decode workgroup

@@ -15,6 +15,11 @@
 // visible to every query i >= j when j < S; items then visit the sink tiles
 // before their window tiles (forward and dQ), and dK/dV items of sink keys
 // run to the last query tile (the planner's range).
+// With ENT / ONORM set, the fp32 forward also writes each row's attention
+// entropy -sum_j p_j ln p_j and the Euclidean norm of its output row
+// ("Asymmetric Attention Heads" section 5.3 diagnostics): entropy =
+// ln 2 (log2 l - a / l) with a = sum_j w_j (s_j - m), kept against the running
+// max like l.
 #include <cmath>
 
 #include "kernels.hpp"
@@ -56,8 +61,9 @@ __device__ inline void stage_rows(float* dst, const E* src, int r0, int T) {
 template <int D>
 __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T, float c) {
+    float* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ENT, float* __restrict__ ONORM,
+    const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff,
+    int H, int T, float c) {
   __shared__ float ks[kCols * D];
   __shared__ float vs[kCols * D];
   const WorkItem it = items[blockIdx.x];
@@ -76,6 +82,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     acc[x] = 0.f;
   }
   float m = -INFINITY, l = 0.f;  // log2-domain running max and running sum
+  float a = 0.f;                 // sum of the weights times their offsets from the max (entropy)
+  const bool diag = ENT != nullptr;
 
   for (int v = 0; v < ns + it.hi - it.lo; ++v) {
     const int k0 = (v < ns ? v : v - ns + it.lo) * kCols;
@@ -99,12 +107,14 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
       const float m_new = fmaxf(m, mx);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2f(m - m_use);
+      if (diag) a = m == -INFINITY ? 0.f : alpha * fmaf(m - m_use, l, a);
       l *= alpha;
 #pragma unroll
       for (int x = 0; x < D; ++x) acc[x] *= alpha;
 #pragma unroll
       for (int j = 0; j < kChunk; ++j) {
         const float p = exp2f(s[j] - m_use);
+        if (diag && p > 0.f) a = fmaf(p, s[j] - m_use, a);
         l += p;
 #pragma unroll
         for (int x = 0; x < D; ++x) acc[x] = fmaf(p, vs[(j0 + j) * D + x], acc[x]);
@@ -114,9 +124,18 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
   }
   if (!row_ok) return;
   const float inv = 1.f / l;
+  float sq = 0.f;
 #pragma unroll
-  for (int x = 0; x < D; ++x) O[base + static_cast<size_t>(qi) * D + x] = acc[x] * inv;
-  LSE[static_cast<size_t>(it.bh) * T + qi] = (m + log2f(l)) * kLn2;
+  for (int x = 0; x < D; ++x) {
+    O[base + static_cast<size_t>(qi) * D + x] = acc[x] * inv;
+    sq = fmaf(acc[x] * inv, acc[x] * inv, sq);
+  }
+  const size_t row = static_cast<size_t>(it.bh) * T + qi;
+  LSE[row] = (m + log2f(l)) * kLn2;
+  if (diag) {
+    ENT[row] = (log2f(l) - a * inv) * kLn2;
+    ONORM[row] = sqrtf(sq);
+  }
 }
 
 // ---------------------------------------------------------------- backward preprocess
@@ -275,10 +294,10 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
 }
 
 template <int D>
-hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, float* lse,
-                     const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                     const AttnShape& s, hipStream_t stream) {
-  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(n_items), dim3(kRows), 0, stream, q, k, v, o, lse, items,
+hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, float* lse, float* ent,
+                     float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
+                     const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+  hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(n_items), dim3(kRows), 0, stream, q, k, v, o, lse, ent, onorm, items,
                      win_eff, sink_eff, s.H, s.T, s.scale * kLog2e);
   return hipGetLastError();
 }
@@ -297,13 +316,13 @@ hipError_t pre_d(const void* o, const void* dout, const float* lse, float* nl2, 
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                          const AttnShape& s, hipStream_t stream) {
+hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, float* ent,
+                          float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
+                          const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
   switch (s.d) {
-    case 32: return fwd_f32_d<32>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
-    case 64: return fwd_f32_d<64>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
-    case 128: return fwd_f32_d<128>(q, k, v, o, lse, items, n_items, win_eff, sink_eff, s, stream);
+    case 32: return fwd_f32_d<32>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    case 64: return fwd_f32_d<64>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    case 128: return fwd_f32_d<128>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -109,6 +109,44 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
                         aah_stream_t stream);
 
 /*
+ * Forward pass with the attention diagnostics of "Asymmetric Attention Heads"
+ * section 5.3 (the controller's head features include the attention entropy
+ * and the output norm, taken from the most recent attention statistics).
+ * Does exactly what aah_attn_fwd does (same o and lse) and also writes, for
+ * every query row, row_entropy[b,h,i] = -sum_j p_ij ln p_ij over the row's
+ * visible keys and row_onorm[b,h,i] = ||o_i||_2 (of the fp32 output before its
+ * rounding to dt), both fp32 [B,H,T] device arrays, 4-byte aligned.  In bf16
+ * the entropy is formed from the same rounded weights as lse: it is within
+ * 2^-7 H + 2^-8 of the exact H.
+ */
+aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
+                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* o,
+                             float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream);
+
+/*
+ * Per-head controller features ("Asymmetric Attention Heads" section 5.3):
+ *   x_h = [mu(|q_h|), sigma(q_h), mu(|k_h|), sigma(k_h), mu(|v_h|), sigma(v_h), e_h, n_h, rho_h]
+ * mu(|.|) is the mean of the absolute activations and sigma the population
+ * standard deviation, both over batch, sequence and head dimension of head h;
+ * e_h and n_h are the means over batch and rows of row_entropy and row_onorm
+ * (from aah_attn_fwd_diag; pass both NULL when there are none yet: then they
+ * are 0); rho_h = min(W_h, T) / T, the head's window usage.  Writes x to
+ * features (device float[H * 9], row h = x_h; may be NULL) and smooths
+ * features_ema (device float[H * 9], in/out; may be NULL):
+ *   features_ema = init ? x : alpha * features_ema + (1 - alpha) * x,
+ * with 0 <= alpha <= 1 (the pages use 0.9, initialised from the first x).  At
+ * least one of features, features_ema must be given.  q, k, v as for the
+ * forward.  Workspace: aah_head_features_workspace_size(B, H, T, d) bytes,
+ * 256-byte aligned, scratch.  Deterministic: the same inputs give the same bits.
+ */
+size_t aah_head_features_workspace_size(int B, int H, int T, int d);
+
+aah_status aah_head_features(const void* q, const void* k, const void* v, const float* row_entropy,
+                             const float* row_onorm, const int32_t* windows, int B, int H, int T, int d,
+                             aah_dtype dt, float alpha, int init, float* features, float* features_ema,
+                             void* workspace, size_t workspace_bytes, aah_stream_t stream);
+
+/*
  * Backward pass: gradients of sum(O * dout) with respect to q, k and v, given
  * the forward's o and lse (the log-sum-exp saved by aah_attn_fwd with the same
  * scale, windows and sinks).  Writes dq, dk, dv [B,H,T,d] of dtype dt (each element

@@ -22,6 +22,7 @@ from .attention import (  # noqa: F401
 from .features import (  # noqa: F401
     N_FEATURES,
     attn_row_stats_ref,
+    attn_row_stats_rows_ref,
     head_features_ref,
     features_ema_ref,
 )

@@ -53,6 +53,18 @@ def attn_row_stats_ref(q, k, v, windows, scale, sinks=None):
     return ent, nrm
 
 
+def attn_row_stats_rows_ref(q_h, k_h, v_h, w, scale, rows, sink: int = 0):
+    """attn_row_stats_ref restricted to selected query rows of ONE head (arrays [T, d]), so that
+    large inputs can be spot-checked row by row.  Returns (entropy [len(rows)], norm [len(rows)])."""
+    q_h = np.asarray(q_h, dtype=np.float64)
+    k_h = np.asarray(k_h, dtype=np.float64)
+    v_h = np.asarray(v_h, dtype=np.float64)
+    P, _, _ = _head_probs(q_h, k_h, int(w), scale, rows=np.asarray(rows), sink=int(sink))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        plogp = np.where(P > 0, P * np.log(P), 0.0)
+    return -plogp.sum(axis=1), np.linalg.norm(P @ v_h, axis=1)
+
+
 def _mean_abs_std(x_h):
     x_h = np.asarray(x_h, dtype=np.float64).ravel()
     mu = x_h.mean()

@@ -239,3 +239,32 @@ def test_decode_validation():
     assert lib.aah_kv_cache_fill(F, F, wp, 2, 2, 0, 128, 64, 0, F, F, None) == 1     # T = 0
     assert lib.aah_kv_cache_fill(0, F, wp, 2, 2, 64, 128, 64, 0, F, F, None) == 1    # NULL k
     assert lib.aah_kv_cache_fill(F, F, wp, 2, 2, 64, 128, 64, 1, F, F, None) == 2    # fp32
+
+
+def test_diag_and_feature_validation():
+    lib = _lib.lib()
+    w = np.array([4, 9], dtype=np.int32)
+    wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    # aah_attn_fwd_diag(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream)
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, FAKE + 2,
+                                 None) == 1                                     # misaligned
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                 None) == 2                                     # d = 48
+    need = aah.head_features_workspace_size(2, 2, 64, 64)
+    assert need == 256 * -(-(3 * 2 * 2 * 1 * 4 * 8) // 256)                     # one 32768-element span per slice
+    assert aah.head_features_workspace_size(1, 1, 4096, 128) == 256 * -(-(3 * 16 * 4 * 8) // 256)
+    assert aah.head_features_workspace_size(0, 1, 1, 64) == 0
+
+    def feat(ent=FAKE, on=FAKE, feats=FAKE, ema=FAKE, alpha=0.9, ws=FAKE, nbytes=need, d=64):
+        # aah_head_features(q, k, v, row_entropy, row_onorm, windows, B, H, T, d, dt, alpha, init,
+        #                   features, features_ema, workspace, bytes, stream)
+        return lib.aah_head_features(FAKE, FAKE, FAKE, ent, on, wp, 2, 2, 64, d, 0, alpha, 0, feats, ema, ws, nbytes,
+                                     None)
+    assert feat(ent=0) == 1                  # one diagnostic row array without the other
+    assert feat(feats=0, ema=0) == 1         # nothing to write
+    assert feat(alpha=1.5) == 1
+    assert feat(alpha=float("nan")) == 1
+    assert feat(nbytes=need - 8) == 3
+    assert feat(ws=FAKE + 64) == 1           # workspace must be 256-byte aligned
+    assert feat(d=40) == 2

@@ -119,3 +119,14 @@ def test_ema_closed_forms():
         xbar = oracle.features_ema_ref(xbar, x, 0.9, init=False)
         assert np.allclose(xbar, x + 0.9 ** t * (a - x), atol=1e-14)
     assert np.array_equal(oracle.features_ema_ref(a, x, 0.0, init=False), x)
+
+
+def test_row_stats_rows_match_full():
+    """The row-restricted form is the full definition on the selected rows."""
+    q, k, v = _rand(1, 2, 50, 8, seed=7)
+    ent, nrm = oracle.attn_row_stats_ref(q, k, v, [6, 20], 0.7, sinks=[4, 0])
+    rows = [0, 3, 17, 49]
+    for h, (w, s) in enumerate(((6, 4), (20, 0))):
+        e, n = oracle.attn_row_stats_rows_ref(q[0, h], k[0, h], v[0, h], w, 0.7, rows, sink=s)
+        assert np.allclose(e, ent[0, h, rows], rtol=0, atol=1e-14)
+        assert np.allclose(n, nrm[0, h, rows], rtol=0, atol=1e-14)
