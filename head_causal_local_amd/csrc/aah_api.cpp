@@ -386,7 +386,8 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
 }
 
 size_t features_workspace(int B, int H, int T, int d) {
-  return round_up(static_cast<size_t>(3) * H * B * aah::feature_chunks(T, d) * 4 * sizeof(double), 256);
+  // Q/K/V partials (count, mean, M2, sum |x|) and the row sums (entropy, norm) per (b, h, chunk).
+  return round_up(static_cast<size_t>(3 * 4 + 2) * H * B * aah::feature_chunks(T, d) * sizeof(double), 256);
 }
 
 }  // namespace

@@ -83,7 +83,7 @@ inline int feature_chunks(int T, int d) {
 // Writes features [H, 9] (if non-null) and updates ema [H, 9] (if non-null;
 // ema = x when init) from q, k, v [B,H,T,d] (bf16 or fp32) and the per-row
 // entropy / output norm [B,H,T] (nullptr: those features are 0).  partials:
-// 3 * H * B * feature_chunks(T, d) * 4 doubles of scratch.
+// (3 * 4 + 2) * H * B * feature_chunks(T, d) doubles of scratch.
 hipError_t launch_head_features(const void* q, const void* k, const void* v, bool is_bf16, const float* ent,
                                 const float* onorm, const int32_t* win_eff, int B, int H, int T, int d,
                                 float alpha, bool init, float* features, float* ema, double* partials,
