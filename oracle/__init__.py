@@ -12,6 +12,7 @@ printed worked example); no function here is "parity unpinned".
 """
 from .attention import (  # noqa: F401
     window_allowed,
+    kv_head,
     attn_fwd_ref,
     attn_fwd_rows_ref,
     attn_bwd_ref,

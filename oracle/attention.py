@@ -24,6 +24,14 @@ attends to the first s_sink tokens and to its recent window.  With a sink size S
 per head, key t_k is allowed for query t_q iff t_k <= t_q and (t_k >= t_q - W + 1
 or t_k < S); S = 0 is the plain local window.
 
+Grouped K/V heads ("Asymmetric Attention Heads" section 3.3 relates the method to
+grouped-query attention; its appendix A.3 inserts it into a grouped-query model,
+and "Autonomy-of-Heads" section 4 and section 5 assign query heads to KV groups):
+with H query heads and H_kv = H / G key/value heads, query head h reads key/value
+head floor(h / G) (the G query heads of a group are consecutive); windows and
+sink sizes stay per query head.  The gradients of a key/value head sum over the
+query heads of its group.
+
 Readings where the pages are silent (each listed in the design notes):
   * the additive mask value is -inf, so masked weights are exactly zero;
   * the log-sum-exp is the natural log of sum_j exp(scaled score) over the
@@ -76,20 +84,30 @@ def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None, s
     return E / l, m[:, 0], l[:, 0]
 
 
+def kv_head(h: int, H: int, H_kv: int) -> int:
+    """Key/value head read by query head h: floor(h / G), G = H / H_kv query heads per group."""
+    if H_kv < 1 or H % H_kv != 0:
+        raise ValueError("H must be a multiple of H_kv")
+    return h // (H // H_kv)
+
+
 def attn_fwd_ref(q, k, v, windows, scale, sinks=None):
-    """Forward pass for Q/K/V laid out [B, H, T, d] with one window (and sink size) per head.
+    """Forward pass for Q [B, H, T, d] and K/V [B, H_kv, T, d] (H_kv divides H; H_kv = H is
+    plain multi-head attention) with one window (and sink size) per query head.
 
     Returns (O [B,H,T,d], LSE [B,H,T]) in float64.  AAH section 5.8; AoH section 5 for sinks."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, H, T, d = q.shape
+    H_kv = k.shape[1]
     O = np.empty((B, H, T, v.shape[-1]), dtype=np.float64)
     LSE = np.empty((B, H, T), dtype=np.float64)
     for b in range(B):
         for h in range(H):
-            P, m, l = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
-            O[b, h] = P @ v[b, h]
+            g = kv_head(h, H, H_kv)
+            P, m, l = _head_probs(q[b, h], k[b, g], int(windows[h]), scale, sink=_sink(sinks, h))
+            O[b, h] = P @ v[b, g]
             LSE[b, h] = m + np.log(l)
     return O, LSE
 
@@ -109,27 +127,30 @@ def attn_fwd_rows_ref(q_h, k_h, v_h, w, scale, rows, sink: int = 0):
 def attn_bwd_ref(q, k, v, windows, scale, do, sinks=None):
     """Gradients (dQ, dK, dV) of sum(O * dO) by matrix calculus of section 5.8.
 
-    With P the masked row softmax of S = scale Q K^T and O = P V:
+    With P the masked row softmax of S = scale Q K^T and O = P V, per query head:
       dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
       dS = P * (dP - D 1^T)  (zero where masked, since P is),
-      dQ = scale dS K,  dK = scale dS^T Q."""
+      dQ = scale dS K,  dK = scale dS^T Q;
+    a key/value head shared by a group of query heads gets the sum of their dK, dV."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
     B, H, T, d = q.shape
+    H_kv = k.shape[1]
     dq = np.empty_like(q)
-    dk = np.empty_like(k)
-    dv = np.empty_like(v)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
     for b in range(B):
         for h in range(H):
-            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
-            dv[b, h] = P.T @ do[b, h]
-            dP = do[b, h] @ v[b, h].T
+            g = kv_head(h, H, H_kv)
+            P, _, _ = _head_probs(q[b, h], k[b, g], int(windows[h]), scale, sink=_sink(sinks, h))
+            dv[b, g] += P.T @ do[b, h]
+            dP = do[b, h] @ v[b, g].T
             D = (P * dP).sum(axis=1, keepdims=True)
             dS = P * (dP - D)
-            dq[b, h] = scale * (dS @ k[b, h])
-            dk[b, h] = scale * (dS.T @ q[b, h])
+            dq[b, h] = scale * (dS @ k[b, g])
+            dk[b, g] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
 
 

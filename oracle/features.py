@@ -27,7 +27,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import _head_probs, _sink
+from .attention import _head_probs, _sink, kv_head
 
 N_FEATURES = 9
 
@@ -45,11 +45,12 @@ def attn_row_stats_ref(q, k, v, windows, scale, sinks=None):
     nrm = np.empty((B, H, T))
     for b in range(B):
         for h in range(H):
-            P, _, _ = _head_probs(q[b, h], k[b, h], int(windows[h]), scale, sink=_sink(sinks, h))
+            g = kv_head(h, H, k.shape[1])
+            P, _, _ = _head_probs(q[b, h], k[b, g], int(windows[h]), scale, sink=_sink(sinks, h))
             with np.errstate(divide="ignore", invalid="ignore"):
                 plogp = np.where(P > 0, P * np.log(P), 0.0)
             ent[b, h] = -plogp.sum(axis=1)
-            nrm[b, h] = np.linalg.norm(P @ v[b, h], axis=1)
+            nrm[b, h] = np.linalg.norm(P @ v[b, g], axis=1)
     return ent, nrm
 
 
@@ -72,14 +73,16 @@ def _mean_abs_std(x_h):
 
 
 def head_features_ref(q, k, v, windows, row_entropy=None, row_norm=None):
-    """Base features x [H, 9] (section 5.3) from Q/K/V [B,H,T,d] and, if given, the
-    per-row diagnostics of the most recent forward pass ([B,H,T] each; None = zero)."""
+    """Base features x [H, 9] (section 5.3) from Q [B,H,T,d], K/V [B,H_kv,T,d] and, if given, the
+    per-row diagnostics of the most recent forward pass ([B,H,T] each; None = zero).  With
+    grouped K/V heads, query head h's key and value statistics are those of its group's head."""
     q = np.asarray(q, dtype=np.float64)
     B, H, T, _ = q.shape
     x = np.zeros((H, N_FEATURES))
     for h in range(H):
-        for slot, t in enumerate((q, k, v)):
-            x[h, 2 * slot], x[h, 2 * slot + 1] = _mean_abs_std(np.asarray(t)[:, h])
+        g = kv_head(h, H, np.asarray(k).shape[1])
+        for slot, (t, hh) in enumerate(((q, h), (k, g), (v, g))):
+            x[h, 2 * slot], x[h, 2 * slot + 1] = _mean_abs_std(np.asarray(t)[:, hh])
         x[h, 6] = 0.0 if row_entropy is None else np.asarray(row_entropy, dtype=np.float64)[:, h].mean()
         x[h, 7] = 0.0 if row_norm is None else np.asarray(row_norm, dtype=np.float64)[:, h].mean()
         x[h, 8] = min(int(windows[h]), T) / T
