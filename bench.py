@@ -16,7 +16,8 @@ with sink tokens, the sinks each row sees before its window).
 
 --workload 5 times the same step on the streaming-head layer (heads 0-15 full
 causal, heads 16-31 sink 128 + recent window 256; "Autonomy-of-Heads" section
-5 and 6.1).
+5 and 6.1); --workload 6 on a grouped-query layer (32 query heads over 8
+key/value heads, d = 128, per-query-head windows).
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -229,14 +230,11 @@ def calibrate_copy(steps):
                       "launches": steps}), flush=True)
 
 
-KERNEL_SOURCES = {
-    "fwd_bf16_kernel<64, false>": "head_causal_local_amd/csrc/fwd_bf16.hip",
-    "bwd_dkdv_kernel<64, false>": "head_causal_local_amd/csrc/bwd_bf16.hip",
-    "bwd_dq_kernel<64, false>": "head_causal_local_amd/csrc/bwd_bf16.hip",
-    "fwd_bf16_kernel<64, true>": "head_causal_local_amd/csrc/fwd_bf16.hip",
-    "bwd_dkdv_kernel<64, true>": "head_causal_local_amd/csrc/bwd_bf16.hip",
-    "bwd_dq_kernel<64, true>": "head_causal_local_amd/csrc/bwd_bf16.hip",
-    "decode_kernel<64>": "head_causal_local_amd/csrc/decode.hip",
+KERNEL_SOURCES = {  # kernel template name -> its source file
+    "fwd_bf16_kernel": "head_causal_local_amd/csrc/fwd_bf16.hip",
+    "bwd_dkdv_kernel": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "bwd_dq_kernel": "head_causal_local_amd/csrc/bwd_bf16.hip",
+    "decode_kernel": "head_causal_local_amd/csrc/decode.hip",
 }
 
 
@@ -245,7 +243,7 @@ def measured_traffic(kernel):
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hbm_traffic.txt")
-    src = KERNEL_SOURCES.get(kernel)
+    src = KERNEL_SOURCES.get(kernel.split("<")[0])
     if src is None or not os.path.exists(path):
         return None
     sha = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()[:16]
@@ -288,10 +286,12 @@ def cpu_baseline(wl, n_heads, with_bwd):
     t0 = time.perf_counter()
     for h in heads:
         sl = (slice(0, 1), slice(h, h + 1))
+        g = h // (wl.H // wl.k.shape[1])                     # the query head's key/value head
+        kv = (slice(0, 1), slice(g, g + 1))
         sk = None if wl.sinks is None else wl.sinks[h:h + 1]
-        oracle.attn_fwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, sinks=sk)
+        oracle.attn_fwd_ref(wl.q[sl], wl.k[kv], wl.v[kv], wl.windows[h:h + 1], wl.scale, sinks=sk)
         if with_bwd:
-            oracle.attn_bwd_ref(wl.q[sl], wl.k[sl], wl.v[sl], wl.windows[h:h + 1], wl.scale, wl.do[sl], sinks=sk)
+            oracle.attn_bwd_ref(wl.q[sl], wl.k[kv], wl.v[kv], wl.windows[h:h + 1], wl.scale, wl.do[sl], sinks=sk)
     dt = time.perf_counter() - t0
     flops = (4 + (10 if with_bwd else 0)) * wl.d * pairs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
@@ -332,11 +332,12 @@ def main():
     with_bwd = (wl.do is not None) and not args.fwd_only
     B, H, T, d = wl.B, wl.H, wl.T, wl.d
     q, k, v = to_dev(wl, "q"), to_dev(wl, "k"), to_dev(wl, "v")
+    H_kv = k.shape[1]
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device="cuda")
     if with_bwd:
         do = to_dev(wl, "do")
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
         ws = torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     n_ev = 4 if with_bwd else 2
@@ -386,12 +387,14 @@ def main():
     # Roofline of the kernel that dominates the step (each step is one launch on `stream`).
     # Algorithmic FLOPs per in-window pair: forward 4 d (Q K^T, P V); dK/dV kernel 8 d
     # (Q K^T, dO V^T, dO^T P, Q^T dS); dQ kernel 6 d (K Q^T, V dO^T, K^T dS^T).
-    # Heads with sinks run the kernels' SINK instantiations.
-    tag = f"<{d}, {'true' if wl.sinks is not None and int(np.max(wl.sinks)) > 0 else 'false'}>"
-    kernels = [("fwd_bf16_kernel" + tag, float(fwd_ms.mean()), f_fwd)]
+    # Instantiations the library launches: <d, sinks, diagnostics> forward, <d, sinks> dQ,
+    # <d, sinks, grouped heads> dK/dV.
+    sink = "true" if wl.sinks is not None and int(np.max(wl.sinks)) > 0 else "false"
+    gqa = "true" if H_kv != H else "false"
+    kernels = [(f"fwd_bf16_kernel<{d}, {sink}, false>", float(fwd_ms.mean()), f_fwd)]
     if with_bwd:
-        kernels += [("bwd_dkdv_kernel" + tag, float(dkdv_ms.mean()), 8 * d * pairs),
-                    ("bwd_dq_kernel" + tag, float(dq_ms.mean()), 6 * d * pairs)]
+        kernels += [(f"bwd_dkdv_kernel<{d}, {sink}, {gqa}>", float(dkdv_ms.mean()), 8 * d * pairs),
+                    (f"bwd_dq_kernel<{d}, {sink}>", float(dq_ms.mean()), 6 * d * pairs)]
     kname, kms, kflops = max(kernels, key=lambda x: x[1])
     achieved = kflops / (kms * 1e-3) / 1e12
     roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -413,7 +416,7 @@ def main():
         "data": "synthetic (N(0,1) bf16 Q/K/V/dO, seed 0)",
         "config": {
             "workload": wl.name + (" fwd+bwd" if with_bwd else " fwd"),
-            "B": B, "H": H, "T": T, "d": d,
+            "B": B, "H": H, "H_kv": H_kv, "T": T, "d": d,
             "windows": [int(x) for x in wl.windows],
             **({"sinks": [int(x) for x in wl.sinks]} if wl.sinks is not None else {}),
             "in_window_pairs": int(pairs),

@@ -69,9 +69,23 @@ def _check_operand(name, t, ref):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
     if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
-        raise ValueError(f"{name} must match q in shape, dtype and device")
+        raise ValueError(f"{name} must match {'q' if ref.dim() == 4 else 'its reference'} in shape, dtype and device")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, T, d]")
+
+
+def _kv_heads(q, k, v) -> int:
+    """H_kv of k, v [B, H_kv, T, d] against q [B, H, T, d] (grouped key/value heads: H_kv divides H)."""
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, T, d] and [B, H_kv, T, d]")
+    B, H, T, d = q.shape
+    H_kv = k.shape[1]
+    if k.shape != (B, H_kv, T, d) or H_kv < 1 or H % H_kv != 0:
+        raise ValueError(f"k must be [B, H_kv, T, d] with H_kv dividing H = {H} (got {tuple(k.shape)})")
+    if not k.is_cuda or k.dtype != q.dtype or k.device != q.device or not k.is_contiguous():
+        raise ValueError("k must be a contiguous device tensor of q's dtype and device")
+    _check_operand("v", v, k)
+    return H_kv
 
 
 def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None, sinks=None):
@@ -84,8 +98,8 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_operand(name, t, q)
+    _check_operand("q", q, q)
+    H_kv = _kv_heads(q, k, v)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
@@ -101,7 +115,7 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
     elif lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     sk = _sinks_arg(sinks, H)
-    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d,
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d,
                             _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(), None, 0,
                             _stream_ptr(q, stream))
     check(st)
@@ -116,8 +130,8 @@ def attn_fwd_diag(q, k, v, windows, scale: Optional[float] = None, out=None, lse
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        _check_operand(name, t, q)
+    _check_operand("q", q, q)
+    H_kv = _kv_heads(q, k, v)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
@@ -134,7 +148,7 @@ def attn_fwd_diag(q, k, v, windows, scale: Optional[float] = None, out=None, lse
         rows.append(t)
     lse, row_entropy, row_onorm = rows
     sk = _sinks_arg(sinks, H)
-    check(lib().aah_attn_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d,
+    check(lib().aah_attn_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d,
                                   _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(),
                                   row_entropy.data_ptr(), row_onorm.data_ptr(), _stream_ptr(q, stream)))
     return out, lse, row_entropy, row_onorm
@@ -153,8 +167,7 @@ def head_features(q, k, v, windows, row_entropy=None, row_onorm=None, features_e
     attn_fwd_diag (None: entropy and norm features are 0); if features_ema ([H, 9] float32) is given it is
     updated in place: init ? x : alpha * ema + (1 - alpha) * x.  Returns x."""
     import torch
-    for name, t in (("k", k), ("v", v)):
-        _check_operand(name, t, q)
+    H_kv = _kv_heads(q, k, v)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
@@ -174,7 +187,7 @@ def head_features(q, k, v, windows, row_entropy=None, row_onorm=None, features_e
     ptr, nbytes = _ws(workspace)
     check(lib().aah_head_features(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   None if row_entropy is None else row_entropy.data_ptr(),
-                                  None if row_onorm is None else row_onorm.data_ptr(), _wptr(w), B, H, T, d,
+                                  None if row_onorm is None else row_onorm.data_ptr(), _wptr(w), B, H, H_kv, T, d,
                                   _dtype_code(q), float(alpha), 1 if init else 0, out.data_ptr(),
                                   None if features_ema is None else features_ema.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
@@ -188,10 +201,11 @@ def workspace_size(B: int, H: int, T: int, d: int, dtype: str = "bf16", is_bwd: 
 
 def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=None, dk=None, dv=None,
              workspace=None, stream=None, sinks=None):
-    """dQ, dK, dV of sum(O * do) for local-window attention (see attn_fwd)."""
+    """dQ, dK, dV of sum(O * do) for local-window attention (see attn_fwd); dK, dV have k's shape."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("q", q), ("o", o), ("do", do)):
         _check_operand(name, t, q)
+    H_kv = _kv_heads(q, k, v)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
@@ -203,15 +217,16 @@ def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=Non
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-        _check_operand(name, t, q)
+    _check_operand("dq", dq, q)
+    for name, t in (("dk", dk), ("dv", dv)):
+        _check_operand(name, t, k)
     code = _dtype_code(q)
     need = int(lib().aah_attn_workspace_size(B, H, T, d, code, 1))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     sk = _sinks_arg(sinks, H)
     st = lib().aah_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
-                            _wptr(w), _sptr(sk), B, H, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(),
+                            _wptr(w), _sptr(sk), B, H, H_kv, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(),
                             dv.data_ptr(),
                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                             _stream_ptr(q, stream))
@@ -224,21 +239,21 @@ def _ws(workspace):
 
 
 def _bwd_args(q, k, v, do, windows, scale):
-    for name, t in (("k", k), ("v", v), ("do", do)):
-        _check_operand(name, t, q)
+    _check_operand("do", do, q)
+    H_kv = _kv_heads(q, k, v)
     B, H, T, d = q.shape
     w = _windows_arg(windows)
     if w.shape[0] != H:
         raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    return B, H, T, d, w, float(scale)
+    return B, H, H_kv, T, d, w, float(scale)
 
 
 def attn_bwd_dq(q, k, v, o, do, lse, windows, dq, workspace, scale: Optional[float] = None, stream=None,
                 sinks=None):
     """Backward step 1: dQ, and the per-row -lse * log2(e) and -rowsum(do * o) into the workspace."""
     import torch
-    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
+    B, H, H_kv, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
     sk = _sinks_arg(sinks, H)
     _check_operand("o", o, q)
     _check_operand("dq", dq, q)
@@ -246,20 +261,20 @@ def attn_bwd_dq(q, k, v, o, do, lse, windows, dq, workspace, scale: Optional[flo
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     ptr, nbytes = _ws(workspace)
     check(lib().aah_attn_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
-                                lse.data_ptr(), _wptr(w), _sptr(sk), B, H, T, d, _dtype_code(q), scale,
+                                lse.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d, _dtype_code(q), scale,
                                 dq.data_ptr(), ptr, nbytes, _stream_ptr(q, stream)))
 
 
 def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float] = None, stream=None,
                   sinks=None):
     """Backward step 2: dK and dV (reads the workspace rows attn_bwd_dq wrote; run it after that step)."""
-    B, H, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
+    B, H, H_kv, T, d, w, scale = _bwd_args(q, k, v, do, windows, scale)
     sk = _sinks_arg(sinks, H)
-    _check_operand("dk", dk, q)
-    _check_operand("dv", dv, q)
+    _check_operand("dk", dk, k)
+    _check_operand("dv", dv, k)
     ptr, nbytes = _ws(workspace)
     check(lib().aah_attn_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(), _wptr(w), _sptr(sk),
-                                  B, H, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
+                                  B, H, H_kv, T, d, _dtype_code(q), scale, dk.data_ptr(), dv.data_ptr(), ptr, nbytes,
                                   _stream_ptr(q, stream)))
 
 
@@ -340,29 +355,30 @@ def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:
     return r.value, c.value
 
 
-def _plan(fn, windows, sinks, B, H, T, q_tile, kv_tile, n_queues) -> np.ndarray:
+def _plan(fn, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv) -> np.ndarray:
     w = _windows_arg(windows)
     sk = None if sinks is None else _windows_arg(sinks)
+    H_kv = H if H_kv is None else H_kv
     n = ctypes.c_int64()
-    st = fn(_wptr(w), _sptr(sk), B, H, T, q_tile, kv_tile, n_queues, None, 0, ctypes.byref(n))
+    st = fn(_wptr(w), _sptr(sk), B, H, H_kv, T, q_tile, kv_tile, n_queues, None, 0, ctypes.byref(n))
     if st not in (0, 1):
         check(st)
     buf = (WorkItem * max(n.value, 1))()
-    check(fn(_wptr(w), _sptr(sk), B, H, T, q_tile, kv_tile, n_queues, buf, n.value, ctypes.byref(n)))
+    check(fn(_wptr(w), _sptr(sk), B, H, H_kv, T, q_tile, kv_tile, n_queues, buf, n.value, ctypes.byref(n)))
     arr = np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[: n.value].copy()
     return arr
 
 
 def plan_fwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8,
-             sinks: Optional[Sequence[int]] = None):
+             sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None):
     """Forward work list as an int32 array [n, 4] of (bh, q_tile_index, kv_lo, kv_hi)."""
-    return _plan(lib().aah_plan_fwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
+    return _plan(lib().aah_plan_fwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv)
 
 
 def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8,
-             sinks: Optional[Sequence[int]] = None):
-    """Backward work list as an int32 array [n, 4] of (bh, kv_tile_index, q_lo, q_hi)."""
-    return _plan(lib().aah_plan_bwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
+             sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None):
+    """Backward work list as an int32 array [n, 4] of (b * H_kv + g, kv_tile_index, q_lo, q_hi)."""
+    return _plan(lib().aah_plan_bwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv)
 
 
 def window_stats(windows: Sequence[int], T: int, sinks: Optional[Sequence[int]] = None) -> Tuple[int, float]:

@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
@@ -63,25 +63,27 @@ def _declare(lib):
     lib.aah_last_error_detail.argtypes = []
     lib.aah_attn_fwd.restype = c_int
     lib.aah_attn_fwd.argtypes = [c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
-                                 c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                 c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_fwd_diag.restype = c_int
     lib.aah_attn_fwd_diag.argtypes = [c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
-                                      c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+                                      c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
     lib.aah_head_features_workspace_size.restype = c_size_t
     lib.aah_head_features_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
     lib.aah_head_features.restype = c_int
     lib.aah_head_features.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int, c_int,
-                                      c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                      c_int, c_int, c_int, c_float, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
+                                      c_void_p]
     lib.aah_attn_bwd.restype = c_int
     lib.aah_attn_bwd.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int,
-                                 c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                                 c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
                                  c_size_t, c_void_p]
     lib.aah_attn_bwd_dkdv.restype = c_int
     lib.aah_attn_bwd_dkdv.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int,
-                                      c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+                                      c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_bwd_dq.restype = c_int
     lib.aah_attn_bwd_dq.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int,
-                                    c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_size_t, c_void_p]
+                                    c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_size_t,
+                                    c_void_p]
     lib.aah_attn_workspace_size.restype = c_size_t
     lib.aah_attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_tile_shape.restype = c_int
@@ -89,7 +91,7 @@ def _declare(lib):
     for name in ("aah_plan_fwd", "aah_plan_bwd"):
         fn = getattr(lib, name)
         fn.restype = c_int
-        fn.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int, P_item, c_int64, P_i64]
+        fn.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, c_int64, P_i64]
     lib.aah_window_stats.restype = c_int
     lib.aah_window_stats.argtypes = [P_i32, P_i32, c_int, c_int, P_i64, P_double]
     lib.aah_cache_clear.restype = None

@@ -63,10 +63,18 @@ aah_status check_windows(const int32_t* windows, const int32_t* sinks, int H) {
   return AAH_OK;
 }
 
+aah_status check_kv_heads(int H, int H_kv) {
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0)
+    return fail(AAH_ERR_INVALID_ARG, "H_kv = %d must divide H = %d (1 <= H_kv <= H)", H_kv, H);
+  return AAH_OK;
+}
+
 // Shape checks shared by every entry point that takes windows (and sink sizes, may be NULL).
-aah_status check_shape(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt) {
+aah_status check_shape(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt,
+                       int H_kv = -1) {
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
   AAH_TRY_INNER(check_dims(B, H, T, d, dt));
+  AAH_TRY_INNER(check_kv_heads(H, H_kv < 0 ? H : H_kv));
   return check_windows(windows, sinks, H);
 }
 
@@ -112,8 +120,8 @@ std::map<std::vector<int64_t>, DevicePlan> g_cache;
 
 constexpr int kQueues = 8;  // MI355X has eight XCDs; workgroups are placed round-robin over them
 
-aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int row_tile,
-                    int col_tile, DevicePlan* out) {
+aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                    int row_tile, int col_tile, DevicePlan* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -126,7 +134,7 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks,
   }
   // Heads whose sinks change nothing plan (and run) exactly as without sinks.
   const int32_t* sink_arg = any_sink ? win.data() + H : nullptr;
-  std::vector<int64_t> key = {kind, dev, B, H, T, row_tile, col_tile, kQueues, any_sink ? 1 : 0};
+  std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, row_tile, col_tile, kQueues, any_sink ? 1 : 0};
   key.insert(key.end(), win.begin(), win.end());
 
   std::lock_guard<std::mutex> lock(g_mu);
@@ -138,8 +146,8 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks,
   // Forward: row tile = query rows per item, col tile = keys per step.
   // Backward: row tile = keys per item, col tile = query rows per step.
   const std::vector<WorkItem> items =
-      kind == kPlanFwd ? aah::plan_forward(windows, sink_arg, B, H, T, row_tile, col_tile, kQueues)
-                       : aah::plan_backward(windows, sink_arg, B, H, T, col_tile, row_tile, kQueues);
+      kind == kPlanFwd ? aah::plan_forward(windows, sink_arg, B, H, H_kv, T, row_tile, col_tile, kQueues)
+                       : aah::plan_backward(windows, sink_arg, B, H, H_kv, T, col_tile, row_tile, kQueues);
 
   DevicePlan p;
   p.n_items = static_cast<int>(items.size());
@@ -297,17 +305,18 @@ aah_status check_decode(const int32_t* windows, int B, int H, int T_max, int d, 
   return AAH_OK;
 }
 
-aah_status plan_to_host(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int T,
-                        int q_tile, int kv_tile, int n_queues, aah_work_item* items, int64_t capacity,
+aah_status plan_to_host(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                        int T, int q_tile, int kv_tile, int n_queues, aah_work_item* items, int64_t capacity,
                         int64_t* n_items) {
   if (n_items == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items is NULL");
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
   if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
   if (q_tile < 1 || kv_tile < 1 || n_queues < 1) return fail(AAH_ERR_INVALID_ARG, "tiles and n_queues must be >= 1");
+  AAH_TRY_INNER(check_kv_heads(H, H_kv));
   AAH_TRY_INNER(check_windows(windows, sinks, H));
   const std::vector<WorkItem> v = kind == kPlanFwd
-                                      ? aah::plan_forward(windows, sinks, B, H, T, q_tile, kv_tile, n_queues)
-                                      : aah::plan_backward(windows, sinks, B, H, T, q_tile, kv_tile, n_queues);
+                                      ? aah::plan_forward(windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues)
+                                      : aah::plan_backward(windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues);
   *n_items = static_cast<int64_t>(v.size());
   if (capacity < static_cast<int64_t>(v.size()))
     return fail(AAH_ERR_INVALID_ARG, "capacity %lld < %zu items", static_cast<long long>(capacity), v.size());
@@ -358,9 +367,9 @@ namespace {
 
 // Forward, with the per-row diagnostics when ent / onorm are set (both or neither).
 aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks, int B,
-                    int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, float* ent, float* onorm,
-                    aah_stream_t stream) {
-  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
+                    int H, int H_kv, int T, int d, aah_dtype dt, float scale, void* o, float* lse, float* ent,
+                    float* onorm, aah_stream_t stream) {
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -371,8 +380,8 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, T, row, col, &plan));
-  const aah::AttnShape s{B, H, T, d, scale};
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
+  const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (dt == AAH_BF16)
@@ -395,21 +404,21 @@ size_t features_workspace(int B, int H, int T, int d) {
 extern "C" {
 
 aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks,
-                        int B, int H, int T, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
-                        size_t workspace_bytes, aah_stream_t stream) {
+                        int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale, void* o, float* lse,
+                        void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   (void)workspace;
   (void)workspace_bytes;
   g_detail.clear();
-  return fwd_impl(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, nullptr, nullptr, stream);
+  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, nullptr, nullptr, stream);
 }
 
 aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
-                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* o,
-                             float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream) {
+                             const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
+                             void* o, float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
   AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
-  return fwd_impl(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream);
+  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream);
 }
 
 size_t aah_head_features_workspace_size(int B, int H, int T, int d) {
@@ -418,11 +427,11 @@ size_t aah_head_features_workspace_size(int B, int H, int T, int d) {
 }
 
 aah_status aah_head_features(const void* q, const void* k, const void* v, const float* row_entropy,
-                             const float* row_onorm, const int32_t* windows, int B, int H, int T, int d,
+                             const float* row_onorm, const int32_t* windows, int B, int H, int H_kv, int T, int d,
                              aah_dtype dt, float alpha, int init, float* features, float* features_ema,
                              void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_shape(windows, nullptr, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, nullptr, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -448,19 +457,20 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, nullptr, B, H, T, row, col, &plan));
-  const hipError_t e = aah::launch_head_features(q, k, v, dt == AAH_BF16, row_entropy, row_onorm, plan.win, B, H, T,
-                                                 d, alpha, init != 0, features, features_ema,
+  AAH_TRY(get_plan(kPlanFwd, windows, nullptr, B, H, H_kv, T, row, col, &plan));
+  const hipError_t e = aah::launch_head_features(q, k, v, dt == AAH_BF16, row_entropy, row_onorm, plan.win, B, H,
+                                                 H_kv, T, d, alpha, init != 0, features, features_ema,
                                                  static_cast<double*>(workspace), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "head features launch");
   return AAH_OK;
 }
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const int32_t* windows,
-                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* dk,
-                             void* dv, const void* workspace, size_t workspace_bytes, aah_stream_t stream) {
+                             const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
+                             void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                             aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -469,14 +479,14 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   AAH_TRY(check_tensor(dv, "dv", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  const aah::AttnShape s{B, H, T, d, scale};
+  const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   const float* nl2 = ws_nl2(workspace);
   const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
     e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nl2, nd, dk, dv, plan.items, plan.n_items, plan.win, plan.sink, s,
@@ -491,11 +501,11 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
 }
 
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
-                           aah_dtype dt, float scale, void* dq, void* workspace, size_t workspace_bytes,
-                           aah_stream_t stream) {
+                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                           int T, int d, aah_dtype dt, float scale, void* dq, void* workspace,
+                           size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -505,14 +515,14 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   AAH_TRY(check_tensor(dq, "dq", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  const aah::AttnShape s{B, H, T, d, scale};
+  const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   float* nl2 = const_cast<float*>(ws_nl2(workspace));
   float* nd = const_cast<float*>(ws_nd(workspace, B, H, T));
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   hipError_t e;
   if (dt == AAH_BF16) {
     // One kernel: D and the workspace rows come out of the dQ kernel's prologue.
@@ -530,12 +540,12 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
 }
 
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                        const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
-                        aah_dtype dt, float scale, void* dq, void* dk, void* dv, void* workspace,
+                        const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                        int d, aah_dtype dt, float scale, void* dq, void* dk, void* dv, void* workspace,
                         size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   // Validate everything up front so that no step runs unless all of them can.
-  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt));
+  AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -547,10 +557,10 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dv, "dv", 16));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
-  AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, T, d, dt, scale, dq, workspace,
+  AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, H_kv, T, d, dt, scale, dq, workspace,
                           workspace_bytes, stream));
-  return aah_attn_bwd_dkdv(q, k, v, dout, windows, sinks, B, H, T, d, dt, scale, dk, dv, workspace, workspace_bytes,
-                           stream);
+  return aah_attn_bwd_dkdv(q, k, v, dout, windows, sinks, B, H, H_kv, T, d, dt, scale, dk, dv, workspace,
+                           workspace_bytes, stream);
 }
 
 int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max) {
@@ -616,16 +626,16 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   return AAH_OK;
 }
 
-aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int q_tile, int kv_tile,
-                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
+aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int q_tile,
+                        int kv_tile, int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();
-  return plan_to_host(kPlanFwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+  return plan_to_host(kPlanFwd, windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
 }
 
-aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int q_tile, int kv_tile,
-                        int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
+aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int q_tile,
+                        int kv_tile, int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();
-  return plan_to_host(kPlanBwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
+  return plan_to_host(kPlanBwd, windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues, items, capacity, n_items);
 }
 
 aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H, int T, int64_t* pairs_per_batch,

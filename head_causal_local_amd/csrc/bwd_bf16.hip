@@ -42,6 +42,12 @@
 // accumulator in HBM and no atomics (which this device resolves in memory,
 // not in L2), and every gradient is deterministic.
 //
+// Grouped key/value heads (G query heads share one K/V head): the dQ kernel
+// reads the K / V tiles of its query head's group; a dK/dV item holds one key
+// tile of the shared head and walks the group's G query heads one after
+// another, each over its own query-tile range, so the group's contributions to
+// dK and dV add up in registers (still no atomics).
+//
 // Both kernels skip 32-row blocks that no row of the wave sees and mask only
 // blocks that cross the diagonal or the window's trailing edge.  Tiles are
 // row-major with the XOR chunk swizzle of the forward kernel.  Rows past T
@@ -139,13 +145,26 @@ __device__ __forceinline__ void copy_tile(const bf16* head, int r0, int T, char*
 
 // ---------------------------------------------------------------- dK, dV
 
-template <int D, bool SINK>
+// Query tiles [lo, hi) of one query head (window W, effective sink S) that see
+// keys [k0, k1): the planner's per-head range (query_range in workplan.hpp).
+__device__ __forceinline__ int query_hi(int k0, int k1, int W, int S, int T) {
+  const int last = k0 < S ? T - 1 : min(T, k1 + W - 1) - 1;
+  return last / kStep + 1;
+}
+
+// Scalar walk over the steps of a key/value item: query head j of the group,
+// query tile qt of that head's range [lo, hi), its window and sink.
+struct StepCursor {
+  int j, qt, hi, W, S;
+};
+
+template <int D, bool SINK, bool GQA>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
-                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T,
-                     float scale) {
+                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
+                     int T, float scale) {
   using C = Cfg<D>;
   // Three-stage ring; stage = {Q tile, dO tile, nl2 row, nD row}.
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
@@ -156,9 +175,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
-  const int W = win_eff[it.bh % H];
-  const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
-  const size_t base = static_cast<size_t>(it.bh) * T * D;
+  // Without grouping it.bh = b * H + h indexes Q, K and V alike.  With grouping it.bh = b * H_kv + g
+  // indexes K / V / dK / dV, and the item walks the group's query heads g G .. g G + G - 1.
+  const int G = GQA ? H / H_kv : 1;
+  const int qh0 = GQA ? (it.bh / H_kv) * H + (it.bh % H_kv) * G : it.bh;  // first query head (b H + h)
+  const int W = win_eff[qh0 % H];
+  const int S = SINK ? sink_eff[qh0 % H] : 0;  // keys 0 .. S - 1 are sinks
+  const size_t base = static_cast<size_t>(it.bh) * T * D;  // K, V, dK, dV (and Q, dO without grouping)
   const size_t rbase = static_cast<size_t>(it.bh) * T;
   const float c = scale * kLog2e;
 
@@ -166,24 +189,25 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ln = lane & 31;
   const int k0w = it.tile * kStat + 32 * wave;  // first key of this wave
-  const bool wave_sink = SINK && k0w < S;         // every later query sees some key of this wave
   const int key = k0w + ln;                      // this lane's key (column of S)
   const bool wave_active = k0w < T;
   const Offsets<D> off(wave, lane);
 
   bf16x8 kf[C::kSteps], vf[C::kSteps];
 
-  // Stage fill: Q and dO tiles (every wave its share), nl2 row (wave 0), nD row (wave 1).
-  auto fill = [&](int qt, char* st) __attribute__((always_inline)) {
+  // Stage fill: Q and dO tiles (every wave its share), nl2 row (wave 0), nD row (wave 1) of the query
+  // head whose rows start at qb (elements) and rb (rows).
+  auto fill_rows = [&](size_t qb, size_t rb, int qt, char* st) __attribute__((always_inline)) {
     const int q0 = qt * kStep;
-    copy_tile<D>(Q + base, q0, T, st, wave, lane);
-    copy_tile<D>(dO + base, q0, T, st + kG, wave, lane);
+    copy_tile<D>(Q + qb, q0, T, st, wave, lane);
+    copy_tile<D>(dO + qb, q0, T, st + kG, wave, lane);
     if (wave < 2) {
-      const float* src = (wave == 0 ? NL2 : ND) + rbase + q0;
+      const float* src = (wave == 0 ? NL2 : ND) + rb + q0;
       dma4(rsrc_words(src, static_cast<uint32_t>(T - q0) * 4), st + (wave == 0 ? kL : kDd),
            static_cast<uint32_t>(lane) * 4);
     }
   };
+  auto fill = [&](int qt, char* st) __attribute__((always_inline)) { fill_rows(base, rbase, qt, st); };
   constexpr int kFill = 2 * C::kDmaPerWave;  // copies per wave per fill, plus one for waves 0 and 1
   auto wait_barrier = [&](bool keep_next) __attribute__((always_inline)) {
     if (keep_next) {
@@ -254,8 +278,9 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // One 64-query step, block by block.  Query i sees key j iff 0 <= i - j < W
   // (or j < S and i >= j); the wave's keys are [k0w, k0w + 32).  Blocks no key
   // sees are skipped; only blocks crossing the diagonal or the window's
-  // trailing edge are masked.
-  auto do_step = [&](const char* st, int q0) __attribute__((always_inline)) {
+  // trailing edge are masked.  W and S are those of the step's query head.
+  auto do_step = [&](const char* st, int q0, int W, int S) __attribute__((always_inline)) {
+    const bool wave_sink = SINK && k0w < S;  // every later query sees some key of this wave
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int qb = q0 + 32 * mb;
@@ -280,19 +305,70 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     }
   };
 
-  // Ring: step qt uses stage (qt - lo) % 3 and fills the stage of step qt + 2.
-  auto step = [&](int qt, const char* cur, char* nxt2) __attribute__((always_inline)) {
-    const bool more = qt + 2 < it.hi;
-    if (more) fill(qt + 2, nxt2);
-    do_step(cur, qt * kStep);
-    if (qt + 1 >= it.hi) return true;
-    wait_barrier(more);
-    return false;
+  // Grouped heads: the item's steps are the group's query heads one after another, each over its own
+  // query-tile range (all starting at it.lo); two cursors follow the step being filled (two ahead) and
+  // the step being computed.
+  const int k0 = it.tile * kStat, k1 = min(T, k0 + kStat);
+  auto set_head = [&](StepCursor& cu, int j) __attribute__((always_inline)) {
+    cu.j = j;
+    cu.qt = it.lo;
+    cu.W = win_eff[(qh0 + j) % H];
+    cu.S = SINK ? sink_eff[(qh0 + j) % H] : 0;
+    cu.hi = query_hi(k0, k1, cu.W, cu.S, T);
+  };
+  auto advance = [&](StepCursor& cu) __attribute__((always_inline)) {
+    if (++cu.qt == cu.hi && cu.j + 1 < G) set_head(cu, cu.j + 1);
+  };
+  StepCursor dc{0, it.lo, it.hi, W, S}, fc{0, it.lo, it.hi, W, S};
+  int n_steps = it.hi - it.lo;
+  if constexpr (GQA) {
+    set_head(dc, 0);
+    n_steps = 0;
+    for (int j = 0; j < G; ++j)
+      n_steps += query_hi(k0, k1, win_eff[(qh0 + j) % H], SINK ? sink_eff[(qh0 + j) % H] : 0, T) - it.lo;
+    fc = dc;
+  }
+  auto fill_cursor = [&](const StepCursor& cu, char* st) __attribute__((always_inline)) {
+    const size_t qh = static_cast<size_t>(qh0 + cu.j);
+    fill_rows(qh * T * D, qh * T, cu.qt, st);
+  };
+
+  // Ring: step v uses stage v % 3 and fills the stage of step v + 2.
+  auto step = [&](int v, const char* cur, char* nxt2) __attribute__((always_inline)) {
+    if constexpr (GQA) {
+      const bool more = v + 2 < n_steps;
+      if (more) {
+        fill_cursor(fc, nxt2);
+        advance(fc);
+      }
+      do_step(cur, dc.qt * kStep, dc.W, dc.S);
+      advance(dc);
+      if (v + 1 >= n_steps) return true;
+      wait_barrier(more);
+      return false;
+    } else {
+      const int qt = it.lo + v;
+      const bool more = qt + 2 < it.hi;
+      if (more) fill(qt + 2, nxt2);
+      do_step(cur, qt * kStep, W, S);
+      if (qt + 1 >= it.hi) return true;
+      wait_barrier(more);
+      return false;
+    }
   };
   // Prologue: the first two stages' copies and the K / V row loads all go out
   // before the first wait, so their latencies overlap.
-  fill(it.lo, ring0);
-  if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+  if constexpr (GQA) {
+    fill_cursor(fc, ring0);
+    advance(fc);
+    if (n_steps > 1) {
+      fill_cursor(fc, ring1);
+      advance(fc);
+    }
+  } else {
+    fill(it.lo, ring0);
+    if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+  }
   // K and V rows (B operands of S = Q K^T and dP = dO V^T): lane holds dims
   // 16 st + 8 hl + 0..7; K premultiplied by c.
   {
@@ -313,10 +389,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
   }
   wait_vm_barrier(0);
-  for (int qt = it.lo;; qt += 3) {
-    if (step(qt, ring0, ring2)) break;
-    if (step(qt + 1, ring1, ring0)) break;
-    if (step(qt + 2, ring2, ring1)) break;
+  for (int v = 0;; v += 3) {
+    if (step(v, ring0, ring2)) break;
+    if (step(v + 1, ring1, ring0)) break;
+    if (step(v + 2, ring2, ring1)) break;
   }
 
   if (key >= T) return;
@@ -342,7 +418,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
                    float* __restrict__ NL2, float* __restrict__ ND, bf16* __restrict__ dQ,
                    const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
-                   const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
+                   const int32_t* __restrict__ sink_eff, int H, int H_kv, int T, float scale) {
   using C = Cfg<D>;
   constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
   __shared__ __attribute__((aligned(1024))) char ring0[kStage];
@@ -371,10 +447,12 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   const int wave_key_hi = min(q0w + 31, T - 1);
   const Offsets<D> off(wave, lane);
 
+  // K / V tiles of this query head's key/value head, h / (H / H_kv).
+  const size_t kvbase = (static_cast<size_t>(it.bh / H) * H_kv + (it.bh % H) / (H / H_kv)) * T * D;
   auto fill = [&](int kt, char* st) __attribute__((always_inline)) {
     const int k0 = kt * kStep;
-    copy_tile<D>(K + base, k0, T, st, wave, lane);
-    copy_tile<D>(V + base, k0, T, st + C::kTileBytes, wave, lane);
+    copy_tile<D>(K + kvbase, k0, T, st, wave, lane);
+    copy_tile<D>(V + kvbase, k0, T, st + C::kTileBytes, wave, lane);
   };
   constexpr int kFill = 2 * C::kDmaPerWave;
 
@@ -518,14 +596,14 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    acc[b][4 * i + 2] * scale, acc[b][4 * i + 3] * scale);
 }
 
-template <int D, bool SINK>
+template <int D, bool SINK, bool GQA>
 hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
                   const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SINK>), dim3(n_items), dim3(kThreads), 0, stream,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, SINK, GQA>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<const bf16*>(dout), nl2, nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items,
-                     win_eff, sink_eff, s.H, s.T, s.scale);
+                     win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale);
   return hipGetLastError();
 }
 
@@ -536,7 +614,7 @@ hipError_t dq_d(const void* q, const void* k, const void* v, const void* o, cons
   hipLaunchKernelGGL((bwd_dq_kernel<D, SINK>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, nl2, nd,
-                     static_cast<bf16*>(dq), items, win_eff, sink_eff, s.H, s.T, s.scale);
+                     static_cast<bf16*>(dq), items, win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale);
   return hipGetLastError();
 }
 
@@ -544,9 +622,14 @@ template <int D>
 hipError_t dkdv_s(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
                   const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
-  return sink_eff != nullptr
-             ? dkdv_d<D, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream)
-             : dkdv_d<D, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+  const bool sink = sink_eff != nullptr, gqa = s.H_kv != s.H;
+  if (sink && gqa)
+    return dkdv_d<D, true, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+  if (sink)
+    return dkdv_d<D, true, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+  if (gqa)
+    return dkdv_d<D, false, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
+  return dkdv_d<D, false, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream);
 }
 
 template <int D>

@@ -89,12 +89,16 @@ __global__ __launch_bounds__(kThreads) void qkv_stats_kernel(const E* __restrict
                                                              const float* __restrict__ ONORM, int T,
                                                              int64_t slice, int chunks,
                                                              double* __restrict__ partials,
-                                                             double* __restrict__ row_partials, int H, int B) {
+                                                             double* __restrict__ row_partials, int H, int H_kv,
+                                                             int B) {
   constexpr int kPer = 16 / sizeof(E);  // elements per 16-byte vector
   constexpr int kUnroll = 4;            // vectors in flight per lane
   __shared__ Mom sm[kThreads];
   const int bh = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
   const int tensor = blockIdx.y;
+  // K and V have H_kv heads per batch entry: workgroups past B H_kv slices have nothing to do.
+  if ((tensor == 1 || tensor == 2) && bh >= B * H_kv) return;
+  const int Ht = (tensor == 1 || tensor == 2) ? H_kv : H;  // heads of this tensor
   if (tensor == 3) {  // uniform over the workgroup
     const int b = bh / H, h = bh % H;
     row_sums(ENT, ONORM, bh, chunk, chunks, T, row_partials + ((static_cast<int64_t>(h) * B + b) * chunks + chunk) * 2);
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(kThreads) void qkv_stats_kernel(const E* __restrict
     __syncthreads();
   }
   if (threadIdx.x == 0) {
-    const int b = bh / H, h = bh % H;
+    const int b = bh / Ht, h = bh % Ht;
     double* out = partials + ((static_cast<int64_t>(tensor) * H + h) * B + b) * chunks * 4 + chunk * 4;
     out[0] = sm[0].n;
     out[1] = sm[0].mean;
@@ -155,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void qkv_stats_kernel(const E* __restrict
 __global__ __launch_bounds__(64) void features_kernel(const double* __restrict__ partials,
                                                       const double* __restrict__ row_partials, int chunks,
                                                       bool have_rows, const int32_t* __restrict__ win_eff, int B,
-                                                      int H, int T, float alpha, int init,
+                                                      int H, int H_kv, int T, float alpha, int init,
                                                       float* __restrict__ features, float* __restrict__ ema) {
   __shared__ Mom sm[3][64];
   __shared__ double sr[2][64];
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(64) void features_kernel(const double* __restrict__
     Mom in[3];
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
-      const double* p = partials + ((static_cast<int64_t>(t) * H + h) * n + i) * 4;
+      const int hh = t == 0 ? h : h / (H / H_kv);  // K and V: the query head's key/value head
+      const double* p = partials + ((static_cast<int64_t>(t) * H + hh) * n + i) * 4;
       in[t] = Mom{p[0], p[1], p[2], p[3]};
     }
     if (have_rows) {
@@ -223,7 +228,7 @@ __global__ __launch_bounds__(64) void features_kernel(const double* __restrict__
 }  // namespace
 
 hipError_t launch_head_features(const void* q, const void* k, const void* v, bool is_bf16, const float* ent,
-                                const float* onorm, const int32_t* win_eff, int B, int H, int T, int d,
+                                const float* onorm, const int32_t* win_eff, int B, int H, int H_kv, int T, int d,
                                 float alpha, bool init, float* features, float* ema, double* partials,
                                 hipStream_t stream) {
   const int64_t slice = static_cast<int64_t>(T) * d;
@@ -234,15 +239,15 @@ hipError_t launch_head_features(const void* q, const void* k, const void* v, boo
   if (is_bf16)
     hipLaunchKernelGGL(qkv_stats_kernel<bf16>, grid, dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
                        static_cast<const bf16*>(k), static_cast<const bf16*>(v), ent, onorm, T, slice, chunks,
-                       partials, row_partials, H, B);
+                       partials, row_partials, H, H_kv, B);
   else
     hipLaunchKernelGGL(qkv_stats_kernel<float>, grid, dim3(kThreads), 0, stream, static_cast<const float*>(q),
                        static_cast<const float*>(k), static_cast<const float*>(v), ent, onorm, T, slice, chunks,
-                       partials, row_partials, H, B);
+                       partials, row_partials, H, H_kv, B);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(features_kernel, dim3(H), dim3(64), 0, stream, partials, row_partials, chunks, rows, win_eff,
-                     B, H, T, alpha, init ? 1 : 0, features, ema);
+                     B, H, H_kv, T, alpha, init ? 1 : 0, features, ema);
   return hipGetLastError();
 }
 

@@ -6,7 +6,9 @@
 // log-sum-exp of the scaled scores, used by the backward pass.
 //
 // One workgroup = one work item = 128 query rows of one head (4 waves x 32
-// rows) and the contiguous range of 64-key tiles the planner listed for them;
+// rows) and the contiguous range of 64-key tiles the planner listed for them
+// (with grouped key/value heads the tiles come from the group's K/V head; the
+// planner sends a group's query heads to the same XCD, so they meet in its L2);
 // tiles wholly outside the window are never visited.  Each wave walks the
 // tile in two 32-key blocks and classifies each block against its own 32
 // rows: blocks no row sees are skipped (no MFMA, no exp), blocks every row
@@ -101,8 +103,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(Cfg<D>
 void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ENT,
                      float* __restrict__ ONORM, const WorkItem* __restrict__ items,
-                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T,
-                     float c) {
+                     const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
+                     int T, float c) {
   using C = Cfg<D>;
   constexpr int NC = C::kNC;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes];
@@ -120,9 +122,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int n_tiles = ns + it.hi - it.lo;
   auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + it.lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
+  // Key/value head of this query head: its group's, h / (H / H_kv).
+  const size_t kvbase = (static_cast<size_t>(it.bh / H) * H_kv + (it.bh % H) / (H / H_kv)) * T * D;
   const bf16* Qh = Q + base;
-  const bf16* Kh = K + base;
-  const bf16* Vh = V + base;
+  const bf16* Kh = K + kvbase;
+  const bf16* Vh = V + kvbase;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -384,7 +388,7 @@ void launch_k(const void* q, const void* k, const void* v, void* o, float* lse, 
   const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
   hipLaunchKernelGGL((fwd_bf16_kernel<D, SINK, DIAG>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.T, c);
+                     static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.H_kv, s.T, c);
 }
 
 template <int D>

@@ -28,6 +28,7 @@ constexpr int kSimpleColTile = 64;
 struct AttnShape {
   int B, H, T, d;
   float scale;          // softmax scale applied to q . k
+  int H_kv;             // key/value heads; query head h reads head h / (H / H_kv)
 };
 
 // bf16 forward on MFMA (d in {32, 64, 128}).  ent / onorm: nullptr, or fp32
@@ -48,7 +49,8 @@ hipError_t launch_bwd_preprocess(const void* o, const void* dout, const float* l
                                  float* nd, const AttnShape& s, hipStream_t stream);
 
 // bf16 backward on MFMA, no atomics.  dK, dV: items from the backward
-// planner (kBwdBf16RowTile keys per item, kBwdBf16ColTile queries per step).
+// planner (kBwdBf16RowTile keys of one key/value head per item, kBwdBf16ColTile
+// queries per step, over every query head of the group).
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
                                 const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
@@ -81,11 +83,11 @@ inline int feature_chunks(int T, int d) {
 }
 
 // Writes features [H, 9] (if non-null) and updates ema [H, 9] (if non-null;
-// ema = x when init) from q, k, v [B,H,T,d] (bf16 or fp32) and the per-row
-// entropy / output norm [B,H,T] (nullptr: those features are 0).  partials:
+// ema = x when init) from q [B,H,T,d], k, v [B,H_kv,T,d] (bf16 or fp32) and the
+// per-row entropy / output norm [B,H,T] (nullptr: those features are 0).  partials:
 // (3 * 4 + 2) * H * B * feature_chunks(T, d) doubles of scratch.
 hipError_t launch_head_features(const void* q, const void* k, const void* v, bool is_bf16, const float* ent,
-                                const float* onorm, const int32_t* win_eff, int B, int H, int T, int d,
+                                const float* onorm, const int32_t* win_eff, int B, int H, int H_kv, int T, int d,
                                 float alpha, bool init, float* features, float* ema, double* partials,
                                 hipStream_t stream);
 

@@ -44,6 +44,11 @@ __device__ inline bool visible(int i, int j, int W, int S) { return j <= i && (j
 
 // Sink tiles an item visits before its window tiles [lo, hi).
 __device__ inline int n_sink_tiles(int S, int lo) { return min((S + kCols - 1) / kCols, lo); }
+
+// First element of the key/value head read by query head bh = b H + h: b H_kv + h / (H / H_kv).
+__device__ inline size_t kv_base(int bh, int H, int H_kv, int T, int D) {
+  return (static_cast<size_t>(bh / H) * H_kv + (bh % H) / (H / H_kv)) * T * D;
+}
 template <typename E> __device__ inline E from_f32(float x);
 template <> __device__ inline float from_f32<float>(float x) { return x; }
 
@@ -63,7 +68,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ENT, float* __restrict__ ONORM,
     const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff,
-    int H, int T, float c) {
+    int H, int H_kv, int T, float c) {
   __shared__ float ks[kCols * D];
   __shared__ float vs[kCols * D];
   const WorkItem it = items[blockIdx.x];
@@ -72,6 +77,7 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
   const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
   const int ns = n_sink_tiles(S, it.lo);
   const size_t base = static_cast<size_t>(it.bh) * T * D;
+  const size_t kvbase = kv_base(it.bh, H, H_kv, T, D);
   const int qi = it.tile * kRows + threadIdx.x;
   const bool row_ok = qi < T;
 
@@ -88,8 +94,8 @@ __global__ __launch_bounds__(kRows) void fwd_f32_kernel(
   for (int v = 0; v < ns + it.hi - it.lo; ++v) {
     const int k0 = (v < ns ? v : v - ns + it.lo) * kCols;
     __syncthreads();
-    stage_rows<float, D>(ks, K + base, k0, T);
-    stage_rows<float, D>(vs, V + base, k0, T);
+    stage_rows<float, D>(ks, K + kvbase, k0, T);
+    stage_rows<float, D>(vs, V + kvbase, k0, T);
     __syncthreads();
     for (int j0 = 0; j0 < kCols; j0 += kChunk) {
       float s[kChunk];
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dQ, const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
-    const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
+    const int32_t* __restrict__ sink_eff, int H, int H_kv, int T, float scale) {
   __shared__ float ks[kCols * D];
   __shared__ float vs[kCols * D];
   const WorkItem it = items[blockIdx.x];
@@ -187,6 +193,7 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
   const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
   const int ns = n_sink_tiles(S, it.lo);
   const size_t base = static_cast<size_t>(it.bh) * T * D;
+  const size_t kvbase = kv_base(it.bh, H, H_kv, T, D);
   const int qi = it.tile * kRows + threadIdx.x;
   const bool row_ok = qi < T;
   const float c = scale * kLog2e;
@@ -204,8 +211,8 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
   for (int v = 0; v < ns + it.hi - it.lo; ++v) {
     const int k0 = (v < ns ? v : v - ns + it.lo) * kCols;
     __syncthreads();
-    stage_rows<E, D>(ks, K + base, k0, T);
-    stage_rows<E, D>(vs, V + base, k0, T);
+    stage_rows<E, D>(ks, K + kvbase, k0, T);
+    stage_rows<E, D>(vs, V + kvbase, k0, T);
     __syncthreads();
     for (int j = 0; j < kCols; ++j) {
       const int key = k0 + j;
@@ -227,23 +234,25 @@ __global__ __launch_bounds__(kRows) void bwd_dq_simple_kernel(
   for (int x = 0; x < D; ++x) dQ[base + static_cast<size_t>(qi) * D + x] = from_f32<E>(dq[x] * scale);
 }
 
-// dK, dV: one key row per lane, over the backward work list (key tile, query tiles).
+// dK, dV: one key row per lane, over the backward work list: it.bh = b H_kv + g
+// is a key/value head, whose G = H / H_kv query heads are walked one after
+// another, each over the query tiles that see this key tile.
 template <typename E, int D>
 __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     const E* __restrict__ Q, const E* __restrict__ K, const E* __restrict__ V,
     const E* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
     E* __restrict__ dK, E* __restrict__ dV, const WorkItem* __restrict__ items,
-    const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int T, float scale) {
+    const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv, int T,
+    float scale) {
   __shared__ float qs[kCols * D];
   __shared__ float gs[kCols * D];
   __shared__ float ls[kCols];
   __shared__ float ds_[kCols];
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
-  const int W = win_eff[it.bh % H];
-  const int S = sink_eff == nullptr ? 0 : sink_eff[it.bh % H];
-  const size_t base = static_cast<size_t>(it.bh) * T * D;
-  const size_t rbase = static_cast<size_t>(it.bh) * T;
+  const int G = H / H_kv;
+  const int qh0 = (it.bh / H_kv) * H + (it.bh % H_kv) * G;  // first query head of the group (b H + h)
+  const size_t base = static_cast<size_t>(it.bh) * T * D;   // K, V, dK, dV
   const int kj = it.tile * kRows + threadIdx.x;
   const bool row_ok = kj < T;
   const float c = scale * kLog2e;
@@ -256,32 +265,42 @@ __global__ __launch_bounds__(kRows) void bwd_dkdv_simple_kernel(
     dk[x] = 0.f;
     dv[x] = 0.f;
   }
-  for (int qt = it.lo; qt < it.hi; ++qt) {
-    const int q0 = qt * kCols;
-    __syncthreads();
-    stage_rows<E, D>(qs, Q + base, q0, T);
-    stage_rows<E, D>(gs, dO + base, q0, T);
-    for (int e = threadIdx.x; e < kCols; e += blockDim.x) {
-      const int row = q0 + e;
-      ls[e] = row < T ? NL2[rbase + row] : 0.f;  // -lse * log2(e)
-      ds_[e] = row < T ? ND[rbase + row] : 0.f;
-    }
-    __syncthreads();
-    for (int i = 0; i < kCols; ++i) {
-      const int qrow = q0 + i;
-      if (!(visible(qrow, kj, W, S) && qrow < T && row_ok)) continue;
-      float s = 0.f, dp = 0.f;
-#pragma unroll
-      for (int x = 0; x < D; ++x) {
-        s = fmaf(qs[i * D + x], kr[x], s);
-        dp = fmaf(gs[i * D + x], vr[x], dp);
+  const int k0 = it.tile * kRows, k1 = min(T, k0 + kRows);
+  for (int j = 0; j < G; ++j) {
+    const int h = (qh0 + j) % H;
+    const int W = win_eff[h];
+    const int S = sink_eff == nullptr ? 0 : sink_eff[h];
+    // The query tiles that see keys [k0, k1) in this head (the planner's per-head range).
+    const int hi = (k0 < S ? T - 1 : min(T, k1 + W - 1) - 1) / kCols + 1;
+    const size_t qbase = static_cast<size_t>(qh0 + j) * T * D;
+    const size_t rbase = static_cast<size_t>(qh0 + j) * T;
+    for (int qt = it.lo; qt < hi; ++qt) {
+      const int q0 = qt * kCols;
+      __syncthreads();
+      stage_rows<E, D>(qs, Q + qbase, q0, T);
+      stage_rows<E, D>(gs, dO + qbase, q0, T);
+      for (int e = threadIdx.x; e < kCols; e += blockDim.x) {
+        const int row = q0 + e;
+        ls[e] = row < T ? NL2[rbase + row] : 0.f;  // -lse * log2(e)
+        ds_[e] = row < T ? ND[rbase + row] : 0.f;
       }
-      const float p = exp2f(fmaf(s, c, ls[i]));
-      const float dsv = p * (dp + ds_[i]);
+      __syncthreads();
+      for (int i = 0; i < kCols; ++i) {
+        const int qrow = q0 + i;
+        if (!(visible(qrow, kj, W, S) && qrow < T && row_ok)) continue;
+        float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int x = 0; x < D; ++x) {
-        dv[x] = fmaf(p, gs[i * D + x], dv[x]);
-        dk[x] = fmaf(dsv, qs[i * D + x], dk[x]);
+        for (int x = 0; x < D; ++x) {
+          s = fmaf(qs[i * D + x], kr[x], s);
+          dp = fmaf(gs[i * D + x], vr[x], dp);
+        }
+        const float p = exp2f(fmaf(s, c, ls[i]));
+        const float dsv = p * (dp + ds_[i]);
+#pragma unroll
+        for (int x = 0; x < D; ++x) {
+          dv[x] = fmaf(p, gs[i * D + x], dv[x]);
+          dk[x] = fmaf(dsv, qs[i * D + x], dk[x]);
+        }
       }
     }
   }
@@ -298,7 +317,7 @@ hipError_t fwd_f32_d(const float* q, const float* k, const float* v, float* o, f
                      float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
                      const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
   hipLaunchKernelGGL(fwd_f32_kernel<D>, dim3(n_items), dim3(kRows), 0, stream, q, k, v, o, lse, ent, onorm, items,
-                     win_eff, sink_eff, s.H, s.T, s.scale * kLog2e);
+                     win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -345,7 +364,7 @@ hipError_t launch_bwd_dq_simple(const float* q, const float* k, const float* v, 
                                 const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
 #define AAH_DQ(DD)                                                                                                \
   hipLaunchKernelGGL((bwd_dq_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, nl2, \
-                     nd, dq, items, win_eff, sink_eff, s.H, s.T, s.scale)
+                     nd, dq, items, win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DQ(32); break;
     case 64: AAH_DQ(64); break;
@@ -362,7 +381,7 @@ hipError_t launch_bwd_dkdv_simple(const float* q, const float* k, const float* v
                                   hipStream_t stream) {
 #define AAH_DKDV(DD)                                                                                            \
   hipLaunchKernelGGL((bwd_dkdv_simple_kernel<float, DD>), dim3(n_items), dim3(kRows), 0, stream, q, k, v, dout, \
-                     nl2, nd, dk, dv, items, win_eff, sink_eff, s.H, s.T, s.scale)
+                     nl2, nd, dk, dv, items, win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale)
   switch (s.d) {
     case 32: AAH_DKDV(32); break;
     case 64: AAH_DKDV(64); break;

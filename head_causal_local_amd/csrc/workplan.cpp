@@ -10,7 +10,10 @@
 // With sink keys ("Autonomy-of-Heads", section 5: a streaming head also keeps
 // its first tokens), a forward item additionally visits the sink tiles before
 // its window, and a backward item whose key tile holds a sink runs to the last
-// query tile.
+// query tile.  With grouped key/value heads (G query heads per key/value head),
+// the G heads' forward items share a queue (so their K/V tiles meet in one
+// XCD's L2), and one backward item covers a key tile of the shared head for
+// all G query heads, so dK and dV are summed in registers.
 #include "workplan.hpp"
 
 #include <algorithm>
@@ -23,7 +26,8 @@ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 struct Planned {
   WorkItem item;
-  int cost;  // streamed tiles the item visits
+  int cost;   // streamed tiles the item visits
+  int32_t group;  // key/value group: items of one group share a queue and sort next to each other
 };
 
 // Deal the items of each head to n_queues queues (longest head first, each to
@@ -51,10 +55,13 @@ std::vector<WorkItem> interleave(const std::vector<std::vector<Planned>>& per_he
   }
   size_t longest = 0;
   for (auto& q : queues) {
+    // Equal costs: group, then tile, then head, so that the query heads of one key/value group
+    // visit the same tile back to back (with one head per group this is head, then tile).
     std::stable_sort(q.begin(), q.end(), [](const Planned& a, const Planned& b) {
       if (a.cost != b.cost) return a.cost > b.cost;
-      if (a.item.bh != b.item.bh) return a.item.bh < b.item.bh;
-      return a.item.tile < b.item.tile;
+      if (a.group != b.group) return a.group < b.group;
+      if (a.item.tile != b.item.tile) return a.item.tile < b.item.tile;
+      return a.item.bh < b.item.bh;
     });
     longest = std::max(longest, q.size());
   }
@@ -72,51 +79,59 @@ int head_sink(const int32_t* sinks, const int32_t* windows, int h, int T) {
 
 }  // namespace
 
-std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                    int q_tile, int kv_tile, int n_queues) {
   const int n_qt = ceil_div(T, q_tile);
-  std::vector<std::vector<Planned>> per_head(static_cast<size_t>(B) * H);
+  const int G = H / H_kv;
+  // One list per (b, key/value group): its G query heads' items, dealt to one queue together.
+  std::vector<std::vector<Planned>> per_group(static_cast<size_t>(B) * H_kv);
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < H; ++h) {
       const int W = effective_window(windows[h], T);
       const int S = head_sink(sinks, windows, h, T);
-      auto& list = per_head[static_cast<size_t>(b) * H + h];
-      list.reserve(n_qt);
+      const int32_t group = b * H_kv + h / G;
+      auto& list = per_group[static_cast<size_t>(group)];
       for (int qt = 0; qt < n_qt; ++qt) {
         const int q0 = qt * q_tile;
         const int q1 = std::min(T, q0 + q_tile);
         const int key_first = std::max(0, q0 - W + 1);  // row q0's window start
         const int key_last = q1 - 1;                     // row q1-1's diagonal
         const WorkItem it{b * H + h, qt, key_first / kv_tile, key_last / kv_tile + 1};
-        list.push_back(Planned{it, it.hi - it.lo + sink_tiles(S, it.lo, kv_tile)});
+        list.push_back(Planned{it, it.hi - it.lo + sink_tiles(S, it.lo, kv_tile), group});
       }
     }
   }
-  return interleave(per_head, n_queues);
+  return interleave(per_group, n_queues);
 }
 
-std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                     int q_tile, int kv_tile, int n_queues) {
   const int n_kt = ceil_div(T, kv_tile);
-  std::vector<std::vector<Planned>> per_head(static_cast<size_t>(B) * H);
+  const int G = H / H_kv;
+  std::vector<std::vector<Planned>> per_group(static_cast<size_t>(B) * H_kv);
   for (int b = 0; b < B; ++b) {
-    for (int h = 0; h < H; ++h) {
-      const int W = effective_window(windows[h], T);
-      const int S = head_sink(sinks, windows, h, T);
-      auto& list = per_head[static_cast<size_t>(b) * H + h];
+    for (int g = 0; g < H_kv; ++g) {
+      const int32_t group = b * H_kv + g;
+      auto& list = per_group[static_cast<size_t>(group)];
       list.reserve(n_kt);
       for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * kv_tile;
         const int k1 = std::min(T, k0 + kv_tile);
-        const int query_first = k0;  // key k0's own row
-        // Last row that sees key k1-1, or every later row when the tile holds a sink key.
-        const int query_last = k0 < S ? T - 1 : std::min(T, k1 + W - 1) - 1;
-        const WorkItem it{b * H + h, kt, query_first / q_tile, query_last / q_tile + 1};
-        list.push_back(Planned{it, it.hi - it.lo});
+        int lo = 0, hi = 0, cost = 0;
+        for (int j = 0; j < G; ++j) {  // the group's query heads, each over its own range
+          const int h = g * G + j;
+          int lo_j = 0, hi_j = 0;
+          query_range(k0, k1, effective_window(windows[h], T), head_sink(sinks, windows, h, T), T, q_tile, &lo_j,
+                      &hi_j);
+          lo = lo_j;
+          hi = std::max(hi, hi_j);
+          cost += hi_j - lo_j;
+        }
+        list.push_back(Planned{WorkItem{group, kt, lo, hi}, cost, group});
       }
     }
   }
-  return interleave(per_head, n_queues);
+  return interleave(per_group, n_queues);
 }
 
 }  // namespace aah

@@ -9,7 +9,7 @@
 namespace aah {
 
 struct WorkItem {
-  int32_t bh;    // b * H + h, or -1 for a padding slot
+  int32_t bh;    // b * H + h (forward: query head; backward: b * H_kv + key/value head), or -1 for padding
   int32_t tile;  // stationary row tile
   int32_t lo;    // first streamed tile (inclusive)
   int32_t hi;    // last streamed tile (exclusive)
@@ -44,13 +44,24 @@ inline int64_t pair_count(int T, int w, int s = 0) {
   return W * (W + 1) / 2 + U * W + sinks;
 }
 
+// Query tiles [lo, hi) that see keys [k0, k1) of a query head with window w and
+// effective sink S (every later query when the tile holds a sink key).
+inline void query_range(int k0, int k1, int W, int S, int T, int q_tile, int* lo, int* hi) {
+  const int last = k0 < S ? T - 1 : (k1 + W - 1 < T ? k1 + W - 1 : T) - 1;
+  *lo = k0 / q_tile;
+  *hi = last / q_tile + 1;
+}
+
 // Forward items: one per (b, h, query tile), with the key-tile range it needs.
 // sinks: int32[H] or nullptr; an item's sink tiles are implied (sink_tiles).
-std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+// The H / H_kv query heads of a key/value group go to the same queue.
+std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                    int q_tile, int kv_tile, int n_queues);
 
-// Backward items: one per (b, h, key tile), with the query-tile range that sees it.
-std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+// Backward items: one per (b, key/value head g, key tile); [lo, hi) spans the
+// query tiles that see the keys in any of the group's query heads (each head's
+// own range is query_range, starting at the same lo).
+std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                     int q_tile, int kv_tile, int n_queues);
 
 }  // namespace aah

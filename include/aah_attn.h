@@ -17,9 +17,17 @@
  * return AAH_ERR_UNSUPPORTED.
  *
  * Conventions shared by every entry point:
- *   - Q, K, V, O, dO, dQ, dK, dV are dense row-major [B, H, T, d] tensors
- *     (d fastest), all of one dtype `dt`, device pointers aligned to 16 bytes.
- *     LSE and the backward's D are fp32 [B, H, T].
+ *   - Q, O, dO, dQ are dense row-major [B, H, T, d] tensors and K, V, dK, dV
+ *     [B, H_kv, T, d] (d fastest), all of one dtype `dt`, device pointers
+ *     aligned to 16 bytes.  LSE and the backward's D are fp32 [B, H, T].
+ *   - H_kv (1 <= H_kv <= H, H_kv divides H) is the number of key/value heads:
+ *     query head h reads key/value head h / G, G = H / H_kv, so the G query
+ *     heads of a group are consecutive (grouped-query attention; H_kv = H is
+ *     plain multi-head attention).  Windows and sinks stay per query head, and
+ *     the gradients of a shared key/value head sum over its G query heads.
+ *     "Asymmetric Attention Heads" section 3.3 sets the method beside grouped
+ *     K/V sharing and appendix A.3 inserts it into a grouped-query model;
+ *     "Autonomy-of-Heads" section 4 assigns query heads to KV groups.
  *   - `windows` is a HOST pointer to int32[H], one window per head, shared by
  *     every batch entry (section 5.8 maps one decision per head).  Each entry
  *     must be >= 1; entries above T act as T.  No lower clamp is applied: the
@@ -59,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 4
+#define AAH_ABI_VERSION 5
 
 typedef enum {
   AAH_OK = 0,
@@ -103,7 +111,7 @@ const char* aah_last_error_detail(void);
  * (a non-NULL workspace is accepted and ignored).
  */
 aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
-                        const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
+                        const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
                         aah_dtype dt, float scale, void* o, float* lse,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
@@ -120,8 +128,8 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
  * 2^-7 H + 2^-8 of the exact H.
  */
 aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
-                             const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt, float scale, void* o,
-                             float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream);
+                             const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
+                             void* o, float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream);
 
 /*
  * Per-head controller features ("Asymmetric Attention Heads" section 5.3):
@@ -130,7 +138,9 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
  * standard deviation, both over batch, sequence and head dimension of head h;
  * e_h and n_h are the means over batch and rows of row_entropy and row_onorm
  * (from aah_attn_fwd_diag; pass both NULL when there are none yet: then they
- * are 0); rho_h = min(W_h, T) / T, the head's window usage.  Writes x to
+ * are 0); rho_h = min(W_h, T) / T, the head's window usage.  With grouped
+ * key/value heads the k and v entries of query head h are those of its
+ * group's head.  Writes x to
  * features (device float[H * 9], row h = x_h; may be NULL) and smooths
  * features_ema (device float[H * 9], in/out; may be NULL):
  *   features_ema = init ? x : alpha * features_ema + (1 - alpha) * x,
@@ -142,12 +152,13 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
 size_t aah_head_features_workspace_size(int B, int H, int T, int d);
 
 aah_status aah_head_features(const void* q, const void* k, const void* v, const float* row_entropy,
-                             const float* row_onorm, const int32_t* windows, int B, int H, int T, int d,
+                             const float* row_onorm, const int32_t* windows, int B, int H, int H_kv, int T, int d,
                              aah_dtype dt, float alpha, int init, float* features, float* features_ema,
                              void* workspace, size_t workspace_bytes, aah_stream_t stream);
 
 /*
- * Backward pass: gradients of sum(O * dout) with respect to q, k and v, given
+ * Backward pass: gradients of sum(O * dout) with respect to q, k and v (dk, dv
+ * [B, H_kv, T, d]: a shared head's gradient sums over its query heads), given
  * the forward's o and lse (the log-sum-exp saved by aah_attn_fwd with the same
  * scale, windows and sinks).  Writes dq, dk, dv [B,H,T,d] of dtype dt (each element
  * exactly once: no atomics, results are bitwise reproducible).  Needs a device
@@ -157,7 +168,7 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
  */
 aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
                         const void* o, const void* dout, const float* lse,
-                        const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d,
+                        const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
                         aah_dtype dt, float scale, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
@@ -175,14 +186,14 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
  *     aah_attn_bwd_dq has completed on the same workspace.
  */
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int T,
-                           int d, aah_dtype dt, float scale, void* dq, void* workspace, size_t workspace_bytes,
-                           aah_stream_t stream);
+                           const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                           int T, int d, aah_dtype dt, float scale, void* dq, void* workspace,
+                           size_t workspace_bytes, aah_stream_t stream);
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                             const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d, aah_dtype dt,
-                             float scale, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
-                             aah_stream_t stream);
+                             const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
+                             aah_dtype dt, float scale, void* dk, void* dv, const void* workspace,
+                             size_t workspace_bytes, aah_stream_t stream);
 
 /*
  * Decoding over per-head trimmed K/V caches (bf16).
@@ -250,18 +261,21 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
  * Forward: for each (b, h, query tile qt) with rows [qt*q_tile, min(T, (qt+1)*q_tile)),
  * the keys needed are [max(0, q0 - W + 1), q1 - 1], i.e. key tiles
  * [floor(max(0, q0 - W + 1) / kv_tile), floor((q1 - 1) / kv_tile) + 1).
- * Backward: for each (b, h, key tile kt) with keys [k0, k1), the queries that
- * see them are [k0, min(T, k1 + W - 1)), i.e. query tiles
- * [floor(k0 / q_tile), floor((min(T, k1 + W - 1) - 1) / q_tile) + 1).
+ * Backward: for each (b, key/value head g, key tile kt) with keys [k0, k1),
+ * bh = b * H_kv + g; in query head h the queries that see them are
+ * [k0, min(T, k1 + W - 1)), i.e. query tiles
+ * [floor(k0 / q_tile), floor((min(T, k1 + W - 1) - 1) / q_tile) + 1); the item's
+ * [lo, hi) is the union over the group's query heads, its cost their sum.
  * W = min(windows[h], T).  Tiles wholly outside every row's window are never
  * listed.  With sinks (NULL = none), S = min(sinks[h], T - W): a forward
  * item also visits the sink key tiles [0, min(ceil(S / kv_tile), lo)) before
  * [lo, hi) (implied, not stored); a backward item whose keys start below S
  * runs to the last query tile, [floor(k0 / q_tile), ceil(T / q_tile)).
- * Items are grouped into `n_queues` queues (heads are dealt to
+ * Items are grouped into `n_queues` queues (key/value groups -- the G query
+ * heads of one key/value head, or one head when H_kv = H -- are dealt to
  * queues longest-total-first, each to the least-loaded queue); each queue is
  * sorted by item cost (tiles visited, sink tiles included) descending, ties
- * by (bh, tile) ascending; the
+ * by (group, tile, bh) ascending; the
  * output interleaves the queues so that slot s belongs to queue s % n_queues,
  * padding short queues with bh = -1 slots.  With n_queues = 8 this matches
  * the round-robin placement of workgroups on MI355X's eight XCDs, so the
@@ -271,11 +285,11 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
  * and always stores the full slot count in *n_items; returns
  * AAH_ERR_INVALID_ARG if capacity is too small (after setting *n_items).
  */
-aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
 
-aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int T,
+aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
 

@@ -11,7 +11,11 @@ weights; N(0, 1) activations stand in for the projected Q/K/V.  The
 streaming-head workload follows "Autonomy-of-Heads" (section 5: retrieval
 heads keep full attention, streaming heads keep sink + recent-window caches;
 section 6.1: 128 sinks and a recent window of 256; section 6.4: sparsity
-around 0.5) on the same 1B-scale layer shape.
+around 0.5) on the same 1B-scale layer shape.  The grouped-query workload has
+32 query heads over 8 key/value heads (the Qwen3 grouping "Autonomy-of-Heads"
+section 6.1 lists; AAH appendix A.3 transfers the method to a pretrained Qwen3
+model at context 4096 in bf16), head dimension 128, and per-query-head windows
+drawn like the 1B-scale groups.
 
 Recipe (fixed, so every consumer sees identical bits):
   * ``numpy.random.default_rng(seed)``; fp32 standard normals drawn in the
@@ -75,13 +79,15 @@ def _draw(rng: np.random.Generator, shape, dtype: str):
 
 def random_workload(B: int, H: int, T: int, d: int, windows, dtype: str = "bf16",
                     seed: int = 0, backward: bool = True, name: str = "random",
-                    value_scale: float = 1.0, sinks=None) -> Workload:
-    """Q, K, V (and dO) ~ N(0, 1) * value_scale for an arbitrary shape and window vector."""
+                    value_scale: float = 1.0, sinks=None, H_kv: Optional[int] = None) -> Workload:
+    """Q, K, V (and dO) ~ N(0, 1) * value_scale for an arbitrary shape and window vector;
+    K and V have H_kv heads (default H)."""
     rng = np.random.default_rng(seed)
-    shape = (B, H, T, d)
+    H_kv = H if H_kv is None else H_kv
     out = {}
     bits = {}
     for key in ("q", "k", "v", "do"):
+        shape = (B, H_kv if key in ("k", "v") else H, T, d)
         x = rng.standard_normal(size=shape, dtype=np.float32)
         if value_scale != 1.0:
             x = (x * np.float32(value_scale)).astype(np.float32)
@@ -121,6 +127,8 @@ DESCRIPTIONS = {
     "4c": "coverage control fwd+bwd: B=4 H=32 T=4096 d=64 bf16, even heads 512, odd heads 4096",
     5: "streaming heads fwd+bwd: B=4 H=32 T=4096 d=64 bf16, heads 0-15 full causal (4096), "
        "heads 16-31 sink 128 + recent window 256",
+    6: "grouped-query layer fwd+bwd: B=4 H=32 H_kv=8 T=4096 d=128 bf16, "
+       "per-query-head windows from {512..4096}, P=(.5,.25,.125,.125)",
 }
 
 
@@ -179,4 +187,14 @@ def make_workload(idx, seed: int = 0) -> Workload:
                         scale=1.0 / np.sqrt(d), q=arrs["q"], k=arrs["k"], v=arrs["v"],
                         do=arrs["do"] if backward else None, bits=bits, backward=backward,
                         meta=meta, sinks=sinks)
+    if idx == 6:
+        B, H, H_kv, T, d = 4, 32, 8, 4096, 128
+        rng = np.random.default_rng(seed)
+        arrs, bits = {}, {}
+        for key in ("q", "k", "v", "do"):
+            arrs[key], bits[key] = _draw(rng, (B, H_kv if key in ("k", "v") else H, T, d), "bf16")
+        windows = rng.choice(np.array(CANDIDATE_WINDOWS), size=H, p=[0.5, 0.25, 0.125, 0.125]).astype(np.int32)
+        return Workload(name="gqa-B4-H32-Hkv8-T4096-d128-fwdbwd", B=B, H=H, T=T, d=d, dtype="bf16",
+                        windows=windows, scale=1.0 / np.sqrt(d), q=arrs["q"], k=arrs["k"], v=arrs["v"],
+                        do=arrs["do"], bits=bits, backward=True, meta={"H_kv": H_kv})
     raise KeyError(f"unknown workload {idx!r}")

@@ -8,7 +8,10 @@ code with the oracle and does not import it.
 
 With sink sizes, the forward items visit the implied sink tiles
 [0, min(ceil(S / kv_tile), lo)) first, S = min(sinks[h], T - W) (the library's
-effective sink), exactly as the kernels do.
+effective sink), exactly as the kernels do.  With grouped key/value heads
+(k, v [B, H_kv, T, d]) forward items read head h // G, and a backward item
+(bh = b H_kv + g) walks the group's query heads, each over its own query-tile
+range from lo, as the kernels do.
 """
 import numpy as np
 
@@ -30,6 +33,7 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
         if bh < 0:
             continue
         b, h = divmod(int(bh), H)
+        g = h // (H // k.shape[1])
         W = min(int(windows[h]), T)
         S = _eff_sink(sinks, h, T, W)
         rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
@@ -39,7 +43,7 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
         n_sink = min(-(-S // kv_tile), int(lo))
         for kt in list(range(n_sink)) + list(range(lo, hi)):
             keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
-            s = scale * q[b, h, rows] @ k[b, h, keys].T
+            s = scale * q[b, h, rows] @ k[b, g, keys].T
             ok = _visible(rows, keys, W, S)
             s = np.where(ok, s, -np.inf)
             m_new = np.maximum(m, s.max(axis=1))
@@ -47,7 +51,7 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
             alpha = np.exp(m - m_use)
             p = np.exp(s - m_use[:, None])
             l = l * alpha + p.sum(axis=1)
-            acc = acc * alpha[:, None] + p @ v[b, h, keys]
+            acc = acc * alpha[:, None] + p @ v[b, g, keys]
             m = m_new
         O[b, h, rows] = acc / l[:, None]
         L[b, h, rows] = m + np.log(l)
@@ -55,39 +59,43 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
 
 
 def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None):
-    """KV-stationary backward over the backward work list: dK, dV per key tile,
-    dQ accumulated from every key tile (as the device's atomic dQ does)."""
+    """Key-stationary backward over the backward work list: dK, dV per key tile of a key/value head
+    (summed over its query heads), dQ accumulated from every key tile."""
     q, k, v, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, lse))
     B, H, T, d = q.shape
+    H_kv = k.shape[1]
+    G = H // H_kv
     dq = np.zeros_like(q)
     dk = np.full_like(k, np.nan)
     dv = np.full_like(v, np.nan)
-    # D_i = dO_i . O_i, with O recomputed from lse over the full window (as the preprocess does from O).
     for bh, kt, lo, hi in items:
         if bh < 0:
             continue
-        b, h = divmod(int(bh), H)
-        W = min(int(windows[h]), T)
-        S = _eff_sink(sinks, h, T, W)
+        b, g = divmod(int(bh), H_kv)
         keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
+        k0, k1 = int(keys[0]), int(keys[-1]) + 1
         dk_t = np.zeros((len(keys), d))
         dv_t = np.zeros((len(keys), d))
-        for qt in range(lo, hi):
-            rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
-            s = scale * q[b, h, rows] @ k[b, h, keys].T
-            ok = _visible(rows, keys, W, S)
-            p = np.where(ok, np.exp(s - lse[b, h, rows][:, None]), 0.0)
-            # D for these rows: sum over the row's whole key set of P * dP
-            Drow = np.empty(len(rows))
-            for n, i in enumerate(rows):
-                kk = np.union1d(np.arange(max(0, i - W + 1), i + 1), np.arange(min(S, i + 1)))
-                pi = np.exp(scale * k[b, h, kk] @ q[b, h, i] - lse[b, h, i])
-                Drow[n] = pi @ (v[b, h, kk] @ do[b, h, i])
-            dp = do[b, h, rows] @ v[b, h, keys].T
-            ds = p * (dp - Drow[:, None])
-            dv_t += p.T @ do[b, h, rows]
-            dk_t += scale * ds.T @ q[b, h, rows]
-            dq[b, h, rows] += scale * ds @ k[b, h, keys]
-        dk[b, h, keys] = dk_t
-        dv[b, h, keys] = dv_t
+        for h in range(g * G, (g + 1) * G):
+            W = min(int(windows[h]), T)
+            S = _eff_sink(sinks, h, T, W)
+            last = T - 1 if k0 < S else min(T, k1 + W - 1) - 1
+            for qt in range(lo, last // q_tile + 1):
+                rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
+                s = scale * q[b, h, rows] @ k[b, g, keys].T
+                ok = _visible(rows, keys, W, S)
+                p = np.where(ok, np.exp(s - lse[b, h, rows][:, None]), 0.0)
+                # D for these rows: sum over the row's whole key set of P * dP
+                Drow = np.empty(len(rows))
+                for n, i in enumerate(rows):
+                    kk = np.union1d(np.arange(max(0, i - W + 1), i + 1), np.arange(min(S, i + 1)))
+                    pi = np.exp(scale * k[b, g, kk] @ q[b, h, i] - lse[b, h, i])
+                    Drow[n] = pi @ (v[b, g, kk] @ do[b, h, i])
+                dp = do[b, h, rows] @ v[b, g, keys].T
+                ds = p * (dp - Drow[:, None])
+                dv_t += p.T @ do[b, h, rows]
+                dk_t += scale * ds.T @ q[b, h, rows]
+                dq[b, h, rows] += scale * ds @ k[b, g, keys]
+        dk[b, g, keys] = dk_t
+        dv[b, g, keys] = dv_t
     return dq, dk, dv

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 4
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 5
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -42,13 +42,15 @@ def test_abi_version_and_status_strings():
 FAKE = 0x10000  # an aligned, never-dereferenced stand-in for a device pointer
 
 
-def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, scale=0.125, sinks=None):
+def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, scale=0.125, sinks=None,
+         H_kv=None):
     w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
     H = len(w) if H is None else H
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if len(w) else None
     sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.int32))
     sp = None if sk is None else sk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    return _lib.lib().aah_attn_fwd(q, k, v, wp, sp, B, H, T, d, dt, scale, o, lse, None, 0, None)
+    H_kv = H if H_kv is None else H_kv
+    return _lib.lib().aah_attn_fwd(q, k, v, wp, sp, B, H, H_kv, T, d, dt, scale, o, lse, None, 0, None)
 
 
 @pytest.mark.parametrize("kwargs,status", [
@@ -67,6 +69,9 @@ def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
     (dict(windows=[4], scale=float("inf")), 1),
     (dict(windows=[4, 8], sinks=[0, -1]), 1),     # sink size < 0
     (dict(windows=[4, 8], sinks=[2, 3], d=48), 2),
+    (dict(windows=[4, 8, 8, 8], H_kv=3), 1),      # H_kv must divide H
+    (dict(windows=[4, 8], H_kv=0), 1),
+    (dict(windows=[4, 8], H_kv=4), 1),            # H_kv > H
 ])
 def test_fwd_validation(kwargs, status):
     st = _fwd(**kwargs)
@@ -75,11 +80,11 @@ def test_fwd_validation(kwargs, status):
 
 
 def test_fwd_null_windows():
-    st = _lib.lib().aah_attn_fwd(FAKE, FAKE, FAKE, None, None, 1, 1, 8, 64, 0, 0.1, FAKE, FAKE, None, 0, None)
+    st = _lib.lib().aah_attn_fwd(FAKE, FAKE, FAKE, None, None, 1, 1, 1, 8, 64, 0, 0.1, FAKE, FAKE, None, 0, None)
     assert st == 1
 
 
-def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE, sinks=None):
+def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE, sinks=None, H_kv=None):
     w = np.ascontiguousarray(np.asarray(windows, dtype=np.int32))
     H = len(w)
     need = aah.workspace_size(B, H, T, d, "bf16" if dt == 0 else "f32")
@@ -87,8 +92,8 @@ def _bwd(windows, ws=FAKE, ws_bytes=None, B=1, T=64, d=64, dt=0, dq=FAKE, sinks=
     sk = None if sinks is None else np.ascontiguousarray(np.asarray(sinks, dtype=np.int32))
     sp = None if sk is None else sk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     return _lib.lib().aah_attn_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                   w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), sp, B, H, T, d, dt, 0.125,
-                                   dq, FAKE, FAKE, ws, ws_bytes, None)
+                                   w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), sp, B, H,
+                                   H if H_kv is None else H_kv, T, d, dt, 0.125, dq, FAKE, FAKE, ws, ws_bytes, None)
 
 
 def test_bwd_validation():
@@ -99,6 +104,7 @@ def test_bwd_validation():
     assert _bwd([4], ws=FAKE + 16) == 1       # workspace must be 256-byte aligned
     assert _bwd([4], d=40) == 2
     assert _bwd([4, 2], sinks=[1, -5]) == 1
+    assert _bwd([4, 2, 3], H_kv=2) == 1
 
 
 def test_workspace_sizes():
@@ -117,26 +123,27 @@ def test_bwd_step_validation():
     w = np.array([4, 0], dtype=np.int32)
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     need = aah.workspace_size(1, 2, 64, 64, "bf16")
-    assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need,
                                  None) == 1
     w[1] = 3
     bad = np.array([0, -1], dtype=np.int32)
     assert lib.aah_attn_bwd_dkdv(FAKE, FAKE, FAKE, FAKE, wp, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
-                                 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need, None) == 1   # sink < 0
-    # aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, T, d, dt, scale, dq, workspace, bytes, stream)
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, 0, FAKE, need,
+                                 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, need, None) == 1   # sink < 0
+    # aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, H_kv, T, d, dt, scale, dq, workspace, bytes,
+    #                 stream)
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, 0, FAKE, need,
                                None) == 1                                                      # NULL dq
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, 8,
                                None) == 3                                                      # small ws
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 48, 0, 0.1, FAKE, FAKE, need,
                                None) == 2                                                      # d = 48
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 0, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, 0, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
                                None) == 1                                                      # NULL lse
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, 0, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, 0, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, need,
                                None) == 1                                                      # NULL o
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.0, FAKE, FAKE, need,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.0, FAKE, FAKE, need,
                                None) == 1                                                      # scale 0
-    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
+    assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
                                need, None) == 1                                                # scale inf
 
 
@@ -183,7 +190,7 @@ def test_plan_capacity_reporting():
     lib = _lib.lib()
     w = np.array([5, 9], dtype=np.int32)
     n = ctypes.c_int64()
-    st = lib.aah_plan_fwd(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 2, 2, 100, 16, 16, 8, None, 0,
+    st = lib.aah_plan_fwd(w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 2, 2, 2, 100, 16, 16, 8, None, 0,
                           ctypes.byref(n))
     assert st == 1 and n.value >= 2 * 2 * 7
 
@@ -245,22 +252,23 @@ def test_diag_and_feature_validation():
     lib = _lib.lib()
     w = np.array([4, 9], dtype=np.int32)
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    # aah_attn_fwd_diag(q, k, v, windows, sinks, B, H, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream)
-    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, 0, FAKE, None) == 1
-    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, FAKE + 2,
+    # aah_attn_fwd_diag(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm,
+    #                   stream)
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, 0, FAKE, None) == 1
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, FAKE + 2,
                                  None) == 1                                     # misaligned
-    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 64, 48, 0, 0.1, FAKE, FAKE, FAKE, FAKE,
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 48, 0, 0.1, FAKE, FAKE, FAKE, FAKE,
                                  None) == 2                                     # d = 48
     need = aah.head_features_workspace_size(2, 2, 64, 64)
-    assert need == 256 * -(-(3 * 2 * 2 * 1 * 4 * 8) // 256)                     # one 32768-element span per slice
-    assert aah.head_features_workspace_size(1, 1, 4096, 128) == 256 * -(-(3 * 16 * 4 * 8) // 256)
+    assert need == 256 * -(-(14 * 2 * 2 * 1 * 8) // 256)                        # one 32768-element span per slice
+    assert aah.head_features_workspace_size(1, 1, 4096, 128) == 256 * -(-(14 * 16 * 8) // 256)
     assert aah.head_features_workspace_size(0, 1, 1, 64) == 0
 
-    def feat(ent=FAKE, on=FAKE, feats=FAKE, ema=FAKE, alpha=0.9, ws=FAKE, nbytes=need, d=64):
-        # aah_head_features(q, k, v, row_entropy, row_onorm, windows, B, H, T, d, dt, alpha, init,
+    def feat(ent=FAKE, on=FAKE, feats=FAKE, ema=FAKE, alpha=0.9, ws=FAKE, nbytes=need, d=64, H_kv=2):
+        # aah_head_features(q, k, v, row_entropy, row_onorm, windows, B, H, H_kv, T, d, dt, alpha, init,
         #                   features, features_ema, workspace, bytes, stream)
-        return lib.aah_head_features(FAKE, FAKE, FAKE, ent, on, wp, 2, 2, 64, d, 0, alpha, 0, feats, ema, ws, nbytes,
-                                     None)
+        return lib.aah_head_features(FAKE, FAKE, FAKE, ent, on, wp, 2, 2, H_kv, 64, d, 0, alpha, 0, feats, ema, ws,
+                                     nbytes, None)
     assert feat(ent=0) == 1                  # one diagnostic row array without the other
     assert feat(feats=0, ema=0) == 1         # nothing to write
     assert feat(alpha=1.5) == 1
@@ -268,3 +276,4 @@ def test_diag_and_feature_validation():
     assert feat(nbytes=need - 8) == 3
     assert feat(ws=FAKE + 64) == 1           # workspace must be 256-byte aligned
     assert feat(d=40) == 2
+    assert feat(H_kv=3) == 1

@@ -196,3 +196,57 @@ def test_emulated_backward_with_sinks_equals_oracle(B, H, T, windows, sinks, qt_
 def test_plan_rejects_negative_sinks():
     with pytest.raises(aah.AahError):
         aah.plan_fwd([3, 4], 1, 2, 16, 8, 8, sinks=[0, -1])
+
+
+GQA_CASES = [
+    # (B, H, H_kv, T, windows, sinks, q_tile, kv_tile, n_queues)
+    (2, 4, 2, 100, [1, 30, 7, 100], None, 16, 32, 8),
+    (1, 6, 2, 77, [5, 5, 5, 60, 1, 200], [0, 3, 0, 0, 10, 2], 8, 16, 3),
+    (1, 8, 1, 64, [2, 4, 8, 16, 32, 64, 3, 9], None, 16, 16, 8),
+]
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,windows,sinks,qt_,kt_,nq", GQA_CASES)
+def test_gqa_plans(B, H, H_kv, T, windows, sinks, qt_, kt_, nq):
+    """Forward: the items are those of plain attention, with the G query heads of a key/value group in one queue.
+    Backward: one item per (b, key/value head, key tile) whose range is the union of the group's per-head
+    ranges."""
+    G = H // H_kv
+    f = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks, H_kv=H_kv)
+    plain = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks)
+    assert {tuple(x) for x in f[f[:, 0] >= 0]} == {tuple(x) for x in plain[plain[:, 0] >= 0]}
+    queue_of = {}
+    for slot, (bh, _, _, _) in enumerate(f):
+        if bh >= 0:
+            queue_of.setdefault((bh // H, (bh % H) // G), set()).add(slot % nq)
+    assert all(len(v) == 1 for v in queue_of.values())
+    b_items = aah.plan_bwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks, H_kv=H_kv)
+    real = b_items[b_items[:, 0] >= 0]
+    assert len({(int(x[0]), int(x[1])) for x in real}) == len(real) == B * H_kv * -(-T // kt_)
+    for bh, kt, lo, hi in real:
+        g = bh % H_kv
+        need = set()
+        for h in range(g * G, (g + 1) * G):
+            s = 0 if sinks is None else sinks[h]
+            for j in range(kt * kt_, min(T, (kt + 1) * kt_)):
+                for i in range(j, T):
+                    if j > i - windows[h] or j < s:
+                        need.add(i // qt_)
+        assert need == set(range(lo, hi))
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,windows,sinks,qt_,kt_,nq", GQA_CASES)
+def test_emulated_gqa_equals_oracle(B, H, H_kv, T, windows, sinks, qt_, kt_, nq):
+    rng = np.random.default_rng(25)
+    q, do = (rng.standard_normal((B, H, T, 8)) for _ in range(2))
+    k, v = (rng.standard_normal((B, H_kv, T, 8)) for _ in range(2))
+    f = aah.plan_fwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks, H_kv=H_kv)
+    O, L = emulate_forward(f, q, k, v, windows, 0.4, qt_, kt_, sinks=sinks)
+    Or, Lr = oracle.attn_fwd_ref(q, k, v, windows, 0.4, sinks=sinks)
+    np.testing.assert_allclose(O, Or, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, Lr, rtol=0, atol=1e-12)
+    bi = aah.plan_bwd(windows, B, H, T, qt_, kt_, nq, sinks=sinks, H_kv=H_kv)
+    dq, dk, dv = emulate_backward(bi, q, k, v, do, Lr, windows, 0.4, qt_, kt_, sinks=sinks)
+    rq, rk, rv = oracle.attn_bwd_ref(q, k, v, windows, 0.4, do, sinks=sinks)
+    for a, r in ((dq, rq), (dk, rk), (dv, rv)):
+        np.testing.assert_allclose(a, r, rtol=0, atol=1e-11)
