@@ -58,23 +58,27 @@ def parse():
 def bench_decode(args, wl):
     """Decoding over per-head trimmed K/V caches: the layer's caches hold positions 0..T-2 (a prefill), and
     every timed step decodes the token at position T-1 (every ring full; repeating the step rewrites the same
-    row and reads the same bytes).  Bound: HBM.  Algorithmic bytes per step = the K and V rows attended
-    (2 * 2 d bytes each) + q, k_new, v_new read + o written + the new K/V rows written + lse."""
+    row and reads the same bytes).  Bound: HBM.  Algorithmic bytes per step = the cached K and V rows
+    (2 * 2 d bytes each; with grouped key/value heads each row once for its group) + q, k_new, v_new read +
+    o written + the new K/V rows written + lse."""
     import torch
     import head_causal_local_amd as aah
     B, H, T, d = wl.B, wl.H, wl.T, wl.d
     k, v, q = to_dev(wl, "k"), to_dev(wl, "v"), to_dev(wl, "q")
-    kc, vc = aah.kv_cache_fill(k[:, :, :T - 1].contiguous(), v[:, :, :T - 1].contiguous(), wl.windows, T)
+    H_kv = k.shape[1]
+    kc, vc = aah.kv_cache_fill(k[:, :, :T - 1].contiguous(), v[:, :, :T - 1].contiguous(), wl.windows, T,
+                               sinks=wl.sinks)
     qt, kt, vt = (x[:, :, T - 1].contiguous() for x in (q, k, v))
     pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
-    ws = torch.zeros(aah.decode_workspace_size(wl.windows, B, T, d), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(aah.decode_workspace_size(wl.windows, B, T, d, sinks=wl.sinks, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
     o = torch.empty_like(qt)
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
     def step():
         aah.attn_decode(qt, kt, vt, kc, vc, pos, wl.windows, T, scale=wl.scale, out=o, lse=lse, workspace=ws,
-                        stream=stream)
+                        stream=stream, sinks=wl.sinks)
 
     for _ in range(args.warmup):
         step()
@@ -98,7 +102,7 @@ def bench_decode(args, wl):
         with torch.cuda.graph(g, stream=gs):
             for _ in range(10):
                 aah.attn_decode(qt, kt, vt, kc, vc, pos, wl.windows, T, scale=wl.scale, out=o, lse=lse,
-                                workspace=ws, stream=gs)
+                                workspace=ws, stream=gs, sinks=wl.sinks)
     stream.wait_stream(gs)
     torch.cuda.synchronize()
     reps = max(1, args.steps // 10)
@@ -110,8 +114,9 @@ def bench_decode(args, wl):
     e1.record(stream)
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (10 * reps)
-    rows = int(sum(min(int(w), T) for w in wl.windows))            # attended rows per batch entry (every ring full)
-    alg = B * (rows * 2 * 2 * d + 3 * H * 2 * d + H * 2 * d + 2 * H * 2 * d + H * 4)
+    # Every cached row is read at position T - 1 (rings full, sinks before every window).
+    rows = aah.kv_cache_rows(wl.windows, T, sinks=wl.sinks, H_kv=H_kv)
+    alg = B * (rows * 2 * 2 * d + H * 2 * d + 2 * H_kv * 2 * d + H * 2 * d + 2 * H_kv * 2 * d + H * 4)
     gbs = alg / (us * 1e-6) / 1e9
     out = {
         "metric": "decode step: algorithmic HBM bytes per step / device time per step (graph replay; "
@@ -127,14 +132,17 @@ def bench_decode(args, wl):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (N(0,1) bf16 Q/K/V, seed 0)",
-        "config": {"workload": wl.name + " decode at position T-1", "B": B, "H": H, "T_max": T, "d": d,
-                   "windows": [int(x) for x in wl.windows], "cache_rows_per_batch_entry": rows,
+        "config": {"workload": wl.name + " decode at position T-1", "B": B, "H": H, "H_kv": H_kv, "T_max": T, "d": d,
+                   "windows": [int(x) for x in wl.windows],
+                   **({"sinks": [int(x) for x in wl.sinks]} if wl.sinks is not None else {}),
+                   "cache_rows_per_batch_entry": rows,
                    "step_us": round(us, 3), "eager_step_us": round(eager_us, 3),
                    "tokens_per_s": round(B / (us * 1e-6), 1),
                    "algorithmic_bytes_per_step": int(alg)},
-        "roofline": {"kernel": "decode_kernel<64>", "bound": "hbm",
+        "roofline": {"kernel": f"decode_kernel<{d}, {'true' if H_kv != H else 'false'}>", "bound": "hbm",
                      "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": measured_traffic("decode_kernel<64>"),
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(f"decode_kernel<{d}, {'true' if H_kv != H else 'false'}>", args.workload),
                      "avg_launch_us": round(us, 3),
                      "algorithmic_bytes_per_launch": int(alg)},
     }
@@ -238,8 +246,9 @@ KERNEL_SOURCES = {  # kernel template name -> its source file
 }
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from profiles/hbm_traffic.txt, if taken on the current kernel source."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/hbm_traffic.txt, if taken on the current
+    kernel source."""
     import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hbm_traffic.txt")
@@ -251,10 +260,10 @@ def measured_traffic(kernel):
         parts = line.split()
         if line.startswith("#"):
             continue
-        # <kernel name (may hold spaces)> <source sha16> <fetch bytes> <write bytes>
-        parts = line.rsplit(None, 3)
-        if len(parts) == 4 and parts[0] == kernel and parts[1] == sha:
-            return int(parts[2]) + int(parts[3])
+        # <kernel name (may hold spaces)> <workload> <source sha16> <fetch bytes> <write bytes>
+        parts = line.rsplit(None, 4)
+        if len(parts) == 5 and parts[0] == kernel and parts[1] == str(workload) and parts[2] == sha:
+            return int(parts[3]) + int(parts[4])
     return None
 
 
@@ -398,7 +407,7 @@ def main():
     kname, kms, kflops = max(kernels, key=lambda x: x[1])
     achieved = kflops / (kms * 1e-3) / 1e12
     roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname),
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": measured_traffic(kname, args.workload),
             "avg_launch_us": round(kms * 1e3, 2), "algorithmic_flops_per_launch": int(kflops)}
 
     out = {

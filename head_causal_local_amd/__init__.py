@@ -23,11 +23,17 @@ __all__ = ["attn_fwd", "attn_fwd_diag", "head_features", "head_features_workspac
            "cache_clear", "AahError", "LIB_PATH"]
 
 
+_I32 = np.iinfo(np.int32)
+
+
 def _windows_arg(windows) -> np.ndarray:
+    if isinstance(windows, np.ndarray) and windows.dtype == np.int32 and windows.ndim == 1 \
+            and windows.flags.c_contiguous:
+        return windows
     w = np.ascontiguousarray(np.asarray(windows, dtype=np.int64))
     if w.ndim != 1:
         raise ValueError("windows must be a 1-D sequence with one entry per head")
-    if np.any(w > np.iinfo(np.int32).max) or np.any(w < np.iinfo(np.int32).min):
+    if w.size and (w.max() > _I32.max or w.min() < _I32.min):
         raise ValueError("window out of int32 range")
     return np.ascontiguousarray(w.astype(np.int32))
 
@@ -278,30 +284,36 @@ def attn_bwd_dkdv(q, k, v, do, windows, dk, dv, workspace, scale: Optional[float
                                   _stream_ptr(q, stream)))
 
 
-def kv_cache_rows(windows, T_max: int) -> int:
-    """Rows per batch entry of the trimmed decode caches: sum over heads of min(W_h, T_max)."""
+def _decode_heads(windows, sinks, H_kv):
     w = _windows_arg(windows)
-    r = int(lib().aah_kv_cache_rows(_wptr(w), w.shape[0], int(T_max)))
+    H = w.shape[0]
+    H_kv = H if H_kv is None else int(H_kv)
+    return w, _sinks_arg(sinks, H), H, H_kv
+
+
+def kv_cache_rows(windows, T_max: int, sinks=None, H_kv: Optional[int] = None) -> int:
+    """Rows per batch entry of the trimmed decode caches (see aah_kv_cache_rows)."""
+    w, sk, H, H_kv = _decode_heads(windows, sinks, H_kv)
+    r = int(lib().aah_kv_cache_rows(_wptr(w), _sptr(sk), H, H_kv, int(T_max)))
     if r < 0:
-        raise ValueError("invalid windows or T_max")
+        raise ValueError("invalid windows, sinks, H_kv or T_max")
     return r
 
 
-def decode_workspace_size(windows, B: int, T_max: int, d: int) -> int:
+def decode_workspace_size(windows, B: int, T_max: int, d: int, sinks=None, H_kv: Optional[int] = None) -> int:
     """Workspace bytes of one decoding step (bf16)."""
-    w = _windows_arg(windows)
-    return int(lib().aah_attn_decode_workspace_size(_wptr(w), B, w.shape[0], int(T_max), d, AAH_BF16))
+    w, sk, H, H_kv = _decode_heads(windows, sinks, H_kv)
+    return int(lib().aah_attn_decode_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, int(T_max), d, AAH_BF16))
 
 
-def kv_cache_fill(k, v, windows, T_max: int, kcache=None, vcache=None, stream=None):
-    """Store a prefill's K/V [B, H, T, d] (positions 0..T-1) into trimmed caches [B, R, d]."""
+def kv_cache_fill(k, v, windows, T_max: int, kcache=None, vcache=None, stream=None, sinks=None):
+    """Store a prefill's K/V [B, H_kv, T, d] (positions 0..T-1) into trimmed caches [B, R, d]; windows (and
+    sinks) have one entry per query head, H = len(windows) a multiple of H_kv."""
     import torch
     _check_operand("v", v, k)
-    B, H, T, d = k.shape
-    w = _windows_arg(windows)
-    if w.shape[0] != H:
-        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
-    R = kv_cache_rows(w, T_max)
+    B, H_kv, T, d = k.shape
+    w, sk, H, H_kv = _decode_heads(windows, sinks, H_kv)
+    R = kv_cache_rows(w, T_max, sinks=sk, H_kv=H_kv)
     if kcache is None:
         kcache = torch.zeros((B, R, d), dtype=k.dtype, device=k.device)
     if vcache is None:
@@ -309,24 +321,28 @@ def kv_cache_fill(k, v, windows, T_max: int, kcache=None, vcache=None, stream=No
     for name, t in (("kcache", kcache), ("vcache", vcache)):
         if t.shape != (B, R, d) or t.dtype != k.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [{B}, {R}, {d}] tensor of k's dtype")
-    check(lib().aah_kv_cache_fill(k.data_ptr(), v.data_ptr(), _wptr(w), B, H, T, int(T_max), d, _dtype_code(k),
-                                  kcache.data_ptr(), vcache.data_ptr(), _stream_ptr(k, stream)))
+    check(lib().aah_kv_cache_fill(k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, int(T_max), d,
+                                  _dtype_code(k), kcache.data_ptr(), vcache.data_ptr(), _stream_ptr(k, stream)))
     return kcache, vcache
 
 
 def attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, scale: Optional[float] = None,
-                out=None, lse=None, workspace=None, stream=None):
-    """One decoding step: q, k_new, v_new [B, H, d] at positions pos (int32 device tensor [B]).
+                out=None, lse=None, workspace=None, stream=None, sinks=None):
+    """One decoding step: q [B, H, d], k_new, v_new [B, H_kv, d] at positions pos (int32 device tensor [B]).
 
     Stores k_new / v_new into the caches and returns (o [B, H, d], lse [B, H])."""
     import torch
-    for name, t in (("k_new", k_new), ("v_new", v_new)):
-        _check_operand(name, t, q)
+    _check_operand("v_new", v_new, k_new)
     B, H, d = q.shape
-    w = _windows_arg(windows)
-    if w.shape[0] != H:
-        raise ValueError(f"windows has {w.shape[0]} entries, expected H = {H}")
-    R = kv_cache_rows(w, T_max)
+    H_kv = k_new.shape[1]
+    if k_new.shape != (B, H_kv, d) or H % H_kv != 0 or k_new.dtype != q.dtype or not k_new.is_contiguous():
+        raise ValueError("k_new must be a contiguous [B, H_kv, d] tensor of q's dtype with H_kv dividing H")
+    if not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous device tensor")
+    w, sk, Hw, H_kv = _decode_heads(windows, sinks, H_kv)
+    if Hw != H:
+        raise ValueError(f"windows has {Hw} entries, expected H = {H}")
+    R = kv_cache_rows(w, T_max, sinks=sk, H_kv=H_kv)
     for name, t in (("kcache", kcache), ("vcache", vcache)):
         if t.shape != (B, R, d) or t.dtype != q.dtype or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous [{B}, {R}, {d}] tensor of q's dtype")
@@ -338,12 +354,14 @@ def attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, scale
     _check_operand("out", out, q)
     if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
-    if workspace is None:   # zeroed: its first B*H int32 are the kernels' merge counters
-        workspace = torch.zeros(max(decode_workspace_size(w, B, T_max, d), 1), dtype=torch.uint8, device=q.device)
+    if workspace is None:   # zeroed: its first B*H_kv int32 are the kernels' merge counters
+        workspace = torch.zeros(max(decode_workspace_size(w, B, T_max, d, sinks=sk, H_kv=H_kv), 1),
+                                dtype=torch.uint8, device=q.device)
     ptr, nbytes = _ws(workspace)
     check(lib().aah_attn_decode(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(),
-                                vcache.data_ptr(), pos.data_ptr(), _wptr(w), B, H, int(T_max), d, _dtype_code(q),
-                                scale, out.data_ptr(), lse.data_ptr(), ptr, nbytes, _stream_ptr(q, stream)))
+                                vcache.data_ptr(), pos.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, int(T_max), d,
+                                _dtype_code(q), scale, out.data_ptr(), lse.data_ptr(), ptr, nbytes,
+                                _stream_ptr(q, stream)))
     return out, lse
 
 

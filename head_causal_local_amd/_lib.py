@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
@@ -97,15 +97,16 @@ def _declare(lib):
     lib.aah_cache_clear.restype = None
     lib.aah_cache_clear.argtypes = []
     lib.aah_kv_cache_rows.restype = c_int64
-    lib.aah_kv_cache_rows.argtypes = [P_i32, c_int, c_int]
+    lib.aah_kv_cache_rows.argtypes = [P_i32, P_i32, c_int, c_int, c_int]
     lib.aah_attn_decode_workspace_size.restype = c_size_t
-    lib.aah_attn_decode_workspace_size.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int]
+    lib.aah_attn_decode_workspace_size.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_kv_cache_fill.restype = c_int
-    lib.aah_kv_cache_fill.argtypes = [c_void_p, c_void_p, P_i32, c_int, c_int, c_int, c_int, c_int, c_int,
-                                      c_void_p, c_void_p, c_void_p]
+    lib.aah_kv_cache_fill.argtypes = [c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int,
+                                      c_int, c_void_p, c_void_p, c_void_p]
     lib.aah_attn_decode.restype = c_int
-    lib.aah_attn_decode.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, c_int, c_int,
-                                    c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.aah_attn_decode.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int,
+                                    c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t,
+                                    c_void_p]
 
 
 def lib():

@@ -213,37 +213,66 @@ aah_status check_workspace(const void* workspace, size_t workspace_bytes, int B,
 
 struct DecodePlan {
   aah::DecodeChunk* chunks = nullptr;
-  int32_t* tables = nullptr;  // head_off[H], head_cap[H], head_first[H + 1]
-  std::vector<int32_t> host_cap;
+  // kv_off[H_kv], kv_sink[H_kv], kv_ring[H_kv], kv_first[H_kv + 1], q_cap[H], q_sink[H]
+  int32_t* tables = nullptr;
+  std::vector<int32_t> host_sink, host_ring;
   int n_chunks = 0;
   int rows = 0;
-  int H = 0;
+  int H = 0, H_kv = 0;
   aah::DecodePlanView view() const {
-    return aah::DecodePlanView{chunks, n_chunks, tables, tables + H, tables + 2 * H, rows, host_cap.data()};
+    const int32_t* t = tables;
+    return aah::DecodePlanView{chunks,         n_chunks,         t,    t + H_kv, t + 2 * H_kv, t + 3 * H_kv,
+                               t + 4 * H_kv + 1, t + 4 * H_kv + 1 + H, rows, H, H_kv, host_sink.data(),
+                               host_ring.data()};
   }
 };
 
 std::map<std::vector<int64_t>, DecodePlan> g_decode_cache;
 
-// Rows R = sum_h min(W_h, T_max) of one batch entry's cache; -1 if it does not fit in int32.
-int64_t decode_rows(const int32_t* windows, int H, int T_max) {
-  int64_t r = 0;
-  for (int h = 0; h < H; ++h) r += std::min<int64_t>(windows[h], T_max);
+// Per query head: C_h = min(W_h, T_max) and the effective sink min(S_h, T_max - C_h) (sinks past it are
+// always inside the window); per key/value head: the largest of each over its query heads.
+struct DecodeShape {
+  std::vector<int64_t> cap, sink;  // per query head
+  std::vector<int64_t> ring, ksink;  // per key/value head
+  int64_t rows = 0, chunks = 0;
+};
+
+DecodeShape decode_shape(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max) {
+  DecodeShape s;
+  const int G = H / H_kv;
+  s.cap.resize(H);
+  s.sink.resize(H);
+  s.ring.assign(H_kv, 0);
+  s.ksink.assign(H_kv, 0);
+  for (int h = 0; h < H; ++h) {
+    s.cap[h] = std::min<int64_t>(windows[h], T_max);
+    const int64_t sk = sinks == nullptr ? 0 : sinks[h];
+    s.sink[h] = std::max<int64_t>(0, std::min<int64_t>(sk, T_max - s.cap[h]));
+    s.ring[h / G] = std::max(s.ring[h / G], s.cap[h]);
+    s.ksink[h / G] = std::max(s.ksink[h / G], s.sink[h]);
+  }
+  for (int g = 0; g < H_kv; ++g) {
+    s.rows += s.ksink[g] + s.ring[g];
+    s.chunks += (s.ksink[g] + s.ring[g] + aah::kDecodeRows - 1) / aah::kDecodeRows;
+  }
+  return s;
+}
+
+// Rows R of one batch entry's cache; -1 if it does not fit in int32.
+int64_t decode_rows(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max) {
+  const int64_t r = decode_shape(windows, sinks, H, H_kv, T_max).rows;
   return r > INT32_MAX ? -1 : r;
 }
 
-int decode_chunks(const int32_t* windows, int H, int T_max) {
-  int64_t n = 0;
-  for (int h = 0; h < H; ++h) n += (std::min<int64_t>(windows[h], T_max) + aah::kDecodeRows - 1) / aah::kDecodeRows;
-  return static_cast<int>(n);
-}
-
-aah_status get_decode_plan(const int32_t* windows, int H, int T_max, const DecodePlan** out) {
+aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max,
+                           const DecodePlan** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::vector<int64_t> key = {dev, H, T_max};
-  for (int h = 0; h < H; ++h) key.push_back(std::min(windows[h], T_max));
+  const DecodeShape sh = decode_shape(windows, sinks, H, H_kv, T_max);
+  std::vector<int64_t> key = {dev, H, H_kv, T_max};
+  key.insert(key.end(), sh.cap.begin(), sh.cap.end());
+  key.insert(key.end(), sh.sink.begin(), sh.sink.end());
   std::lock_guard<std::mutex> lock(g_mu);
   auto found = g_decode_cache.find(key);
   if (found != g_decode_cache.end()) {
@@ -252,21 +281,28 @@ aah_status get_decode_plan(const int32_t* windows, int H, int T_max, const Decod
   }
   DecodePlan p;
   p.H = H;
-  std::vector<int32_t> tables(3 * H + 1);
+  p.H_kv = H_kv;
+  std::vector<int32_t> tables(4 * H_kv + 1 + 2 * H);
   std::vector<aah::DecodeChunk> chunks;
   int32_t off = 0;
-  for (int h = 0; h < H; ++h) {
-    const int32_t cap = std::min(windows[h], T_max);
-    tables[h] = off;
-    tables[H + h] = cap;
-    tables[2 * H + h] = static_cast<int32_t>(chunks.size());
-    for (int32_t s0 = 0; s0 < cap; s0 += aah::kDecodeRows) chunks.push_back(aah::DecodeChunk{h, s0});
-    off += cap;
+  for (int g = 0; g < H_kv; ++g) {
+    const int32_t n = static_cast<int32_t>(sh.ksink[g] + sh.ring[g]);
+    tables[g] = off;
+    tables[H_kv + g] = static_cast<int32_t>(sh.ksink[g]);
+    tables[2 * H_kv + g] = static_cast<int32_t>(sh.ring[g]);
+    tables[3 * H_kv + g] = static_cast<int32_t>(chunks.size());
+    for (int32_t r0 = 0; r0 < n; r0 += aah::kDecodeRows) chunks.push_back(aah::DecodeChunk{g, r0});
+    off += n;
   }
-  tables[3 * H] = static_cast<int32_t>(chunks.size());
+  tables[4 * H_kv] = static_cast<int32_t>(chunks.size());
+  for (int h = 0; h < H; ++h) {
+    tables[4 * H_kv + 1 + h] = static_cast<int32_t>(sh.cap[h]);
+    tables[4 * H_kv + 1 + H + h] = static_cast<int32_t>(sh.sink[h]);
+  }
   p.rows = off;
   p.n_chunks = static_cast<int>(chunks.size());
-  p.host_cap.assign(tables.begin() + H, tables.begin() + 2 * H);
+  p.host_sink.assign(tables.begin() + H_kv, tables.begin() + 2 * H_kv);
+  p.host_ring.assign(tables.begin() + 2 * H_kv, tables.begin() + 3 * H_kv);
   e = hipMalloc(&p.chunks, chunks.size() * sizeof(aah::DecodeChunk));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(decode chunks)");
   e = hipMalloc(&p.tables, tables.size() * sizeof(int32_t));
@@ -286,22 +322,26 @@ aah_status get_decode_plan(const int32_t* windows, int H, int T_max, const Decod
   return AAH_OK;
 }
 
-// Decode workspace: B*H int32 merge counters (256-byte rounded), then the partials.
-size_t decode_counter_bytes(int B, int H) { return round_up(static_cast<size_t>(B) * H * sizeof(int32_t), 256); }
-size_t decode_workspace(const int32_t* windows, int B, int H, int T_max, int d) {
-  return decode_counter_bytes(B, H) +
-         round_up(static_cast<size_t>(B) * decode_chunks(windows, H, T_max) * (2 + d) * sizeof(float), 256);
+// Decode workspace: B*H_kv int32 merge counters (256-byte rounded), then the partials: one per
+// (batch entry, chunk, query head of the chunk's group).
+size_t decode_counter_bytes(int B, int H_kv) { return round_up(static_cast<size_t>(B) * H_kv * sizeof(int32_t), 256); }
+size_t decode_workspace(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T_max, int d) {
+  const DecodeShape sh = decode_shape(windows, sinks, H, H_kv, T_max);
+  return decode_counter_bytes(B, H_kv) +
+         round_up(static_cast<size_t>(B) * sh.chunks * (H / H_kv) * (2 + d) * sizeof(float), 256);
 }
 
 // Checks shared by the decode entry points (bf16 only; T_max plays the role of T).
-aah_status check_decode(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt) {
-  AAH_TRY_INNER(check_shape(windows, nullptr, B, H, T_max, d, dt));
+aah_status check_decode(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T_max, int d,
+                        aah_dtype dt) {
+  AAH_TRY_INNER(check_shape(windows, sinks, B, H, T_max, d, dt, H_kv));
   if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
-  if (decode_rows(windows, H, T_max) < 0) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
-  // The decode and cache-fill launches put B (and B * H) on the second grid dimension.
-  if (static_cast<int64_t>(B) * H > 65535) return fail(AAH_ERR_UNSUPPORTED, "B * H = %lld exceeds 65535", static_cast<long long>(B) * H);
-  if (static_cast<int64_t>(B) * decode_rows(windows, H, T_max) * d >= (int64_t{1} << 40))
-    return fail(AAH_ERR_UNSUPPORTED, "cache too large");
+  const int64_t rows = decode_rows(windows, sinks, H, H_kv, T_max);
+  if (rows < 0) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
+  // The decode and cache-fill launches put B (and B * H_kv) on the second grid dimension.
+  if (static_cast<int64_t>(B) * H_kv > 65535)
+    return fail(AAH_ERR_UNSUPPORTED, "B * H_kv = %lld exceeds 65535", static_cast<long long>(B) * H_kv);
+  if (static_cast<int64_t>(B) * rows * d >= (int64_t{1} << 40)) return fail(AAH_ERR_UNSUPPORTED, "cache too large");
   return AAH_OK;
 }
 
@@ -563,44 +603,47 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
                            workspace_bytes, stream);
 }
 
-int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max) {
+int64_t aah_kv_cache_rows(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max) {
   g_detail.clear();
-  if (windows == nullptr || H < 1 || T_max < 1) return -1;
+  if (windows == nullptr || H < 1 || T_max < 1 || H_kv < 1 || H_kv > H || H % H_kv != 0) return -1;
   for (int h = 0; h < H; ++h)
-    if (windows[h] < 1) return -1;
-  return decode_rows(windows, H, T_max);
+    if (windows[h] < 1 || (sinks != nullptr && sinks[h] < 0)) return -1;
+  return decode_rows(windows, sinks, H, H_kv, T_max);
 }
 
-size_t aah_attn_decode_workspace_size(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt) {
+size_t aah_attn_decode_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                      int T_max, int d, aah_dtype dt) {
   if (windows == nullptr || B < 1 || H < 1 || T_max < 1 || !supported_d(d) || dt != AAH_BF16) return 0;
+  if (H_kv < 1 || H_kv > H || H % H_kv != 0) return 0;
   for (int h = 0; h < H; ++h)
-    if (windows[h] < 1) return 0;
-  return decode_workspace(windows, B, H, T_max, d);
+    if (windows[h] < 1 || (sinks != nullptr && sinks[h] < 0)) return 0;
+  return decode_workspace(windows, sinks, B, H, H_kv, T_max, d);
 }
 
-aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, int B, int H, int T, int T_max,
-                             int d, aah_dtype dt, void* kcache, void* vcache, aah_stream_t stream) {
+aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, const int32_t* sinks, int B, int H,
+                             int H_kv, int T, int T_max, int d, aah_dtype dt, void* kcache, void* vcache,
+                             aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_decode(windows, B, H, T_max, d, dt));
+  AAH_TRY(check_decode(windows, sinks, B, H, H_kv, T_max, d, dt));
   if (T < 1 || T > T_max) return fail(AAH_ERR_INVALID_ARG, "prefill length T = %d must be in [1, T_max = %d]", T, T_max);
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(kcache, "kcache", 16));
   AAH_TRY(check_tensor(vcache, "vcache", 16));
   const DecodePlan* plan = nullptr;
-  AAH_TRY(get_decode_plan(windows, H, T_max, &plan));
-  const hipError_t e = aah::launch_cache_fill_bf16(k, v, kcache, vcache, plan->view(), B, H, T, d,
-                                                   static_cast<hipStream_t>(stream));
+  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, &plan));
+  const hipError_t e =
+      aah::launch_cache_fill_bf16(k, v, kcache, vcache, plan->view(), B, T, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache fill launch");
   return AAH_OK;
 }
 
 aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
-                           const int32_t* pos, const int32_t* windows, int B, int H, int T_max, int d,
-                           aah_dtype dt, float scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                           aah_stream_t stream) {
+                           const int32_t* pos, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                           int T_max, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_decode(windows, B, H, T_max, d, dt));
+  AAH_TRY(check_decode(windows, sinks, B, H, H_kv, T_max, d, dt));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k_new, "k_new", 16));
   AAH_TRY(check_tensor(v_new, "v_new", 16));
@@ -610,17 +653,17 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
-  const size_t need = decode_workspace(windows, B, H, T_max, d);
+  const size_t need = decode_workspace(windows, sinks, B, H, H_kv, T_max, d);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
                 need);
   if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   const DecodePlan* plan = nullptr;
-  AAH_TRY(get_decode_plan(windows, H, T_max, &plan));
+  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, &plan));
   const hipError_t e = aah::launch_decode_bf16(
-      q, k_new, v_new, kcache, vcache, pos, plan->view(), B, H, T_max, d, scale, o, lse,
+      q, k_new, v_new, kcache, vcache, pos, plan->view(), B, T_max, d, scale, o, lse,
       static_cast<int32_t*>(workspace),
-      reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, H)),
+      reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, H_kv)),
       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return AAH_OK;

@@ -92,39 +92,45 @@ hipError_t launch_head_features(const void* q, const void* k, const void* v, boo
                                 hipStream_t stream);
 
 // ---- decoding over per-head trimmed K/V caches (bf16)
-constexpr int kDecodeRows = 256;  // ring rows per decode workgroup
+constexpr int kDecodeRows = 256;  // cache rows per decode workgroup
 
-// One decode workgroup's share: ring rows [slot0, slot0 + kDecodeRows) of one head.
+// One decode workgroup's share: local rows [row0, row0 + kDecodeRows) of one
+// key/value head's region (its sink rows, then its ring rows).
 struct DecodeChunk {
-  int32_t head;
-  int32_t slot0;
+  int32_t kvhead;
+  int32_t row0;
 };
 static_assert(sizeof(DecodeChunk) == 8, "DecodeChunk layout");
 
-// Device tables of one (H, T_max, windows) combination: head h's ring has
-// head_cap[h] = min(W_h, T_max) rows starting at row head_off[h]; its chunks
-// are [head_first[h], head_first[h + 1]).
+// Device tables of one (windows, sinks, H, H_kv, T_max) combination.  Key/value
+// head g owns kv_sink[g] sink rows then kv_ring[g] ring rows from row
+// kv_off[g]; its chunks are [kv_first[g], kv_first[g + 1]).  Query head h has
+// window q_cap[h] = min(W_h, T_max) and effective sink q_sink[h].
 struct DecodePlanView {
   const DecodeChunk* chunks;
   int n_chunks;
-  const int32_t* head_off;
-  const int32_t* head_cap;
-  const int32_t* head_first;
-  int rows;                  // R = sum of head_cap
-  const int32_t* host_cap;   // host copy of head_cap
+  const int32_t* kv_off;
+  const int32_t* kv_sink;
+  const int32_t* kv_ring;
+  const int32_t* kv_first;
+  const int32_t* q_cap;
+  const int32_t* q_sink;
+  int rows;  // R = sum over key/value heads of sink + ring rows
+  int H, H_kv;
+  const int32_t* host_kv_sink;  // host copies of kv_sink / kv_ring
+  const int32_t* host_kv_ring;
 };
 
-// Writes k_new / v_new [B,H,d] into the ring row of position pos[b] (device
+// Writes k_new / v_new [B,H_kv,d] into the rows of position pos[b] (device
 // int32[B], clamped to [0, T_max)) and o [B,H,d] / lse [B,H] of that token.
-// counters: int32[B*H], zero on entry and left zero; partials: B * n_chunks *
-// (2 + d) floats.
+// counters: int32[B*H_kv], zero on entry and left zero; partials: B * n_chunks *
+// (H / H_kv) * (2 + d) floats.
 hipError_t launch_decode_bf16(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
-                              const int32_t* pos, const DecodePlanView& plan, int B, int H, int T_max, int d,
-                              float scale, void* o, float* lse, int32_t* counters, float* partials,
-                              hipStream_t stream);
+                              const int32_t* pos, const DecodePlanView& plan, int B, int T_max, int d, float scale,
+                              void* o, float* lse, int32_t* counters, float* partials, hipStream_t stream);
 
-// Copies the positions each ring keeps (the last min(C_h, T)) of a prefill k, v [B,H,T,d].
+// Copies the positions each region keeps of a prefill k, v [B,H_kv,T,d].
 hipError_t launch_cache_fill_bf16(const void* k, const void* v, void* kcache, void* vcache,
-                                  const DecodePlanView& plan, int B, int H, int T, int d, hipStream_t stream);
+                                  const DecodePlanView& plan, int B, int T, int d, hipStream_t stream);
 
 }  // namespace aah

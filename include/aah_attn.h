@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 5
+#define AAH_ABI_VERSION 6
 
 typedef enum {
   AAH_OK = 0,
@@ -199,53 +199,67 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
  * Decoding over per-head trimmed K/V caches (bf16).
  *
  * One decoding step is section 5.8 for the newest position only: the token at
- * position p of head h (window W_h) attends to positions max(0, p - C_h + 1)
- * .. p, where C_h = min(W_h, T_max) and T_max is the maximum context the
- * caches are built for.  Table 6 runs inference with per-head windows, and
- * "Autonomy-of-Heads" section 5 bounds a streaming head's decode-time cache
- * by its window: here head h keeps exactly C_h rows of K and of V.
+ * position p of query head h (window W_h) attends to positions
+ * max(0, p - C_h + 1) .. p, where C_h = min(W_h, T_max) and T_max is the
+ * maximum context the caches are built for, and, with sinks (a streaming head
+ * of "Autonomy-of-Heads" section 5: sink tokens plus a recent window), also to
+ * positions 0 .. min(sinks[h], p + 1) - 1.  Table 6 runs inference with
+ * per-head windows, and AoH section 5 bounds a streaming head's decode-time
+ * cache by its sinks and window.  With grouped key/value heads (H_kv < H,
+ * G = H / H_kv) query head h reads key/value head h / G, and the caches hold
+ * H_kv heads.
  *
- * Cache layout: kcache and vcache are device tensors [B, R, d] of dtype dt
- * with R = aah_kv_cache_rows(windows, H, T_max) = sum_h C_h.  Head h owns rows
- * off_h .. off_h + C_h - 1 (off_h = sum of C over the heads before h), and
- * position t of head h lives in row off_h + (t mod C_h).  Rows not yet written
- * are never read.  Only dt = AAH_BF16 is supported (AAH_ERR_UNSUPPORTED
- * otherwise); d in {32, 64, 128}; windows and stream as for the other calls.
+ * Cache layout: kcache and vcache are device tensors [B, R, d] of dtype dt with
+ * R = aah_kv_cache_rows(windows, sinks, H, H_kv, T_max).  Key/value head g
+ * owns S_g sink rows followed by R_g ring rows, from row off_g (the sum of
+ * S + R over the heads before g), where
+ *   R_g = max over its query heads of C_h,
+ *   S_g = max over its query heads of min(sinks[h], T_max - C_h)
+ * (a sink at or past T_max - C_h is always inside the window).  Position t
+ * lives in ring row off_g + S_g + (t mod R_g) and, if t < S_g, also in sink row
+ * off_g + t.  Rows not yet written are never read.  Only dt = AAH_BF16 is
+ * supported (AAH_ERR_UNSUPPORTED otherwise); d in {32, 64, 128}; sinks may be
+ * NULL; windows, sinks, H_kv and stream as for the other calls.  Without sinks
+ * and grouping head h simply owns C_h ring rows.
  */
 
-/* R = sum_h min(windows[h], T_max) rows per batch entry; -1 for invalid arguments. */
-int64_t aah_kv_cache_rows(const int32_t* windows, int H, int T_max);
+/* R rows per batch entry (see above); -1 for invalid arguments. */
+int64_t aah_kv_cache_rows(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max);
 
-/* Workspace bytes aah_attn_decode needs: B*H int32 merge counters (rounded up
- * to 256 bytes), then B * chunks * (2 + d) floats of partial results, chunks =
- * sum_h ceil(C_h / 256); 0 for invalid arguments. */
-size_t aah_attn_decode_workspace_size(const int32_t* windows, int B, int H, int T_max, int d, aah_dtype dt);
+/* Workspace bytes aah_attn_decode needs: B*H_kv int32 merge counters (rounded
+ * up to 256 bytes), then B * chunks * G * (2 + d) floats of partial results,
+ * chunks = sum over key/value heads of ceil((S_g + R_g) / 256); 0 for invalid
+ * arguments. */
+size_t aah_attn_decode_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                      int T_max, int d, aah_dtype dt);
 
 /*
- * Prefill into the caches: k, v [B,H,T,d] hold positions 0 .. T - 1
- * (1 <= T <= T_max); writes the positions each head keeps, the last
- * min(C_h, T) of them, into their rows.  Other rows are left as they are.
+ * Prefill into the caches: k, v [B,H_kv,T,d] hold positions 0 .. T - 1
+ * (1 <= T <= T_max); writes the positions each key/value head keeps (its first
+ * min(S_g, T) into the sink rows, its last min(R_g, T) into the ring) into
+ * their rows.  Other rows are left as they are.
  */
-aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, int B, int H, int T, int T_max,
-                             int d, aah_dtype dt, void* kcache, void* vcache, aah_stream_t stream);
+aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* windows, const int32_t* sinks, int B, int H,
+                             int H_kv, int T, int T_max, int d, aah_dtype dt, void* kcache, void* vcache,
+                             aah_stream_t stream);
 
 /*
- * One decoding step.  q, k_new, v_new [B,H,d]: the new token of every
- * sequence; pos: DEVICE pointer to int32[B], the new token's position in each
- * sequence, 0 <= pos[b] < T_max (values outside are clamped into that range),
- * with positions max(0, pos[b] - C_h + 1) .. pos[b] - 1 already in the cache.
- * Writes k_new / v_new into the row of position pos[b] and o [B,H,d] (dtype
- * dt), lse [B,H] (fp32, natural log of sum_j exp(scale q . k_j) over the
- * attended positions).  Workspace: at least aah_attn_decode_workspace_size
- * bytes, 256-byte aligned.  Its first B*H int32 (the merge counters) must be
- * zero before the first call that uses it; every call leaves them zero again,
- * the rest of it carries nothing between calls.  Calls that share a
- * workspace must not run concurrently.
+ * One decoding step.  q [B,H,d] and k_new, v_new [B,H_kv,d]: the new token of
+ * every sequence; pos: DEVICE pointer to int32[B], the new token's position in
+ * each sequence, 0 <= pos[b] < T_max (values outside are clamped into that
+ * range), with every earlier position the step attends to already in the
+ * cache.  Writes k_new / v_new into the rows of position pos[b] and
+ * o [B,H,d] (dtype dt), lse [B,H] (fp32, natural log of sum_j exp(scale q . k_j)
+ * over the attended positions).  Workspace: at least
+ * aah_attn_decode_workspace_size bytes, 256-byte aligned.  Its first B*H_kv
+ * int32 (the merge counters) must be zero before the first call that uses it;
+ * every call leaves them zero again, the rest of it carries nothing between
+ * calls.  Calls that share a workspace must not run concurrently.
  */
 aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
-                           const int32_t* pos, const int32_t* windows, int B, int H, int T_max, int d,
-                           aah_dtype dt, float scale, void* o, float* lse, void* workspace, size_t workspace_bytes,
-                           aah_stream_t stream);
+                           const int32_t* pos, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                           int T_max, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
+                           size_t workspace_bytes, aah_stream_t stream);
 
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 5
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 6
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -196,22 +196,31 @@ def test_plan_capacity_reporting():
 
 
 def test_decode_cache_rows_and_workspace():
-    """Cache rows = sum_h min(W_h, T_max) (the layout oracle.cache_rows_ref states); workspace from the chunk count."""
+    """Cache rows = the layout oracle.cache_rows_ref states (per key/value head: sink rows + ring rows);
+    workspace from the chunk count and group size."""
     import oracle
     w = np.array([512, 4096, 1, 300], dtype=np.int32)
+    sk = np.array([128, 0, 3, 10], dtype=np.int32)
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    sp = sk.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     lib = _lib.lib()
     for T_max in (1, 300, 1000, 8192):
-        _, caps = oracle.cache_rows_ref(w, T_max)
-        assert lib.aah_kv_cache_rows(wp, 4, T_max) == int(caps.sum()) == aah.kv_cache_rows(w, T_max)
-        chunks = int(sum((c + 255) // 256 for c in caps))
-        need = aah.decode_workspace_size(w, 3, T_max, 64)
-        assert need >= 3 * chunks * (2 + 64) * 4 and need % 256 == 0
+        for sinks, H_kv in ((None, 4), (sk, 4), (sk, 2), (None, 1)):
+            _, sink, ring = oracle.cache_rows_ref(w, T_max, sinks, H_kv)
+            rows = int((sink + ring).sum())
+            assert lib.aah_kv_cache_rows(wp, None if sinks is None else sp, 4, H_kv, T_max) == rows
+            assert aah.kv_cache_rows(w, T_max, sinks=sinks, H_kv=H_kv) == rows
+            chunks = int(sum((s_ + r + 255) // 256 for s_, r in zip(sink, ring)))
+            need = aah.decode_workspace_size(w, 3, T_max, 64, sinks=sinks, H_kv=H_kv)
+            assert need >= 3 * chunks * (4 // H_kv) * (2 + 64) * 4 and need % 256 == 0
     bad = np.array([4, 0], dtype=np.int32)
-    assert lib.aah_kv_cache_rows(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 2, 10) == -1
-    assert lib.aah_kv_cache_rows(wp, 4, 0) == -1
-    assert lib.aah_attn_decode_workspace_size(wp, 1, 4, 100, 64, 1) == 0      # fp32: no decode kernel
-    assert lib.aah_attn_decode_workspace_size(wp, 1, 4, 100, 48, 0) == 0      # d = 48
+    assert lib.aah_kv_cache_rows(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 2, 2, 10) == -1
+    assert lib.aah_kv_cache_rows(wp, None, 4, 4, 0) == -1
+    assert lib.aah_kv_cache_rows(wp, None, 4, 3, 100) == -1                   # H_kv must divide H
+    neg = np.array([0, -1, 0, 0], dtype=np.int32)
+    assert lib.aah_kv_cache_rows(wp, neg.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 4, 4, 100) == -1
+    assert lib.aah_attn_decode_workspace_size(wp, None, 1, 4, 4, 100, 64, 1) == 0      # fp32: no decode kernel
+    assert lib.aah_attn_decode_workspace_size(wp, None, 1, 4, 4, 100, 48, 0) == 0      # d = 48
 
 
 def test_decode_validation():
@@ -221,31 +230,35 @@ def test_decode_validation():
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     need = aah.decode_workspace_size(w, 2, 128, 64)
     F = FAKE
-    # aah_attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, B, H, T_max, d, dt, scale, o, lse, ws, bytes, s)
-    ok = [F, F, F, F, F, F, wp, 2, 2, 128, 64, 0, 0.125, F, F, F, need, None]
+    # aah_attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, sinks, B, H, H_kv, T_max, d, dt, scale, o, lse,
+    #                 ws, bytes, stream)
+    ok = [F, F, F, F, F, F, wp, None, 2, 2, 2, 128, 64, 0, 0.125, F, F, F, need, None]
 
     def call(i=None, val=None):
         a = list(ok)
         if i is not None:
             a[i] = val
         return lib.aah_attn_decode(*a)
-    for i, name in ((0, "q"), (1, "k_new"), (2, "v_new"), (3, "kcache"), (4, "vcache"), (5, "pos"), (13, "o"),
-                    (14, "lse")):
+    for i, name in ((0, "q"), (1, "k_new"), (2, "v_new"), (3, "kcache"), (4, "vcache"), (5, "pos"), (15, "o"),
+                    (16, "lse")):
         assert call(i, 0) == 1, name
     assert call(6, None) == 1                       # NULL windows
-    assert call(11, 1) == 2                         # fp32 caches: unsupported
-    assert call(10, 48) == 2                        # d = 48
-    assert call(12, 0.0) == 1 and call(12, float("inf")) == 1
-    assert call(16, need - 1) == 3                  # small workspace
-    assert call(15, 0) == 3                         # NULL workspace
-    assert call(9, 0) == 1                          # T_max = 0
+    assert call(13, 1) == 2                         # fp32 caches: unsupported
+    assert call(12, 48) == 2                        # d = 48
+    assert call(14, 0.0) == 1 and call(14, float("inf")) == 1
+    assert call(18, need - 1) == 3                  # small workspace
+    assert call(17, 0) == 3                         # NULL workspace
+    assert call(11, 0) == 1                         # T_max = 0
+    assert call(10, 3) == 1                         # H_kv does not divide H
     bad = np.array([16, 0], dtype=np.int32)
     assert call(6, bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == 1
-    # aah_kv_cache_fill(k, v, windows, B, H, T, T_max, d, dt, kcache, vcache, stream)
-    assert lib.aah_kv_cache_fill(F, F, wp, 2, 2, 129, 128, 64, 0, F, F, None) == 1   # T > T_max
-    assert lib.aah_kv_cache_fill(F, F, wp, 2, 2, 0, 128, 64, 0, F, F, None) == 1     # T = 0
-    assert lib.aah_kv_cache_fill(0, F, wp, 2, 2, 64, 128, 64, 0, F, F, None) == 1    # NULL k
-    assert lib.aah_kv_cache_fill(F, F, wp, 2, 2, 64, 128, 64, 1, F, F, None) == 2    # fp32
+    negs = np.array([0, -4], dtype=np.int32)
+    assert call(7, negs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == 1
+    # aah_kv_cache_fill(k, v, windows, sinks, B, H, H_kv, T, T_max, d, dt, kcache, vcache, stream)
+    assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 129, 128, 64, 0, F, F, None) == 1   # T > T_max
+    assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 0, 128, 64, 0, F, F, None) == 1     # T = 0
+    assert lib.aah_kv_cache_fill(0, F, wp, None, 2, 2, 2, 64, 128, 64, 0, F, F, None) == 1    # NULL k
+    assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 64, 128, 64, 1, F, F, None) == 2    # fp32
 
 
 def test_diag_and_feature_validation():

@@ -159,3 +159,111 @@ def test_decode_graph_replays_match_eager():
         aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, workspace=ws)
     ref_o, ref_l = oracle.decode_ref(qh[:, :, p], kh, vh, windows, np.array([p, p]), T_max, 1.0 / np.sqrt(d))
     _check_o(o, ref_o)
+
+
+# ---------------------------------------------------------------- sinks and grouped key/value heads
+
+def _history_g(B, H, H_kv, L, d, seed):
+    """bf16-exact histories q [B, H, L, d], k, v [B, H_kv, L, d] and their device copies."""
+    rng = np.random.default_rng(seed)
+    host, devs = [], []
+    for heads in (H, H_kv, H_kv):
+        bits = bf16_bits(rng.standard_normal((B, heads, L, d), dtype=np.float32))
+        host.append(bf16_to_f32(bits).astype(np.float64))
+        devs.append(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda"))
+    return host, devs
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("H,H_kv,windows,sinks,T_max,T0", [
+    # streaming heads (sinks), a head whose sinks reach past T_max - C (trimmed), full windows, W = 1
+    (4, 4, [16, 300, 1, 40], [4, 10, 3, 300], 320, 12),
+    # groups of three query heads over two key/value heads, different windows and sinks in a group
+    (6, 2, [1, 64, 300, 7, 256, 33], [0, 5, 0, 128, 0, 2], 512, 200),
+    # one key/value head for all query heads, rings of several chunks
+    (4, 1, [600, 5, 1000, 129], [0, 130, 1, 0], 1024, 700),
+])
+def test_decode_sinks_and_groups(d, H, H_kv, windows, sinks, T_max, T0):
+    """Prefill T0 positions, then 40 steps (sequence 1 repeats position T0 for its first 7 steps): every step
+    against the oracle, and the caches bit-exact against the storage rule at the end."""
+    _require_gpu()
+    B, steps = 2, 40
+    L = T0 + steps
+    (qh, kh, vh), (q, k, v) = _history_g(B, H, H_kv, L, d, seed=d + H)
+    scale = 1.0 / np.sqrt(d)
+    kc, vc = aah.kv_cache_fill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), windows, T_max, sinks=sinks)
+    for cache, hist in ((kc, kh), (vc, vh)):
+        rows, valid = oracle.cache_content_ref(hist, windows, [T0, T0], T_max, sinks)
+        assert np.array_equal(cache.float().cpu().numpy().astype(np.float64)[valid], rows[valid])
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d, sinks=sinks, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
+    bi = np.arange(B)
+    for i in range(steps):
+        p = np.array([T0 + i, T0 + max(0, i - 7)])
+        pos = torch.tensor(p, dtype=torch.int32, device="cuda")
+        qt, kt, vt = q[bi, :, p].contiguous(), k[bi, :, p].contiguous(), v[bi, :, p].contiguous()
+        o, lse = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, scale=scale, workspace=ws, sinks=sinks)
+        ref_o, ref_l = oracle.decode_ref(qh[bi, :, p], kh, vh, windows, p, T_max, scale, sinks=sinks)
+        _check_o(o, ref_o)
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL, i
+    torch.cuda.synchronize()
+    for cache, hist in ((kc, kh), (vc, vh)):
+        rows, valid = oracle.cache_content_ref(hist, windows, [T0 + steps, T0 + steps - 7], T_max, sinks)
+        assert np.array_equal(cache.float().cpu().numpy().astype(np.float64)[valid], rows[valid])
+
+
+def test_decode_sinks_from_empty_cache():
+    """Positions 0 .. 11 with nothing prefilled and 5 sinks on a window of 2: the sink rows fill as the steps
+    pass them, and are attended once the window has moved past them."""
+    _require_gpu()
+    B, H, d, T_max = 1, 2, 64, 64
+    windows, sinks = [2, 64], [5, 0]
+    (qh, kh, vh), (q, k, v) = _history_g(B, H, H, 12, d, seed=13)
+    R = aah.kv_cache_rows(windows, T_max, sinks=sinks)
+    kc = torch.zeros((B, R, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    for t in range(12):
+        pos = torch.tensor([t], dtype=torch.int32, device="cuda")
+        o, lse = aah.attn_decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(),
+                                 kc, vc, pos, windows, T_max, scale=0.125, sinks=sinks)
+        ref_o, ref_l = oracle.decode_ref(qh[:, :, t], kh, vh, windows, np.array([t]), T_max, 0.125, sinks=sinks)
+        _check_o(o, ref_o)
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL, t
+
+
+def test_decode_grouped_graph_replays_match_eager():
+    """Grouped heads with sinks captured in a HIP graph: every replay equals the eager call bit for bit."""
+    _require_gpu()
+    B, H, H_kv, d, T_max = 2, 8, 2, 128, 1024
+    windows = [128, 1024, 256, 64, 512, 1024, 32, 256]
+    sinks = [4, 0, 128, 0, 0, 0, 128, 16]
+    (qh, kh, vh), (q, k, v) = _history_g(B, H, H_kv, T_max, d, seed=23)
+    p = T_max - 1
+    kc, vc = aah.kv_cache_fill(k[:, :, :p].contiguous(), v[:, :, :p].contiguous(), windows, T_max, sinks=sinks)
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    qt, kt, vt = (x[:, :, p].contiguous() for x in (q, k, v))
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d, sinks=sinks, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
+    o_eager, l_eager = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, workspace=ws, sinks=sinks)
+    o_eager, l_eager = o_eager.clone(), l_eager.clone()
+    o = torch.empty_like(o_eager)
+    lse = torch.empty_like(l_eager)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, out=o, lse=lse, workspace=ws, stream=s,
+                            sinks=sinks)
+    torch.cuda.current_stream().wait_stream(s)
+    for r in range(3):
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_eager) and torch.equal(lse, l_eager), r
+        aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, workspace=ws, sinks=sinks)
+    ref_o, ref_l = oracle.decode_ref(qh[:, :, p], kh, vh, windows, np.array([p, p]), T_max, 1.0 / np.sqrt(d),
+                                     sinks=sinks)
+    _check_o(o, ref_o)
