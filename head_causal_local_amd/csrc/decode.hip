@@ -276,27 +276,45 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   if (!sm_last) return;
   if (tid == 0) __hip_atomic_store(&counters[bg], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
   // The last workgroup of (b, g) merges every chunk's partial of each query head: wave w takes heads
-  // w, w + kDecodeWaves, ...
+  // w, w + kDecodeWaves, ...  One pass with running rescaling (as in online softmax): chunks go in
+  // batches of kMergeBatch whose loads (every lane reads each chunk's max and sum, and its own value
+  // dimensions) all leave before the first is used, so a step with up to kMergeBatch chunks per head
+  // pays one round trip for the merge.  Some chunk holds the new token's row, which every head
+  // attends to, so the final max is finite and the sum positive.
+  constexpr int kX = (D + 63) / 64;
+  constexpr int kMergeBatch = 16;
+  const int nc = c1 - c0;
   for (int jh = wave; jh < G; jh += kDecodeWaves) {
     const size_t bh = static_cast<size_t>(b) * H + g * G + jh;
-    float m = -INFINITY;
-    for (int cc = c0; cc < c1; ++cc) m = fmaxf(m, coherent_load(pbase + (static_cast<size_t>(cc) * G + jh) * (2 + D)));
-    float l = 0.f;
-    float o[(D + 63) / 64];
+    float m = -INFINITY, l = 0.f, o[kX];
 #pragma unroll
-    for (int x = 0; x < (D + 63) / 64; ++x) o[x] = 0.f;
-    for (int cc = c0; cc < c1; ++cc) {
-      const float* pc = pbase + (static_cast<size_t>(cc) * G + jh) * (2 + D);
-      const float mc = coherent_load(pc);
-      const float fc = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - m);
-      l = fmaf(fc, coherent_load(pc + 1), l);
+    for (int x = 0; x < kX; ++x) o[x] = 0.f;
+    for (int base = 0; base < nc; base += kMergeBatch) {
+      float mu[kMergeBatch], lu[kMergeBatch], vu[kMergeBatch][kX];
 #pragma unroll
-      for (int x = 0; x < (D + 63) / 64; ++x)
-        if (lane + 64 * x < D) o[x] = fmaf(fc, coherent_load(pc + 2 + lane + 64 * x), o[x]);
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const int cc = c0 + min(base + u, nc - 1);  // slots past the last chunk re-read it and are dropped
+        const float* pc = pbase + (static_cast<size_t>(cc) * G + jh) * (2 + D);
+        mu[u] = coherent_load(pc);
+        lu[u] = coherent_load(pc + 1);
+#pragma unroll
+        for (int x = 0; x < kX; ++x) vu[u][x] = lane + 64 * x < D ? coherent_load(pc + 2 + lane + 64 * x) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < kMergeBatch; ++u) {
+        const float mc = base + u < nc ? mu[u] : -INFINITY;
+        const float mn = fmaxf(m, mc);
+        const float a = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - mn);
+        const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - mn);
+        l = fmaf(f, lu[u], l * a);
+#pragma unroll
+        for (int x = 0; x < kX; ++x) o[x] = fmaf(f, vu[u][x], o[x] * a);
+        m = mn;
+      }
     }
     const float inv = 1.f / l;
 #pragma unroll
-    for (int x = 0; x < (D + 63) / 64; ++x)
+    for (int x = 0; x < kX; ++x)
       if (lane + 64 * x < D) O[bh * D + lane + 64 * x] = static_cast<bf16>(o[x] * inv);
     if (lane == 0) LSE[bh] = (m + log2f(l)) * kLn2;
   }

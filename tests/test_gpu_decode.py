@@ -125,6 +125,30 @@ def test_decode_1b_layer_shape_sampled():
         assert len(js) == min(int(wl.windows[h]), T)
 
 
+@pytest.mark.parametrize("idx", [3, 5, 6])
+def test_decode_bench_layers_all_heads(idx):
+    """The decode bench's layers at full size and in its launch configuration: the 1B-scale layer, the
+    streaming-head layer (sinks 128 + recent 256 beside full-context heads) and the grouped layer (H = 32
+    over H_kv = 8, d = 128); a prefill of positions 0 .. T - 2, then position T - 1; every (b, h) against
+    the oracle."""
+    _require_gpu()
+    import synth
+    wl = synth.make_workload(idx)
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    dev = lambda key: torch.from_numpy(wl.bits[key].view(np.int16)).view(torch.bfloat16).to("cuda")
+    q, k, v = dev("q"), dev("k"), dev("v")
+    kc, vc = aah.kv_cache_fill(k[:, :, :T - 1].contiguous(), v[:, :, :T - 1].contiguous(), wl.windows, T,
+                               sinks=wl.sinks)
+    pos = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    o, lse = aah.attn_decode(q[:, :, T - 1].contiguous(), k[:, :, T - 1].contiguous(), v[:, :, T - 1].contiguous(),
+                             kc, vc, pos, wl.windows, T, scale=wl.scale, sinks=wl.sinks)
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle.decode_ref(wl.q[:, :, T - 1], wl.k, wl.v, wl.windows, np.full(B, T - 1), T, wl.scale,
+                                     sinks=wl.sinks)
+    _check_o(o, ref_o)
+    assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL
+
+
 def test_decode_graph_replays_match_eager():
     """The step has no allocation or memset, so it can be captured in a HIP graph: every replay
     (with eager work and synchronisations in between) gives the eager result bit for bit."""
