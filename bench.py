@@ -383,6 +383,7 @@ def main():
     dq_ms = span(1, 2) if with_bwd else np.zeros(1)
     dkdv_ms = span(2, 3) if with_bwd else np.zeros(1)
     bwd_ms = span(1, 3) if with_bwd else np.zeros(1)
+    step_dev_ms = span(0, n_ev - 1)  # device time of each step, first launch to last
     ms_per_step = wall * 1e3 / args.steps
 
     pairs_b, acr = aah.window_stats(wl.windows, T, sinks=wl.sinks)
@@ -439,6 +440,7 @@ def main():
             "fwd_pct_bf16_peak": round(100 * fwd_tf / PEAK_BF16_TFLOPS, 2),
             "bwd_pct_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2) if with_bwd else None,
             "step_pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "step_device_ms_p10_median_p90": [round(float(np.percentile(step_dev_ms, p)), 4) for p in (10, 50, 90)],
         },
         "roofline": roof,
     }
