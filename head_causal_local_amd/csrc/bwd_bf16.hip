@@ -421,9 +421,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    const int32_t* __restrict__ sink_eff, int H, int H_kv, int T, float scale) {
   using C = Cfg<D>;
   constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
-  __shared__ __attribute__((aligned(1024))) char ring0[kStage];
-  __shared__ __attribute__((aligned(1024))) char ring1[kStage];
-  __shared__ __attribute__((aligned(1024))) char ring2[kStage];
+  // Three stages (copies two steps ahead) up to d = 64; at d = 128 a stage is 32 KiB and two stages let
+  // two workgroups share a CU's LDS (the registers allow two waves per SIMD).
+  constexpr int kStages = D >= 128 ? 2 : 3;
+  __shared__ __attribute__((aligned(1024))) char ring[kStages][kStage];
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;
@@ -456,10 +457,10 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   };
   constexpr int kFill = 2 * C::kDmaPerWave;
 
-  // Prologue: the first two stages' copies go out before the row loads below,
-  // so that their latencies overlap.
-  fill(tile_at(0), ring0);
-  if (1 < n_tiles) fill(tile_at(1), ring1);
+  // Prologue: the copies of the first kStages - 1 tiles go out before the row loads below, so that
+  // their latencies overlap.
+  fill(tile_at(0), ring[0]);
+  if (kStages == 3 && 1 < n_tiles) fill(tile_at(1), ring[1]);
 
   // Q (premultiplied by c) and dO rows of this lane's query: the B operands of
   // S^T = K Q^T and dP^T = V dO^T.  Lanes ln and ln + 32 hold the two halves
@@ -557,25 +558,35 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     }
   };
 
-  // Ring: the v-th tile visited uses stage v % 3 and fills the stage of tile v + 2.
-  auto step = [&](int v, const char* cur, char* nxt2) __attribute__((always_inline)) {
-    const bool more = v + 2 < n_tiles;
-    if (more) fill(tile_at(v + 2), nxt2);
+  // Ring: the v-th tile visited uses stage v % kStages and fills the stage of tile v + kStages - 1, which
+  // held tile v - 1: the barrier that ended step v - 1 saw every wave finish with it.  A step ends
+  // once the next tile's copies have landed (each wave waits for its own, then the barrier); with
+  // three stages the copies issued in this step may stay in flight.
+  auto step = [&](int v, const char* cur, char* nxtf) __attribute__((always_inline)) {
+    const bool more = v + kStages - 1 < n_tiles;
+    if (more) fill(tile_at(v + kStages - 1), nxtf);
     const int k0 = tile_at(v) * kStep;
     do_block(cur, k0, 0);
     do_block(cur, k0 + 32, 1);
     if (v + 1 >= n_tiles) return true;
-    if (more)
+    if (kStages == 3 && more)
       wait_vm_barrier(kFill);
     else
       wait_vm_barrier(0);
     return false;
   };
   wait_vm_barrier(0);
-  for (int v = 0;; v += 3) {
-    if (step(v, ring0, ring2)) break;
-    if (step(v + 1, ring1, ring0)) break;
-    if (step(v + 2, ring2, ring1)) break;
+  if constexpr (kStages == 3) {
+    for (int v = 0;; v += 3) {
+      if (step(v, ring[0], ring[2])) break;
+      if (step(v + 1, ring[1], ring[0])) break;
+      if (step(v + 2, ring[2], ring[1])) break;
+    }
+  } else {
+    for (int v = 0;; v += 2) {
+      if (step(v, ring[0], ring[1])) break;
+      if (step(v + 1, ring[1], ring[0])) break;
+    }
   }
 
   if (qi >= T) return;
