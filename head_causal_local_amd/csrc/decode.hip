@@ -93,8 +93,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   constexpr int kPairs = kRowsPerWave / 2;
   using vec_t = typename std::conditional<kDL == 1, bf16,
                                           typename std::conditional<kDL == 2, bf16x2, bf16x4>::type>::type;
-  __shared__ float sm_m[kDecodeWaves], sm_l[kDecodeWaves];
-  __shared__ float sm_o[kDecodeWaves][D];
+  // Per-wave partials of up to kGB query heads at a time, merged across the waves after one barrier.
+  constexpr int kGB = GROUPED ? kDecodeWaves : 1;
+  __shared__ float sm_m[kGB][kDecodeWaves], sm_l[kGB][kDecodeWaves];
+  __shared__ float sm_o[kGB][kDecodeWaves][D];
   __shared__ int sm_last;
 
   const int ch = blockIdx.x, b = blockIdx.y;
@@ -172,77 +174,85 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 
   const int c0 = kv_first[g], c1 = kv_first[g + 1];
   float* pbase = part + static_cast<size_t>(b) * n_chunks * G * (2 + D);
-  // ---- one query head of the group at a time: scores, softmax partial, P V, merge of the waves
-  for (int jh = 0; jh < G; ++jh) {
-    const int h = g * G + jh;
-    const int C_h = q_cap[h];
-    const bool valid = is_sink ? row < min(q_sink[h], p - C_h + 1)
-                               : static_cast<unsigned>(row - S_g) < static_cast<unsigned>(ring_live) && age < C_h;
-    const bf16* qrow = Q + (static_cast<size_t>(b) * H + h) * D;
-    float s = -INFINITY;
-    if (valid) {
-      float s0 = 0.f, s1 = 0.f;
+  // ---- the group's query heads in rounds of kGB: each wave forms every head's scores, softmax partial
+  // and P V over its rows into LDS; after one barrier wave w merges head w of the round across the waves
+  // and writes the workgroup's partial.
+  for (int jb = 0; jb < G; jb += kGB) {
+    const int nb = GROUPED ? min(kGB, G - jb) : 1;
+    for (int u = 0; u < nb; ++u) {
+      const int jh = jb + u;
+      const int h = g * G + jh;
+      const int C_h = q_cap[h];
+      const bool valid = is_sink ? row < min(q_sink[h], p - C_h + 1)
+                                 : static_cast<unsigned>(row - S_g) < static_cast<unsigned>(ring_live) && age < C_h;
+      const bf16* qrow = Q + (static_cast<size_t>(b) * H + h) * D;
+      float s = -INFINITY;
+      if (valid) {
+        float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 8 * i);
+        for (int i = 0; i < D / 8; ++i) {
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 8 * i);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const bf16x2 a = {kr[i][e], kr[i][e + 1]};
-          const bf16x2 q2 = {qv[e], qv[e + 1]};
-          if (e & 2)
-            s1 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s1, false);
-          else
-            s0 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s0, false);
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 a = {kr[i][e], kr[i][e + 1]};
+            const bf16x2 q2 = {qv[e], qv[e + 1]};
+            if (e & 2)
+              s1 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s1, false);
+            else
+              s0 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s0, false);
+          }
+        }
+        s = (s0 + s1) * c;
+      }
+      if (jh == 0 && owns_new) {  // the new token's K (from registers) and V enter its rows
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) {
+          *reinterpret_cast<bf16x8*>(kreg + static_cast<size_t>(row) * D + 8 * i) = kr[i];
+          *reinterpret_cast<bf16x8*>(vreg + static_cast<size_t>(row) * D + 8 * i) =
+              *reinterpret_cast<const bf16x8*>(vnew + 8 * i);
         }
       }
-      s = (s0 + s1) * c;
-    }
-    if (jh == 0 && owns_new) {  // the new token's K (from registers) and V enter its rows
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        *reinterpret_cast<bf16x8*>(kreg + static_cast<size_t>(row) * D + 8 * i) = kr[i];
-        *reinterpret_cast<bf16x8*>(vreg + static_cast<size_t>(row) * D + 8 * i) =
-            *reinterpret_cast<const bf16x8*>(vnew + 8 * i);
-      }
-    }
-    const float m_w = wave_max(s);
-    const float pw = (valid && m_w != -INFINITY) ? __builtin_amdgcn_exp2f(s - m_w) : 0.f;
-    const float l_w = wave_sum(pw);
+      const float m_w = wave_max(s);
+      const float pw = (valid && m_w != -INFINITY) ? __builtin_amdgcn_exp2f(s - m_w) : 0.f;
+      const float l_w = wave_sum(pw);
 
-    // P V: lanes (hl, j) take rows 2 r + hl of the wave and dimensions kDL j .. kDL j + kDL - 1
-    float acc[kDL];
+      // P V: lanes (hl, j) take rows 2 r + hl of the wave and dimensions kDL j .. kDL j + kDL - 1
+      float acc[kDL];
 #pragma unroll
-    for (int x = 0; x < kDL; ++x) acc[x] = 0.f;
+      for (int x = 0; x < kDL; ++x) acc[x] = 0.f;
 #pragma unroll
-    for (int r = 0; r < kPairs; ++r) {
-      const float pk = __shfl(pw, 2 * r + hl);  // 0 for rows this head does not attend to
-      if constexpr (kDL == 1) {
-        acc[0] = fmaf(pk, static_cast<float>(vr[r]), acc[0]);
-      } else {
+      for (int r = 0; r < kPairs; ++r) {
+        const float pk = __shfl(pw, 2 * r + hl);  // 0 for rows this head does not attend to
+        if constexpr (kDL == 1) {
+          acc[0] = fmaf(pk, static_cast<float>(vr[r]), acc[0]);
+        } else {
 #pragma unroll
-        for (int x = 0; x < kDL; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[r][x]), acc[x]);
+          for (int x = 0; x < kDL; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[r][x]), acc[x]);
+        }
       }
-    }
-    // Even and odd rows: lanes j and j + 32 hold the same dimensions.
+      // Even and odd rows: lanes j and j + 32 hold the same dimensions.
 #pragma unroll
-    for (int x = 0; x < kDL; ++x) acc[x] += __shfl_xor(acc[x], 32);
+      for (int x = 0; x < kDL; ++x) acc[x] += __shfl_xor(acc[x], 32);
 
-    if (lane == 0) {
-      sm_m[wave] = m_w;
-      sm_l[wave] = l_w;
-    }
-    if (hl == 0) {
+      if (lane == 0) {
+        sm_m[u][wave] = m_w;
+        sm_l[u][wave] = l_w;
+      }
+      if (hl == 0) {
 #pragma unroll
-      for (int x = 0; x < kDL; ++x) sm_o[wave][kDL * j + x] = acc[x];
+        for (int x = 0; x < kDL; ++x) sm_o[u][wave][kDL * j + x] = acc[x];
+      }
     }
     __syncthreads();
-    if (wave == 0) {
-      float m = sm_m[0];
+    if (wave < nb) {
+      const int u = wave, jh = jb + wave;
+      float m = sm_m[u][0];
 #pragma unroll
-      for (int w = 1; w < kDecodeWaves; ++w) m = fmaxf(m, sm_m[w]);
+      for (int w = 1; w < kDecodeWaves; ++w) m = fmaxf(m, sm_m[u][w]);
       float f[kDecodeWaves];
 #pragma unroll
-      for (int w = 0; w < kDecodeWaves; ++w) f[w] = sm_m[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[w] - m);
+      for (int w = 0; w < kDecodeWaves; ++w)
+        f[w] = sm_m[u][w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sm_m[u][w] - m);
       // The workgroups of one (b, g) may run on different XCDs, whose L2 caches are not coherent
       // with each other: partials go out with device-coherent stores, the counter is a
       // device-scope atomic issued once those stores have completed, and the merging workgroup
@@ -253,17 +263,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         coherent_store(out, m);
         float lsum = 0.f;
 #pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) lsum = fmaf(f[w], sm_l[w], lsum);
+        for (int w = 0; w < kDecodeWaves; ++w) lsum = fmaf(f[w], sm_l[u][w], lsum);
         coherent_store(out + 1, lsum);
       }
       for (int d = lane; d < D; d += 64) {
         float od = 0.f;
 #pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) od = fmaf(f[w], sm_o[w][d], od);
+        for (int w = 0; w < kDecodeWaves; ++w) od = fmaf(f[w], sm_o[u][w][d], od);
         coherent_store(out + 2 + d, od);
       }
     }
-    if (jh + 1 < G) __syncthreads();  // the next head reuses the LDS buffers
+    if (jb + kGB < G) __syncthreads();  // the next round reuses the LDS buffers
+  }
+  if constexpr (GROUPED) {
+    // Several waves stored partials: each waits for its own stores, then the barrier orders them
+    // before the counter.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
   if (wave == 0) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
