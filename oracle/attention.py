@@ -46,8 +46,9 @@ from __future__ import annotations
 import numpy as np
 
 
-def window_allowed(T: int, w: int, sink: int = 0) -> np.ndarray:
-    """Boolean [T, T] matrix; entry (i, j) is True when key j is in query i's window.
+def window_allowed(T: int, w: int, sink: int = 0, rows=None) -> np.ndarray:
+    """Boolean [T, T] matrix (or [len(rows), T] for the given query rows only); entry (i, j) is True
+    when key j is in query i's window.
 
     AAH section 5.8: t_q - W + 1 <= t_k <= t_q, with W clamped to T; with a sink
     size S (AoH section 5), keys t_k < S are allowed too (still t_k <= t_q)."""
@@ -56,7 +57,7 @@ def window_allowed(T: int, w: int, sink: int = 0) -> np.ndarray:
     if sink < 0:
         raise ValueError("sink must be >= 0")
     w = min(int(w), T)
-    i = np.arange(T)[:, None]
+    i = (np.arange(T) if rows is None else np.asarray(rows))[:, None]
     j = np.arange(T)[None, :]
     return (j <= i) & ((j >= i - w + 1) | (j < sink))
 
@@ -72,9 +73,8 @@ def _head_probs(q: np.ndarray, k: np.ndarray, w: int, scale: float, rows=None, s
     key j, m the row max of the scaled masked scores and l the row sum of
     exp(score - m)."""
     T = k.shape[0]
-    allowed = window_allowed(T, w, sink)
+    allowed = window_allowed(T, w, sink, rows=rows)
     if rows is not None:
-        allowed = allowed[rows]
         q = q[rows]
     S = scale * (q @ k.T)                      # explicit scores
     S = np.where(allowed, S, -np.inf)          # additive -inf mask M_W

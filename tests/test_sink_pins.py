@@ -159,3 +159,16 @@ def test_pair_count_with_sinks_brute_force(T, w, s):
     """Brute force: the pair count equals the size of every row's key set, summed."""
     assert oracle.pair_count_ref(T, w, s) == sum(len(_key_set(i, w, s)) for i in range(T))
     assert oracle.pair_count_ref(T, w, s) == int(oracle.window_allowed(T, w, s).sum())
+
+
+@pytest.mark.parametrize("T,w,s", [(1, 1, 0), (9, 3, 2), (40, 7, 0), (40, 100, 5), (33, 1, 33)])
+def test_window_rows_restriction_matches_full_mask_and_brute_force(T, w, s):
+    """The row-restricted mask (used for spot checks of long sequences) is the full mask's rows, and both
+    agree entry by entry with the visibility rule written as a loop."""
+    full = oracle.window_allowed(T, w, s)
+    rows = sorted({0, T // 2, T - 1})
+    assert np.array_equal(oracle.window_allowed(T, w, s, rows=rows), full[rows])
+    W = min(w, T)
+    for i in range(T):
+        for j in range(T):
+            assert full[i, j] == (j <= i and (j > i - W or j < s))
