@@ -290,3 +290,24 @@ def test_diag_and_feature_validation():
     assert feat(ws=FAKE + 64) == 1           # workspace must be 256-byte aligned
     assert feat(d=40) == 2
     assert feat(H_kv=3) == 1
+
+
+def test_missing_library_fails_loudly():
+    """Without the built library every entry point raises (there is no CPU or PyTorch fallback)."""
+    import subprocess
+    import sys
+    code = (
+        "import head_causal_local_amd as aah\n"
+        "from head_causal_local_amd import _lib\n"
+        "_lib.LIB_PATH = '/nonexistent/libaah_attn.so'\n"
+        "_lib._lib = None\n"
+        "try:\n"
+        "    aah.window_stats([4, 8], 16)\n"
+        "except RuntimeError as e:\n"
+        "    print('raised:', e)\n"
+        "else:\n"
+        "    print('no error')\n")
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert res.returncode == 0, res.stderr
+    assert "raised:" in res.stdout and "missing" in res.stdout and "no fallback" in res.stdout
