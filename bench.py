@@ -39,8 +39,10 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # After idle the device needs some 60 steps (about 30 ms) of this load before its clock settles; the
+    # default warm-up covers that, so the timed steps measure the sustained rate.
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="3", help="catalogued workload id (default 3: fwd+bwd 1B-scale layer)")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
