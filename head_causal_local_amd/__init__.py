@@ -121,9 +121,12 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
     elif lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     sk = _sinks_arg(sinks, H)
+    # Workspace for the split launch (partial results of long items' chunks) when the library asks for one.
+    ws_bytes = lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, T, d, _dtype_code(q))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d,
-                            _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(), None, 0,
-                            _stream_ptr(q, stream))
+                            _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(),
+                            ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q, stream))
     check(st)
     return out, lse
 
@@ -397,6 +400,28 @@ def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_til
              sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None):
     """Backward work list as an int32 array [n, 4] of (b * H_kv + g, kv_tile_index, q_lo, q_hi)."""
     return _plan(lib().aah_plan_bwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv)
+
+
+def plan_fwd_split(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, chunk_tiles: int,
+                   n_queues: int = 8, H_kv: Optional[int] = None):
+    """Split forward work list: (items int32 [n, 4] as plan_fwd, slots int32 [n] (-1: the item writes its own
+    rows), merge records int32 [m, 4] of (bh, q_tile_index, first slot, chunks))."""
+    w = _windows_arg(windows)
+    H_kv = H if H_kv is None else H_kv
+    n, m = ctypes.c_int64(), ctypes.c_int64()
+    fn = lib().aah_plan_fwd_split
+    st = fn(_wptr(w), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, None, None, 0, ctypes.byref(n), None, 0,
+            ctypes.byref(m))
+    if st not in (0, 1):
+        check(st)
+    items = (WorkItem * max(n.value, 1))()
+    slots = np.zeros(max(n.value, 1), dtype=np.int32)
+    merges = (WorkItem * max(m.value, 1))()
+    check(fn(_wptr(w), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, items,
+             slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n), merges, m.value,
+             ctypes.byref(m)))
+    as_arr = lambda buf, k: np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[:k].copy()  # noqa: E731
+    return as_arr(items, n.value), slots[: n.value].copy(), as_arr(merges, m.value)
 
 
 def window_stats(windows: Sequence[int], T: int, sinks: Optional[Sequence[int]] = None) -> Tuple[int, float]:

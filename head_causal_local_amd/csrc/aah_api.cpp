@@ -191,6 +191,133 @@ void bwd_tiles(aah_dtype dt, int* row, int* col) {
   }
 }
 
+// ------------------------------------------------------------------ split forward
+//
+// A bf16 forward with fewer items than the device holds workgroups leaves
+// most of it idle, and its time is that of its longest items.  Then every
+// item longer than L key tiles is split into chunks of at most L tiles
+// (plan_forward_split), L = max(kMinChunkTiles, total tiles / resident
+// workgroups), so that about one chunk per resident workgroup remains; a merge
+// launch combines each split item's chunks.  The chunks' partial results live in
+// the caller's workspace (aah_attn_fwd_workspace_size).
+
+// Does some head keep sink keys that change its mask (an effective sink size above 0)?
+bool any_sink(const int32_t* windows, const int32_t* sinks, int H, int T) {
+  if (sinks == nullptr) return false;
+  for (int h = 0; h < H; ++h)
+    if (aah::effective_sink(sinks[h], windows[h], T) > 0) return true;
+  return false;
+}
+
+// Shortest chunk.  Each chunk adds a partial result (128 rows x (d + 2) fp32) that the merge reads back,
+// so short chunks cost traffic; on the single layer B=1 H=16 T=4096 d=64 minimums of 8 / 12 / 16 / 24 / 32
+// tiles measured 366 / 379 / 380 / 415 / 397 TFLOP/s.
+constexpr int kMinChunkTiles = 24;
+
+// Resident workgroups of the plain bf16 forward on the current device (occupancy query cached per device and d).
+int resident_workgroups(int d) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::pair<int, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto found = cache.find({dev, d});
+  if (found != cache.end()) return found->second;
+  const int n = aah::fwd_bf16_resident(d);
+  if (n > 0) cache.emplace(std::make_pair(dev, d), n);
+  return n;
+}
+
+// Chunk length for a bf16 forward without sinks, or 0 when splitting does not apply.
+int split_chunk_tiles(const int32_t* windows, int B, int H, int T, int d) {
+  const int q_tile = aah::kFwdBf16RowTile, kv_tile = aah::kFwdBf16ColTile;
+  const int n_qt = (T + q_tile - 1) / q_tile;
+  const int64_t n_items = static_cast<int64_t>(B) * H * n_qt;
+  const int resident = resident_workgroups(d);
+  if (resident <= 0 || n_items >= resident) return 0;
+  int64_t total = 0;
+  int longest = 0;
+  for (int h = 0; h < H; ++h) {
+    const int W = aah::effective_window(windows[h], T);
+    for (int qt = 0; qt < n_qt; ++qt) {
+      const int q0 = qt * q_tile, q1 = std::min(T, q0 + q_tile);
+      const int n = (q1 - 1) / kv_tile + 1 - std::max(0, q0 - W + 1) / kv_tile;
+      total += n;
+      longest = std::max(longest, n);
+    }
+  }
+  total *= B;
+  const int L = static_cast<int>(std::max<int64_t>(kMinChunkTiles, (total + resident - 1) / resident));
+  return longest > L ? L : 0;
+}
+
+struct SplitDevicePlan {
+  WorkItem* items = nullptr;
+  int32_t* slots = nullptr;
+  WorkItem* merges = nullptr;
+  int32_t* win = nullptr;
+  int n_items = 0, n_merges = 0, n_slots = 0;
+};
+std::map<std::vector<int64_t>, SplitDevicePlan> g_split_cache;
+
+// Partial-result bytes of a split plan: accumulators, then (max, sum) pairs, each 256-byte aligned.
+size_t split_acc_bytes(int n_slots, int d) {
+  return round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * d * sizeof(float), 256);
+}
+size_t split_workspace(int n_slots, int d) {
+  return split_acc_bytes(n_slots, d) +
+         round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * 2 * sizeof(float), 256);
+}
+
+// Split plan of a bf16 forward without sinks with chunk length L (> 0), uploaded once per key.
+aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T, int d, int L,
+                          SplitDevicePlan* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::vector<int32_t> win(H);
+  for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
+  std::vector<int64_t> key = {dev, B, H, H_kv, T, d, L};
+  key.insert(key.end(), win.begin(), win.end());
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto found = g_split_cache.find(key);
+  if (found != g_split_cache.end()) {
+    *out = found->second;
+    return AAH_OK;
+  }
+  const aah::SplitPlan sp = aah::plan_forward_split(windows, B, H, H_kv, T, aah::kFwdBf16RowTile,
+                                                    aah::kFwdBf16ColTile, kQueues, L);
+  SplitDevicePlan p;
+  p.n_items = static_cast<int>(sp.items.size());
+  p.n_merges = static_cast<int>(sp.merges.size());
+  p.n_slots = sp.n_slots;
+  auto upload = [](const void* host, size_t bytes, void** dev_ptr) {
+    hipError_t err = hipMalloc(dev_ptr, bytes);
+    if (err != hipSuccess) return err;
+    err = hipMemcpy(*dev_ptr, host, bytes, hipMemcpyHostToDevice);
+    if (err != hipSuccess) {
+      (void)hipFree(*dev_ptr);
+      *dev_ptr = nullptr;
+    }
+    return err;
+  };
+  e = upload(sp.items.data(), sp.items.size() * sizeof(WorkItem), reinterpret_cast<void**>(&p.items));
+  if (e == hipSuccess) e = upload(sp.slot.data(), sp.slot.size() * sizeof(int32_t), reinterpret_cast<void**>(&p.slots));
+  if (e == hipSuccess)
+    e = upload(sp.merges.data(), std::max<size_t>(1, sp.merges.size()) * sizeof(WorkItem),
+               reinterpret_cast<void**>(&p.merges));
+  if (e == hipSuccess) e = upload(win.data(), win.size() * sizeof(int32_t), reinterpret_cast<void**>(&p.win));
+  if (e != hipSuccess) {
+    for (void* ptr : {static_cast<void*>(p.items), static_cast<void*>(p.slots), static_cast<void*>(p.merges),
+                      static_cast<void*>(p.win)})
+      if (ptr != nullptr) (void)hipFree(ptr);
+    return hip_fail(e, "hipMalloc / hipMemcpy(split plan)");
+  }
+  g_split_cache.emplace(std::move(key), p);
+  *out = p;
+  return AAH_OK;
+}
+
 // Workspace of the backward: nl2 = -lse log2(e) and nD = -D, fp32 [B,H,T]
 // each, every array starting on a 256-byte boundary.
 size_t bwd_array_bytes(int B, int H, int T) { return round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256); }
@@ -390,6 +517,18 @@ size_t aah_attn_workspace_size(int B, int H, int T, int d, aah_dtype dt, int is_
   return is_bwd ? bwd_workspace(B, H, T, d, dt) : 0;
 }
 
+size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                                   int d, aah_dtype dt) {
+  if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
+  g_detail.clear();
+  if (any_sink(windows, sinks, H, T)) return 0;
+  const int L = split_chunk_tiles(windows, B, H, T, d);
+  if (L == 0) return 0;
+  SplitDevicePlan sp;
+  if (get_split_plan(windows, B, H, H_kv, T, d, L, &sp) != AAH_OK) return 0;
+  return split_workspace(sp.n_slots, d);
+}
+
 aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* col_tile) {
   if (row_tile == nullptr || col_tile == nullptr) return fail(AAH_ERR_INVALID_ARG, "NULL output pointer");
   if (dt != AAH_BF16 && dt != AAH_F32) return fail(AAH_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
@@ -408,7 +547,7 @@ namespace {
 // Forward, with the per-row diagnostics when ent / onorm are set (both or neither).
 aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks, int B,
                     int H, int H_kv, int T, int d, aah_dtype dt, float scale, void* o, float* lse, float* ent,
-                    float* onorm, aah_stream_t stream) {
+                    float* onorm, void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
@@ -420,12 +559,31 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
+  // Split launch: bf16, no diagnostics, no sink keys, and a workspace large enough for the partials.
+  const int L = dt == AAH_BF16 && ent == nullptr && !any_sink(windows, sinks, H, T) && workspace != nullptr
+                    ? split_chunk_tiles(windows, B, H, T, d)
+                    : 0;
+  if (L > 0) {
+    SplitDevicePlan sp;
+    AAH_TRY(get_split_plan(windows, B, H, H_kv, T, d, L, &sp));
+    if (workspace_bytes >= split_workspace(sp.n_slots, d)) {
+      if (!aligned(workspace, 256)) return fail(AAH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+      float* part_acc = static_cast<float*>(workspace);
+      float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_acc_bytes(sp.n_slots, d));
+      const aah::FwdSplit split{sp.slots, sp.merges, sp.n_merges, part_acc, part_ml};
+      e = aah::launch_fwd_bf16(q, k, v, o, lse, nullptr, nullptr, sp.items, sp.n_items, sp.win, nullptr, s, &split,
+                               st);
+      if (e != hipSuccess) return hip_fail(e, "split forward launch");
+      return AAH_OK;
+    }
+  }
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   if (dt == AAH_BF16)
-    e = aah::launch_fwd_bf16(q, k, v, o, lse, ent, onorm, plan.items, plan.n_items, plan.win, plan.sink, s, st);
+    e = aah::launch_fwd_bf16(q, k, v, o, lse, ent, onorm, plan.items, plan.n_items, plan.win, plan.sink, s, nullptr,
+                             st);
   else
     e = aah::launch_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
                             static_cast<const float*>(v), static_cast<float*>(o), lse, ent, onorm, plan.items,
@@ -446,10 +604,9 @@ extern "C" {
 aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32_t* windows, const int32_t* sinks,
                         int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale, void* o, float* lse,
                         void* workspace, size_t workspace_bytes, aah_stream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   g_detail.clear();
-  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, nullptr, nullptr, stream);
+  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, nullptr, nullptr, workspace,
+                  workspace_bytes, stream);
 }
 
 aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
@@ -458,7 +615,8 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
   g_detail.clear();
   AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
   AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
-  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, stream);
+  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, nullptr, 0,
+                  stream);
 }
 
 size_t aah_head_features_workspace_size(int B, int H, int T, int d) {
@@ -699,6 +857,33 @@ aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H,
   return AAH_OK;
 }
 
+aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
+                              int n_queues, int chunk_tiles, aah_work_item* items, int32_t* slots,
+                              int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,
+                              int64_t* n_merges) {
+  g_detail.clear();
+  if (n_items == nullptr || n_merges == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items / n_merges is NULL");
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
+  if (q_tile < 1 || kv_tile < 1 || n_queues < 1 || chunk_tiles < 1)
+    return fail(AAH_ERR_INVALID_ARG, "tiles, n_queues and chunk_tiles must be >= 1");
+  AAH_TRY(check_kv_heads(H, H_kv));
+  AAH_TRY(check_windows(windows, nullptr, H));
+  const aah::SplitPlan sp = aah::plan_forward_split(windows, B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles);
+  *n_items = static_cast<int64_t>(sp.items.size());
+  *n_merges = static_cast<int64_t>(sp.merges.size());
+  if (capacity < *n_items || merge_capacity < *n_merges)
+    return fail(AAH_ERR_INVALID_ARG, "capacity %lld / %lld < %lld items / %lld merge records",
+                static_cast<long long>(capacity), static_cast<long long>(merge_capacity),
+                static_cast<long long>(*n_items), static_cast<long long>(*n_merges));
+  if ((*n_items > 0 && (items == nullptr || slots == nullptr)) || (*n_merges > 0 && merges == nullptr))
+    return fail(AAH_ERR_INVALID_ARG, "output array is NULL");
+  std::memcpy(items, sp.items.data(), sp.items.size() * sizeof(WorkItem));
+  std::memcpy(slots, sp.slot.data(), sp.slot.size() * sizeof(int32_t));
+  if (!sp.merges.empty()) std::memcpy(merges, sp.merges.data(), sp.merges.size() * sizeof(WorkItem));
+  return AAH_OK;
+}
+
 void aah_cache_clear(void) {
   std::lock_guard<std::mutex> lock(g_mu);
   for (auto& kv : g_cache) {
@@ -706,6 +891,13 @@ void aah_cache_clear(void) {
     (void)hipFree(kv.second.win);
   }
   g_cache.clear();
+  for (auto& kv : g_split_cache) {
+    (void)hipFree(kv.second.items);
+    (void)hipFree(kv.second.slots);
+    (void)hipFree(kv.second.merges);
+    (void)hipFree(kv.second.win);
+  }
+  g_split_cache.clear();
   for (auto& kv : g_decode_cache) {
     (void)hipFree(kv.second.chunks);
     (void)hipFree(kv.second.tables);

@@ -104,7 +104,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
                      bf16* __restrict__ O, float* __restrict__ LSE, float* __restrict__ ENT,
                      float* __restrict__ ONORM, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
-                     int T, float c) {
+                     int T, float c, const int32_t* __restrict__ slots, float* __restrict__ part_acc,
+                     float* __restrict__ part_ml) {
   using C = Cfg<D>;
   constexpr int NC = C::kNC;
   __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes];
@@ -114,6 +115,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
+  // A chunk of a split item leaves its rows' partial result in its slot instead of O and LSE.
+  const int slot = slots != nullptr ? slots[blockIdx.x] : -1;
   const int W = win_eff[it.bh % H];
   const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
   // Tiles in visiting order: sink tiles 0 .. ns - 1 (those before the window's
@@ -362,6 +365,20 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     sq_tot = half_swap_sum(sq);
   }
   if (!row_ok) return;
+  if (slot >= 0) {
+    // Unnormalised partial of row qi over this chunk's keys: acc (fp32, [d]), then (m, l) with m in
+    // the log2 domain (-inf and l = 0 if the row saw none of them).
+    const size_t prow = static_cast<size_t>(slot) * kRows + wave * 32 + ln;
+    float* arow = part_acc + prow * D;
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(arow + 32 * b + 8 * i + 4 * hl) =
+            f32x4{acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]};
+    if (hl == 0) *reinterpret_cast<u32x2*>(part_ml + prow * 2) = u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)};
+    return;
+  }
   const float inv = 1.f / l_tot;
   bf16* Orow = O + base + static_cast<size_t>(qi) * D;
   // O^T block b, register r holds dim 32 b + 8 (r/4) + 4 hl + r%4 of query qi.
@@ -381,41 +398,94 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   }
 }
 
+// Combines the chunks of each split item: with (acc_c, m_c, l_c) the partials
+// of row i over chunk c and M = max_c m_c, O_i = sum_c 2^(m_c - M) acc_c /
+// sum_c 2^(m_c - M) l_c and LSE_i = (M + log2 sum_c 2^(m_c - M) l_c) ln 2.
+// Workgroup (merge record, row group); D / 4 threads per row, four dims each.
+template <int D>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(const WorkItem* __restrict__ merges,
+                                                        const float* __restrict__ part_acc,
+                                                        const float* __restrict__ part_ml, bf16* __restrict__ O,
+                                                        float* __restrict__ LSE, int T) {
+  constexpr int kPerRow = D / 4;
+  constexpr int kRowsPerWg = 256 / kPerRow;
+  const WorkItem mg = merges[blockIdx.x];  // {bh, tile, first slot, chunks}
+  const int r = blockIdx.y * kRowsPerWg + static_cast<int>(threadIdx.x) / kPerRow;
+  const int dq = (static_cast<int>(threadIdx.x) % kPerRow) * 4;
+  const int row = mg.tile * kRows + r;
+  if (r >= kRows || row >= T) return;
+  float M = -INFINITY;
+  for (int ch = 0; ch < mg.hi; ++ch) M = fmaxf(M, part_ml[(static_cast<size_t>(mg.lo + ch) * kRows + r) * 2]);
+  float L = 0.f;
+  f32x4 a = f32x4{};
+  for (int ch = 0; ch < mg.hi; ++ch) {
+    const size_t prow = static_cast<size_t>(mg.lo + ch) * kRows + r;
+    const float w = __builtin_amdgcn_exp2f(part_ml[prow * 2] - M);  // 0 for a chunk the row did not see
+    L = fmaf(w, part_ml[prow * 2 + 1], L);
+    const f32x4 x = *reinterpret_cast<const f32x4*>(part_acc + prow * D + dq);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = fmaf(w, x[j], a[j]);
+  }
+  const float inv = 1.f / L;
+  store_bf16x4(O + (static_cast<size_t>(mg.bh) * T + row) * D + dq, a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
+  if (dq == 0) LSE[static_cast<size_t>(mg.bh) * T + row] = (M + log2f(L)) * kLn2;
+}
+
 template <int D, bool SINK, bool DIAG>
 void launch_k(const void* q, const void* k, const void* v, void* o, float* lse, float* ent, float* onorm,
               const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-              const AttnShape& s, hipStream_t stream) {
+              const AttnShape& s, const FwdSplit* split, hipStream_t stream) {
   const float c = s.scale * 1.4426950408889634f;  // scale * log2(e)
   hipLaunchKernelGGL((fwd_bf16_kernel<D, SINK, DIAG>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.H_kv, s.T, c);
+                     static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.H_kv, s.T, c,
+                     split != nullptr ? split->slots : nullptr, split != nullptr ? split->part_acc : nullptr,
+                     split != nullptr ? split->part_ml : nullptr);
+  if (split != nullptr && split->n_merges > 0)
+    hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3(split->n_merges, kRows / (256 / (D / 4))), dim3(256), 0, stream,
+                       split->merges, split->part_acc, split->part_ml, static_cast<bf16*>(o), lse, s.T);
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o, float* lse, float* ent, float* onorm,
                     const WorkItem* items, int n_items, const int32_t* win_eff, const int32_t* sink_eff,
-                    const AttnShape& s, hipStream_t stream) {
+                    const AttnShape& s, const FwdSplit* split, hipStream_t stream) {
   const bool sink = sink_eff != nullptr, diag = ent != nullptr;
   if (sink && diag)
-    launch_k<D, true, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    launch_k<D, true, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
   else if (sink)
-    launch_k<D, true, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    launch_k<D, true, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
   else if (diag)
-    launch_k<D, false, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    launch_k<D, false, true>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
   else
-    launch_k<D, false, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    launch_k<D, false, false>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int fwd_bf16_resident(int d) {
+  const void* fn = nullptr;
+  switch (d) {
+    case 32: fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<32, false, false>); break;
+    case 64: fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<64, false, false>); break;
+    case 128: fn = reinterpret_cast<const void*>(&fwd_bf16_kernel<128, false, false>); break;
+    default: return 0;
+  }
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ent,
                            float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
-                           const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+                           const int32_t* sink_eff, const AttnShape& s, const FwdSplit* split, hipStream_t stream) {
   switch (s.d) {
-    case 32: return launch_d<32>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
-    case 64: return launch_d<64>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
-    case 128: return launch_d<128>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, stream);
+    case 32: return launch_d<32>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 64: return launch_d<64>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 128: return launch_d<128>(q, k, v, o, lse, ent, onorm, items, n_items, win_eff, sink_eff, s, split, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,9 +34,26 @@ struct AttnShape {
 // bf16 forward on MFMA (d in {32, 64, 128}).  ent / onorm: nullptr, or fp32
 // [B,H,T] outputs of each row's attention entropy and output-row norm (both set
 // or both null).
+// Split forward (plan_forward_split): slots[i] is item i's partial slot or -1;
+// a chunk writes its rows' fp32 accumulator to part_acc [slot][128][d] and
+// (max in the log2 domain, row sum) to part_ml [slot][128][2]; after the
+// forward, one merge workgroup group per record in merges combines them into O
+// and LSE.
+struct FwdSplit {
+  const int32_t* slots;
+  const WorkItem* merges;
+  int n_merges;
+  float* part_acc;
+  float* part_ml;
+};
+
+// split: nullptr, or the split plan's device arrays and the partial buffers.
 hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, float* ent,
                            float* onorm, const WorkItem* items, int n_items, const int32_t* win_eff,
-                           const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
+                           const int32_t* sink_eff, const AttnShape& s, const FwdSplit* split, hipStream_t stream);
+
+// Workgroups of the plain bf16 forward the current device holds at once, or 0 if the query fails.
+int fwd_bf16_resident(int d);
 
 // Scalar forward for fp32 (d in {32, 64, 128}); ent / onorm as for bf16.
 hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, float* ent,

@@ -28,12 +28,14 @@ struct Planned {
   WorkItem item;
   int cost;   // streamed tiles the item visits
   int32_t group;  // key/value group: items of one group share a queue and sort next to each other
+  int32_t slot = -1;  // partial-result slot of a chunk of a split item, or -1
 };
 
 // Deal the items of each head to n_queues queues (longest head first, each to
 // the least-loaded queue), sort each queue by cost descending, and interleave
 // the queues slot by slot.  Items arrive grouped by head in `per_head`.
-std::vector<WorkItem> interleave(const std::vector<std::vector<Planned>>& per_head, int n_queues) {
+std::vector<WorkItem> interleave(const std::vector<std::vector<Planned>>& per_head, int n_queues,
+                                 std::vector<int32_t>* slots = nullptr) {
   const int n_heads = static_cast<int>(per_head.size());
   std::vector<int64_t> head_cost(n_heads, 0);
   for (int i = 0; i < n_heads; ++i)
@@ -67,9 +69,13 @@ std::vector<WorkItem> interleave(const std::vector<std::vector<Planned>>& per_he
   }
   std::vector<WorkItem> out;
   out.reserve(longest * n_queues);
+  if (slots != nullptr) slots->clear();
   for (size_t i = 0; i < longest; ++i)
-    for (int qi = 0; qi < n_queues; ++qi)
-      out.push_back(i < queues[qi].size() ? queues[qi][i].item : WorkItem{-1, 0, 0, 0});
+    for (int qi = 0; qi < n_queues; ++qi) {
+      const bool real = i < queues[qi].size();
+      out.push_back(real ? queues[qi][i].item : WorkItem{-1, 0, 0, 0});
+      if (slots != nullptr) slots->push_back(real ? queues[qi][i].slot : -1);
+    }
   return out;
 }
 
@@ -102,6 +108,41 @@ std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks,
     }
   }
   return interleave(per_group, n_queues);
+}
+
+SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
+                             int n_queues, int chunk_tiles) {
+  const int n_qt = ceil_div(T, q_tile);
+  const int G = H / H_kv;
+  SplitPlan plan;
+  std::vector<std::vector<Planned>> per_group(static_cast<size_t>(B) * H_kv);
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int W = effective_window(windows[h], T);
+      const int32_t group = b * H_kv + h / G;
+      auto& list = per_group[static_cast<size_t>(group)];
+      for (int qt = 0; qt < n_qt; ++qt) {
+        const int q0 = qt * q_tile;
+        const int q1 = std::min(T, q0 + q_tile);
+        const int lo = std::max(0, q0 - W + 1) / kv_tile, hi = (q1 - 1) / kv_tile + 1;
+        const int n = hi - lo;
+        if (chunk_tiles < 1 || n <= chunk_tiles) {
+          list.push_back(Planned{WorkItem{b * H + h, qt, lo, hi}, n, group});
+          continue;
+        }
+        const int n_chunks = ceil_div(n, chunk_tiles);
+        plan.merges.push_back(WorkItem{b * H + h, qt, plan.n_slots, n_chunks});
+        for (int c = 0; c < n_chunks; ++c) {
+          // Near-equal chunks: the first n % n_chunks get one tile more.
+          const int c_lo = lo + c * (n / n_chunks) + std::min(c, n % n_chunks);
+          const int c_hi = c_lo + n / n_chunks + (c < n % n_chunks ? 1 : 0);
+          list.push_back(Planned{WorkItem{b * H + h, qt, c_lo, c_hi}, c_hi - c_lo, group, plan.n_slots++});
+        }
+      }
+    }
+  }
+  plan.items = interleave(per_group, n_queues, &plan.slot);
+  return plan;
 }
 
 std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,

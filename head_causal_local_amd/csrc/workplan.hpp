@@ -58,6 +58,24 @@ inline void query_range(int k0, int k1, int W, int S, int T, int q_tile, int* lo
 std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                    int q_tile, int kv_tile, int n_queues);
 
+// Forward items with long key ranges split into chunks (for launches with
+// fewer items than the device holds workgroups).  Every item of more than
+// chunk_tiles key tiles becomes ceil(n / chunk_tiles) items over consecutive
+// sub-ranges of its tiles; each chunk writes its rows' unnormalised partial
+// result to its own slot (slot[i] >= 0) and one merge record {bh, tile, first
+// slot, number of chunks} per split item combines them.  Items of at most
+// chunk_tiles tiles keep slot -1 and write O and LSE themselves.  Chunks are
+// dealt to queues and ordered like plan_forward's items (longest first).
+// No sink keys: a sink tile belongs to the first chunk of an item only.
+struct SplitPlan {
+  std::vector<WorkItem> items;
+  std::vector<int32_t> slot;
+  std::vector<WorkItem> merges;
+  int n_slots = 0;
+};
+SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
+                             int n_queues, int chunk_tiles);
+
 // Backward items: one per (b, key/value head g, key tile); [lo, hi) spans the
 // query tiles that see the keys in any of the group's query heads (each head's
 // own range is query_range, starting at the same lo).

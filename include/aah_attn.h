@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 6
+#define AAH_ABI_VERSION 7
 
 typedef enum {
   AAH_OK = 0,
@@ -107,14 +107,33 @@ const char* aah_last_error_detail(void);
  * o [B,H,T,d] (dtype dt) and lse [B,H,T] (fp32): lse[b,h,i] is the natural log
  * of sum_j exp(scale * q_i . k_j) over the window of row i.  Accumulation and
  * softmax run in fp32 whatever dt is; bf16 outputs are rounded to nearest even.
- * The forward needs no workspace: pass workspace = NULL, workspace_bytes = 0
- * (a non-NULL workspace is accepted and ignored).
+ * Workspace is optional.  With workspace = NULL (or fewer bytes than
+ * aah_attn_fwd_workspace_size reports) every work item writes its own rows.
+ * With a device workspace of at least that many bytes, 256-byte aligned, a bf16
+ * launch with fewer work items than the device holds workgroups splits its long
+ * items' key ranges into chunks whose partial results (row max, row sum, fp32
+ * accumulator) land in the workspace, and a second kernel on the same stream
+ * merges them into o and lse.  That fills the device when B * H * ceil(T / 128)
+ * is small (one sequence, few heads).  The results agree within the bf16
+ * bounds, not bitwise, since each chunk rounds its weights against its own
+ * reference.  The workspace carries nothing between calls; calls that share one
+ * must not run concurrently.
  */
 aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
                         const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
                         aah_dtype dt, float scale, void* o, float* lse,
                         void* workspace, size_t workspace_bytes,
                         aah_stream_t stream);
+
+/*
+ * Workspace bytes with which aah_attn_fwd splits long items (see above) for
+ * these windows and shape on the current device: 0 when it would not split
+ * (fp32, sink keys, enough work items already, or invalid arguments).  Queries
+ * the device's occupancy and builds the split work list on first use per shape
+ * (cached like the other work lists).
+ */
+size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                                   int d, aah_dtype dt);
 
 /*
  * Forward pass with the attention diagnostics of "Asymmetric Attention Heads"
@@ -302,6 +321,22 @@ aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* c
 aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
+
+/*
+ * Split forward work list (host only, no GPU): as aah_plan_fwd without sinks,
+ * but every item of more than chunk_tiles key tiles becomes items over
+ * consecutive near-equal sub-ranges of its tiles (the split launch of
+ * aah_attn_fwd).  slots[i] is item i's partial-result slot, -1 for an item
+ * that writes its own rows; merges holds one record per split item:
+ * (bh, q_tile_index, first slot, number of chunks).  Writes up to `capacity`
+ * items and slots and up to `merge_capacity` records, stores the full counts
+ * in *n_items and *n_merges, and returns AAH_ERR_INVALID_ARG if either
+ * capacity is too small (after setting both counts).
+ */
+aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
+                              int n_queues, int chunk_tiles, aah_work_item* items, int32_t* slots,
+                              int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,
+                              int64_t* n_merges);
 
 aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,

@@ -58,6 +58,54 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
     return O, L
 
 
+def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile, kv_tile):
+    """The split forward: each item runs its own key tiles; an item with a slot leaves (m, l, acc) of its
+    rows there, and every merge record (bh, q tile, first slot, chunks) combines its chunks as
+    M = max m_c, L = sum exp(m_c - M) l_c, O = sum exp(m_c - M) acc_c / L, LSE = M + ln L."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, H, T, d = q.shape
+    O = np.full((B, H, T, d), np.nan)
+    L = np.full((B, H, T), np.nan)
+    parts = {}
+    for (bh, qt, lo, hi), slot in zip(items, slots):
+        if bh < 0:
+            continue
+        b, h = divmod(int(bh), H)
+        g = h // (H // k.shape[1])
+        W = min(int(windows[h]), T)
+        rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        acc = np.zeros((len(rows), d))
+        for kt in range(lo, hi):
+            keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
+            s = np.where(_visible(rows, keys, W, 0), scale * q[b, h, rows] @ k[b, g, keys].T, -np.inf)
+            m_new = np.maximum(m, s.max(axis=1))
+            m_use = np.where(np.isneginf(m_new), 0.0, m_new)
+            alpha = np.exp(m - m_use)
+            p = np.exp(s - m_use[:, None])
+            l = l * alpha + p.sum(axis=1)
+            acc = acc * alpha[:, None] + p @ v[b, g, keys]
+            m = m_new
+        if slot < 0:
+            O[b, h, rows] = acc / l[:, None]
+            L[b, h, rows] = m + np.log(l)
+        else:
+            assert int(slot) not in parts, "slot written twice"
+            parts[int(slot)] = (m, l, acc)
+    for bh, qt, first, n in merges:
+        b, h = divmod(int(bh), H)
+        rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
+        ms = np.stack([parts[first + c][0] for c in range(n)])
+        M = ms.max(axis=0)
+        w = np.exp(ms - M)  # 0 for a chunk a row did not see (m = -inf)
+        l = sum(w[c] * parts[first + c][1] for c in range(n))
+        acc = sum(w[c][:, None] * parts[first + c][2] for c in range(n))
+        O[b, h, rows] = acc / l[:, None]
+        L[b, h, rows] = M + np.log(l)
+    return O, L
+
+
 def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None):
     """Key-stationary backward over the backward work list: dK, dV per key tile of a key/value head
     (summed over its query heads), dQ accumulated from every key tile."""

@@ -1,0 +1,106 @@
+"""Split forward launches (long items' key ranges in chunks, merged afterwards) against the fp64 oracle.
+
+A bf16 forward with fewer work items than the device holds workgroups splits every item longer than
+the chunk length when the caller passes aah_attn_fwd_workspace_size bytes of workspace (the binding
+does).  Tolerances as for every bf16 forward (tests/test_gpu_parity.py): O within max(1e-2, 2^-8 |O|),
+LSE within 4e-3; each chunk's weights are rounded against the chunk's own reference, which the same
+bounds cover.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import head_causal_local_amd as aah
+import oracle
+import synth
+from head_causal_local_amd._lib import lib
+
+pytestmark = pytest.mark.gpu
+
+O_TOL_BF16 = 1e-2
+LSE_TOL_BF16 = 4e-3
+BF16, F32 = 0, 1
+
+
+def _require_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("these tests need a HIP device")
+
+
+def _dev(wl, key):
+    return torch.from_numpy(wl.bits[key].view(np.int16)).view(torch.bfloat16).to("cuda")
+
+
+def _ws_bytes(windows, B, H, T, d, sinks=None, dt=BF16, H_kv=None):
+    w = np.ascontiguousarray(windows, dtype=np.int32)
+    P = ctypes.POINTER(ctypes.c_int32)
+    sp = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.int32).ctypes.data_as(P)
+    return lib().aah_attn_fwd_workspace_size(w.ctypes.data_as(P), sp, B, H, H if H_kv is None else H_kv, T, d, dt)
+
+
+def _fwd_unsplit(q, k, v, windows, scale):
+    """The forward with no workspace: one workgroup per item, every item writes its own rows."""
+    B, H, T, d = q.shape
+    w = np.ascontiguousarray(windows, dtype=np.int32)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, B, H, H, T, d, BF16,
+                            float(scale), o.data_ptr(), lse.data_ptr(), None, 0,
+                            torch.cuda.current_stream().cuda_stream)
+    aah.check(st)
+    return o, lse
+
+
+def _check_full(wl, o, lse):
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale)
+    got = o.float().cpu().numpy().astype(np.float64)
+    bound = np.maximum(O_TOL_BF16, np.abs(O) * 2.0 ** -8)
+    assert (np.abs(got - O) - bound).max() <= 0, f"max |dO| {np.abs(got - O).max():.3e}"
+    assert np.abs(lse.cpu().numpy() - L).max() < LSE_TOL_BF16
+
+
+def test_split_applies_only_where_it_should():
+    """Workspace (and so a split launch) only for bf16 without sinks and with too few items."""
+    _require_gpu()
+    single = synth.make_workload(1)
+    assert _ws_bytes(single.windows, 1, 16, 4096, 64) > 0          # 512 items: splits
+    assert _ws_bytes([4096] * 32, 4, 32, 4096, 64) == 0            # 4096 items fill the device
+    assert _ws_bytes([4096] * 16, 1, 16, 4096, 64, dt=F32) == 0   # the fp32 path never splits
+    assert _ws_bytes([256] * 4, 1, 4, 4096, 64, sinks=[128] * 4) == 0
+    assert _ws_bytes([1024] * 4, 1, 4, 1024, 64) == 0              # no item longer than the shortest chunk
+    assert _ws_bytes([0] * 4, 1, 4, 512, 64) == 0                  # invalid window: no workspace
+
+
+@pytest.mark.parametrize("B,H,T,d,windows", [
+    (1, 1, 4096, 64, [4096]),            # 64-tile items: several chunks each
+    (1, 2, 2000, 64, [2000, 300]),        # ragged tail, mixed split / unsplit items
+    (1, 3, 1777, 32, [1777, 64, 1]),
+    (2, 2, 2048, 128, [2048, 100]),
+    (1, 4, 3000, 64, [1, 17, 2999, 5000]),
+])
+def test_split_forward_matches_oracle(B, H, T, d, windows):
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=B * 131 + H * 7 + T + d, backward=False)
+    assert _ws_bytes(wl.windows, B, H, T, d) > 0  # every case has items longer than the chunk
+    o, lse = aah.attn_fwd(_dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v"), wl.windows, wl.scale)
+    torch.cuda.synchronize()
+    _check_full(wl, o, lse)
+
+
+def test_split_close_to_unsplit_and_deterministic():
+    """The single-layer workload (B=1 H=16 T=4096): split and one-workgroup-per-item launches agree within
+    the bf16 bounds, and repeated split launches are bitwise equal."""
+    _require_gpu()
+    wl = synth.make_workload(1)
+    q, k, v = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v")
+    o1, l1 = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+    o2, l2 = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+    ou, lu = _fwd_unsplit(q, k, v, wl.windows, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    a, b = o1.float().cpu().numpy(), ou.float().cpu().numpy()
+    assert (np.abs(a - b) - np.maximum(2 * O_TOL_BF16, np.abs(b) * 2.0 ** -7)).max() <= 0
+    assert (l1 - lu).abs().max().item() < 2 * LSE_TOL_BF16
