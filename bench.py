@@ -403,7 +403,10 @@ def main():
     # <d, sinks, grouped heads> dK/dV.
     sink = "true" if wl.sinks is not None and int(np.max(wl.sinks)) > 0 else "false"
     gqa = "true" if H_kv != H else "false"
-    kernels = [(f"fwd_bf16_kernel<{d}, {sink}, false>", float(fwd_ms.mean()), f_fwd)]
+    fname = f"fwd_bf16_kernel<{d}, {sink}, false>"
+    if aah.fwd_workspace_size(wl.windows, B, H, T, d, sinks=wl.sinks, H_kv=H_kv) > 0:
+        fname += f" + fwd_merge_kernel<{d}>"  # split launch: the forward's events hold both kernels
+    kernels = [(fname, float(fwd_ms.mean()), f_fwd)]
     if with_bwd:
         kernels += [(f"bwd_dkdv_kernel<{d}, {sink}, {gqa}>", float(dkdv_ms.mean()), 8 * d * pairs),
                     (f"bwd_dq_kernel<{d}, {sink}>", float(dq_ms.mean()), 6 * d * pairs)]

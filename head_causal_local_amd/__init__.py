@@ -402,6 +402,15 @@ def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_til
     return _plan(lib().aah_plan_bwd, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv)
 
 
+def fwd_workspace_size(windows: Sequence[int], B: int, H: int, T: int, d: int, dtype: str = "bf16",
+                       sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None) -> int:
+    """Workspace bytes with which the forward splits long items on the current device (0: it does not)."""
+    w = _windows_arg(windows)
+    sk = _sinks_arg(sinks, H)
+    code = AAH_BF16 if dtype == "bf16" else AAH_F32
+    return int(lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H if H_kv is None else H_kv, T, d, code))
+
+
 def plan_fwd_split(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, chunk_tiles: int,
                    n_queues: int = 8, H_kv: Optional[int] = None):
     """Split forward work list: (items int32 [n, 4] as plan_fwd, slots int32 [n] (-1: the item writes its own
