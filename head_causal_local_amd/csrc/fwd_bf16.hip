@@ -63,6 +63,12 @@
 // (when m moves by -delta, a becomes alpha (a + delta l)).  Using the rounded
 // weights for both sums makes the result the cross entropy of the normalised
 // rounded weights against the exact ones, within 2^-7 H + 2^-8 of the exact H.
+//
+// Split launches (few work items for the device): an item may be one chunk of
+// a longer item's key range.  Such a chunk ends by leaving, per row, its
+// unnormalised accumulator, its reference m and its row sum in a slot of the
+// caller's workspace; fwd_merge_kernel then rescales the chunks of each split
+// item to a common reference and writes O and LSE.
 #include <cmath>
 
 #include "device_common.hpp"
