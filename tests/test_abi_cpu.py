@@ -118,6 +118,17 @@ def test_workspace_sizes():
     assert _lib.lib().aah_attn_workspace_size(1, 1, 1, 48, 0, 1) == 0
 
 
+def test_fwd_split_workspace_size_never_for_fp32_sinks_or_bad_arguments():
+    # The split forward's workspace: 0 for fp32, for heads with sinks and for invalid arguments, on any
+    # machine (a positive size also needs the device's occupancy, so it is tested on the GPU).
+    assert aah.fwd_workspace_size([4096] * 16, 1, 16, 4096, 64, dtype="f32") == 0
+    assert aah.fwd_workspace_size([256] * 4, 1, 4, 4096, 64, sinks=[128] * 4) == 0
+    assert aah.fwd_workspace_size([0, 4096], 1, 2, 4096, 64) == 0
+    assert aah.fwd_workspace_size([4096] * 2, 1, 2, 4096, 48) == 0
+    assert aah.fwd_workspace_size([4096] * 3, 1, 3, 4096, 64, H_kv=2) == 0
+    assert _lib.lib().aah_attn_fwd_workspace_size(None, None, 1, 2, 2, 4096, 64, 0) == 0
+
+
 def test_bwd_step_validation():
     lib = _lib.lib()
     w = np.array([4, 0], dtype=np.int32)
