@@ -104,3 +104,39 @@ def test_split_close_to_unsplit_and_deterministic():
     a, b = o1.float().cpu().numpy(), ou.float().cpu().numpy()
     assert (np.abs(a - b) - np.maximum(2 * O_TOL_BF16, np.abs(b) * 2.0 ** -7)).max() <= 0
     assert (l1 - lu).abs().max().item() < 2 * LSE_TOL_BF16
+
+
+def test_split_concurrent_streams_and_misaligned_workspace():
+    """Two split forwards on two streams (each with its own workspace) equal the sequential results; a
+    workspace that is large enough but not 256-byte aligned is refused before anything is written."""
+    _require_gpu()
+    wls = [synth.random_workload(1, 2, 4096, 64, [4096, 3000], dtype="bf16", seed=s, backward=False)
+           for s in (5, 6)]
+    ins = [tuple(_dev(wl, key) for key in ("q", "k", "v")) for wl in wls]
+    seq = [aah.attn_fwd(*x, wl.windows, wl.scale) for x, wl in zip(ins, wls)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for st in streams:
+        st.wait_stream(torch.cuda.current_stream())
+    par = []
+    for st, x, wl in zip(streams, ins, wls):
+        with torch.cuda.stream(st):
+            par.append(aah.attn_fwd(*x, wl.windows, wl.scale))
+    torch.cuda.synchronize()
+    for (o1, l1), (o2, l2) in zip(seq, par):
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+    wl, (q, k, v) = wls[0], ins[0]
+    need = _ws_bytes(wl.windows, 1, 2, 4096, 64)
+    assert need > 0
+    ws = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+    o = torch.full_like(q, 7.0)
+    lse = torch.full((1, 2, 4096), 7.0, dtype=torch.float32, device="cuda")
+    w = np.ascontiguousarray(wl.windows, dtype=np.int32)
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 1, 2, 2, 4096, 64, BF16,
+                            float(wl.scale), o.data_ptr(), lse.data_ptr(), ws.data_ptr() + 16, need,
+                            torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 3  # AAH_ERR_WORKSPACE
+    assert bool((o.float() == 7.0).all()) and bool((lse == 7.0).all())
