@@ -232,7 +232,11 @@ def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=Non
     code = _dtype_code(q)
     need = int(lib().aah_attn_workspace_size(B, H, T, d, code, 1))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+        # With few work items the library splits long ones when given room for their partial results.
+        sk = _sinks_arg(sinks, H)
+        split = int(lib().aah_attn_bwd_split_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, T, d,
+                                                             code))
+        workspace = torch.empty(max(need, split, 1), dtype=torch.uint8, device=q.device)
     sk = _sinks_arg(sinks, H)
     st = lib().aah_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
                             _wptr(w), _sptr(sk), B, H, H_kv, T, d, code, float(scale), dq.data_ptr(), dk.data_ptr(),

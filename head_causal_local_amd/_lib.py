@@ -19,12 +19,12 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
     "aah_attn_workspace_size", "aah_attn_fwd_workspace_size", "aah_tile_shape", "aah_plan_fwd", "aah_plan_bwd",
-    "aah_plan_fwd_split", "aah_window_stats",
+    "aah_plan_fwd_split", "aah_attn_bwd_split_workspace_size", "aah_window_stats",
     "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
     "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode", "aah_attn_fwd_diag",
     "aah_head_features_workspace_size", "aah_head_features",
@@ -85,6 +85,8 @@ def _declare(lib):
     lib.aah_attn_bwd_dq.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int,
                                     c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_size_t,
                                     c_void_p]
+    lib.aah_attn_bwd_split_workspace_size.restype = c_size_t
+    lib.aah_attn_bwd_split_workspace_size.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_attn_fwd_workspace_size.restype = c_size_t
     lib.aah_attn_fwd_workspace_size.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_attn_workspace_size.restype = c_size_t

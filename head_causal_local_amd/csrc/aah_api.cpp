@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <tuple>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -270,14 +271,15 @@ size_t split_workspace(int n_slots, int d) {
 }
 
 // Split plan of a bf16 forward without sinks with chunk length L (> 0), uploaded once per key.
+// kind 0: query-stationary items (forward, dQ); kind 1: key-stationary items (dK/dV, H_kv = H, no sinks).
 aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T, int d, int L,
-                          SplitDevicePlan* out) {
+                          SplitDevicePlan* out, int kind = 0) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   std::vector<int32_t> win(H);
   for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
-  std::vector<int64_t> key = {dev, B, H, H_kv, T, d, L};
+  std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, d, L};
   key.insert(key.end(), win.begin(), win.end());
   std::lock_guard<std::mutex> lock(g_mu);
   auto found = g_split_cache.find(key);
@@ -285,8 +287,9 @@ aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T,
     *out = found->second;
     return AAH_OK;
   }
-  const aah::SplitPlan sp = aah::plan_forward_split(windows, B, H, H_kv, T, aah::kFwdBf16RowTile,
-                                                    aah::kFwdBf16ColTile, kQueues, L);
+  const aah::SplitPlan sp =
+      kind == 0 ? aah::plan_forward_split(windows, B, H, H_kv, T, aah::kFwdBf16RowTile, aah::kFwdBf16ColTile, kQueues, L)
+                : aah::plan_backward_split(windows, B, H, T, aah::kBwdBf16ColTile, aah::kBwdBf16RowTile, kQueues, L);
   SplitDevicePlan p;
   p.n_items = static_cast<int>(sp.items.size());
   p.n_merges = static_cast<int>(sp.merges.size());
@@ -316,6 +319,80 @@ aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T,
   g_split_cache.emplace(std::move(key), p);
   *out = p;
   return AAH_OK;
+}
+
+// Split backward: the same rule per kernel, with that kernel's residency and items (dQ: the forward's
+// query items; dK/dV: key items over their query-tile ranges).
+int resident_bwd(bool dkdv, int d) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  static std::mutex mu;
+  static std::map<std::tuple<int, int, int>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(dev, d, dkdv ? 1 : 0);
+  auto found = cache.find(key);
+  if (found != cache.end()) return found->second;
+  const int n = dkdv ? aah::bwd_dkdv_resident(d) : aah::bwd_dq_resident(d);
+  if (n > 0) cache.emplace(key, n);
+  return n;
+}
+
+int chunk_len(const std::vector<int>& tiles, int resident) {
+  if (resident <= 0 || static_cast<int64_t>(tiles.size()) >= resident) return 0;
+  int64_t total = 0;
+  int longest = 0;
+  for (int t : tiles) {
+    total += t;
+    longest = std::max(longest, t);
+  }
+  const int L = static_cast<int>(std::max<int64_t>(kMinChunkTiles, (total + resident - 1) / resident));
+  return longest > L ? L : 0;
+}
+
+// Streamed tiles of every dQ item (query tile, key tiles) or dK/dV item (key tile, query tiles), no sinks.
+std::vector<int> bwd_item_tiles(bool dkdv, const int32_t* windows, int B, int H, int T) {
+  std::vector<int> tiles;
+  const int rt = dkdv ? aah::kBwdBf16RowTile : aah::kFwdBf16RowTile;
+  const int ct = dkdv ? aah::kBwdBf16ColTile : aah::kFwdBf16ColTile;
+  const int n_rt = (T + rt - 1) / rt;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int W = aah::effective_window(windows[h], T);
+      for (int t = 0; t < n_rt; ++t) {
+        const int r0 = t * rt, r1 = std::min(T, r0 + rt);
+        if (dkdv) {
+          int lo = 0, hi = 0;
+          aah::query_range(r0, r1, W, 0, T, ct, &lo, &hi);
+          tiles.push_back(hi - lo);
+        } else {
+          tiles.push_back((r1 - 1) / ct + 1 - std::max(0, r0 - W + 1) / ct);
+        }
+      }
+    }
+  return tiles;
+}
+
+struct BwdSplitLayout {
+  SplitDevicePlan q, k;  // dQ and dK/dV split plans (n_slots = 0 when that kernel does not split)
+  int q_L = 0, k_L = 0;
+  size_t q_off = 0, k_off = 0, total = 0;  // byte offsets of the partials in the workspace, and its size
+};
+
+// Layout of a split backward's workspace: [nl2 | nD | dQ partials | dK/dV partials].  Returns false when
+// splitting does not apply (dtype, grouped heads, sinks, enough items, or a failed plan upload).
+bool bwd_split_layout(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
+                      aah_dtype dt, BwdSplitLayout* lay) {
+  if (dt != AAH_BF16 || H_kv != H || any_sink(windows, sinks, H, T)) return false;
+  lay->q_L = chunk_len(bwd_item_tiles(false, windows, B, H, T), resident_bwd(false, d));
+  lay->k_L = chunk_len(bwd_item_tiles(true, windows, B, H, T), resident_bwd(true, d));
+  if (lay->q_L == 0 && lay->k_L == 0) return false;
+  if (lay->q_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->q_L, &lay->q, 0) != AAH_OK) return false;
+  if (lay->k_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->k_L, &lay->k, 1) != AAH_OK) return false;
+  const size_t rows = static_cast<size_t>(aah::kBwdBf16RowTile) * d * sizeof(float);
+  lay->q_off = 2 * round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256);
+  lay->k_off = lay->q_off + round_up(static_cast<size_t>(lay->q_L > 0 ? lay->q.n_slots : 0) * rows, 256);
+  lay->total = lay->k_off + round_up(static_cast<size_t>(lay->k_L > 0 ? lay->k.n_slots : 0) * 2 * rows, 256);
+  return true;
 }
 
 // Workspace of the backward: nl2 = -lse log2(e) and nD = -D, fp32 [B,H,T]
@@ -529,6 +606,14 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
   return split_workspace(sp.n_slots, d);
 }
 
+size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                         int T, int d, aah_dtype dt) {
+  if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
+  g_detail.clear();
+  BwdSplitLayout lay;
+  return bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) ? lay.total : 0;
+}
+
 aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* col_tile) {
   if (row_tile == nullptr || col_tile == nullptr) return fail(AAH_ERR_INVALID_ARG, "NULL output pointer");
   if (dt != AAH_BF16 && dt != AAH_F32) return fail(AAH_ERR_UNSUPPORTED, "unknown dtype %d", static_cast<int>(dt));
@@ -683,6 +768,15 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   const float* nd = ws_nd(workspace, B, H, T);
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
+  BwdSplitLayout lay;
+  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) && lay.k_L > 0 && workspace_bytes >= lay.total) {
+    const aah::BwdSplit split{lay.k.slots, lay.k.merges, lay.k.n_merges,
+                              reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + lay.k_off)};
+    const hipError_t e = aah::launch_bwd_dkdv_bf16_split(q, k, v, dout, nl2, nd, dk, dv, lay.k.items, lay.k.n_items,
+                                                         lay.k.win, s, split, st);
+    if (e != hipSuccess) return hip_fail(e, "split dK/dV launch");
+    return AAH_OK;
+  }
   DevicePlan plan;
   AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   hipError_t e;
@@ -719,6 +813,15 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   float* nd = const_cast<float*>(ws_nd(workspace, B, H, T));
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
+  BwdSplitLayout lay;
+  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) && lay.q_L > 0 && workspace_bytes >= lay.total) {
+    const aah::BwdSplit split{lay.q.slots, lay.q.merges, lay.q.n_merges,
+                              reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.q_off)};
+    const hipError_t e = aah::launch_bwd_dq_bf16_split(q, k, v, o, dout, lse, nl2, nd, dq, lay.q.items,
+                                                       lay.q.n_items, lay.q.win, s, split, st);
+    if (e != hipSuccess) return hip_fail(e, "split dQ launch");
+    return AAH_OK;
+  }
   DevicePlan plan;
   AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
   hipError_t e;

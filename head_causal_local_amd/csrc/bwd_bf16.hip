@@ -164,7 +164,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
                      const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
-                     int T, float scale) {
+                     int T, float scale, const int32_t* __restrict__ slots, float* __restrict__ part) {
   using C = Cfg<D>;
   // Three-stage ring; stage = {Q tile, dO tile, nl2 row, nD row}.
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
@@ -396,6 +396,21 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   }
 
   if (key >= T) return;
+  if (slots != nullptr && slots[blockIdx.x] >= 0) {
+    // A chunk of a split item: its fp32 dK (before the softmax scale) and dV sums over its query tiles.
+    const size_t prow = static_cast<size_t>(slots[blockIdx.x]) * 2 * kStat + 32 * wave + ln;
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int col = 32 * b + 8 * i + 4 * hl;
+        *reinterpret_cast<f32x4*>(part + prow * D + col) = f32x4{dk[b][4 * i], dk[b][4 * i + 1], dk[b][4 * i + 2],
+                                                                 dk[b][4 * i + 3]};
+        *reinterpret_cast<f32x4*>(part + (prow + kStat) * D + col) =
+            f32x4{dv[b][4 * i], dv[b][4 * i + 1], dv[b][4 * i + 2], dv[b][4 * i + 3]};
+      }
+    return;
+  }
   bf16* dkrow = dK + base + static_cast<size_t>(key) * D;
   bf16* dvrow = dV + base + static_cast<size_t>(key) * D;
   // dK^T / dV^T block b, register r: dim 32 b + 8 (r/4) + 4 hl + r%4 of this lane's key.
@@ -418,7 +433,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    const bf16* __restrict__ O, const bf16* __restrict__ dO, const float* __restrict__ LSE,
                    float* __restrict__ NL2, float* __restrict__ ND, bf16* __restrict__ dQ,
                    const WorkItem* __restrict__ items, const int32_t* __restrict__ win_eff,
-                   const int32_t* __restrict__ sink_eff, int H, int H_kv, int T, float scale) {
+                   const int32_t* __restrict__ sink_eff, int H, int H_kv, int T, float scale,
+                   const int32_t* __restrict__ slots, float* __restrict__ part) {
   using C = Cfg<D>;
   constexpr int kStage = 2 * C::kTileBytes;  // {K tile, V tile}
   // Three stages (copies two steps ahead) up to d = 64; at d = 128 a stage is 32 KiB and two stages let
@@ -597,6 +613,17 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     NL2[rbase + qi] = cl;
     ND[rbase + qi] = nD;
   }
+  if (slots != nullptr && slots[blockIdx.x] >= 0) {
+    // A chunk of a split item: its fp32 dQ sum (before the softmax scale) over its key tiles.
+    float* prow = part + (static_cast<size_t>(slots[blockIdx.x]) * kStat + q0w - it.tile * kStat + ln) * D;
+#pragma unroll
+    for (int b = 0; b < C::kBlocks; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(prow + 32 * b + 8 * i + 4 * hl) =
+            f32x4{acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]};
+    return;
+  }
   bf16* dqrow = dQ + base + static_cast<size_t>(qi) * D;
   // dQ^T block b, register r: dim 32 b + 8 (r/4) + 4 hl + r%4 of this lane's query.
 #pragma unroll
@@ -607,25 +634,53 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
                    acc[b][4 * i + 2] * scale, acc[b][4 * i + 3] * scale);
 }
 
+// Sums the chunks of each split item (record {bh, tile, first slot, chunks}):
+// out0 = f0 * sum_c part[c][0] and, for dK / dV, out1 = sum_c part[c][1], each
+// [128 rows][D] in fp32, rounded to bf16.  D / 4 threads per row, four dims each;
+// chunks are added in order, so the result is deterministic.
+template <int D, int NOUT>
+__global__ __launch_bounds__(256) void bwd_merge_kernel(const WorkItem* __restrict__ merges,
+                                                        const float* __restrict__ part, bf16* __restrict__ out0,
+                                                        bf16* __restrict__ out1, float f0, int T) {
+  constexpr int kPerRow = D / 4;
+  constexpr int kRowsPerWg = 256 / kPerRow;
+  const WorkItem mg = merges[blockIdx.x];
+  const int r = blockIdx.y * kRowsPerWg + static_cast<int>(threadIdx.x) / kPerRow;
+  const int dq = (static_cast<int>(threadIdx.x) % kPerRow) * 4;
+  const int row = mg.tile * kStat + r;
+  if (r >= kStat || row >= T) return;
+  f32x4 a0 = f32x4{}, a1 = f32x4{};
+  for (int ch = 0; ch < mg.hi; ++ch) {
+    const size_t base = (static_cast<size_t>(mg.lo + ch) * NOUT * kStat + r) * D + dq;
+    a0 += *reinterpret_cast<const f32x4*>(part + base);
+    if constexpr (NOUT == 2) a1 += *reinterpret_cast<const f32x4*>(part + base + static_cast<size_t>(kStat) * D);
+  }
+  const size_t o = (static_cast<size_t>(mg.bh) * T + row) * D + dq;
+  store_bf16x4(out0 + o, a0[0] * f0, a0[1] * f0, a0[2] * f0, a0[3] * f0);
+  if constexpr (NOUT == 2) store_bf16x4(out1 + o, a1[0], a1[1], a1[2], a1[3]);
+}
+
 template <int D, bool SINK, bool GQA>
 hipError_t dkdv_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                   void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
-                  const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+                  const int32_t* sink_eff, const AttnShape& s, hipStream_t stream, const BwdSplit* split = nullptr) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, SINK, GQA>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<const bf16*>(dout), nl2, nd, static_cast<bf16*>(dk), static_cast<bf16*>(dv), items,
-                     win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale);
+                     win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale, split != nullptr ? split->slots : nullptr,
+                     split != nullptr ? split->part : nullptr);
   return hipGetLastError();
 }
 
 template <int D, bool SINK>
 hipError_t dq_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                 float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                const int32_t* sink_eff, const AttnShape& s, hipStream_t stream) {
+                const int32_t* sink_eff, const AttnShape& s, hipStream_t stream, const BwdSplit* split = nullptr) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, SINK>), dim3(n_items), dim3(kThreads), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, nl2, nd,
-                     static_cast<bf16*>(dq), items, win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale);
+                     static_cast<bf16*>(dq), items, win_eff, sink_eff, s.H, s.H_kv, s.T, s.scale,
+                     split != nullptr ? split->slots : nullptr, split != nullptr ? split->part : nullptr);
   return hipGetLastError();
 }
 
@@ -652,7 +707,84 @@ hipError_t dq_s(const void* q, const void* k, const void* v, const void* o, cons
              : dq_d<D, false>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream);
 }
 
+template <int D>
+hipError_t dkdv_split_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
+                        void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
+                        const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
+  const hipError_t e =
+      dkdv_d<D, false, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, nullptr, s, stream, &split);
+  if (e != hipSuccess || split.n_merges == 0) return e;
+  hipLaunchKernelGGL((bwd_merge_kernel<D, 2>), dim3(split.n_merges, kStat / (256 / (D / 4))), dim3(256), 0, stream,
+                     split.merges, split.part, static_cast<bf16*>(dk), static_cast<bf16*>(dv), s.scale, s.T);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dq_split_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                      float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
+                      const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
+  const hipError_t e =
+      dq_d<D, false>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, nullptr, s, stream, &split);
+  if (e != hipSuccess || split.n_merges == 0) return e;
+  hipLaunchKernelGGL((bwd_merge_kernel<D, 1>), dim3(split.n_merges, kStat / (256 / (D / 4))), dim3(256), 0, stream,
+                     split.merges, split.part, static_cast<bf16*>(dq), nullptr, s.scale, s.T);
+  return hipGetLastError();
+}
+
+template <typename Fn>
+int resident_of(Fn fn) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(fn), kThreads, 0) !=
+      hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
+
 }  // namespace
+
+hipError_t launch_bwd_dkdv_bf16_split(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
+                                      const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
+                                      const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
+                                      hipStream_t stream) {
+  switch (s.d) {
+    case 32: return dkdv_split_d<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
+    case 64: return dkdv_split_d<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
+    case 128: return dkdv_split_d<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_dq_bf16_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                    const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items,
+                                    int n_items, const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
+                                    hipStream_t stream) {
+  switch (s.d) {
+    case 32: return dq_split_d<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
+    case 64: return dq_split_d<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
+    case 128: return dq_split_d<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int bwd_dq_resident(int d) {
+  switch (d) {
+    case 32: return resident_of(&bwd_dq_kernel<32, false>);
+    case 64: return resident_of(&bwd_dq_kernel<64, false>);
+    case 128: return resident_of(&bwd_dq_kernel<128, false>);
+    default: return 0;
+  }
+}
+
+int bwd_dkdv_resident(int d) {
+  switch (d) {
+    case 32: return resident_of(&bwd_dkdv_kernel<32, false, false>);
+    case 64: return resident_of(&bwd_dkdv_kernel<64, false, false>);
+    case 128: return resident_of(&bwd_dkdv_kernel<128, false, false>);
+    default: return 0;
+  }
+}
 
 hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                 const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,

@@ -145,6 +145,39 @@ SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int
   return plan;
 }
 
+SplitPlan plan_backward_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                              int chunk_tiles) {
+  const int n_kt = ceil_div(T, kv_tile);
+  SplitPlan plan;
+  std::vector<std::vector<Planned>> per_head(static_cast<size_t>(B) * H);
+  for (int b = 0; b < B; ++b) {
+    for (int h = 0; h < H; ++h) {
+      const int32_t bh = b * H + h;
+      auto& list = per_head[static_cast<size_t>(bh)];
+      const int W = effective_window(windows[h], T);
+      for (int kt = 0; kt < n_kt; ++kt) {
+        const int k0 = kt * kv_tile, k1 = std::min(T, k0 + kv_tile);
+        int lo = 0, hi = 0;
+        query_range(k0, k1, W, 0, T, q_tile, &lo, &hi);
+        const int n = hi - lo;
+        if (chunk_tiles < 1 || n <= chunk_tiles) {
+          list.push_back(Planned{WorkItem{bh, kt, lo, hi}, n, bh});
+          continue;
+        }
+        const int n_chunks = ceil_div(n, chunk_tiles);
+        plan.merges.push_back(WorkItem{bh, kt, plan.n_slots, n_chunks});
+        for (int c = 0; c < n_chunks; ++c) {
+          const int c_lo = lo + c * (n / n_chunks) + std::min(c, n % n_chunks);
+          const int c_hi = c_lo + n / n_chunks + (c < n % n_chunks ? 1 : 0);
+          list.push_back(Planned{WorkItem{bh, kt, c_lo, c_hi}, c_hi - c_lo, bh, plan.n_slots++});
+        }
+      }
+    }
+  }
+  plan.items = interleave(per_head, n_queues, &plan.slot);
+  return plan;
+}
+
 std::vector<WorkItem> plan_backward(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                     int q_tile, int kv_tile, int n_queues) {
   const int n_kt = ceil_div(T, kv_tile);

@@ -76,6 +76,13 @@ struct SplitPlan {
 SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
                              int n_queues, int chunk_tiles);
 
+// Backward (key-stationary) items split the same way along their query-tile
+// ranges, for one key/value head per query head and no sink keys: every item
+// of more than chunk_tiles query tiles becomes chunks with slots, and a merge
+// record {bh, key tile, first slot, chunks} per split item.
+SplitPlan plan_backward_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                              int chunk_tiles);
+
 // Backward items: one per (b, key/value head g, key tile); [lo, hi) spans the
 // query tiles that see the keys in any of the group's query heads (each head's
 // own range is query_range, starting at the same lo).

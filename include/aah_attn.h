@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 7
+#define AAH_ABI_VERSION 8
 
 typedef enum {
   AAH_OK = 0,
@@ -134,6 +134,19 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
  */
 size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                                    int d, aah_dtype dt);
+
+/*
+ * Workspace bytes with which the backward (aah_attn_bwd, and each of its two
+ * steps) splits long items as the forward does, for these windows and shape
+ * on the current device; 0 when it would not (fp32, sink keys, grouped
+ * key/value heads, enough work items, invalid arguments).  Such a workspace
+ * holds the usual rows first (so it also serves an unsplit call), then each
+ * split kernel's partial sums; a merge launch after each split kernel adds
+ * them in a fixed order (results stay deterministic, and agree with the
+ * unsplit launch within the bf16 bounds).
+ */
+size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                         int T, int d, aah_dtype dt);
 
 /*
  * Forward pass with the attention diagnostics of "Asymmetric Attention Heads"

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 7
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 8
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -127,6 +127,17 @@ def test_fwd_split_workspace_size_never_for_fp32_sinks_or_bad_arguments():
     assert aah.fwd_workspace_size([4096] * 2, 1, 2, 4096, 48) == 0
     assert aah.fwd_workspace_size([4096] * 3, 1, 3, 4096, 64, H_kv=2) == 0
     assert _lib.lib().aah_attn_fwd_workspace_size(None, None, 1, 2, 2, 4096, 64, 0) == 0
+    # and the split backward's: 0 for fp32, sinks, grouped heads and invalid arguments
+    P = ctypes.POINTER(ctypes.c_int32)
+    def bws(windows, H, H_kv, dt=0, sinks=None, d=64):
+        w = np.ascontiguousarray(windows, dtype=np.int32)
+        sp = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.int32).ctypes.data_as(P)
+        return _lib.lib().aah_attn_bwd_split_workspace_size(w.ctypes.data_as(P), sp, 1, H, H_kv, 4096, d, dt)
+    assert bws([4096] * 2, 2, 2, dt=1) == 0
+    assert bws([256] * 2, 2, 2, sinks=[128] * 2) == 0
+    assert bws([4096] * 4, 4, 2) == 0
+    assert bws([0, 4096], 2, 2) == 0
+    assert bws([4096] * 2, 2, 2, d=48) == 0
 
 
 def test_bwd_step_validation():
