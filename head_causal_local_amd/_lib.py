@@ -24,7 +24,7 @@ ABI_VERSION = 8
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
     "aah_attn_workspace_size", "aah_attn_fwd_workspace_size", "aah_tile_shape", "aah_plan_fwd", "aah_plan_bwd",
-    "aah_plan_fwd_split", "aah_attn_bwd_split_workspace_size", "aah_window_stats",
+    "aah_plan_fwd_split", "aah_plan_bwd_split", "aah_attn_bwd_split_workspace_size", "aah_window_stats",
     "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
     "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode", "aah_attn_fwd_diag",
     "aah_head_features_workspace_size", "aah_head_features",
@@ -100,6 +100,9 @@ def _declare(lib):
     lib.aah_plan_fwd_split.restype = c_int
     lib.aah_plan_fwd_split.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, P_i32,
                                        c_int64, P_i64, P_item, c_int64, P_i64]
+    lib.aah_plan_bwd_split.restype = c_int
+    lib.aah_plan_bwd_split.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, P_i32, c_int64,
+                                       P_i64, P_item, c_int64, P_i64]
     lib.aah_window_stats.restype = c_int
     lib.aah_window_stats.argtypes = [P_i32, P_i32, c_int, c_int, P_i64, P_double]
     lib.aah_cache_clear.restype = None

@@ -960,6 +960,39 @@ aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H,
   return AAH_OK;
 }
 
+namespace {
+// Copies a split plan to the caller's arrays (the capacities checked after the counts are stored).
+aah_status split_to_host(const aah::SplitPlan& sp, aah_work_item* items, int32_t* slots, int64_t capacity,
+                         int64_t* n_items, aah_work_item* merges, int64_t merge_capacity, int64_t* n_merges) {
+  *n_items = static_cast<int64_t>(sp.items.size());
+  *n_merges = static_cast<int64_t>(sp.merges.size());
+  if (capacity < *n_items || merge_capacity < *n_merges)
+    return fail(AAH_ERR_INVALID_ARG, "capacity %lld / %lld < %lld items / %lld merge records",
+                static_cast<long long>(capacity), static_cast<long long>(merge_capacity),
+                static_cast<long long>(*n_items), static_cast<long long>(*n_merges));
+  if ((*n_items > 0 && (items == nullptr || slots == nullptr)) || (*n_merges > 0 && merges == nullptr))
+    return fail(AAH_ERR_INVALID_ARG, "output array is NULL");
+  std::memcpy(items, sp.items.data(), sp.items.size() * sizeof(WorkItem));
+  std::memcpy(slots, sp.slot.data(), sp.slot.size() * sizeof(int32_t));
+  if (!sp.merges.empty()) std::memcpy(merges, sp.merges.data(), sp.merges.size() * sizeof(WorkItem));
+  return AAH_OK;
+}
+}  // namespace
+
+aah_status aah_plan_bwd_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                              int chunk_tiles, aah_work_item* items, int32_t* slots, int64_t capacity,
+                              int64_t* n_items, aah_work_item* merges, int64_t merge_capacity, int64_t* n_merges) {
+  g_detail.clear();
+  if (n_items == nullptr || n_merges == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items / n_merges is NULL");
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
+  if (q_tile < 1 || kv_tile < 1 || n_queues < 1 || chunk_tiles < 1)
+    return fail(AAH_ERR_INVALID_ARG, "tiles, n_queues and chunk_tiles must be >= 1");
+  AAH_TRY(check_windows(windows, nullptr, H));
+  return split_to_host(aah::plan_backward_split(windows, B, H, T, q_tile, kv_tile, n_queues, chunk_tiles), items,
+                       slots, capacity, n_items, merges, merge_capacity, n_merges);
+}
+
 aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
                               int n_queues, int chunk_tiles, aah_work_item* items, int32_t* slots,
                               int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,

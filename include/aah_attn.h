@@ -351,6 +351,17 @@ aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, in
                               int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,
                               int64_t* n_merges);
 
+/*
+ * Split backward (dK/dV) work list, host only: as aah_plan_bwd for one
+ * key/value head per query head and no sinks, with every key item of more
+ * than chunk_tiles query tiles cut into items over consecutive near-equal
+ * sub-ranges; slots and merge records (bh, key tile index, first slot,
+ * chunks) as for aah_plan_fwd_split.
+ */
+aah_status aah_plan_bwd_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
+                              int chunk_tiles, aah_work_item* items, int32_t* slots, int64_t capacity,
+                              int64_t* n_items, aah_work_item* merges, int64_t merge_capacity, int64_t* n_merges);
+
 aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,
                         aah_work_item* items, int64_t capacity, int64_t* n_items);

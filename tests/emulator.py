@@ -106,16 +106,17 @@ def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile,
     return O, L
 
 
-def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None):
+def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None, split=False):
     """Key-stationary backward over the backward work list: dK, dV per key tile of a key/value head
-    (summed over its query heads), dQ accumulated from every key tile."""
+    (summed over its query heads), dQ accumulated from every key tile.  split: the list may hold several
+    chunks of one key tile, each over its own query tiles [lo, hi); their dK, dV sums add up."""
     q, k, v, do, lse = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, lse))
     B, H, T, d = q.shape
     H_kv = k.shape[1]
     G = H // H_kv
     dq = np.zeros_like(q)
-    dk = np.full_like(k, np.nan)
-    dv = np.full_like(v, np.nan)
+    dk = np.zeros_like(k) if split else np.full_like(k, np.nan)
+    dv = np.zeros_like(v) if split else np.full_like(v, np.nan)
     for bh, kt, lo, hi in items:
         if bh < 0:
             continue
@@ -128,7 +129,7 @@ def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, s
             W = min(int(windows[h]), T)
             S = _eff_sink(sinks, h, T, W)
             last = T - 1 if k0 < S else min(T, k1 + W - 1) - 1
-            for qt in range(lo, last // q_tile + 1):
+            for qt in range(lo, min(hi, last // q_tile + 1) if split else last // q_tile + 1):
                 rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
                 s = scale * q[b, h, rows] @ k[b, g, keys].T
                 ok = _visible(rows, keys, W, S)
@@ -144,6 +145,10 @@ def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, s
                 dv_t += p.T @ do[b, h, rows]
                 dk_t += scale * ds.T @ q[b, h, rows]
                 dq[b, h, rows] += scale * ds @ k[b, g, keys]
-        dk[b, g, keys] = dk_t
-        dv[b, g, keys] = dv_t
+        if split:
+            dk[b, g, keys] += dk_t
+            dv[b, g, keys] += dv_t
+        else:
+            dk[b, g, keys] = dk_t
+            dv[b, g, keys] = dv_t
     return dq, dk, dv

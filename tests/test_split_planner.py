@@ -13,7 +13,7 @@ import pytest
 
 import head_causal_local_amd as aah
 import oracle
-from emulator import emulate_forward_split
+from emulator import emulate_backward, emulate_forward_split
 
 Q_TILE, KV_TILE = 128, 64
 
@@ -86,3 +86,51 @@ def test_split_plan_argument_errors():
         aah.plan_fwd_split([0, 4], 1, 2, 100, Q_TILE, KV_TILE, 4)
     with pytest.raises(aah.AahError):
         aah.plan_fwd_split([4, 4], 1, 2, 100, Q_TILE, KV_TILE, 0)
+
+
+BWD_CASES = [
+    # windows, B, H, T, chunk_tiles (query tiles of 64 per chunk at most)
+    ([4096, 512, 100], 1, 3, 4096, 24),
+    ([700, 1, 5000], 2, 3, 700, 2),
+    ([64, 300], 1, 2, 333, 1),
+]
+
+
+@pytest.mark.parametrize("windows,B,H,T,chunk", BWD_CASES)
+def test_backward_chunks_partition_items(windows, B, H, T, chunk):
+    base = aah.plan_bwd(windows, B, H, T, KV_TILE, Q_TILE)
+    items, slots, merges = aah.plan_bwd_split(windows, B, H, T, KV_TILE, Q_TILE, chunk)
+    pieces = defaultdict(list)
+    for i, (bh, kt, lo, hi) in enumerate(items):
+        if bh >= 0:
+            pieces[(bh, kt)].append((lo, hi, int(slots[i])))
+    records = {(int(bh), int(t)): (int(first), int(n)) for bh, t, first, n in merges}
+    used = []
+    for bh, kt, lo, hi in base:
+        if bh < 0:
+            continue
+        ps = sorted(pieces.pop((int(bh), int(kt))))
+        assert ps[0][0] == lo and ps[-1][1] == hi and all(a[1] == b[0] for a, b in zip(ps, ps[1:]))
+        n = hi - lo
+        if n <= chunk:
+            assert len(ps) == 1 and ps[0][2] == -1
+            continue
+        first, count = records.pop((int(bh), int(kt)))
+        assert count == math.ceil(n / chunk) == len(ps) and [p[2] for p in ps] == list(range(first, first + count))
+        used += [p[2] for p in ps]
+    assert not pieces and not records and sorted(used) == list(range(len(used)))
+
+
+@pytest.mark.parametrize("windows,B,H,T,chunk", BWD_CASES[1:])
+def test_backward_split_emulation_matches_oracle(windows, B, H, T, chunk):
+    rng = np.random.default_rng(T + 7 * chunk)
+    d = 8
+    q, k, v, do = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    scale = 1 / np.sqrt(d)
+    items, slots, merges = aah.plan_bwd_split(windows, B, H, T, KV_TILE, Q_TILE, chunk)
+    assert len(merges) > 0
+    _, lse = oracle.attn_fwd_ref(q, k, v, windows, scale)
+    dq, dk, dv = emulate_backward(items, q, k, v, do, lse, windows, scale, KV_TILE, Q_TILE, split=True)
+    rq, rk, rv = oracle.attn_bwd_ref(q, k, v, windows, scale, do)
+    for got, ref in ((dq, rq), (dk, rk), (dv, rv)):
+        assert np.abs(got - ref).max() < 1e-10
