@@ -173,7 +173,7 @@ def head_features_workspace_size(B: int, H: int, T: int, d: int) -> int:
 def head_features(q, k, v, windows, row_entropy=None, row_onorm=None, features_ema=None, alpha: float = 0.9,
                   init: bool = False, out=None, workspace=None, stream=None):
     """Per-head controller features x [H, 9] (float32) of q, k, v [B, H, T, d] and the diagnostic rows of
-    attn_fwd_diag (None: entropy and norm features are 0); if features_ema ([H, 9] float32) is given it is
+    the attn_fwd_diag call that ran with `windows` (None: entropy, norm and usage features are 0); if features_ema ([H, 9] float32) is given it is
     updated in place: init ? x : alpha * ema + (1 - alpha) * x.  Returns x."""
     import torch
     H_kv = _kv_heads(q, k, v)

@@ -640,6 +640,10 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
   if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  // An optional workspace, when given, follows the same alignment rule as every other workspace, whether or
+  // not this launch would split (checked here, before any HIP call).
+  if (workspace != nullptr && !aligned(workspace, 256))
+    return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
@@ -655,7 +659,6 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
     SplitDevicePlan sp;
     AAH_TRY(get_split_plan(windows, B, H, H_kv, T, d, L, &sp));
     if (workspace_bytes >= split_workspace(sp.n_slots, d)) {
-      if (!aligned(workspace, 256)) return fail(AAH_ERR_WORKSPACE, "workspace is not 256-byte aligned");
       float* part_acc = static_cast<float*>(workspace);
       float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_acc_bytes(sp.n_slots, d));
       const aah::FwdSplit split{sp.slots, sp.merges, sp.n_merges, part_acc, part_ml};
@@ -736,7 +739,7 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
   if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
   if (static_cast<int64_t>(B) * H * aah::feature_chunks(T, d) > INT32_MAX)
     return fail(AAH_ERR_UNSUPPORTED, "too many statistics workgroups");
-  // The effective windows (usage = min(W, T) / T) come from the cached forward work list's table.
+  // The effective windows (usage = min(W, T) / T, with diagnostic rows) come from the cached forward work list's table.
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
@@ -750,7 +753,7 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout, const int32_t* windows,
                              const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
-                             void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                             void* dk, void* dv, void* workspace, size_t workspace_bytes,
                              aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
@@ -771,7 +774,7 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   BwdSplitLayout lay;
   if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) && lay.k_L > 0 && workspace_bytes >= lay.total) {
     const aah::BwdSplit split{lay.k.slots, lay.k.merges, lay.k.n_merges,
-                              reinterpret_cast<float*>(static_cast<char*>(const_cast<void*>(workspace)) + lay.k_off)};
+                              reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.k_off)};
     const hipError_t e = aah::launch_bwd_dkdv_bf16_split(q, k, v, dout, nl2, nd, dk, dv, lay.k.items, lay.k.n_items,
                                                          lay.k.win, s, split, st);
     if (e != hipSuccess) return hip_fail(e, "split dK/dV launch");

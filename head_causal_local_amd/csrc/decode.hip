@@ -258,6 +258,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       // device-scope atomic issued once those stores have completed, and the merging workgroup
       // reads the partials with device-coherent loads.  (Release / acquire fences would write back
       // and invalidate whole L2 caches instead.)
+      //
+      // Why this handoff is ordered, in the terms of the AMDGPU memory model (LLVM's AMDGPUUsage,
+      // the GFX942 / gfx950 code sequences): an agent-scope atomic load, store or RMW is a plain
+      // global memory instruction with the sc1 cache-policy bit, so a store writes through the
+      // XCD's L2 to the device-coherent level and a load or RMW is served from that level, never
+      // from a stale L2 line.  On this target stores are counted by vmcnt, and vmcnt reaches 0
+      // only once each store is acknowledged at the scope its policy names; the writer waits for
+      // vmcnt(0) (and, with several storing waves, a barrier after each wave's own wait) before
+      // the counter RMW is issued.  That is the release sequence of the model without its
+      // buffer_wbl2, which only writes back lines of earlier non-coherent stores; every access to
+      // a partial here is agent-scope.  On the reading side the merge's loads depend on the RMW's
+      // returned value (branch on sm_last after a barrier), so they issue after the RMW has
+      // completed and see every partial whose writer incremented the counter before it; the
+      // acquire sequence's buffer_inv is again only for later non-coherent loads.
       float* out = pbase + (static_cast<size_t>(ch) * G + jh) * (2 + D);
       if (lane == 0) {
         coherent_store(out, m);

@@ -4,8 +4,10 @@
 // with the Q/K/V entries reduced over batch, sequence and head dimension of head
 // h (mean of the absolute activations; population standard deviation), e_h and
 // n_h the means over batch and rows of the per-row attention entropy and output
-// norm that a diagnostic forward pass wrote, rho_h = min(W_h, T) / T, and the
-// smoothing xbar = alpha xbar + (1 - alpha) x (xbar = x at the first update).
+// norm that a diagnostic forward pass wrote, rho_h = min(W_h, T) / T the window
+// usage of that pass (all three 0 when there are no such rows: missing
+// previous-attention diagnostics start at zero), and the smoothing
+// xbar = alpha xbar + (1 - alpha) x (xbar = x at the first update).
 //
 // Two launches, deterministic (fixed reduction order, no atomics):
 //   qkv_stats_kernel: one workgroup per 32768-element span of one (b, h) slice
@@ -215,7 +217,9 @@ __global__ __launch_bounds__(64) void features_kernel(const double* __restrict__
     const double rows = static_cast<double>(B) * T;
     sx[6] = sr[0][0] / rows;
     sx[7] = sr[1][0] / rows;
-    sx[8] = static_cast<double>(w_h) / T;
+    // Usage belongs to the stored statistics like e_h and n_h: zero when there are none (section 5.3),
+    // else the share of the context the window of the forward that produced them covers.
+    sx[8] = have_rows ? static_cast<double>(w_h) / T : 0.0;
   }
   __syncthreads();
   if (!owner) return;

@@ -67,11 +67,12 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 8
+#define AAH_ABI_VERSION 9
 
 typedef enum {
   AAH_OK = 0,
-  AAH_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, window < 1, misalignment, non-finite scale */
+  AAH_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, window < 1, misalignment (of any tensor or
+                               workspace), non-finite scale */
   AAH_ERR_UNSUPPORTED = 2,  /* dtype / head dim combination without a kernel */
   AAH_ERR_WORKSPACE = 3,    /* workspace smaller than aah_attn_workspace_size() */
   AAH_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
@@ -109,7 +110,9 @@ const char* aah_last_error_detail(void);
  * softmax run in fp32 whatever dt is; bf16 outputs are rounded to nearest even.
  * Workspace is optional.  With workspace = NULL (or fewer bytes than
  * aah_attn_fwd_workspace_size reports) every work item writes its own rows.
- * With a device workspace of at least that many bytes, 256-byte aligned, a bf16
+ * A non-NULL workspace must be 256-byte aligned (AAH_ERR_INVALID_ARG otherwise,
+ * whether or not the launch would split).
+ * With a device workspace of at least that many bytes, a bf16
  * launch with fewer work items than the device holds workgroups splits its long
  * items' key ranges into chunks whose partial results (row max, row sum, fp32
  * accumulator) land in the workspace, and a second kernel on the same stream
@@ -169,8 +172,11 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
  * mu(|.|) is the mean of the absolute activations and sigma the population
  * standard deviation, both over batch, sequence and head dimension of head h;
  * e_h and n_h are the means over batch and rows of row_entropy and row_onorm
- * (from aah_attn_fwd_diag; pass both NULL when there are none yet: then they
- * are 0); rho_h = min(W_h, T) / T, the head's window usage.  With grouped
+ * (from aah_attn_fwd_diag), and rho_h = min(W_h, T) / T is the window usage of
+ * that forward pass, whose windows the caller passes here.  These three are
+ * the previous-attention diagnostics: pass both row arrays NULL when there
+ * are none yet, and all three are 0 (section 5.3 starts missing diagnostics
+ * at zero).  With grouped
  * key/value heads the k and v entries of query head h are those of its
  * group's head.  Writes x to
  * features (device float[H * 9], row h = x_h; may be NULL) and smooths
@@ -215,7 +221,11 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v,
  *     row, nl2 and nD into the workspace.
  *   aah_attn_bwd_dkdv: writes dk and dv (key-stationary kernel) from q, k,
  *     v, dout and the workspace rows; it must not start before
- *     aah_attn_bwd_dq has completed on the same workspace.
+ *     aah_attn_bwd_dq has completed on the same workspace.  It only reads
+ *     those rows, but a launch that splits (a workspace of
+ *     aah_attn_bwd_split_workspace_size bytes) also writes its dK/dV partial
+ *     sums past them, so two dK/dV calls that share a workspace must not run
+ *     concurrently either.
  */
 aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                            const float* lse, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
@@ -224,7 +234,7 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
 
 aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                              const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
-                             aah_dtype dt, float scale, void* dk, void* dv, const void* workspace,
+                             aah_dtype dt, float scale, void* dk, void* dv, void* workspace,
                              size_t workspace_bytes, aah_stream_t stream);
 
 /*

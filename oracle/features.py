@@ -10,7 +10,8 @@ per-head feature axes of that head (mu(|.|) is the mean ABSOLUTE activation,
 not the absolute value of the mean), and e_h, n_h, rho_h are the previous
 attention diagnostics: entropy, output norm and usage.  The features are
 smoothed as xbar_t = alpha xbar_{t-1} + (1 - alpha) x_t, with xbar_0 = x_0 at the
-first control update; missing diagnostics are zero.
+first control update.  When there are no previous attention diagnostics, all
+three of them (e_h, n_h and rho_h) are zero.
 
 Readings where the page is silent (each listed in the design notes):
   * sigma is the population standard deviation (divide by the count N); with
@@ -19,9 +20,12 @@ Readings where the page is silent (each listed in the design notes):
     entropy -sum_j p_ij ln p_ij (natural log) over its visible keys;
   * n_h is the mean over batch entries and query rows of the Euclidean norm of
     the head's output row O_i;
-  * rho_h, the usage, is the fraction of the context the head's window covers,
-    min(W_h, T) / T: the head's term of the coverage ratio of section 5.10,
-    matching the pages' window-branch usage (Table 6 caption).
+  * rho_h, the usage, is the fraction of the context the window of the stored
+    statistics' forward pass covered, min(W_h, T) / T: the head's term of the
+    coverage ratio of section 5.10, matching the pages' window-branch usage
+    (Table 6 caption).  It belongs to the stored statistics like e_h and n_h:
+    with no diagnostics given it is zero, and with them it is taken from the
+    windows of the forward pass that produced them (the `windows` argument).
 """
 from __future__ import annotations
 
@@ -74,8 +78,12 @@ def _mean_abs_std(x_h):
 
 def head_features_ref(q, k, v, windows, row_entropy=None, row_norm=None):
     """Base features x [H, 9] (section 5.3) from Q [B,H,T,d], K/V [B,H_kv,T,d] and, if given, the
-    per-row diagnostics of the most recent forward pass ([B,H,T] each; None = zero).  With
-    grouped K/V heads, query head h's key and value statistics are those of its group's head."""
+    per-row diagnostics of the most recent forward pass ([B,H,T] each), run with `windows`.  Without
+    them (both None) e_h, n_h and rho_h are zero.  With grouped K/V heads, query head h's key and
+    value statistics are those of its group's head."""
+    if (row_entropy is None) != (row_norm is None):
+        raise ValueError("row_entropy and row_norm are the stored statistics of one forward pass: give both or neither")
+    have_diag = row_entropy is not None
     q = np.asarray(q, dtype=np.float64)
     B, H, T, _ = q.shape
     x = np.zeros((H, N_FEATURES))
@@ -83,9 +91,10 @@ def head_features_ref(q, k, v, windows, row_entropy=None, row_norm=None):
         g = kv_head(h, H, np.asarray(k).shape[1])
         for slot, (t, hh) in enumerate(((q, h), (k, g), (v, g))):
             x[h, 2 * slot], x[h, 2 * slot + 1] = _mean_abs_std(np.asarray(t)[:, hh])
-        x[h, 6] = 0.0 if row_entropy is None else np.asarray(row_entropy, dtype=np.float64)[:, h].mean()
-        x[h, 7] = 0.0 if row_norm is None else np.asarray(row_norm, dtype=np.float64)[:, h].mean()
-        x[h, 8] = min(int(windows[h]), T) / T
+        if have_diag:
+            x[h, 6] = np.asarray(row_entropy, dtype=np.float64)[:, h].mean()
+            x[h, 7] = np.asarray(row_norm, dtype=np.float64)[:, h].mean()
+            x[h, 8] = min(int(windows[h]), T) / T
     return x
 
 

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 8
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 9
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -167,6 +167,30 @@ def test_bwd_step_validation():
                                None) == 1                                                      # scale 0
     assert lib.aah_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, float("inf"), FAKE, FAKE,
                                need, None) == 1                                                # scale inf
+
+
+def test_misaligned_workspace_is_one_status_everywhere():
+    """A workspace that is large enough but not 256-byte aligned is AAH_ERR_INVALID_ARG (the header's status
+    for every misalignment) in every entry point that takes one, and is found before any HIP call: the
+    optional forward workspace included, whether or not the launch would split."""
+    lib = _lib.lib()
+    w = np.array([4, 64], dtype=np.int32)
+    wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    F, bad = FAKE, FAKE + 16
+    need = aah.workspace_size(1, 2, 64, 64, "bf16")
+    # aah_attn_fwd(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, ws, bytes, stream): a short
+    # bf16 call (never split) and an fp32 one (never split) with a misaligned workspace of any size.
+    for dt, nbytes in ((0, 0), (0, 1 << 20), (1, 1 << 20)):
+        assert lib.aah_attn_fwd(F, F, F, wp, None, 1, 2, 2, 64, 64, dt, 0.1, F, F, bad, nbytes, None) == 1
+        assert "aligned" in lib.aah_last_error_detail().decode()
+    assert lib.aah_attn_bwd(F, F, F, F, F, F, wp, None, 1, 2, 2, 64, 64, 0, 0.1, F, F, F, bad, need, None) == 1
+    assert lib.aah_attn_bwd_dq(F, F, F, F, F, F, wp, None, 1, 2, 2, 64, 64, 0, 0.1, F, bad, need, None) == 1
+    assert lib.aah_attn_bwd_dkdv(F, F, F, F, wp, None, 1, 2, 2, 64, 64, 0, 0.1, F, F, bad, need, None) == 1
+    dneed = aah.decode_workspace_size(w, 2, 128, 64)
+    assert lib.aah_attn_decode(F, F, F, F, F, F, wp, None, 2, 2, 2, 128, 64, 0, 0.125, F, F, bad, dneed, None) == 1
+    fneed = aah.head_features_workspace_size(2, 2, 64, 64)
+    assert lib.aah_head_features(F, F, F, None, None, wp, 2, 2, 2, 64, 64, 0, 0.9, 0, F, None, bad, fneed,
+                                 None) == 1
 
 
 def test_slice_limit():

@@ -4,7 +4,8 @@ Library routines (scipy's softmax and entropy over each row's key set, torch sca
 for the output rows, torch's mean / population std of a head's slice), closed forms (uniform attention over
 identical keys, a window of one, constant and two-valued activations, the EMA of a constant input), and the
 mistakes a plausible implementation makes: |mean| instead of mean |x|, reducing over the wrong axis, an unbiased
-instead of a population deviation, usage above 1 for windows longer than T.
+instead of a population deviation, usage above 1 for windows longer than T, a nonzero usage with no stored
+statistics.
 """
 import numpy as np
 import pytest
@@ -92,20 +93,25 @@ def test_qkv_statistics_closed_forms():
 
 
 def test_diagnostics_usage_and_missing_entries():
-    """e_h and n_h are the means of the given rows over (B, T); missing rows give zero (section 5.3);
-    usage is min(W_h, T) / T, so a window longer than T is 1."""
+    """"Asymmetric Attention Heads" section 5.3 (Head features and EMA smoothing): the previous-attention
+    diagnostics (e_h, n_h, rho_h) start at zero when missing, so with no stored statistics all three entries
+    are exactly 0 -- rho_h included.  With them, e_h and n_h are the means of the given rows over (B, T), and
+    rho_h, the usage of the forward pass that produced them, is min(W_h, T) / T: a window longer than T is 1.
+    Giving only one of the two row arrays is refused (they come from one forward pass)."""
     B, H, T, d = 2, 3, 16, 4
     q, k, v = _rand(B, H, T, d, seed=5)
     x0 = oracle.head_features_ref(q, k, v, [4, 16, 1000])
-    assert np.array_equal(x0[:, 6:8], np.zeros((H, 2)))
-    assert np.array_equal(x0[:, 8], [0.25, 1.0, 1.0])
+    assert np.array_equal(x0[:, 6:9], np.zeros((H, 3)))
     ent = np.arange(B * H * T, dtype=np.float64).reshape(B, H, T)
     nrm = ent[:, ::-1] * 0.5
     x1 = oracle.head_features_ref(q, k, v, [4, 16, 1000], row_entropy=ent, row_norm=nrm)
     for h in range(H):
         assert x1[h, 6] == pytest.approx(np.mean([ent[b, h, t] for b in range(B) for t in range(T)]), abs=1e-12)
         assert x1[h, 7] == pytest.approx(np.mean([nrm[b, h, t] for b in range(B) for t in range(T)]), abs=1e-12)
+    assert np.array_equal(x1[:, 8], [0.25, 1.0, 1.0])
     assert np.array_equal(x1[:, :6], x0[:, :6])
+    with pytest.raises(ValueError):
+        oracle.head_features_ref(q, k, v, [4, 16, 1000], row_entropy=ent)
 
 
 def test_ema_closed_forms():

@@ -128,7 +128,8 @@ def test_head_features_and_ema(dtype):
 
 
 def test_features_without_diagnostics_and_determinism():
-    """No diagnostic rows: entropy and norm features are 0.  Same inputs, same bits."""
+    """No diagnostic rows: entropy, norm and usage features are 0 (AAH section 5.3 starts missing
+    previous-attention diagnostics at zero).  Same inputs, same bits."""
     _require_gpu()
     wl = synth.random_workload(3, 4, 500, 32, [16, 128, 500, 2], dtype="bf16", seed=3, backward=False)
     q, k, v = dev(wl, "q"), dev(wl, "k"), dev(wl, "v")
@@ -137,10 +138,10 @@ def test_features_without_diagnostics_and_determinism():
     torch.cuda.synchronize()
     assert torch.equal(x1, x2)
     xh = host(x1)
-    assert np.array_equal(xh[:, 6:8], np.zeros((4, 2)))
+    assert np.array_equal(xh[:, 6:9], np.zeros((4, 3)))
     ref = oracle.head_features_ref(wl.q, wl.k, wl.v, wl.windows)
     assert np.allclose(xh[:, :6], ref[:, :6], rtol=1e-5, atol=1e-6)
-    assert np.allclose(xh[:, 8], ref[:, 8], rtol=1e-7, atol=0)
+    assert np.array_equal(ref[:, 6:9], np.zeros((4, 3)))
 
 
 SAMPLE_ROWS = [0, 1, 127, 128, 511, 512, 1023, 2048, 3000, 4095]

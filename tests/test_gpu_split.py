@@ -43,11 +43,12 @@ def _ws_bytes(windows, B, H, T, d, sinks=None, dt=BF16, H_kv=None):
 def _fwd_unsplit(q, k, v, windows, scale):
     """The forward with no workspace: one workgroup per item, every item writes its own rows."""
     B, H, T, d = q.shape
+    H_kv = k.shape[1]
     w = np.ascontiguousarray(windows, dtype=np.int32)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
     st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, B, H, H, T, d, BF16,
+                            w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, B, H, H_kv, T, d, BF16,
                             float(scale), o.data_ptr(), lse.data_ptr(), None, 0,
                             torch.cuda.current_stream().cuda_stream)
     aah.check(st)
@@ -88,6 +89,25 @@ def test_split_forward_matches_oracle(B, H, T, d, windows):
     o, lse = aah.attn_fwd(_dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v"), wl.windows, wl.scale)
     torch.cuda.synchronize()
     _check_full(wl, o, lse)
+
+
+def test_split_forward_grouped_heads_matches_oracle():
+    """Grouped K/V heads take the split launch too (B=1, 8 query heads over 2 K/V heads, T=4096: 256 items,
+    fewer than the device holds): every row of O and LSE against the oracle, which reads head h's keys from
+    K/V head h // 4; split and unsplit launches agree within the bf16 bounds."""
+    _require_gpu()
+    B, H, H_kv, T, d = 1, 8, 2, 4096, 64
+    windows = [4096, 512, 2048, 1, 4096, 3000, 100, 4096]
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=77, backward=False, H_kv=H_kv)
+    assert _ws_bytes(wl.windows, B, H, T, d, H_kv=H_kv) > 0
+    q, k, v = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+    ou, lu = _fwd_unsplit(q, k, v, wl.windows, wl.scale)
+    torch.cuda.synchronize()
+    _check_full(wl, o, lse)
+    a, b = o.float().cpu().numpy(), ou.float().cpu().numpy()
+    assert (np.abs(a - b) - np.maximum(2 * O_TOL_BF16, np.abs(b) * 2.0 ** -7)).max() <= 0
+    assert (lse - lu).abs().max().item() < 2 * LSE_TOL_BF16
 
 
 def test_split_close_to_unsplit_and_deterministic():
@@ -138,7 +158,7 @@ def test_split_concurrent_streams_and_misaligned_workspace():
                             float(wl.scale), o.data_ptr(), lse.data_ptr(), ws.data_ptr() + 16, need,
                             torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    assert st == 3  # AAH_ERR_WORKSPACE
+    assert st == 1  # AAH_ERR_INVALID_ARG, as for every misaligned workspace
     assert bool((o.float() == 7.0).all()) and bool((lse == 7.0).all())
 
 
