@@ -372,6 +372,39 @@ def attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, scale
     return out, lse
 
 
+def attn_decode_noalloc(q, k_new, v_new, kcache, vcache, pos, windows, T_max: int, out, lse,
+                        scale: Optional[float] = None, stream=None, sinks=None):
+    """attn_decode without a workspace (aah_attn_decode_noalloc): the library's per-device scratch array holds
+    the counters, plan and partials, so this call allocates nothing.  out [B, H, d] and lse [B, H] must be
+    given.  Returns (out, lse)."""
+    import torch
+    _check_operand("v_new", v_new, k_new)
+    B, H, d = q.shape
+    H_kv = k_new.shape[1]
+    if k_new.shape != (B, H_kv, d) or H % H_kv != 0 or k_new.dtype != q.dtype or not k_new.is_contiguous():
+        raise ValueError("k_new must be a contiguous [B, H_kv, d] tensor of q's dtype with H_kv dividing H")
+    if not q.is_cuda or not q.is_contiguous():
+        raise ValueError("q must be a contiguous device tensor")
+    w, sk, Hw, H_kv = _decode_heads(windows, sinks, H_kv)
+    if Hw != H:
+        raise ValueError(f"windows has {Hw} entries, expected H = {H}")
+    R = kv_cache_rows(w, T_max, sinks=sk, H_kv=H_kv)
+    for name, t in (("kcache", kcache), ("vcache", vcache)):
+        if t.shape != (B, R, d) or t.dtype != q.dtype or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{B}, {R}, {d}] tensor of q's dtype")
+    if pos.shape != (B,) or pos.dtype != torch.int32 or not pos.is_contiguous() or pos.device != q.device:
+        raise ValueError("pos must be a contiguous int32 [B] tensor on q's device")
+    _check_operand("out", out, q)
+    if lse.shape != (B, H) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    check(lib().aah_attn_decode_noalloc(q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), kcache.data_ptr(),
+                                        vcache.data_ptr(), pos.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv,
+                                        int(T_max), d, _dtype_code(q), scale, out.data_ptr(), lse.data_ptr(),
+                                        _stream_ptr(q, stream)))
+    return out, lse
+
+
 def tile_shape(dtype: str, d: int, is_bwd: bool) -> Tuple[int, int]:
     """(row tile, column tile) the kernels use for this dtype / head dim / pass."""
     code = AAH_BF16 if dtype in ("bf16", "bfloat16") else AAH_F32

@@ -27,7 +27,7 @@ EXPORTS = (
     "aah_plan_fwd_split", "aah_plan_bwd_split", "aah_attn_bwd_split_workspace_size", "aah_window_stats",
     "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
     "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode", "aah_attn_fwd_diag",
-    "aah_head_features_workspace_size", "aah_head_features",
+    "aah_head_features_workspace_size", "aah_head_features", "aah_attn_decode_noalloc",
 )
 
 
@@ -114,6 +114,10 @@ def _declare(lib):
     lib.aah_kv_cache_fill.restype = c_int
     lib.aah_kv_cache_fill.argtypes = [c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int,
                                       c_int, c_void_p, c_void_p, c_void_p]
+    lib.aah_attn_decode_noalloc.restype = c_int
+    lib.aah_attn_decode_noalloc.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32,
+                                            c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p,
+                                            c_void_p]
     lib.aah_attn_decode.restype = c_int
     lib.aah_attn_decode.argtypes = [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int,
                                     c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t,

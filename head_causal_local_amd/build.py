@@ -27,7 +27,8 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-mllvm", "-amdgpu-mfma-vgpr-form"]
 HOST_ONLY = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I", "/opt/rocm/include"]
 
-SOURCES = ["workplan.cpp", "aah_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "simple.hip", "decode.hip", "diag.hip"]
+SOURCES = ["workplan.cpp", "aah_api.cpp", "fwd_bf16.hip", "bwd_bf16.hip", "simple.hip", "decode.hip", "diag.hip",
+           "noalloc.hip"]
 
 
 def _compile(src: str) -> str:

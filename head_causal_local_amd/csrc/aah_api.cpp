@@ -933,6 +933,64 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   return AAH_OK;
 }
 
+aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                                   const int32_t* pos, const int32_t* windows, const int32_t* sinks, int B, int H,
+                                   int H_kv, int T_max, int d, aah_dtype dt, float scale, void* o, float* lse,
+                                   aah_stream_t stream) {
+  g_detail.clear();
+  // The same checks as aah_attn_decode, on fixed-size tables: nothing here allocates (host or device).
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  AAH_TRY(check_dims(B, H, T_max, d, dt));
+  AAH_TRY(check_kv_heads(H, H_kv));
+  AAH_TRY(check_windows(windows, sinks, H));
+  if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
+  if (H > aah::kNoAllocMaxHeads)
+    return fail(AAH_ERR_UNSUPPORTED, "H = %d: the allocation-free decode takes at most %d query heads", H,
+                aah::kNoAllocMaxHeads);
+  if (static_cast<int64_t>(B) * H_kv > 65535)
+    return fail(AAH_ERR_UNSUPPORTED, "B * H_kv = %lld exceeds 65535", static_cast<long long>(B) * H_kv);
+  AAH_TRY(check_tensor(q, "q", 16));
+  AAH_TRY(check_tensor(k_new, "k_new", 16));
+  AAH_TRY(check_tensor(v_new, "v_new", 16));
+  AAH_TRY(check_tensor(kcache, "kcache", 16));
+  AAH_TRY(check_tensor(vcache, "vcache", 16));
+  AAH_TRY(check_tensor(pos, "pos", 4));
+  AAH_TRY(check_tensor(o, "o", 16));
+  AAH_TRY(check_tensor(lse, "lse", 4));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  // Per query head C_h and effective sink, per key/value head ring and sink rows (as decode_shape).
+  aah::NoAllocHeads heads;
+  const int G = H / H_kv;
+  int64_t rows = 0, chunks = 0;
+  for (int g = 0; g < H_kv; ++g) {
+    int64_t ring = 0, ksink = 0;
+    for (int j = 0; j < G; ++j) {
+      const int h = g * G + j;
+      const int64_t cap = std::min<int64_t>(windows[h], T_max);
+      const int64_t sk = std::max<int64_t>(0, std::min<int64_t>(sinks == nullptr ? 0 : sinks[h], T_max - cap));
+      heads.cap[h] = static_cast<int32_t>(cap);
+      heads.sink[h] = static_cast<int32_t>(sk);
+      ring = std::max(ring, cap);
+      ksink = std::max(ksink, sk);
+    }
+    rows += ksink + ring;
+    chunks += (ksink + ring + aah::kDecodeRows - 1) / aah::kDecodeRows;
+  }
+  if (rows > INT32_MAX) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
+  if (static_cast<int64_t>(B) * rows * d >= (int64_t{1} << 40)) return fail(AAH_ERR_UNSUPPORTED, "cache too large");
+  const aah::NoAllocLayout lay = aah::noalloc_layout(B, H, H_kv, d, chunks);
+  if (lay.total > aah::kNoAllocScratchBytes)
+    return fail(AAH_ERR_UNSUPPORTED,
+                "this step needs %zu bytes of scratch (counters, plan, partials); the library holds %zu per device: "
+                "use aah_attn_decode with a workspace",
+                lay.total, aah::kNoAllocScratchBytes);
+  const hipError_t e = aah::launch_decode_noalloc_bf16(
+      q, k_new, v_new, kcache, vcache, pos, heads, H, H_kv, static_cast<int>(chunks), static_cast<int>(rows), B, T_max,
+      d, scale, o, lse, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "allocation-free decode launch");
+  return AAH_OK;
+}
+
 aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int q_tile,
                         int kv_tile, int n_queues, aah_work_item* items, int64_t capacity, int64_t* n_items) {
   g_detail.clear();

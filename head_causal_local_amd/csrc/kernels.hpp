@@ -173,4 +173,39 @@ hipError_t launch_decode_bf16(const void* q, const void* knew, const void* vnew,
 hipError_t launch_cache_fill_bf16(const void* k, const void* v, void* kcache, void* vcache,
                                   const DecodePlanView& plan, int B, int T, int d, hipStream_t stream);
 
+// ---- decoding with no caller workspace (counters, plan tables and partials in a library-held device array)
+constexpr int kNoAllocMaxHeads = 256;                     // query heads (the per-head table travels by value)
+constexpr size_t kNoAllocScratchBytes = size_t{8} << 20;  // bytes of that array on each device
+
+// Per query head: C_h = min(W_h, T_max) and the effective sink min(S_h, T_max - C_h), passed to the
+// planning kernel as a kernel argument.
+struct NoAllocHeads {
+  int32_t cap[kNoAllocMaxHeads];
+  int32_t sink[kNoAllocMaxHeads];
+};
+
+// Byte offsets of the scratch regions of one call: merge counters (at 0), plan tables, decode chunks,
+// partials, and the bytes used in all.
+struct NoAllocLayout {
+  size_t tables, chunks, partials, total;
+};
+inline NoAllocLayout noalloc_layout(int B, int H, int H_kv, int d, int64_t n_chunks) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  NoAllocLayout l;
+  l.tables = up(static_cast<size_t>(B) * H_kv * sizeof(int32_t));
+  l.chunks = l.tables + up(static_cast<size_t>(4 * H_kv + 1 + 2 * H) * sizeof(int32_t));
+  l.partials = l.chunks + up(static_cast<size_t>(n_chunks) * sizeof(DecodeChunk));
+  l.total = l.partials + static_cast<size_t>(B) * n_chunks * (H / H_kv) * (2 + d) * sizeof(float);
+  return l;
+}
+
+// One decoding step as launch_decode_bf16, with the plan built on the device from `heads` (one small
+// kernel that also clears the counters) and every buffer in the library's scratch array.  The caller
+// has checked the arguments and that noalloc_layout(...).total <= kNoAllocScratchBytes; n_chunks and
+// rows are the decode plan's chunk and cache-row counts for these heads.
+hipError_t launch_decode_noalloc_bf16(const void* q, const void* knew, const void* vnew, void* kcache, void* vcache,
+                                      const int32_t* pos, const NoAllocHeads& heads, int H, int H_kv, int n_chunks,
+                                      int rows, int B, int T_max, int d, float scale, void* o, float* lse,
+                                      hipStream_t stream);
+
 }  // namespace aah

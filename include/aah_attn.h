@@ -303,6 +303,29 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
                            int T_max, int d, aah_dtype dt, float scale, void* o, float* lse, void* workspace,
                            size_t workspace_bytes, aah_stream_t stream);
 
+/*
+ * One decoding step that allocates nothing, for callers that cannot allocate
+ * device memory when they call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Arguments, caches, results and
+ * status codes are those of aah_attn_decode, without the workspace.  Its merge
+ * counters, plan tables and partial results live in one fixed device array
+ * per GPU that the library holds until the process ends (8 MiB, allocated
+ * when the library's code is loaded on that device, not by this call); a
+ * small planning kernel rebuilds the tables from the windows and clears the
+ * counters on every call, so the call reads no host memory after it returns
+ * and a captured graph replays the whole step.  No work list is cached.
+ * Limits: H <= 256, and the step's counters, tables and partials
+ * (B * H_kv * 4 bytes, (4 H_kv + 1 + 2 H) * 4 bytes, 8 bytes per 256 cache rows
+ * of a batch entry, and B * chunks * (H / H_kv) * (2 + d) * 4 bytes, each
+ * region rounded up to 256 bytes) must fit in the array; a larger step returns
+ * AAH_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race.
+ */
+aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                                   const int32_t* pos, const int32_t* windows, const int32_t* sinks, int B, int H,
+                                   int H_kv, int T_max, int d, aah_dtype dt, float scale, void* o, float* lse,
+                                   aah_stream_t stream);
+
 /* Workspace bytes needed by aah_attn_fwd (is_bwd = 0) or aah_attn_bwd (is_bwd != 0);
  * 0 for invalid arguments. */
 size_t aah_attn_workspace_size(int B, int H, int T, int d, aah_dtype dt, int is_bwd);

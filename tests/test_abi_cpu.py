@@ -307,6 +307,44 @@ def test_decode_validation():
     assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 64, 128, 64, 1, F, F, None) == 2    # fp32
 
 
+def test_decode_noalloc_validation():
+    """The allocation-free decode reports every argument error before any HIP call: the decode checks, more
+    than 256 query heads, and a step whose counters, plan and partials exceed the library's array."""
+    lib = _lib.lib()
+    w = np.array([16, 64], dtype=np.int32)
+    wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    F = FAKE
+    # aah_attn_decode_noalloc(q, k_new, v_new, kcache, vcache, pos, windows, sinks, B, H, H_kv, T_max, d, dt, scale,
+    #                         o, lse, stream)
+    ok = [F, F, F, F, F, F, wp, None, 2, 2, 2, 128, 64, 0, 0.125, F, F, None]
+
+    def call(i=None, val=None):
+        a = list(ok)
+        if i is not None:
+            a[i] = val
+        return lib.aah_attn_decode_noalloc(*a)
+    for i, name in ((0, "q"), (1, "k_new"), (2, "v_new"), (3, "kcache"), (4, "vcache"), (5, "pos"), (15, "o"),
+                    (16, "lse")):
+        assert call(i, 0) == 1, name
+    assert call(4, F + 8) == 1                      # misaligned vcache
+    assert call(6, None) == 1                       # NULL windows
+    assert call(13, 1) == 2                         # fp32 caches: unsupported
+    assert call(12, 48) == 2                        # d = 48
+    assert call(14, 0.0) == 1 and call(14, float("nan")) == 1
+    assert call(10, 3) == 1                         # H_kv does not divide H
+    negs = np.array([0, -4], dtype=np.int32)
+    assert call(7, negs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == 1
+    many = np.full(257, 64, dtype=np.int32)         # 257 query heads
+    a = list(ok)
+    a[6], a[9], a[10] = many.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 257, 257
+    assert lib.aah_attn_decode_noalloc(*a) == 2
+    big = np.full(2, 1 << 21, dtype=np.int32)       # 16384 chunks of partials at d = 128: more than 8 MiB
+    a = list(ok)
+    a[6], a[8], a[11], a[12] = big.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 1 << 21, 128
+    assert lib.aah_attn_decode_noalloc(*a) == 2
+    assert "scratch" in lib.aah_last_error_detail().decode()
+
+
 def test_diag_and_feature_validation():
     lib = _lib.lib()
     w = np.array([4, 9], dtype=np.int32)
