@@ -10,16 +10,17 @@
 // (with grouped key/value heads the tiles come from the group's K/V head; the
 // planner sends a group's query heads to the same XCD, so they meet in its L2);
 // tiles wholly outside the window are never visited.  Each wave walks the
-// tile in two 32-key blocks and classifies each block against its own 32
-// rows: blocks no row sees are skipped (no MFMA, no exp), blocks every row
-// sees in full run without a mask, and only the (at most two) partial blocks
-// per wave -- the diagonal and the window's trailing edge -- apply a
-// one-sided mask.
+// keys in 32-key blocks and classifies each block against its own 32 rows:
+// blocks no row sees are skipped (no MFMA, no exp), blocks every row sees in
+// full run without a mask, and only the (at most two) partial blocks per
+// wave -- the diagonal and the window's trailing edge -- apply a one-sided
+// mask.
 //
-// Data flow per 64-key tile:
+// Data flow per LDS stage (64 keys in two stages at d <= 64; 32 keys in three
+// stages at d = 128):
 //   * K and V tiles go from HBM straight into LDS (buffer_load ... lds, no
-//     register staging), double-buffered: the next tile's copies are in flight
-//     while the current tile is used.  Tiles are row-major with an XOR swizzle
+//     register staging) through a ring: the next stages' copies are in flight
+//     while the current one is used.  Tiles are row-major with an XOR swizzle
 //     of their 16-byte chunks so that both read patterns below are free of
 //     bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (M = keys, N = queries, K = d).
@@ -81,24 +82,30 @@ using namespace dev;
 
 constexpr int kWaves = 4;
 constexpr int kRows = 32 * kWaves;  // query rows per item
-constexpr int kKeys = 64;           // keys per LDS stage
+constexpr int kPlanKeys = 64;       // keys per tile of the planner's ranges
 constexpr int kThreads = 64 * kWaves;
 constexpr float kThresh = 1024.0f;  // lazy-rescale bound on every weight p (2^10)
-static_assert(kRows == kFwdBf16RowTile && kKeys == kFwdBf16ColTile, "planner tile mismatch");
+static_assert(kRows == kFwdBf16RowTile && kPlanKeys == kFwdBf16ColTile, "planner tile mismatch");
 
 template <int D>
 struct Cfg {
   static constexpr int kNC = D / 8;                 // 16-byte chunks per row
   static constexpr int kRowBytes = D * 2;
-  static constexpr int kTileBytes = kKeys * kRowBytes;  // one K or V stage
-  static constexpr int kDmaPerWave = kNC / kWaves;  // 1 KiB DMA instructions per wave per tensor per tile
+  // Keys per LDS stage and stages in the ring.  At d = 128 a stage holds 32 keys and the ring three
+  // stages (copies issued two steps ahead): 48 KiB instead of 64, so a CU holds three workgroups, not
+  // two (grouped d = 128 layer: forward 292 -> 274 us).  At d <= 64 LDS is no tighter than registers
+  // with 64-key stages and two of them (32 KiB at d = 64: four workgroups per CU); 32-key stages there
+  // measured 2.5 % slower (twice the barriers per key, and a fifth workgroup per CU bought nothing).
+  static constexpr int kKT = D >= 128 ? 32 : 64;
+  static constexpr int kNS = D >= 128 ? 3 : 2;
+  static constexpr int kTileBytes = kKT * kRowBytes;              // one K or V stage
+  static constexpr int kDmaPerWave = kKT * kNC / (64 * kWaves);  // 1 KiB DMA instructions per wave per tensor per stage
   static constexpr int kSteps = D / 16;             // MFMA k-steps over d for S^T
   static constexpr int kBlocks = D / 32;            // 32-row blocks of O^T
-  // Resident waves per SIMD the register allocation is sized for.  At d = 64
-  // LDS is the tighter bound: a CU holds four workgroups of 32 KiB (five only
-  // at 32000 bytes or less), so registers up to 128 would cost nothing.
-  static constexpr int kWavesPerSimd = D <= 32 ? 4 : D <= 64 ? 4 : 1;
-  static_assert(kDmaPerWave >= 1 && kDmaPerWave * kWaves == kNC, "tile / wave split");
+  // Resident waves per SIMD the register allocation is sized for.
+  static constexpr int kWavesPerSimd = D <= 64 ? 4 : 1;
+  static_assert(kDmaPerWave >= 1 && kDmaPerWave * 64 * kWaves == kKT * kNC, "tile / wave split");
+  static_assert(kPlanKeys % kKT == 0, "stages subdivide the planner's tiles");
 };
 
 // Key offset (within its 32-key block, before the 4 hl lane offset) held by S^T register r.
@@ -114,10 +121,10 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
                      float* __restrict__ part_ml) {
   using C = Cfg<D>;
   constexpr int NC = C::kNC;
-  __shared__ __attribute__((aligned(1024))) char k_lds0[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds0[C::kTileBytes];
-  __shared__ __attribute__((aligned(1024))) char v_lds1[C::kTileBytes];
+  constexpr int KT = C::kKT;
+  constexpr int kSub = kPlanKeys / KT;  // stages per planner tile
+  // Ring slot i: K tile at lds + 2 i kTileBytes, its V tile right after it.
+  __shared__ __attribute__((aligned(1024))) char lds[C::kNS * 2 * C::kTileBytes];
 
   const WorkItem it = items[blockIdx.x];
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
@@ -125,11 +132,15 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int slot = slots != nullptr ? slots[blockIdx.x] : -1;
   const int W = win_eff[it.bh % H];
   const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
-  // Tiles in visiting order: sink tiles 0 .. ns - 1 (those before the window's
-  // first tile), then the window tiles it.lo .. it.hi - 1.
-  const int ns = SINK ? min((S + kKeys - 1) / kKeys, it.lo) : 0;
-  const int n_tiles = ns + it.hi - it.lo;
-  auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + it.lo; };
+  // Stages (KT keys each) in visiting order: sink stages 0 .. ns - 1 (those before the window's first
+  // stage), then the window's stages w_lo .. w_hi - 1 -- the planner's tiles [lo, hi) trimmed to the keys
+  // [q0 - W + 1, q1 - 1] the item's rows see.
+  const int q0i = it.tile * kRows, q1i = min(T, q0i + kRows);
+  const int w_lo = max(it.lo * kSub, max(0, q0i - W + 1) / KT);
+  const int w_hi = min(it.hi * kSub, (q1i - 1) / KT + 1);
+  const int ns = SINK ? min((S + KT - 1) / KT, w_lo) : 0;
+  const int n_tiles = ns + w_hi - w_lo;
+  auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + w_lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
   // Key/value head of this query head: its group's, h / (H / H_kv).
   const size_t kvbase = (static_cast<size_t>(it.bh / H) * H_kv + (it.bh % H) / (H / H_kv)) * T * D;
@@ -184,7 +195,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     dma_off[j] = static_cast<uint32_t>(row * C::kRowBytes + (((P % NC) ^ swz<NC>(row)) * 16));
   }
   auto issue_tile = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
-    const int k0 = kt * kKeys;
+    const int k0 = kt * KT;
     // Resources start at the tile's first row and end at row T: keys past T read as zero.
     const uint32_t left = static_cast<uint32_t>(T - k0) * C::kRowBytes;
     const i32x4 rk = rsrc_words(Kh + static_cast<size_t>(k0) * D, left);
@@ -330,32 +341,50 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   };
 
   auto do_tile = [&](const char* kt_lds, const char* vt_lds, int kt) __attribute__((always_inline)) {
-    const int k0 = kt * kKeys;
-    do_block(kt_lds, vt_lds, k0, 0);
-    do_block(kt_lds, vt_lds, k0 + 32, 1);
+    const int k0 = kt * KT;
+#pragma unroll
+    for (int mb = 0; mb < KT / 32; ++mb) do_block(kt_lds, vt_lds, k0 + 32 * mb, mb);
   };
+  auto kst = [&](int i) __attribute__((always_inline)) { return lds + 2 * i * C::kTileBytes; };
+  auto vst = [&](int i) __attribute__((always_inline)) { return lds + (2 * i + 1) * C::kTileBytes; };
 
-  // Two-stage ring: the v-th tile visited lives in stage v % 2.  A step issues
-  // the copies of the next tile into the other stage (which every wave finished
-  // reading before the barrier that ended the previous step), computes the
-  // current tile, then waits for its own copies and meets the other waves at
-  // the barrier.  Returns true after the last tile.  Two stages instead of
-  // three leave room for four workgroups per CU at d = 64 instead of three;
-  // the copies still have a whole step to land.
-  auto step = [&](int v, const char* kc, const char* vc, char* kn, char* vn) __attribute__((always_inline)) {
-    const bool fill = v + 1 < n_tiles;
-    if (fill) issue_tile(tile_at(v + 1), kn, vn);
-    do_tile(kc, vc, tile_at(v));
-    if (!fill) return true;  // nothing left to wait for; the workgroup is done with LDS
-    wait_vm_barrier(0);
+  // Ring of kNS slots: the v-th stage visited lives in slot v % kNS.  A step
+  // issues the copies of stage v + kNS - 1 into the slot every wave finished
+  // reading before the barrier that ended the previous step, computes stage v,
+  // then waits until its own copies of stage v + 1 have landed (those of later
+  // stages may still be in flight) and meets the other waves at the barrier.
+  // Returns true after the last stage.
+  constexpr int kFill = 2 * C::kDmaPerWave;  // copies per wave per stage
+  auto step = [&](int v, int cur, int nxt) __attribute__((always_inline)) {
+    const bool fill = v + C::kNS - 1 < n_tiles;
+    if (fill) issue_tile(tile_at(v + C::kNS - 1), kst(nxt), vst(nxt));
+    do_tile(kst(cur), vst(cur), tile_at(v));
+    if (v + 1 >= n_tiles) return true;  // nothing left to wait for; the workgroup is done with LDS
+    if (C::kNS == 3 && fill)
+      wait_vm_barrier(kFill);
+    else
+      wait_vm_barrier(0);
     return false;
   };
 
-  issue_tile(tile_at(0), k_lds0, v_lds0);
-  wait_vm_barrier(0);
-  for (int v = 0;; v += 2) {
-    if (step(v, k_lds0, v_lds0, k_lds1, v_lds1)) break;
-    if (step(v + 1, k_lds1, v_lds1, k_lds0, v_lds0)) break;
+  issue_tile(tile_at(0), kst(0), vst(0));
+  if (C::kNS == 3 && n_tiles > 1) {
+    issue_tile(tile_at(1), kst(1), vst(1));
+    wait_vm_barrier(kFill);
+  } else {
+    wait_vm_barrier(0);
+  }
+  if constexpr (C::kNS == 3) {
+    for (int v = 0;; v += 3) {
+      if (step(v, 0, 2)) break;
+      if (step(v + 1, 1, 0)) break;
+      if (step(v + 2, 2, 1)) break;
+    }
+  } else {
+    for (int v = 0;; v += 2) {
+      if (step(v, 0, 1)) break;
+      if (step(v + 1, 1, 0)) break;
+    }
   }
 
   if (!wave_active) return;
