@@ -127,17 +127,25 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   __shared__ __attribute__((aligned(1024))) char lds[C::kNS * 2 * C::kTileBytes];
 
   const WorkItem it = items[blockIdx.x];
+  // The kernel arguments the prologue needs are read here, so that their loads go out with the
+  // item's rather than one scalar round trip after the padding test.
+  __asm__ volatile("" ::"s"(H), "s"(H_kv), "s"(T), "s"(Q), "s"(K), "s"(V), "s"(slots), "s"(win_eff));
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
   // A chunk of a split item leaves its rows' partial result in its slot instead of O and LSE.
   const int slot = slots != nullptr ? slots[blockIdx.x] : -1;
-  const int W = win_eff[it.bh % H];
+  // The window (and sink size) come from a table indexed by the item's head.  Where the first
+  // copies do not depend on them (64-key stages, no sinks) that load is issued after those copies,
+  // so that waiting for it (scalar loads complete in any order) does not hold them back.
+  constexpr bool kLateW = kSub == 1 && !SINK;
+  int W = 0;
+  if constexpr (!kLateW) W = win_eff[it.bh % H];
   const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
   // Stages (KT keys each) in visiting order: sink stages 0 .. ns - 1 (those before the window's first
   // stage), then the window's stages w_lo .. w_hi - 1 -- the planner's tiles [lo, hi) trimmed to the keys
   // [q0 - W + 1, q1 - 1] the item's rows see.
   const int q0i = it.tile * kRows, q1i = min(T, q0i + kRows);
-  const int w_lo = max(it.lo * kSub, max(0, q0i - W + 1) / KT);
-  const int w_hi = min(it.hi * kSub, (q1i - 1) / KT + 1);
+  const int w_lo = kSub == 1 ? it.lo : max(it.lo * kSub, max(0, q0i - W + 1) / KT);
+  const int w_hi = kSub == 1 ? it.hi : min(it.hi * kSub, (q1i - 1) / KT + 1);
   const int ns = SINK ? min((S + KT - 1) / KT, w_lo) : 0;
   const int n_tiles = ns + w_hi - w_lo;
   auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + w_lo; };
@@ -158,24 +166,11 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int qi = q0w + ln;                      // this lane's query row
   const bool row_ok = qi < T;
   const bool wave_active = q0w < T;
-  const int wave_key_lo = q0w - W + 1;          // first key any row of the wave sees (may be < 0)
+  int wave_key_lo = q0w - W + 1;                // first key any row of the wave sees (may be < 0; set again
+                                                // below where W is read late)
   const int wave_key_hi = min(q0w + 31, T - 1); // last key any row of the wave sees
 
-  // Q^T fragments (B operand of S^T = K Q^T): lane holds q[qi][16 s + 8 hl + 0..7].
-  const uint32_t slice_bytes = static_cast<uint32_t>(T) * C::kRowBytes;
-  bf16x8 qf[C::kSteps];
-  {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, slice_bytes);
-#pragma unroll
-    for (int s = 0; s < C::kSteps; ++s)
-      qf[s] = __builtin_bit_cast(bf16x8, load16(rq, static_cast<uint32_t>(qi) * C::kRowBytes + (16 * s + 8 * hl) * 2));
-    // Consume the fragments here, so that the compiler waits for these loads now
-    // rather than at their first use inside the loop, where its wait would also
-    // cover the LDS copies in flight.
-#pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) __asm__ volatile("" ::"v"(qf[s]));
-  }
-
+  bf16x8 qf[C::kSteps];  // Q^T fragments (B operand of S^T = K Q^T), loaded in the prologue below
   f32x16 acc[C::kBlocks];
 #pragma unroll
   for (int b = 0; b < C::kBlocks; ++b) acc[b] = f32x16{};
@@ -367,7 +362,27 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     return false;
   };
 
+  // Prologue: the first stage's copies go out before the Q rows are loaded, so
+  // that the two round trips overlap; waiting for the rows (which the compiler
+  // does where they are consumed, in issue order) then also covers the copies.
   issue_tile(tile_at(0), kst(0), vst(0));
+  // Q^T fragments: lane holds q[qi][16 s + 8 hl + 0..7].
+  {
+    const uint32_t slice_bytes = static_cast<uint32_t>(T) * C::kRowBytes;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(Qh, slice_bytes);
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s)
+      qf[s] = __builtin_bit_cast(bf16x8, load16(rq, static_cast<uint32_t>(qi) * C::kRowBytes + (16 * s + 8 * hl) * 2));
+    if constexpr (kLateW) {
+      W = win_eff[it.bh % H];
+      wave_key_lo = q0w - W + 1;
+    }
+    // Consume the fragments here, so that the compiler waits for these loads now
+    // rather than at their first use inside the loop, where its wait would also
+    // cover the LDS copies in flight.
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) __asm__ volatile("" ::"v"(qf[s]));
+  }
   if (C::kNS == 3 && n_tiles > 1) {
     issue_tile(tile_at(1), kst(1), vst(1));
     wait_vm_barrier(kFill);
