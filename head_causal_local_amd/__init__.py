@@ -503,3 +503,8 @@ def window_stats(windows: Sequence[int], T: int, sinks: Optional[Sequence[int]] 
 
 def cache_clear() -> None:
     lib().aah_cache_clear()
+
+
+def cache_entries() -> int:
+    """Work lists the library currently caches (all kinds; at most 64 per kind besides graph-pinned ones)."""
+    return int(lib().aah_cache_entries())

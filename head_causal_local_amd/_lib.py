@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 9
+ABI_VERSION = 10
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
@@ -27,7 +27,7 @@ EXPORTS = (
     "aah_plan_fwd_split", "aah_plan_bwd_split", "aah_attn_bwd_split_workspace_size", "aah_window_stats",
     "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
     "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode", "aah_attn_fwd_diag",
-    "aah_head_features_workspace_size", "aah_head_features", "aah_attn_decode_noalloc",
+    "aah_head_features_workspace_size", "aah_head_features", "aah_attn_decode_noalloc", "aah_cache_entries",
 )
 
 
@@ -107,6 +107,8 @@ def _declare(lib):
     lib.aah_window_stats.argtypes = [P_i32, P_i32, c_int, c_int, P_i64, P_double]
     lib.aah_cache_clear.restype = None
     lib.aah_cache_clear.argtypes = []
+    lib.aah_cache_entries.restype = c_int64
+    lib.aah_cache_entries.argtypes = []
     lib.aah_kv_cache_rows.restype = c_int64
     lib.aah_kv_cache_rows.argtypes = [P_i32, P_i32, c_int, c_int, c_int]
     lib.aah_attn_decode_workspace_size.restype = c_size_t

@@ -17,6 +17,7 @@
 #include <vector>
 
 #include "kernels.hpp"
+#include "plan_cache.hpp"
 #include "workplan.hpp"
 
 namespace {
@@ -105,9 +106,175 @@ aah_status check_tensor(const void* p, const char* name, size_t align) {
     if (st_ != AAH_OK) return st_;    \
   } while (0)
 
+// ------------------------------------------------------------------ device copies of work lists
+//
+// A work list reaches the device without synchronising it: its arrays are
+// packed into a ring of pinned host memory (one per device, allocated on
+// first use), a stream-ordered allocation (hipMallocAsync) receives them by
+// hipMemcpyAsync on the caller's stream, and an event marks the copy's end.
+// A later call on another stream waits for that event before its kernels read
+// the list.  A list evicted from its cache is released by hipFreeAsync on the
+// stream of the call that evicts it.  Lists larger than the ring (over a
+// quarter of a million work items) take the old path: hipMalloc and a
+// blocking hipMemcpy, and hipFree on release.
+
+struct DeviceBlob {
+  char* dev = nullptr;
+  hipEvent_t ready = nullptr;   // recorded on `stream` after the copy
+  hipStream_t stream = nullptr;
+  bool async = true;            // allocated with hipMallocAsync (else hipMalloc)
+};
+
+constexpr size_t kStagingBytes = size_t{4} << 20;  // pinned staging ring per device
+
+struct Staging {
+  char* host = nullptr;
+  size_t head = 0;
+  struct Region {
+    size_t begin, end;
+    hipEvent_t done;  // recorded after the copy out of [begin, end)
+  };
+  std::vector<Region> inflight;
+};
+
+std::mutex g_mu;  // guards every cache and the staging rings
+std::map<int, Staging> g_staging;
+
+size_t round_up256(size_t x) { return (x + 255) / 256 * 256; }
+
+bool stream_capturing(hipStream_t stream) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &st) != hipSuccess) return false;
+  return st != hipStreamCaptureStatusNone;
+}
+
+// Copies parts[i] (host pointer, bytes) to one device allocation, part i at (*offsets)[i] (256-byte
+// aligned), ordered on `stream`.  Called with g_mu held.
+aah_status upload_blob(int dev, const std::vector<std::pair<const void*, size_t>>& parts, hipStream_t stream,
+                       DeviceBlob* out, std::vector<size_t>* offsets) {
+  size_t total = 0;
+  offsets->clear();
+  for (const auto& p : parts) {
+    offsets->push_back(total);
+    total += round_up256(std::max<size_t>(p.second, 1));
+  }
+  DeviceBlob b;
+  b.stream = stream;
+  hipError_t e = hipEventCreateWithFlags(&b.ready, hipEventDisableTiming);
+  if (e != hipSuccess) return hip_fail(e, "hipEventCreate(work list)");
+  auto fail_blob = [&](hipError_t err, const char* what) {
+    if (b.dev != nullptr) (void)(b.async ? hipFreeAsync(b.dev, stream) : hipFree(b.dev));
+    (void)hipEventDestroy(b.ready);
+    return hip_fail(err, what);
+  };
+  if (total > kStagingBytes) {
+    b.async = false;
+    e = hipMalloc(reinterpret_cast<void**>(&b.dev), total);
+    if (e != hipSuccess) return fail_blob(e, "hipMalloc(work list)");
+    for (size_t i = 0; i < parts.size() && e == hipSuccess; ++i)
+      e = hipMemcpy(b.dev + (*offsets)[i], parts[i].first, parts[i].second, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipEventRecord(b.ready, stream);
+    if (e != hipSuccess) return fail_blob(e, "hipMemcpy(work list)");
+    *out = b;
+    return AAH_OK;
+  }
+  Staging& sg = g_staging[dev];
+  if (sg.host == nullptr) {
+    e = hipHostMalloc(reinterpret_cast<void**>(&sg.host), kStagingBytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      sg.host = nullptr;
+      return fail_blob(e, "hipHostMalloc(staging)");
+    }
+  }
+  if (sg.head + total > kStagingBytes) sg.head = 0;
+  const size_t begin = sg.head, end = begin + total;
+  // Regions this one overlaps must have been copied out (in practice long ago).
+  for (size_t i = 0; i < sg.inflight.size();) {
+    const Staging::Region& r = sg.inflight[i];
+    if (r.begin < end && begin < r.end) {
+      e = hipEventSynchronize(r.done);
+      (void)hipEventDestroy(r.done);
+      if (e != hipSuccess) return fail_blob(e, "hipEventSynchronize(staging)");
+      sg.inflight.erase(sg.inflight.begin() + static_cast<std::ptrdiff_t>(i));
+    } else {
+      ++i;
+    }
+  }
+  for (size_t i = 0; i < parts.size(); ++i) std::memcpy(sg.host + begin + (*offsets)[i], parts[i].first, parts[i].second);
+  hipEvent_t done = nullptr;
+  e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+  if (e != hipSuccess) return fail_blob(e, "hipEventCreate(staging)");
+  e = hipMallocAsync(reinterpret_cast<void**>(&b.dev), total, stream);
+  if (e == hipSuccess) e = hipMemcpyAsync(b.dev, sg.host + begin, total, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipEventRecord(done, stream);
+  if (e == hipSuccess) e = hipEventRecord(b.ready, stream);
+  if (e != hipSuccess) {
+    // Nothing may reuse the region before the device is done with it.
+    (void)hipEventSynchronize(done);
+    (void)hipEventDestroy(done);
+    return fail_blob(e, "hipMallocAsync / hipMemcpyAsync(work list)");
+  }
+  sg.inflight.push_back(Staging::Region{begin, end, done});
+  sg.head = end;
+  *out = b;
+  return AAH_OK;
+}
+
+// Releases a list evicted by a call on `stream` (in that stream's order).
+void release_blob(DeviceBlob& b, hipStream_t stream) {
+  if (b.dev != nullptr) (void)(b.async ? hipFreeAsync(b.dev, stream) : hipFree(b.dev));
+  if (b.ready != nullptr) (void)hipEventDestroy(b.ready);
+  b = DeviceBlob{};
+}
+
+// Before a call on `stream` uses a cached list: order it after the list's copy when that copy went out on
+// another stream.  Under graph capture no wait on an outside event is recorded; the copy must be done.
+aah_status order_after_upload(const DeviceBlob& b, hipStream_t stream, bool capturing) {
+  if (b.stream == stream) return AAH_OK;
+  if (capturing) {
+    const hipError_t q = hipEventQuery(b.ready);
+    if (q == hipSuccess) return AAH_OK;
+    return fail(AAH_ERR_UNSUPPORTED,
+                "the work list for these windows is still being copied on another stream; synchronise it before "
+                "capturing a graph that uses it");
+  }
+  const hipError_t e = hipStreamWaitEvent(stream, b.ready, 0);
+  return e == hipSuccess ? AAH_OK : hip_fail(e, "hipStreamWaitEvent(work list)");
+}
+
+// Looks key up in cache under g_mu: on a hit copies the entry to *out (pinning it when the stream is
+// capturing a graph, which will refer to it for good) and returns true.  A miss during capture is an
+// error (status in *st): building and uploading a list there would record the upload into the graph.
+template <class V>
+bool cache_lookup(aah::PlanLru<V>& cache, const std::vector<int64_t>& key, hipStream_t stream, bool capturing,
+                  V* out, aah_status* st) {
+  V* hit = cache.find(key);
+  *st = AAH_OK;
+  if (hit == nullptr) {
+    if (capturing)
+      *st = fail(AAH_ERR_UNSUPPORTED,
+                 "no cached work list for these windows and shape: run the same call once outside graph capture");
+    return capturing;
+  }
+  if (capturing) cache.pin(key);
+  *st = order_after_upload(hit->blob, stream, capturing);
+  if (*st == AAH_OK) *out = *hit;
+  return true;
+}
+
+template <class V>
+void cache_insert(aah::PlanLru<V>& cache, std::vector<int64_t> key, const V& value, hipStream_t stream) {
+  for (V& old : cache.insert(std::move(key), value)) release_blob(old.blob, stream);
+}
+
+// Work lists kept per cache (forward / backward lists, split lists, decoding plans): enough for the
+// layers of a model whose windows change at every control update, bounded for any run.
+constexpr size_t kCacheCapacity = 64;
+
 // ------------------------------------------------------------------ plan cache
 
 struct DevicePlan {
+  DeviceBlob blob;
   WorkItem* items = nullptr;
   int n_items = 0;
   int32_t* win = nullptr;   // effective windows int32[H], then effective sink sizes int32[H]
@@ -116,13 +283,12 @@ struct DevicePlan {
 
 enum PlanKind : int64_t { kPlanFwd = 0, kPlanBwd = 1 };
 
-std::mutex g_mu;
-std::map<std::vector<int64_t>, DevicePlan> g_cache;
+aah::PlanLru<DevicePlan> g_cache(kCacheCapacity);
 
 constexpr int kQueues = 8;  // MI355X has eight XCDs; workgroups are placed round-robin over them
 
 aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
-                    int row_tile, int col_tile, DevicePlan* out) {
+                    int row_tile, int col_tile, hipStream_t stream, DevicePlan* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -138,12 +304,10 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks,
   std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, row_tile, col_tile, kQueues, any_sink ? 1 : 0};
   key.insert(key.end(), win.begin(), win.end());
 
+  const bool capturing = stream_capturing(stream);
   std::lock_guard<std::mutex> lock(g_mu);
-  auto found = g_cache.find(key);
-  if (found != g_cache.end()) {
-    *out = found->second;
-    return AAH_OK;
-  }
+  aah_status st;
+  if (cache_lookup(g_cache, key, stream, capturing, out, &st)) return st;
   // Forward: row tile = query rows per item, col tile = keys per step.
   // Backward: row tile = keys per item, col tile = query rows per step.
   const std::vector<WorkItem> items =
@@ -152,22 +316,13 @@ aah_status get_plan(PlanKind kind, const int32_t* windows, const int32_t* sinks,
 
   DevicePlan p;
   p.n_items = static_cast<int>(items.size());
-  e = hipMalloc(&p.items, items.size() * sizeof(WorkItem));
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(work list)");
-  e = hipMalloc(&p.win, win.size() * sizeof(int32_t));
-  if (e != hipSuccess) {
-    (void)hipFree(p.items);
-    return hip_fail(e, "hipMalloc(windows)");
-  }
-  e = hipMemcpy(p.items, items.data(), items.size() * sizeof(WorkItem), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(p.win, win.data(), win.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(p.items);
-    (void)hipFree(p.win);
-    return hip_fail(e, "hipMemcpy(work list)");
-  }
+  std::vector<size_t> off;
+  AAH_TRY_INNER(upload_blob(dev, {{items.data(), items.size() * sizeof(WorkItem)}, {win.data(), win.size() * sizeof(int32_t)}},
+                            stream, &p.blob, &off));
+  p.items = reinterpret_cast<WorkItem*>(p.blob.dev + off[0]);
+  p.win = reinterpret_cast<int32_t*>(p.blob.dev + off[1]);
   p.sink = any_sink ? p.win + H : nullptr;
-  g_cache.emplace(std::move(key), p);
+  cache_insert(g_cache, std::move(key), p, stream);
   *out = p;
   return AAH_OK;
 }
@@ -253,13 +408,14 @@ int split_chunk_tiles(const int32_t* windows, int B, int H, int T, int d) {
 }
 
 struct SplitDevicePlan {
+  DeviceBlob blob;
   WorkItem* items = nullptr;
   int32_t* slots = nullptr;
   WorkItem* merges = nullptr;
   int32_t* win = nullptr;
   int n_items = 0, n_merges = 0, n_slots = 0;
 };
-std::map<std::vector<int64_t>, SplitDevicePlan> g_split_cache;
+aah::PlanLru<SplitDevicePlan> g_split_cache(kCacheCapacity);
 
 // Partial-result bytes of a split plan: accumulators, then (max, sum) pairs, each 256-byte aligned.
 size_t split_acc_bytes(int n_slots, int d) {
@@ -272,7 +428,7 @@ size_t split_workspace(int n_slots, int d) {
 
 // Split plan of a bf16 forward without sinks with chunk length L (> 0), uploaded once per key.
 // kind 0: query-stationary items (forward, dQ); kind 1: key-stationary items (dK/dV, H_kv = H, no sinks).
-aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T, int d, int L,
+aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T, int d, int L, hipStream_t stream,
                           SplitDevicePlan* out, int kind = 0) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -281,12 +437,10 @@ aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T,
   for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
   std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, d, L};
   key.insert(key.end(), win.begin(), win.end());
+  const bool capturing = stream_capturing(stream);
   std::lock_guard<std::mutex> lock(g_mu);
-  auto found = g_split_cache.find(key);
-  if (found != g_split_cache.end()) {
-    *out = found->second;
-    return AAH_OK;
-  }
+  aah_status st;
+  if (cache_lookup(g_split_cache, key, stream, capturing, out, &st)) return st;
   const aah::SplitPlan sp =
       kind == 0 ? aah::plan_forward_split(windows, B, H, H_kv, T, aah::kFwdBf16RowTile, aah::kFwdBf16ColTile, kQueues, L)
                 : aah::plan_backward_split(windows, B, H, T, aah::kBwdBf16ColTile, aah::kBwdBf16RowTile, kQueues, L);
@@ -294,29 +448,18 @@ aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T,
   p.n_items = static_cast<int>(sp.items.size());
   p.n_merges = static_cast<int>(sp.merges.size());
   p.n_slots = sp.n_slots;
-  auto upload = [](const void* host, size_t bytes, void** dev_ptr) {
-    hipError_t err = hipMalloc(dev_ptr, bytes);
-    if (err != hipSuccess) return err;
-    err = hipMemcpy(*dev_ptr, host, bytes, hipMemcpyHostToDevice);
-    if (err != hipSuccess) {
-      (void)hipFree(*dev_ptr);
-      *dev_ptr = nullptr;
-    }
-    return err;
-  };
-  e = upload(sp.items.data(), sp.items.size() * sizeof(WorkItem), reinterpret_cast<void**>(&p.items));
-  if (e == hipSuccess) e = upload(sp.slot.data(), sp.slot.size() * sizeof(int32_t), reinterpret_cast<void**>(&p.slots));
-  if (e == hipSuccess)
-    e = upload(sp.merges.data(), std::max<size_t>(1, sp.merges.size()) * sizeof(WorkItem),
-               reinterpret_cast<void**>(&p.merges));
-  if (e == hipSuccess) e = upload(win.data(), win.size() * sizeof(int32_t), reinterpret_cast<void**>(&p.win));
-  if (e != hipSuccess) {
-    for (void* ptr : {static_cast<void*>(p.items), static_cast<void*>(p.slots), static_cast<void*>(p.merges),
-                      static_cast<void*>(p.win)})
-      if (ptr != nullptr) (void)hipFree(ptr);
-    return hip_fail(e, "hipMalloc / hipMemcpy(split plan)");
-  }
-  g_split_cache.emplace(std::move(key), p);
+  std::vector<size_t> off;
+  AAH_TRY_INNER(upload_blob(dev,
+                            {{sp.items.data(), sp.items.size() * sizeof(WorkItem)},
+                             {sp.slot.data(), sp.slot.size() * sizeof(int32_t)},
+                             {sp.merges.data(), sp.merges.size() * sizeof(WorkItem)},
+                             {win.data(), win.size() * sizeof(int32_t)}},
+                            stream, &p.blob, &off));
+  p.items = reinterpret_cast<WorkItem*>(p.blob.dev + off[0]);
+  p.slots = reinterpret_cast<int32_t*>(p.blob.dev + off[1]);
+  p.merges = reinterpret_cast<WorkItem*>(p.blob.dev + off[2]);
+  p.win = reinterpret_cast<int32_t*>(p.blob.dev + off[3]);
+  cache_insert(g_split_cache, std::move(key), p, stream);
   *out = p;
   return AAH_OK;
 }
@@ -381,13 +524,13 @@ struct BwdSplitLayout {
 // Layout of a split backward's workspace: [nl2 | nD | dQ partials | dK/dV partials].  Returns false when
 // splitting does not apply (dtype, grouped heads, sinks, enough items, or a failed plan upload).
 bool bwd_split_layout(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
-                      aah_dtype dt, BwdSplitLayout* lay) {
+                      aah_dtype dt, hipStream_t stream, BwdSplitLayout* lay) {
   if (dt != AAH_BF16 || H_kv != H || any_sink(windows, sinks, H, T)) return false;
   lay->q_L = chunk_len(bwd_item_tiles(false, windows, B, H, T), resident_bwd(false, d));
   lay->k_L = chunk_len(bwd_item_tiles(true, windows, B, H, T), resident_bwd(true, d));
   if (lay->q_L == 0 && lay->k_L == 0) return false;
-  if (lay->q_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->q_L, &lay->q, 0) != AAH_OK) return false;
-  if (lay->k_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->k_L, &lay->k, 1) != AAH_OK) return false;
+  if (lay->q_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->q_L, stream, &lay->q, 0) != AAH_OK) return false;
+  if (lay->k_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->k_L, stream, &lay->k, 1) != AAH_OK) return false;
   const size_t rows = static_cast<size_t>(aah::kBwdBf16RowTile) * d * sizeof(float);
   lay->q_off = 2 * round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256);
   lay->k_off = lay->q_off + round_up(static_cast<size_t>(lay->q_L > 0 ? lay->q.n_slots : 0) * rows, 256);
@@ -416,6 +559,7 @@ aah_status check_workspace(const void* workspace, size_t workspace_bytes, int B,
 // ------------------------------------------------------------------ decode plans
 
 struct DecodePlan {
+  DeviceBlob blob;
   aah::DecodeChunk* chunks = nullptr;
   // kv_off[H_kv], kv_sink[H_kv], kv_ring[H_kv], kv_first[H_kv + 1], q_cap[H], q_sink[H]
   int32_t* tables = nullptr;
@@ -431,7 +575,7 @@ struct DecodePlan {
   }
 };
 
-std::map<std::vector<int64_t>, DecodePlan> g_decode_cache;
+aah::PlanLru<DecodePlan> g_decode_cache(kCacheCapacity);
 
 // Per query head: C_h = min(W_h, T_max) and the effective sink min(S_h, T_max - C_h) (sinks past it are
 // always inside the window); per key/value head: the largest of each over its query heads.
@@ -469,7 +613,7 @@ int64_t decode_rows(const int32_t* windows, const int32_t* sinks, int H, int H_k
 }
 
 aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, int H_kv, int T_max,
-                           const DecodePlan** out) {
+                           hipStream_t stream, DecodePlan* out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -477,12 +621,10 @@ aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, 
   std::vector<int64_t> key = {dev, H, H_kv, T_max};
   key.insert(key.end(), sh.cap.begin(), sh.cap.end());
   key.insert(key.end(), sh.sink.begin(), sh.sink.end());
+  const bool capturing = stream_capturing(stream);
   std::lock_guard<std::mutex> lock(g_mu);
-  auto found = g_decode_cache.find(key);
-  if (found != g_decode_cache.end()) {
-    *out = &found->second;
-    return AAH_OK;
-  }
+  aah_status st;
+  if (cache_lookup(g_decode_cache, key, stream, capturing, out, &st)) return st;
   DecodePlan p;
   p.H = H;
   p.H_kv = H_kv;
@@ -507,22 +649,15 @@ aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, 
   p.n_chunks = static_cast<int>(chunks.size());
   p.host_sink.assign(tables.begin() + H_kv, tables.begin() + 2 * H_kv);
   p.host_ring.assign(tables.begin() + 2 * H_kv, tables.begin() + 3 * H_kv);
-  e = hipMalloc(&p.chunks, chunks.size() * sizeof(aah::DecodeChunk));
-  if (e != hipSuccess) return hip_fail(e, "hipMalloc(decode chunks)");
-  e = hipMalloc(&p.tables, tables.size() * sizeof(int32_t));
-  if (e != hipSuccess) {
-    (void)hipFree(p.chunks);
-    return hip_fail(e, "hipMalloc(decode tables)");
-  }
-  e = hipMemcpy(p.chunks, chunks.data(), chunks.size() * sizeof(aah::DecodeChunk), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemcpy(p.tables, tables.data(), tables.size() * sizeof(int32_t), hipMemcpyHostToDevice);
-  if (e != hipSuccess) {
-    (void)hipFree(p.chunks);
-    (void)hipFree(p.tables);
-    return hip_fail(e, "hipMemcpy(decode tables)");
-  }
-  auto it = g_decode_cache.emplace(std::move(key), std::move(p)).first;
-  *out = &it->second;
+  std::vector<size_t> at;
+  AAH_TRY_INNER(upload_blob(dev,
+                            {{chunks.data(), chunks.size() * sizeof(aah::DecodeChunk)},
+                             {tables.data(), tables.size() * sizeof(int32_t)}},
+                            stream, &p.blob, &at));
+  p.chunks = reinterpret_cast<aah::DecodeChunk*>(p.blob.dev + at[0]);
+  p.tables = reinterpret_cast<int32_t*>(p.blob.dev + at[1]);
+  cache_insert(g_decode_cache, std::move(key), p, stream);
+  *out = std::move(p);
   return AAH_OK;
 }
 
@@ -602,7 +737,7 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
   const int L = split_chunk_tiles(windows, B, H, T, d);
   if (L == 0) return 0;
   SplitDevicePlan sp;
-  if (get_split_plan(windows, B, H, H_kv, T, d, L, &sp) != AAH_OK) return 0;
+  if (get_split_plan(windows, B, H, H_kv, T, d, L, nullptr, &sp) != AAH_OK) return 0;
   return split_workspace(sp.n_slots, d);
 }
 
@@ -611,7 +746,7 @@ size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* 
   if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
   g_detail.clear();
   BwdSplitLayout lay;
-  return bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) ? lay.total : 0;
+  return bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, nullptr, &lay) ? lay.total : 0;
 }
 
 aah_status aah_tile_shape(aah_dtype dt, int d, int is_bwd, int* row_tile, int* col_tile) {
@@ -657,7 +792,7 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
                     : 0;
   if (L > 0) {
     SplitDevicePlan sp;
-    AAH_TRY(get_split_plan(windows, B, H, H_kv, T, d, L, &sp));
+    AAH_TRY(get_split_plan(windows, B, H, H_kv, T, d, L, st, &sp));
     if (workspace_bytes >= split_workspace(sp.n_slots, d)) {
       float* part_acc = static_cast<float*>(workspace);
       float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_acc_bytes(sp.n_slots, d));
@@ -668,7 +803,7 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
       return AAH_OK;
     }
   }
-  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, st, &plan));
   if (dt == AAH_BF16)
     e = aah::launch_fwd_bf16(q, k, v, o, lse, ent, onorm, plan.items, plan.n_items, plan.win, plan.sink, s, nullptr,
                              st);
@@ -743,7 +878,7 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, nullptr, B, H, H_kv, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, nullptr, B, H, H_kv, T, row, col, static_cast<hipStream_t>(stream), &plan));
   const hipError_t e = aah::launch_head_features(q, k, v, dt == AAH_BF16, row_entropy, row_onorm, plan.win, B, H,
                                                  H_kv, T, d, alpha, init != 0, features, features_ema,
                                                  static_cast<double*>(workspace), static_cast<hipStream_t>(stream));
@@ -772,7 +907,7 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
   int row = 0, col = 0;
   bwd_tiles(dt, &row, &col);
   BwdSplitLayout lay;
-  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) && lay.k_L > 0 && workspace_bytes >= lay.total) {
+  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, st, &lay) && lay.k_L > 0 && workspace_bytes >= lay.total) {
     const aah::BwdSplit split{lay.k.slots, lay.k.merges, lay.k.n_merges,
                               reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.k_off)};
     const hipError_t e = aah::launch_bwd_dkdv_bf16_split(q, k, v, dout, nl2, nd, dk, dv, lay.k.items, lay.k.n_items,
@@ -781,7 +916,7 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
     return AAH_OK;
   }
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanBwd, windows, sinks, B, H, H_kv, T, row, col, st, &plan));
   hipError_t e;
   if (dt == AAH_BF16)
     e = aah::launch_bwd_dkdv_bf16(q, k, v, dout, nl2, nd, dk, dv, plan.items, plan.n_items, plan.win, plan.sink, s,
@@ -817,7 +952,7 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   int row = 0, col = 0;
   fwd_tiles(dt, &row, &col);  // dQ walks the forward's (query tile, key tiles) items
   BwdSplitLayout lay;
-  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, &lay) && lay.q_L > 0 && workspace_bytes >= lay.total) {
+  if (bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, st, &lay) && lay.q_L > 0 && workspace_bytes >= lay.total) {
     const aah::BwdSplit split{lay.q.slots, lay.q.merges, lay.q.n_merges,
                               reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.q_off)};
     const hipError_t e = aah::launch_bwd_dq_bf16_split(q, k, v, o, dout, lse, nl2, nd, dq, lay.q.items,
@@ -826,7 +961,7 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
     return AAH_OK;
   }
   DevicePlan plan;
-  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, &plan));
+  AAH_TRY(get_plan(kPlanFwd, windows, sinks, B, H, H_kv, T, row, col, st, &plan));
   hipError_t e;
   if (dt == AAH_BF16) {
     // One kernel: D and the workspace rows come out of the dQ kernel's prologue.
@@ -894,10 +1029,10 @@ aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* window
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(kcache, "kcache", 16));
   AAH_TRY(check_tensor(vcache, "vcache", 16));
-  const DecodePlan* plan = nullptr;
-  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, &plan));
+  DecodePlan plan;
+  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, static_cast<hipStream_t>(stream), &plan));
   const hipError_t e =
-      aah::launch_cache_fill_bf16(k, v, kcache, vcache, plan->view(), B, T, d, static_cast<hipStream_t>(stream));
+      aah::launch_cache_fill_bf16(k, v, kcache, vcache, plan.view(), B, T, d, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "cache fill launch");
   return AAH_OK;
 }
@@ -922,10 +1057,10 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
     return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
                 need);
   if (!aligned(workspace, 256)) return fail(AAH_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
-  const DecodePlan* plan = nullptr;
-  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, &plan));
+  DecodePlan plan;
+  AAH_TRY(get_decode_plan(windows, sinks, H, H_kv, T_max, static_cast<hipStream_t>(stream), &plan));
   const hipError_t e = aah::launch_decode_bf16(
-      q, k_new, v_new, kcache, vcache, pos, plan->view(), B, T_max, d, scale, o, lse,
+      q, k_new, v_new, kcache, vcache, pos, plan.view(), B, T_max, d, scale, o, lse,
       static_cast<int32_t*>(workspace),
       reinterpret_cast<float*>(static_cast<char*>(workspace) + decode_counter_bytes(B, H_kv)),
       static_cast<hipStream_t>(stream));
@@ -1083,23 +1218,28 @@ aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, in
 
 void aah_cache_clear(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  for (auto& kv : g_cache) {
-    (void)hipFree(kv.second.items);
-    (void)hipFree(kv.second.win);
+  // hipFree synchronises the device: nothing still queued can be using the lists afterwards.
+  auto drop = [](DeviceBlob& b) {
+    if (b.dev != nullptr) (void)hipFree(b.dev);
+    if (b.ready != nullptr) (void)hipEventDestroy(b.ready);
+    b = DeviceBlob{};
+  };
+  for (auto& p : g_cache.clear()) drop(p.blob);
+  for (auto& p : g_split_cache.clear()) drop(p.blob);
+  for (auto& p : g_decode_cache.clear()) drop(p.blob);
+  for (auto& kv : g_staging) {
+    for (auto& r : kv.second.inflight) {
+      (void)hipEventSynchronize(r.done);
+      (void)hipEventDestroy(r.done);
+    }
+    kv.second.inflight.clear();
+    kv.second.head = 0;
   }
-  g_cache.clear();
-  for (auto& kv : g_split_cache) {
-    (void)hipFree(kv.second.items);
-    (void)hipFree(kv.second.slots);
-    (void)hipFree(kv.second.merges);
-    (void)hipFree(kv.second.win);
-  }
-  g_split_cache.clear();
-  for (auto& kv : g_decode_cache) {
-    (void)hipFree(kv.second.chunks);
-    (void)hipFree(kv.second.tables);
-  }
-  g_decode_cache.clear();
+}
+
+int64_t aah_cache_entries(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  return static_cast<int64_t>(g_cache.size() + g_split_cache.size() + g_decode_cache.size());
 }
 
 }  // extern "C"

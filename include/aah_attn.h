@@ -43,13 +43,24 @@
  *     ignored; lse then covers the sink keys too.
  *   - `stream` is a hipStream_t passed as an opaque pointer (NULL = the null
  *     stream).  Calls only enqueue work on it and return; they never
- *     synchronise the device, except that the first call for a new
- *     (B, H, T, dtype, d, windows) combination builds its work list on the
- *     host and uploads it once (hipMalloc + hipMemcpy), to be reused by every
- *     later call with the same combination.
+ *     synchronise the device.  The first call for a new (B, H, T, dtype, d,
+ *     windows, sinks) combination builds its work list on the host and
+ *     uploads it on `stream` (a stream-ordered allocation filled by
+ *     hipMemcpyAsync from pinned staging memory); later calls with the same
+ *     combination reuse it, and a call on another stream first waits for that
+ *     upload.  Work lists larger than 4 MiB are uploaded synchronously.
+ *   - The library keeps at most 64 work lists per kind (forward / backward,
+ *     split, decoding).  A new one beyond that replaces the least recently
+ *     used, which is released in the order of the stream of the call that
+ *     replaces it: a caller that runs calls on several streams concurrently
+ *     with more distinct window vectors in flight than that must order those
+ *     streams.  During HIP graph capture no work list is built (AAH_ERR_
+ *     UNSUPPORTED for a combination not yet cached: run it once outside the
+ *     capture); one used there is kept until aah_cache_clear(), since the
+ *     graph refers to it.
  *   - The caller allocates and owns every tensor, the workspace and the
  *     stream.  The library owns only its cached work lists, released by
- *     aah_cache_clear().
+ *     aah_cache_clear(), and the staging memory they are uploaded through.
  *   - Every argument check runs before any HIP call; on an error nothing is
  *     written to any output and the call returns a status other than AAH_OK.
  *     aah_last_error_detail() then describes the failure (thread-local).
@@ -67,7 +78,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 9
+#define AAH_ABI_VERSION 10
 
 typedef enum {
   AAH_OK = 0,
@@ -410,9 +421,13 @@ aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int
 aah_status aah_window_stats(const int32_t* windows, const int32_t* sinks, int H, int T,
                             int64_t* pairs_per_batch, double* acr);
 
-/* Free every cached device work list.  Not thread-safe against concurrent
- * aah_attn_* calls that may be using them. */
+/* Free every cached device work list (synchronising the device).  Not
+ * thread-safe against concurrent aah_attn_* calls that may be using them. */
 void aah_cache_clear(void);
+
+/* Number of work lists currently cached (all kinds together); each kind holds
+ * at most 64 besides those pinned by graph capture. */
+int64_t aah_cache_entries(void);
 
 #ifdef __cplusplus
 }
