@@ -91,32 +91,61 @@ struct Cfg {
 __device__ constexpr int reg_row(int r) { return 8 * (r >> 2) + (r & 3); }
 
 // Lane-constant LDS offsets shared by both kernels, for a row-major swizzled tile:
-//   rd[st]: MFMA A operand read with ds_read_b128 -- row ln, logical chunk 2 st + hl;
-//   tr[half][b]: ds_read_b64_tr_b16 of row 4 hl + s16 / 4 + 8 half (+ 16 step),
+//   rd(st): MFMA A operand read with ds_read_b128 -- row ln, logical chunk 2 st + hl;
+//   tr(half, b): ds_read_b64_tr_b16 of row 4 hl + s16 / 4 + 8 half (+ 16 step),
 //           columns 32 b + 16 (g & 1) + 4 (s16 & 3) .. + 3 (the swizzle depends on
-//           the row modulo 16, so each half has its own offset);
+//           the row modulo 16, so each half has its own offset).
+// Up to d = 64 every offset is kept in a register.  At d = 128 that would be
+// 16 registers, which the dK/dV kernel cannot spare (it needs two waves per
+// SIMD in 256), so only bases are kept: with the swizzle an XOR of the chunk
+// index, rd(st) = base + 32 (st ^ z1) and tr(half, b) = base_half + 64 (b ^ zh),
+// one v_xad_u32 per use.
 // (The copy offsets, dma_off below, are recomputed per copy: cheap, and they
 // would otherwise hold registers through the whole loop.)
 template <int D>
 struct Offsets {
-  uint32_t rd[Cfg<D>::kSteps];
-  uint32_t tr[2][Cfg<D>::kBlocks];
+  using C = Cfg<D>;
+  static constexpr bool kCompact = D >= 128;
+  uint32_t rd_[kCompact ? 1 : C::kSteps];
+  uint32_t tr_[2][kCompact ? 1 : C::kBlocks];
+  uint32_t rdx = 0, trx[2] = {0, 0};  // compact form: the XOR masks, pre-shifted
   __device__ Offsets(int /*wave*/, int lane) {
-    using C = Cfg<D>;
     constexpr int NC = C::kNC;
     const int hl = lane >> 5, ln = lane & 31, g = lane >> 4, s16 = lane & 15;
+    if constexpr (kCompact) {
+      const int z = swz<NC>(ln);
+      rd_[0] = static_cast<uint32_t>(ln * C::kRowBytes + 16 * (hl ^ (z & 1)));
+      rdx = static_cast<uint32_t>((z >> 1) << 5);
 #pragma unroll
-    for (int st = 0; st < C::kSteps; ++st)
-      rd[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-#pragma unroll
-      for (int b = 0; b < C::kBlocks; ++b) {
+      for (int half = 0; half < 2; ++half) {
         const int trow = 4 * hl + (s16 >> 2) + 8 * half;
-        const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
-        tr[half][b] =
-            static_cast<uint32_t>(trow * C::kRowBytes + (((col >> 3) ^ swz<NC>(trow)) * 16) + (col & 7) * 2);
+        const int zt = swz<NC>(trow);
+        const int c0 = 2 * (g & 1) + ((s16 & 3) >> 1);
+        tr_[half][0] = static_cast<uint32_t>(trow * C::kRowBytes + 16 * (c0 ^ (zt & 3)) + 8 * (s16 & 1));
+        trx[half] = static_cast<uint32_t>((zt >> 2) << 6);
       }
+    } else {
+#pragma unroll
+      for (int st = 0; st < C::kSteps; ++st)
+        rd_[st] = static_cast<uint32_t>(ln * C::kRowBytes + (((2 * st + hl) ^ swz<NC>(ln)) * 16));
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int b = 0; b < C::kBlocks; ++b) {
+          const int trow = 4 * hl + (s16 >> 2) + 8 * half;
+          const int col = 32 * b + 16 * (g & 1) + 4 * (s16 & 3);
+          tr_[half][b] =
+              static_cast<uint32_t>(trow * C::kRowBytes + (((col >> 3) ^ swz<NC>(trow)) * 16) + (col & 7) * 2);
+        }
+    }
+  }
+  __device__ __forceinline__ uint32_t rd(int st) const {
+    if constexpr (kCompact) return ((static_cast<uint32_t>(st) << 5) ^ rdx) + rd_[0];
+    else return rd_[st];
+  }
+  __device__ __forceinline__ uint32_t tr(int half, int b) const {
+    if constexpr (kCompact) return ((static_cast<uint32_t>(b) << 6) ^ trx[half]) + tr_[half][0];
+    else return tr_[half][b];
   }
 };
 
@@ -159,18 +188,20 @@ struct StepCursor {
 };
 
 template <int D, bool SINK, bool GQA>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 3 : 2)))
 void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
                      const bf16* __restrict__ dO, const float* __restrict__ NL2, const float* __restrict__ ND,
                      bf16* __restrict__ dK, bf16* __restrict__ dV, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
                      int T, float scale, const int32_t* __restrict__ slots, float* __restrict__ part) {
   using C = Cfg<D>;
-  // Three-stage ring; stage = {Q tile, dO tile, nl2 row, nD row}.
+  // Ring of stages = {Q tile, dO tile, nl2 row, nD row}: three (copies two steps ahead) up to d = 64; at
+  // d = 128 a stage is 33 KiB and two stages let two workgroups share a CU (with at most 256 registers
+  // per lane, two waves per SIMD).
   constexpr int kStage = 2 * C::kTileBytes + 2 * kStep * 4;
-  __shared__ __attribute__((aligned(1024))) char ring0[kStage];
-  __shared__ __attribute__((aligned(1024))) char ring1[kStage];
-  __shared__ __attribute__((aligned(1024))) char ring2[kStage];
+  constexpr int kStages = D >= 128 ? 2 : 3;
+  constexpr int kStagePitch = (kStage + 1023) / 1024 * 1024;  // every stage starts 1 KiB aligned
+  __shared__ __attribute__((aligned(1024))) char ring[kStages][kStagePitch];
   constexpr int kG = C::kTileBytes, kL = 2 * C::kTileBytes, kDd = kL + kStep * 4;  // offsets in a stage
 
   const WorkItem it = items[blockIdx.x];
@@ -194,6 +225,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const Offsets<D> off(wave, lane);
 
   bf16x8 kf[C::kSteps], vf[C::kSteps];
+  // At d = 128 the last two K fragments and the last V fragment of each lane wait in LDS between their
+  // uses (12 KiB), which keeps the kernel within 256 registers per lane without spilling to memory.
+  constexpr int kStash = D >= 128 ? 1 : 0;
+  __shared__ __attribute__((aligned(16))) bf16x8 stash[3][kStash ? kThreads : 1];
 
   // Stage fill: Q and dO tiles (every wave its share), nl2 row (wave 0), nD row (wave 1) of the query
   // head whose rows start at qb (elements) and rb (rows).
@@ -247,8 +282,11 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     }
 #pragma unroll
     for (int k = 0; k < C::kSteps; ++k) {
-      s = mfma(*reinterpret_cast<const bf16x8*>(qs + 32 * mb * C::kRowBytes + off.rd[k]), kf[k], s);
-      dp = mfma(*reinterpret_cast<const bf16x8*>(gs + 32 * mb * C::kRowBytes + off.rd[k]), vf[k], dp);
+      // stash[0]: K fragment kSteps - 1, stash[1]: K fragment kSteps - 2, stash[2]: V fragment kSteps - 1.
+      const bf16x8 kb = kStash && k >= C::kSteps - 2 ? stash[C::kSteps - 1 - k][tid] : kf[k];
+      const bf16x8 vb = kStash && k == C::kSteps - 1 ? stash[2][tid] : vf[k];
+      s = mfma(*reinterpret_cast<const bf16x8*>(qs + 32 * mb * C::kRowBytes + off.rd(k)), kb, s);
+      dp = mfma(*reinterpret_cast<const bf16x8*>(gs + 32 * mb * C::kRowBytes + off.rd(k)), vb, dp);
     }
   };
   // P and dS (bf16 B operands; step h takes registers 8 h .. 8 h + 7).
@@ -269,8 +307,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
 #pragma unroll
       for (int b = 0; b < C::kBlocks; ++b) {
-        dv[b] = mfma(read_tr(gs + row0 + off.tr[0][b], gs + row0 + off.tr[1][b]), pf[h], dv[b]);
-        dk[b] = mfma(read_tr(qs + row0 + off.tr[0][b], qs + row0 + off.tr[1][b]), df[h], dk[b]);
+        dv[b] = mfma(read_tr(gs + row0 + off.tr(0, b), gs + row0 + off.tr(1, b)), pf[h], dv[b]);
+        dk[b] = mfma(read_tr(qs + row0 + off.tr(0, b), qs + row0 + off.tr(1, b)), df[h], dk[b]);
       }
     }
   };
@@ -333,41 +371,45 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     fill_rows(qh * T * D, qh * T, cu.qt, st);
   };
 
-  // Ring: step v uses stage v % 3 and fills the stage of step v + 2.
-  auto step = [&](int v, const char* cur, char* nxt2) __attribute__((always_inline)) {
+  // Ring: step v uses stage v % kStages and fills the stage of step v + kStages - 1, which held step v - 1:
+  // the barrier that ended step v - 1 saw every wave finish with it.  A step ends once the next step's
+  // copies have landed (each wave waits for its own, then the barrier); with three stages the copies
+  // issued in this step may stay in flight.
+  constexpr int kAhead = kStages - 1;
+  auto step = [&](int v, const char* cur, char* nxtf) __attribute__((always_inline)) {
     if constexpr (GQA) {
-      const bool more = v + 2 < n_steps;
+      const bool more = v + kAhead < n_steps;
       if (more) {
-        fill_cursor(fc, nxt2);
+        fill_cursor(fc, nxtf);
         advance(fc);
       }
       do_step(cur, dc.qt * kStep, dc.W, dc.S);
       advance(dc);
       if (v + 1 >= n_steps) return true;
-      wait_barrier(more);
+      wait_barrier(kStages == 3 && more);
       return false;
     } else {
       const int qt = it.lo + v;
-      const bool more = qt + 2 < it.hi;
-      if (more) fill(qt + 2, nxt2);
+      const bool more = qt + kAhead < it.hi;
+      if (more) fill(qt + kAhead, nxtf);
       do_step(cur, qt * kStep, W, S);
       if (qt + 1 >= it.hi) return true;
-      wait_barrier(more);
+      wait_barrier(kStages == 3 && more);
       return false;
     }
   };
-  // Prologue: the first two stages' copies and the K / V row loads all go out
-  // before the first wait, so their latencies overlap.
+  // Prologue: the first kStages - 1 stages' copies and the K / V row loads all
+  // go out before the first wait, so their latencies overlap.
   if constexpr (GQA) {
-    fill_cursor(fc, ring0);
+    fill_cursor(fc, ring[0]);
     advance(fc);
-    if (n_steps > 1) {
-      fill_cursor(fc, ring1);
+    if (kStages == 3 && n_steps > 1) {
+      fill_cursor(fc, ring[1]);
       advance(fc);
     }
   } else {
-    fill(it.lo, ring0);
-    if (it.lo + 1 < it.hi) fill(it.lo + 1, ring1);
+    fill(it.lo, ring[0]);
+    if (kStages == 3 && it.lo + 1 < it.hi) fill(it.lo + 1, ring[1]);
   }
   // K and V rows (B operands of S = Q K^T and dP = dO V^T): lane holds dims
   // 16 st + 8 hl + 0..7; K premultiplied by c.
@@ -387,12 +429,24 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     // the copies above) then sits before the loop, not inside it.
 #pragma unroll
     for (int st = 0; st < C::kSteps; ++st) __asm__ volatile("" ::"v"(kf[st]), "v"(vf[st]));
+    if constexpr (kStash) {
+      stash[0][tid] = kf[C::kSteps - 1];
+      stash[1][tid] = kf[C::kSteps - 2];
+      stash[2][tid] = vf[C::kSteps - 1];
+    }
   }
   wait_vm_barrier(0);
-  for (int v = 0;; v += 3) {
-    if (step(v, ring0, ring2)) break;
-    if (step(v + 1, ring1, ring0)) break;
-    if (step(v + 2, ring2, ring1)) break;
+  if constexpr (kStages == 3) {
+    for (int v = 0;; v += 3) {
+      if (step(v, ring[0], ring[2])) break;
+      if (step(v + 1, ring[1], ring[0])) break;
+      if (step(v + 2, ring[2], ring[1])) break;
+    }
+  } else {
+    for (int v = 0;; v += 2) {
+      if (step(v, ring[0], ring[1])) break;
+      if (step(v + 1, ring[1], ring[0])) break;
+    }
   }
 
   if (key >= T) return;
@@ -542,8 +596,8 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
     f32x16 s = cl16, dp = nd16;
 #pragma unroll
     for (int k = 0; k < C::kSteps; ++k) {
-      s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd[k]), qf[k], s);
-      dp = mfma(*reinterpret_cast<const bf16x8*>(vs + 32 * mb * C::kRowBytes + off.rd[k]), gf[k], dp);
+      s = mfma(*reinterpret_cast<const bf16x8*>(ks + 32 * mb * C::kRowBytes + off.rd(k)), qf[k], s);
+      dp = mfma(*reinterpret_cast<const bf16x8*>(vs + 32 * mb * C::kRowBytes + off.rd(k)), gf[k], dp);
     }
     // Register r holds key kb + 4 hl + reg_row(r), visible iff lim - W < reg_row(r) <= lim
     // (or reg_row(r) < sl, a sink, with reg_row(r) <= lim).
@@ -570,7 +624,7 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
       const int row0 = (32 * mb + 16 * h) * C::kRowBytes;
 #pragma unroll
       for (int b = 0; b < C::kBlocks; ++b)
-        acc[b] = mfma(read_tr(ks + row0 + off.tr[0][b], ks + row0 + off.tr[1][b]), df[h], acc[b]);
+        acc[b] = mfma(read_tr(ks + row0 + off.tr(0, b), ks + row0 + off.tr(1, b)), df[h], acc[b]);
     }
   };
 

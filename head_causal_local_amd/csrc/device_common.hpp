@@ -66,6 +66,20 @@ __device__ inline i32x4 rsrc_words(const void* p, uint32_t bytes) {
   return r;
 }
 
+// The resource words as wave-uniform values.  They always are uniform (built
+// from kernel arguments and workgroup-uniform indices), but under register
+// pressure the compiler may keep them in vector registers, which the "s"
+// operands of the copy instructions below cannot take; reading the first lane
+// makes them scalar again (and costs nothing when they already are).
+__device__ inline i32x4 uniform(const i32x4& r) {
+  i32x4 u;
+  u[0] = __builtin_amdgcn_readfirstlane(r[0]);
+  u[1] = __builtin_amdgcn_readfirstlane(r[1]);
+  u[2] = __builtin_amdgcn_readfirstlane(r[2]);
+  u[3] = __builtin_amdgcn_readfirstlane(r[3]);
+  return u;
+}
+
 // Asynchronous copy of 16 bytes per lane from a buffer straight into LDS
 // (buffer_load_dwordx4 ... lds): lane i's bytes land at lds_base + 16 i, where
 // lds_base must be uniform across the wave.  Loads past the resource's range
@@ -78,7 +92,7 @@ __device__ inline void dma16(const i32x4& rsrc, const void* lds_base, uint32_t b
       (const __attribute__((address_space(3))) char*)(lds_base)));
   __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                    :
-                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(rsrc)
+                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(uniform(rsrc))
                    : "memory", "m0");
 }
 
@@ -89,7 +103,7 @@ __device__ inline void dma4(const i32x4& rsrc, const void* lds_base, uint32_t by
       (const __attribute__((address_space(3))) char*)(lds_base)));
   __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                    :
-                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(rsrc)
+                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(uniform(rsrc))
                    : "memory", "m0");
 }
 
