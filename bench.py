@@ -229,15 +229,19 @@ COPY_BYTES = 512 * 1024 * 1024
 
 
 def calibrate_copy(steps):
-    """A plain copy of COPY_BYTES: counter readings on it convert FETCH_SIZE/WRITE_SIZE to bytes."""
+    """Kernels of known traffic whose counter readings convert FETCH_SIZE / WRITE_SIZE to bytes: a fill that
+    writes COPY_BYTES, a plain copy that reads and writes COPY_BYTES, and a sum that only reads them."""
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
+    total = torch.zeros((), dtype=torch.float32, device="cuda")
     for _ in range(steps):
         dst.copy_(src)
+    for _ in range(steps):
+        total += src.sum()
     torch.cuda.synchronize()
-    print(json.dumps({"calibration": "device copy", "bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
-                      "launches": steps}), flush=True)
+    print(json.dumps({"calibration": "device fill, copy and sum", "bytes_read": COPY_BYTES,
+                      "bytes_written": COPY_BYTES, "launches": steps}), flush=True)
 
 
 KERNEL_SOURCES = {  # kernel template name -> its source file
