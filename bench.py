@@ -57,6 +57,15 @@ def parse():
     return ap.parse_args()
 
 
+def quiet_gc():
+    """Collect once and move every live object out of the collector's generations.  A full collection over
+    torch's heap takes 30-60 ms; left alone, one lands inside the timed steps every few hundred library calls
+    (each call makes a few small Python objects) and the device idles while the host is paused."""
+    import gc
+    gc.collect()
+    gc.freeze()
+
+
 def bench_decode(args, wl):
     """Decoding over per-head trimmed K/V caches: the layer's caches hold positions 0..T-2 (a prefill), and
     every timed step decodes the token at position T-1 (every ring full; repeating the step rewrites the same
@@ -82,6 +91,7 @@ def bench_decode(args, wl):
         aah.attn_decode(qt, kt, vt, kc, vc, pos, wl.windows, T, scale=wl.scale, out=o, lse=lse, workspace=ws,
                         stream=stream, sinks=wl.sinks)
 
+    quiet_gc()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -181,6 +191,7 @@ def bench_diag(args, wl):
                           stream=stream)
         mark(3)
 
+    quiet_gc()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -381,6 +392,7 @@ def main():
                               stream=stream, sinks=wl.sinks)
             mark(3)
 
+    quiet_gc()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
