@@ -631,13 +631,22 @@ aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, 
   std::vector<int32_t> tables(4 * H_kv + 1 + 2 * H);
   std::vector<aah::DecodeChunk> chunks;
   int32_t off = 0;
+  const int G = H / H_kv;
   for (int g = 0; g < H_kv; ++g) {
     const int32_t n = static_cast<int32_t>(sh.ksink[g] + sh.ring[g]);
+    const int32_t first = static_cast<int32_t>(chunks.size());
+    const int32_t count = (n + aah::kDecodeRows - 1) / aah::kDecodeRows;
+    int64_t cap_s = INT64_MAX;
+    for (int j = 0; j < G; ++j)
+      if (sh.sink[g * G + j] > 0) cap_s = std::min(cap_s, sh.cap[g * G + j]);
+    if (cap_s == INT64_MAX) cap_s = 1;  // no query head of g has sink keys (then S_g = 0): any positive value
     tables[g] = off;
     tables[H_kv + g] = static_cast<int32_t>(sh.ksink[g]);
     tables[2 * H_kv + g] = static_cast<int32_t>(sh.ring[g]);
-    tables[3 * H_kv + g] = static_cast<int32_t>(chunks.size());
-    for (int32_t r0 = 0; r0 < n; r0 += aah::kDecodeRows) chunks.push_back(aah::DecodeChunk{g, r0});
+    tables[3 * H_kv + g] = first;
+    for (int32_t r0 = 0; r0 < n; r0 += aah::kDecodeRows)
+      chunks.push_back(aah::DecodeChunk{g, r0, static_cast<int32_t>(sh.ksink[g]), static_cast<int32_t>(sh.ring[g]), off,
+                                        first, count, static_cast<int32_t>(cap_s)});
     off += n;
   }
   tables[4 * H_kv] = static_cast<int32_t>(chunks.size());

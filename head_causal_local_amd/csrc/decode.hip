@@ -85,9 +85,8 @@ template <int D, bool GROUPED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Knew, const bf16* __restrict__ Vnew,
     bf16* __restrict__ Kc, bf16* __restrict__ Vc, const int32_t* __restrict__ pos,
-    const DecodeChunk* __restrict__ chunks, const int32_t* __restrict__ kv_off, const int32_t* __restrict__ kv_sink,
-    const int32_t* __restrict__ kv_ring, const int32_t* __restrict__ kv_first, const int32_t* __restrict__ q_cap,
-    const int32_t* __restrict__ q_sink, int H, int H_kv, int R, int T_max, float c, int32_t* __restrict__ counters,
+    const DecodeChunk* __restrict__ chunks, const int32_t* __restrict__ q_cap, const int32_t* __restrict__ q_sink,
+    int H, int H_kv, int R, int T_max, float c, int32_t* __restrict__ counters,
     float* __restrict__ part, int n_chunks, bf16* __restrict__ O, float* __restrict__ LSE) {
   constexpr int kDL = D / 32;  // value dimensions per lane in P V
   constexpr int kPairs = kRowsPerWave / 2;
@@ -100,21 +99,23 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   __shared__ int sm_last;
 
   const int ch = blockIdx.x, b = blockIdx.y;
-  const DecodeChunk ck = chunks[ch];
+  const DecodeChunk ck = chunks[ch];  // everything the row addresses need, in one scalar load
   const int g = ck.kvhead;
   const int G = GROUPED ? H / H_kv : 1;  // query heads per key/value head (one: plain heads)
-  const int S_g = kv_sink[g], R_g = kv_ring[g];
+  const int S_g = ck.sink, R_g = ck.ring;
   const int p = min(max(pos[b], 0), T_max - 1);
   const int pr = p % R_g;
   const int new_ring = S_g + pr;            // local row of the new token in the ring
   const int new_sink = p < S_g ? p : -1;     // and of its sink copy
-  // Sink rows below sink_lim are attended by some query head of the group.
-  int sink_lim = 0;
-  for (int jh = 0; jh < G; ++jh) sink_lim = max(sink_lim, min(q_sink[g * G + jh], p - q_cap[g * G + jh] + 1));
+  // Sink rows below sink_lim may be attended by some query head of the group: head h attends to the sink
+  // rows j < min(S_h, p - C_h + 1), and S_h <= S_g, C_h >= cap_s for every head with sinks (S_g = 0 if none).
+  // Exact with one query head per group; with several it may also load rows no head attends to, which
+  // are positions already written (j <= p) and get zero weight.
+  const int sink_lim = max(0, min(S_g, p - ck.cap_s + 1));
   const size_t bg = static_cast<size_t>(b) * H_kv + g;
   const bf16* knew = Knew + bg * D;
   const bf16* vnew = Vnew + bg * D;
-  const size_t region = (static_cast<size_t>(b) * R + kv_off[g]) * D;  // first element of head g's rows
+  const size_t region = (static_cast<size_t>(b) * R + ck.off) * D;  // first element of head g's rows
   bf16* kreg = Kc + region;
   bf16* vreg = Vc + region;
 
@@ -172,7 +173,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     }
   }
 
-  const int c0 = kv_first[g], c1 = kv_first[g + 1];
+  const int c0 = ck.first, c1 = ck.first + ck.count;
   float* pbase = part + static_cast<size_t>(b) * n_chunks * G * (2 + D);
   // ---- the group's query heads in rounds of kGB: each wave forms every head's scores, softmax partial
   // and P V over its rows into LDS; after one barrier wave w merges head w of the round across the waves
@@ -388,15 +389,13 @@ hipError_t decode_d(const void* q, const void* knew, const void* vnew, void* kc,
   if (pl.H_kv != pl.H)
     hipLaunchKernelGGL((decode_kernel<D, true>), dim3(pl.n_chunks, B), dim3(kDecodeThreads), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(knew), static_cast<const bf16*>(vnew),
-                       static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.kv_off, pl.kv_sink,
-                       pl.kv_ring, pl.kv_first, pl.q_cap, pl.q_sink, pl.H, pl.H_kv, pl.rows, T_max, c, counters, part,
-                       pl.n_chunks, static_cast<bf16*>(o), lse);
+                       static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.q_cap, pl.q_sink, pl.H,
+                       pl.H_kv, pl.rows, T_max, c, counters, part, pl.n_chunks, static_cast<bf16*>(o), lse);
   else
     hipLaunchKernelGGL((decode_kernel<D, false>), dim3(pl.n_chunks, B), dim3(kDecodeThreads), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(knew), static_cast<const bf16*>(vnew),
-                       static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.kv_off, pl.kv_sink,
-                       pl.kv_ring, pl.kv_first, pl.q_cap, pl.q_sink, pl.H, pl.H_kv, pl.rows, T_max, c, counters, part,
-                       pl.n_chunks, static_cast<bf16*>(o), lse);
+                       static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.q_cap, pl.q_sink, pl.H,
+                       pl.H_kv, pl.rows, T_max, c, counters, part, pl.n_chunks, static_cast<bf16*>(o), lse);
   return hipGetLastError();
 }
 

@@ -135,12 +135,20 @@ hipError_t launch_head_features(const void* q, const void* k, const void* v, boo
 constexpr int kDecodeRows = 256;  // cache rows per decode workgroup
 
 // One decode workgroup's share: local rows [row0, row0 + kDecodeRows) of one
-// key/value head's region (its sink rows, then its ring rows).
+// key/value head's region (its sink rows, then its ring rows), with what the
+// workgroup needs of its key/value head before it can address its rows, so
+// that one 32-byte scalar load precedes the row loads.
 struct DecodeChunk {
-  int32_t kvhead;
+  int32_t kvhead;  // g
   int32_t row0;
+  int32_t sink;    // S_g sink rows
+  int32_t ring;    // R_g ring rows
+  int32_t off;     // first row of g's region in a batch entry's cache
+  int32_t first;   // g's first chunk
+  int32_t count;   // g's chunks
+  int32_t cap_s;   // smallest C_h among g's query heads with sink keys (any positive value if none)
 };
-static_assert(sizeof(DecodeChunk) == 8, "DecodeChunk layout");
+static_assert(sizeof(DecodeChunk) == 32, "DecodeChunk layout");
 
 // Device tables of one (windows, sinks, H, H_kv, T_max) combination.  Key/value
 // head g owns kv_sink[g] sink rows then kv_ring[g] ring rows from row

@@ -48,14 +48,14 @@ constexpr int kPlanThreads = 256;
 // The decode plan of aah_attn_decode's cache, computed on the device: per key/value head g (query heads
 // g G .. g G + G - 1) the ring R_g = max C_h and sink rows S_g = max effective sink, its first row
 // off_g = sum over g' < g of (S_g' + R_g'), its first chunk, and one chunk record per kDecodeRows rows of
-// its region.  Tables: kv_off[H_kv], kv_sink[H_kv], kv_ring[H_kv], kv_first[H_kv + 1], q_cap[H],
-// q_sink[H].  Also sets the B * H_kv merge counters to zero (each decode call leaves them zero, but
-// nothing else clears this array).  One workgroup.
+// its region (carrying those per-head values, as the host plan's records do).  Tables: kv_off[H_kv],
+// kv_sink[H_kv], kv_ring[H_kv], kv_first[H_kv + 1], q_cap[H], q_sink[H].  Also sets the B * H_kv merge
+// counters to zero (each decode call leaves them zero, but nothing else clears this array).  One workgroup.
 __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads heads, int H, int H_kv, int B,
                                                                    int32_t* __restrict__ counters,
                                                                    int32_t* __restrict__ tables,
                                                                    DecodeChunk* __restrict__ chunks) {
-  __shared__ int32_t s_ring[kNoAllocMaxHeads], s_sink[kNoAllocMaxHeads];
+  __shared__ int32_t s_ring[kNoAllocMaxHeads], s_sink[kNoAllocMaxHeads], s_caps[kNoAllocMaxHeads];
   __shared__ int32_t s_off[kNoAllocMaxHeads + 1], s_first[kNoAllocMaxHeads + 1];
   const int tid = threadIdx.x;
   const int G = H / H_kv;
@@ -65,13 +65,15 @@ __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads
     tables[4 * H_kv + 1 + H + h] = heads.sink[h];
   }
   for (int g = tid; g < H_kv; g += kPlanThreads) {
-    int ring = 0, sink = 0;
+    int ring = 0, sink = 0, cap_s = INT32_MAX;
     for (int j = 0; j < G; ++j) {
       ring = max(ring, heads.cap[g * G + j]);
       sink = max(sink, heads.sink[g * G + j]);
+      if (heads.sink[g * G + j] > 0) cap_s = min(cap_s, heads.cap[g * G + j]);
     }
     s_ring[g] = ring;
     s_sink[g] = sink;
+    s_caps[g] = cap_s == INT32_MAX ? 1 : cap_s;
   }
   __syncthreads();
   if (tid == 0) {
@@ -96,7 +98,8 @@ __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads
   if (tid == 0) tables[4 * H_kv] = s_first[H_kv];
   for (int g = 0; g < H_kv; ++g) {
     const int n_g = s_first[g + 1] - s_first[g];
-    for (int c = tid; c < n_g; c += kPlanThreads) chunks[s_first[g] + c] = DecodeChunk{g, c * kDecodeRows};
+    for (int c = tid; c < n_g; c += kPlanThreads)
+      chunks[s_first[g] + c] = DecodeChunk{g, c * kDecodeRows, s_sink[g], s_ring[g], s_off[g], s_first[g], n_g, s_caps[g]};
   }
 }
 

@@ -326,7 +326,7 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
  * counters on every call, so the call reads no host memory after it returns
  * and a captured graph replays the whole step.  No work list is cached.
  * Limits: H <= 256, and the step's counters, tables and partials
- * (B * H_kv * 4 bytes, (4 H_kv + 1 + 2 H) * 4 bytes, 8 bytes per 256 cache rows
+ * (B * H_kv * 4 bytes, (4 H_kv + 1 + 2 H) * 4 bytes, 32 bytes per 256 cache rows
  * of a batch entry, and B * chunks * (H / H_kv) * (2 + d) * 4 bytes, each
  * region rounded up to 256 bytes) must fit in the array; a larger step returns
  * AAH_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU shares that
