@@ -21,11 +21,14 @@
 //   decode_kernel -- one workgroup = kDecodeRows rows of one key/value head's
 //     region; each wave takes 64 rows.  Lane = row for the scores (its K row is
 //     one contiguous 2 d-byte read; q . k with v_dot2_f32_bf16 on bf16 pairs);
-//     lanes = dimension slices for P V (two rows per load instruction).  All K
-//     and V loads are issued before the first wait, so a workgroup pays one
-//     HBM round trip.  The new token's K / V come from k_new / v_new and are
-//     stored into their rows by the lanes that own them, so no separate append
-//     launch and no ordering between workgroups is needed.  For each query
+//     for P V each lane takes 16 bytes (8 dimensions) of d / 8 rows, so every
+//     V load instruction reads 512 / d whole rows.  The query rows, K and V
+//     are all requested, through buffer resources whose range check turns the
+//     rows no head needs into zeros, before the first wait and with no branch
+//     among them, so a workgroup pays one HBM round trip.  The new token's
+//     K / V come from k_new / v_new and are stored into their rows by the
+//     lanes that hold them, so no separate append launch and no ordering
+//     between workgroups is needed.  For each query
 //     head of the group in turn the waves merge (max, sum, weighted values) in
 //     LDS and the workgroup writes one unnormalised partial; the last
 //     workgroup of a (b, g) to finish (a per-(b, g) counter in the workspace,
@@ -88,22 +91,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     const DecodeChunk* __restrict__ chunks, const int32_t* __restrict__ q_cap, const int32_t* __restrict__ q_sink,
     int H, int H_kv, int R, int T_max, float c, int32_t* __restrict__ counters,
     float* __restrict__ part, int n_chunks, bf16* __restrict__ O, float* __restrict__ LSE) {
-  constexpr int kDL = D / 32;  // value dimensions per lane in P V
-  constexpr int kPairs = kRowsPerWave / 2;
-  using vec_t = typename std::conditional<kDL == 1, bf16,
-                                          typename std::conditional<kDL == 2, bf16x2, bf16x4>::type>::type;
   // Per-wave partials of up to kGB query heads at a time, merged across the waves after one barrier.
   constexpr int kGB = GROUPED ? kDecodeWaves : 1;
   __shared__ float sm_m[kGB][kDecodeWaves], sm_l[kGB][kDecodeWaves];
   __shared__ float sm_o[kGB][kDecodeWaves][D];
+  __shared__ __attribute__((aligned(16))) bf16 sm_q[kDecodeWaves][kGB * D];  // one copy per wave
+  __shared__ u32x4 sm_knew[D / 8];
   __shared__ int sm_last;
 
   const int ch = blockIdx.x, b = blockIdx.y;
-  const DecodeChunk ck = chunks[ch];  // everything the row addresses need, in one scalar load
+  // The position and the chunk record (everything the row addresses need) are independent scalar loads:
+  // both are issued before either is waited for.
+  const int pos_b = pos[b];
+  const DecodeChunk ck = chunks[ch];
+  __asm__ volatile("" ::"s"(pos_b), "s"(ck.kvhead));
   const int g = ck.kvhead;
   const int G = GROUPED ? H / H_kv : 1;  // query heads per key/value head (one: plain heads)
   const int S_g = ck.sink, R_g = ck.ring;
-  const int p = min(max(pos[b], 0), T_max - 1);
+  const int p = min(max(pos_b, 0), T_max - 1);
   const int pr = p % R_g;
   const int new_ring = S_g + pr;            // local row of the new token in the ring
   const int new_sink = p < S_g ? p : -1;     // and of its sink copy
@@ -122,7 +127,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int hl = lane >> 5, j = lane & 31;
   const int w0 = ck.row0 + wave * kRowsPerWave;  // first local row of this wave
 
   // The rows some query head of the group attends to form two runs: sink rows [0, sink_lim) and ring
@@ -130,8 +134,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // and while p < R_g the ring rows no older than p are exactly its first p + 1.
   const int ring_live = min(p + 1, R_g);
   auto needed_any = [&](int r) __attribute__((always_inline)) {
-    return static_cast<unsigned>(r) < static_cast<unsigned>(sink_lim) ||
-           static_cast<unsigned>(r - S_g) < static_cast<unsigned>(ring_live);
+    return (static_cast<unsigned>(r) < static_cast<unsigned>(sink_lim)) |
+           (static_cast<unsigned>(r - S_g) < static_cast<unsigned>(ring_live));
   };
   // Wave-uniform: every row of the wave is needed (the usual case once the ring has filled).
   const bool wave_full = w0 + kRowsPerWave <= sink_lim || (w0 >= S_g && w0 + kRowsPerWave - S_g <= ring_live);
@@ -140,37 +144,73 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   const bool is_sink = row < S_g;
   const int age = ring_age(row, S_g, R_g, pr);
 
-  // ---- all loads first: this lane's K row (scores) and its V slices of the wave's rows (P V).  The rows
-  // of the new token (its ring row and, while p < S_g, its sink row) take k_new / v_new, and the lanes
-  // holding them store them into the cache once used (no workgroup reads either row from memory during
-  // this step; the sink copy is first attended once the window has moved past it).
+  // ---- all loads first, with no branch among them, so that a workgroup pays one round trip for its rows.
+  // K: lane = row, its whole row.  V: lane (rg, dg) takes dimensions 8 dg .. 8 dg + 7 of rows rg + kRG i
+  // (kLR lanes per row, so each load instruction reads kRG whole rows).  Both come through buffer
+  // resources over the region's rows: a row no query head attends to, and each row of the new token, is
+  // addressed past the range and reads as zero (a zero weight then never meets stale bits); the new
+  // token's K and V come from k_new / v_new below.
+  constexpr int kLR = D / 8;                // lanes per V row, 16 bytes each
+  constexpr int kRG = 64 / kLR;             // rows per V load instruction
+  constexpr int kVL = kRowsPerWave / kRG;   // V loads per lane
+  constexpr uint32_t kPast = 0x80000000u;   // an offset past any region
+  const uint32_t region_bytes = static_cast<uint32_t>(S_g + R_g) * D * 2;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kreg, region_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(vreg, region_bytes);
+  // Query rows of the current round of (at most kGB) query heads go through LDS, every lane then reading
+  // the same bytes (a broadcast): each wave's first nb D / 8 lanes read 16 bytes each into the wave's
+  // own copy (so no barrier: one wave's LDS accesses are in order), issued before the rows so that they
+  // arrive first.  (No branch around any load: a value defined on one side of a branch makes the
+  // compiler wait for it at the join, before the loads after it are issued.)
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(Q + static_cast<size_t>(b) * H * D, static_cast<uint32_t>(H) * D * 2);
+  auto q_piece = [&](int jb) __attribute__((always_inline)) {
+    const int nb = GROUPED ? min(kGB, G - jb) : 1;
+    const bool has = lane < nb * (D / 8);  // other lanes read past the range (no access)
+    return load16(rq, has ? static_cast<uint32_t>((g * G + jb) * D + 8 * lane) * 2 : kPast);
+  };
+  u32x4 qpiece = q_piece(0);
   const bool owns_new = row == new_ring || row == new_sink;
+  const uint32_t koff = any & !owns_new ? static_cast<uint32_t>(row) * D * 2 : kPast;
   bf16x8 kr[D / 8];
-  if (any || owns_new) {
-    const bf16* krow = owns_new ? knew : kreg + static_cast<size_t>(row) * D;
 #pragma unroll
-    for (int i = 0; i < D / 8; ++i) kr[i] = *reinterpret_cast<const bf16x8*>(krow + 8 * i);
+  for (int i = 0; i < D / 8; ++i) kr[i] = __builtin_bit_cast(bf16x8, load16(rk, koff + 16 * i));
+  const int dg = lane % kLR, rg = lane / kLR;
+  bf16x8 vr[kVL];
+#pragma unroll
+  for (int i = 0; i < kVL; ++i) {
+    const int vrow = w0 + rg + kRG * i;
+    const bool use = needed_any(vrow) & (vrow != new_ring);  // (the new token's sink copy is never attended)
+    vr[i] = __builtin_bit_cast(bf16x8, load16(rv, use ? static_cast<uint32_t>(vrow) * D * 2 + 16 * dg : kPast));
   }
-  // Rows no head attends to get zero V slices, so that their (zero) weights never meet stale bits.
-  vec_t vr[kPairs];
-  if (wave_full) {
+  // The wave holding a row of the new token (its ring row and, while p < S_g, its sink row) takes that
+  // row's K and V from k_new / v_new and stores them into the cache; no workgroup reads either row from
+  // memory during this step (the sink copy is first attended once the window has moved past it).
+  const bool wave_new = static_cast<unsigned>(new_ring - w0) < static_cast<unsigned>(kRowsPerWave) ||
+                        static_cast<unsigned>(new_sink - w0) < static_cast<unsigned>(kRowsPerWave);
+  if (wave_new) {
+    // Vector loads, past the range where not needed (in scalar registers the rows would crowd out the
+    // addressing state): lanes 0 .. D / 8 - 1 read k_new, which goes to the owning lanes through LDS
+    // (one wave's LDS accesses are in order), and every lane reads v_new's 16 bytes at its dimensions.
+    const __amdgpu_buffer_rsrc_t rkn = make_rsrc(knew, D * 2), rvn = make_rsrc(vnew, D * 2);
+    const u32x4 kpiece = load16(rkn, lane < D / 8 ? 16u * lane : kPast);
+    const bf16x8 vslice = __builtin_bit_cast(bf16x8, load16(rvn, 16 * dg));
+    if (lane < D / 8) sm_knew[lane] = kpiece;  // two waves of a workgroup may both write: the same bytes
+    if (owns_new) {
 #pragma unroll
-    for (int r = 0; r < kPairs; ++r) {
-      const int sk = w0 + 2 * r + hl;
-      const bf16* vrow = sk == new_ring ? vnew : vreg + static_cast<size_t>(sk) * D;
-      vr[r] = *reinterpret_cast<const vec_t*>(vrow + kDL * j);
-    }
-  } else {
-#pragma unroll
-    for (int r = 0; r < kPairs; ++r) {
-      const int sk = w0 + 2 * r + hl;
-      if (needed_any(sk)) {
-        const bf16* vrow = sk == new_ring ? vnew : vreg + static_cast<size_t>(sk) * D;
-        vr[r] = *reinterpret_cast<const vec_t*>(vrow + kDL * j);
-      } else {
-        vr[r] = vec_t{};
+      for (int i = 0; i < D / 8; ++i) {
+        kr[i] = __builtin_bit_cast(bf16x8, sm_knew[i]);
+        *reinterpret_cast<bf16x8*>(kreg + static_cast<size_t>(row) * D + 8 * i) = kr[i];
       }
     }
+    if (rg == 0) {  // lanes 0 .. D / 8 - 1 hold the new V row between them
+      if (static_cast<unsigned>(new_ring - w0) < static_cast<unsigned>(kRowsPerWave))
+        *reinterpret_cast<bf16x8*>(vreg + static_cast<size_t>(new_ring) * D + 8 * dg) = vslice;
+      if (static_cast<unsigned>(new_sink - w0) < static_cast<unsigned>(kRowsPerWave))
+        *reinterpret_cast<bf16x8*>(vreg + static_cast<size_t>(new_sink) * D + 8 * dg) = vslice;
+    }
+#pragma unroll
+    for (int i = 0; i < kVL; ++i)
+      if (w0 + rg + kRG * i == new_ring) vr[i] = vslice;
   }
 
   const int c0 = ck.first, c1 = ck.first + ck.count;
@@ -180,68 +220,56 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   // and writes the workgroup's partial.
   for (int jb = 0; jb < G; jb += kGB) {
     const int nb = GROUPED ? min(kGB, G - jb) : 1;
+    if (jb > 0) qpiece = q_piece(jb);
+    if (lane < nb * (D / 8)) *reinterpret_cast<u32x4*>(sm_q[wave] + 8 * lane) = qpiece;
     for (int u = 0; u < nb; ++u) {
       const int jh = jb + u;
       const int h = g * G + jh;
       const int C_h = q_cap[h];
       const bool valid = is_sink ? row < min(q_sink[h], p - C_h + 1)
                                  : static_cast<unsigned>(row - S_g) < static_cast<unsigned>(ring_live) && age < C_h;
-      const bf16* qrow = Q + (static_cast<size_t>(b) * H + h) * D;
-      float s = -INFINITY;
-      if (valid) {
-        float s0 = 0.f, s1 = 0.f;
+      float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(qrow + 8 * i);
+      for (int i = 0; i < D / 8; ++i) {
+        const bf16x8 qv = *reinterpret_cast<const bf16x8*>(sm_q[wave] + u * D + 8 * i);
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 a = {kr[i][e], kr[i][e + 1]};
-            const bf16x2 q2 = {qv[e], qv[e + 1]};
-            if (e & 2)
-              s1 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s1, false);
-            else
-              s0 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s0, false);
-          }
-        }
-        s = (s0 + s1) * c;
-      }
-      if (jh == 0 && owns_new) {  // the new token's K (from registers) and V enter its rows
-#pragma unroll
-        for (int i = 0; i < D / 8; ++i) {
-          *reinterpret_cast<bf16x8*>(kreg + static_cast<size_t>(row) * D + 8 * i) = kr[i];
-          *reinterpret_cast<bf16x8*>(vreg + static_cast<size_t>(row) * D + 8 * i) =
-              *reinterpret_cast<const bf16x8*>(vnew + 8 * i);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 a = {kr[i][e], kr[i][e + 1]};
+          const bf16x2 q2 = {qv[e], qv[e + 1]};
+          if (e & 2)
+            s1 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s1, false);
+          else
+            s0 = __builtin_amdgcn_fdot2_f32_bf16(a, q2, s0, false);
         }
       }
+      const float s = valid ? (s0 + s1) * c : -INFINITY;
       const float m_w = wave_max(s);
       const float pw = (valid && m_w != -INFINITY) ? __builtin_amdgcn_exp2f(s - m_w) : 0.f;
       const float l_w = wave_sum(pw);
 
-      // P V: lanes (hl, j) take rows 2 r + hl of the wave and dimensions kDL j .. kDL j + kDL - 1
-      float acc[kDL];
+      // P V: lane (rg, dg) sums its kVL rows for its 8 dimensions, then the kRG row groups of the wave
+      // that hold the same dimensions (lanes dg, dg + kLR, ...) add up theirs.
+      float acc[8];
 #pragma unroll
-      for (int x = 0; x < kDL; ++x) acc[x] = 0.f;
+      for (int x = 0; x < 8; ++x) acc[x] = 0.f;
 #pragma unroll
-      for (int r = 0; r < kPairs; ++r) {
-        const float pk = __shfl(pw, 2 * r + hl);  // 0 for rows this head does not attend to
-        if constexpr (kDL == 1) {
-          acc[0] = fmaf(pk, static_cast<float>(vr[r]), acc[0]);
-        } else {
+      for (int i = 0; i < kVL; ++i) {
+        const float pk = __shfl(pw, rg + kRG * i);  // 0 for rows this head does not attend to
 #pragma unroll
-          for (int x = 0; x < kDL; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[r][x]), acc[x]);
-        }
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[i][x]), acc[x]);
       }
-      // Even and odd rows: lanes j and j + 32 hold the same dimensions.
 #pragma unroll
-      for (int x = 0; x < kDL; ++x) acc[x] += __shfl_xor(acc[x], 32);
+      for (int o = kLR; o < 64; o <<= 1)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[x] += __shfl_xor(acc[x], o);
 
       if (lane == 0) {
         sm_m[u][wave] = m_w;
         sm_l[u][wave] = l_w;
       }
-      if (hl == 0) {
+      if (rg == 0) {
 #pragma unroll
-        for (int x = 0; x < kDL; ++x) sm_o[u][wave][kDL * j + x] = acc[x];
+        for (int x = 0; x < 8; ++x) sm_o[u][wave][8 * dg + x] = acc[x];
       }
     }
     __syncthreads();
