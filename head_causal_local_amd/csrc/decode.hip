@@ -52,10 +52,24 @@ constexpr int kDecodeWaves = kDecodeRows / kRowsPerWave;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
 static_assert(kDecodeWaves * kRowsPerWave == kDecodeRows && kDecodeWaves <= 4, "chunk size");
 
+// Lane x from lane l ^ 1, l ^ 2 (quad permutations) or rotated by 4 / 8 within its 16-lane row (DPP).
+template <int CTRL>
+__device__ inline float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppRor4 = 0x124, kDppRor8 = 0x128;
+
+// Wave-wide max and sum without LDS traffic: within quads, across the quads of each 16-lane row by
+// rotations, then the 16- and 32-lane swaps.
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, dpp<kDppXor1>(x));
+  x = fmaxf(x, dpp<kDppXor2>(x));
+  x = fmaxf(x, dpp<kDppRor4>(x));
+  x = fmaxf(x, dpp<kDppRor8>(x));
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
 // Device-coherent (all XCDs) store and load of one float.
@@ -66,10 +80,22 @@ __device__ inline float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Sum over the lanes l, l + LR, l + 2 LR, ... of a wave (LR in {4, 8, 16}: the lanes holding the same
+// P V dimensions), with no LDS traffic: rotations within each 16-lane row, then the 16- and 32-lane swaps.
+template <int LR>
+__device__ inline float group_sum(float x) {
+  if constexpr (LR <= 4) x += dpp<kDppRor4>(x);
+  if constexpr (LR <= 8) x += dpp<kDppRor8>(x);
+  auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r16[0]) + __uint_as_float(r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r32[0]) + __uint_as_float(r32[1]);
+}
+
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+  x += dpp<kDppXor1>(x);
+  x += dpp<kDppXor2>(x);
+  return group_sum<4>(x);
 }
 
 // Local rows of key/value head g's region: rows [0, S_g) are sinks (row j holds position j), rows
@@ -259,9 +285,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
         for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[i][x]), acc[x]);
       }
 #pragma unroll
-      for (int o = kLR; o < 64; o <<= 1)
-#pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] += __shfl_xor(acc[x], o);
+      for (int x = 0; x < 8; ++x) acc[x] = group_sum<kLR>(acc[x]);
 
       if (lane == 0) {
         sm_m[u][wave] = m_w;
