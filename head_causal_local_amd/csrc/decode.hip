@@ -123,6 +123,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   __shared__ float sm_o[kGB][kDecodeWaves][D];
   __shared__ __attribute__((aligned(16))) bf16 sm_q[kDecodeWaves][kGB * D];  // one copy per wave
   __shared__ u32x4 sm_knew[D / 8];
+  __shared__ __attribute__((aligned(16))) float sm_p[kDecodeWaves][kRowsPerWave];  // one head's weights, per wave
   __shared__ int sm_last;
 
   const int ch = blockIdx.x, b = blockIdx.y;
@@ -278,11 +279,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       float acc[8];
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc[x] = 0.f;
+      // The weights reach the P V lanes through the wave's LDS row: lane r writes its weight at
+      // (r mod kRG) kVL + r / kRG, so lane (rg, dg) reads its kVL weights (rows rg + kRG i, 0 for rows
+      // this head does not attend to) as consecutive floats.  One wave's LDS accesses are in order.
+      sm_p[wave][(lane % kRG) * kVL + lane / kRG] = pw;
+      float pk[kVL];
+#pragma unroll
+      for (int i = 0; i < kVL; i += 4) *reinterpret_cast<f32x4*>(pk + i) = *reinterpret_cast<const f32x4*>(&sm_p[wave][rg * kVL + i]);
 #pragma unroll
       for (int i = 0; i < kVL; ++i) {
-        const float pk = __shfl(pw, rg + kRG * i);  // 0 for rows this head does not attend to
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk, static_cast<float>(vr[i][x]), acc[x]);
+        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk[i], static_cast<float>(vr[i][x]), acc[x]);
       }
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc[x] = group_sum<kLR>(acc[x]);
