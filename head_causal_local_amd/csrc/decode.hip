@@ -164,8 +164,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     return (static_cast<unsigned>(r) < static_cast<unsigned>(sink_lim)) |
            (static_cast<unsigned>(r - S_g) < static_cast<unsigned>(ring_live));
   };
-  // Wave-uniform: every row of the wave is needed (the usual case once the ring has filled).
-  const bool wave_full = w0 + kRowsPerWave <= sink_lim || (w0 >= S_g && w0 + kRowsPerWave - S_g <= ring_live);
   const int row = w0 + lane;
   const bool any = needed_any(row);
   const bool is_sink = row < S_g;
@@ -240,6 +238,20 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       if (w0 + rg + kRG * i == new_ring) vr[i] = vslice;
   }
 
+  // Grouped heads: V regrouped for v_dot2_f32_bf16, dword x of vpk[j] holding dimension x of this lane's
+  // rows 2 j and 2 j + 1, so each of the G heads' P V takes one dot2 per dimension and row pair with no
+  // conversions (one head alone does not repay the regrouping).
+  uint32_t vpk[kVL / 2][8];
+#pragma unroll
+  for (int j = 0; j < (GROUPED ? kVL / 2 : 0); ++j) {
+    const u32x4 a = __builtin_bit_cast(u32x4, vr[2 * j]), bb = __builtin_bit_cast(u32x4, vr[2 * j + 1]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      vpk[j][2 * k] = __builtin_amdgcn_perm(bb[k], a[k], 0x05040100u);      // low halves: dimension 2 k
+      vpk[j][2 * k + 1] = __builtin_amdgcn_perm(bb[k], a[k], 0x07060302u);  // high halves: dimension 2 k + 1
+    }
+  }
+
   const int c0 = ck.first, c1 = ck.first + ck.count;
   float* pbase = part + static_cast<size_t>(b) * n_chunks * G * (2 + D);
   // ---- the group's query heads in rounds of kGB: each wave forms every head's scores, softmax partial
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       const float s = valid ? (s0 + s1) * c : -INFINITY;
       const float m_w = wave_max(s);
       const float pw = (valid && m_w != -INFINITY) ? __builtin_amdgcn_exp2f(s - m_w) : 0.f;
-      const float l_w = wave_sum(pw);
+      const float l_w = wave_sum(pw);  // exact fp32 row sum, so the log-sum-exp stays fp32-accurate
 
       // P V: lane (rg, dg) sums its kVL rows for its 8 dimensions, then the kRG row groups of the wave
       // that hold the same dimensions (lanes dg, dg + kLR, ...) add up theirs.
@@ -286,10 +298,21 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
       float pk[kVL];
 #pragma unroll
       for (int i = 0; i < kVL; i += 4) *reinterpret_cast<f32x4*>(pk + i) = *reinterpret_cast<const f32x4*>(&sm_p[wave][rg * kVL + i]);
+      if constexpr (GROUPED) {
 #pragma unroll
-      for (int i = 0; i < kVL; ++i) {
+        for (int j = 0; j < kVL / 2; ++j) {
+          // P V multiplies bf16-rounded weights (relative error 2^-9 each, so |o| moves by at most
+          // 2^-9 max |v|, below the output's own bf16 rounding)
+          const bf16x2 pp = {static_cast<bf16>(pk[2 * j]), static_cast<bf16>(pk[2 * j + 1])};
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk[i], static_cast<float>(vr[i][x]), acc[x]);
+          for (int x = 0; x < 8; ++x)
+            acc[x] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, vpk[j][x]), pp, acc[x], false);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kVL; ++i)
+#pragma unroll
+          for (int x = 0; x < 8; ++x) acc[x] = fmaf(pk[i], static_cast<float>(vr[i][x]), acc[x]);
       }
 #pragma unroll
       for (int x = 0; x < 8; ++x) acc[x] = group_sum<kLR>(acc[x]);
