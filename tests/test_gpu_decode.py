@@ -206,6 +206,11 @@ def _history_g(B, H, H_kv, L, d, seed):
     (6, 2, [1, 64, 300, 7, 256, 33], [0, 5, 0, 128, 0, 2], 512, 200),
     # one key/value head for all query heads, rings of several chunks
     (4, 1, [600, 5, 1000, 129], [0, 130, 1, 0], 1024, 700),
+    # groups larger than the kernel's rounds of four query heads: ten heads per group (rounds of 4, 4, 2),
+    # mixed windows and sinks within the group
+    (10, 1, [600, 5, 1000, 129, 1, 64, 300, 7, 256, 33], [0, 130, 1, 0, 0, 5, 0, 128, 0, 2], 1024, 700),
+    # eight heads per group over two key/value heads (two full rounds each)
+    (16, 2, [512, 64, 300, 1, 1024, 16, 700, 33] * 2, [0] * 16, 1024, 600),
 ])
 def test_decode_sinks_and_groups(d, H, H_kv, windows, sinks, T_max, T0):
     """Prefill T0 positions, then 40 steps (sequence 1 repeats position T0 for its first 7 steps): every step
