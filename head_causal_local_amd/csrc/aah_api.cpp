@@ -690,6 +690,11 @@ aah_status check_decode(const int32_t* windows, const int32_t* sinks, int B, int
   if (static_cast<int64_t>(B) * H_kv > 65535)
     return fail(AAH_ERR_UNSUPPORTED, "B * H_kv = %lld exceeds 65535", static_cast<long long>(B) * H_kv);
   if (static_cast<int64_t>(B) * rows * d >= (int64_t{1} << 40)) return fail(AAH_ERR_UNSUPPORTED, "cache too large");
+  // The kernel reads a batch entry's query rows and a key/value head's region (under 2 T_max rows, so
+  // under 2^31 bytes by check_dims) through 32-bit buffer offsets.
+  if (static_cast<int64_t>(H) * d * 2 >= (int64_t{1} << 31))
+    return fail(AAH_ERR_UNSUPPORTED, "H * d = %lld is too large for one step's query rows",
+                static_cast<long long>(H) * d);
   return AAH_OK;
 }
 

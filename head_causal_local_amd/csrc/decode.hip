@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   constexpr int kLR = D / 8;                // lanes per V row, 16 bytes each
   constexpr int kRG = 64 / kLR;             // rows per V load instruction
   constexpr int kVL = kRowsPerWave / kRG;   // V loads per lane
-  constexpr uint32_t kPast = 0x80000000u;   // an offset past any region
+  constexpr uint32_t kPast = 0x80000000u;   // past any region (regions are under 2 T_max rows, < 2^31 bytes)
   const uint32_t region_bytes = static_cast<uint32_t>(S_g + R_g) * D * 2;
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(kreg, region_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(vreg, region_bytes);

@@ -271,7 +271,8 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
  * (a sink at or past T_max - C_h is always inside the window).  Position t
  * lives in ring row off_g + S_g + (t mod R_g) and, if t < S_g, also in sink row
  * off_g + t.  Rows not yet written are never read.  Only dt = AAH_BF16 is
- * supported (AAH_ERR_UNSUPPORTED otherwise); d in {32, 64, 128}; sinks may be
+ * supported (AAH_ERR_UNSUPPORTED otherwise, and when one step's query rows,
+ * H * d * 2 bytes, reach 2^31); d in {32, 64, 128}; sinks may be
  * NULL; windows, sinks, H_kv and stream as for the other calls.  Without sinks
  * and grouping head h simply owns C_h ring rows.
  */
