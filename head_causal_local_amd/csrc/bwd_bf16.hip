@@ -60,6 +60,7 @@
 // does), and a dK/dV item holding a sink key runs over every later query tile
 // (its planner range says so).  Without sinks the SINK = false code runs.
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "kernels.hpp"
@@ -375,7 +376,46 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // the barrier that ended step v - 1 saw every wave finish with it.  A step ends once the next step's
   // copies have landed (each wave waits for its own, then the barrier); with three stages the copies
   // issued in this step may stay in flight.
+  //
+  // Skewed waves (three stages, one query head, an item that starts at its diagonal tile): waves 2 and 3
+  // hold keys 64 .. 127 of the item, which no query of its first tile sees and which see the queries of
+  // one more tile at the end than waves 0 and 1 do.  So at step v waves 0 and 1 take tile lo + v and waves
+  // 2 and 3 tile lo + v + 1 (both resident: the ring holds three stages), and the item needs one step
+  // fewer: 9 instead of 10 at a 512-key window.  The price: every copy issued in a step is waited for at
+  // its end (waves 2 and 3 use it in the next step).
   constexpr int kAhead = kStages - 1;
+  const bool skew = kStages == 3 && !GQA && it.lo * kStep == k0;
+  const int sk = skew && wave >= 2 ? 1 : 0;  // tile offset of this wave (uniform)
+  int n_plain = it.hi - it.lo;
+  if (skew) {
+    // The last tile waves 0 and 1 need, and then the steps the skewed walk takes.
+    const int hi01 = min(it.hi, query_hi(k0, min(T, k0 + kStat / 2), W, S, T));
+    n_plain = max(hi01 - it.lo, it.hi - it.lo - 1);
+  }
+  // SK: this wave takes the next tile (waves 2 and 3); each wave pair runs its own copy of the loop, so
+  // that every LDS address keeps a compile-time stage (the pairs meet at the same barriers).
+  auto step_skew = [&](auto sk_t, int v, const char* cur, const char* nxt1, char* nxtf)
+                       __attribute__((always_inline)) {
+    constexpr bool SK = decltype(sk_t)::value;
+    const int qt = it.lo + v;
+    const bool more = qt + kAhead < it.hi;
+    if (more) fill(qt + kAhead, nxtf);
+    if constexpr (SK) {
+      if (qt + 1 < it.hi) do_step(nxt1, (qt + 1) * kStep, W, S);
+    } else {
+      do_step(cur, qt * kStep, W, S);
+    }
+    if (v + 1 >= n_plain) return true;
+    wait_barrier(false);
+    return false;
+  };
+  auto loop_skew = [&](auto sk_t) __attribute__((always_inline)) {
+    for (int v = 0;; v += 3) {
+      if (step_skew(sk_t, v, ring[0], ring[1], ring[2])) break;
+      if (step_skew(sk_t, v + 1, ring[1], ring[2], ring[0])) break;
+      if (step_skew(sk_t, v + 2, ring[2], ring[0], ring[1])) break;
+    }
+  };
   auto step = [&](int v, const char* cur, char* nxtf) __attribute__((always_inline)) {
     if constexpr (GQA) {
       const bool more = v + kAhead < n_steps;
@@ -437,10 +477,17 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   }
   wait_vm_barrier(0);
   if constexpr (kStages == 3) {
-    for (int v = 0;; v += 3) {
-      if (step(v, ring[0], ring[2])) break;
-      if (step(v + 1, ring[1], ring[0])) break;
-      if (step(v + 2, ring[2], ring[1])) break;
+    if (skew) {
+      if (sk)
+        loop_skew(std::true_type{});
+      else
+        loop_skew(std::false_type{});
+    } else {
+      for (int v = 0;; v += 3) {
+        if (step(v, ring[0], ring[2])) break;
+        if (step(v + 1, ring[1], ring[0])) break;
+        if (step(v + 2, ring[2], ring[1])) break;
+      }
     }
   } else {
     for (int v = 0;; v += 2) {
