@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 10
+ABI_VERSION = 11
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",

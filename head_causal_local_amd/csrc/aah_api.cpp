@@ -81,7 +81,8 @@ aah_status check_shape(const int32_t* windows, const int32_t* sinks, int B, int 
 }
 
 aah_status check_dims(int B, int H, int T, int d, aah_dtype dt) {
-  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1 (got %d, %d, %d)", B, H, T);
+  if (B < 0 || H < 1 || T < 0)
+    return fail(AAH_ERR_INVALID_ARG, "B, T must be >= 0 and H >= 1 (got B = %d, H = %d, T = %d)", B, H, T);
   if (static_cast<int64_t>(B) * H > INT32_MAX / 2)
     return fail(AAH_ERR_INVALID_ARG, "B * H = %lld is too large", static_cast<long long>(B) * H);
   if (T > (1 << 28)) return fail(AAH_ERR_INVALID_ARG, "T = %d is too large", T);
@@ -93,6 +94,10 @@ aah_status check_dims(int B, int H, int T, int d, aah_dtype dt) {
     return fail(AAH_ERR_UNSUPPORTED, "T * d = %lld is too large for one head slice", static_cast<long long>(T) * d);
   return AAH_OK;
 }
+
+// No batch entries or no tokens: nothing to compute.  Such a call checks its other arguments and returns
+// AAH_OK without touching any tensor (they may be NULL: an empty tensor has no storage).
+bool empty_problem(int B, int T) { return B == 0 || T == 0; }
 
 aah_status check_tensor(const void* p, const char* name, size_t align) {
   if (p == nullptr) return fail(AAH_ERR_INVALID_ARG, "%s is NULL", name);
@@ -683,6 +688,7 @@ size_t decode_workspace(const int32_t* windows, const int32_t* sinks, int B, int
 aah_status check_decode(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T_max, int d,
                         aah_dtype dt) {
   AAH_TRY_INNER(check_shape(windows, sinks, B, H, T_max, d, dt, H_kv));
+  if (T_max < 1) return fail(AAH_ERR_INVALID_ARG, "T_max must be >= 1 (got %d)", T_max);
   if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
   const int64_t rows = decode_rows(windows, sinks, H, H_kv, T_max);
   if (rows < 0) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
@@ -747,7 +753,7 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
                                    int d, aah_dtype dt) {
   if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
   g_detail.clear();
-  if (any_sink(windows, sinks, H, T)) return 0;
+  if (empty_problem(B, T) || any_sink(windows, sinks, H, T)) return 0;
   const int L = split_chunk_tiles(windows, B, H, T, d);
   if (L == 0) return 0;
   SplitDevicePlan sp;
@@ -759,6 +765,7 @@ size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* 
                                          int T, int d, aah_dtype dt) {
   if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
   g_detail.clear();
+  if (empty_problem(B, T)) return 0;
   BwdSplitLayout lay;
   return bwd_split_layout(windows, sinks, B, H, H_kv, T, d, dt, nullptr, &lay) ? lay.total : 0;
 }
@@ -783,12 +790,13 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
                     int H, int H_kv, int T, int d, aah_dtype dt, float scale, void* o, float* lse, float* ent,
                     float* onorm, void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (empty_problem(B, T)) return AAH_OK;
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   // An optional workspace, when given, follows the same alignment rule as every other workspace, whether or
   // not this launch would split (checked here, before any HIP call).
   if (workspace != nullptr && !aligned(workspace, 256))
@@ -850,8 +858,10 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
                              const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
                              void* o, float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream) {
   g_detail.clear();
-  AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
-  AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
+  if (!empty_problem(B, T)) {
+    AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
+    AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
+  }
   return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, nullptr, 0,
                   stream);
 }
@@ -867,6 +877,8 @@ aah_status aah_head_features(const void* q, const void* k, const void* v, const 
                              void* workspace, size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_shape(windows, nullptr, B, H, T, d, dt, H_kv));
+  // The statistics are means over tokens: they need at least one.
+  if (empty_problem(B, T)) return fail(AAH_ERR_INVALID_ARG, "head features need B, T >= 1 (got %d, %d)", B, T);
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -906,13 +918,14 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
                              aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (empty_problem(B, T)) return AAH_OK;
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(dout, "dout", 16));
   AAH_TRY(check_tensor(dk, "dk", 16));
   AAH_TRY(check_tensor(dv, "dv", 16));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -950,6 +963,8 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
                            size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (empty_problem(B, T)) return AAH_OK;
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -957,7 +972,6 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
   AAH_TRY(check_tensor(dout, "dout", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
   AAH_TRY(check_tensor(dq, "dq", 16));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -999,6 +1013,8 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   g_detail.clear();
   // Validate everything up front so that no step runs unless all of them can.
   AAH_TRY(check_shape(windows, sinks, B, H, T, d, dt, H_kv));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (empty_problem(B, T)) return AAH_OK;
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
@@ -1008,7 +1024,6 @@ aah_status aah_attn_bwd(const void* q, const void* k, const void* v, const void*
   AAH_TRY(check_tensor(dq, "dq", 16));
   AAH_TRY(check_tensor(dk, "dk", 16));
   AAH_TRY(check_tensor(dv, "dv", 16));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   AAH_TRY(check_workspace(workspace, workspace_bytes, B, H, T, d, dt));
   AAH_TRY(aah_attn_bwd_dq(q, k, v, o, dout, lse, windows, sinks, B, H, H_kv, T, d, dt, scale, dq, workspace,
                           workspace_bytes, stream));
@@ -1038,7 +1053,8 @@ aah_status aah_kv_cache_fill(const void* k, const void* v, const int32_t* window
                              aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_decode(windows, sinks, B, H, H_kv, T_max, d, dt));
-  if (T < 1 || T > T_max) return fail(AAH_ERR_INVALID_ARG, "prefill length T = %d must be in [1, T_max = %d]", T, T_max);
+  if (T < 0 || T > T_max) return fail(AAH_ERR_INVALID_ARG, "prefill length T = %d must be in [0, T_max = %d]", T, T_max);
+  if (empty_problem(B, T)) return AAH_OK;
   AAH_TRY(check_tensor(k, "k", 16));
   AAH_TRY(check_tensor(v, "v", 16));
   AAH_TRY(check_tensor(kcache, "kcache", 16));
@@ -1057,6 +1073,8 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
                            size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   AAH_TRY(check_decode(windows, sinks, B, H, H_kv, T_max, d, dt));
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (B == 0) return AAH_OK;  // no sequences: nothing to decode
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k_new, "k_new", 16));
   AAH_TRY(check_tensor(v_new, "v_new", 16));
@@ -1065,7 +1083,6 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
   AAH_TRY(check_tensor(pos, "pos", 4));
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   const size_t need = decode_workspace(windows, sinks, B, H, H_kv, T_max, d);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(AAH_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace == nullptr ? 0 : workspace_bytes,
@@ -1090,6 +1107,7 @@ aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void*
   // The same checks as aah_attn_decode, on fixed-size tables: nothing here allocates (host or device).
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
   AAH_TRY(check_dims(B, H, T_max, d, dt));
+  if (T_max < 1) return fail(AAH_ERR_INVALID_ARG, "T_max must be >= 1 (got %d)", T_max);
   AAH_TRY(check_kv_heads(H, H_kv));
   AAH_TRY(check_windows(windows, sinks, H));
   if (dt != AAH_BF16) return fail(AAH_ERR_UNSUPPORTED, "decoding runs on bf16 caches only");
@@ -1098,6 +1116,8 @@ aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void*
                 aah::kNoAllocMaxHeads);
   if (static_cast<int64_t>(B) * H_kv > 65535)
     return fail(AAH_ERR_UNSUPPORTED, "B * H_kv = %lld exceeds 65535", static_cast<long long>(B) * H_kv);
+  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
+  if (B == 0) return AAH_OK;  // no sequences: nothing to decode
   AAH_TRY(check_tensor(q, "q", 16));
   AAH_TRY(check_tensor(k_new, "k_new", 16));
   AAH_TRY(check_tensor(v_new, "v_new", 16));
@@ -1106,7 +1126,6 @@ aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void*
   AAH_TRY(check_tensor(pos, "pos", 4));
   AAH_TRY(check_tensor(o, "o", 16));
   AAH_TRY(check_tensor(lse, "lse", 4));
-  if (!std::isfinite(scale) || scale == 0.0f) return fail(AAH_ERR_INVALID_ARG, "scale must be finite and nonzero");
   // Per query head C_h and effective sink, per key/value head ring and sink rows (as decode_shape).
   aah::NoAllocHeads heads;
   const int G = H / H_kv;

@@ -67,6 +67,11 @@
  *   - Supported: dt = AAH_BF16 with d in {32, 64, 128}; dt = AAH_F32 with d in
  *     {32, 64, 128}; any T >= 1 (ragged tails are masked) with T * d * 4 < 2^31
  *     (one head's slice is addressed with 32-bit offsets).
+ *   - Empty problems: B = 0 or T = 0 (decoding: B = 0; the cache fill: B = 0 or
+ *     T = 0) leave nothing to compute.  The call checks its other arguments
+ *     (H >= 1, windows, sinks, H_kv, d, dt, scale) and returns AAH_OK without
+ *     touching any tensor or workspace, which may then be NULL (an empty
+ *     tensor has no storage).  aah_head_features has no empty case.
  */
 #ifndef AAH_ATTN_H
 #define AAH_ATTN_H
@@ -78,11 +83,11 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 10
+#define AAH_ABI_VERSION 11
 
 typedef enum {
   AAH_OK = 0,
-  AAH_ERR_INVALID_ARG = 1,  /* null pointer, size < 1, window < 1, misalignment (of any tensor or
+  AAH_ERR_INVALID_ARG = 1,  /* null pointer, negative size (or H < 1), window < 1, misalignment (of any tensor or
                                workspace), non-finite scale */
   AAH_ERR_UNSUPPORTED = 2,  /* dtype / head dim combination without a kernel */
   AAH_ERR_WORKSPACE = 3,    /* workspace smaller than aah_attn_workspace_size() */
@@ -195,8 +200,9 @@ aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const 
  *   features_ema = init ? x : alpha * features_ema + (1 - alpha) * x,
  * with 0 <= alpha <= 1 (the pages use 0.9, initialised from the first x).  At
  * least one of features, features_ema must be given.  q, k, v as for the
- * forward.  Workspace: aah_head_features_workspace_size(B, H, T, d) bytes,
- * 256-byte aligned, scratch.  Deterministic: the same inputs give the same bits.
+ * forward, with B, T >= 1 (the statistics are means over tokens).  Workspace:
+ * aah_head_features_workspace_size(B, H, T, d) bytes, 256-byte aligned,
+ * scratch.  Deterministic: the same inputs give the same bits.
  */
 size_t aah_head_features_workspace_size(int B, int H, int T, int d);
 
@@ -289,7 +295,7 @@ size_t aah_attn_decode_workspace_size(const int32_t* windows, const int32_t* sin
 
 /*
  * Prefill into the caches: k, v [B,H_kv,T,d] hold positions 0 .. T - 1
- * (1 <= T <= T_max); writes the positions each key/value head keeps (its first
+ * (0 <= T <= T_max; T_max >= 1); writes the positions each key/value head keeps (its first
  * min(S_g, T) into the sink rows, its last min(R_g, T) into the ring) into
  * their rows.  Other rows are left as they are.
  */

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 10
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 11
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -56,8 +56,9 @@ def _fwd(windows, B=1, H=None, T=64, d=64, dt=0, q=FAKE, k=FAKE, v=FAKE, o=FAKE,
 @pytest.mark.parametrize("kwargs,status", [
     (dict(windows=[4, 0]), 1),                    # window < 1
     (dict(windows=[4, -3]), 1),
-    (dict(windows=[4], B=0), 1),                  # B < 1
-    (dict(windows=[4], T=0), 1),
+    (dict(windows=[4], B=-1), 1),                 # negative sizes (B = 0 or T = 0 is an empty problem)
+    (dict(windows=[4], T=-1), 1),
+    (dict(windows=[4], H=0), 1),                  # H < 1
     (dict(windows=[4], d=48), 2),                 # unsupported head dim
     (dict(windows=[4], d=256), 2),
     (dict(windows=[4], dt=7), 2),                 # unknown dtype
@@ -302,7 +303,7 @@ def test_decode_validation():
     assert call(7, negs.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))) == 1
     # aah_kv_cache_fill(k, v, windows, sinks, B, H, H_kv, T, T_max, d, dt, kcache, vcache, stream)
     assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 129, 128, 64, 0, F, F, None) == 1   # T > T_max
-    assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 0, 128, 64, 0, F, F, None) == 1     # T = 0
+    assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, -1, 128, 64, 0, F, F, None) == 1    # T < 0
     assert lib.aah_kv_cache_fill(0, F, wp, None, 2, 2, 2, 64, 128, 64, 0, F, F, None) == 1    # NULL k
     assert lib.aah_kv_cache_fill(F, F, wp, None, 2, 2, 2, 64, 128, 64, 1, F, F, None) == 2    # fp32
 
@@ -395,3 +396,50 @@ def test_missing_library_fails_loudly():
                          cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
     assert res.returncode == 0, res.stderr
     assert "raised:" in res.stdout and "missing" in res.stdout and "no fallback" in res.stdout
+
+
+def test_empty_problems():
+    """B = 0 or T = 0 (decoding: B = 0) is an empty problem: every other argument is still checked, then the call
+    returns AAH_OK without touching a tensor or the workspace, so all of them may be NULL."""
+    lib = _lib.lib()
+    w = np.array([16, 64], dtype=np.int32)
+    wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    bad = np.array([16, 0], dtype=np.int32)
+    bp = bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    N = None
+    for B, T in ((0, 64), (3, 0), (0, 0)):
+        # aah_attn_fwd(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, ws, bytes, stream)
+        assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 0
+        assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 1, T, 32, 1, 0.125, N, N, N, 0, N) == 0
+        assert lib.aah_attn_fwd_diag(N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, N, N) == 0
+        # aah_attn_bwd(q, k, v, o, dout, lse, windows, sinks, B, H, H_kv, T, d, dt, scale, dq, dk, dv, ws, bytes, s)
+        assert lib.aah_attn_bwd(N, N, N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, N, 0, N) == 0
+        assert lib.aah_attn_bwd_dq(N, N, N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, 0, N) == 0
+        assert lib.aah_attn_bwd_dkdv(N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 0
+        # aah_kv_cache_fill(k, v, windows, sinks, B, H, H_kv, T, T_max, d, dt, kcache, vcache, stream)
+        assert lib.aah_kv_cache_fill(N, N, wp, N, B, 2, 2, T, 128, 64, 0, N, N, N) == 0
+        # the workspace queries agree: an empty problem needs none
+        assert lib.aah_attn_workspace_size(B, 2, T, 64, 0, 1) == 0
+        assert lib.aah_attn_fwd_workspace_size(wp, N, B, 2, 2, T, 64, 0) == 0
+        assert lib.aah_attn_bwd_split_workspace_size(wp, N, B, 2, 2, T, 64, 0) == 0
+        # the statistics of the controller features are means over tokens: no empty case
+        assert lib.aah_head_features(N, N, N, N, N, wp, B, 2, 2, T, 64, 0, 0.9, 1, N, N, N, 0, N) == 1
+        # the other arguments are still checked
+        assert lib.aah_attn_fwd(N, N, N, bp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 1   # window 0
+        assert lib.aah_attn_fwd(N, N, N, N, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 1    # NULL windows
+        assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 2, T, 48, 0, 0.125, N, N, N, 0, N) == 2   # d = 48
+        assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 2, T, 64, 0, float("nan"), N, N, N, 0, N) == 1
+        assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 3, T, 64, 0, 0.125, N, N, N, 0, N) == 1   # H_kv > H
+        assert lib.aah_attn_bwd(N, N, N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.0, N, N, N, N, 0, N) == 1
+        assert lib.aah_attn_bwd_dkdv(N, N, N, N, bp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 1
+    # decoding: no sequences
+    # aah_attn_decode(q, k_new, v_new, kcache, vcache, pos, windows, sinks, B, H, H_kv, T_max, d, dt, scale, o, lse,
+    #                 ws, bytes, stream)
+    assert lib.aah_attn_decode(N, N, N, N, N, N, wp, N, 0, 2, 2, 128, 64, 0, 0.125, N, N, N, 0, N) == 0
+    assert lib.aah_attn_decode_noalloc(N, N, N, N, N, N, wp, N, 0, 2, 2, 128, 64, 0, 0.125, N, N, N) == 0
+    assert lib.aah_attn_decode_workspace_size(wp, N, 0, 2, 2, 128, 64, 0) == 0
+    assert lib.aah_attn_decode(N, N, N, N, N, N, wp, N, 0, 2, 2, 0, 64, 0, 0.125, N, N, N, 0, N) == 1    # T_max = 0
+    assert lib.aah_attn_decode_noalloc(N, N, N, N, N, N, wp, N, 0, 2, 2, 0, 64, 0, 0.125, N, N, N) == 1  # T_max = 0
+    assert lib.aah_attn_decode(N, N, N, N, N, N, wp, N, 0, 2, 2, 128, 64, 1, 0.125, N, N, N, 0, N) == 2  # fp32
+    assert lib.aah_attn_decode(N, N, N, N, N, N, wp, N, -1, 2, 2, 128, 64, 0, 0.125, N, N, N, 0, N) == 1
+    assert lib.aah_kv_cache_fill(N, N, wp, N, 2, 2, 2, 0, 0, 64, 0, N, N, N) == 1    # T_max = 0

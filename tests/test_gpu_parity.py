@@ -250,3 +250,40 @@ def test_backward_deterministic_and_steps():
     for a, b, c in zip(g1, g2, (dq, dk, dv)):
         assert torch.equal(a, b)
         assert torch.equal(a, c)
+
+
+@pytest.mark.parametrize("B,T", [(0, 64), (2, 0)])
+def test_empty_problems(B, T):
+    """B = 0 or T = 0: every call returns empty results (nothing is computed; empty tensors have no storage),
+    and a prefill of no tokens leaves the caches as they were."""
+    _require_gpu()
+    H, H_kv, d = 4, 2, 64
+    windows = [3, 16, 64, 200]
+    for dt in (torch.bfloat16, torch.float32):
+        q = torch.zeros((B, H, T, d), dtype=dt, device="cuda")
+        k = torch.zeros((B, H_kv, T, d), dtype=dt, device="cuda")
+        v = torch.zeros_like(k)
+        o, lse = aah.attn_fwd(q, k, v, windows)
+        assert o.shape == (B, H, T, d) and lse.shape == (B, H, T)
+        dq, dk, dv = aah.attn_bwd(q, k, v, o, torch.zeros_like(q), lse, windows)
+        assert dq.shape == q.shape and dk.shape == k.shape and dv.shape == v.shape
+    q = torch.zeros((B, H, T, d), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((B, H_kv, T, d), dtype=torch.bfloat16, device="cuda")
+    o, lse, ent, onorm = aah.attn_fwd_diag(q, k, k, windows)
+    assert ent.shape == (B, H, T) and onorm.shape == (B, H, T)
+    T_max = 128
+    R = aah.kv_cache_rows(windows, T_max, H_kv=H_kv)
+    kc = torch.full((B, R, d), 7.0, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((B, R, d), -3.0, dtype=torch.bfloat16, device="cuda")
+    aah.kv_cache_fill(k, k, windows, T_max, kcache=kc, vcache=vc)
+    torch.cuda.synchronize()
+    assert bool((kc == 7.0).all()) and bool((vc == -3.0).all())
+    if B == 0:
+        qd = torch.zeros((0, H, d), dtype=torch.bfloat16, device="cuda")
+        kn = torch.zeros((0, H_kv, d), dtype=torch.bfloat16, device="cuda")
+        pos = torch.zeros((0,), dtype=torch.int32, device="cuda")
+        od, ld = aah.attn_decode(qd, kn, kn, kc, vc, pos, windows, T_max)
+        assert od.shape == (0, H, d) and ld.shape == (0, H)
+        aah.attn_decode_noalloc(qd, kn, kn, kc, vc, pos, windows, T_max, out=torch.empty_like(qd),
+                                lse=torch.empty((0, H), dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
