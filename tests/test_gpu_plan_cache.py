@@ -5,7 +5,7 @@ Every call below uses a window vector not seen before, so every call builds, upl
 pinned staging memory) and, once the cache is full, evicts a work list; every result is checked against the
 fp64 oracle (bounds of tests/test_gpu_parity.py), and the cache never holds more than its capacity.  A list
 built on one stream and used at once on another (which must wait for the upload) is checked too, as is the
-refusal to build a list during graph capture.
+refusal to build a list during graph capture, and a list too large for the staging ring (synchronous upload).
 """
 import warnings
 
@@ -133,3 +133,34 @@ def test_no_list_is_built_during_graph_capture():
         g.replay()
         torch.cuda.synchronize()
         _check_fwd(wl, o, lse)
+
+
+def test_work_list_larger_than_staging_ring():
+    """A work list over 4 MiB (more than a quarter of a million items: here B = 1100, H = 256, one tile per
+    head) does not fit the pinned staging ring and takes the synchronous upload, and hipFree on release.
+    Forward and backward, run twice (the second call reuses the cached list), checked against the oracle on
+    sampled batch entries; the windows (1, 2 and 3 over T = 3 tokens) give every row a different key set."""
+    _require_gpu()
+    aah.cache_clear()
+    B, H, T, d = 1100, 256, 3, 32
+    assert B * H * 16 > 4 << 20
+    windows = [1 + h % 3 for h in range(H)]
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=77, backward=True)
+    q, k, v, do = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v"), _dev(wl, "do")
+    sel = [0, 1, 549, 1099]
+    sub = dict(q=wl.q[sel], k=wl.k[sel], v=wl.v[sel])
+    O, L = oracle.attn_fwd_ref(sub["q"], sub["k"], sub["v"], wl.windows, wl.scale)
+    refs = oracle.attn_bwd_ref(sub["q"], sub["k"], sub["v"], wl.windows, wl.scale, wl.do[sel])
+    for rep in range(2):
+        o, lse = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+        dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale)
+        torch.cuda.synchronize()
+        got = o[sel].float().cpu().numpy().astype(np.float64)
+        assert (np.abs(got - O) - np.maximum(O_TOL, np.abs(O) * 2.0 ** -8)).max() <= 0, rep
+        assert np.abs(lse[sel].cpu().numpy() - L).max() < LSE_TOL, rep
+        for g, ref in zip((dq, dk, dv), refs):
+            err = np.abs(g[sel].float().cpu().numpy() - ref).max()
+            assert err <= GRAD_REL * np.abs(ref).max(), rep
+    assert aah.cache_entries() >= 1
+    aah.cache_clear()
+    assert aah.cache_entries() == 0
