@@ -1,4 +1,5 @@
-"""Long sequences: T = 2^17 positions per head, 32 times the bench layers, through the C ABI.
+"""Long sequences through the C ABI: T = 2^17 positions per head (32 times the bench layers), and the
+largest T the ABI accepts at d = 128 (4,194,303: one head's fp32 slice just under 2^31 bytes).
 
 Forward: sampled rows (start, every power-of-two boundary region, middle, end) against
 oracle.attn_fwd_rows_ref.  Backward: with window W a query row needs only the W keys ending at it, and a
@@ -121,3 +122,84 @@ def test_long_sequence_backward_slices():
         for h, (a, b), g, r in items:
             err = np.abs(g - r).max()
             assert err <= GRAD_REL * scale, f"{name} head {h} slice [{a}, {b}): {err:.3e} vs {GRAD_REL * scale:.3e}"
+
+
+def fwd_row_slice(T, W, i):
+    """The slice [a, i + 1) of the sequence holding every key row i of a window-W head sees (no sinks)."""
+    return max(0, i - W + 1), i + 1
+
+
+@pytest.mark.parametrize("W", [1, 7, 40])
+def test_forward_row_slice_equals_full_sequence_oracle(W):
+    """CPU pin of the forward slicing rule: the oracle run on `fwd_row_slice` gives row i exactly the whole
+    sequence's output and log-sum-exp."""
+    T = 300
+    wl = synth.random_workload(1, 1, T, 8, [W], dtype="f32", seed=50 + W, backward=False)
+    fo, fl = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, [W], wl.scale)
+    for i in (0, 1, W - 1, W, 150, T - 1):
+        if i < 0:
+            continue
+        a, b = fwd_row_slice(T, W, i)
+        ro, rl = oracle.attn_fwd_rows_ref(wl.q[0, 0, a:b], wl.k[0, 0, a:b], wl.v[0, 0, a:b], W, wl.scale, [i - a])
+        assert np.allclose(ro[0], fo[0, 0, i], rtol=0, atol=1e-12) and abs(rl[0] - fl[0, 0, i]) < 1e-12
+
+
+# The largest T the ABI takes at d = 128: one head's fp32 [T, d] slice just under 2^31 bytes (its kernels
+# address a slice with 32-bit byte offsets; T * d * 4 >= 2^31 is refused).
+T_MAX_D128 = ((1 << 31) - 1) // (4 * 128)
+MAX_WINDOWS = [40, 3]
+MAX_ROWS = [0, 1, 39, 40, 41, 127, 128, T_MAX_D128 // 2, (1 << 21) + 5, T_MAX_D128 - 129, T_MAX_D128 - 128,
+            T_MAX_D128 - 2, T_MAX_D128 - 1]
+
+
+def _device_normal(shape, seed, dtype):
+    """Seeded N(0, 1) inputs drawn on the device (a whole input set is 8-16 GiB); the oracle reads the same
+    bits back, row slice by row slice."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(dtype)
+
+
+def _rows64(t, h, a, b):
+    return t[0, h, a:b].float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dt", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_largest_sequence_forward_and_backward(dt):
+    """T = 4,194,303 at d = 128 (the fp32 slice's last row ends 512 bytes below 2^31): forward rows at the
+    start, the middle and the end against the oracle on each row's slice, and backward slices at the start,
+    past 2^21 rows and at the end (rows `exact_rows` keeps), bf16 and fp32."""
+    if not torch.cuda.is_available():
+        pytest.fail("this test needs a HIP device")
+    T, d, H = T_MAX_D128, 128, len(MAX_WINDOWS)
+    assert T * d * 4 < (1 << 31) <= (T + 1) * d * 4
+    scale = 1.0 / np.sqrt(d)
+    q, k, v, do = (_device_normal((1, H, T, d), 100 + i, dt) for i in range(4))
+    o, lse = aah.attn_fwd(q, k, v, MAX_WINDOWS, scale)
+    dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, MAX_WINDOWS, scale=scale)
+    torch.cuda.synchronize()
+    o_tol = O_TOL_BF16 if dt == torch.bfloat16 else 1e-5
+    l_tol = LSE_TOL_BF16 if dt == torch.bfloat16 else 1e-5
+    for h, W in enumerate(MAX_WINDOWS):
+        for i in MAX_ROWS:
+            a, b = fwd_row_slice(T, W, i)
+            ro, rl = oracle.attn_fwd_rows_ref(_rows64(q, h, a, b), _rows64(k, h, a, b), _rows64(v, h, a, b), W,
+                                              scale, [i - a])
+            got = o[0, h, i].float().cpu().numpy().astype(np.float64)
+            bound = np.maximum(o_tol, np.abs(ro[0]) * 2.0 ** -8) if dt == torch.bfloat16 else o_tol
+            assert (np.abs(got - ro[0]) - bound).max() <= 0, f"head {h} row {i}"
+            assert abs(float(lse[0, h, i]) - rl[0]) < l_tol, f"head {h} row {i}"
+        half = 2 * W + 64
+        for c in (0, (1 << 21) + 5, T - 1):
+            a, b = max(0, c - half), min(T, c + half)
+            sl = (slice(0, 1), slice(h, h + 1), slice(a, b))
+            rq, rk, rv = oracle.attn_bwd_ref(*(t[sl].float().cpu().numpy().astype(np.float64) for t in (q, k, v)),
+                                             [W], scale, do[sl].float().cpu().numpy().astype(np.float64))
+            q_rows, k_rows = exact_rows(T, W, a, b)
+            for name, got, ref, rows in (("dq", dq, rq, q_rows), ("dk", dk, rk, k_rows), ("dv", dv, rv, k_rows)):
+                g = _rows64(got, h, a, b)[rows - a]
+                r = ref[0, 0, rows - a]
+                err = np.abs(g - r).max()
+                bound = (GRAD_REL if dt == torch.bfloat16 else 1e-4) * np.abs(r).max()
+                assert err <= bound, f"{name} head {h} slice [{a}, {b}): {err:.3e} vs {bound:.3e}"
