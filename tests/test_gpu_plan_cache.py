@@ -5,7 +5,8 @@ Every call below uses a window vector not seen before, so every call builds, upl
 pinned staging memory) and, once the cache is full, evicts a work list; every result is checked against the
 fp64 oracle (bounds of tests/test_gpu_parity.py), and the cache never holds more than its capacity.  A list
 built on one stream and used at once on another (which must wait for the upload) is checked too, as is the
-refusal to build a list during graph capture, and a list too large for the staging ring (synchronous upload).
+refusal to build a list during graph capture, a list too large for the staging ring (synchronous upload), and
+eight host threads on streams of their own building and using lists at the same time.
 """
 import warnings
 
@@ -164,3 +165,47 @@ def test_work_list_larger_than_staging_ring():
     assert aah.cache_entries() >= 1
     aah.cache_clear()
     assert aah.cache_entries() == 0
+
+
+def test_concurrent_host_threads():
+    """Eight host threads, each on a stream of its own, run forwards and backwards at the same time, each call
+    with a window vector no other call uses (48 in all, within the cache's capacity, so no list is evicted
+    while another stream may still read it): every list is built, uploaded and used under the library's lock,
+    and every result matches the oracle."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    _require_gpu()
+    torch.cuda.synchronize()
+    aah.cache_clear()
+    B, H, T, d = 1, 3, 160, 64
+    wl = synth.random_workload(B, H, T, d, [1] * H, dtype="bf16", seed=404, backward=True)
+    q, k, v, do = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v"), _dev(wl, "do")
+    torch.cuda.synchronize()
+
+    def windows(tid, it):
+        return [1 + tid, 20 + 10 * it, 100 + 6 * tid + it]
+
+    def worker(tid):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.default_stream())
+        out = []
+        with torch.cuda.stream(s):
+            for it in range(6):
+                w = windows(tid, it)
+                o, lse = aah.attn_fwd(q, k, v, w, wl.scale, stream=s)
+                dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, w, wl.scale, stream=s)
+                out.append((w, o, lse, dq, dk, dv))
+        s.synchronize()
+        return out
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        results = [r for rs in ex.map(worker, range(8)) for r in rs]
+    assert len({tuple(r[0]) for r in results}) == 48
+    for w, o, lse, dq, dk, dv in results:
+        wl.windows = np.asarray(w, dtype=np.int32)
+        _check_fwd(wl, o, lse)
+        refs = oracle.attn_bwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, wl.do)
+        for got, ref in zip((dq, dk, dv), refs):
+            err = np.abs(got.float().cpu().numpy() - ref).max()
+            assert err <= GRAD_REL * np.abs(ref).max(), w
+    assert aah.cache_entries() <= 3 * CAPACITY
