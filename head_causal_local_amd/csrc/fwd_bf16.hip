@@ -118,7 +118,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
                      float* __restrict__ ONORM, const WorkItem* __restrict__ items,
                      const int32_t* __restrict__ win_eff, const int32_t* __restrict__ sink_eff, int H, int H_kv,
                      int T, float c, const int32_t* __restrict__ slots, float* __restrict__ part_acc,
-                     float* __restrict__ part_ml) {
+                     float* __restrict__ part_ml, int h_shift, int g_shift) {
   using C = Cfg<D>;
   constexpr int NC = C::kNC;
   constexpr int KT = C::kKT;
@@ -129,8 +129,14 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const WorkItem it = items[blockIdx.x];
   // The kernel arguments the prologue needs are read here, so that their loads go out with the
   // item's rather than one scalar round trip after the padding test.
-  __asm__ volatile("" ::"s"(H), "s"(H_kv), "s"(T), "s"(Q), "s"(K), "s"(V), "s"(slots), "s"(win_eff));
+  __asm__ volatile("" ::"s"(H), "s"(H_kv), "s"(T), "s"(Q), "s"(K), "s"(V), "s"(slots), "s"(win_eff), "s"(h_shift),
+                   "s"(g_shift));
   if (it.bh < 0) return;  // padding slot (uniform over the workgroup)
+  // Head h = bh mod H of batch entry bh / H, and its key/value head h / G (G = H / H_kv): shifts and masks
+  // when H (and G) are powers of two (h_shift, g_shift >= 0), else divisions.
+  const int hq = h_shift >= 0 ? it.bh & ((1 << h_shift) - 1) : it.bh % H;
+  const int bq = h_shift >= 0 ? it.bh >> h_shift : it.bh / H;
+  const int hkv = g_shift >= 0 ? hq >> g_shift : hq / (H / H_kv);
   // A chunk of a split item leaves its rows' partial result in its slot instead of O and LSE.
   const int slot = slots != nullptr ? slots[blockIdx.x] : -1;
   // The window (and sink size) come from a table indexed by the item's head.  Where the first
@@ -138,8 +144,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   // so that waiting for it (scalar loads complete in any order) does not hold them back.
   constexpr bool kLateW = kSub == 1 && !SINK;
   int W = 0;
-  if constexpr (!kLateW) W = win_eff[it.bh % H];
-  const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
+  if constexpr (!kLateW) W = win_eff[hq];
+  const int S = SINK ? sink_eff[hq] : 0;  // keys 0 .. S - 1 are sinks
   // Stages (KT keys each) in visiting order: sink stages 0 .. ns - 1 (those before the window's first
   // stage), then the window's stages w_lo .. w_hi - 1 -- the planner's tiles [lo, hi) trimmed to the keys
   // [q0 - W + 1, q1 - 1] the item's rows see.
@@ -150,8 +156,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int n_tiles = ns + w_hi - w_lo;
   auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + w_lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
-  // Key/value head of this query head: its group's, h / (H / H_kv).
-  const size_t kvbase = (static_cast<size_t>(it.bh / H) * H_kv + (it.bh % H) / (H / H_kv)) * T * D;
+  const size_t kvbase = (static_cast<size_t>(bq) * H_kv + hkv) * T * D;
   const bf16* Qh = Q + base;
   const bf16* Kh = K + kvbase;
   const bf16* Vh = V + kvbase;
@@ -307,13 +312,18 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
       const float m_new = fmaxf(m_run, half_swap_max(mx) * c);
-      if (m_new > m_run) {
-        // m_run = -inf (nothing seen yet): alpha = 0 clears the still-empty state.
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        if constexpr (DIAG) a_run = m_run == -INFINITY ? 0.f : alpha * fmaf(m_run - m_new, l_run, a_run);
+      // Only rows that held a finite reference rescale their sums when it moves up: a row whose
+      // reference is still -inf has seen no visible key, so its sums are exactly 0.  On a wave's first
+      // block no row has one, and the rescaling is skipped.
+      const bool rescale = m_new > m_run && m_run != -INFINITY;
+      if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+        const float alpha = rescale ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        if constexpr (DIAG) a_run = rescale ? alpha * fmaf(m_run - m_new, l_run, a_run) : a_run;
         l_run *= alpha;
 #pragma unroll
         for (int b = 0; b < C::kBlocks; ++b) acc[b] *= alpha;
+      }
+      if (m_new > m_run) {
         m_run = m_new;
         m_use = m_new;
       }
@@ -374,7 +384,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     for (int s = 0; s < C::kSteps; ++s)
       qf[s] = __builtin_bit_cast(bf16x8, load16(rq, static_cast<uint32_t>(qi) * C::kRowBytes + (16 * s + 8 * hl) * 2));
     if constexpr (kLateW) {
-      W = win_eff[it.bh % H];
+      W = win_eff[hq];
       wave_key_lo = q0w - W + 1;
     }
     // Consume the fragments here, so that the compiler waits for these loads now
@@ -429,7 +439,7 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     if (hl == 0) *reinterpret_cast<u32x2*>(part_ml + prow * 2) = u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)};
     return;
   }
-  const float inv = 1.f / l_tot;
+  const float inv = __builtin_amdgcn_rcpf(l_tot);  // l_tot >= 1: the key that set the reference weighs 1
   bf16* Orow = O + base + static_cast<size_t>(qi) * D;
   // O^T block b, register r holds dim 32 b + 8 (r/4) + 4 hl + r%4 of query qi.
 #pragma unroll
@@ -490,7 +500,7 @@ void launch_k(const void* q, const void* k, const void* v, void* o, float* lse, 
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<bf16*>(o), lse, ent, onorm, items, win_eff, sink_eff, s.H, s.H_kv, s.T, c,
                      split != nullptr ? split->slots : nullptr, split != nullptr ? split->part_acc : nullptr,
-                     split != nullptr ? split->part_ml : nullptr);
+                     split != nullptr ? split->part_ml : nullptr, log2_exact(s.H), log2_exact(s.H / s.H_kv));
   if (split != nullptr && split->n_merges > 0)
     hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3(split->n_merges, kRows / (256 / (D / 4))), dim3(256), 0, stream,
                        split->merges, split->part_acc, split->part_ml, static_cast<bf16*>(o), lse, s.T);

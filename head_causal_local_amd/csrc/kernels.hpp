@@ -31,6 +31,14 @@ struct AttnShape {
   int H_kv;             // key/value heads; query head h reads head h / (H / H_kv)
 };
 
+// log2(n) when n is a power of two, else -1: the kernels split a (batch, head) index with a shift and a
+// mask instead of a division when the head counts allow it.
+inline int log2_exact(int n) {
+  int l = 0;
+  while (l < 30 && (1 << l) < n) ++l;
+  return (1 << l) == n ? l : -1;
+}
+
 // bf16 forward on MFMA (d in {32, 64, 128}).  ent / onorm: nullptr, or fp32
 // [B,H,T] outputs of each row's attention entropy and output-row norm (both set
 // or both null).
