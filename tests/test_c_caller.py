@@ -21,7 +21,7 @@ def _build(tmp_path):
     if shutil.which("gcc") is None:
         pytest.skip("gcc is not installed")
     if not os.path.exists(os.path.join(PKG, "libaah_attn.so")):
-        pytest.fail("libaah_attn.so is not built (run __graft_entry__.build())")
+        pytest.fail("libaah_attn.so is not built (python -m head_causal_local_amd.build)")
     exe = tmp_path / "c_caller"
     subprocess.run(["gcc", "-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
                     "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
