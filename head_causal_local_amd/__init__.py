@@ -94,13 +94,16 @@ def _kv_heads(q, k, v) -> int:
     return H_kv
 
 
-def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None, sinks=None):
+def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, stream=None, sinks=None,
+             workspace=None):
     """O, LSE = local-window attention of q, k, v ([B, H, T, d] device tensors).
 
     windows: one int per head (>= 1; values above T act as T).  sinks: None or
     one int per head (>= 0), the number of leading keys every later query also
-    sees.  scale defaults to 1/sqrt(d).  Returns (O with q's dtype, LSE float32
-    [B, H, T])."""
+    sees.  scale defaults to 1/sqrt(d).  workspace: None (the call asks the
+    library how much it needs for a split launch and allocates it), or a device
+    tensor the caller keeps, of at least fwd_workspace_size(...) bytes (an empty
+    one means no split).  Returns (O with q's dtype, LSE float32 [B, H, T])."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
@@ -121,9 +124,13 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
     elif lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     sk = _sinks_arg(sinks, H)
-    # Workspace for the split launch (partial results of long items' chunks) when the library asks for one.
-    ws_bytes = lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, T, d, _dtype_code(q))
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    if workspace is None:
+        # Workspace for the split launch (partial results of long items' chunks) when the library asks for one.
+        ws_bytes = lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, T, d, _dtype_code(q))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+        ws = workspace if ws_bytes else None
     st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d,
                             _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(),
                             ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q, stream))

@@ -110,6 +110,25 @@ def test_split_forward_grouped_heads_matches_oracle():
     assert (lse - lu).abs().max().item() < 2 * LSE_TOL_BF16
 
 
+def test_caller_workspace_through_the_binding():
+    """attn_fwd with a workspace the caller keeps: one of fwd_workspace_size bytes gives the split launch's
+    results bitwise (the same as the binding's own allocation), an empty one the unsplit launch's."""
+    _require_gpu()
+    wl = synth.make_workload(1)
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    q, k, v = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v")
+    n = aah.fwd_workspace_size(wl.windows, B, H, T, d)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    o1, l1 = aah.attn_fwd(q, k, v, wl.windows, wl.scale, workspace=ws)
+    o2, l2 = aah.attn_fwd(q, k, v, wl.windows, wl.scale)
+    o3, l3 = aah.attn_fwd(q, k, v, wl.windows, wl.scale, workspace=torch.empty(0, dtype=torch.uint8, device="cuda"))
+    ou, lu = _fwd_unsplit(q, k, v, wl.windows, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    assert torch.equal(o3, ou) and torch.equal(l3, lu)
+
+
 def test_split_close_to_unsplit_and_deterministic():
     """The single-layer workload (B=1 H=16 T=4096): split and one-workgroup-per-item launches agree within
     the bf16 bounds, and repeated split launches are bitwise equal."""
