@@ -328,6 +328,9 @@ def cpu_baseline(wl, n_heads, with_bwd):
 
 def main():
     args = parse()
+    if args.steps < 1 or args.warmup < 0:
+        print(f"--steps must be >= 1 and --warmup >= 0 (got {args.steps}, {args.warmup})", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library runs every head of a layer on a single MI355X "
               "(no sharding or collectives); run with --gpus 1.", file=sys.stderr)

@@ -46,3 +46,11 @@ def test_more_than_one_gpu_is_refused():
                          text=True, timeout=120, cwd=ROOT)
     assert res.returncode != 0
     assert "one GPU" in (res.stdout + res.stderr)
+
+
+def test_step_counts_are_checked():
+    for flags in (["--steps", "0"], ["--warmup", "-1"]):
+        res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *flags], capture_output=True,
+                             text=True, timeout=120, cwd=ROOT)
+        assert res.returncode == 2, flags
+        assert "--steps must be" in res.stderr
