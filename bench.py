@@ -261,18 +261,31 @@ KERNEL_SOURCES = {  # kernel template name -> its source file
     "bwd_dq_kernel": "head_causal_local_amd/csrc/bwd_bf16.hip",
     "decode_kernel": "head_causal_local_amd/csrc/decode.hip",
 }
+KERNEL_HEADERS = ("head_causal_local_amd/csrc/device_common.hpp", "head_causal_local_amd/csrc/kernels.hpp")
+
+
+def kernel_source_sha(kernel):
+    """First 16 hex digits of the SHA-256 of a kernel's source file followed by the headers it includes (the
+    key of its rows in profiles/hbm_traffic.txt), or None for a kernel without a listed source."""
+    import hashlib
+    src = KERNEL_SOURCES.get(kernel.split("<")[0])
+    if src is None:
+        return None
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in (src,) + KERNEL_HEADERS:
+        h.update(open(os.path.join(root, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
     """HBM bytes per launch of `kernel` on `workload` from profiles/hbm_traffic.txt, if taken on the current
     kernel source."""
-    import hashlib
     root = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(root, "profiles", "hbm_traffic.txt")
-    src = KERNEL_SOURCES.get(kernel.split("<")[0])
-    if src is None or not os.path.exists(path):
+    sha = kernel_source_sha(kernel)
+    if sha is None or not os.path.exists(path):
         return None
-    sha = hashlib.sha256(open(os.path.join(root, src), "rb").read()).hexdigest()[:16]
     for line in open(path):
         parts = line.split()
         if line.startswith("#"):

@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
   };
   u32x4 qpiece = q_piece(0);
   const bool owns_new = row == new_ring || row == new_sink;
-  const uint32_t koff = any & !owns_new ? static_cast<uint32_t>(row) * D * 2 : kPast;
+  const uint32_t koff = (any & !owns_new) ? static_cast<uint32_t>(row) * D * 2 : kPast;
   bf16x8 kr[D / 8];
 #pragma unroll
   for (int i = 0; i < D / 8; ++i) kr[i] = __builtin_bit_cast(bf16x8, load16(rk, koff + 16 * i));

@@ -86,14 +86,16 @@ __device__ inline i32x4 uniform(const i32x4& r) {
 // deliver zeros.  Completion is counted by vmcnt and is the caller's to wait
 // for (wait_vm_barrier).  Issued as inline assembly so that the compiler's own
 // wait-count bookkeeping does not serialise later LDS reads of other buffers
-// behind these copies.
+// behind these copies.  The LDS address goes in M0, which the compiler itself
+// sets from the "{m0}" operand (it keeps M0 for its own uses, so the assembly
+// names it as an input rather than writing it).
 __device__ inline void dma16(const i32x4& rsrc, const void* lds_base, uint32_t byte_off) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) char*)(lds_base)));
-  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  __asm__ volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(uniform(rsrc))
-                   : "memory", "m0");
+                   : "v"(byte_off), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory");
 }
 
 // As dma16 with 4 bytes per lane (buffer_load_dword ... lds): lane i's word
@@ -101,10 +103,10 @@ __device__ inline void dma16(const i32x4& rsrc, const void* lds_base, uint32_t b
 __device__ inline void dma4(const i32x4& rsrc, const void* lds_base, uint32_t byte_off) {
   const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (const __attribute__((address_space(3))) char*)(lds_base)));
-  __asm__ volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  __asm__ volatile("buffer_load_dword %0, %1, 0 offen lds"
                    :
-                   : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(uniform(rsrc))
-                   : "memory", "m0");
+                   : "v"(byte_off), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory");
 }
 
 // Workgroup barrier after waiting until at most n of this wave's vector-memory

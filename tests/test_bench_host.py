@@ -30,8 +30,10 @@ def test_traffic_table_rows_are_well_formed():
 
 def test_traffic_lookup_matches_kernel_workload_and_source_hash():
     for kernel, workload, sha, fetch, write in _table():
-        src = os.path.join(ROOT, bench.KERNEL_SOURCES[kernel.split("<")[0]])
-        current = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        h = hashlib.sha256()
+        for f in (bench.KERNEL_SOURCES[kernel.split("<")[0]],) + bench.KERNEL_HEADERS:
+            h.update(open(os.path.join(ROOT, f), "rb").read())
+        current = h.hexdigest()[:16]
         got = bench.measured_traffic(kernel, workload)
         if current == sha:
             assert got == int(fetch) + int(write)
