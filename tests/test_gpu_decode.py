@@ -296,3 +296,37 @@ def test_decode_grouped_graph_replays_match_eager():
     ref_o, ref_l = oracle.decode_ref(qh[:, :, p], kh, vh, windows, np.array([p, p]), T_max, 1.0 / np.sqrt(d),
                                      sinks=sinks)
     _check_o(o, ref_o)
+
+
+@pytest.mark.parametrize("d,H,H_kv,windows,sinks", [
+    # a full-context head of 65536 rows (256 chunks: the merge reads its partials in 16 batches) beside a
+    # streaming head
+    (64, 2, 2, [65536, 300], [0, 17]),
+    # grouped heads: a group with the full-context ring and a sink head, a group with a ring of 5000 rows
+    # (20 chunks: two merge batches) and a window of 1
+    (128, 4, 2, [65536, 300, 5000, 1], [0, 17, 0, 0]),
+])
+def test_decode_long_context(d, H, H_kv, windows, sinks):
+    """T_max = 65536: prefill 65533 positions, then 3 steps (sequence 1 repeats its first position once), each
+    against the oracle over every attended position; the caches against the storage rule at the end."""
+    _require_gpu()
+    B, T_max, steps = 2, 65536, 3
+    T0 = T_max - steps
+    (qh, kh, vh), (q, k, v) = _history_g(B, H, H_kv, T_max, d, seed=7 + d)
+    scale = 1.0 / np.sqrt(d)
+    kc, vc = aah.kv_cache_fill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), windows, T_max, sinks=sinks)
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d, sinks=sinks, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
+    bi = np.arange(B)
+    for i in range(steps):
+        p = np.array([T0 + i, T0 + max(0, i - 1)])
+        pos = torch.tensor(p, dtype=torch.int32, device="cuda")
+        qt, kt, vt = q[bi, :, p].contiguous(), k[bi, :, p].contiguous(), v[bi, :, p].contiguous()
+        o, lse = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, scale=scale, workspace=ws, sinks=sinks)
+        ref_o, ref_l = oracle.decode_ref(qh[bi, :, p], kh, vh, windows, p, T_max, scale, sinks=sinks)
+        _check_o(o, ref_o)
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < LSE_TOL, i
+    torch.cuda.synchronize()
+    for cache, hist in ((kc, kh), (vc, vh)):
+        rows, valid = oracle.cache_content_ref(hist, windows, [T0 + steps, T0 + steps - 1], T_max, sinks)
+        assert np.array_equal(cache.float().cpu().numpy().astype(np.float64)[valid], rows[valid])
