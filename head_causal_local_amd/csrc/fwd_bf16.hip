@@ -61,7 +61,7 @@
 // the kernel already has: with w_j the bf16 weights that enter the row sum l
 // and x_j = s_j c - m their log2 offsets from the reference m, the entropy is
 // ln 2 (log2 l - sum_j w_j x_j / l).  The sum follows the reference like l does
-// (when m moves by -delta, a becomes alpha (a + delta l)).  Using the rounded
+// (when m moves up by delta, a becomes alpha (a - delta l), alpha = 2^-delta).  Using the rounded
 // weights for both sums makes the result the cross entropy of the normalised
 // rounded weights against the exact ones, within 2^-7 H + 2^-8 of the exact H.
 //
