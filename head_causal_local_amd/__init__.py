@@ -18,7 +18,7 @@ import numpy as np
 
 from ._lib import (AAH_BF16, AAH_F32, AahError, EXPORTS, LIB_PATH, WorkItem, check, lib)  # noqa: F401
 
-__all__ = ["attn_fwd", "attn_fwd_diag", "head_features", "head_features_workspace_size", "N_FEATURES", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "kv_cache_fill", "kv_cache_rows",
+__all__ = ["local_window_attention", "attn_fwd", "attn_fwd_diag", "head_features", "head_features_workspace_size", "N_FEATURES", "attn_bwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_decode", "kv_cache_fill", "kv_cache_rows",
            "decode_workspace_size", "workspace_size", "tile_shape", "plan_fwd", "plan_bwd", "window_stats",
            "cache_clear", "AahError", "LIB_PATH"]
 
@@ -256,6 +256,46 @@ def attn_bwd(q, k, v, o, do, lse, windows, scale: Optional[float] = None, dq=Non
 
 def _ws(workspace):
     return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+
+
+_AUTOGRAD_FN = None
+
+
+def _autograd_fn():
+    """The torch.autograd.Function behind local_window_attention (built on first use, so importing this
+    module does not import torch)."""
+    global _AUTOGRAD_FN
+    if _AUTOGRAD_FN is None:
+        import torch
+
+        class _LocalWindowAttention(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, q, k, v, windows, scale, sinks):
+                o, lse = attn_fwd(q, k, v, windows, scale, sinks=sinks)
+                ctx.save_for_backward(q, k, v, o, lse)
+                ctx.windows, ctx.scale, ctx.sinks = windows, scale, sinks
+                return o
+
+            @staticmethod
+            def backward(ctx, do):
+                q, k, v, o, lse = ctx.saved_tensors
+                dq, dk, dv = attn_bwd(q, k, v, o, do.contiguous(), lse, ctx.windows, ctx.scale, sinks=ctx.sinks)
+                return dq, dk, dv, None, None, None
+
+        _AUTOGRAD_FN = _LocalWindowAttention
+    return _AUTOGRAD_FN
+
+
+def local_window_attention(q, k, v, windows, scale: Optional[float] = None, sinks=None):
+    """O = local-window attention of q [B, H, T, d] and k, v [B, H_kv, T, d] (device tensors, bf16 or
+    float32), differentiable: autograd's backward runs aah_attn_bwd on the saved O and log-sum-exp.
+
+    windows: one int per query head (>= 1); sinks: None or one int per query head.  scale defaults to
+    1/sqrt(d).  For the log-sum-exp as well, call attn_fwd (not differentiable)."""
+    w = _windows_arg(windows)
+    sk = None if sinks is None else _windows_arg(sinks)
+    d = q.shape[-1]
+    return _autograd_fn().apply(q, k, v, w, 1.0 / math.sqrt(d) if scale is None else float(scale), sk)
 
 
 def _bwd_args(q, k, v, do, windows, scale):
