@@ -1,7 +1,8 @@
 """Seeded random shapes through the C ABI against the oracle: batch, query heads, key/value heads, length,
 head dimension, dtype, windows and sink sizes drawn from one generator (the list below is fixed by its seed),
 forward and backward.  Small layers have few work items, so the binding's split launches run here too.
-Bounds as in tests/test_gpu_parity.py."""
+Bounds as in tests/test_gpu_parity.py.  Random decoding layers likewise, against oracle.decode_ref and the
+cache storage rule."""
 import numpy as np
 import pytest
 import torch
@@ -63,3 +64,62 @@ def test_random_shape_forward_backward(case):
         scale = max(np.abs(r).max(), 1e-12)
         err = np.abs(g.float().cpu().numpy() - r).max()
         assert err <= rel * scale, f"{name}: {err:.3e} vs {rel * scale:.3e}"
+
+
+def _decode_shapes(n=24, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H_kv = int(rng.integers(1, 4))
+        H = H_kv * int(rng.integers(1, 6))
+        T_max = int(rng.integers(8, 1500))
+        d = int(rng.choice([32, 64, 128]))
+        windows = [int(x) for x in rng.integers(1, T_max + 40, size=H)]
+        sinks = None if rng.random() < 0.5 else [int(x) for x in rng.integers(0, T_max // 2 + 1, size=H)]
+        T0 = int(rng.integers(0, T_max - 3))
+        out.append((H, H_kv, T_max, d, windows, sinks, T0))
+    return out
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_decode_steps(case):
+    """Random layers of trimmed caches: a prefill of T0 positions (none when T0 = 0), then three decoding
+    steps per sequence (the second sequence a step behind), each against the oracle; the caches against the
+    storage rule at the end."""
+    if not torch.cuda.is_available():
+        pytest.fail("this test needs a HIP device")
+    H, H_kv, T_max, d, windows, sinks, T0 = _decode_shapes()[case]
+    print(f"decode case {case}: H={H} H_kv={H_kv} T_max={T_max} d={d} T0={T0} windows={windows} sinks={sinks}",
+          flush=True)
+    B, steps = 2, 3
+    L = T0 + steps
+    rng = np.random.default_rng(500 + case)
+    host, devs = [], []
+    for heads in (H, H_kv, H_kv):
+        bits = synth.bf16_bits(rng.standard_normal((B, heads, L, d), dtype=np.float32))
+        host.append(synth.bf16_to_f32(bits).astype(np.float64))
+        devs.append(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda"))
+    (qh, kh, vh), (q, k, v) = host, devs
+    scale = 1.0 / np.sqrt(d)
+    R = aah.kv_cache_rows(windows, T_max, sinks=sinks, H_kv=H_kv)
+    kc = torch.zeros((B, R, d), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros_like(kc)
+    if T0 > 0:
+        aah.kv_cache_fill(k[:, :, :T0].contiguous(), v[:, :, :T0].contiguous(), windows, T_max, kcache=kc,
+                          vcache=vc, sinks=sinks)
+    ws = torch.zeros(aah.decode_workspace_size(windows, B, T_max, d, sinks=sinks, H_kv=H_kv), dtype=torch.uint8,
+                     device="cuda")
+    bi = np.arange(B)
+    for i in range(steps):
+        p = np.array([T0 + i, T0 + max(0, i - 1)])
+        pos = torch.tensor(p, dtype=torch.int32, device="cuda")
+        qt, kt, vt = q[bi, :, p].contiguous(), k[bi, :, p].contiguous(), v[bi, :, p].contiguous()
+        o, lse = aah.attn_decode(qt, kt, vt, kc, vc, pos, windows, T_max, scale=scale, workspace=ws, sinks=sinks)
+        ref_o, ref_l = oracle.decode_ref(qh[bi, :, p], kh, vh, windows, p, T_max, scale, sinks=sinks)
+        got = o.float().cpu().numpy().astype(np.float64)
+        assert (np.abs(got - ref_o) - np.maximum(O_TOL_BF16, np.abs(ref_o) * 2.0 ** -8)).max() <= 0, i
+        assert np.abs(lse.cpu().numpy() - ref_l).max() < 1e-3, i
+    torch.cuda.synchronize()
+    for cache, hist in ((kc, kh), (vc, vh)):
+        rows, valid = oracle.cache_content_ref(hist, windows, [T0 + steps, T0 + steps - 1], T_max, sinks)
+        assert np.array_equal(cache.float().cpu().numpy().astype(np.float64)[valid], rows[valid])
