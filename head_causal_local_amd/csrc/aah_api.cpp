@@ -604,9 +604,10 @@ DecodeShape decode_shape(const int32_t* windows, const int32_t* sinks, int H, in
     s.ring[h / G] = std::max(s.ring[h / G], s.cap[h]);
     s.ksink[h / G] = std::max(s.ksink[h / G], s.sink[h]);
   }
+  const int cr = aah::decode_chunk_rows(H, H_kv);
   for (int g = 0; g < H_kv; ++g) {
     s.rows += s.ksink[g] + s.ring[g];
-    s.chunks += (s.ksink[g] + s.ring[g] + aah::kDecodeRows - 1) / aah::kDecodeRows;
+    s.chunks += (s.ksink[g] + s.ring[g] + cr - 1) / cr;
   }
   return s;
 }
@@ -637,10 +638,11 @@ aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, 
   std::vector<aah::DecodeChunk> chunks;
   int32_t off = 0;
   const int G = H / H_kv;
+  const int cr = aah::decode_chunk_rows(H, H_kv);
   for (int g = 0; g < H_kv; ++g) {
     const int32_t n = static_cast<int32_t>(sh.ksink[g] + sh.ring[g]);
     const int32_t first = static_cast<int32_t>(chunks.size());
-    const int32_t count = (n + aah::kDecodeRows - 1) / aah::kDecodeRows;
+    const int32_t count = (n + cr - 1) / cr;
     int64_t cap_s = INT64_MAX;
     for (int j = 0; j < G; ++j)
       if (sh.sink[g * G + j] > 0) cap_s = std::min(cap_s, sh.cap[g * G + j]);
@@ -649,7 +651,7 @@ aah_status get_decode_plan(const int32_t* windows, const int32_t* sinks, int H, 
     tables[H_kv + g] = static_cast<int32_t>(sh.ksink[g]);
     tables[2 * H_kv + g] = static_cast<int32_t>(sh.ring[g]);
     tables[3 * H_kv + g] = first;
-    for (int32_t r0 = 0; r0 < n; r0 += aah::kDecodeRows)
+    for (int32_t r0 = 0; r0 < n; r0 += cr)
       chunks.push_back(aah::DecodeChunk{g, r0, static_cast<int32_t>(sh.ksink[g]), static_cast<int32_t>(sh.ring[g]), off,
                                         first, count, static_cast<int32_t>(cap_s)});
     off += n;
@@ -1129,6 +1131,7 @@ aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void*
   // Per query head C_h and effective sink, per key/value head ring and sink rows (as decode_shape).
   aah::NoAllocHeads heads;
   const int G = H / H_kv;
+  const int cr = aah::decode_chunk_rows(H, H_kv);
   int64_t rows = 0, chunks = 0;
   for (int g = 0; g < H_kv; ++g) {
     int64_t ring = 0, ksink = 0;
@@ -1142,7 +1145,7 @@ aah_status aah_attn_decode_noalloc(const void* q, const void* k_new, const void*
       ksink = std::max(ksink, sk);
     }
     rows += ksink + ring;
-    chunks += (ksink + ring + aah::kDecodeRows - 1) / aah::kDecodeRows;
+    chunks += (ksink + ring + cr - 1) / cr;
   }
   if (rows > INT32_MAX) return fail(AAH_ERR_UNSUPPORTED, "cache rows per batch entry exceed 2^31");
   if (static_cast<int64_t>(B) * rows * d >= (int64_t{1} << 40)) return fail(AAH_ERR_UNSUPPORTED, "cache too large");

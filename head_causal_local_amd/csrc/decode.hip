@@ -19,7 +19,9 @@
 // share the loads), so it is bound by HBM bandwidth, not by arithmetic.
 // Kernels:
 //   decode_kernel -- one workgroup = kDecodeRows rows of one key/value head's
-//     region; each wave takes 64 rows.  Lane = row for the scores (its K row is
+//     region (kDecodeRowsGrouped with grouped heads, whose rows serve G query
+//     heads each, so that fewer partials per head are left to merge); each
+//     wave takes 64 rows.  Lane = row for the scores (its K row is
 //     one contiguous 2 d-byte read; q . k with v_dot2_f32_bf16 on bf16 pairs);
 //     for P V each lane takes 16 bytes (8 dimensions) of d / 8 rows, so every
 //     V load instruction reads 512 / d whole rows.  The query rows, K and V
@@ -48,9 +50,12 @@ namespace {
 using namespace dev;
 
 constexpr int kRowsPerWave = 64;
-constexpr int kDecodeWaves = kDecodeRows / kRowsPerWave;
-constexpr int kDecodeThreads = 64 * kDecodeWaves;
-static_assert(kDecodeWaves * kRowsPerWave == kDecodeRows && kDecodeWaves <= 4, "chunk size");
+// Waves per workgroup: kDecodeRows (kDecodeRowsGrouped with grouped heads) rows, 64 per wave.
+template <bool GROUPED>
+constexpr int decode_waves() { return (GROUPED ? kDecodeRowsGrouped : kDecodeRows) / kRowsPerWave; }
+static_assert(decode_waves<false>() * kRowsPerWave == kDecodeRows &&
+                  decode_waves<true>() * kRowsPerWave == kDecodeRowsGrouped && decode_waves<true>() <= 8,
+              "chunk size");
 
 // Lane x from lane l ^ 1, l ^ 2 (quad permutations) or rotated by 4 / 8 within its 16-lane row (DPP).
 template <int CTRL>
@@ -111,14 +116,16 @@ __device__ __forceinline__ int ring_age(int local, int S_g, int R_g, int pr) {
 }
 
 template <int D, bool GROUPED>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
+__global__ __launch_bounds__(64 * decode_waves<GROUPED>()) void decode_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ Knew, const bf16* __restrict__ Vnew,
     bf16* __restrict__ Kc, bf16* __restrict__ Vc, const int32_t* __restrict__ pos,
     const DecodeChunk* __restrict__ chunks, const int32_t* __restrict__ q_cap, const int32_t* __restrict__ q_sink,
     int H, int H_kv, int R, int T_max, float c, int32_t* __restrict__ counters,
     float* __restrict__ part, int n_chunks, bf16* __restrict__ O, float* __restrict__ LSE) {
-  // Per-wave partials of up to kGB query heads at a time, merged across the waves after one barrier.
-  constexpr int kGB = GROUPED ? kDecodeWaves : 1;
+  constexpr int kDecodeWaves = decode_waves<GROUPED>();
+  // Per-wave partials of up to kGB query heads at a time, merged across the waves after one barrier (a
+  // round's query rows, kGB * D / 8 pieces of 16 bytes, are read by one wave's lanes).
+  constexpr int kGB = GROUPED ? (kDecodeWaves < 512 / D ? kDecodeWaves : 512 / D) : 1;
   __shared__ float sm_m[kGB][kDecodeWaves], sm_l[kGB][kDecodeWaves];
   __shared__ float sm_o[kGB][kDecodeWaves][D];
   __shared__ __attribute__((aligned(16))) bf16 sm_q[kDecodeWaves][kGB * D];  // one copy per wave
@@ -469,12 +476,12 @@ hipError_t decode_d(const void* q, const void* knew, const void* vnew, void* kc,
                     int32_t* counters, float* part, hipStream_t stream) {
   const float c = scale * kLog2e;
   if (pl.H_kv != pl.H)
-    hipLaunchKernelGGL((decode_kernel<D, true>), dim3(pl.n_chunks, B), dim3(kDecodeThreads), 0, stream,
+    hipLaunchKernelGGL((decode_kernel<D, true>), dim3(pl.n_chunks, B), dim3(64 * decode_waves<true>()), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(knew), static_cast<const bf16*>(vnew),
                        static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.q_cap, pl.q_sink, pl.H,
                        pl.H_kv, pl.rows, T_max, c, counters, part, pl.n_chunks, static_cast<bf16*>(o), lse);
   else
-    hipLaunchKernelGGL((decode_kernel<D, false>), dim3(pl.n_chunks, B), dim3(kDecodeThreads), 0, stream,
+    hipLaunchKernelGGL((decode_kernel<D, false>), dim3(pl.n_chunks, B), dim3(64 * decode_waves<false>()), 0, stream,
                        static_cast<const bf16*>(q), static_cast<const bf16*>(knew), static_cast<const bf16*>(vnew),
                        static_cast<bf16*>(kc), static_cast<bf16*>(vc), pos, pl.chunks, pl.q_cap, pl.q_sink, pl.H,
                        pl.H_kv, pl.rows, T_max, c, counters, part, pl.n_chunks, static_cast<bf16*>(o), lse);

@@ -140,9 +140,13 @@ hipError_t launch_head_features(const void* q, const void* k, const void* v, boo
                                 hipStream_t stream);
 
 // ---- decoding over per-head trimmed K/V caches (bf16)
-constexpr int kDecodeRows = 256;  // cache rows per decode workgroup
+constexpr int kDecodeRows = 256;  // cache rows per decode workgroup (4 waves of 64 rows)
+constexpr int kDecodeRowsGrouped = 512;  // ... with grouped key/value heads (8 waves of 64 rows)
+// Rows per decode workgroup: a grouped step forms every query head of the group from each loaded row, so
+// it has more work per byte and takes longer chunks (fewer partials per head to merge).
+inline int decode_chunk_rows(int H, int H_kv) { return H_kv < H ? kDecodeRowsGrouped : kDecodeRows; }
 
-// One decode workgroup's share: local rows [row0, row0 + kDecodeRows) of one
+// One decode workgroup's share: local rows [row0, row0 + decode_chunk_rows) of one
 // key/value head's region (its sink rows, then its ring rows), with what the
 // workgroup needs of its key/value head before it can address its rows, so
 // that one 32-byte scalar load precedes the row loads.

@@ -47,7 +47,7 @@ constexpr int kPlanThreads = 256;
 
 // The decode plan of aah_attn_decode's cache, computed on the device: per key/value head g (query heads
 // g G .. g G + G - 1) the ring R_g = max C_h and sink rows S_g = max effective sink, its first row
-// off_g = sum over g' < g of (S_g' + R_g'), its first chunk, and one chunk record per kDecodeRows rows of
+// off_g = sum over g' < g of (S_g' + R_g'), its first chunk, and one chunk record per cr rows of
 // its region (carrying those per-head values, as the host plan's records do).  Tables: kv_off[H_kv],
 // kv_sink[H_kv], kv_ring[H_kv], kv_first[H_kv + 1], q_cap[H], q_sink[H].  Also sets the B * H_kv merge
 // counters to zero (each decode call leaves them zero, but nothing else clears this array).  One workgroup.
@@ -59,6 +59,7 @@ __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads
   __shared__ int32_t s_off[kNoAllocMaxHeads + 1], s_first[kNoAllocMaxHeads + 1];
   const int tid = threadIdx.x;
   const int G = H / H_kv;
+  const int cr = H_kv < H ? kDecodeRowsGrouped : kDecodeRows;  // rows per chunk, as decode_chunk_rows
   for (int i = tid; i < B * H_kv; i += kPlanThreads) counters[i] = 0;
   for (int h = tid; h < H; h += kPlanThreads) {
     tables[4 * H_kv + 1 + h] = heads.cap[h];
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads
       s_first[g] = first;
       const int n = s_sink[g] + s_ring[g];
       off += n;
-      first += (n + kDecodeRows - 1) / kDecodeRows;
+      first += (n + cr - 1) / cr;
     }
     s_off[H_kv] = off;
     s_first[H_kv] = first;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(kPlanThreads) void noalloc_plan_kernel(NoAllocHeads
   for (int g = 0; g < H_kv; ++g) {
     const int n_g = s_first[g + 1] - s_first[g];
     for (int c = tid; c < n_g; c += kPlanThreads)
-      chunks[s_first[g] + c] = DecodeChunk{g, c * kDecodeRows, s_sink[g], s_ring[g], s_off[g], s_first[g], n_g, s_caps[g]};
+      chunks[s_first[g] + c] = DecodeChunk{g, c * cr, s_sink[g], s_ring[g], s_off[g], s_first[g], n_g, s_caps[g]};
   }
 }
 

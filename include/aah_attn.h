@@ -288,7 +288,8 @@ int64_t aah_kv_cache_rows(const int32_t* windows, const int32_t* sinks, int H, i
 
 /* Workspace bytes aah_attn_decode needs: B*H_kv int32 merge counters (rounded
  * up to 256 bytes), then B * chunks * G * (2 + d) floats of partial results,
- * chunks = sum over key/value heads of ceil((S_g + R_g) / 256); 0 for invalid
+ * chunks = sum over key/value heads of ceil((S_g + R_g) / 256) (of
+ * ceil((S_g + R_g) / 512) with grouped heads, H_kv < H); 0 for invalid
  * arguments. */
 size_t aah_attn_decode_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
                                       int T_max, int d, aah_dtype dt);
@@ -333,7 +334,7 @@ aah_status aah_attn_decode(const void* q, const void* k_new, const void* v_new, 
  * counters on every call, so the call reads no host memory after it returns
  * and a captured graph replays the whole step.  No work list is cached.
  * Limits: H <= 256, and the step's counters, tables and partials
- * (B * H_kv * 4 bytes, (4 H_kv + 1 + 2 H) * 4 bytes, 32 bytes per 256 cache rows
+ * (B * H_kv * 4 bytes, (4 H_kv + 1 + 2 H) * 4 bytes, 32 bytes per chunk
  * of a batch entry, and B * chunks * (H / H_kv) * (2 + d) * 4 bytes, each
  * region rounded up to 256 bytes) must fit in the array; a larger step returns
  * AAH_ERR_UNSUPPORTED before any HIP call.  Every call on one GPU shares that

@@ -257,9 +257,12 @@ def test_decode_cache_rows_and_workspace():
             rows = int((sink + ring).sum())
             assert lib.aah_kv_cache_rows(wp, None if sinks is None else sp, 4, H_kv, T_max) == rows
             assert aah.kv_cache_rows(w, T_max, sinks=sinks, H_kv=H_kv) == rows
-            chunks = int(sum((s_ + r + 255) // 256 for s_, r in zip(sink, ring)))
+            cr = 256 if H_kv == 4 else 512  # rows per chunk: 512 with grouped heads
+            chunks = int(sum((s_ + r + cr - 1) // cr for s_, r in zip(sink, ring)))
             need = aah.decode_workspace_size(w, 3, T_max, 64, sinks=sinks, H_kv=H_kv)
-            assert need >= 3 * chunks * (4 // H_kv) * (2 + 64) * 4 and need % 256 == 0
+            counters = -(-3 * H_kv * 4 // 256) * 256
+            partials = -(-3 * chunks * (4 // H_kv) * (2 + 64) * 4 // 256) * 256
+            assert need == counters + partials
     bad = np.array([4, 0], dtype=np.int32)
     assert lib.aah_kv_cache_rows(bad.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, 2, 2, 10) == -1
     assert lib.aah_kv_cache_rows(wp, None, 4, 4, 0) == -1
