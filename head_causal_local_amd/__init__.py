@@ -495,47 +495,39 @@ def fwd_workspace_size(windows: Sequence[int], B: int, H: int, T: int, d: int, d
     return int(lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H if H_kv is None else H_kv, T, d, code))
 
 
-def plan_fwd_split(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, chunk_tiles: int,
-                   n_queues: int = 8, H_kv: Optional[int] = None):
-    """Split forward work list: (items int32 [n, 4] as plan_fwd, slots int32 [n] (-1: the item writes its own
-    rows), merge records int32 [m, 4] of (bh, q_tile_index, first slot, chunks))."""
+def _plan_split(fn, windows, sinks, B, H, T, q_tile, kv_tile, chunk_tiles, n_queues, H_kv):
     w = _windows_arg(windows)
+    sk = _sinks_arg(sinks, H)
     H_kv = H if H_kv is None else H_kv
     n, m = ctypes.c_int64(), ctypes.c_int64()
-    fn = lib().aah_plan_fwd_split
-    st = fn(_wptr(w), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, None, None, 0, ctypes.byref(n), None, 0,
-            ctypes.byref(m))
+    st = fn(_wptr(w), _sptr(sk), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, None, None, 0,
+            ctypes.byref(n), None, 0, ctypes.byref(m))
     if st not in (0, 1):
         check(st)
     items = (WorkItem * max(n.value, 1))()
     slots = np.zeros(max(n.value, 1), dtype=np.int32)
     merges = (WorkItem * max(m.value, 1))()
-    check(fn(_wptr(w), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, items,
+    check(fn(_wptr(w), _sptr(sk), B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles, items,
              slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n), merges, m.value,
              ctypes.byref(m)))
     as_arr = lambda buf, k: np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[:k].copy()  # noqa: E731
     return as_arr(items, n.value), slots[: n.value].copy(), as_arr(merges, m.value)
+
+
+def plan_fwd_split(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, chunk_tiles: int,
+                   n_queues: int = 8, H_kv: Optional[int] = None, sinks: Optional[Sequence[int]] = None):
+    """Split forward work list: (items int32 [n, 4] as plan_fwd, slots int32 [n] (-1: the item writes its own
+    rows), merge records int32 [m, 4] of (bh, q_tile_index, first slot, chunks))."""
+    return _plan_split(lib().aah_plan_fwd_split, windows, sinks, B, H, T, q_tile, kv_tile, chunk_tiles, n_queues,
+                       H_kv)
 
 
 def plan_bwd_split(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, chunk_tiles: int,
-                   n_queues: int = 8):
+                   n_queues: int = 8, H_kv: Optional[int] = None, sinks: Optional[Sequence[int]] = None):
     """Split dK/dV work list: (items int32 [n, 4] as plan_bwd, slots int32 [n], merge records int32 [m, 4] of
-    (bh, key_tile_index, first slot, chunks))."""
-    w = _windows_arg(windows)
-    n, m = ctypes.c_int64(), ctypes.c_int64()
-    fn = lib().aah_plan_bwd_split
-    st = fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, chunk_tiles, None, None, 0, ctypes.byref(n), None, 0,
-            ctypes.byref(m))
-    if st not in (0, 1):
-        check(st)
-    items = (WorkItem * max(n.value, 1))()
-    slots = np.zeros(max(n.value, 1), dtype=np.int32)
-    merges = (WorkItem * max(m.value, 1))()
-    check(fn(_wptr(w), B, H, T, q_tile, kv_tile, n_queues, chunk_tiles, items,
-             slots.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n.value, ctypes.byref(n), merges, m.value,
-             ctypes.byref(m)))
-    as_arr = lambda buf, k: np.frombuffer(buf, dtype=np.int32).reshape(-1, 4)[:k].copy()  # noqa: E731
-    return as_arr(items, n.value), slots[: n.value].copy(), as_arr(merges, m.value)
+    (b * H_kv + g, key_tile_index, first slot, chunks))."""
+    return _plan_split(lib().aah_plan_bwd_split, windows, sinks, B, H, T, q_tile, kv_tile, chunk_tiles, n_queues,
+                       H_kv)
 
 
 def window_stats(windows: Sequence[int], T: int, sinks: Optional[Sequence[int]] = None) -> Tuple[int, float]:

@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 11
+ABI_VERSION = 12
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
@@ -97,12 +97,11 @@ def _declare(lib):
         fn = getattr(lib, name)
         fn.restype = c_int
         fn.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, c_int64, P_i64]
-    lib.aah_plan_fwd_split.restype = c_int
-    lib.aah_plan_fwd_split.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, P_i32,
-                                       c_int64, P_i64, P_item, c_int64, P_i64]
-    lib.aah_plan_bwd_split.restype = c_int
-    lib.aah_plan_bwd_split.argtypes = [P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, P_i32, c_int64,
-                                       P_i64, P_item, c_int64, P_i64]
+    for name in ("aah_plan_fwd_split", "aah_plan_bwd_split"):
+        fn = getattr(lib, name)
+        fn.restype = c_int
+        fn.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, P_item, P_i32, c_int64,
+                       P_i64, P_item, c_int64, P_i64]
     lib.aah_window_stats.restype = c_int
     lib.aah_window_stats.argtypes = [P_i32, P_i32, c_int, c_int, P_i64, P_double]
     lib.aah_cache_clear.restype = None

@@ -389,8 +389,9 @@ int resident_workgroups(int d) {
   return n;
 }
 
-// Chunk length for a bf16 forward without sinks, or 0 when splitting does not apply.
-int split_chunk_tiles(const int32_t* windows, int B, int H, int T, int d) {
+// Chunk length for a bf16 forward (items cut along their window tiles; an item's sink tiles go with its first
+// chunk and count in the total), or 0 when splitting does not apply.
+int split_chunk_tiles(const int32_t* windows, const int32_t* sinks, int B, int H, int T, int d) {
   const int q_tile = aah::kFwdBf16RowTile, kv_tile = aah::kFwdBf16ColTile;
   const int n_qt = (T + q_tile - 1) / q_tile;
   const int64_t n_items = static_cast<int64_t>(B) * H * n_qt;
@@ -400,10 +401,12 @@ int split_chunk_tiles(const int32_t* windows, int B, int H, int T, int d) {
   int longest = 0;
   for (int h = 0; h < H; ++h) {
     const int W = aah::effective_window(windows[h], T);
+    const int S = sinks == nullptr ? 0 : aah::effective_sink(sinks[h], windows[h], T);
     for (int qt = 0; qt < n_qt; ++qt) {
       const int q0 = qt * q_tile, q1 = std::min(T, q0 + q_tile);
-      const int n = (q1 - 1) / kv_tile + 1 - std::max(0, q0 - W + 1) / kv_tile;
-      total += n;
+      const int lo = std::max(0, q0 - W + 1) / kv_tile;
+      const int n = (q1 - 1) / kv_tile + 1 - lo;
+      total += n + aah::sink_tiles(S, lo, kv_tile);
       longest = std::max(longest, n);
     }
   }
@@ -418,6 +421,7 @@ struct SplitDevicePlan {
   int32_t* slots = nullptr;
   WorkItem* merges = nullptr;
   int32_t* win = nullptr;
+  int32_t* sink = nullptr;  // effective sink sizes, or nullptr when no head has one
   int n_items = 0, n_merges = 0, n_slots = 0;
 };
 aah::PlanLru<SplitDevicePlan> g_split_cache(kCacheCapacity);
@@ -431,24 +435,31 @@ size_t split_workspace(int n_slots, int d) {
          round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * 2 * sizeof(float), 256);
 }
 
-// Split plan of a bf16 forward without sinks with chunk length L (> 0), uploaded once per key.
-// kind 0: query-stationary items (forward, dQ); kind 1: key-stationary items (dK/dV, H_kv = H, no sinks).
-aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T, int d, int L, hipStream_t stream,
-                          SplitDevicePlan* out, int kind = 0) {
+// Split plan with chunk length L (> 0), uploaded once per key.  kind 0: query-stationary items (forward,
+// dQ); kind 1: key-stationary items (dK/dV).
+aah_status get_split_plan(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d, int L,
+                          hipStream_t stream, SplitDevicePlan* out, int kind = 0) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::vector<int32_t> win(H);
-  for (int h = 0; h < H; ++h) win[h] = aah::effective_window(windows[h], T);
-  std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, d, L};
+  const bool has_sink = any_sink(windows, sinks, H, T);
+  std::vector<int32_t> win(H), sink(H, 0);
+  for (int h = 0; h < H; ++h) {
+    win[h] = aah::effective_window(windows[h], T);
+    if (has_sink) sink[h] = aah::effective_sink(sinks[h], windows[h], T);
+  }
+  std::vector<int64_t> key = {kind, dev, B, H, H_kv, T, d, L, has_sink ? 1 : 0};
   key.insert(key.end(), win.begin(), win.end());
+  if (has_sink) key.insert(key.end(), sink.begin(), sink.end());
   const bool capturing = stream_capturing(stream);
   std::lock_guard<std::mutex> lock(g_mu);
   aah_status st;
   if (cache_lookup(g_split_cache, key, stream, capturing, out, &st)) return st;
   const aah::SplitPlan sp =
-      kind == 0 ? aah::plan_forward_split(windows, B, H, H_kv, T, aah::kFwdBf16RowTile, aah::kFwdBf16ColTile, kQueues, L)
-                : aah::plan_backward_split(windows, B, H, T, aah::kBwdBf16ColTile, aah::kBwdBf16RowTile, kQueues, L);
+      kind == 0 ? aah::plan_forward_split(windows, sinks, B, H, H_kv, T, aah::kFwdBf16RowTile, aah::kFwdBf16ColTile,
+                                          kQueues, L)
+                : aah::plan_backward_split(windows, sinks, B, H, H_kv, T, aah::kBwdBf16ColTile, aah::kBwdBf16RowTile,
+                                           kQueues, L);
   SplitDevicePlan p;
   p.n_items = static_cast<int>(sp.items.size());
   p.n_merges = static_cast<int>(sp.merges.size());
@@ -458,12 +469,14 @@ aah_status get_split_plan(const int32_t* windows, int B, int H, int H_kv, int T,
                             {{sp.items.data(), sp.items.size() * sizeof(WorkItem)},
                              {sp.slot.data(), sp.slot.size() * sizeof(int32_t)},
                              {sp.merges.data(), sp.merges.size() * sizeof(WorkItem)},
-                             {win.data(), win.size() * sizeof(int32_t)}},
+                             {win.data(), win.size() * sizeof(int32_t)},
+                             {sink.data(), sink.size() * sizeof(int32_t)}},
                             stream, &p.blob, &off));
   p.items = reinterpret_cast<WorkItem*>(p.blob.dev + off[0]);
   p.slots = reinterpret_cast<int32_t*>(p.blob.dev + off[1]);
   p.merges = reinterpret_cast<WorkItem*>(p.blob.dev + off[2]);
   p.win = reinterpret_cast<int32_t*>(p.blob.dev + off[3]);
+  p.sink = has_sink ? reinterpret_cast<int32_t*>(p.blob.dev + off[4]) : nullptr;
   cache_insert(g_split_cache, std::move(key), p, stream);
   *out = p;
   return AAH_OK;
@@ -497,26 +510,40 @@ int chunk_len(const std::vector<int>& tiles, int resident) {
   return longest > L ? L : 0;
 }
 
-// Streamed tiles of every dQ item (query tile, key tiles) or dK/dV item (key tile, query tiles), no sinks.
-std::vector<int> bwd_item_tiles(bool dkdv, const int32_t* windows, int B, int H, int T) {
+// Streamed tiles of every dQ item (query tile: its window's key tiles and the sink tiles before them) or
+// dK/dV item (key tile of a key/value head: query tiles summed over the group's query heads).
+std::vector<int> bwd_item_tiles(bool dkdv, const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                int T) {
   std::vector<int> tiles;
   const int rt = dkdv ? aah::kBwdBf16RowTile : aah::kFwdBf16RowTile;
   const int ct = dkdv ? aah::kBwdBf16ColTile : aah::kFwdBf16ColTile;
   const int n_rt = (T + rt - 1) / rt;
-  for (int b = 0; b < B; ++b)
-    for (int h = 0; h < H; ++h) {
-      const int W = aah::effective_window(windows[h], T);
-      for (int t = 0; t < n_rt; ++t) {
-        const int r0 = t * rt, r1 = std::min(T, r0 + rt);
-        if (dkdv) {
-          int lo = 0, hi = 0;
-          aah::query_range(r0, r1, W, 0, T, ct, &lo, &hi);
-          tiles.push_back(hi - lo);
-        } else {
-          tiles.push_back((r1 - 1) / ct + 1 - std::max(0, r0 - W + 1) / ct);
+  const int G = H / H_kv;
+  auto sink_of = [&](int h) { return sinks == nullptr ? 0 : aah::effective_sink(sinks[h], windows[h], T); };
+  for (int b = 0; b < B; ++b) {
+    if (dkdv) {
+      for (int g = 0; g < H_kv; ++g)
+        for (int t = 0; t < n_rt; ++t) {
+          const int r0 = t * rt, r1 = std::min(T, r0 + rt);
+          int steps = 0;
+          for (int h = g * G; h < (g + 1) * G; ++h) {
+            int lo = 0, hi = 0;
+            aah::query_range(r0, r1, aah::effective_window(windows[h], T), sink_of(h), T, ct, &lo, &hi);
+            steps += hi - lo;
+          }
+          tiles.push_back(steps);
+        }
+    } else {
+      for (int h = 0; h < H; ++h) {
+        const int W = aah::effective_window(windows[h], T);
+        for (int t = 0; t < n_rt; ++t) {
+          const int r0 = t * rt, r1 = std::min(T, r0 + rt);
+          const int lo = std::max(0, r0 - W + 1) / ct;
+          tiles.push_back((r1 - 1) / ct + 1 - lo + aah::sink_tiles(sink_of(h), lo, ct));
         }
       }
     }
+  }
   return tiles;
 }
 
@@ -527,15 +554,17 @@ struct BwdSplitLayout {
 };
 
 // Layout of a split backward's workspace: [nl2 | nD | dQ partials | dK/dV partials].  Returns false when
-// splitting does not apply (dtype, grouped heads, sinks, enough items, or a failed plan upload).
+// splitting does not apply (dtype, enough items, or a failed plan upload).
 bool bwd_split_layout(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
                       aah_dtype dt, hipStream_t stream, BwdSplitLayout* lay) {
-  if (dt != AAH_BF16 || H_kv != H || any_sink(windows, sinks, H, T)) return false;
-  lay->q_L = chunk_len(bwd_item_tiles(false, windows, B, H, T), resident_bwd(false, d));
-  lay->k_L = chunk_len(bwd_item_tiles(true, windows, B, H, T), resident_bwd(true, d));
+  if (dt != AAH_BF16) return false;
+  lay->q_L = chunk_len(bwd_item_tiles(false, windows, sinks, B, H, H_kv, T), resident_bwd(false, d));
+  lay->k_L = chunk_len(bwd_item_tiles(true, windows, sinks, B, H, H_kv, T), resident_bwd(true, d));
   if (lay->q_L == 0 && lay->k_L == 0) return false;
-  if (lay->q_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->q_L, stream, &lay->q, 0) != AAH_OK) return false;
-  if (lay->k_L > 0 && get_split_plan(windows, B, H, H_kv, T, d, lay->k_L, stream, &lay->k, 1) != AAH_OK) return false;
+  if (lay->q_L > 0 && get_split_plan(windows, sinks, B, H, H_kv, T, d, lay->q_L, stream, &lay->q, 0) != AAH_OK)
+    return false;
+  if (lay->k_L > 0 && get_split_plan(windows, sinks, B, H, H_kv, T, d, lay->k_L, stream, &lay->k, 1) != AAH_OK)
+    return false;
   const size_t rows = static_cast<size_t>(aah::kBwdBf16RowTile) * d * sizeof(float);
   lay->q_off = 2 * round_up(static_cast<size_t>(B) * H * T * sizeof(float), 256);
   lay->k_off = lay->q_off + round_up(static_cast<size_t>(lay->q_L > 0 ? lay->q.n_slots : 0) * rows, 256);
@@ -755,11 +784,11 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
                                    int d, aah_dtype dt) {
   if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
   g_detail.clear();
-  if (empty_problem(B, T) || any_sink(windows, sinks, H, T)) return 0;
-  const int L = split_chunk_tiles(windows, B, H, T, d);
+  if (empty_problem(B, T)) return 0;
+  const int L = split_chunk_tiles(windows, sinks, B, H, T, d);
   if (L == 0) return 0;
   SplitDevicePlan sp;
-  if (get_split_plan(windows, B, H, H_kv, T, d, L, nullptr, &sp) != AAH_OK) return 0;
+  if (get_split_plan(windows, sinks, B, H, H_kv, T, d, L, nullptr, &sp) != AAH_OK) return 0;
   return split_workspace(sp.n_slots, d);
 }
 
@@ -810,18 +839,18 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // Split launch: bf16, no diagnostics, no sink keys, and a workspace large enough for the partials.
-  const int L = dt == AAH_BF16 && ent == nullptr && !any_sink(windows, sinks, H, T) && workspace != nullptr
-                    ? split_chunk_tiles(windows, B, H, T, d)
+  // Split launch: bf16, no diagnostics, and a workspace large enough for the partials.
+  const int L = dt == AAH_BF16 && ent == nullptr && workspace != nullptr
+                    ? split_chunk_tiles(windows, sinks, B, H, T, d)
                     : 0;
   if (L > 0) {
     SplitDevicePlan sp;
-    AAH_TRY(get_split_plan(windows, B, H, H_kv, T, d, L, st, &sp));
+    AAH_TRY(get_split_plan(windows, sinks, B, H, H_kv, T, d, L, st, &sp));
     if (workspace_bytes >= split_workspace(sp.n_slots, d)) {
       float* part_acc = static_cast<float*>(workspace);
       float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_acc_bytes(sp.n_slots, d));
       const aah::FwdSplit split{sp.slots, sp.merges, sp.n_merges, part_acc, part_ml};
-      e = aah::launch_fwd_bf16(q, k, v, o, lse, nullptr, nullptr, sp.items, sp.n_items, sp.win, nullptr, s, &split,
+      e = aah::launch_fwd_bf16(q, k, v, o, lse, nullptr, nullptr, sp.items, sp.n_items, sp.win, sp.sink, s, &split,
                                st);
       if (e != hipSuccess) return hip_fail(e, "split forward launch");
       return AAH_OK;
@@ -940,7 +969,7 @@ aah_status aah_attn_bwd_dkdv(const void* q, const void* k, const void* v, const 
     const aah::BwdSplit split{lay.k.slots, lay.k.merges, lay.k.n_merges,
                               reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.k_off)};
     const hipError_t e = aah::launch_bwd_dkdv_bf16_split(q, k, v, dout, nl2, nd, dk, dv, lay.k.items, lay.k.n_items,
-                                                         lay.k.win, s, split, st);
+                                                         lay.k.win, lay.k.sink, s, split, st);
     if (e != hipSuccess) return hip_fail(e, "split dK/dV launch");
     return AAH_OK;
   }
@@ -986,7 +1015,7 @@ aah_status aah_attn_bwd_dq(const void* q, const void* k, const void* v, const vo
     const aah::BwdSplit split{lay.q.slots, lay.q.merges, lay.q.n_merges,
                               reinterpret_cast<float*>(static_cast<char*>(workspace) + lay.q_off)};
     const hipError_t e = aah::launch_bwd_dq_bf16_split(q, k, v, o, dout, lse, nl2, nd, dq, lay.q.items,
-                                                       lay.q.n_items, lay.q.win, s, split, st);
+                                                       lay.q.n_items, lay.q.win, lay.q.sink, s, split, st);
     if (e != hipSuccess) return hip_fail(e, "split dQ launch");
     return AAH_OK;
   }
@@ -1211,24 +1240,10 @@ aah_status split_to_host(const aah::SplitPlan& sp, aah_work_item* items, int32_t
 }
 }  // namespace
 
-aah_status aah_plan_bwd_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                              int chunk_tiles, aah_work_item* items, int32_t* slots, int64_t capacity,
-                              int64_t* n_items, aah_work_item* merges, int64_t merge_capacity, int64_t* n_merges) {
-  g_detail.clear();
-  if (n_items == nullptr || n_merges == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items / n_merges is NULL");
-  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
-  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
-  if (q_tile < 1 || kv_tile < 1 || n_queues < 1 || chunk_tiles < 1)
-    return fail(AAH_ERR_INVALID_ARG, "tiles, n_queues and chunk_tiles must be >= 1");
-  AAH_TRY(check_windows(windows, nullptr, H));
-  return split_to_host(aah::plan_backward_split(windows, B, H, T, q_tile, kv_tile, n_queues, chunk_tiles), items,
-                       slots, capacity, n_items, merges, merge_capacity, n_merges);
-}
-
-aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
-                              int n_queues, int chunk_tiles, aah_work_item* items, int32_t* slots,
-                              int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,
-                              int64_t* n_merges) {
+aah_status aah_plan_bwd_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles, aah_work_item* items,
+                              int32_t* slots, int64_t capacity, int64_t* n_items, aah_work_item* merges,
+                              int64_t merge_capacity, int64_t* n_merges) {
   g_detail.clear();
   if (n_items == nullptr || n_merges == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items / n_merges is NULL");
   if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
@@ -1236,20 +1251,27 @@ aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, in
   if (q_tile < 1 || kv_tile < 1 || n_queues < 1 || chunk_tiles < 1)
     return fail(AAH_ERR_INVALID_ARG, "tiles, n_queues and chunk_tiles must be >= 1");
   AAH_TRY(check_kv_heads(H, H_kv));
-  AAH_TRY(check_windows(windows, nullptr, H));
-  const aah::SplitPlan sp = aah::plan_forward_split(windows, B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles);
-  *n_items = static_cast<int64_t>(sp.items.size());
-  *n_merges = static_cast<int64_t>(sp.merges.size());
-  if (capacity < *n_items || merge_capacity < *n_merges)
-    return fail(AAH_ERR_INVALID_ARG, "capacity %lld / %lld < %lld items / %lld merge records",
-                static_cast<long long>(capacity), static_cast<long long>(merge_capacity),
-                static_cast<long long>(*n_items), static_cast<long long>(*n_merges));
-  if ((*n_items > 0 && (items == nullptr || slots == nullptr)) || (*n_merges > 0 && merges == nullptr))
-    return fail(AAH_ERR_INVALID_ARG, "output array is NULL");
-  std::memcpy(items, sp.items.data(), sp.items.size() * sizeof(WorkItem));
-  std::memcpy(slots, sp.slot.data(), sp.slot.size() * sizeof(int32_t));
-  if (!sp.merges.empty()) std::memcpy(merges, sp.merges.data(), sp.merges.size() * sizeof(WorkItem));
-  return AAH_OK;
+  AAH_TRY(check_windows(windows, sinks, H));
+  return split_to_host(
+      aah::plan_backward_split(windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles), items, slots,
+      capacity, n_items, merges, merge_capacity, n_merges);
+}
+
+aah_status aah_plan_fwd_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles, aah_work_item* items,
+                              int32_t* slots, int64_t capacity, int64_t* n_items, aah_work_item* merges,
+                              int64_t merge_capacity, int64_t* n_merges) {
+  g_detail.clear();
+  if (n_items == nullptr || n_merges == nullptr) return fail(AAH_ERR_INVALID_ARG, "n_items / n_merges is NULL");
+  if (windows == nullptr) return fail(AAH_ERR_INVALID_ARG, "windows is NULL");
+  if (B < 1 || H < 1 || T < 1) return fail(AAH_ERR_INVALID_ARG, "B, H, T must be >= 1");
+  if (q_tile < 1 || kv_tile < 1 || n_queues < 1 || chunk_tiles < 1)
+    return fail(AAH_ERR_INVALID_ARG, "tiles, n_queues and chunk_tiles must be >= 1");
+  AAH_TRY(check_kv_heads(H, H_kv));
+  AAH_TRY(check_windows(windows, sinks, H));
+  return split_to_host(
+      aah::plan_forward_split(windows, sinks, B, H, H_kv, T, q_tile, kv_tile, n_queues, chunk_tiles), items, slots,
+      capacity, n_items, merges, merge_capacity, n_merges);
 }
 
 void aah_cache_clear(void) {

@@ -345,15 +345,19 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   };
 
   // Grouped heads: the item's steps are the group's query heads one after another, each over its own
-  // query-tile range (all starting at it.lo); two cursors follow the step being filled (two ahead) and
-  // the step being computed.
+  // query-tile range (all starting at it.lo), cut at it.hi; two cursors follow the step being filled (two
+  // ahead) and the step being computed.  A chunk of a split item (query tiles [it.lo, it.hi) of the
+  // group's union range) skips the heads whose range ends before it.lo.
   const int k0 = it.tile * kStat, k1 = min(T, k0 + kStat);
   auto set_head = [&](StepCursor& cu, int j) __attribute__((always_inline)) {
-    cu.j = j;
-    cu.qt = it.lo;
-    cu.W = win_eff[(qh0 + j) % H];
-    cu.S = SINK ? sink_eff[(qh0 + j) % H] : 0;
-    cu.hi = query_hi(k0, k1, cu.W, cu.S, T);
+    for (;; ++j) {
+      cu.j = j;
+      cu.qt = it.lo;
+      cu.W = win_eff[(qh0 + j) % H];
+      cu.S = SINK ? sink_eff[(qh0 + j) % H] : 0;
+      cu.hi = min(it.hi, query_hi(k0, k1, cu.W, cu.S, T));
+      if (cu.hi > it.lo || j + 1 >= G) break;
+    }
   };
   auto advance = [&](StepCursor& cu) __attribute__((always_inline)) {
     if (++cu.qt == cu.hi && cu.j + 1 < G) set_head(cu, cu.j + 1);
@@ -364,7 +368,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
     set_head(dc, 0);
     n_steps = 0;
     for (int j = 0; j < G; ++j)
-      n_steps += query_hi(k0, k1, win_eff[(qh0 + j) % H], SINK ? sink_eff[(qh0 + j) % H] : 0, T) - it.lo;
+      n_steps += max(0, min(it.hi, query_hi(k0, k1, win_eff[(qh0 + j) % H], SINK ? sink_eff[(qh0 + j) % H] : 0, T)) -
+                            it.lo);
     fc = dc;
   }
   auto fill_cursor = [&](const StepCursor& cu, char* st) __attribute__((always_inline)) {
@@ -547,8 +552,13 @@ void bwd_dq_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, const
   if (it.bh < 0) return;
   const int W = win_eff[it.bh % H];
   const int S = SINK ? sink_eff[it.bh % H] : 0;  // keys 0 .. S - 1 are sinks
-  // Tiles in visiting order: the sink tiles before the window's first tile, then it.lo .. it.hi - 1.
-  const int ns = SINK ? min((S + kStep - 1) / kStep, it.lo) : 0;
+  // Tiles in visiting order: the sink tiles before the window's first tile, then it.lo .. it.hi - 1.  Only
+  // the first chunk of a split item (the one that starts at the window's first tile, as every unsplit item
+  // does) visits the sink tiles.
+  int ns = 0;
+  if constexpr (SINK) {
+    if (it.lo * kStep <= max(0, it.tile * kStat - W + 1)) ns = min((S + kStep - 1) / kStep, it.lo);
+  }
   const int n_tiles = ns + it.hi - it.lo;
   auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + it.lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;
@@ -811,9 +821,18 @@ hipError_t dq_s(const void* q, const void* k, const void* v, const void* o, cons
 template <int D>
 hipError_t dkdv_split_d(const void* q, const void* k, const void* v, const void* dout, const float* nl2, const float* nd,
                         void* dk, void* dv, const WorkItem* items, int n_items, const int32_t* win_eff,
-                        const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
-  const hipError_t e =
-      dkdv_d<D, false, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, nullptr, s, stream, &split);
+                        const int32_t* sink_eff, const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
+  const bool sink = sink_eff != nullptr, gqa = s.H_kv != s.H;
+  const BwdSplit* sp = &split;
+  hipError_t e;
+  if (sink && gqa)
+    e = dkdv_d<D, true, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream, sp);
+  else if (sink)
+    e = dkdv_d<D, true, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream, sp);
+  else if (gqa)
+    e = dkdv_d<D, false, true>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream, sp);
+  else
+    e = dkdv_d<D, false, false>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, stream, sp);
   if (e != hipSuccess || split.n_merges == 0) return e;
   hipLaunchKernelGGL((bwd_merge_kernel<D, 2>), dim3(split.n_merges, kStat / (256 / (D / 4))), dim3(256), 0, stream,
                      split.merges, split.part, static_cast<bf16*>(dk), static_cast<bf16*>(dv), s.scale, s.T);
@@ -823,9 +842,11 @@ hipError_t dkdv_split_d(const void* q, const void* k, const void* v, const void*
 template <int D>
 hipError_t dq_split_d(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
                       float* nl2, float* nd, void* dq, const WorkItem* items, int n_items, const int32_t* win_eff,
-                      const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
+                      const int32_t* sink_eff, const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
   const hipError_t e =
-      dq_d<D, false>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, nullptr, s, stream, &split);
+      sink_eff != nullptr
+          ? dq_d<D, true>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, stream, &split)
+          : dq_d<D, false>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, nullptr, s, stream, &split);
   if (e != hipSuccess || split.n_merges == 0) return e;
   hipLaunchKernelGGL((bwd_merge_kernel<D, 1>), dim3(split.n_merges, kStat / (256 / (D / 4))), dim3(256), 0, stream,
                      split.merges, split.part, static_cast<bf16*>(dq), nullptr, s.scale, s.T);
@@ -847,24 +868,31 @@ int resident_of(Fn fn) {
 
 hipError_t launch_bwd_dkdv_bf16_split(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                       const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
-                                      const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
-                                      hipStream_t stream) {
+                                      const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s,
+                                      const BwdSplit& split, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dkdv_split_d<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
-    case 64: return dkdv_split_d<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
-    case 128: return dkdv_split_d<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, s, split, stream);
+    case 32:
+      return dkdv_split_d<32>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 64:
+      return dkdv_split_d<64>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 128:
+      return dkdv_split_d<128>(q, k, v, dout, nl2, nd, dk, dv, items, n_items, win_eff, sink_eff, s, split, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_bwd_dq_bf16_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                     const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items,
-                                    int n_items, const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
-                                    hipStream_t stream) {
+                                    int n_items, const int32_t* win_eff, const int32_t* sink_eff,
+                                    const AttnShape& s, const BwdSplit& split, hipStream_t stream) {
   switch (s.d) {
-    case 32: return dq_split_d<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
-    case 64: return dq_split_d<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
-    case 128: return dq_split_d<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, s, split, stream);
+    case 32:
+      return dq_split_d<32>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 64:
+      return dq_split_d<64>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, split, stream);
+    case 128:
+      return dq_split_d<128>(q, k, v, o, dout, lse, nl2, nd, dq, items, n_items, win_eff, sink_eff, s, split,
+                             stream);
     default: return hipErrorInvalidValue;
   }
 }

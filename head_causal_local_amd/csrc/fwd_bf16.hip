@@ -152,7 +152,9 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   const int q0i = it.tile * kRows, q1i = min(T, q0i + kRows);
   const int w_lo = kSub == 1 ? it.lo : max(it.lo * kSub, max(0, q0i - W + 1) / KT);
   const int w_hi = kSub == 1 ? it.hi : min(it.hi * kSub, (q1i - 1) / KT + 1);
-  const int ns = SINK ? min((S + KT - 1) / KT, w_lo) : 0;
+  // Only the first chunk of a split item (the one that starts at the window's first tile, as every unsplit
+  // item does) visits the sink stages.
+  const int ns = SINK && it.lo * kPlanKeys <= max(0, q0i - W + 1) ? min((S + KT - 1) / KT, w_lo) : 0;
   const int n_tiles = ns + w_hi - w_lo;
   auto tile_at = [&](int v) __attribute__((always_inline)) { return SINK && v < ns ? v : v - ns + w_lo; };
   const size_t base = static_cast<size_t>(it.bh) * T * D;

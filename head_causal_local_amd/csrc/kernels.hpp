@@ -88,10 +88,11 @@ hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const
                               const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s, hipStream_t stream);
 
 // Split backward (plan_forward_split items for dQ, plan_backward_split items
-// for dK/dV; one key/value head per query head, no sinks): slots[i] is item i's
-// partial slot or -1.  A dQ chunk leaves its fp32 dQ sum (before the scale) in
-// part [slot][128][d]; a dK/dV chunk its dK and dV sums in part [slot][2][128][d];
-// a merge launch per kernel adds each split item's chunks and writes bf16.
+// for dK/dV; sink_eff and grouped heads as for the unsplit launches): slots[i]
+// is item i's partial slot or -1.  A dQ chunk leaves its fp32 dQ sum (before
+// the scale) in part [slot][128][d]; a dK/dV chunk its dK and dV sums (over
+// the group's query heads) in part [slot][2][128][d]; a merge launch per
+// kernel adds each split item's chunks and writes bf16.
 struct BwdSplit {
   const int32_t* slots;
   const WorkItem* merges;
@@ -100,12 +101,12 @@ struct BwdSplit {
 };
 hipError_t launch_bwd_dkdv_bf16_split(const void* q, const void* k, const void* v, const void* dout, const float* nl2,
                                       const float* nd, void* dk, void* dv, const WorkItem* items, int n_items,
-                                      const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
-                                      hipStream_t stream);
+                                      const int32_t* win_eff, const int32_t* sink_eff, const AttnShape& s,
+                                      const BwdSplit& split, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16_split(const void* q, const void* k, const void* v, const void* o, const void* dout,
                                     const float* lse, float* nl2, float* nd, void* dq, const WorkItem* items,
-                                    int n_items, const int32_t* win_eff, const AttnShape& s, const BwdSplit& split,
-                                    hipStream_t stream);
+                                    int n_items, const int32_t* win_eff, const int32_t* sink_eff,
+                                    const AttnShape& s, const BwdSplit& split, hipStream_t stream);
 // Workgroups of the plain bf16 dQ / dK,dV kernels the current device holds at once (0 if the query fails).
 int bwd_dq_resident(int d);
 int bwd_dkdv_resident(int d);

@@ -110,8 +110,8 @@ std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks,
   return interleave(per_group, n_queues);
 }
 
-SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
-                             int n_queues, int chunk_tiles) {
+SplitPlan plan_forward_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                             int q_tile, int kv_tile, int n_queues, int chunk_tiles) {
   const int n_qt = ceil_div(T, q_tile);
   const int G = H / H_kv;
   SplitPlan plan;
@@ -119,6 +119,7 @@ SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int
   for (int b = 0; b < B; ++b) {
     for (int h = 0; h < H; ++h) {
       const int W = effective_window(windows[h], T);
+      const int S = head_sink(sinks, windows, h, T);
       const int32_t group = b * H_kv + h / G;
       auto& list = per_group[static_cast<size_t>(group)];
       for (int qt = 0; qt < n_qt; ++qt) {
@@ -126,8 +127,9 @@ SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int
         const int q1 = std::min(T, q0 + q_tile);
         const int lo = std::max(0, q0 - W + 1) / kv_tile, hi = (q1 - 1) / kv_tile + 1;
         const int n = hi - lo;
+        const int ns = sink_tiles(S, lo, kv_tile);  // visited by the item's first chunk only
         if (chunk_tiles < 1 || n <= chunk_tiles) {
-          list.push_back(Planned{WorkItem{b * H + h, qt, lo, hi}, n, group});
+          list.push_back(Planned{WorkItem{b * H + h, qt, lo, hi}, n + ns, group});
           continue;
         }
         const int n_chunks = ceil_div(n, chunk_tiles);
@@ -136,7 +138,8 @@ SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int
           // Near-equal chunks: the first n % n_chunks get one tile more.
           const int c_lo = lo + c * (n / n_chunks) + std::min(c, n % n_chunks);
           const int c_hi = c_lo + n / n_chunks + (c < n % n_chunks ? 1 : 0);
-          list.push_back(Planned{WorkItem{b * H + h, qt, c_lo, c_hi}, c_hi - c_lo, group, plan.n_slots++});
+          list.push_back(
+              Planned{WorkItem{b * H + h, qt, c_lo, c_hi}, c_hi - c_lo + (c == 0 ? ns : 0), group, plan.n_slots++});
         }
       }
     }
@@ -145,36 +148,55 @@ SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int
   return plan;
 }
 
-SplitPlan plan_backward_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                              int chunk_tiles) {
+SplitPlan plan_backward_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles) {
   const int n_kt = ceil_div(T, kv_tile);
+  const int G = H / H_kv;
   SplitPlan plan;
-  std::vector<std::vector<Planned>> per_head(static_cast<size_t>(B) * H);
+  std::vector<std::vector<Planned>> per_group(static_cast<size_t>(B) * H_kv);
+  std::vector<int> hi_j(G);
   for (int b = 0; b < B; ++b) {
-    for (int h = 0; h < H; ++h) {
-      const int32_t bh = b * H + h;
-      auto& list = per_head[static_cast<size_t>(bh)];
-      const int W = effective_window(windows[h], T);
+    for (int g = 0; g < H_kv; ++g) {
+      const int32_t group = b * H_kv + g;
+      auto& list = per_group[static_cast<size_t>(group)];
       for (int kt = 0; kt < n_kt; ++kt) {
         const int k0 = kt * kv_tile, k1 = std::min(T, k0 + kv_tile);
-        int lo = 0, hi = 0;
-        query_range(k0, k1, W, 0, T, q_tile, &lo, &hi);
-        const int n = hi - lo;
+        // The group's query heads share the first query tile; each ends at its own.  Steps: query tiles
+        // summed over the heads.
+        int lo = 0, hi = 0, n = 0;
+        for (int j = 0; j < G; ++j) {
+          const int h = g * G + j;
+          query_range(k0, k1, effective_window(windows[h], T), head_sink(sinks, windows, h, T), T, q_tile, &lo,
+                      &hi_j[j]);
+          hi = std::max(hi, hi_j[j]);
+          n += hi_j[j] - lo;
+        }
         if (chunk_tiles < 1 || n <= chunk_tiles) {
-          list.push_back(Planned{WorkItem{bh, kt, lo, hi}, n, bh});
+          list.push_back(Planned{WorkItem{group, kt, lo, hi}, n, group});
           continue;
         }
+        // Chunks are query-tile ranges [c_lo, c_hi) of [lo, hi), each running every head of the group over
+        // its part of the range; the cuts fall where the steps before them first reach c n / n_chunks.
         const int n_chunks = ceil_div(n, chunk_tiles);
-        plan.merges.push_back(WorkItem{bh, kt, plan.n_slots, n_chunks});
+        plan.merges.push_back(WorkItem{group, kt, plan.n_slots, n_chunks});
+        int c_lo = lo, steps = 0;  // steps of the tiles before c_lo
         for (int c = 0; c < n_chunks; ++c) {
-          const int c_lo = lo + c * (n / n_chunks) + std::min(c, n % n_chunks);
-          const int c_hi = c_lo + n / n_chunks + (c < n % n_chunks ? 1 : 0);
-          list.push_back(Planned{WorkItem{bh, kt, c_lo, c_hi}, c_hi - c_lo, bh, plan.n_slots++});
+          int c_hi = c_lo, c_steps = 0;
+          const int64_t target = static_cast<int64_t>(c + 1) * n / n_chunks;
+          while (c_hi < hi && (c == n_chunks - 1 || steps + c_steps < target || c_hi == c_lo)) {
+            for (int j = 0; j < G; ++j) c_steps += c_hi < hi_j[j] ? 1 : 0;
+            ++c_hi;
+          }
+          if (c_hi == c_lo) break;  // fewer distinct tiles than chunks (cannot happen with one head per group)
+          list.push_back(Planned{WorkItem{group, kt, c_lo, c_hi}, c_steps, group, plan.n_slots++});
+          steps += c_steps;
+          c_lo = c_hi;
         }
+        plan.merges.back().hi = plan.n_slots - plan.merges.back().lo;
       }
     }
   }
-  plan.items = interleave(per_head, n_queues, &plan.slot);
+  plan.items = interleave(per_group, n_queues, &plan.slot);
   return plan;
 }
 

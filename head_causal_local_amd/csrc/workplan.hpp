@@ -60,28 +60,33 @@ std::vector<WorkItem> plan_forward(const int32_t* windows, const int32_t* sinks,
 
 // Forward items with long key ranges split into chunks (for launches with
 // fewer items than the device holds workgroups).  Every item of more than
-// chunk_tiles key tiles becomes ceil(n / chunk_tiles) items over consecutive
-// sub-ranges of its tiles; each chunk writes its rows' unnormalised partial
-// result to its own slot (slot[i] >= 0) and one merge record {bh, tile, first
-// slot, number of chunks} per split item combines them.  Items of at most
-// chunk_tiles tiles keep slot -1 and write O and LSE themselves.  Chunks are
-// dealt to queues and ordered like plan_forward's items (longest first).
-// No sink keys: a sink tile belongs to the first chunk of an item only.
+// chunk_tiles window tiles becomes ceil(n / chunk_tiles) items over
+// consecutive sub-ranges of its tiles; each chunk writes its rows'
+// unnormalised partial result to its own slot (slot[i] >= 0) and one merge
+// record {bh, tile, first slot, number of chunks} per split item combines
+// them.  Items of at most chunk_tiles tiles keep slot -1 and write O and LSE
+// themselves.  Chunks are dealt to queues and ordered like plan_forward's
+// items (longest first).  sinks: int32[H] or nullptr; an item's sink tiles are
+// visited by its first chunk only (the one whose range starts at the window's
+// first tile), and count in that chunk's cost.
 struct SplitPlan {
   std::vector<WorkItem> items;
   std::vector<int32_t> slot;
   std::vector<WorkItem> merges;
   int n_slots = 0;
 };
-SplitPlan plan_forward_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
-                             int n_queues, int chunk_tiles);
+SplitPlan plan_forward_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                             int q_tile, int kv_tile, int n_queues, int chunk_tiles);
 
-// Backward (key-stationary) items split the same way along their query-tile
-// ranges, for one key/value head per query head and no sink keys: every item
-// of more than chunk_tiles query tiles becomes chunks with slots, and a merge
-// record {bh, key tile, first slot, chunks} per split item.
-SplitPlan plan_backward_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                              int chunk_tiles);
+// Backward (key-stationary) items of plan_backward split along their query-tile
+// ranges: an item whose steps (query tiles summed over the group's query
+// heads, each over its own range from lo) exceed chunk_tiles becomes
+// ceil(steps / chunk_tiles) chunks over consecutive sub-ranges [c_lo, c_hi) of
+// [lo, hi) with near-equal steps, each running every head of the group over
+// its part of the range (a head whose range ends before c_lo has none), with
+// slots, and a merge record {bh, key tile, first slot, chunks} per split item.
+SplitPlan plan_backward_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles);
 
 // Backward items: one per (b, key/value head g, key tile); [lo, hi) spans the
 // query tiles that see the keys in any of the group's query heads (each head's

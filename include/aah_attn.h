@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 11
+#define AAH_ABI_VERSION 12
 
 typedef enum {
   AAH_OK = 0,
@@ -133,7 +133,8 @@ const char* aah_last_error_detail(void);
  * items' key ranges into chunks whose partial results (row max, row sum, fp32
  * accumulator) land in the workspace, and a second kernel on the same stream
  * merges them into o and lse.  That fills the device when B * H * ceil(T / 128)
- * is small (one sequence, few heads).  The results agree within the bf16
+ * is small (one sequence, few heads).  With sink keys the first chunk of an
+ * item also visits its sink tiles.  The results agree within the bf16
  * bounds, not bitwise, since each chunk rounds its weights against its own
  * reference.  The workspace carries nothing between calls; calls that share one
  * must not run concurrently.
@@ -147,7 +148,7 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v,
 /*
  * Workspace bytes with which aah_attn_fwd splits long items (see above) for
  * these windows and shape on the current device: 0 when it would not split
- * (fp32, sink keys, enough work items already, or invalid arguments).  Queries
+ * (fp32, enough work items already, or invalid arguments).  Queries
  * the device's occupancy and builds the split work list on first use per shape
  * (cached like the other work lists).
  */
@@ -157,8 +158,10 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
 /*
  * Workspace bytes with which the backward (aah_attn_bwd, and each of its two
  * steps) splits long items as the forward does, for these windows and shape
- * on the current device; 0 when it would not (fp32, sink keys, grouped
- * key/value heads, enough work items, invalid arguments).  Such a workspace
+ * on the current device; 0 when it would not (fp32, enough work items,
+ * invalid arguments).  Sink keys and grouped key/value heads split too (the
+ * dK/dV chunks of a grouped item cut its query-tile range, each running every
+ * query head of the group over its part).  Such a workspace
  * holds the usual rows first (so it also serves an unsplit call), then each
  * split kernel's partial sums; a merge launch after each split kernel adds
  * them in a fixed order (results stay deterministic, and agree with the
@@ -388,31 +391,35 @@ aah_status aah_plan_fwd(const int32_t* windows, const int32_t* sinks, int B, int
                         aah_work_item* items, int64_t capacity, int64_t* n_items);
 
 /*
- * Split forward work list (host only, no GPU): as aah_plan_fwd without sinks,
- * but every item of more than chunk_tiles key tiles becomes items over
- * consecutive near-equal sub-ranges of its tiles (the split launch of
- * aah_attn_fwd).  slots[i] is item i's partial-result slot, -1 for an item
- * that writes its own rows; merges holds one record per split item:
+ * Split forward work list (host only, no GPU): as aah_plan_fwd, but every
+ * item of more than chunk_tiles window tiles becomes items over consecutive
+ * near-equal sub-ranges of those tiles (the split launch of aah_attn_fwd); an
+ * item's sink tiles belong to its first chunk, the one whose range starts at
+ * the window's first tile.  slots[i] is item i's partial-result slot, -1 for
+ * an item that writes its own rows; merges holds one record per split item:
  * (bh, q_tile_index, first slot, number of chunks).  Writes up to `capacity`
  * items and slots and up to `merge_capacity` records, stores the full counts
  * in *n_items and *n_merges, and returns AAH_ERR_INVALID_ARG if either
  * capacity is too small (after setting both counts).
  */
-aah_status aah_plan_fwd_split(const int32_t* windows, int B, int H, int H_kv, int T, int q_tile, int kv_tile,
-                              int n_queues, int chunk_tiles, aah_work_item* items, int32_t* slots,
-                              int64_t capacity, int64_t* n_items, aah_work_item* merges, int64_t merge_capacity,
-                              int64_t* n_merges);
+aah_status aah_plan_fwd_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles, aah_work_item* items,
+                              int32_t* slots, int64_t capacity, int64_t* n_items, aah_work_item* merges,
+                              int64_t merge_capacity, int64_t* n_merges);
 
 /*
- * Split backward (dK/dV) work list, host only: as aah_plan_bwd for one
- * key/value head per query head and no sinks, with every key item of more
- * than chunk_tiles query tiles cut into items over consecutive near-equal
- * sub-ranges; slots and merge records (bh, key tile index, first slot,
- * chunks) as for aah_plan_fwd_split.
+ * Split backward (dK/dV) work list, host only: as aah_plan_bwd, with every
+ * key item whose steps (query tiles summed over the group's query heads, each
+ * over its own range from lo) exceed chunk_tiles cut into items over
+ * consecutive sub-ranges [c_lo, c_hi) of its range [lo, hi) with near-equal
+ * steps, each running every head of the group over its part of the range;
+ * slots and merge records (bh, key tile index, first slot, chunks) as for
+ * aah_plan_fwd_split.
  */
-aah_status aah_plan_bwd_split(const int32_t* windows, int B, int H, int T, int q_tile, int kv_tile, int n_queues,
-                              int chunk_tiles, aah_work_item* items, int32_t* slots, int64_t capacity,
-                              int64_t* n_items, aah_work_item* merges, int64_t merge_capacity, int64_t* n_merges);
+aah_status aah_plan_bwd_split(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                              int q_tile, int kv_tile, int n_queues, int chunk_tiles, aah_work_item* items,
+                              int32_t* slots, int64_t capacity, int64_t* n_items, aah_work_item* merges,
+                              int64_t merge_capacity, int64_t* n_merges);
 
 aah_status aah_plan_bwd(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
                         int q_tile, int kv_tile, int n_queues,

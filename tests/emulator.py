@@ -58,10 +58,12 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
     return O, L
 
 
-def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile, kv_tile):
+def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile, kv_tile, sinks=None):
     """The split forward: each item runs its own key tiles; an item with a slot leaves (m, l, acc) of its
     rows there, and every merge record (bh, q tile, first slot, chunks) combines its chunks as
-    M = max m_c, L = sum exp(m_c - M) l_c, O = sum exp(m_c - M) acc_c / L, LSE = M + ln L."""
+    M = max m_c, L = sum exp(m_c - M) l_c, O = sum exp(m_c - M) acc_c / L, LSE = M + ln L.  With sink
+    sizes, the chunk whose range starts at the window's first tile (every unsplit item's does) also visits
+    the sink tiles [0, min(ceil(S / kv_tile), lo))."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, T, d = q.shape
     O = np.full((B, H, T, d), np.nan)
@@ -73,13 +75,16 @@ def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile,
         b, h = divmod(int(bh), H)
         g = h // (H // k.shape[1])
         W = min(int(windows[h]), T)
+        S = _eff_sink(sinks, h, T, W)
         rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
         m = np.full(len(rows), -np.inf)
         l = np.zeros(len(rows))
         acc = np.zeros((len(rows), d))
-        for kt in range(lo, hi):
+        first = int(lo) == max(0, int(rows[0]) - W + 1) // kv_tile
+        n_sink = min(-(-S // kv_tile), int(lo)) if first else 0
+        for kt in list(range(n_sink)) + list(range(lo, hi)):
             keys = np.arange(kt * kv_tile, min(T, (kt + 1) * kv_tile))
-            s = np.where(_visible(rows, keys, W, 0), scale * q[b, h, rows] @ k[b, g, keys].T, -np.inf)
+            s = np.where(_visible(rows, keys, W, S), scale * q[b, h, rows] @ k[b, g, keys].T, -np.inf)
             m_new = np.maximum(m, s.max(axis=1))
             m_use = np.where(np.isneginf(m_new), 0.0, m_new)
             alpha = np.exp(m - m_use)

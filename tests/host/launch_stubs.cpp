@@ -36,13 +36,13 @@ hipError_t launch_bwd_dq_bf16(const void*, const void*, const void*, const void*
   return hipErrorNoDevice;
 }
 hipError_t launch_bwd_dkdv_bf16_split(const void*, const void*, const void*, const void*, const float*, const float*,
-                                      void*, void*, const WorkItem*, int, const int32_t*, const AttnShape&,
-                                      const BwdSplit&, hipStream_t) {
+                                      void*, void*, const WorkItem*, int, const int32_t*, const int32_t*,
+                                      const AttnShape&, const BwdSplit&, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_bwd_dq_bf16_split(const void*, const void*, const void*, const void*, const void*, const float*,
-                                    float*, float*, void*, const WorkItem*, int, const int32_t*, const AttnShape&,
-                                    const BwdSplit&, hipStream_t) {
+                                    float*, float*, void*, const WorkItem*, int, const int32_t*, const int32_t*,
+                                    const AttnShape&, const BwdSplit&, hipStream_t) {
   return hipErrorNoDevice;
 }
 hipError_t launch_bwd_dq_simple(const float*, const float*, const float*, const float*, const float*, const float*,

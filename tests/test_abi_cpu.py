@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 11
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 12
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name

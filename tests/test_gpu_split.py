@@ -40,15 +40,17 @@ def _ws_bytes(windows, B, H, T, d, sinks=None, dt=BF16, H_kv=None):
     return lib().aah_attn_fwd_workspace_size(w.ctypes.data_as(P), sp, B, H, H if H_kv is None else H_kv, T, d, dt)
 
 
-def _fwd_unsplit(q, k, v, windows, scale):
+def _fwd_unsplit(q, k, v, windows, scale, sinks=None):
     """The forward with no workspace: one workgroup per item, every item writes its own rows."""
     B, H, T, d = q.shape
     H_kv = k.shape[1]
     w = np.ascontiguousarray(windows, dtype=np.int32)
+    P = ctypes.POINTER(ctypes.c_int32)
+    sk = None if sinks is None else np.ascontiguousarray(sinks, dtype=np.int32)
     o = torch.empty_like(q)
     lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
-    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                            w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, B, H, H_kv, T, d, BF16,
+    st = lib().aah_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), w.ctypes.data_as(P),
+                            None if sk is None else sk.ctypes.data_as(P), B, H, H_kv, T, d, BF16,
                             float(scale), o.data_ptr(), lse.data_ptr(), None, 0,
                             torch.cuda.current_stream().cuda_stream)
     aah.check(st)
@@ -56,7 +58,7 @@ def _fwd_unsplit(q, k, v, windows, scale):
 
 
 def _check_full(wl, o, lse):
-    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale)
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, sinks=wl.sinks)
     got = o.float().cpu().numpy().astype(np.float64)
     bound = np.maximum(O_TOL_BF16, np.abs(O) * 2.0 ** -8)
     assert (np.abs(got - O) - bound).max() <= 0, f"max |dO| {np.abs(got - O).max():.3e}"
@@ -64,13 +66,14 @@ def _check_full(wl, o, lse):
 
 
 def test_split_applies_only_where_it_should():
-    """Workspace (and so a split launch) only for bf16 without sinks and with too few items."""
+    """Workspace (and so a split launch) only for bf16 with too few items, some of them long."""
     _require_gpu()
     single = synth.make_workload(1)
     assert _ws_bytes(single.windows, 1, 16, 4096, 64) > 0          # 512 items: splits
     assert _ws_bytes([4096] * 32, 4, 32, 4096, 64) == 0            # 4096 items fill the device
     assert _ws_bytes([4096] * 16, 1, 16, 4096, 64, dt=F32) == 0   # the fp32 path never splits
-    assert _ws_bytes([256] * 4, 1, 4, 4096, 64, sinks=[128] * 4) == 0
+    assert _ws_bytes([256] * 4, 1, 4, 4096, 64, sinks=[128] * 4) == 0  # sink + 256: no long item
+    assert _ws_bytes([2048, 256] * 2, 1, 4, 4096, 64, sinks=[64, 128] * 2) > 0
     assert _ws_bytes([1024] * 4, 1, 4, 1024, 64) == 0              # no item longer than the shortest chunk
     assert _ws_bytes([0] * 4, 1, 4, 512, 64) == 0                  # invalid window: no workspace
 
@@ -214,7 +217,7 @@ def test_split_backward_matches_oracle(B, H, T, d, windows):
 
 def test_split_backward_close_to_unsplit_and_deterministic():
     """B=1 H=16 T=4096 (the single layer with dO): split and unsplit backward agree within the gradient bound,
-    and repeated split calls are bitwise equal; grouped heads and sinks never ask for a split workspace."""
+    and repeated split calls are bitwise equal; a layer with enough items asks for no split workspace."""
     _require_gpu()
     wl = synth.random_workload(1, 16, 4096, 64, synth.make_workload(1).windows, dtype="bf16", seed=3, backward=True)
     q, k, v, do = (_dev(wl, key) for key in ("q", "k", "v", "do"))
@@ -230,6 +233,57 @@ def test_split_backward_close_to_unsplit_and_deterministic():
         assert torch.equal(a, b)
         ref = c.float()
         assert (a.float() - ref).abs().max().item() <= 2 * GRAD_REL * ref.abs().max().item()
-    assert _bwd_ws_bytes([4096] * 4, 1, 4, 4096, 64, H_kv=2) == 0
-    assert _bwd_ws_bytes([256] * 4, 1, 4, 4096, 64, sinks=[128] * 4) == 0
     assert _bwd_ws_bytes([4096] * 32, 4, 32, 4096, 64) == 0
+
+
+def test_split_forward_sinks_matches_oracle():
+    """Sink heads ("Autonomy-of-Heads", section 5) take the split launch: only the first chunk of an item (the
+    one that starts at its window's first tile) visits the sink tiles, so no sink key counts twice.  B=1,
+    H=4, ragged T=3000: heads with sink 64 / window 2000 and sink 300 / window 1500 have items of 25-33 key
+    tiles, cut into chunks; every row against the oracle, and split against unsplit within the bf16 bounds."""
+    _require_gpu()
+    B, H, T, d = 1, 4, 3000, 64
+    windows, sinks = [2000, 256, 3000, 1500], [64, 128, 0, 300]
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=91, backward=False, sinks=sinks)
+    assert _ws_bytes(wl.windows, B, H, T, d, sinks=sinks) > 0
+    q, k, v = _dev(wl, "q"), _dev(wl, "k"), _dev(wl, "v")
+    o, lse = aah.attn_fwd(q, k, v, wl.windows, wl.scale, sinks=sinks)
+    o2, l2 = aah.attn_fwd(q, k, v, wl.windows, wl.scale, sinks=sinks)
+    ou, lu = _fwd_unsplit(q, k, v, wl.windows, wl.scale, sinks=sinks)
+    torch.cuda.synchronize()
+    _check_full(wl, o, lse)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)
+    a, b = o.float().cpu().numpy(), ou.float().cpu().numpy()
+    assert (np.abs(a - b) - np.maximum(2 * O_TOL_BF16, np.abs(b) * 2.0 ** -7)).max() <= 0
+    assert (lse - lu).abs().max().item() < 2 * LSE_TOL_BF16
+
+
+@pytest.mark.parametrize("B,H,H_kv,T,d,windows,sinks", [
+    (1, 4, 2, 2048, 64, [2048, 300, 1000, 64], None),            # groups whose heads end at different tiles
+    (1, 4, 4, 2500, 64, [256, 2500, 1000, 128], [128, 0, 64, 300]),  # sink key tiles run to the last query
+    (1, 4, 1, 2000, 128, [600, 2000, 64, 900], [0, 0, 200, 64]),     # one K/V head for all, with sinks
+])
+def test_split_backward_sinks_and_groups_match_oracle(B, H, H_kv, T, d, windows, sinks):
+    """Few-item backward with grouped K/V heads (AAH appendix A.3) and sink keys: dQ chunks (sink tiles with
+    the first chunk only) and dK/dV chunks (a grouped item's query-tile range cut, each chunk running every
+    head of the group over its part) summed by the merges.  Gradients against the oracle; split against the
+    unsplit launch within twice the bound; repeated split calls bitwise equal."""
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=T + 3 * d + H_kv, backward=True,
+                               sinks=sinks, H_kv=H_kv)
+    need = _bwd_ws_bytes(wl.windows, B, H, T, d, sinks=sinks, H_kv=H_kv)
+    assert need > aah.workspace_size(B, H, T, d, "bf16")
+    q, k, v, do = (_dev(wl, key) for key in ("q", "k", "v", "do"))
+    o, lse = aah.attn_fwd(q, k, v, wl.windows, wl.scale, sinks=sinks)
+    g1 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, sinks=sinks)
+    g2 = aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, sinks=sinks)
+    plain = torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda")
+    gu = aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, workspace=plain, sinks=sinks)
+    torch.cuda.synchronize()
+    refs = oracle.attn_bwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, wl.do, sinks=sinks)
+    for name, a, b, c, ref in zip(("dq", "dk", "dv"), g1, g2, gu, refs):
+        assert torch.equal(a, b), name
+        err = np.abs(a.float().cpu().numpy() - ref).max()
+        assert err <= GRAD_REL * np.abs(ref).max(), (name, err)
+        ru = c.float()
+        assert (a.float() - ru).abs().max().item() <= 2 * GRAD_REL * ru.abs().max().item(), name
