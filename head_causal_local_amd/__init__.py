@@ -139,8 +139,9 @@ def attn_fwd(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None
 
 
 def attn_fwd_diag(q, k, v, windows, scale: Optional[float] = None, out=None, lse=None, row_entropy=None,
-                  row_onorm=None, stream=None, sinks=None):
-    """attn_fwd plus the per-row attention entropy and output norm (float32 [B, H, T] each).
+                  row_onorm=None, stream=None, sinks=None, workspace=None):
+    """attn_fwd plus the per-row attention entropy and output norm (float32 [B, H, T] each).  workspace as
+    for attn_fwd, sized by fwd_diag_workspace_size.
 
     Returns (O, LSE, row_entropy, row_onorm)."""
     import torch
@@ -164,9 +165,17 @@ def attn_fwd_diag(q, k, v, windows, scale: Optional[float] = None, out=None, lse
         rows.append(t)
     lse, row_entropy, row_onorm = rows
     sk = _sinks_arg(sinks, H)
+    if workspace is None:
+        # Workspace for the split launch when the library asks for one.
+        ws_bytes = lib().aah_attn_fwd_diag_workspace_size(_wptr(w), _sptr(sk), B, H, H_kv, T, d, _dtype_code(q))
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    else:
+        ws_bytes = workspace.numel() * workspace.element_size()
+        ws = workspace if ws_bytes else None
     check(lib().aah_attn_fwd_diag(q.data_ptr(), k.data_ptr(), v.data_ptr(), _wptr(w), _sptr(sk), B, H, H_kv, T, d,
                                   _dtype_code(q), float(scale), out.data_ptr(), lse.data_ptr(),
-                                  row_entropy.data_ptr(), row_onorm.data_ptr(), _stream_ptr(q, stream)))
+                                  row_entropy.data_ptr(), row_onorm.data_ptr(),
+                                  ws.data_ptr() if ws is not None else None, ws_bytes, _stream_ptr(q, stream)))
     return out, lse, row_entropy, row_onorm
 
 
@@ -487,12 +496,14 @@ def plan_bwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_til
 
 
 def fwd_workspace_size(windows: Sequence[int], B: int, H: int, T: int, d: int, dtype: str = "bf16",
-                       sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None) -> int:
-    """Workspace bytes with which the forward splits long items on the current device (0: it does not)."""
+                       sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None, diag: bool = False) -> int:
+    """Workspace bytes with which the forward (diag: the diagnostic forward) splits long items on the current
+    device (0: it does not)."""
     w = _windows_arg(windows)
     sk = _sinks_arg(sinks, H)
     code = AAH_BF16 if dtype == "bf16" else AAH_F32
-    return int(lib().aah_attn_fwd_workspace_size(_wptr(w), _sptr(sk), B, H, H if H_kv is None else H_kv, T, d, code))
+    fn = lib().aah_attn_fwd_diag_workspace_size if diag else lib().aah_attn_fwd_workspace_size
+    return int(fn(_wptr(w), _sptr(sk), B, H, H if H_kv is None else H_kv, T, d, code))
 
 
 def _plan_split(fn, windows, sinks, B, H, T, q_tile, kv_tile, chunk_tiles, n_queues, H_kv):

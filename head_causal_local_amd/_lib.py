@@ -19,7 +19,7 @@ AAH_ERR_WORKSPACE = 3
 AAH_ERR_HIP = 4
 AAH_BF16 = 0
 AAH_F32 = 1
-ABI_VERSION = 12
+ABI_VERSION = 13
 
 EXPORTS = (
     "aah_abi_version", "aah_status_string", "aah_last_error_detail", "aah_attn_fwd", "aah_attn_bwd",
@@ -28,6 +28,7 @@ EXPORTS = (
     "aah_cache_clear", "aah_attn_bwd_dq", "aah_attn_bwd_dkdv", "aah_kv_cache_rows",
     "aah_attn_decode_workspace_size", "aah_kv_cache_fill", "aah_attn_decode", "aah_attn_fwd_diag",
     "aah_head_features_workspace_size", "aah_head_features", "aah_attn_decode_noalloc", "aah_cache_entries",
+    "aah_attn_fwd_diag_workspace_size",
 )
 
 
@@ -67,7 +68,8 @@ def _declare(lib):
                                  c_int, c_float, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.aah_attn_fwd_diag.restype = c_int
     lib.aah_attn_fwd_diag.argtypes = [c_void_p, c_void_p, c_void_p, P_i32, P_i32, c_int, c_int, c_int, c_int, c_int,
-                                      c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]
+                                      c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                      c_void_p]
     lib.aah_head_features_workspace_size.restype = c_size_t
     lib.aah_head_features_workspace_size.argtypes = [c_int, c_int, c_int, c_int]
     lib.aah_head_features.restype = c_int
@@ -87,8 +89,9 @@ def _declare(lib):
                                     c_void_p]
     lib.aah_attn_bwd_split_workspace_size.restype = c_size_t
     lib.aah_attn_bwd_split_workspace_size.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
-    lib.aah_attn_fwd_workspace_size.restype = c_size_t
-    lib.aah_attn_fwd_workspace_size.argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
+    for name in ("aah_attn_fwd_workspace_size", "aah_attn_fwd_diag_workspace_size"):
+        getattr(lib, name).restype = c_size_t
+        getattr(lib, name).argtypes = [P_i32, P_i32, c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_attn_workspace_size.restype = c_size_t
     lib.aah_attn_workspace_size.argtypes = [c_int, c_int, c_int, c_int, c_int, c_int]
     lib.aah_tile_shape.restype = c_int

@@ -430,9 +430,10 @@ aah::PlanLru<SplitDevicePlan> g_split_cache(kCacheCapacity);
 size_t split_acc_bytes(int n_slots, int d) {
   return round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * d * sizeof(float), 256);
 }
-size_t split_workspace(int n_slots, int d) {
+size_t split_workspace(int n_slots, int d, bool diag = false) {
   return split_acc_bytes(n_slots, d) +
-         round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * 2 * sizeof(float), 256);
+         round_up(static_cast<size_t>(n_slots) * aah::kFwdBf16RowTile * (diag ? aah::kMlDiag : 2) * sizeof(float),
+                  256);
 }
 
 // Split plan with chunk length L (> 0), uploaded once per key.  kind 0: query-stationary items (forward,
@@ -780,8 +781,9 @@ size_t aah_attn_workspace_size(int B, int H, int T, int d, aah_dtype dt, int is_
   return is_bwd ? bwd_workspace(B, H, T, d, dt) : 0;
 }
 
-size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
-                                   int d, aah_dtype dt) {
+// Forward split workspace (with the diagnostics' larger per-row partials when diag is set).
+size_t fwd_split_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T, int d,
+                                aah_dtype dt, bool diag) {
   if (dt != AAH_BF16 || check_shape(windows, sinks, B, H, T, d, dt, H_kv) != AAH_OK) return 0;
   g_detail.clear();
   if (empty_problem(B, T)) return 0;
@@ -789,7 +791,17 @@ size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks,
   if (L == 0) return 0;
   SplitDevicePlan sp;
   if (get_split_plan(windows, sinks, B, H, H_kv, T, d, L, nullptr, &sp) != AAH_OK) return 0;
-  return split_workspace(sp.n_slots, d);
+  return split_workspace(sp.n_slots, d, diag);
+}
+
+size_t aah_attn_fwd_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                                   int d, aah_dtype dt) {
+  return fwd_split_workspace_size(windows, sinks, B, H, H_kv, T, d, dt, false);
+}
+
+size_t aah_attn_fwd_diag_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv, int T,
+                                        int d, aah_dtype dt) {
+  return fwd_split_workspace_size(windows, sinks, B, H, H_kv, T, d, dt, true);
 }
 
 size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
@@ -839,19 +851,16 @@ aah_status fwd_impl(const void* q, const void* k, const void* v, const int32_t* 
   const aah::AttnShape s{B, H, T, d, scale, H_kv};
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
-  // Split launch: bf16, no diagnostics, and a workspace large enough for the partials.
-  const int L = dt == AAH_BF16 && ent == nullptr && workspace != nullptr
-                    ? split_chunk_tiles(windows, sinks, B, H, T, d)
-                    : 0;
+  // Split launch: bf16 and a workspace large enough for the partials (larger with the diagnostics).
+  const int L = dt == AAH_BF16 && workspace != nullptr ? split_chunk_tiles(windows, sinks, B, H, T, d) : 0;
   if (L > 0) {
     SplitDevicePlan sp;
     AAH_TRY(get_split_plan(windows, sinks, B, H, H_kv, T, d, L, st, &sp));
-    if (workspace_bytes >= split_workspace(sp.n_slots, d)) {
+    if (workspace_bytes >= split_workspace(sp.n_slots, d, ent != nullptr)) {
       float* part_acc = static_cast<float*>(workspace);
       float* part_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_acc_bytes(sp.n_slots, d));
       const aah::FwdSplit split{sp.slots, sp.merges, sp.n_merges, part_acc, part_ml};
-      e = aah::launch_fwd_bf16(q, k, v, o, lse, nullptr, nullptr, sp.items, sp.n_items, sp.win, sp.sink, s, &split,
-                               st);
+      e = aah::launch_fwd_bf16(q, k, v, o, lse, ent, onorm, sp.items, sp.n_items, sp.win, sp.sink, s, &split, st);
       if (e != hipSuccess) return hip_fail(e, "split forward launch");
       return AAH_OK;
     }
@@ -887,14 +896,15 @@ aah_status aah_attn_fwd(const void* q, const void* k, const void* v, const int32
 
 aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
                              const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
-                             void* o, float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream) {
+                             void* o, float* lse, float* row_entropy, float* row_onorm, void* workspace,
+                             size_t workspace_bytes, aah_stream_t stream) {
   g_detail.clear();
   if (!empty_problem(B, T)) {
     AAH_TRY(check_tensor(row_entropy, "row_entropy", 4));
     AAH_TRY(check_tensor(row_onorm, "row_onorm", 4));
   }
-  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, nullptr, 0,
-                  stream);
+  return fwd_impl(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm, workspace,
+                  workspace_bytes, stream);
 }
 
 size_t aah_head_features_workspace_size(int B, int H, int T, int d) {

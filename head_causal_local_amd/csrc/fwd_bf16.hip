@@ -429,7 +429,8 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
   if (!row_ok) return;
   if (slot >= 0) {
     // Unnormalised partial of row qi over this chunk's keys: acc (fp32, [d]), then (m, l) with m in
-    // the log2 domain (-inf and l = 0 if the row saw none of them).
+    // the log2 domain (-inf and l = 0 if the row saw none of them); DIAG adds a = sum p x, the weights
+    // times their offsets x = s c - m (0 for such a row).
     const size_t prow = static_cast<size_t>(slot) * kRows + wave * 32 + ln;
     float* arow = part_acc + prow * D;
 #pragma unroll
@@ -438,7 +439,13 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
       for (int i = 0; i < 4; ++i)
         *reinterpret_cast<f32x4*>(arow + 32 * b + 8 * i + 4 * hl) =
             f32x4{acc[b][4 * i], acc[b][4 * i + 1], acc[b][4 * i + 2], acc[b][4 * i + 3]};
-    if (hl == 0) *reinterpret_cast<u32x2*>(part_ml + prow * 2) = u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)};
+    if constexpr (DIAG) {
+      if (hl == 0)
+        *reinterpret_cast<f32x4*>(part_ml + prow * kMlDiag) = f32x4{m_run, l_tot, a_tot, 0.f};
+    } else {
+      if (hl == 0)
+        *reinterpret_cast<u32x2*>(part_ml + prow * 2) = u32x2{__float_as_uint(m_run), __float_as_uint(l_tot)};
+    }
     return;
   }
   const float inv = __builtin_amdgcn_rcpf(l_tot);  // l_tot >= 1: the key that set the reference weighs 1
@@ -463,34 +470,57 @@ void fwd_bf16_kernel(const bf16* __restrict__ Q, const bf16* __restrict__ K, con
 // Combines the chunks of each split item: with (acc_c, m_c, l_c) the partials
 // of row i over chunk c and M = max_c m_c, O_i = sum_c 2^(m_c - M) acc_c /
 // sum_c 2^(m_c - M) l_c and LSE_i = (M + log2 sum_c 2^(m_c - M) l_c) ln 2.
+// DIAG: the chunks' weighted offsets a_c, taken to the common reference M,
+// add up to A = sum_c 2^(m_c - M) (a_c + (m_c - M) l_c) (chunks the row did not
+// see count 0), so the entropy is (log2 L - A / L) ln 2 as in an unsplit row,
+// and the output norm is |sum_c 2^(m_c - M) acc_c| / L (the D / 4 threads of a
+// row, consecutive lanes of one wave, add their squares by lane swaps).
 // Workgroup (merge record, row group); D / 4 threads per row, four dims each.
-template <int D>
+template <int D, bool DIAG>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(const WorkItem* __restrict__ merges,
                                                         const float* __restrict__ part_acc,
                                                         const float* __restrict__ part_ml, bf16* __restrict__ O,
-                                                        float* __restrict__ LSE, int T) {
+                                                        float* __restrict__ LSE, float* __restrict__ ENT,
+                                                        float* __restrict__ ONORM, int T) {
   constexpr int kPerRow = D / 4;
   constexpr int kRowsPerWg = 256 / kPerRow;
+  constexpr int kMl = DIAG ? kMlDiag : 2;  // floats per row of part_ml
   const WorkItem mg = merges[blockIdx.x];  // {bh, tile, first slot, chunks}
   const int r = blockIdx.y * kRowsPerWg + static_cast<int>(threadIdx.x) / kPerRow;
   const int dq = (static_cast<int>(threadIdx.x) % kPerRow) * 4;
   const int row = mg.tile * kRows + r;
+  // Rows past T leave together with the rest of their kPerRow-thread group, so the DIAG lane swaps
+  // below only ever combine lanes that are all present.
   if (r >= kRows || row >= T) return;
   float M = -INFINITY;
-  for (int ch = 0; ch < mg.hi; ++ch) M = fmaxf(M, part_ml[(static_cast<size_t>(mg.lo + ch) * kRows + r) * 2]);
-  float L = 0.f;
+  for (int ch = 0; ch < mg.hi; ++ch) M = fmaxf(M, part_ml[(static_cast<size_t>(mg.lo + ch) * kRows + r) * kMl]);
+  float L = 0.f, A = 0.f;
   f32x4 a = f32x4{};
   for (int ch = 0; ch < mg.hi; ++ch) {
     const size_t prow = static_cast<size_t>(mg.lo + ch) * kRows + r;
-    const float w = __builtin_amdgcn_exp2f(part_ml[prow * 2] - M);  // 0 for a chunk the row did not see
-    L = fmaf(w, part_ml[prow * 2 + 1], L);
+    const float m_c = part_ml[prow * kMl];
+    const float w = __builtin_amdgcn_exp2f(m_c - M);  // 0 for a chunk the row did not see
+    L = fmaf(w, part_ml[prow * kMl + 1], L);
+    if constexpr (DIAG) {
+      if (m_c != -INFINITY) A = fmaf(w, fmaf(m_c - M, part_ml[prow * kMl + 1], part_ml[prow * kMl + 2]), A);
+    }
     const f32x4 x = *reinterpret_cast<const f32x4*>(part_acc + prow * D + dq);
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = fmaf(w, x[j], a[j]);
   }
   const float inv = 1.f / L;
   store_bf16x4(O + (static_cast<size_t>(mg.bh) * T + row) * D + dq, a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv);
-  if (dq == 0) LSE[static_cast<size_t>(mg.bh) * T + row] = (M + log2f(L)) * kLn2;
+  const size_t orow = static_cast<size_t>(mg.bh) * T + row;
+  if constexpr (DIAG) {
+    float sq = a[0] * a[0] + a[1] * a[1] + a[2] * a[2] + a[3] * a[3];
+#pragma unroll
+    for (int o = 1; o < kPerRow; o <<= 1) sq += __shfl_xor(sq, o);
+    if (dq == 0) {
+      ENT[orow] = (log2f(L) - A * inv) * kLn2;
+      ONORM[orow] = sqrtf(sq) * inv;
+    }
+  }
+  if (dq == 0) LSE[orow] = (M + log2f(L)) * kLn2;
 }
 
 template <int D, bool SINK, bool DIAG>
@@ -504,8 +534,9 @@ void launch_k(const void* q, const void* k, const void* v, void* o, float* lse, 
                      split != nullptr ? split->slots : nullptr, split != nullptr ? split->part_acc : nullptr,
                      split != nullptr ? split->part_ml : nullptr, log2_exact(s.H), log2_exact(s.H / s.H_kv));
   if (split != nullptr && split->n_merges > 0)
-    hipLaunchKernelGGL((fwd_merge_kernel<D>), dim3(split->n_merges, kRows / (256 / (D / 4))), dim3(256), 0, stream,
-                       split->merges, split->part_acc, split->part_ml, static_cast<bf16*>(o), lse, s.T);
+    hipLaunchKernelGGL((fwd_merge_kernel<D, DIAG>), dim3(split->n_merges, kRows / (256 / (D / 4))), dim3(256), 0,
+                       stream, split->merges, split->part_acc, split->part_ml, static_cast<bf16*>(o), lse, ent, onorm,
+                       s.T);
 }
 
 template <int D>

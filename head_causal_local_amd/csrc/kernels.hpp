@@ -44,9 +44,11 @@ inline int log2_exact(int n) {
 // or both null).
 // Split forward (plan_forward_split): slots[i] is item i's partial slot or -1;
 // a chunk writes its rows' fp32 accumulator to part_acc [slot][128][d] and
-// (max in the log2 domain, row sum) to part_ml [slot][128][2]; after the
-// forward, one merge workgroup group per record in merges combines them into O
-// and LSE.
+// (max in the log2 domain, row sum) to part_ml [slot][128][2] -- with the
+// diagnostics, (max, row sum, sum of weights times offsets, unused) to
+// part_ml [slot][128][kMlDiag]; after the forward, one merge workgroup group
+// per record in merges combines them into O and LSE (and the diagnostics).
+constexpr int kMlDiag = 4;
 struct FwdSplit {
   const int32_t* slots;
   const WorkItem* merges;

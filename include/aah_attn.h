@@ -83,7 +83,7 @@
 extern "C" {
 #endif
 
-#define AAH_ABI_VERSION 12
+#define AAH_ABI_VERSION 13
 
 typedef enum {
   AAH_OK = 0,
@@ -179,11 +179,24 @@ size_t aah_attn_bwd_split_workspace_size(const int32_t* windows, const int32_t* 
  * visible keys and row_onorm[b,h,i] = ||o_i||_2 (of the fp32 output before its
  * rounding to dt), both fp32 [B,H,T] device arrays, 4-byte aligned.  In bf16
  * the entropy is formed from the same rounded weights as lse: it is within
- * 2^-7 H + 2^-8 of the exact H.
+ * 2^-7 H + 2^-8 of the exact H.  Workspace: optional, as for aah_attn_fwd,
+ * with aah_attn_fwd_diag_workspace_size bytes for a split launch; its chunks
+ * also leave each row's sum of weights times their log-domain offsets, from
+ * which the merge forms the entropy, and the merge takes the output norm of
+ * the combined fp32 row.
  */
 aah_status aah_attn_fwd_diag(const void* q, const void* k, const void* v, const int32_t* windows,
                              const int32_t* sinks, int B, int H, int H_kv, int T, int d, aah_dtype dt, float scale,
-                             void* o, float* lse, float* row_entropy, float* row_onorm, aah_stream_t stream);
+                             void* o, float* lse, float* row_entropy, float* row_onorm, void* workspace,
+                             size_t workspace_bytes, aah_stream_t stream);
+
+/*
+ * Workspace bytes with which aah_attn_fwd_diag splits long items, as
+ * aah_attn_fwd_workspace_size for aah_attn_fwd (a little more: four floats
+ * of per-row partials instead of two); 0 when it would not split.
+ */
+size_t aah_attn_fwd_diag_workspace_size(const int32_t* windows, const int32_t* sinks, int B, int H, int H_kv,
+                                        int T, int d, aah_dtype dt);
 
 /*
  * Per-head controller features ("Asymmetric Attention Heads" section 5.3):

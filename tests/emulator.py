@@ -58,16 +58,22 @@ def emulate_forward(items, q, k, v, windows, scale, q_tile, kv_tile, sinks=None)
     return O, L
 
 
-def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile, kv_tile, sinks=None):
+def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile, kv_tile, sinks=None, diag=False):
     """The split forward: each item runs its own key tiles; an item with a slot leaves (m, l, acc) of its
     rows there, and every merge record (bh, q tile, first slot, chunks) combines its chunks as
     M = max m_c, L = sum exp(m_c - M) l_c, O = sum exp(m_c - M) acc_c / L, LSE = M + ln L.  With sink
     sizes, the chunk whose range starts at the window's first tile (every unsplit item's does) also visits
-    the sink tiles [0, min(ceil(S / kv_tile), lo))."""
+    the sink tiles [0, min(ceil(S / kv_tile), lo)).
+
+    diag: also the per-row entropy and output norm, each chunk keeping a = sum_j p_j (s_j - m) against its
+    own reference m and the merge taking it to M as A = sum_c exp(m_c - M) (a_c + (m_c - M) l_c), so that
+    entropy = ln L - A / L and norm = |acc| / L; returns (O, LSE, entropy, norm)."""
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, H, T, d = q.shape
     O = np.full((B, H, T, d), np.nan)
     L = np.full((B, H, T), np.nan)
+    ENT = np.full((B, H, T), np.nan)
+    NRM = np.full((B, H, T), np.nan)
     parts = {}
     for (bh, qt, lo, hi), slot in zip(items, slots):
         if bh < 0:
@@ -79,6 +85,7 @@ def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile,
         rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
         m = np.full(len(rows), -np.inf)
         l = np.zeros(len(rows))
+        a = np.zeros(len(rows))
         acc = np.zeros((len(rows), d))
         first = int(lo) == max(0, int(rows[0]) - W + 1) // kv_tile
         n_sink = min(-(-S // kv_tile), int(lo)) if first else 0
@@ -89,15 +96,21 @@ def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile,
             m_use = np.where(np.isneginf(m_new), 0.0, m_new)
             alpha = np.exp(m - m_use)
             p = np.exp(s - m_use[:, None])
+            # a about the new reference: the old terms move by (m - m_use) each (rows with a reference only)
+            shift = np.where(np.isneginf(m), 0.0, m - m_use)
+            with np.errstate(invalid="ignore"):  # masked keys: p = 0 times s - m = -inf, dropped by the where
+                a = alpha * (a + shift * l) + np.where(p > 0, p * (s - m_use[:, None]), 0.0).sum(axis=1)
             l = l * alpha + p.sum(axis=1)
             acc = acc * alpha[:, None] + p @ v[b, g, keys]
             m = m_new
         if slot < 0:
             O[b, h, rows] = acc / l[:, None]
             L[b, h, rows] = m + np.log(l)
+            ENT[b, h, rows] = np.log(l) - a / l
+            NRM[b, h, rows] = np.linalg.norm(acc, axis=1) / l
         else:
             assert int(slot) not in parts, "slot written twice"
-            parts[int(slot)] = (m, l, acc)
+            parts[int(slot)] = (m, l, acc, a)
     for bh, qt, first, n in merges:
         b, h = divmod(int(bh), H)
         rows = np.arange(qt * q_tile, min(T, (qt + 1) * q_tile))
@@ -106,9 +119,14 @@ def emulate_forward_split(items, slots, merges, q, k, v, windows, scale, q_tile,
         w = np.exp(ms - M)  # 0 for a chunk a row did not see (m = -inf)
         l = sum(w[c] * parts[first + c][1] for c in range(n))
         acc = sum(w[c][:, None] * parts[first + c][2] for c in range(n))
+        with np.errstate(invalid="ignore"):  # a chunk the row did not see: -inf times 0, dropped by the where
+            A = sum(np.where(np.isneginf(ms[c]), 0.0,
+                             w[c] * (parts[first + c][3] + (ms[c] - M) * parts[first + c][1])) for c in range(n))
         O[b, h, rows] = acc / l[:, None]
         L[b, h, rows] = M + np.log(l)
-    return O, L
+        ENT[b, h, rows] = np.log(l) - A / l
+        NRM[b, h, rows] = np.linalg.norm(acc, axis=1) / l
+    return (O, L, ENT, NRM) if diag else (O, L)
 
 
 def emulate_backward(items, q, k, v, do, lse, windows, scale, q_tile, kv_tile, sinks=None, split=False):

@@ -32,7 +32,7 @@ def test_header_symbols_exported():
 
 def test_abi_version_and_status_strings():
     lib = _lib.lib()
-    assert lib.aah_abi_version() == _lib.ABI_VERSION == 12
+    assert lib.aah_abi_version() == _lib.ABI_VERSION == 13
     for code, name in [(0, b"AAH_OK"), (1, b"AAH_ERR_INVALID_ARG"), (2, b"AAH_ERR_UNSUPPORTED"),
                        (3, b"AAH_ERR_WORKSPACE"), (4, b"AAH_ERR_HIP")]:
         assert lib.aah_status_string(code) == name
@@ -354,12 +354,18 @@ def test_diag_and_feature_validation():
     w = np.array([4, 9], dtype=np.int32)
     wp = w.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     # aah_attn_fwd_diag(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, row_entropy, row_onorm,
-    #                   stream)
-    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, 0, FAKE, None) == 1
+    #                   workspace, workspace_bytes, stream)
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, 0, FAKE, None, 0,
+                                 None) == 1
     assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, FAKE + 2,
-                                 None) == 1                                     # misaligned
+                                 None, 0, None) == 1                            # misaligned
     assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 48, 0, 0.1, FAKE, FAKE, FAKE, FAKE,
-                                 None) == 2                                     # d = 48
+                                 None, 0, None) == 2                            # d = 48
+    assert lib.aah_attn_fwd_diag(FAKE, FAKE, FAKE, wp, None, 1, 2, 2, 64, 64, 0, 0.1, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE + 16, 4096, None) == 1                    # misaligned workspace
+    # The diagnostic forward's split workspace query: 0 for fp32 and for invalid arguments.
+    assert lib.aah_attn_fwd_diag_workspace_size(wp, None, 1, 2, 2, 4096, 64, 1) == 0
+    assert lib.aah_attn_fwd_diag_workspace_size(wp, None, 1, 2, 2, 4096, 48, 0) == 0
     need = aah.head_features_workspace_size(2, 2, 64, 64)
     assert need == 256 * -(-(14 * 2 * 2 * 1 * 8) // 256)                        # one 32768-element span per slice
     assert aah.head_features_workspace_size(1, 1, 4096, 128) == 256 * -(-(14 * 16 * 8) // 256)
@@ -414,7 +420,7 @@ def test_empty_problems():
         # aah_attn_fwd(q, k, v, windows, sinks, B, H, H_kv, T, d, dt, scale, o, lse, ws, bytes, stream)
         assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, 0, N) == 0
         assert lib.aah_attn_fwd(N, N, N, wp, N, B, 2, 1, T, 32, 1, 0.125, N, N, N, 0, N) == 0
-        assert lib.aah_attn_fwd_diag(N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, N, N) == 0
+        assert lib.aah_attn_fwd_diag(N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, N, N, 0, N) == 0
         # aah_attn_bwd(q, k, v, o, dout, lse, windows, sinks, B, H, H_kv, T, d, dt, scale, dq, dk, dv, ws, bytes, s)
         assert lib.aah_attn_bwd(N, N, N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, N, N, 0, N) == 0
         assert lib.aah_attn_bwd_dq(N, N, N, N, N, N, wp, N, B, 2, 2, T, 64, 0, 0.125, N, N, 0, N) == 0

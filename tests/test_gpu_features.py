@@ -89,6 +89,38 @@ def test_fp32_forward_diagnostics(B, H, T, d, windows, sinks):
     assert np.abs(host(nrm) - nrm_ref).max() < 1e-5
 
 
+@pytest.mark.parametrize("B,H,H_kv,T,d,windows,sinks", [
+    (1, 4, 4, 3000, 64, [2000, 256, 3000, 1500], [64, 128, 0, 300]),
+    (1, 4, 2, 2048, 128, [2048, 300, 1000, 2048], None),
+])
+def test_split_diagnostics(B, H, H_kv, T, d, windows, sinks):
+    """Few-item shapes split the diagnostic forward too: each chunk leaves its rows' weighted offsets with
+    (m, l, acc), and the merge forms the entropy and the norm of the combined row.  o and lse bitwise equal to
+    the split attn_fwd (same chunks, same arithmetic); entropy and norm against the oracle within the same
+    bounds as unsplit rows (each weight is still rounded within 2^-8 of its exact value, against its chunk's
+    reference); repeated calls bitwise equal; an empty workspace gives the unsplit launch."""
+    _require_gpu()
+    wl = synth.random_workload(B, H, T, d, windows, dtype="bf16", seed=T + H_kv, backward=False, sinks=sinks,
+                               H_kv=H_kv)
+    assert aah.fwd_workspace_size(wl.windows, B, H, T, d, sinks=sinks, H_kv=H_kv, diag=True) > \
+        aah.fwd_workspace_size(wl.windows, B, H, T, d, sinks=sinks, H_kv=H_kv) > 0
+    q, k, v = dev(wl, "q"), dev(wl, "k"), dev(wl, "v")
+    o0, l0 = aah.attn_fwd(q, k, v, wl.windows, sinks=sinks)
+    o, lse, ent, nrm = aah.attn_fwd_diag(q, k, v, wl.windows, sinks=sinks)
+    _, _, ent2, nrm2 = aah.attn_fwd_diag(q, k, v, wl.windows, sinks=sinks)
+    empty = torch.empty(0, dtype=torch.uint8, device="cuda")
+    ou, lu, eu, nu = aah.attn_fwd_diag(q, k, v, wl.windows, sinks=sinks, workspace=empty)
+    ou0, lu0 = aah.attn_fwd(q, k, v, wl.windows, sinks=sinks, workspace=empty)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(lse, l0)
+    assert torch.equal(ent, ent2) and torch.equal(nrm, nrm2)
+    assert torch.equal(ou, ou0) and torch.equal(lu, lu0)
+    ent_ref, nrm_ref = oracle.attn_row_stats_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, sinks=sinks)
+    vmax = np.repeat(vmax_per_head(wl), H // H_kv, axis=1)
+    check_rows_bf16(host(ent), host(nrm), ent_ref, nrm_ref, vmax)
+    check_rows_bf16(host(eu), host(nu), ent_ref, nrm_ref, vmax)
+
+
 def _check_features(x, wl, ent_dev, nrm_dev):
     ref_dev_rows = oracle.head_features_ref(wl.q, wl.k, wl.v, wl.windows, ent_dev, nrm_dev)
     assert np.allclose(x[:, :6], ref_dev_rows[:, :6], rtol=1e-5, atol=1e-6)

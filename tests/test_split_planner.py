@@ -99,6 +99,25 @@ def test_split_emulation_matches_oracle(windows, B, H, H_kv, T, chunk, sinks):
     assert np.abs(O - Or).max() < 1e-12 and np.abs(L - Lr).max() < 1e-12
 
 
+@pytest.mark.parametrize("windows,B,H,H_kv,T,chunk,sinks", [CASES[1], CASES[4]])
+def test_split_diagnostics_emulation_matches_oracle(windows, B, H, H_kv, T, chunk, sinks):
+    """The split diagnostic forward's merge ("Asymmetric Attention Heads", section 5.3: per-row attention
+    entropy and output norm): chunks keep their weighted offsets against their own references, the merge
+    moves them to the common one; entropy and norm equal the oracle's rows."""
+    rng = np.random.default_rng(2 * T + chunk)
+    d = 8
+    q = rng.standard_normal((B, H, T, d))
+    k = rng.standard_normal((B, H_kv, T, d))
+    v = rng.standard_normal((B, H_kv, T, d))
+    scale = 1 / np.sqrt(d)
+    items, slots, merges = aah.plan_fwd_split(windows, B, H, T, Q_TILE, KV_TILE, chunk, H_kv=H_kv, sinks=sinks)
+    assert len(merges) > 0
+    O, L, E, N = emulate_forward_split(items, slots, merges, q, k, v, windows, scale, Q_TILE, KV_TILE, sinks=sinks,
+                                       diag=True)
+    Er, Nr = oracle.attn_row_stats_ref(q, k, v, windows, scale, sinks=sinks)
+    assert np.abs(E - Er).max() < 1e-10 and np.abs(N - Nr).max() < 1e-12
+
+
 def test_split_plan_argument_errors():
     with pytest.raises(aah.AahError):
         aah.plan_fwd_split([0, 4], 1, 2, 100, Q_TILE, KV_TILE, 4)
