@@ -123,3 +123,52 @@ def test_random_decode_steps(case):
     for cache, hist in ((kc, kh), (vc, vh)):
         rows, valid = oracle.cache_content_ref(hist, windows, [T0 + steps, T0 + steps - 1], T_max, sinks)
         assert np.array_equal(cache.float().cpu().numpy().astype(np.float64)[valid], rows[valid])
+
+
+def _split_shapes(n=10, seed=77):
+    """One sequence, few heads, long windows: layers whose items are few and long, so the forward, the
+    diagnostic forward and both backward kernels take their split launches (head 0 always sees every key)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        H_kv = int(rng.choice([1, 2, 3]))
+        H = H_kv * int(rng.integers(1, 4))
+        T = int(rng.integers(1700, 2700))
+        d = int(rng.choice([32, 64, 128]))
+        windows = [T + 5] + [int(rng.choice([1, 64, 300, 1000, 1800, T + 50])) for _ in range(H - 1)]
+        sinks = None if rng.random() < 0.3 else [int(x) for x in rng.choice([0, 1, 64, 130, 700], size=H)]
+        out.append((H, H_kv, T, d, windows, sinks))
+    return out
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_random_split_layer(case):
+    """Forward, diagnostics and backward of seeded small layers through the split launches, against the
+    oracle (bounds as above; entropy and norm as in tests/test_gpu_features.py)."""
+    if not torch.cuda.is_available():
+        pytest.fail("this test needs a HIP device")
+    H, H_kv, T, d, windows, sinks = _split_shapes()[case]
+    print(f"split case {case}: H={H} H_kv={H_kv} T={T} d={d} windows={windows} sinks={sinks}", flush=True)
+    wl = synth.random_workload(1, H, T, d, windows, dtype="bf16", seed=3000 + case, backward=True, sinks=sinks,
+                               H_kv=H_kv)
+    assert aah.fwd_workspace_size(wl.windows, 1, H, T, d, sinks=sinks, H_kv=H_kv) > 0
+    assert aah.fwd_workspace_size(wl.windows, 1, H, T, d, sinks=sinks, H_kv=H_kv, diag=True) > 0
+    q, k, v, do = (_dev(wl, x, "bf16") for x in ("q", "k", "v", "do"))
+    o, lse, ent, nrm = aah.attn_fwd_diag(q, k, v, wl.windows, wl.scale, sinks=sinks)
+    dq, dk, dv = aah.attn_bwd(q, k, v, o, do, lse, wl.windows, wl.scale, sinks=sinks)
+    torch.cuda.synchronize()
+    O, L = oracle.attn_fwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, sinks=sinks)
+    got = o.float().cpu().numpy().astype(np.float64)
+    assert (np.abs(got - O) - np.maximum(O_TOL_BF16, np.abs(O) * 2.0 ** -8)).max() <= 0
+    assert np.abs(lse.cpu().numpy() - L).max() < LSE_TOL_BF16
+    E, N = oracle.attn_row_stats_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, sinks=sinks)
+    u = 2.0 ** -8 * 1.01
+    vmax = np.repeat(np.linalg.norm(wl.v.astype(np.float64), axis=-1).max(axis=-1)[..., None], H // H_kv, axis=1)
+    e_err = np.abs(ent.cpu().numpy().astype(np.float64) - E)
+    assert (e_err - (2 * u * E + u + 1e-4)).max() <= 0, f"entropy max err {e_err.max():.3e}"
+    n_err = np.abs(nrm.cpu().numpy().astype(np.float64) - N)
+    assert (n_err - (2 * u * vmax + 1e-4)).max() <= 0, f"norm max err {n_err.max():.3e}"
+    refs = oracle.attn_bwd_ref(wl.q, wl.k, wl.v, wl.windows, wl.scale, wl.do, sinks=sinks)
+    for name, g, ref in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+        err = np.abs(g.float().cpu().numpy() - ref).max()
+        assert err <= GRAD_REL * np.abs(ref).max(), (name, err)
