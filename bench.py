@@ -17,7 +17,8 @@ with sink tokens, the sinks each row sees before its window).
 --workload 5 times the same step on the streaming-head layer (heads 0-15 full
 causal, heads 16-31 sink 128 + recent window 256; "Autonomy-of-Heads" section
 5 and 6.1); --workload 6 on a grouped-query layer (32 query heads over 8
-key/value heads, d = 128, per-query-head windows).
+key/value heads, d = 128, per-query-head windows); --workload 6s on that layer
+for one sequence, whose dK/dV kernel takes its split launch.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -44,6 +45,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="3", help="catalogued workload id (default 3: fwd+bwd 1B-scale layer)")
+    ap.add_argument("--no-split", action="store_true",
+                    help="pass workspaces too small for the split launches (one workgroup per work item), to time "
+                         "what splitting buys on layers with few work items")
     ap.add_argument("--cpu-heads", type=int, default=48, help="heads of the oracle CPU-baseline sample (0 = skip)")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward pass only")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -378,13 +382,20 @@ def main():
     # Two resident copies of every input and output, used by alternate steps: a step never finds the
     # previous step's operands still in the device's last-level cache (the inputs of one step, 0.27-0.54 GB
     # on the 1B-scale layer, are about the size of that cache).
+    bwd_split_bytes = (aah.bwd_split_workspace_size(wl.windows, B, H, T, d, sinks=wl.sinks, H_kv=H_kv)
+                       if with_bwd and not args.no_split else 0)
+    fwd_ws = torch.empty(0, dtype=torch.uint8, device="cuda") if args.no_split else None  # None: the binding sizes it
+
     def buffers():
         q, k, v = to_dev(wl, "q"), to_dev(wl, "k"), to_dev(wl, "v")
         bufs = {"q": q, "k": k, "v": v, "o": torch.empty_like(q),
                 "lse": torch.empty((B, H, T), dtype=torch.float32, device="cuda")}
         if with_bwd:
+            # The backward's workspace: the per-row arrays, or, where the library splits the backward's long
+            # items (few work items: one sequence, few heads), the larger split workspace.
+            ws_bytes = max(aah.workspace_size(B, H, T, d, "bf16"), bwd_split_bytes)
             bufs.update(do=to_dev(wl, "do"), dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-                        ws=torch.empty(aah.workspace_size(B, H, T, d, "bf16"), dtype=torch.uint8, device="cuda"))
+                        ws=torch.empty(ws_bytes, dtype=torch.uint8, device="cuda"))
         return bufs
 
     sets = [buffers(), buffers()]
@@ -398,7 +409,7 @@ def main():
         x = sets[i % 2]
         mark(0)
         aah.attn_fwd(x["q"], x["k"], x["v"], wl.windows, wl.scale, out=x["o"], lse=x["lse"], stream=stream,
-                     sinks=wl.sinks)
+                     sinks=wl.sinks, workspace=fwd_ws)
         mark(1)
         if with_bwd:
             aah.attn_bwd_dq(x["q"], x["k"], x["v"], x["o"], x["do"], x["lse"], wl.windows, x["dq"], x["ws"], wl.scale,
@@ -448,12 +459,15 @@ def main():
     sink = "true" if wl.sinks is not None and int(np.max(wl.sinks)) > 0 else "false"
     gqa = "true" if H_kv != H else "false"
     fname = f"fwd_bf16_kernel<{d}, {sink}, false>"
-    if aah.fwd_workspace_size(wl.windows, B, H, T, d, sinks=wl.sinks, H_kv=H_kv) > 0:
+    if not args.no_split and aah.fwd_workspace_size(wl.windows, B, H, T, d, sinks=wl.sinks, H_kv=H_kv) > 0:
         fname += f" + fwd_merge_kernel<{d}>"  # split launch: the forward's events hold both kernels
     kernels = [(fname, float(fwd_ms.mean()), f_fwd)]
     if with_bwd:
-        kernels += [(f"bwd_dkdv_kernel<{d}, {sink}, {gqa}>", float(dkdv_ms.mean()), 8 * d * pairs),
-                    (f"bwd_dq_kernel<{d}, {sink}>", float(dq_ms.mean()), 2 * d * pairs)]
+        # With a split workspace, a backward kernel the library splits is followed by its merge launch, which
+        # that kernel's events then also hold.
+        merge = " (+ bwd_merge_kernel where split)" if bwd_split_bytes > 0 else ""
+        kernels += [(f"bwd_dkdv_kernel<{d}, {sink}, {gqa}>{merge}", float(dkdv_ms.mean()), 8 * d * pairs),
+                    (f"bwd_dq_kernel<{d}, {sink}>{merge}", float(dq_ms.mean()), 2 * d * pairs)]
     kname, kms, kflops = max(kernels, key=lambda x: x[1])
     achieved = kflops / (kms * 1e-3) / 1e12
     roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
@@ -490,6 +504,8 @@ def main():
             "bwd_pct_bf16_peak": round(100 * bwd_tf / PEAK_BF16_TFLOPS, 2) if with_bwd else None,
             "step_pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "step_device_ms_p10_median_p90": [round(float(np.percentile(step_dev_ms, p)), 4) for p in (10, 50, 90)],
+            "bwd_split_workspace": bool(bwd_split_bytes > 0),
+            "split_launches": not args.no_split,
         },
         "roofline": roof,
     }

@@ -483,6 +483,17 @@ def _plan(fn, windows, sinks, B, H, T, q_tile, kv_tile, n_queues, H_kv) -> np.nd
     return arr
 
 
+def bwd_split_workspace_size(windows: Sequence[int], B: int, H: int, T: int, d: int, dtype: str = "bf16",
+                             sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None) -> int:
+    """Workspace bytes with which the backward (and each of its two steps) splits long items on the current
+    device, 0 when it does not; such a workspace also serves the unsplit calls."""
+    w = _windows_arg(windows)
+    sk = _sinks_arg(sinks, H)
+    code = AAH_BF16 if dtype == "bf16" else AAH_F32
+    return int(lib().aah_attn_bwd_split_workspace_size(_wptr(w), _sptr(sk), B, H, H if H_kv is None else H_kv, T,
+                                                       d, code))
+
+
 def plan_fwd(windows: Sequence[int], B: int, H: int, T: int, q_tile: int, kv_tile: int, n_queues: int = 8,
              sinks: Optional[Sequence[int]] = None, H_kv: Optional[int] = None):
     """Forward work list as an int32 array [n, 4] of (bh, q_tile_index, kv_lo, kv_hi)."""

@@ -129,7 +129,13 @@ DESCRIPTIONS = {
        "heads 16-31 sink 128 + recent window 256",
     6: "grouped-query layer fwd+bwd: B=4 H=32 H_kv=8 T=4096 d=128 bf16, "
        "per-query-head windows from {512..4096}, P=(.5,.25,.125,.125)",
+    "6s": "the grouped-query layer for one sequence (B=1) with workload 6's windows: its dK/dV kernel has 256 "
+          "grouped work items for 512 resident workgroups and takes its split launch",
 }
+
+# Workload 6's per-query-head windows (its seed-0 draw, which follows the draw of its tensors).
+GQA_WINDOWS = (512, 2048, 512, 512, 1024, 4096, 1024, 512, 1024, 512, 2048, 512, 2048, 4096, 1024, 512,
+               1024, 512, 2048, 1024, 1024, 2048, 512, 512, 512, 512, 4096, 1024, 4096, 1024, 512, 512)
 
 
 def make_workload(idx, seed: int = 0) -> Workload:
@@ -197,4 +203,13 @@ def make_workload(idx, seed: int = 0) -> Workload:
         return Workload(name="gqa-B4-H32-Hkv8-T4096-d128-fwdbwd", B=B, H=H, T=T, d=d, dtype="bf16",
                         windows=windows, scale=1.0 / np.sqrt(d), q=arrs["q"], k=arrs["k"], v=arrs["v"],
                         do=arrs["do"], bits=bits, backward=True, meta={"H_kv": H_kv})
+    if idx == "6s":
+        B, H, H_kv, T, d = 1, 32, 8, 4096, 128
+        rng = np.random.default_rng(seed)
+        arrs, bits = {}, {}
+        for key in ("q", "k", "v", "do"):
+            arrs[key], bits[key] = _draw(rng, (B, H_kv if key in ("k", "v") else H, T, d), "bf16")
+        return Workload(name="gqa-B1-H32-Hkv8-T4096-d128-fwdbwd", B=B, H=H, T=T, d=d, dtype="bf16",
+                        windows=np.array(GQA_WINDOWS, dtype=np.int32), scale=1.0 / np.sqrt(d), q=arrs["q"],
+                        k=arrs["k"], v=arrs["v"], do=arrs["do"], bits=bits, backward=True, meta={"H_kv": H_kv})
     raise KeyError(f"unknown workload {idx!r}")

@@ -56,3 +56,13 @@ def test_step_counts_are_checked():
                              text=True, timeout=120, cwd=ROOT)
         assert res.returncode == 2, flags
         assert "--steps must be" in res.stderr
+
+
+def test_single_sequence_grouped_workload_shares_the_grouped_layers_windows():
+    """Workload 6s is workload 6 for one sequence: the same per-query-head windows (workload 6 draws them
+    after its tensors, so 6s holds them as a table), which this checks against workload 6's own draw."""
+    import synth
+    w6 = synth.make_workload(6)
+    w6s = synth.make_workload("6s")
+    assert w6s.windows.tolist() == w6.windows.tolist() == list(synth.GQA_WINDOWS)
+    assert (w6s.B, w6s.H, w6s.T, w6s.d, w6s.k.shape[1]) == (1, 32, 4096, 128, 8)
