@@ -354,11 +354,12 @@ void bwd_tiles(aah_dtype dt, int* row, int* col) {
 
 // ------------------------------------------------------------------ split forward
 //
-// A bf16 forward with fewer items than the device holds workgroups leaves
-// most of it idle, and its time is that of its longest items.  Then every
-// item longer than L key tiles is split into chunks of at most L tiles
-// (plan_forward_split), L = max(kMinChunkTiles, total tiles / resident
-// workgroups), so that about one chunk per resident workgroup remains; a merge
+// A bf16 forward whose longest items hold more key tiles than a resident
+// workgroup's share of the whole launch (few items: one sequence, few heads; or
+// items of very unequal length) takes the time of those items while the rest of
+// the device idles.  Then every item longer than L key tiles is split into
+// chunks of at most L tiles (plan_forward_split), L = max(kMinChunkTiles, total
+// tiles / resident workgroups), so that no chunk exceeds that share; a merge
 // launch combines each split item's chunks.  The chunks' partial results live in
 // the caller's workspace (aah_attn_fwd_workspace_size).
 
@@ -396,7 +397,7 @@ int split_chunk_tiles(const int32_t* windows, const int32_t* sinks, int B, int H
   const int n_qt = (T + q_tile - 1) / q_tile;
   const int64_t n_items = static_cast<int64_t>(B) * H * n_qt;
   const int resident = resident_workgroups(d);
-  if (resident <= 0 || n_items >= resident) return 0;
+  if (resident <= 0 || n_items == 0) return 0;
   int64_t total = 0;
   int longest = 0;
   for (int h = 0; h < H; ++h) {
@@ -500,7 +501,7 @@ int resident_bwd(bool dkdv, int d) {
 }
 
 int chunk_len(const std::vector<int>& tiles, int resident) {
-  if (resident <= 0 || static_cast<int64_t>(tiles.size()) >= resident) return 0;
+  if (resident <= 0 || tiles.empty()) return 0;
   int64_t total = 0;
   int longest = 0;
   for (int t : tiles) {

@@ -129,8 +129,9 @@ const char* aah_last_error_detail(void);
  * A non-NULL workspace must be 256-byte aligned (AAH_ERR_INVALID_ARG otherwise,
  * whether or not the launch would split).
  * With a device workspace of at least that many bytes, a bf16
- * launch with fewer work items than the device holds workgroups splits its long
- * items' key ranges into chunks whose partial results (row max, row sum, fp32
+ * launch whose longest items hold more key tiles than L = max(24, total key
+ * tiles / workgroups the device holds at once) splits those items' key ranges
+ * into chunks of at most L tiles whose partial results (row max, row sum, fp32
  * accumulator) land in the workspace, and a second kernel on the same stream
  * merges them into o and lse.  That fills the device when B * H * ceil(T / 128)
  * is small (one sequence, few heads).  With sink keys the first chunk of an
