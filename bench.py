@@ -18,7 +18,8 @@ with sink tokens, the sinks each row sees before its window).
 causal, heads 16-31 sink 128 + recent window 256; "Autonomy-of-Heads" section
 5 and 6.1); --workload 6 on a grouped-query layer (32 query heads over 8
 key/value heads, d = 128, per-query-head windows); --workload 6s on that layer
-for one sequence, whose dK/dV kernel takes its split launch.
+for one sequence, and --workload 5s the streaming-head layer for one sequence,
+both of which take the split launches.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """

@@ -129,6 +129,8 @@ DESCRIPTIONS = {
        "heads 16-31 sink 128 + recent window 256",
     6: "grouped-query layer fwd+bwd: B=4 H=32 H_kv=8 T=4096 d=128 bf16, "
        "per-query-head windows from {512..4096}, P=(.5,.25,.125,.125)",
+    "5s": "the streaming-head layer of workload 5 for one sequence (B=1): its full-causal heads' long items "
+          "exceed a workgroup's share of each launch, so the launches split",
     "6s": "the grouped-query layer for one sequence (B=1) with workload 6's windows: its dK/dV kernel has 256 "
           "grouped work items for 512 resident workgroups and takes its split launch",
 }
@@ -150,9 +152,11 @@ def make_workload(idx, seed: int = 0) -> Workload:
                         windows=np.array([16, 32, 64, 256], dtype=np.int32),
                         scale=1.0 / np.sqrt(32), q=q, k=k, v=v, backward=False)
 
-    if idx in (1, 2, 3, "4a", "4b", "4c", 5):
+    if idx in (1, 2, 3, "4a", "4b", "4c", 5, "5s"):
         if idx == 1:
             B, H = 1, 16
+        elif idx == "5s":
+            B, H = 1, 32
         else:
             B, H = 4, 32
         T, d = 4096, 64
@@ -186,7 +190,7 @@ def make_workload(idx, seed: int = 0) -> Workload:
             # "Autonomy-of-Heads" section 5), half of each at sparsity 0.5 (section 6.4).
             windows = np.where(np.arange(H) < H // 2, T, 256).astype(np.int32)
             meta["sinks"] = np.where(np.arange(H) < H // 2, 0, 128).astype(np.int32)
-            name = "streaming-B4-H32-T4096-d64-sink128-recent256"
+            name = f"streaming-B{B}-H32-T4096-d64-sink128-recent256"
         backward = idx != 1 and idx != 2
         sinks = meta.pop("sinks", None)
         return Workload(name=name, B=B, H=H, T=T, d=d, dtype="bf16", windows=windows,
